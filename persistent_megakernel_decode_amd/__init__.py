@@ -1,0 +1,263 @@
+"""Persistent decode megakernel for AMD MI355X (gfx950) -- Python binding.
+
+A thin ctypes layer over libmk.so, whose C ABI is include/mk.h.  Every step
+of the decode path runs inside the HIP megakernel; this module only moves
+arguments across the boundary.  PyTorch supplies device memory and streams.
+
+The library is required: importing this package without a built libmk.so
+raises, and there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmk.so")
+
+MK_ABI_VERSION = 1
+MK_OK, MK_ERR_INVALID_ARG, MK_ERR_UNSUPPORTED, MK_ERR_HIP, MK_ERR_DEVICE_INPUT, MK_ERR_TIMEOUT, MK_ERR_STATE = \
+    0, -1, -2, -3, -4, -5, -6
+MK_LAYER_ATTN, MK_LAYER_DELTA = 0, 1
+MK_MID_X_MIXER, MK_MID_X_MLP, MK_MID_MIXER_O, MK_MID_MLP_M = 0, 1, 2, 3
+
+STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID_ARG", -2: "MK_ERR_UNSUPPORTED", -3: "MK_ERR_HIP",
+                -4: "MK_ERR_DEVICE_INPUT", -5: "MK_ERR_TIMEOUT", -6: "MK_ERR_STATE"}
+
+P = ctypes.c_void_p
+I32 = ctypes.c_int32
+
+
+class mk_model_desc(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_uint32), ("struct_size", ctypes.c_uint32),
+                ("n_layers", I32), ("hidden", I32), ("vocab", I32), ("ffn", I32),
+                ("n_q_heads", I32), ("n_kv_heads", I32), ("head_dim", I32), ("qk_norm", I32),
+                ("tied_embeddings", I32), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
+                ("n_delta_heads", I32), ("delta_dk", I32), ("delta_dv", I32), ("conv_width", I32),
+                ("layer_kind", P), ("max_batch", I32), ("max_ctx", I32), ("page_size", I32)]
+
+
+LAYER_FIELDS = ["attn_norm", "wq", "wk", "wv", "wo", "q_norm", "k_norm", "w_qkv_delta", "w_gates", "conv_w",
+                "wo_delta", "mlp_norm", "w_gate", "w_up", "w_down"]
+
+
+class mk_layer_weights(ctypes.Structure):
+    _fields_ = [(f, P) for f in LAYER_FIELDS]
+
+
+class mk_weights(ctypes.Structure):
+    _fields_ = [("embed", P), ("final_norm", P), ("lm_head", P), ("layers", P)]
+
+
+class mk_kv_cache(ctypes.Structure):
+    _fields_ = [("k_pages", P), ("v_pages", P), ("num_pages", I32), ("max_pages_per_seq", I32),
+                ("page_table", P), ("delta_state", P), ("conv_state", P)]
+
+
+class mk_plan_info(ctypes.Structure):
+    _fields_ = [("n_cus", I32), ("n_ops", I32), ("n_stages", I32), ("max_ops_per_cu", I32),
+                ("weight_bytes", ctypes.c_double), ("max_cu_bytes", ctypes.c_double),
+                ("mean_cu_bytes", ctypes.c_double), ("errors", I32)]
+
+
+EXPORTED = ["mk_workspace_size", "mk_create", "mk_decode_step", "mk_sync_status", "mk_reset", "mk_last_error",
+            "mk_destroy", "mk_plan", "mk_copy_midstate"]
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmk.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with persistent_megakernel_decode_amd/build.py "
+                               "(there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.mk_workspace_size.argtypes = [ctypes.POINTER(mk_model_desc), ctypes.POINTER(ctypes.c_size_t)]
+        L.mk_create.argtypes = [ctypes.POINTER(mk_model_desc), ctypes.POINTER(mk_weights),
+                                ctypes.POINTER(mk_kv_cache), P, ctypes.c_size_t, ctypes.POINTER(P)]
+        L.mk_decode_step.argtypes = [P, P, P, P, I32, P, P]
+        L.mk_sync_status.argtypes = [P]
+        L.mk_reset.argtypes = [P]
+        L.mk_last_error.argtypes = []
+        L.mk_last_error.restype = ctypes.c_char_p
+        L.mk_destroy.argtypes = [P]
+        L.mk_destroy.restype = None
+        L.mk_plan.argtypes = [ctypes.POINTER(mk_model_desc), I32, ctypes.POINTER(mk_plan_info)]
+        L.mk_copy_midstate.argtypes = [P, I32, I32, P, ctypes.c_size_t, P]
+        for f in ("mk_workspace_size", "mk_create", "mk_decode_step", "mk_sync_status", "mk_reset", "mk_plan",
+                  "mk_copy_midstate"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+class MKError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().mk_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+
+
+def check(status: int, where: str) -> None:
+    if status != MK_OK:
+        raise MKError(status, where)
+
+
+# ---------------------------------------------------------------- C-ABI wrappers (same names)
+def make_desc(n_layers, hidden, vocab, ffn, n_q_heads, n_kv_heads, head_dim, qk_norm, tied_embeddings, rms_eps,
+              rope_base, layer_kinds: Sequence[int], max_batch, max_ctx, n_delta_heads=0, delta_dk=0, delta_dv=0,
+              conv_width=0, page_size=16):
+    kinds = (I32 * n_layers)(*layer_kinds)
+    d = mk_model_desc(MK_ABI_VERSION, ctypes.sizeof(mk_model_desc), n_layers, hidden, vocab, ffn, n_q_heads,
+                      n_kv_heads, head_dim, qk_norm, tied_embeddings, rms_eps, rope_base, n_delta_heads, delta_dk,
+                      delta_dv, conv_width, ctypes.cast(kinds, P), max_batch, max_ctx, page_size)
+    d._kinds = kinds  # keep the array alive with the struct
+    return d
+
+
+def mk_workspace_size(desc: mk_model_desc) -> int:
+    n = ctypes.c_size_t(0)
+    check(lib().mk_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "mk_workspace_size")
+    return n.value
+
+
+def mk_plan(desc: mk_model_desc, n_cus: int) -> mk_plan_info:
+    info = mk_plan_info()
+    check(lib().mk_plan(ctypes.byref(desc), n_cus, ctypes.byref(info)), "mk_plan")
+    return info
+
+
+def mk_create(desc, weights: mk_weights, cache: mk_kv_cache, workspace_ptr: int, workspace_bytes: int) -> int:
+    out = P()
+    check(lib().mk_create(ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(cache), workspace_ptr,
+                          workspace_bytes, ctypes.byref(out)), "mk_create")
+    return out.value
+
+
+def mk_decode_step(ctx: int, tokens_ptr: int, positions_ptr: int, ctx_lens_ptr: int, batch: int, logits_ptr: int,
+                   stream: int = 0) -> int:
+    return lib().mk_decode_step(ctx, tokens_ptr, positions_ptr, ctx_lens_ptr, batch, logits_ptr, stream or None)
+
+
+def mk_sync_status(ctx: int) -> int:
+    return lib().mk_sync_status(ctx)
+
+
+def mk_reset(ctx: int) -> int:
+    return lib().mk_reset(ctx)
+
+
+def mk_last_error() -> str:
+    return lib().mk_last_error().decode(errors="replace")
+
+
+def mk_destroy(ctx: int) -> None:
+    lib().mk_destroy(ctx)
+
+
+def mk_copy_midstate(ctx: int, kind: int, layer: int, dst_ptr: int, count: int, stream: int = 0) -> int:
+    return lib().mk_copy_midstate(ctx, kind, layer, dst_ptr, count, stream or None)
+
+
+# ---------------------------------------------------------------- device-resident model
+class DecodeContext:
+    """Owns the device tensors of one model and its mk_ctx.
+
+    `weights` / `cache` are dicts of host numpy arrays (bf16 as uint16) in the layout include/mk.h
+    documents; they are copied to `device` once.  Only memory and the stream come from PyTorch.
+    """
+
+    def __init__(self, shape: dict, weights: dict, cache: dict, device: str = "cuda:0"):
+        import torch
+        self.torch = torch
+        self.device = torch.device(device)
+        self.shape = dict(shape)
+        t = lambda a, dt=None: torch.from_numpy(a).to(self.device) if dt is None else torch.from_numpy(a).view(dt).to(self.device)
+        i16 = torch.int16
+        self.tensors: Dict[str, "torch.Tensor"] = {}
+        keep: List = self.tensors.setdefault("_all", [])
+
+        def dev(a, dt=None):
+            x = t(a, dt)
+            keep.append(x)
+            return x
+
+        s = self.shape
+        self.desc = make_desc(s["n_layers"], s["hidden"], s["vocab"], s["ffn"], s["n_q_heads"], s["n_kv_heads"],
+                              s["head_dim"], s["qk_norm"], s["tied"], s["rms_eps"], s["rope_base"], s["layer_kinds"],
+                              s["max_batch"], s["max_ctx"], s.get("n_delta_heads", 0), s.get("delta_dk", 0),
+                              s.get("delta_dv", 0), s.get("conv_width", 0), s.get("page_size", 16))
+        self.embed = dev(weights["embed"], i16)
+        final_norm = dev(weights["final_norm"], i16)
+        lm = self.embed if s["tied"] else dev(weights["lm_head"], i16)
+        self.layers = (mk_layer_weights * s["n_layers"])()
+        for l, L in enumerate(weights["layers"]):
+            for f in LAYER_FIELDS:
+                if f in L:
+                    setattr(self.layers[l], f, dev(L[f], i16).data_ptr())
+        self.w = mk_weights(self.embed.data_ptr(), final_norm.data_ptr(), lm.data_ptr(), ctypes.cast(self.layers, P))
+        self.k_pages = dev(cache["k_pages"], i16)
+        self.v_pages = dev(cache["v_pages"], i16)
+        self.page_table = dev(cache["page_table"])
+        self.delta_state = dev(cache["delta_state"]) if "delta_state" in cache else None
+        self.conv_state = dev(cache["conv_state"]) if "conv_state" in cache else None
+        self.c = mk_kv_cache(self.k_pages.data_ptr(), self.v_pages.data_ptr(), int(cache["num_pages"]),
+                             int(cache["max_pages_per_seq"]), self.page_table.data_ptr(),
+                             self.delta_state.data_ptr() if self.delta_state is not None else None,
+                             self.conv_state.data_ptr() if self.conv_state is not None else None)
+        with torch.cuda.device(self.device):
+            self.ws_bytes = mk_workspace_size(self.desc)
+            self.workspace = torch.zeros(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
+            base = self.workspace.data_ptr()
+            self.ws_ptr = (base + 255) // 256 * 256
+            self.ctx = mk_create(self.desc, self.w, self.c, self.ws_ptr, self.ws_bytes)
+        B = s["max_batch"]
+        self.tokens = torch.zeros(B, dtype=torch.int32, device=self.device)
+        self.positions = torch.zeros(B, dtype=torch.int32, device=self.device)
+        self.ctx_lens = torch.zeros(B, dtype=torch.int32, device=self.device)
+        self.logits = torch.zeros((B, s["vocab"]), dtype=torch.float32, device=self.device)
+
+    def stream_ptr(self, stream=None) -> int:
+        st = stream if stream is not None else self.torch.cuda.current_stream(self.device)
+        return int(st.cuda_stream)
+
+    def step(self, tokens, positions, ctx_lens, stream=None) -> int:
+        """Enqueue one decode step from host lists (copied into device int32 arrays first)."""
+        B = len(tokens)
+        T = self.torch
+        self.tokens[:B].copy_(T.as_tensor(list(tokens), dtype=T.int32))
+        self.positions[:B].copy_(T.as_tensor(list(positions), dtype=T.int32))
+        self.ctx_lens[:B].copy_(T.as_tensor(list(ctx_lens), dtype=T.int32))
+        return mk_decode_step(self.ctx, self.tokens.data_ptr(), self.positions.data_ptr(), self.ctx_lens.data_ptr(),
+                              B, self.logits.data_ptr(), self.stream_ptr(stream))
+
+    def step_device(self, batch: int, stream=None) -> int:
+        """Enqueue one decode step reading the device arrays self.tokens / positions / ctx_lens as they are."""
+        return mk_decode_step(self.ctx, self.tokens.data_ptr(), self.positions.data_ptr(), self.ctx_lens.data_ptr(),
+                              batch, self.logits.data_ptr(), self.stream_ptr(stream))
+
+    def sync(self) -> int:
+        return mk_sync_status(self.ctx)
+
+    def reset(self) -> int:
+        return mk_reset(self.ctx)
+
+    def midstate(self, kind: int, layer: int, width: int, batch: int):
+        out = self.torch.empty((batch, width), dtype=self.torch.float32, device=self.device)
+        check(mk_copy_midstate(self.ctx, kind, layer, out.data_ptr(), batch * width, self.stream_ptr()),
+              "mk_copy_midstate")
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "ctx", None):
+            mk_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,51 @@
+"""Build libmk.so (the megakernel, scheduler and C ABI) in-tree with hipcc for gfx950."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libmk.so")
+SOURCES = ["mk_kernel.hip", "mk_api.cpp", "mk_sched.cpp"]
+HEADERS = ["mk_internal.h", "mk_sched.h", os.path.join("..", "..", "include", "mk.h")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-x", "hip",
+    # packed fp32 VALU ops are kept out of every kernel (they are not needed and are avoided on this part)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def sources():
+    return [os.path.join(CSRC, s) for s in SOURCES]
+
+
+def stale() -> bool:
+    if not os.path.exists(LIB):
+        return True
+    t = os.path.getmtime(LIB)
+    return any(os.path.getmtime(os.path.join(CSRC, f)) > t for f in SOURCES + HEADERS)
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    """Compile libmk.so.  With force=False an up-to-date library is kept."""
+    if not force and not stale():
+        return LIB
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, *sources(), "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l and l.strip())
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+    if verbose and out:
+        print(out, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(force=True, verbose=True))

@@ -1,0 +1,143 @@
+// mk_internal.h -- the compiled plan shared by the host scheduler (mk_sched.cpp)
+// and the gfx950 megakernel (mk_kernel.hip).
+//
+// The ForgeMegakernel abstract (arxivdaily / arxiv.science, abstract) builds a
+// decode megakernel from three structures: a fine-grained instruction stream
+// per compute unit, dependency counters in place of grid-wide
+// synchronisation, and an on-chip buffer pool that stages data for the
+// compute.  Here they are:
+//   * Op          -- one queue entry; each workgroup (one per CU) runs its own
+//                    queue of Ops in order.
+//   * Stage       -- a set of Ops whose completion others wait on; each Stage
+//                    owns NSUB split counters in global memory that count
+//                    finished Ops, cumulatively over steps (epoch * count).
+//   * LDS ring    -- NSLOT slots of SLOT bytes, filled by a loader wave with
+//                    LDS-DMA loads of the weight / KV / state bytes every Op
+//                    streams, consumed by the compute waves.
+#pragma once
+#include <stdint.h>
+
+namespace mk {
+
+// ---- workgroup shape ----
+constexpr int NC = 8;                  // compute waves per workgroup (wave 0 is the loader)
+constexpr int NTHREADS = 64 * (NC + 1);
+constexpr int PIECE = 1024;            // bytes moved by one LDS-DMA instruction (64 lanes x 16 B)
+constexpr int SLOT_PIECES = 8;         // pieces per ring slot (== NC: one piece per compute wave)
+constexpr int SLOT = PIECE * SLOT_PIECES;
+constexpr int NSLOT = 16;              // 128 KB ring
+constexpr int LOAD_DEPTH = 4;          // slots in flight per loader wave before it marks the oldest
+constexpr int RED_FLOATS = 4096;       // 16 KB partial-sum / merge area
+constexpr int SCRATCH_FLOATS = 512;    // 2 KB small cross-wave scratch
+
+// ---- dependency counters ----
+constexpr int NSUB = 16;               // split sub-counters per stage
+constexpr int CTR_STRIDE = 32;         // u32 between sub-counters (128 B, one cache line each)
+
+// ---- GEMV geometry ----
+constexpr int PIECE_ELEMS = PIECE / 2; // bf16 weights per piece row-segment
+constexpr int MAX_M = 4;               // pieces of one row per compute wave (rows up to 16384 elements)
+
+enum Opcode : uint8_t { OP_NOP = 0, OP_EMBED = 1, OP_GEMV = 2, OP_ATTN = 3, OP_DELTA = 4 };
+enum Epi : uint8_t { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+
+constexpr int16_t NO_STAGE = -1;
+
+// One queue entry (128 bytes).  Pointers are device addresses.
+//
+// A GEMV op computes output rows [row0, row0 + nrows) of a row space that may
+// be the concatenation of up to three weight tensors: global row r comes from
+// W (r < b1), W2 (b1 <= r < b2) or W3 (r >= b2), each indexed from its own
+// first row.  EPI_SWIGLU streams the gate rows of W, then the same rows of W2
+// (up), and writes silu(gate) * up.
+struct alignas(16) Op {
+  uint8_t opcode;
+  uint8_t epi;
+  uint8_t norm;        // GEMV: 1 = RMSNorm the input with `gamma`
+  uint8_t pad0;
+  int16_t wait_stage;  // stage this op waits for (NO_STAGE = none)
+  int16_t sig_stage;   // stage this op counts towards (NO_STAGE = none)
+  uint32_t sig_index;  // index of this op within sig_stage (selects the sub-counter)
+  uint32_t layer;      // model layer
+  uint32_t row0;       // GEMV: first output row;  ATTN / DELTA: item index
+  uint32_t nrows;      // GEMV: output rows
+  uint32_t K;          // GEMV: input length
+  uint32_t ppr;        // GEMV: pieces per row (padded to 1, 2, 4 or a multiple of 8)
+  uint32_t nslots;     // GEMV / DELTA: ring slots the op consumes (ATTN: computed at run time)
+  uint32_t ld_in;      // floats between batch rows of `in`
+  uint32_t ld_out;     // floats between batch rows of `out` / `res`
+  uint32_t b1, b2;     // GEMV: row-space boundaries between W, W2 and W3
+  uint64_t W, W2, W3;  // GEMV weights, bf16 [rows][K]
+  uint64_t in;         // fp32 [batch][ld_in]
+  uint64_t gamma;      // bf16 [K] norm gain (norm == 1)
+  uint64_t out;        // fp32 [batch][ld_out] (EPI_LOGITS writes the launch's logits instead)
+  uint64_t res;        // fp32 [batch][ld_out] residual (EPI_RESID)
+  uint64_t pad2;
+};
+static_assert(sizeof(Op) == 128, "Op must stay 128 bytes");
+
+// Per-layer device pointers used by ATTN / DELTA ops.
+struct alignas(16) LayerDesc {
+  uint64_t qkv;          // attn: fp32 [B][(Hq + 2 Hkv) d] raw projections;  delta: u fp32 [B][C]
+  uint64_t gates;        // delta: fp32 [B][2 heads]
+  uint64_t q_norm, k_norm;
+  uint64_t k_pages, v_pages;   // this attention layer's pages
+  uint64_t part;         // attn: fp32 partials [n_items][G][d + 2]
+  uint64_t tickets;      // attn: u32 [B][Hkv] merge tickets
+  uint64_t mix_o;        // fp32 [B][mix] attention / delta output before o_proj
+  uint64_t conv_w;       // delta: bf16 [C][W]
+  uint64_t conv_state;   // delta: fp32 [B][C][W-1]
+  uint64_t delta_state;  // delta: fp32 [B][heads][dv][dk]
+};
+
+struct Stage {
+  uint32_t nops;         // ops that signal this stage per step
+  uint32_t pad;
+};
+
+// Everything the kernel needs, passed by value.
+struct KArgs {
+  // plan
+  const Op* ops;              // all queues, concatenated
+  const uint32_t* queue_off;  // [n_cus + 1] start of each CU's queue in ops
+  const Stage* stages;
+  uint32_t* counters;         // [n_stages][NSUB * CTR_STRIDE]
+  const LayerDesc* layers;
+  const float* rope;          // [max_ctx][d/2][2] (cos, sin)
+  uint32_t* status;           // [0] sticky error bits, [1] timeout flag
+  int32_t* row_ok;            // [max_batch]
+  float* x0;                  // embedding output fp32 [max_batch][H]
+  const uint16_t* embed;
+  const int32_t* page_table;
+  // model
+  int32_t H, V, Hq, Hkv, d, G, qk_norm, max_batch, max_ctx, page_size, num_pages, max_pages_per_seq;
+  int32_t nh, dk, dv, C, convw;
+  int32_t n_cus, n_items;     // attention work items per attention layer
+  int32_t mix;                // floats between batch rows of the attention / delta output
+  float rms_eps;
+  // per launch
+  const int32_t* tokens;
+  const int32_t* positions;
+  const int32_t* ctx_lens;
+  float* logits;
+  int32_t batch;
+  uint32_t epoch;
+  uint64_t spin_limit;        // watchdog, in s_memrealtime ticks (100 MHz)
+};
+
+// status bits
+constexpr uint32_t ST_BAD_INPUT = 1u;
+constexpr uint32_t ST_TIMEOUT = 2u;
+
+// Attention work split: chunk size in positions for the current step.
+// Every sequence b is cut into ceil(ctx_b / cs) chunks per KV head; cs is a
+// multiple of the positions one ring slot holds.
+__host__ __device__ inline int32_t attn_chunk_size(int64_t total_ctx, int32_t Hkv, int32_t target_items,
+                                                   int32_t slot_positions) {
+  int64_t per = (total_ctx * Hkv + target_items - 1) / target_items;
+  if (per < 1) per = 1;
+  int64_t cs = (per + slot_positions - 1) / slot_positions * slot_positions;
+  return (int32_t)cs;
+}
+
+}  // namespace mk

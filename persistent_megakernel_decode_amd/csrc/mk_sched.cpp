@@ -1,0 +1,392 @@
+// mk_sched.cpp -- compiles a model into per-compute-unit instruction queues.
+//
+// The ForgeMegakernel abstract (arxivdaily / arxiv.science, abstract) gives
+// each SM a fine-grained instruction stream and replaces global
+// synchronisation with dependency counters.  This scheduler produces exactly
+// that for gfx950: every projection is cut into row tiles (one or more per
+// compute unit, balanced to within one row), attention into (sequence, KV
+// head, position chunk) items, and the delta rule into (sequence, head,
+// 32-column block) items.  Ops are grouped into dependency stages; every
+// queue lists its ops in one global stage order, so the lowest unfinished
+// stage is always runnable and the persistent grid cannot deadlock.
+//
+// Split-K is never used: the MK-KDA pull request (github choiceoh/stkernel
+// #230, commit message) measured split-K slowing an o_proj down once slices
+// got short, and at these shapes every projection has at least as many rows
+// as there are compute units (tiny test shapes aside).
+#include "mk_sched.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+namespace mk {
+
+static constexpr uint64_t WS_TAG = 1ull << 62;  // marks a workspace-relative address
+static inline uint64_t ws(size_t off) { return WS_TAG | (uint64_t)off; }
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+template <typename... Args>
+static std::string fmt(const char* f, Args... a) {
+  char buf[512];
+  snprintf(buf, sizeof buf, f, a...);
+  return buf;
+}
+
+std::string validate_desc(const mk_model_desc* desc, ModelShape* out, mk_status* st) {
+  *st = MK_ERR_INVALID_ARG;
+  if (!desc) return "null model description";
+  if (desc->abi_version != MK_ABI_VERSION) return fmt("abi_version %u, library speaks %u", desc->abi_version, MK_ABI_VERSION);
+  if (desc->struct_size != sizeof(mk_model_desc)) return fmt("struct_size %u != %zu", desc->struct_size, sizeof(mk_model_desc));
+  const mk_model_desc& d = *desc;
+  if (d.n_layers < 1 || d.hidden < 8 || d.vocab < 1 || d.ffn < 8) return "n_layers, hidden, vocab and ffn must be positive";
+  if (!d.layer_kind) return "layer_kind is null";
+  if (d.max_batch < 1 || d.max_ctx < 1) return "max_batch and max_ctx must be positive";
+  *st = MK_ERR_UNSUPPORTED;
+  if (d.max_batch > 8) return "max_batch above 8 is not supported";
+  if (d.hidden % 8 || d.ffn % 8) return "hidden and ffn must be multiples of 8";
+  if (d.page_size != 16) return "page_size must be 16";
+  if (!(d.rms_eps > 0.0f) || !(d.rope_base > 1.0f)) return "rms_eps must be > 0 and rope_base > 1";
+  out->d = d;
+  out->kinds.assign(d.layer_kind, d.layer_kind + d.n_layers);
+  out->n_attn = out->n_delta = 0;
+  for (int32_t k : out->kinds) {
+    if (k == MK_LAYER_ATTN) ++out->n_attn;
+    else if (k == MK_LAYER_DELTA) ++out->n_delta;
+    else return fmt("layer kind %d is not ATTN or DELTA", k);
+  }
+  if (out->n_attn) {
+    if (d.head_dim != 64 && d.head_dim != 128) return "head_dim must be 64 or 128";
+    if (d.n_kv_heads < 1 || d.n_q_heads < 1 || d.n_q_heads % d.n_kv_heads) return "n_q_heads must be a multiple of n_kv_heads";
+    out->G = d.n_q_heads / d.n_kv_heads;
+    if (out->G * d.head_dim > 512) return "query heads per KV head times head_dim must not exceed 512";
+  }
+  if (out->n_delta) {
+    if (d.delta_dk != 64 && d.delta_dk != 128) return "delta_dk must be 64 or 128";
+    if (d.delta_dv < 32 || d.delta_dv % 32) return "delta_dv must be a positive multiple of 32";
+    if (d.conv_width != 4) return "conv_width must be 4";
+    if (d.n_delta_heads < 1) return "n_delta_heads must be positive";
+    out->C = d.n_delta_heads * (2 * d.delta_dk + d.delta_dv);
+  }
+  *st = MK_OK;
+  return "";
+}
+
+static int pad_ppr(int K) {
+  const int real = (K + PIECE_ELEMS - 1) / PIECE_ELEMS;
+  if (real <= 1) return 1;
+  if (real <= 2) return 2;
+  if (real <= 4) return 4;
+  return (real + 7) / 8 * 8;
+}
+static int mmax_for(int B) { return B <= 2 ? 4 : (B <= 4 ? 2 : 1); }
+
+namespace {
+struct Builder {
+  const ModelShape& m;
+  Plan& P;
+  int n_cus;
+  std::vector<std::vector<Op>> stage_ops;  // per stage
+  std::string err;
+
+  int new_stage() {
+    stage_ops.emplace_back();
+    return (int)stage_ops.size() - 1;
+  }
+
+  // Row-tiled GEMV stage over N output rows of length K.
+  void gemv(int stage, int wait, int layer, uint32_t N, uint32_t K, uint8_t epi, bool norm, uint64_t W, uint64_t W2,
+            uint64_t W3, uint32_t b1, uint32_t b2, uint64_t in, uint32_t ld_in, uint64_t gamma, uint64_t out,
+            uint32_t ld_out, uint64_t res) {
+    if (!err.empty()) return;
+    const int B = P.kernel_batch;
+    const int ppr = pad_ppr((int)K);
+    if (ppr >= 8 && ppr / 8 > mmax_for(B)) {
+      err = fmt("projection with %u inputs is too long for batch width %d", K, B);
+      return;
+    }
+    if (K % 8) {
+      err = fmt("projection input length %u is not a multiple of 8", K);
+      return;
+    }
+    const int RW = std::min(ppr, 8);
+    const int mult = epi == EPI_SWIGLU ? 2 : 1;
+    const uint32_t maxrows = (uint32_t)(RED_FLOATS / (RW * B * mult));
+    uint32_t T = std::min<uint32_t>((uint32_t)n_cus, N);
+    if ((N + T - 1) / T > maxrows) {
+      T = (N + maxrows - 1) / maxrows;
+      T = (T + n_cus - 1) / n_cus * n_cus;
+    }
+    for (uint32_t t = 0; t < T; ++t) {
+      const uint32_t r0 = (uint32_t)((uint64_t)N * t / T), r1 = (uint32_t)((uint64_t)N * (t + 1) / T);
+      if (r1 == r0) continue;
+      Op o{};
+      o.opcode = OP_GEMV;
+      o.epi = epi;
+      o.norm = norm ? 1 : 0;
+      o.wait_stage = (int16_t)wait;
+      o.sig_stage = (int16_t)stage;
+      o.layer = (uint32_t)layer;
+      o.row0 = r0;
+      o.nrows = r1 - r0;
+      o.K = K;
+      o.ppr = (uint32_t)ppr;
+      o.nslots = (o.nrows * mult * ppr + SLOT_PIECES - 1) / SLOT_PIECES;
+      o.ld_in = ld_in;
+      o.ld_out = ld_out;
+      o.b1 = b1;
+      o.b2 = b2;
+      o.W = W; o.W2 = W2; o.W3 = W3;
+      o.in = in; o.gamma = gamma; o.out = out; o.res = res;
+      stage_ops[stage].push_back(o);
+    }
+  }
+
+  void items(int stage, int wait, int layer, uint8_t opcode, int n, uint32_t nslots) {
+    for (int i = 0; i < n; ++i) {
+      Op o{};
+      o.opcode = opcode;
+      o.wait_stage = (int16_t)wait;
+      o.sig_stage = (int16_t)stage;
+      o.layer = (uint32_t)layer;
+      o.row0 = (uint32_t)i;
+      o.nslots = nslots;
+      stage_ops[stage].push_back(o);
+    }
+  }
+};
+}  // namespace
+
+std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, const mk_kv_cache* c, Plan* plan) {
+  const mk_model_desc& d = m.d;
+  Plan& P = *plan;
+  P = Plan{};
+  P.n_cus = n_cus;
+  if (n_cus < 1) return "n_cus must be positive";
+  P.kernel_batch = d.max_batch <= 1 ? 1 : d.max_batch <= 2 ? 2 : d.max_batch <= 4 ? 4 : 8;
+  const int B = P.kernel_batch;  // activation buffers are B rows wide
+  const int H = d.hidden, F = d.ffn, L = d.n_layers;
+  const int hd = m.n_attn ? d.head_dim : 0;
+  const int Hq = d.n_q_heads, Hkv = d.n_kv_heads;
+  const int qkv_w = m.n_attn ? (Hq + 2 * Hkv) * hd : 0;
+  const int nh = d.n_delta_heads, dk = d.delta_dk, dv = d.delta_dv;
+  const int u_w = m.n_delta ? m.C + 2 * nh : 0;
+  P.mix_dim = std::max(m.n_attn ? Hq * hd : 0, m.n_delta ? nh * dv : 0);
+  P.n_items = m.n_attn ? n_cus + Hkv * d.max_batch : 0;
+  const int gmax = m.n_attn ? 512 / hd : 0;
+
+  // ---------------- workspace layout (offsets; sizes of the queue sections are known after planning)
+  Layout& Y = P.lay;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
+  // activation sections first (their offsets are needed while building ops)
+  Y.rope = take(m.n_attn ? (size_t)d.max_ctx * (hd / 2) * 2 * sizeof(float) : 16);
+  Y.status = take(256);
+  Y.row_ok = take((size_t)B * 4);
+  Y.x0 = take((size_t)B * H * 4);
+  Y.layer.resize(L);
+  Y.tickets_bytes_per_layer = (size_t)B * std::max(Hkv, nh) * 4;
+  for (int l = 0; l < L; ++l) {
+    auto& Q = Y.layer[l];
+    if (m.kinds[l] == MK_LAYER_ATTN) {
+      Q.qkv = take((size_t)B * qkv_w * 4);
+      Q.part = take((size_t)P.n_items * gmax * (hd + 2) * 4);
+    } else {
+      Q.qkv = take((size_t)B * u_w * 4);
+    }
+    Q.tickets = take(Y.tickets_bytes_per_layer);
+    Q.mix_o = take((size_t)B * P.mix_dim * 4);
+    Q.x_mix = take((size_t)B * H * 4);
+    Q.m = take((size_t)B * F * 4);
+    Q.x_out = take((size_t)B * H * 4);
+  }
+
+  // ---------------- stages and ops
+  Builder bd{m, P, n_cus, {}, ""};
+  auto wptr = [&](const void* p) -> uint64_t { return (uint64_t)(uintptr_t)p; };
+  const mk_layer_weights* LW = w ? w->layers : nullptr;
+  const uint64_t NONE = ~0u;
+  const int s_embed = bd.new_stage();
+  bd.items(s_embed, NO_STAGE, 0, OP_EMBED, n_cus, 0);
+  int prev = s_embed;
+  uint64_t x_in = ws(Y.x0);
+  int ia = 0, id = 0;
+  P.layers.resize(L);
+  for (int l = 0; l < L; ++l) {
+    const auto& Q = Y.layer[l];
+    const mk_layer_weights* lw = LW ? &LW[l] : nullptr;
+    LayerDesc& D = P.layers[l];
+    D.qkv = ws(Q.qkv);
+    D.tickets = ws(Q.tickets);
+    D.mix_o = ws(Q.mix_o);
+    int s_mix;
+    if (m.kinds[l] == MK_LAYER_ATTN) {
+      D.part = ws(Q.part);
+      if (lw) { D.q_norm = wptr(lw->q_norm); D.k_norm = wptr(lw->k_norm); }
+      if (c) {
+        const size_t per_layer = (size_t)c->num_pages * Hkv * d.page_size * hd * 2;
+        D.k_pages = wptr(c->k_pages) + per_layer * ia;
+        D.v_pages = wptr(c->v_pages) + per_layer * ia;
+      }
+      const int s_qkv = bd.new_stage();
+      bd.gemv(s_qkv, prev, l, (uint32_t)qkv_w, (uint32_t)H, EPI_STORE, true, lw ? wptr(lw->wq) : 0,
+              lw ? wptr(lw->wk) : 0, lw ? wptr(lw->wv) : 0, (uint32_t)(Hq * hd), (uint32_t)((Hq + Hkv) * hd), x_in,
+              (uint32_t)H, lw ? wptr(lw->attn_norm) : 0, ws(Q.qkv), (uint32_t)qkv_w, 0);
+      const int s_attn = bd.new_stage();
+      bd.items(s_attn, s_qkv, l, OP_ATTN, P.n_items, 0);
+      s_mix = bd.new_stage();
+      bd.gemv(s_mix, s_attn, l, (uint32_t)H, (uint32_t)(Hq * hd), EPI_RESID, false, lw ? wptr(lw->wo) : 0, 0, 0,
+              (uint32_t)NONE, (uint32_t)NONE, ws(Q.mix_o), (uint32_t)P.mix_dim, 0, ws(Q.x_mix), (uint32_t)H, x_in);
+      ++ia;
+    } else {
+      D.gates = ws(Q.qkv) + (uint64_t)m.C * 4;
+      if (lw) D.conv_w = wptr(lw->conv_w);
+      if (c) {
+        D.conv_state = wptr(c->conv_state) + (uint64_t)id * d.max_batch * m.C * (d.conv_width - 1) * 4;
+        D.delta_state = wptr(c->delta_state) + (uint64_t)id * d.max_batch * nh * dv * dk * 4;
+      }
+      const int s_in = bd.new_stage();
+      bd.gemv(s_in, prev, l, (uint32_t)u_w, (uint32_t)H, EPI_STORE, true, lw ? wptr(lw->w_qkv_delta) : 0,
+              lw ? wptr(lw->w_gates) : 0, 0, (uint32_t)m.C, (uint32_t)NONE, x_in, (uint32_t)H,
+              lw ? wptr(lw->attn_norm) : 0, ws(Q.qkv), (uint32_t)u_w, 0);
+      const int s_delta = bd.new_stage();
+      const int n_items = d.max_batch * nh * (dv / 32);
+      bd.items(s_delta, s_in, l, OP_DELTA, n_items, (uint32_t)(32 * dk * 4 / SLOT));
+      s_mix = bd.new_stage();
+      bd.gemv(s_mix, s_delta, l, (uint32_t)H, (uint32_t)(nh * dv), EPI_RESID, false, lw ? wptr(lw->wo_delta) : 0, 0,
+              0, (uint32_t)NONE, (uint32_t)NONE, ws(Q.mix_o), (uint32_t)P.mix_dim, 0, ws(Q.x_mix), (uint32_t)H, x_in);
+      ++id;
+    }
+    const int s_gu = bd.new_stage();
+    bd.gemv(s_gu, s_mix, l, (uint32_t)F, (uint32_t)H, EPI_SWIGLU, true, lw ? wptr(lw->w_gate) : 0,
+            lw ? wptr(lw->w_up) : 0, 0, (uint32_t)NONE, (uint32_t)NONE, ws(Q.x_mix), (uint32_t)H,
+            lw ? wptr(lw->mlp_norm) : 0, ws(Q.m), (uint32_t)F, 0);
+    const int s_down = bd.new_stage();
+    bd.gemv(s_down, s_gu, l, (uint32_t)H, (uint32_t)F, EPI_RESID, false, lw ? wptr(lw->w_down) : 0, 0, 0,
+            (uint32_t)NONE, (uint32_t)NONE, ws(Q.m), (uint32_t)F, 0, ws(Q.x_out), (uint32_t)H, ws(Q.x_mix));
+    prev = s_down;
+    x_in = ws(Q.x_out);
+  }
+  const int s_lm = bd.new_stage();
+  const void* lm = w ? (d.tied_embeddings ? w->embed : w->lm_head) : nullptr;
+  bd.gemv(s_lm, prev, L, (uint32_t)d.vocab, (uint32_t)H, EPI_LOGITS, true, wptr(lm), 0, 0, (uint32_t)NONE,
+          (uint32_t)NONE, x_in, (uint32_t)H, w ? wptr(w->final_norm) : 0, 0, (uint32_t)d.vocab, 0);
+  if (!bd.err.empty()) return bd.err;
+
+  // ---------------- distribute ops to queues (op j of a stage -> CU j mod n_cus), in stage order
+  const int S = (int)bd.stage_ops.size();
+  P.stages.resize(S);
+  std::vector<std::vector<Op>> q(n_cus);
+  P.cu_bytes.assign(n_cus, 0.0);
+  for (int s = 0; s < S; ++s) {
+    auto& ops = bd.stage_ops[s];
+    P.stages[s].nops = (uint32_t)ops.size();
+    for (size_t j = 0; j < ops.size(); ++j) {
+      Op o = ops[j];
+      o.sig_index = (uint32_t)j;
+      const int cu = (int)(j % (size_t)n_cus);
+      if (o.opcode == OP_GEMV) {
+        const double bytes = (double)o.nrows * (o.epi == EPI_SWIGLU ? 2 : 1) * o.K * 2;
+        P.cu_bytes[cu] += bytes;
+        P.weight_bytes += bytes;
+      }
+      q[cu].push_back(o);
+    }
+  }
+  P.queue_off.assign(n_cus + 1, 0);
+  for (int c2 = 0; c2 < n_cus; ++c2) {
+    P.queue_off[c2 + 1] = P.queue_off[c2] + (uint32_t)q[c2].size();
+    P.ops.insert(P.ops.end(), q[c2].begin(), q[c2].end());
+  }
+  Y.ops = take(P.ops.size() * sizeof(Op));
+  Y.queue_off = take(P.queue_off.size() * 4);
+  Y.stages = take(P.stages.size() * sizeof(Stage));
+  Y.counters_bytes = (size_t)S * NSUB * CTR_STRIDE * 4;
+  Y.counters = take(Y.counters_bytes);
+  Y.layers = take((size_t)L * sizeof(LayerDesc));
+  Y.total = off;
+  return "";
+}
+
+static uint64_t reloc(uint64_t v, uint64_t base) { return (v & WS_TAG) ? base + (v & ~WS_TAG) : v; }
+
+void relocate(Plan* plan, uint64_t base) {
+  for (Op& o : plan->ops) {
+    o.in = reloc(o.in, base);
+    o.out = reloc(o.out, base);
+    o.res = reloc(o.res, base);
+  }
+  for (LayerDesc& D : plan->layers) {
+    D.qkv = reloc(D.qkv, base);
+    D.gates = reloc(D.gates, base);
+    D.part = reloc(D.part, base);
+    D.tickets = reloc(D.tickets, base);
+    D.mix_o = reloc(D.mix_o, base);
+  }
+}
+
+int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
+  int errors = 0;
+  auto bad = [&](const std::string& s) {
+    if (errors < 20) *why += s + "\n";
+    ++errors;
+  };
+  const int S = (int)P.stages.size();
+  std::vector<uint32_t> seen(S, 0);
+  std::vector<std::vector<uint32_t>> idx(S);
+  for (int c = 0; c < P.n_cus; ++c) {
+    int last = -1;
+    for (uint32_t i = P.queue_off[c]; i < P.queue_off[c + 1]; ++i) {
+      const Op& o = P.ops[i];
+      if (o.sig_stage < 0 || o.sig_stage >= S) { bad(fmt("cu %d op %u: bad signal stage", c, i)); continue; }
+      if (o.sig_stage < last) bad(fmt("cu %d op %u: queue not in stage order", c, i));
+      last = o.sig_stage;
+      if (o.wait_stage != NO_STAGE && o.wait_stage >= o.sig_stage)
+        bad(fmt("cu %d op %u: waits on stage %d, not earlier than its own %d", c, i, o.wait_stage, o.sig_stage));
+      seen[o.sig_stage]++;
+      idx[o.sig_stage].push_back(o.sig_index);
+      if (o.opcode == OP_GEMV) {
+        const int mult = o.epi == EPI_SWIGLU ? 2 : 1;
+        const uint32_t RW = std::min<uint32_t>(o.ppr, 8);
+        if ((uint64_t)o.nrows * mult * RW * P.kernel_batch > (uint64_t)RED_FLOATS)
+          bad(fmt("cu %d op %u: tile exceeds the partial-sum area", c, i));
+        if (o.nslots * SLOT_PIECES < o.nrows * mult * o.ppr) bad(fmt("cu %d op %u: too few slots", c, i));
+        if (o.ppr * PIECE_ELEMS < o.K) bad(fmt("cu %d op %u: pieces do not cover a row", c, i));
+      }
+    }
+  }
+  for (int s = 0; s < S; ++s) {
+    if (seen[s] != P.stages[s].nops) bad(fmt("stage %d: %u ops signal it, table says %u", s, seen[s], P.stages[s].nops));
+    std::vector<uint32_t> v = idx[s];
+    std::sort(v.begin(), v.end());
+    for (size_t j = 0; j < v.size(); ++j)
+      if (v[j] != j) { bad(fmt("stage %d: signal indices are not 0..n-1", s)); break; }
+  }
+  // every GEMV stage covers its rows exactly once
+  std::vector<std::vector<std::pair<uint32_t, uint32_t>>> rows(S);
+  for (const Op& o : P.ops)
+    if (o.opcode == OP_GEMV) rows[o.sig_stage].push_back({o.row0, o.row0 + o.nrows});
+  for (int s = 0; s < S; ++s) {
+    auto& r = rows[s];
+    if (r.empty()) continue;
+    std::sort(r.begin(), r.end());
+    if (r[0].first != 0) bad(fmt("stage %d: rows do not start at 0", s));
+    for (size_t j = 1; j < r.size(); ++j)
+      if (r[j].first != r[j - 1].second) bad(fmt("stage %d: row gap or overlap at %u", s, r[j].first));
+  }
+  // streamed weight bytes == the model's projection bytes
+  const mk_model_desc& d = m.d;
+  double want = (double)d.vocab * d.hidden * 2;
+  for (int l = 0; l < d.n_layers; ++l) {
+    want += 3.0 * d.ffn * d.hidden * 2;
+    if (m.kinds[l] == MK_LAYER_ATTN)
+      want += 2.0 * d.hidden * d.head_dim * (d.n_q_heads + d.n_kv_heads) * 2;
+    else
+      want += ((double)m.C + 2.0 * d.n_delta_heads + (double)d.n_delta_heads * d.delta_dv) * d.hidden * 2;
+  }
+  if (std::fabs(want - P.weight_bytes) > 0.5) bad(fmt("streamed %.0f weight bytes, model has %.0f", P.weight_bytes, want));
+  return errors;
+}
+
+}  // namespace mk

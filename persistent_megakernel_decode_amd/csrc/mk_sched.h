@@ -1,0 +1,62 @@
+// mk_sched.h -- host-side scheduler: compiles a model description into
+// per-compute-unit Op queues, dependency stages and a workspace layout.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_internal.h"
+
+namespace mk {
+
+// Byte offsets of every workspace section (all 256-byte aligned).
+struct Layout {
+  size_t ops = 0, queue_off = 0, stages = 0, counters = 0, layers = 0, rope = 0, status = 0, row_ok = 0, x0 = 0;
+  struct PerLayer {
+    size_t qkv = 0, part = 0, tickets = 0, mix_o = 0, x_mix = 0, m = 0, x_out = 0;
+  };
+  std::vector<PerLayer> layer;
+  size_t counters_bytes = 0, tickets_bytes_per_layer = 0;
+  size_t total = 0;
+};
+
+struct Plan {
+  int n_cus = 0;
+  int kernel_batch = 1;          // compiled batch width of the kernel variant
+  int n_items = 0;               // attention items per attention layer
+  int mix_dim = 0;
+  std::vector<Op> ops;           // all queues concatenated (device pointers are offsets until relocated)
+  std::vector<uint32_t> queue_off;
+  std::vector<Stage> stages;
+  std::vector<LayerDesc> layers;
+  Layout lay;
+  double weight_bytes = 0;
+  std::vector<double> cu_bytes;  // streamed weight bytes per CU
+};
+
+// Validated copy of the caller's description.
+struct ModelShape {
+  mk_model_desc d{};
+  std::vector<int32_t> kinds;
+  int n_attn = 0, n_delta = 0, G = 1, C = 0;
+};
+
+// Returns "" on success, else a message.  `status` receives the mk_status code.
+std::string validate_desc(const mk_model_desc* desc, ModelShape* out, mk_status* status);
+
+// Builds the plan with device pointers expressed relative to:
+//   workspace base (bit 62 tag) -- relocated by relocate(); weights / cache pointers are taken
+//   verbatim from `w` / `c` when given (NULL = leave zero, for host-only planning).
+std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, const mk_kv_cache* c, Plan* plan);
+
+// Rewrites workspace-relative addresses in the plan into absolute device addresses.
+void relocate(Plan* plan, uint64_t workspace_base);
+
+// Structural checks (stage order, coverage, capacities).  Returns the number of violations and
+// appends their descriptions to `why`.
+int check_plan(const ModelShape& m, const Plan& plan, std::string* why);
+
+}  // namespace mk

@@ -298,3 +298,12 @@ SMALL: Dict[str, Config] = {
                           vocab=512, layer_kinds=hybrid_kinds(4), n_delta_heads=2, delta_dk=32, delta_dv=32,
                           conv_width=4, batch=2, ctx=[16, 16], steps=4, seed=5, gain_range=(0.5, 1.5)),
 }
+
+
+def shape_of(cfg: Config, max_ctx: int) -> dict:
+    """Model-description fields for the megakernel's C ABI (include/mk.h, mk_model_desc)."""
+    return dict(n_layers=cfg.n_layers, hidden=cfg.hidden, vocab=cfg.vocab, ffn=cfg.ffn, n_q_heads=cfg.n_q_heads,
+                n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, qk_norm=cfg.qk_norm, tied=cfg.tied,
+                rms_eps=cfg.rms_eps, rope_base=cfg.rope_base, layer_kinds=cfg.kinds(), max_batch=cfg.batch,
+                max_ctx=max_ctx, n_delta_heads=cfg.n_delta_heads, delta_dk=cfg.delta_dk, delta_dv=cfg.delta_dv,
+                conv_width=cfg.conv_width, page_size=cfg.page_size)
