@@ -155,7 +155,10 @@ typedef enum {
   MK_MID_X_MIXER = 0, /* fp32 [batch][hidden] residual after layer l's attention / delta sub-layer */
   MK_MID_X_MLP = 1,   /* fp32 [batch][hidden] residual after layer l's MLP */
   MK_MID_MIXER_O = 2, /* fp32 [batch][Hq*d or heads*dv] attention / delta output before o_proj */
-  MK_MID_MLP_M = 3    /* fp32 [batch][ffn] silu(gate) * up */
+  MK_MID_MLP_M = 3,   /* fp32 [batch][ffn] silu(gate) * up */
+  MK_MID_PROJ = 4,    /* fp32 [batch][(Hq+2Hkv)*d] raw q|k|v of an attention layer (before norm / RoPE),
+                         or [batch][C + 2*heads] in_proj|gates of a delta layer (before the conv) */
+  MK_MID_EMBED = 5    /* fp32 [batch][hidden] embedding rows (layer ignored) */
 } mk_midstate;
 
 /* Copy mid-state `kind` of `layer` from the last step into dst (device memory,

@@ -20,7 +20,7 @@ MK_ABI_VERSION = 1
 MK_OK, MK_ERR_INVALID_ARG, MK_ERR_UNSUPPORTED, MK_ERR_HIP, MK_ERR_DEVICE_INPUT, MK_ERR_TIMEOUT, MK_ERR_STATE = \
     0, -1, -2, -3, -4, -5, -6
 MK_LAYER_ATTN, MK_LAYER_DELTA = 0, 1
-MK_MID_X_MIXER, MK_MID_X_MLP, MK_MID_MIXER_O, MK_MID_MLP_M = 0, 1, 2, 3
+MK_MID_X_MIXER, MK_MID_X_MLP, MK_MID_MIXER_O, MK_MID_MLP_M, MK_MID_PROJ, MK_MID_EMBED = 0, 1, 2, 3, 4, 5
 
 STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID_ARG", -2: "MK_ERR_UNSUPPORTED", -3: "MK_ERR_HIP",
                 -4: "MK_ERR_DEVICE_INPUT", -5: "MK_ERR_TIMEOUT", -6: "MK_ERR_STATE"}

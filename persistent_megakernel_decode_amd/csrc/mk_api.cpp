@@ -347,6 +347,12 @@ mk_status mk_copy_midstate(mk_ctx* ctx, int32_t kind, int32_t layer, float* dst,
     case MK_MID_X_MLP: off = Q.x_out; width = d.hidden; break;
     case MK_MID_MIXER_O: off = Q.mix_o; width = ctx->plan.mix_dim; break;
     case MK_MID_MLP_M: off = Q.m; width = d.ffn; break;
+    case MK_MID_PROJ:
+      off = Q.qkv;
+      width = ctx->shape.kinds[layer] == MK_LAYER_ATTN ? (size_t)(d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim
+                                                       : (size_t)ctx->shape.C + 2 * d.n_delta_heads;
+      break;
+    case MK_MID_EMBED: off = ctx->plan.lay.x0; width = d.hidden; break;
     default: return fail(MK_ERR_INVALID_ARG, "unknown mid-state kind");
   }
   if (count > (size_t)d.max_batch * width) return fail(MK_ERR_INVALID_ARG, "count exceeds max_batch * width");

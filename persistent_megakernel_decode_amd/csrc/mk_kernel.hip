@@ -69,25 +69,22 @@ __device__ __forceinline__ T sload(const T* p) {
   return out;
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7FFFFFFF, 0x00020000);
-}
-
-// agent-coherent fp32 accesses for data that crosses compute units
+// Agent-coherent accesses for data that crosses compute units: relaxed agent-scope atomics,
+// i.e. global loads / stores with the sc1 cache-policy bit, with per-lane addresses.
 __device__ __forceinline__ float ld_sc1(const float* p) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(p), 0, 0, AUX_SC1));
+  return __builtin_bit_cast(float, __hip_atomic_load((const u32*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 __device__ __forceinline__ void st_sc1(float* p, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(u32, v), rsrc(p), 0, 0, AUX_SC1);
+  __hip_atomic_store((u32*)p, __builtin_bit_cast(u32, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void ld8_sc1(const float* p, float* out) {  // 8 consecutive floats, 16-B aligned
-  __amdgpu_buffer_rsrc_t r = rsrc(p);
-  u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, AUX_SC1);
-  u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, 16, 0, AUX_SC1);
-  out[0] = __builtin_bit_cast(float, a.x); out[1] = __builtin_bit_cast(float, a.y);
-  out[2] = __builtin_bit_cast(float, a.z); out[3] = __builtin_bit_cast(float, a.w);
-  out[4] = __builtin_bit_cast(float, b.x); out[5] = __builtin_bit_cast(float, b.y);
-  out[6] = __builtin_bit_cast(float, b.z); out[7] = __builtin_bit_cast(float, b.w);
+__device__ __forceinline__ void ld8_sc1(const float* p, float* out) {  // 8 consecutive floats, 8-B aligned
+  const uint64_t* q = (const uint64_t*)p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t v = __hip_atomic_load(q + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    out[2 * i] = __builtin_bit_cast(float, (u32)v);
+    out[2 * i + 1] = __builtin_bit_cast(float, (u32)(v >> 32));
+  }
 }
 __device__ __forceinline__ u32 ld_u32_sc1(const u32* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -47,7 +47,7 @@ class ParityReport:
     failures: List[str] = field(default_factory=list)
 
 
-def make_pair(cfg: synth.Config, steps: int, device: str = "cuda:0", extra_ctx: int = 16):
+def make_pair(cfg: synth.Config, steps: int, device: str = "cuda:0"):
     import persistent_megakernel_decode_amd as mkd
     ctx0 = synth.context_lengths(cfg)
     t0 = time.time()
@@ -55,7 +55,7 @@ def make_pair(cfg: synth.Config, steps: int, device: str = "cuda:0", extra_ctx: 
     cache = synth.make_cache(cfg, ctx0, steps)
     say(f"[{cfg.name}] inputs generated in {time.time() - t0:.1f}s (batch {cfg.batch}, ctx {ctx0})")
     orc = oracle.DecodeOracle(cfg, w, cache)
-    max_ctx = max(ctx0) + steps + extra_ctx
+    max_ctx = int(cache["max_pages_per_seq"]) * cfg.page_size  # what the mapped pages can hold
     gpu = mkd.DecodeContext(synth.shape_of(cfg, max_ctx), w, cache, device)
     say(f"[{cfg.name}] device model ready ({gpu.ws_bytes / 2**20:.1f} MiB workspace)")
     return w, cache, orc, gpu, ctx0

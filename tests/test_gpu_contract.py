@@ -14,7 +14,8 @@ def _ctx(cfg, steps=4):
     ctx0 = synth.context_lengths(cfg)
     w = synth.make_weights(cfg)
     cache = synth.make_cache(cfg, ctx0, steps)
-    return mkd.DecodeContext(synth.shape_of(cfg, max(ctx0) + steps + 16), w, cache), ctx0, cache
+    max_ctx = int(cache["max_pages_per_seq"]) * cfg.page_size
+    return mkd.DecodeContext(synth.shape_of(cfg, max_ctx), w, cache), ctx0, cache
 
 
 def test_host_rejects_bad_calls():
