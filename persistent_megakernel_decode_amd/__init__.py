@@ -170,18 +170,36 @@ class DecodeContext:
     documents; they are copied to `device` once.  Only memory and the stream come from PyTorch.
     """
 
-    def __init__(self, shape: dict, weights: dict, cache: dict, device: str = "cuda:0"):
+    ARENA_ALIGN = 2 << 20  # weights sit 2 MiB-aligned in one arena allocation
+
+    def __init__(self, shape: dict, weights: dict, cache: dict, device: str = "cuda:0", arena: bool = True):
+        import numpy as np
         import torch
         self.torch = torch
         self.device = torch.device(device)
         self.shape = dict(shape)
-        t = lambda a, dt=None: torch.from_numpy(a).to(self.device) if dt is None else torch.from_numpy(a).view(dt).to(self.device)
         i16 = torch.int16
         self.tensors: Dict[str, "torch.Tensor"] = {}
         keep: List = self.tensors.setdefault("_all", [])
+        self.arena = None
+        if arena:  # one allocation for every weight tensor (bf16 bit patterns)
+            arrays = [weights["embed"], weights["final_norm"]] + ([] if shape["tied"] else [weights["lm_head"]])
+            for L in weights["layers"]:
+                arrays += [L[f] for f in LAYER_FIELDS if f in L]
+            A = self.ARENA_ALIGN
+            total = sum((a.nbytes + A - 1) // A * A for a in arrays) + A
+            self.arena = torch.empty(total, dtype=torch.uint8, device=self.device)
+            self._arena_off = (-self.arena.data_ptr()) % A
 
         def dev(a, dt=None):
-            x = t(a, dt)
+            if self.arena is not None and dt is i16:
+                n = a.nbytes
+                view = self.arena[self._arena_off:self._arena_off + n]
+                self._arena_off += (n + self.ARENA_ALIGN - 1) // self.ARENA_ALIGN * self.ARENA_ALIGN
+                view.copy_(torch.from_numpy(np.ascontiguousarray(a).reshape(-1).view(np.uint8)))
+                x = view.view(torch.int16)
+            else:
+                x = torch.from_numpy(a).to(self.device) if dt is None else torch.from_numpy(a).view(dt).to(self.device)
             keep.append(x)
             return x
 
@@ -199,8 +217,9 @@ class DecodeContext:
                 if f in L:
                     setattr(self.layers[l], f, dev(L[f], i16).data_ptr())
         self.w = mk_weights(self.embed.data_ptr(), final_norm.data_ptr(), lm.data_ptr(), ctypes.cast(self.layers, P))
-        self.k_pages = dev(cache["k_pages"], i16)
-        self.v_pages = dev(cache["v_pages"], i16)
+        self.k_pages = torch.from_numpy(cache["k_pages"]).view(i16).to(self.device)
+        self.v_pages = torch.from_numpy(cache["v_pages"]).view(i16).to(self.device)
+        keep += [self.k_pages, self.v_pages]
         self.page_table = dev(cache["page_table"])
         self.delta_state = dev(cache["delta_state"]) if "delta_state" in cache else None
         self.conv_state = dev(cache["conv_state"]) if "conv_state" in cache else None

@@ -37,6 +37,7 @@ constexpr int CTR_STRIDE = 32;         // u32 between sub-counters (128 B, one c
 // ---- GEMV geometry ----
 constexpr int PIECE_ELEMS = PIECE / 2; // bf16 weights per piece row-segment
 constexpr int MAX_M = 4;               // pieces of one row per compute wave (rows up to 16384 elements)
+constexpr int GEMV_BATCH = 4;          // ring slots a compute wave takes per wait
 
 enum Opcode : uint8_t { OP_NOP = 0, OP_EMBED = 1, OP_GEMV = 2, OP_ATTN = 3, OP_DELTA = 4 };
 enum Epi : uint8_t { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
@@ -46,10 +47,11 @@ constexpr int16_t NO_STAGE = -1;
 // One queue entry (128 bytes).  Pointers are device addresses.
 //
 // A GEMV op computes output rows [row0, row0 + nrows) of a row space that may
-// be the concatenation of up to three weight tensors: global row r comes from
-// W (r < b1), W2 (b1 <= r < b2) or W3 (r >= b2), each indexed from its own
-// first row.  EPI_SWIGLU streams the gate rows of W, then the same rows of W2
-// (up), and writes silu(gate) * up.
+// be the concatenation of several weight tensors (q | k | v, or in_proj |
+// gates).  Its weight stream is at most two contiguous row runs: stream rows
+// [0, b1) start at W (already offset to the op's first row) and stream rows
+// [b1, ...) start at W2.  EPI_SWIGLU streams the op's gate rows (W) then the
+// same rows of the up projection (W2, b1 = nrows) and writes silu(gate) * up.
 struct alignas(16) Op {
   uint8_t opcode;
   uint8_t epi;
@@ -62,12 +64,14 @@ struct alignas(16) Op {
   uint32_t row0;       // GEMV: first output row;  ATTN / DELTA: item index
   uint32_t nrows;      // GEMV: output rows
   uint32_t K;          // GEMV: input length
-  uint32_t ppr;        // GEMV: pieces per row (padded to 1, 2, 4 or a multiple of 8)
+  uint32_t ppr;        // GEMV: pieces per row, padded to a power of two (1 .. 32)
   uint32_t nslots;     // GEMV / DELTA: ring slots the op consumes (ATTN: computed at run time)
   uint32_t ld_in;      // floats between batch rows of `in`
   uint32_t ld_out;     // floats between batch rows of `out` / `res`
-  uint32_t b1, b2;     // GEMV: row-space boundaries between W, W2 and W3
-  uint64_t W, W2, W3;  // GEMV weights, bf16 [rows][K]
+  uint32_t b1;         // GEMV: stream rows taken from W before switching to W2
+  uint32_t pad1;
+  uint64_t W, W2;      // GEMV weight runs, bf16 rows of K
+  uint64_t pad3;
   uint64_t in;         // fp32 [batch][ld_in]
   uint64_t gamma;      // bf16 [K] norm gain (norm == 1)
   uint64_t out;        // fp32 [batch][ld_out] (EPI_LOGITS writes the launch's logits instead)

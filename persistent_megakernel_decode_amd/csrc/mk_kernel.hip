@@ -104,11 +104,50 @@ __device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even (f
 
 __device__ __forceinline__ u32 lane_id() { return threadIdx.x & 63u; }
 
-__device__ __forceinline__ float wave_sum(float v) {  // full-wave sum, result in every lane
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
+// Full-wave sum, returned in every lane: four DPP steps give every lane its 16-lane row sum
+// (quad xor 1, quad xor 2, half-row mirror, row mirror), then the four row sums are read out.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dppf<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dppf<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dppf<0x141>(v);  // row_half_mirror
+  v += dppf<0x140>(v);  // row_mirror
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+// Sums of four values over the whole wave at once: after the call, lane q (q < 4) holds the
+// 64-lane sum of v[q].  Butterfly over the quad (xor 1, xor 2) so each lane keeps one value
+// index (lane & 3), rotate-add within each 16-lane row, then pair rows with the lane-32 and
+// lane-16 swaps.  Fixed order, so bitwise reproducible.
+// c + (c of the lane 32 away), and c + (c of the row 16 lanes away).  Written as the swap
+// instruction itself: the compiler's builtin for it folds the two results of a float sum into one.
+// The s_nop covers the wait states the swap needs after a VALU write of its operands.
+__device__ __forceinline__ float add_swap32(float c) {
+  float x = c, y = c;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+  return x + y;
+}
+__device__ __forceinline__ float add_swap16(float c) {
+  float x = c, y = c;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+  return x + y;
+}
+__device__ __forceinline__ float reduce4(float v0, float v1, float v2, float v3) {
+  const bool b0 = (threadIdx.x & 1u) != 0, b1 = (threadIdx.x & 2u) != 0;
+  const float a = (b0 ? v1 : v0) + dppf<0xB1>(b0 ? v0 : v1);   // pair sums of v[lane & 1]
+  const float b = (b0 ? v3 : v2) + dppf<0xB1>(b0 ? v2 : v3);   // pair sums of v[2 + (lane & 1)]
+  float c = (b1 ? b : a) + dppf<0x4E>(b1 ? a : b);             // quad sums of v[lane & 3]
+  c += dppf<0x124>(c);                                          // row_ror:4
+  c += dppf<0x128>(c);                                          // row_ror:8
+  return add_swap16(add_swap32(c));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -139,12 +178,18 @@ __device__ void raise_status(const KArgs& A, u32 bits) {
 
 // Every spin in the kernel is bounded: past the watchdog limit the waiting wave raises
 // ST_TIMEOUT and sets the workgroup abort flag, and every wave of the workgroup leaves.
+// The clock is read only once a wait has actually spun, and then every 64 polls: the fast path
+// (condition already true) costs nothing.
 struct Watchdog {
   uint64_t t0, limit;
   u32* status;
-  __device__ explicit Watchdog(const KArgs& A) : t0(__builtin_amdgcn_s_memrealtime()), limit(A.spin_limit), status(A.status) {}
+  u32 polls;
+  __device__ explicit Watchdog(const KArgs& A) : t0(0), limit(A.spin_limit), status(A.status), polls(0) {}
   __device__ bool expired() {
-    if (__builtin_amdgcn_s_memrealtime() - t0 <= limit) return false;
+    if ((polls++ & 63u) != 0) return false;
+    const uint64_t now = __builtin_amdgcn_s_memrealtime();
+    if (t0 == 0) { t0 = now; return false; }
+    if (now - t0 <= limit) return false;
     if (lane_id() == 0) {
       __hip_atomic_fetch_or(status, ST_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&g_abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -229,9 +274,6 @@ __device__ AttnItem attn_item(const KArgs& A, u32 item, int pps) {
 __device__ __forceinline__ int attn_pps(int d) { return 4096 / (2 * d); }  // positions per ring slot
 
 // ------------------------------------------------------------------ loader
-__device__ __forceinline__ void dma16(const void* g, u32x4* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, AUX_NT);
-}
 
 // Publish "slot `seq` holds its bytes" (after the matching s_waitcnt vmcnt).  Written as an opaque
 // LDS store for the same reason as lds_ld_loader: the compiler would otherwise drain every DMA first.
@@ -253,69 +295,119 @@ __device__ __forceinline__ void wait_oldest(u32 n) {
 }
 static_assert(LOAD_DEPTH == 4, "wait_oldest covers LOAD_DEPTH + 1 in-flight slots");
 
-// GEMV stream: piece p of the op = (stream row p / ppr, row piece p % ppr).
-__device__ void issue_gemv(const Op& o, u32 s, u32x4* dst) {
-  const u32 lane = lane_id();
-  const u32 nrt = o.epi == EPI_SWIGLU ? 2 * o.nrows : o.nrows;
-  const u32 K = o.K;
-  const uint16_t* W0 = (const uint16_t*)o.W;
+// Every loader address is a uniform (scalar) base plus the lane's fixed 16-byte offset, so a
+// DMA costs only scalar work: no per-lane address arithmetic on the issue path.
+__device__ __forceinline__ void dma_at(const char* base, u32 lane_off, u32x4* lds) {
+  __builtin_amdgcn_global_load_lds(base + lane_off, (__attribute__((address_space(3))) void*)lds, 16, 0, AUX_NT);
+}
+
+// GEMV stream: the op's rows in order, each row as ppr (a power of two) pieces of 1 KB.  Slot s
+// holds pieces 8s .. 8s+7.  A piece past the row's end or a row past the op is a dummy that
+// re-reads the first 1 KB of W (an L2 hit) and is never used; a piece that straddles the row's
+// end reads, in its lanes past the end, the row's first bytes instead.
+__device__ __forceinline__ uint64_t uni64(uint64_t v) {  // value held in scalar registers
+  const u32 lo = __builtin_amdgcn_readfirstlane((u32)v), hi = __builtin_amdgcn_readfirstlane((u32)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// The GEMV stream's two row runs, as scalar values.
+struct GemvSeg {
+  uint64_t wa, wb;
+  u32 na, rowbytes;
+};
+__device__ __forceinline__ GemvSeg gemv_seg(const Op& o) {
+  GemvSeg g;
+  g.wa = uni64(o.W);
+  g.wb = uni64(o.W2);
+  g.na = __builtin_amdgcn_readfirstlane(o.b1);
+  g.rowbytes = __builtin_amdgcn_readfirstlane(o.K * 2);
+  return g;
+}
+__device__ __forceinline__ const char* gemv_row(const GemvSeg& g, u32 rl) {
+  const bool a = rl < g.na;
+  const uint64_t base = a ? g.wa : g.wb;
+  const u32 r = a ? rl : rl - g.na;
+  return (const char*)(base + (uint64_t)r * g.rowbytes);
+}
+
+// One ring slot of the GEMV stream.  With ppr >= 8 a slot is 8 consecutive pieces of one row
+// (one row lookup per slot); with ppr < 8 it is 8 / ppr whole rows.
+__device__ void issue_gemv(const GemvSeg& gsg, u32 s, u32 nrt, u32 lgp, u32 real_pieces, u32 lane16, u32x4* dst) {
+  const u32 rowbytes = gsg.rowbytes;
+  const char* dummy = (const char*)gsg.wa;
+  if (lgp >= 3) {
+    const u32 lgm = lgp - 3;
+    const u32 rl = s >> lgm, kp0 = (s & ((1u << lgm) - 1)) << 3;
+    if (rl >= nrt) {
+#pragma unroll
+      for (int i = 0; i < SLOT_PIECES; ++i) dma_at(dummy, lane16, dst + i * 64);
+      return;
+    }
+    const char* row = gemv_row(gsg, rl) + kp0 * PIECE;
+    const u32 nreal = real_pieces > kp0 ? real_pieces - kp0 : 0u;  // full pieces: rowbytes % 1 KB == 0 here
+#pragma unroll
+    for (int i = 0; i < SLOT_PIECES; ++i) {
+      if ((u32)i < nreal) dma_at(row + i * PIECE, lane16, dst + i * 64);
+      else dma_at(dummy, lane16, dst + i * 64);
+    }
+    return;
+  }
+  const u32 ppr = 1u << lgp;
 #pragma unroll
   for (int i = 0; i < SLOT_PIECES; ++i) {
     const u32 p = s * SLOT_PIECES + i;
-    const u32 rl = p / o.ppr, kp = p - rl * o.ppr;
-    const uint16_t* rowp = W0;  // dummy piece (past the op's rows): row 0 of W, always mapped
-    u32 e = (lane * 8) % K;
-    if (rl < nrt && kp * PIECE_ELEMS < K) {
-      const uint16_t* Wt;
-      u32 r;
-      if (o.epi == EPI_SWIGLU) {
-        const bool up = rl >= o.nrows;
-        Wt = up ? (const uint16_t*)o.W2 : W0;
-        r = o.row0 + (up ? rl - o.nrows : rl);
-      } else {
-        const u32 g = o.row0 + rl;
-        if (g < o.b1) { Wt = W0; r = g; }
-        else if (g < o.b2) { Wt = (const uint16_t*)o.W2; r = g - o.b1; }
-        else { Wt = (const uint16_t*)o.W3; r = g - o.b2; }
-      }
-      rowp = Wt + (size_t)r * K;
-      const u32 ee = kp * PIECE_ELEMS + lane * 8;
-      e = ee < K ? ee : e;
+    const u32 rl = p >> lgp, kp = p & (ppr - 1);
+    const u32 off = kp * PIECE;
+    if (rl < nrt && off < rowbytes) {
+      const char* row = gemv_row(gsg, rl);
+      if (off + PIECE <= rowbytes) dma_at(row + off, lane16, dst + i * 64);
+      else dma_at(row, off + lane16 < rowbytes ? off + lane16 : 0u, dst + i * 64);
+    } else {
+      dma_at(dummy, lane16, dst + i * 64);
     }
-    dma16(rowp + e, dst + i * 64);
   }
 }
 
 // Attention stream: slot s = PPS positions of K (pieces 0-3) then the same positions of V (4-7).
-__device__ void issue_attn(const KArgs& A, const LayerDesc& Ld, const AttnItem& it, u32 s, u32x4* dst) {
-  const u32 lane = lane_id();
-  const int d = A.d, pps = attn_pps(d), ppp = pps / 4;  // positions per piece
-  const size_t page_elems = (size_t)A.Hkv * A.page_size * d;
+// A piece covers 1 KB of one page; one page-table lookup per page.
+__device__ void issue_attn(const KArgs& A, const LayerDesc& Ld, const AttnItem& it, u32 s, u32 lane16, u32x4* dst) {
+  const u32 d = (u32)A.d, pps = 4096u / (2u * d), ppp = pps / 4;  // positions per slot / per piece
+  const size_t page_bytes = (size_t)A.Hkv * A.page_size * d * 2;
+  const size_t head_off = (size_t)it.kvh * A.page_size * d * 2;
+  const u32 pbase = (u32)it.p0 + s * pps;
+  const char* kb = (const char*)Ld.k_pages;
+  const char* vb = (const char*)Ld.v_pages;
+  u32 cur = 0xFFFFFFFFu;
+  size_t pg_off = 0;
 #pragma unroll
-  for (int i = 0; i < SLOT_PIECES; ++i) {
-    const uint16_t* base = (const uint16_t*)(i < 4 ? Ld.k_pages : Ld.v_pages);
-    const int pp = it.p0 + (int)s * pps + (i & 3) * ppp;
-    const uint16_t* src = base + lane * 8;  // dummy: page 0
-    if (pp < it.p1) {
-      int pi = pp / A.page_size;
-      pi = pi < A.max_pages_per_seq ? pi : 0;
-      int pg = sload(A.page_table + (size_t)it.b * A.max_pages_per_seq + pi);
-      pg = (pg >= 0 && pg < A.num_pages) ? pg : 0;
-      src = base + (size_t)pg * page_elems + ((size_t)it.kvh * A.page_size + (pp % A.page_size)) * d + lane * 8;
+  for (int j = 0; j < 4; ++j) {
+    const u32 pos = pbase + j * ppp;
+    if (pos < (u32)it.p1) {
+      const u32 pi = pos >> 4;  // page_size == 16
+      if (pi != cur) {
+        cur = pi;
+        int pg = pi < (u32)A.max_pages_per_seq ? sload(A.page_table + (size_t)it.b * A.max_pages_per_seq + pi) : 0;
+        pg = (pg >= 0 && pg < A.num_pages) ? pg : 0;
+        pg_off = (size_t)pg * page_bytes + head_off + (size_t)(pos & 15u) * d * 2;
+      } else {
+        pg_off += (size_t)ppp * d * 2;
+      }
+      dma_at(kb + pg_off, lane16, dst + j * 64);
+      dma_at(vb + pg_off, lane16, dst + (4 + j) * 64);
+    } else {
+      dma_at(kb, lane16, dst + j * 64);
+      dma_at(vb, lane16, dst + (4 + j) * 64);
     }
-    dma16(src, dst + i * 64);
   }
 }
 
 // Delta stream: rows of S^T (fp32) of one column block, contiguous.
-__device__ void issue_delta(const KArgs& A, const LayerDesc& Ld, u32 item, u32 s, u32x4* dst) {
-  const u32 lane = lane_id();
+__device__ void issue_delta(const KArgs& A, const LayerDesc& Ld, u32 item, u32 s, u32 lane16, u32x4* dst) {
   const u32 ncb = (u32)A.dv / 32, cb = item % ncb, bh = item / ncb;  // bh = b * nh + h
   const u32 rps = SLOT / (A.dk * 4);
-  const char* src = (const char*)Ld.delta_state +
-                    (((size_t)bh * A.dv + cb * 32 + s * rps) * A.dk) * 4;
+  const char* src = (const char*)Ld.delta_state + (((size_t)bh * A.dv + cb * 32 + s * rps) * A.dk) * 4;
 #pragma unroll
-  for (int i = 0; i < SLOT_PIECES; ++i) dma16(src + i * PIECE + lane * 16, dst + i * 64);
+  for (int i = 0; i < SLOT_PIECES; ++i) dma_at(src + i * PIECE, lane16, dst + i * 64);
 }
 
 __device__ u32 op_slots(const KArgs& A, const Op& o) {
@@ -329,12 +421,17 @@ __device__ u32 op_slots(const KArgs& A, const Op& o) {
 
 __device__ void loader(const KArgs& A, u32 q0, u32 q1) {
   u32 seq = 0, marked = 0;
+  const u32 lane16 = lane_id() * 16;
   for (u32 oi = q0; oi < q1; ++oi) {
     const Op o = sload(A.ops + oi);
     const u32 ns = op_slots(A, o);
     if (ns == 0) continue;
     LayerDesc Ld{};
     AttnItem it{};
+    const u32 nrt = o.epi == EPI_SWIGLU ? 2 * o.nrows : o.nrows;
+    const u32 lgp = o.opcode == OP_GEMV ? (u32)__builtin_ctz(o.ppr) : 0u;
+    const u32 real_pieces = (o.K + PIECE_ELEMS - 1) / PIECE_ELEMS;
+    const GemvSeg gsg = gemv_seg(o);
     if (o.opcode == OP_ATTN || o.opcode == OP_DELTA) Ld = sload(A.layers + o.layer);
     if (o.opcode == OP_ATTN) it = attn_item(A, o.row0, attn_pps(A.d));
     for (u32 s = 0; s < ns; ++s) {
@@ -353,9 +450,9 @@ __device__ void loader(const KArgs& A, u32 q0, u32 q1) {
         }
       }
       u32x4* dst = g_ring + pos * (SLOT / 16);
-      if (o.opcode == OP_GEMV) issue_gemv(o, s, dst);
-      else if (o.opcode == OP_ATTN) issue_attn(A, Ld, it, s, dst);
-      else issue_delta(A, Ld, o.row0, s, dst);
+      if (o.opcode == OP_GEMV) issue_gemv(gsg, s, nrt, lgp, real_pieces, lane16, dst);
+      else if (o.opcode == OP_ATTN) issue_attn(A, Ld, it, s, lane16, dst);
+      else issue_delta(A, Ld, o.row0, s, lane16, dst);
       ++seq;
       if (seq - marked > LOAD_DEPTH) {
         __builtin_amdgcn_s_waitcnt(MK_VMCNT(8 * LOAD_DEPTH));
@@ -504,40 +601,115 @@ __device__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) 
     }
   }
 
-  // stream the tile: wave w takes piece w of every slot
-  float acc[B];
+  // stream the tile: wave w takes piece w of every slot, GEMV_BATCH slots at a time.
+  // Each slot gets its own partial sum; the batch then folds them by row shape:
+  //   ppr <= 8  (lgm 0): every slot ends one row of this wave -> four rows per reduction;
+  //   ppr == 16 (lgm 1): slot pairs form rows                  -> two rows per reduction;
+  //   ppr >= 32 (lgm 2+): a row spans whole batches           -> running sum, reduced at row end.
+  // With four or more sequences the four values folded together are the sequences of one row.
+  static_assert(GEMV_BATCH == 4, "the batched reduction folds four slots");
+  const u32 lgp = (u32)__builtin_ctz(ppr);  // ppr is a power of two
+  const u32 lgm = ppr >= 8 ? lgp - 3 : 0;   // log2(slots per row)
+  const u32 mmask = (1u << lgm) - 1;
+  float racc[B];
+  for (u32 s0 = 0; s0 < o.nslots; s0 += GEMV_BATCH) {
+    const u32 nb = min((u32)GEMV_BATCH, o.nslots - s0);
+    if (!wait_full(A, seq + nb - 1)) return false;  // slots are published in order
+    u32x4 wv[GEMV_BATCH];
 #pragma unroll
-  for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-  for (u32 s = 0; s < o.nslots; ++s, ++seq) {
-    if (!wait_full(A, seq)) return false;
-    const u32 p = s * SLOT_PIECES + w;
-    const u32 rl = p / ppr, kp = p - rl * ppr;
-    const u32 t = ppr >= 8 ? kp / 8 : 0;
-    if (rl < nrt && kp * PIECE_ELEMS < K && kp * PIECE_ELEMS + lane * 8 < K) {
-      const u32x4 wv = g_ring[(seq % NSLOT) * (SLOT / 16) + w * 64 + lane];
-      const float wf[8] = {bflo(wv.x), bfhi(wv.x), bflo(wv.y), bfhi(wv.y),
-                           bflo(wv.z), bfhi(wv.z), bflo(wv.w), bfhi(wv.w)};
+    for (int i = 0; i < GEMV_BATCH; ++i)
+      if ((u32)i < nb) wv[i] = g_ring[((seq + i) % NSLOT) * (SLOT / 16) + w * 64 + lane];
+    __builtin_amdgcn_s_waitcnt(MK_LGKMCNT0);
+    if (lane == 0)
+      for (u32 i = 0; i < nb; ++i)
+        __hip_atomic_fetch_add(&g_done[(seq + i) % NSLOT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if constexpr (B >= 4) {
+      // wide batches: one running sum per sequence, reduced four sequences at a time at each row end
 #pragma unroll
-      for (int tt = 0; tt < MM; ++tt) {
-        if ((u32)tt == t) {
+      for (int i = 0; i < GEMV_BATCH; ++i) {
+        if ((u32)i < nb) {
+          const u32 s = s0 + i, t = s & mmask;
+          if (t == 0) {
 #pragma unroll
-          for (int b = 0; b < B; ++b)
+            for (int b = 0; b < B; ++b) racc[b] = 0.0f;
+          }
+          const u32x4 q = wv[i];
+          const float wf[8] = {bflo(q.x), bfhi(q.x), bflo(q.y), bfhi(q.y), bflo(q.z), bfhi(q.z), bflo(q.w), bfhi(q.w)};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[b] += wf[e] * xf[tt][b][e];
+          for (int tt = 0; tt < MM; ++tt) {
+            if ((u32)tt == t) {
+#pragma unroll
+              for (int b = 0; b < B; ++b)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) racc[b] += wf[e] * xf[tt][b][e];
+            }
+          }
+          if (t == mmask) {
+            const u32 rl = lgm == 0 ? (s * SLOT_PIECES + w) >> lgp : s >> lgm;
+            const u32 j = w & (RW - 1);
+#pragma unroll
+            for (int b0 = 0; b0 < B; b0 += 4) {
+              const float r = reduce4(racc[b0], racc[b0 + 1], racc[b0 + 2], racc[b0 + 3]);
+              if (lane < 4 && rl < nrt) g_red[(rl * RW + j) * B + b0 + lane] = r;
+            }
+          }
+        }
+      }
+    } else {
+      float acc[GEMV_BATCH][B];
+#pragma unroll
+      for (int i = 0; i < GEMV_BATCH; ++i) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[i][b] = 0.0f;
+        if ((u32)i < nb) {
+          // no lane or row test: inputs of lanes past the row's end are zero and every ring byte is
+          // a finite weight, so those products vanish; rows past the op are never stored
+          const u32 t = (s0 + i) & mmask;  // which 8-piece group of its row this slot holds
+          const u32x4 q = wv[i];
+          const float wf[8] = {bflo(q.x), bfhi(q.x), bflo(q.y), bfhi(q.y), bflo(q.z), bfhi(q.z), bflo(q.w), bfhi(q.w)};
+#pragma unroll
+          for (int tt = 0; tt < MM; ++tt) {
+            if ((u32)tt == t) {
+#pragma unroll
+              for (int b = 0; b < B; ++b)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[i][b] += wf[e] * xf[tt][b][e];
+            }
+          }
+        }
+      }
+      if (lgm == 0) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const float r = reduce4(acc[0][b], acc[1][b], acc[2][b], acc[3][b]);
+          if (lane < nb) {
+            const u32 rl = ((s0 + lane) * SLOT_PIECES + w) >> lgp;  // row of slot s0 + lane
+            const u32 j = w & (RW - 1);
+            if (rl < nrt) g_red[(rl * RW + j) * B + b] = r;
+          }
+        }
+      } else if (lgm == 1) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const float r = reduce4(acc[0][b] + acc[1][b], acc[2][b] + acc[3][b], 0.0f, 0.0f);
+          const u32 rl = (s0 >> 1) + lane;
+          if (lane < nb / 2 && rl < nrt) g_red[(rl * RW + w) * B + b] = r;
+        }
+      } else {
+        if ((s0 & mmask) == 0) {
+#pragma unroll
+          for (int b = 0; b < B; ++b) racc[b] = 0.0f;
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) racc[b] += (acc[0][b] + acc[1][b]) + (acc[2][b] + acc[3][b]);
+        if (((s0 + nb) & mmask) == 0) {  // this batch ends the row
+          const u32 rl = s0 >> lgm;
+          const float r = reduce4(racc[0], B > 1 ? racc[B > 1 ? 1 : 0] : 0.0f, 0.0f, 0.0f);
+          if (lane < (u32)B && rl < nrt) g_red[(rl * RW + w) * B + lane] = r;
         }
       }
     }
-    release_slot(seq, 1);
-    const bool row_end = ppr >= 8 ? (s % M == M - 1) : true;
-    if (row_end) {
-      const u32 j = ppr >= 8 ? w : kp;
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const float r = wave_sum(acc[b]);
-        if (lane == 0 && rl < nrt) g_red[(rl * RW + j) * B + b] = r;
-        acc[b] = 0.0f;
-      }
-    }
+    seq += nb;
   }
   if (!cbar(A, gen)) return false;
 
@@ -890,7 +1062,7 @@ __device__ void compute(const KArgs& A, u32 q0, u32 q1, u32 w) {
 
 template <int B>
 __device__ void megakernel_body(const KArgs& A) {
-  const u32 wv = threadIdx.x >> 6;
+  const u32 wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index: uniform per wave
   if (threadIdx.x < NSLOT) { g_full[threadIdx.x] = 0; g_done[threadIdx.x] = 0; }
   if (threadIdx.x == 0) { g_bar = 0; g_abort = 0; }
   __syncthreads();

@@ -73,12 +73,12 @@ std::string validate_desc(const mk_model_desc* desc, ModelShape* out, mk_status*
   return "";
 }
 
+// Pieces per row, rounded up to a power of two so the kernel indexes pieces with shifts.
 static int pad_ppr(int K) {
   const int real = (K + PIECE_ELEMS - 1) / PIECE_ELEMS;
-  if (real <= 1) return 1;
-  if (real <= 2) return 2;
-  if (real <= 4) return 4;
-  return (real + 7) / 8 * 8;
+  int p = 1;
+  while (p < real) p *= 2;
+  return p;
 }
 static int mmax_for(int B) { return B <= 2 ? 4 : (B <= 4 ? 2 : 1); }
 
@@ -118,9 +118,16 @@ struct Builder {
       T = (N + maxrows - 1) / maxrows;
       T = (T + n_cus - 1) / n_cus * n_cus;
     }
+    const uint32_t bnd[3] = {b1, b2, 0xFFFFFFFFu};
     for (uint32_t t = 0; t < T; ++t) {
-      const uint32_t r0 = (uint32_t)((uint64_t)N * t / T), r1 = (uint32_t)((uint64_t)N * (t + 1) / T);
-      if (r1 == r0) continue;
+      const uint32_t t0 = (uint32_t)((uint64_t)N * t / T), t1 = (uint32_t)((uint64_t)N * (t + 1) / T);
+      for (uint32_t r0 = t0, r1; r0 < t1; r0 = r1) {
+      // an op streams at most two weight runs: cut a tile that would touch three tensors
+      r1 = t1;
+      if (epi != EPI_SWIGLU) {
+        const int sa = r0 < b1 ? 0 : (r0 < b2 ? 1 : 2);
+        if (sa < 2) r1 = std::min<uint32_t>(t1, bnd[sa + 1]);
+      }
       Op o{};
       o.opcode = OP_GEMV;
       o.epi = epi;
@@ -135,11 +142,31 @@ struct Builder {
       o.nslots = (o.nrows * mult * ppr + SLOT_PIECES - 1) / SLOT_PIECES;
       o.ld_in = ld_in;
       o.ld_out = ld_out;
-      o.b1 = b1;
-      o.b2 = b2;
-      o.W = W; o.W2 = W2; o.W3 = W3;
+      // weight runs: at most two contiguous row runs per op
+      const uint64_t rb = (uint64_t)K * 2;
+      if (epi == EPI_SWIGLU) {
+        o.W = W ? W + r0 * rb : 0;
+        o.W2 = W2 ? W2 + r0 * rb : 0;
+        o.b1 = o.nrows;
+      } else {
+        const uint64_t segs[3] = {W, W2, W3};
+        const uint32_t start[3] = {0u, b1, b2}, end[3] = {b1, b2, 0xFFFFFFFFu};
+        int sa = r0 < b1 ? 0 : (r0 < b2 ? 1 : 2);
+        o.W = segs[sa] ? segs[sa] + (uint64_t)(r0 - start[sa]) * rb : 0;
+        const uint32_t na = std::min<uint32_t>(o.nrows, end[sa] - r0);
+        o.b1 = na;
+        o.W2 = 0;
+        if (na < o.nrows) {
+          if (sa == 2 || o.nrows - na > end[sa + 1] - start[sa + 1]) {
+            err = "a projection tile spans more than two weight tensors";
+            return;
+          }
+          o.W2 = segs[sa + 1];
+        }
+      }
       o.in = in; o.gamma = gamma; o.out = out; o.res = res;
       stage_ops[stage].push_back(o);
+      }
     }
   }
 
