@@ -199,7 +199,7 @@ struct Watchdog {
 };
 
 // Barrier among the NC compute waves (the loader never joins).  Returns false on abort.
-__device__ bool cbar(const KArgs& A, u32& gen) {
+__device__ __forceinline__ bool cbar(const KArgs& A, u32& gen) {
   __builtin_amdgcn_s_waitcnt(MK_LGKMCNT0);
   gen += NC;
   if (lane_id() == 0) __hip_atomic_fetch_add(&g_bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -249,20 +249,20 @@ struct AttnItem {
 __device__ __forceinline__ int clamp_ctx(const KArgs& A, int c) { return (c >= 1 && c <= A.max_ctx) ? c : 0; }
 
 // Item i -> (sequence, KV head, position range).  Uniform; reads ctx_lens with scalar loads.
+// Depends only on the launch's context lengths, so callers keep it across layers.
 __device__ AttnItem attn_item(const KArgs& A, u32 item, int pps) {
   AttnItem it{0, 0, 0, 0, 0, 0, false};
-  int64_t total = 0;
-  for (int b = 0; b < A.batch; ++b) total += clamp_ctx(A, sload(A.ctx_lens + b));
-  if (total == 0) return it;
-  const int cs = attn_chunk_size(total, A.Hkv, A.n_cus, pps);
+  auto ctx = [&](int b) { return clamp_ctx(A, sload(A.ctx_lens + b)); };
+  const int cs = attn_chunk_size(ctx, A.batch, A.Hkv, A.n_items, pps);
+  if (cs == 0) return it;
   const int bc = (int)(item / (u32)A.Hkv), kvh = (int)(item % (u32)A.Hkv);
   int acc = 0;
   for (int b = 0; b < A.batch; ++b) {
-    const int ctx = clamp_ctx(A, sload(A.ctx_lens + b));
-    const int nb = (ctx + cs - 1) / cs;
+    const int c = ctx(b);
+    const int nb = (c + cs - 1) / cs;
     if (bc < acc + nb) {
-      const int c = bc - acc;
-      it.b = b; it.kvh = kvh; it.p0 = c * cs; it.p1 = min(ctx, (c + 1) * cs);
+      const int k = bc - acc;
+      it.b = b; it.kvh = kvh; it.p0 = k * cs; it.p1 = min(c, (k + 1) * cs);
       it.n_b = nb; it.first_item = acc * A.Hkv + kvh; it.valid = true;
       return it;
     }
@@ -270,6 +270,15 @@ __device__ AttnItem attn_item(const KArgs& A, u32 item, int pps) {
   }
   return it;
 }
+// attn_item with a one-entry cache keyed by the item index
+struct ItemCache {
+  u32 item = 0xFFFFFFFFu;
+  AttnItem it{};
+  __device__ const AttnItem& get(const KArgs& A, u32 i, int pps) {
+    if (i != item) { it = attn_item(A, i, pps); item = i; }
+    return it;
+  }
+};
 
 __device__ __forceinline__ int attn_pps(int d) { return 4096 / (2 * d); }  // positions per ring slot
 
@@ -369,36 +378,65 @@ __device__ void issue_gemv(const GemvSeg& gsg, u32 s, u32 nrt, u32 lgp, u32 real
 }
 
 // Attention stream: slot s = PPS positions of K (pieces 0-3) then the same positions of V (4-7).
-// A piece covers 1 KB of one page; one page-table lookup per page.
-__device__ void issue_attn(const KArgs& A, const LayerDesc& Ld, const AttnItem& it, u32 s, u32 lane16, u32x4* dst) {
-  const u32 d = (u32)A.d, pps = 4096u / (2u * d), ppp = pps / 4;  // positions per slot / per piece
-  const size_t page_bytes = (size_t)A.Hkv * A.page_size * d * 2;
-  const size_t head_off = (size_t)it.kvh * A.page_size * d * 2;
-  const u32 pbase = (u32)it.p0 + s * pps;
+// Chunks start on page boundaries and a slot holds one page (d = 128) or two (d = 64), so a slot
+// needs at most two page-table entries.  The loader keeps 64 consecutive entries of one sequence
+// in a VGPR (one per lane) and refills the window only when a page falls outside it.
+//
+// K rows are stored swizzled: 16-byte chunk c of row r sits at chunk position c ^ (r mod CPR)
+// (CPR = chunks per row), so the 16 rows one matrix-core operand read touches fall in distinct
+// LDS banks.  A DMA lane chooses its source address, so the swizzle costs nothing: lane i of
+// piece j fills row r = j*RPP + i/CPR, chunk position i mod CPR.
+struct PageWindow {
+  int b = -1;
+  u32 base = 0;
+  int v = 0;  // lane i: physical page of logical page base + i
+};
+__device__ __forceinline__ int page_lookup(const KArgs& A, PageWindow& pw, int b, u32 pi) {
+  if (b != pw.b || pi < pw.base || pi >= pw.base + 64) {
+    pw.b = b;
+    pw.base = pi;
+    const u32 lp = pi + lane_id();
+    int v = lp < (u32)A.max_pages_per_seq ? A.page_table[(size_t)b * A.max_pages_per_seq + lp] : 0;
+    pw.v = (v >= 0 && v < A.num_pages) ? v : 0;  // out-of-range entries stream page 0 (rows get masked)
+  }
+  return __builtin_amdgcn_readlane(pw.v, (int)(pi - pw.base));
+}
+struct AttnLanes {  // per-lane byte offsets of each piece within its page's (kv head) block
+  u32 koff[4], voff[4];
+  u32 kpage[4];     // page of the slot (0 or 1) each piece reads
+};
+__device__ AttnLanes attn_lanes(u32 d) {
+  AttnLanes L;
+  const u32 lane = lane_id(), cpr = d / 8, rpp = 64 / cpr, rb = 2 * d;
+#pragma unroll
+  for (u32 j = 0; j < 4; ++j) {
+    const u32 r = j * rpp + lane / cpr, q = lane % cpr;
+    L.koff[j] = (r % 16) * rb + ((q ^ (r % cpr)) * 16);
+    L.voff[j] = (r % 16) * rb + q * 16;
+    L.kpage[j] = r / 16;
+  }
+  return L;
+}
+__device__ void issue_attn(const KArgs& A, const LayerDesc& Ld, const AttnItem& it, u32 s, const AttnLanes& L,
+                           PageWindow& pw, u32 lane16, u32x4* dst) {
+  const u32 d = (u32)A.d, pps = 4096u / (2u * d);
+  const size_t page_bytes = (size_t)A.Hkv * 16 * d * 2, head_off = (size_t)it.kvh * 16 * d * 2;
+  const u32 pbase = (u32)it.p0 + s * pps, pi0 = pbase / 16;
   const char* kb = (const char*)Ld.k_pages;
   const char* vb = (const char*)Ld.v_pages;
-  u32 cur = 0xFFFFFFFFu;
-  size_t pg_off = 0;
+  size_t off[2];
+#pragma unroll
+  for (u32 k = 0; k < 2; ++k) {
+    const bool used = (pi0 + k) * 16 < (u32)it.p1 && (k == 0 || pps > 16);
+    off[k] = used ? (size_t)page_lookup(A, pw, it.b, pi0 + k) * page_bytes + head_off : 0;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const u32 pos = pbase + j * ppp;
-    if (pos < (u32)it.p1) {
-      const u32 pi = pos >> 4;  // page_size == 16
-      if (pi != cur) {
-        cur = pi;
-        int pg = pi < (u32)A.max_pages_per_seq ? sload(A.page_table + (size_t)it.b * A.max_pages_per_seq + pi) : 0;
-        pg = (pg >= 0 && pg < A.num_pages) ? pg : 0;
-        pg_off = (size_t)pg * page_bytes + head_off + (size_t)(pos & 15u) * d * 2;
-      } else {
-        pg_off += (size_t)ppp * d * 2;
-      }
-      dma_at(kb + pg_off, lane16, dst + j * 64);
-      dma_at(vb + pg_off, lane16, dst + (4 + j) * 64);
-    } else {
-      dma_at(kb, lane16, dst + j * 64);
-      dma_at(vb, lane16, dst + (4 + j) * 64);
-    }
+    const size_t o = L.kpage[j] ? off[1] : off[0];
+    dma_at(kb + o, L.koff[j], dst + j * 64);
+    dma_at(vb + o, L.voff[j], dst + (4 + j) * 64);
   }
+  (void)lane16;
 }
 
 // Delta stream: rows of S^T (fp32) of one column block, contiguous.
@@ -410,21 +448,24 @@ __device__ void issue_delta(const KArgs& A, const LayerDesc& Ld, u32 item, u32 s
   for (int i = 0; i < SLOT_PIECES; ++i) dma_at(src + i * PIECE, lane16, dst + i * 64);
 }
 
-__device__ u32 op_slots(const KArgs& A, const Op& o) {
+__device__ u32 op_slots(const KArgs& A, const Op& o, ItemCache& ic) {
   if (o.opcode == OP_ATTN) {
     const int pps = attn_pps(A.d);
-    AttnItem it = attn_item(A, o.row0, pps);
+    const AttnItem& it = ic.get(A, o.row0, pps);
     return it.valid ? (u32)((it.p1 - it.p0 + pps - 1) / pps) : 0u;
   }
   return o.nslots;
 }
 
-__device__ void loader(const KArgs& A, u32 q0, u32 q1) {
+__device__ __forceinline__ void loader(const KArgs& A, u32 q0, u32 q1) {
   u32 seq = 0, marked = 0;
   const u32 lane16 = lane_id() * 16;
+  ItemCache ic;
+  PageWindow pw;
+  const AttnLanes al = attn_lanes(A.d == 64 ? 64u : 128u);
   for (u32 oi = q0; oi < q1; ++oi) {
     const Op o = sload(A.ops + oi);
-    const u32 ns = op_slots(A, o);
+    const u32 ns = op_slots(A, o, ic);
     if (ns == 0) continue;
     LayerDesc Ld{};
     AttnItem it{};
@@ -433,7 +474,7 @@ __device__ void loader(const KArgs& A, u32 q0, u32 q1) {
     const u32 real_pieces = (o.K + PIECE_ELEMS - 1) / PIECE_ELEMS;
     const GemvSeg gsg = gemv_seg(o);
     if (o.opcode == OP_ATTN || o.opcode == OP_DELTA) Ld = sload(A.layers + o.layer);
-    if (o.opcode == OP_ATTN) it = attn_item(A, o.row0, attn_pps(A.d));
+    if (o.opcode == OP_ATTN) it = ic.get(A, o.row0, attn_pps(A.d));
     for (u32 s = 0; s < ns; ++s) {
       const u32 pos = seq % NSLOT, round = seq / NSLOT;
       Watchdog wd(A);
@@ -451,7 +492,7 @@ __device__ void loader(const KArgs& A, u32 q0, u32 q1) {
       }
       u32x4* dst = g_ring + pos * (SLOT / 16);
       if (o.opcode == OP_GEMV) issue_gemv(gsg, s, nrt, lgp, real_pieces, lane16, dst);
-      else if (o.opcode == OP_ATTN) issue_attn(A, Ld, it, s, lane16, dst);
+      else if (o.opcode == OP_ATTN) issue_attn(A, Ld, it, s, al, pw, lane16, dst);
       else issue_delta(A, Ld, o.row0, s, lane16, dst);
       ++seq;
       if (seq - marked > LOAD_DEPTH) {
@@ -467,7 +508,7 @@ __device__ void loader(const KArgs& A, u32 q0, u32 q1) {
 }
 
 // ------------------------------------------------------------------ dependency wait / signal
-__device__ bool wait_stage(const KArgs& A, int stage) {
+__device__ __forceinline__ bool wait_stage(const KArgs& A, int stage) {
   const u32 lane = lane_id();
   const Stage st = sload(A.stages + stage);
   const u32 per = st.nops / NSUB, rem = st.nops % NSUB;
@@ -482,14 +523,14 @@ __device__ bool wait_stage(const KArgs& A, int stage) {
   }
 }
 
-__device__ void signal_stage(const KArgs& A, int stage, u32 index) {
+__device__ __forceinline__ void signal_stage(const KArgs& A, int stage, u32 index) {
   u32* c = A.counters + (size_t)stage * NSUB * CTR_STRIDE + (size_t)(index % NSUB) * CTR_STRIDE;
   __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ EMBED
 // x0[b][h] = E[token_b][h] for this CU's slice of h (rows with b >= batch or a bad token are zero).
-__device__ void op_embed(const KArgs& A, u32 w) {
+__device__ __forceinline__ void op_embed(const KArgs& A, u32 w) {
   const u32 t = w * 64 + lane_id();
   const int cu = (int)blockIdx.x;
   const int h0 = (int)((int64_t)A.H * cu / A.n_cus), h1 = (int)((int64_t)A.H * (cu + 1) / A.n_cus);
@@ -503,7 +544,7 @@ __device__ void op_embed(const KArgs& A, u32 w) {
 
 // Second phase of EMBED, CU 0 only: validate every row (token, context, position, every page of
 // [0, ctx) mapped), publish row_ok and raise ST_BAD_INPUT for out-of-contract rows.
-__device__ void op_embed_finish(const KArgs& A, u32 w, u32& gen) {
+__device__ __forceinline__ void op_embed_finish(const KArgs& A, u32 w, u32& gen) {
   if (blockIdx.x != 0) return;
   for (int b = 0; b < A.max_batch; ++b) {
     bool ok = row_ok_local(A, b);
@@ -537,7 +578,7 @@ struct MMax { static constexpr int v = B <= 2 ? 4 : (B <= 4 ? 2 : 1); };
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 template <int B>
-__device__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
+__device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
   constexpr int MM = MMax<B>::v;
   const u32 lane = lane_id();
   const u32 ppr = o.ppr, K = o.K;
@@ -740,27 +781,71 @@ __device__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) 
 
 // ------------------------------------------------------------------ ATTENTION (split-KV + merge)
 // One item = (sequence b, KV head, position chunk).  The G query heads sharing the KV head are
-// processed together; each compute wave runs an online softmax over its ring slots, the waves are
-// merged in LDS, the chunk's (m, l, o) partial goes to global memory, and the last chunk of (b, kvh)
-// to finish (a ticket) merges all chunks with the log-sum-exp rule.
+// processed together.  Scores come from the matrix cores: Q (G heads, split into bf16 hi + lo so
+// the product keeps fp32 accuracy) times K^T, 16 positions per 16x16x32 tile.  Each compute wave
+// runs an online softmax over its ring slots and accumulates P V on the vector ALUs; the waves are
+// merged in LDS, the chunk's (m, l, o) partial goes to global memory, and the last chunk of
+// (b, kvh) to finish (a ticket) merges all chunks with the log-sum-exp rule.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float row_max16(float v) {  // max over the 16 lanes of a DPP row
+  v = fmaxf(v, dppf<0xB1>(v));
+  v = fmaxf(v, dppf<0x4E>(v));
+  v = fmaxf(v, dppf<0x141>(v));
+  return fmaxf(v, dppf<0x140>(v));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dppf<0xB1>(v);
+  v += dppf<0x4E>(v);
+  v += dppf<0x141>(v);
+  return v + dppf<0x140>(v);
+}
+// x = hi + lo with both halves bf16 (hi rounded to nearest, lo the rounded remainder)
+__device__ __forceinline__ void split_bf16x8(const float* x, u32x4& hi, u32x4& lo) {
+  u32 h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const u32 h0 = f2bf(x[2 * e]), h1 = f2bf(x[2 * e + 1]);
+    const u32 l0 = f2bf(x[2 * e] - __builtin_bit_cast(float, h0 << 16));
+    const u32 l1 = f2bf(x[2 * e + 1] - __builtin_bit_cast(float, h1 << 16));
+    h[e] = h0 | (h1 << 16);
+    l[e] = l0 | (l1 << 16);
+  }
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
 template <int D>
-__device__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
-  constexpr int DPL = D / 64;        // dims per lane
-  constexpr int PPS = 4096 / (2 * D);
+__device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen, ItemCache& ic) {
+  constexpr int DPL = D / 64;          // dims per lane in the vector layout
+  constexpr int PPS = 4096 / (2 * D);  // positions per ring slot
+  constexpr int NB = PPS / 16;         // 16-position score tiles per slot
+  constexpr int KB = D / 32;           // k-blocks of one score tile
   constexpr int GMAX = 512 / D;
+  constexpr int CPR = D / 8;           // 16-byte chunks per K row
+  constexpr int RB = 2 * D;            // bytes per K or V row
+  constexpr int PWS = PPS * GMAX + GMAX;
+  constexpr int QF = 768 + NC * PWS;  // query fragments: [KB][hi, lo][64 lanes] x 16 bytes
+  static_assert(QF + KB * 2 * 64 * 4 <= RED_FLOATS, "attention LDS areas");
   const u32 lane = lane_id();
-  const AttnItem it = attn_item(A, o.row0, PPS);
+  const AttnItem it = ic.get(A, o.row0, PPS);
   if (!it.valid) return true;
   const u32 ns = (u32)((it.p1 - it.p0 + PPS - 1) / PPS);
+  const u32 seq0 = seq;
+  seq += ns;
   const LayerDesc Ld = sload(A.layers + o.layer);
   const int G = A.G, b = it.b, kvh = it.kvh;
   const int pos = A.positions[b];
-  const bool ok = row_ok_local(A, b);
+  const bool ok = ld_i32_sc1(A.row_ok + b) != 0;
   const int qkv_ld = (A.Hq + 2 * A.Hkv) * D;
   const float* qkv = (const float*)Ld.qkv + (size_t)b * qkv_ld;
   const float scale = 1.0f / sqrtf((float)D);
   const int posc = (pos >= 0 && pos < A.max_ctx) ? pos : 0;
   const float* rope = A.rope + (size_t)posc * (D / 2) * 2;
+  float* qs = g_red;                   // [G][D] rotated, scaled queries
+  float* kvn = g_red + 512;            // [2][D] the new token's rotated K and its V, bf16-rounded
+  float* pwv = g_red + 768 + w * PWS;  // this wave: P[position][head], then the rescale per head
 
   // rotary embedding of a head held as dims [lane*DPL, lane*DPL + DPL): partner lane ^ 32
   auto rotate = [&](float* v) {
@@ -782,94 +867,171 @@ __device__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) 
     for (int e = 0; e < DPL; ++e) v[e] *= r * bf2f(gain[lane * DPL + e]);
   };
 
-  float qv[GMAX][DPL];
-#pragma unroll
-  for (int g = 0; g < GMAX; ++g) {
-    if (g < G) {
-      const int h = kvh * G + g;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) qv[g][e] = ld_sc1(qkv + h * D + lane * DPL + e);
-      if (A.qk_norm) headnorm(qv[g], (const uint16_t*)Ld.q_norm);
-      rotate(qv[g]);
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) qv[g][e] *= scale;
-    }
-  }
+  // 1. one task per wave: query heads 0..G-1, then (chunk holding the new token) its K and V
   const bool has_new = pos >= it.p0 && pos < it.p1;
-  float kn[DPL], vn[DPL];
-  if (has_new) {
+  const int ntask = G + (has_new ? 2 : 0);
+  for (int t = (int)w; t < ntask; t += NC) {
+    const int row = t < G ? kvh * G + t : (t == G ? A.Hq + kvh : A.Hq + A.Hkv + kvh);
+    float v[DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      kn[e] = ld_sc1(qkv + (A.Hq + kvh) * D + lane * DPL + e);
-      vn[e] = ld_sc1(qkv + (A.Hq + A.Hkv + kvh) * D + lane * DPL + e);
+    for (int e = 0; e < DPL; ++e) v[e] = ld_sc1(qkv + row * D + lane * DPL + e);
+    if (t <= G) {
+      if (A.qk_norm) headnorm(v, (const uint16_t*)(t < G ? Ld.q_norm : Ld.k_norm));
+      rotate(v);
     }
-    if (A.qk_norm) headnorm(kn, (const uint16_t*)Ld.k_norm);
-    rotate(kn);
-    uint16_t kb[DPL], vb[DPL];
+    if (t < G) {
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {  // the cache holds bf16: attend to the rounded values
-      kb[e] = f2bf(kn[e]); vb[e] = f2bf(vn[e]);
-      kn[e] = bf2f(kb[e]); vn[e] = bf2f(vb[e]);
-    }
-    if (ok && w == 0) {
-      const int pg = A.page_table[(size_t)b * A.max_pages_per_seq + pos / A.page_size];
-      const size_t off = (((size_t)pg * A.Hkv + kvh) * A.page_size + pos % A.page_size) * D + lane * DPL;
+      for (int e = 0; e < DPL; ++e) qs[t * D + lane * DPL + e] = v[e] * scale;
+    } else {
+      uint16_t hb[DPL];  // the cache holds bf16: attend to the rounded values
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
-        ((uint16_t*)Ld.k_pages)[off + e] = kb[e];
-        ((uint16_t*)Ld.v_pages)[off + e] = vb[e];
+        hb[e] = f2bf(v[e]);
+        kvn[(t - G) * D + lane * DPL + e] = bf2f(hb[e]);
+      }
+      if (ok) {
+        const int pg = A.page_table[(size_t)b * A.max_pages_per_seq + pos / 16];
+        const size_t off = (((size_t)pg * A.Hkv + kvh) * 16 + pos % 16) * D + lane * DPL;
+        uint16_t* dp = (uint16_t*)(t == G ? Ld.k_pages : Ld.v_pages) + off;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) dp[e] = hb[e];
       }
     }
   }
+  if (!cbar(A, gen)) return false;
 
-  float m[GMAX], l[GMAX], ov[GMAX][DPL];
+  // 2. query fragments, built once into LDS by waves 0..KB-1: matrix-core A operand, row = head
+  //    lane % 16, k-chunk lane / 16, each split into bf16 hi + lo
+  u32x4* qf = (u32x4*)(g_red + QF);
+  if ((int)w < KB) {
+    const int kb = (int)w, gq = (int)(lane & 15), kc = (int)(lane >> 4);
+    float x[8];
 #pragma unroll
-  for (int g = 0; g < GMAX; ++g) {
-    m[g] = -INFINITY; l[g] = 0.0f;
+    for (int e = 0; e < 8; ++e) x[e] = gq < G ? qs[gq * D + kb * 32 + kc * 8 + e] : 0.0f;
+    split_bf16x8(x, qf[(kb * 2) * 64 + lane], qf[(kb * 2 + 1) * 64 + lane]);
+  }
+  if (!cbar(A, gen)) return false;
+
+  // 3. this wave's slots: w, w + NC, ...  Score tile lanes: position p = 16*blk + lane % 16,
+  //    heads hr .. hr + 3 with hr = 4 * (lane / 16).
+  const int hr = (int)(lane >> 4) * 4;
+  float m[4], l[4], ov[GMAX][DPL];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.0f; }
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g)
 #pragma unroll
     for (int e = 0; e < DPL; ++e) ov[g][e] = 0.0f;
-  }
-  for (u32 s = 0; s < ns; ++s, ++seq) {
-    if (s % NC != w) continue;
-    if (!wait_full(A, seq)) return false;
-    const uint16_t* kr = (const uint16_t*)(g_ring + (seq % NSLOT) * (SLOT / 16));
-    const uint16_t* vr = kr + 2048;  // V half of the slot (4 KB)
+  for (u32 s = w; s < ns; s += NC) {
+    const u32 sq = seq0 + s;
+    if (!wait_full(A, sq)) return false;
+    char* kslot = (char*)(g_ring + (sq % NSLOT) * (SLOT / 16));
+    char* vslot = kslot + 4096;
     const int pbase = it.p0 + (int)s * PPS;
     const int np = min(PPS, it.p1 - pbase);
-    for (int pp = 0; pp < np; ++pp) {
-      float k[DPL], v[DPL];
+    if (has_new && pos >= pbase && pos < pbase + PPS) {
+      // the new token's K/V are not in the cache the loader read: put them into the slot
+      const int r = pos - pbase, d0 = (int)lane * DPL, c = d0 / 8;
+      uint16_t* kd = (uint16_t*)(kslot + r * RB + ((c ^ (r % CPR)) * 16)) + (d0 % 8);
+      uint16_t* vd = (uint16_t*)(vslot + r * RB) + d0;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
-        k[e] = bf2f(kr[pp * D + lane * DPL + e]);
-        v[e] = bf2f(vr[pp * D + lane * DPL + e]);
-      }
-      if (pbase + pp == pos) {  // the new token: its K/V are not in the cache the loader read
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) { k[e] = kn[e]; v[e] = vn[e]; }
-      }
-#pragma unroll
-      for (int g = 0; g < GMAX; ++g) {
-        if (g < G) {
-          float part = 0.0f;
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) part += qv[g][e] * k[e];
-          const float sc = wave_sum(part);
-          const float mn = fmaxf(m[g], sc);
-          const float corr = __expf(m[g] - mn), pr = __expf(sc - mn);
-          l[g] = l[g] * corr + pr;
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) ov[g][e] = ov[g][e] * corr + pr * v[e];
-          m[g] = mn;
-        }
+        kd[e] = f2bf(kvn[d0 + e]);
+        vd[e] = f2bf(kvn[D + d0 + e]);
       }
     }
-    release_slot(seq, NC);
+    f32x4 sc[NB];
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      const int p = blk * 16 + (int)(lane & 15);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int c = kb * 4 + (int)(lane >> 4);
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(kslot + p * RB + ((c ^ (p % CPR)) * 16)));
+        const bf16x8 qh = __builtin_bit_cast(bf16x8, qf[(kb * 2) * 64 + lane]);
+        const bf16x8 ql = __builtin_bit_cast(bf16x8, qf[(kb * 2 + 1) * 64 + lane]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kf, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, kf, acc, 0, 0, 0);
+      }
+      sc[blk] = acc;
+    }
+    float mx[4], corr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx[i] = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const bool live = blk * 16 + (int)(lane & 15) < np;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!live) sc[blk][i] = -INFINITY;
+        mx[i] = fmaxf(mx[i], sc[blk][i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mn = fmaxf(m[i], row_max16(mx[i]));
+      corr[i] = __expf(m[i] - mn);  // 0 on the first slot (m = -inf)
+      float ps = 0.0f;
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        sc[blk][i] = __expf(sc[blk][i] - mn);
+        ps += sc[blk][i];
+      }
+      l[i] = l[i] * corr[i] + row_sum16(ps);
+      m[i] = mn;
+    }
+    // probabilities and rescale factors to LDS, read back by every lane of this wave for P V
+    if (hr < G) {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) *(f32x4*)&pwv[(blk * 16 + (int)(lane & 15)) * GMAX + hr] = sc[blk];
+      if ((lane & 15) == 0) *(f32x4*)&pwv[PPS * GMAX + hr] = f32x4{corr[0], corr[1], corr[2], corr[3]};
+    }
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      if (g < G) {
+        const float cr = pwv[PPS * GMAX + g];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) ov[g][e] *= cr;
+      }
+    }
+    for (int p = 0; p < np; ++p) {
+      float vv[DPL];
+      if constexpr (DPL == 2) {
+        const u32 u = *(const u32*)(vslot + p * RB + lane * 4);
+        vv[0] = bflo(u); vv[1] = bfhi(u);
+      } else {
+        vv[0] = bf2f(*(const uint16_t*)(vslot + p * RB + lane * 2));
+      }
+      float pp[GMAX];
+#pragma unroll
+      for (int g4 = 0; g4 < GMAX; g4 += 4) {
+        const f32x4 q4 = *(const f32x4*)&pwv[p * GMAX + g4];
+        pp[g4] = q4[0]; pp[g4 + 1] = q4[1]; pp[g4 + 2] = q4[2]; pp[g4 + 3] = q4[3];
+      }
+#pragma unroll
+      for (int g = 0; g < GMAX; ++g)
+        if (g < G)
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) ov[g][e] += pp[g] * vv[e];
+    }
+    release_slot(sq, NC);
   }
+  if (!cbar(A, gen)) return false;  // every wave is done with the query / new-token / P areas
+
   // merge the waves of this workgroup
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (hr + i < G) {
+        g_scr[(w * GMAX + hr + i) * 2] = m[i];
+        g_scr[(w * GMAX + hr + i) * 2 + 1] = l[i];
+      }
+    }
+  }
 #pragma unroll
   for (int g = 0; g < GMAX; ++g) {
     if (g < G) {
-      if (lane == 0) { g_scr[(w * GMAX + g) * 2] = m[g]; g_scr[(w * GMAX + g) * 2 + 1] = l[g]; }
 #pragma unroll
       for (int e = 0; e < DPL; ++e) g_red[(w * GMAX + g) * D + lane * DPL + e] = ov[g][e];
     }
@@ -926,7 +1088,7 @@ __device__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) 
 // column j: kS_j = S[:, j] . k, S'[:, j] = g S[:, j] + beta k (v_j - kS_j), o_j = S'[:, j] . q.
 // The q / k conv state is shared by the blocks of (b, h): the last block to finish writes it.
 template <int DK>
-__device__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
+__device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
   constexpr int DPL = DK / 64;
   constexpr int RPS = SLOT / (DK * 4);  // S^T rows per slot
   constexpr int NSL = 32 / RPS;
@@ -1035,8 +1197,9 @@ __device__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen)
 
 // ------------------------------------------------------------------ compute waves
 template <int B>
-__device__ void compute(const KArgs& A, u32 q0, u32 q1, u32 w) {
+__device__ __forceinline__ void compute(const KArgs& A, u32 q0, u32 q1, u32 w) {
   u32 seq = 0, gen = 0;
+  ItemCache ic;
   for (u32 oi = q0; oi < q1; ++oi) {
     const Op o = sload(A.ops + oi);
     if (w == 0 && o.wait_stage != NO_STAGE) wait_stage(A, o.wait_stage);
@@ -1049,7 +1212,7 @@ __device__ void compute(const KArgs& A, u32 q0, u32 q1, u32 w) {
         op_embed_finish(A, w, gen);
         break;
       case OP_GEMV: alive = op_gemv<B>(A, o, w, seq, gen); break;
-      case OP_ATTN: alive = A.d == 128 ? op_attn<128>(A, o, w, seq, gen) : op_attn<64>(A, o, w, seq, gen); break;
+      case OP_ATTN: alive = A.d == 128 ? op_attn<128>(A, o, w, seq, gen, ic) : op_attn<64>(A, o, w, seq, gen, ic); break;
       case OP_DELTA: alive = A.dk == 128 ? op_delta<128>(A, o, w, seq, gen) : op_delta<64>(A, o, w, seq, gen); break;
       default: break;
     }
@@ -1061,7 +1224,7 @@ __device__ void compute(const KArgs& A, u32 q0, u32 q1, u32 w) {
 }
 
 template <int B>
-__device__ void megakernel_body(const KArgs& A) {
+__device__ __forceinline__ void megakernel_body(const KArgs& A) {
   const u32 wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index: uniform per wave
   if (threadIdx.x < NSLOT) { g_full[threadIdx.x] = 0; g_done[threadIdx.x] = 0; }
   if (threadIdx.x == 0) { g_bar = 0; g_abort = 0; }

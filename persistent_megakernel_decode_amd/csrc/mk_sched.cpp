@@ -200,7 +200,8 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
   const int nh = d.n_delta_heads, dk = d.delta_dk, dv = d.delta_dv;
   const int u_w = m.n_delta ? m.C + 2 * nh : 0;
   P.mix_dim = std::max(m.n_attn ? Hq * hd : 0, m.n_delta ? nh * dv : 0);
-  P.n_items = m.n_attn ? n_cus + Hkv * d.max_batch : 0;
+  // attention items per layer: a whole number of items per CU, at least one per (sequence, KV head)
+  P.n_items = m.n_attn ? n_cus * ((Hkv * d.max_batch + n_cus - 1) / n_cus) : 0;
   const int gmax = m.n_attn ? 512 / hd : 0;
 
   // ---------------- workspace layout (offsets; sizes of the queue sections are known after planning)
