@@ -125,9 +125,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 // 64-lane sum of v[q].  Butterfly over the quad (xor 1, xor 2) so each lane keeps one value
 // index (lane & 3), rotate-add within each 16-lane row, then pair rows with the lane-32 and
 // lane-16 swaps.  Fixed order, so bitwise reproducible.
-// c + (c of the lane 32 away), and c + (c of the row 16 lanes away).  Written as the swap
-// instruction itself: the compiler's builtin for it folds the two results of a float sum into one.
-// The s_nop covers the wait states the swap needs after a VALU write of its operands.
+// c + (c of the lane 32 away), and c + (c of the row 16 lanes away), written as the swap
+// instruction itself.  The s_nop covers the wait states the swap needs after a VALU write of its
+// operands.
 __device__ __forceinline__ float add_swap32(float c) {
   float x = c, y = c;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
@@ -789,6 +789,11 @@ __device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32&
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Lane `l` of a float.  Takes the value by copy: clang's __builtin_bit_cast applied directly to an
+// element of an ext_vector (v[i]) reads element 0, so vector elements must never be its operand.
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
 __device__ __forceinline__ float row_max16(float v) {  // max over the 16 lanes of a DPP row
   v = fmaxf(v, dppf<0xB1>(v));
   v = fmaxf(v, dppf<0x4E>(v));
@@ -825,8 +830,7 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   constexpr int GMAX = 512 / D;
   constexpr int CPR = D / 8;           // 16-byte chunks per K row
   constexpr int RB = 2 * D;            // bytes per K or V row
-  constexpr int PWS = PPS * GMAX + GMAX;
-  constexpr int QF = 768 + NC * PWS;  // query fragments: [KB][hi, lo][64 lanes] x 16 bytes
+  constexpr int QF = 768;              // query fragments: [KB][hi, lo][64 lanes] x 16 bytes
   static_assert(QF + KB * 2 * 64 * 4 <= RED_FLOATS, "attention LDS areas");
   const u32 lane = lane_id();
   const AttnItem it = ic.get(A, o.row0, PPS);
@@ -845,7 +849,6 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   const float* rope = A.rope + (size_t)posc * (D / 2) * 2;
   float* qs = g_red;                   // [G][D] rotated, scaled queries
   float* kvn = g_red + 512;            // [2][D] the new token's rotated K and its V, bf16-rounded
-  float* pwv = g_red + 768 + w * PWS;  // this wave: P[position][head], then the rescale per head
 
   // rotary embedding of a head held as dims [lane*DPL, lane*DPL + DPL): partner lane ^ 32
   auto rotate = [&](float* v) {
@@ -981,43 +984,39 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
       l[i] = l[i] * corr[i] + row_sum16(ps);
       m[i] = mn;
     }
-    // probabilities and rescale factors to LDS, read back by every lane of this wave for P V
-    if (hr < G) {
+    // P V on the vector ALUs.  Lane owns DPL dims of every head; P[head][p] and the rescale
+    // factors are broadcast from their score-tile lanes with readlane.  Heads past G carry
+    // finite junk (zero queries) and are never stored.  Rows past the chunk are zeroed so that
+    // stale ring bytes cannot reach the sums.
+    u32 vw[PPS];
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk) *(f32x4*)&pwv[(blk * 16 + (int)(lane & 15)) * GMAX + hr] = sc[blk];
-      if ((lane & 15) == 0) *(f32x4*)&pwv[PPS * GMAX + hr] = f32x4{corr[0], corr[1], corr[2], corr[3]};
+    for (int p = 0; p < PPS; ++p) {
+      u32 u;
+      if constexpr (DPL == 2) u = *(const u32*)(vslot + p * RB + lane * 4);
+      else u = *(const uint16_t*)(vslot + p * RB + lane * 2);
+      vw[p] = p < np ? u : 0u;
     }
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
-      if (g < G) {
-        const float cr = pwv[PPS * GMAX + g];
+      const float cr = readlane_f(corr[g & 3], (g >> 2) * 16);
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) ov[g][e] *= cr;
-      }
+      for (int e = 0; e < DPL; ++e) ov[g][e] *= cr;
     }
-    for (int p = 0; p < np; ++p) {
+#pragma unroll
+    for (int p = 0; p < PPS; ++p) {
       float vv[DPL];
-      if constexpr (DPL == 2) {
-        const u32 u = *(const u32*)(vslot + p * RB + lane * 4);
-        vv[0] = bflo(u); vv[1] = bfhi(u);
-      } else {
-        vv[0] = bf2f(*(const uint16_t*)(vslot + p * RB + lane * 2));
+      if constexpr (DPL == 2) { vv[0] = bflo(vw[p]); vv[1] = bfhi(vw[p]); }
+      else vv[0] = bflo(vw[p]);
+#pragma unroll
+      for (int g = 0; g < GMAX; ++g) {
+        const float pg = readlane_f(sc[p / 16][g & 3], (g >> 2) * 16 + p % 16);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) ov[g][e] += pg * vv[e];
       }
-      float pp[GMAX];
-#pragma unroll
-      for (int g4 = 0; g4 < GMAX; g4 += 4) {
-        const f32x4 q4 = *(const f32x4*)&pwv[p * GMAX + g4];
-        pp[g4] = q4[0]; pp[g4 + 1] = q4[1]; pp[g4 + 2] = q4[2]; pp[g4 + 3] = q4[3];
-      }
-#pragma unroll
-      for (int g = 0; g < GMAX; ++g)
-        if (g < G)
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) ov[g][e] += pp[g] * vv[e];
     }
     release_slot(sq, NC);
   }
-  if (!cbar(A, gen)) return false;  // every wave is done with the query / new-token / P areas
+  if (!cbar(A, gen)) return false;  // every wave is done with the query / new-token areas
 
   // merge the waves of this workgroup
   if ((lane & 15) == 0) {
@@ -1061,19 +1060,34 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   }
   if (!cbar(A, gen)) return false;
   if (g_bcast[0]) {  // last chunk of (b, kvh): log-sum-exp merge of all its chunks
-    for (int t = (int)(w * 64 + lane); t < G * D; t += NC * 64) {
+    const int tid = (int)(w * 64 + lane);
+    const float* part0 = (const float*)Ld.part + (size_t)it.first_item * GMAX * (D + 2);
+    const size_t cstride = (size_t)A.Hkv * GMAX * (D + 2);  // floats between chunks of (b, kvh)
+    float* ml = g_red;                                         // [n_b][G][m, l]
+    for (int t = tid; t < it.n_b * G; t += NC * 64) {
+      const float* pc = part0 + (size_t)(t / G) * cstride + (t % G) * (D + 2);
+      ml[2 * t] = ld_sc1(pc);
+      ml[2 * t + 1] = ld_sc1(pc + 1);
+    }
+    if (!cbar(A, gen)) return false;
+    for (int t = tid; t < G * D; t += NC * 64) {
       const int g = t / D, dim = t % D;
       float M = -INFINITY;
-      for (int c = 0; c < it.n_b; ++c) {
-        const float* pc = (const float*)Ld.part + (size_t)(it.first_item + c * A.Hkv) * GMAX * (D + 2) + g * (D + 2);
-        M = fmaxf(M, ld_sc1(pc));
-      }
+      for (int c = 0; c < it.n_b; ++c) M = fmaxf(M, ml[2 * (c * G + g)]);
       float den = 0.0f, num = 0.0f;
-      for (int c = 0; c < it.n_b; ++c) {
-        const float* pc = (const float*)Ld.part + (size_t)(it.first_item + c * A.Hkv) * GMAX * (D + 2) + g * (D + 2);
-        const float f = __expf(ld_sc1(pc) - M);
-        den += f * ld_sc1(pc + 1);
-        num += f * ld_sc1(pc + 2 + dim);
+      for (int c0 = 0; c0 < it.n_b; c0 += 16) {  // 16 chunks' outputs in flight at once
+        float oc[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          oc[k] = c0 + k < it.n_b ? ld_sc1(part0 + (size_t)(c0 + k) * cstride + g * (D + 2) + 2 + dim) : 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          if (c0 + k < it.n_b) {
+            const float f = __expf(ml[2 * ((c0 + k) * G + g)] - M);
+            den += f * ml[2 * ((c0 + k) * G + g) + 1];
+            num += f * oc[k];
+          }
+        }
       }
       st_sc1((float*)Ld.mix_o + (size_t)b * A.mix + (kvh * G + g) * D + dim, num / den);
     }

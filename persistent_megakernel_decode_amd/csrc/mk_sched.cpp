@@ -202,6 +202,9 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
   P.mix_dim = std::max(m.n_attn ? Hq * hd : 0, m.n_delta ? nh * dv : 0);
   // attention items per layer: a whole number of items per CU, at least one per (sequence, KV head)
   P.n_items = m.n_attn ? n_cus * ((Hkv * d.max_batch + n_cus - 1) / n_cus) : 0;
+  // the merge of one (sequence, KV head) stages every chunk's (m, l) per query head in LDS
+  if (m.n_attn && (int64_t)(P.n_items / Hkv) * (d.n_q_heads / Hkv) * 2 > RED_FLOATS)
+    return fmt("too many attention chunks per KV head for the merge (%d items, %d KV heads)", P.n_items, Hkv);
   const int gmax = m.n_attn ? 512 / hd : 0;
 
   // ---------------- workspace layout (offsets; sizes of the queue sections are known after planning)

@@ -24,6 +24,12 @@ CASES = {
     "small-mha-b4": (synth.Config("small-mha-b4", n_layers=2, hidden=512, n_q_heads=4, n_kv_heads=4, head_dim=128,
                                   ffn=1024, vocab=2048, batch=4, ctx=[1, 16, 33, 300], steps=3, seed=11,
                                   gain_range=(0.5, 1.5)), 3),
+    # head_dim 128, GQA group 4 (the 8B grouping), batch 2, contexts across several chunks
+    "small-gqa4-d128": (synth.Config("small-gqa4-d128", n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=2,
+                                     head_dim=128, ffn=1024, vocab=2048, batch=2, ctx=[200, 61], steps=3, seed=12), 3),
+    # head_dim 64 with the largest group the kernel takes (8 query heads per KV head)
+    "small-gqa8-d64": (synth.Config("small-gqa8-d64", n_layers=2, hidden=512, n_q_heads=16, n_kv_heads=2,
+                                    head_dim=64, ffn=1024, vocab=2048, batch=1, ctx=[150], steps=3, seed=13), 3),
 }
 
 
