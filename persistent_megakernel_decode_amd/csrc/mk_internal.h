@@ -26,7 +26,10 @@ constexpr int PIECE = 1024;            // bytes moved by one LDS-DMA instruction
 constexpr int SLOT_PIECES = 8;         // pieces per ring slot (== NC: one piece per compute wave)
 constexpr int SLOT = PIECE * SLOT_PIECES;
 constexpr int NSLOT = 16;              // 128 KB ring
-constexpr int LOAD_DEPTH = 4;          // slots in flight per loader wave before it marks the oldest
+#ifndef MK_LOAD_DEPTH
+#define MK_LOAD_DEPTH 4
+#endif
+constexpr int LOAD_DEPTH = MK_LOAD_DEPTH;          // slots in flight per loader wave before it marks the oldest
 constexpr int RED_FLOATS = 4096;       // 16 KB partial-sum / merge area
 constexpr int SCRATCH_FLOATS = 512;    // 2 KB small cross-wave scratch
 

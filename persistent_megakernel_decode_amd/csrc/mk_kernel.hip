@@ -47,8 +47,12 @@ constexpr int AUX_SC1 = 16;  // cache policy: agent-scope coherent
 __shared__ __attribute__((aligned(16))) u32x4 g_ring[NSLOT * SLOT / 16];
 __shared__ __attribute__((aligned(16))) float g_red[RED_FLOATS];
 __shared__ __attribute__((aligned(16))) float g_scr[SCRATCH_FLOATS];
-__shared__ u32 g_full[NSLOT];   // slot seq / NSLOT + 1 once the slot's bytes landed
-__shared__ u32 g_done[NSLOT];   // cumulative consumption count (NC per slot use)
+// Ring protocol: slots are numbered by a per-launch sequence number (slot seq lives in ring
+// position seq % NSLOT).  The loader publishes g_filled = the number of slots whose bytes have
+// landed; compute wave w publishes g_consumed[w] = the sequence number below which it will read
+// no slot again.  The loader may fill slot seq once seq < min_w g_consumed[w] + NSLOT.
+__shared__ u32 g_filled;
+__shared__ __attribute__((aligned(16))) u32 g_consumed[NC];
 __shared__ u32 g_bar;           // compute-wave barrier counter
 __shared__ u32 g_abort;         // set on watchdog expiry: every wave leaves
 __shared__ u32 g_bcast[4];
@@ -154,8 +158,10 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// LDS flags are read by whole waves and every lane sees the same word; readfirstlane tells the
+// compiler so, which keeps every spin loop (and everything carried around it) in scalar registers.
 __device__ __forceinline__ u32 lds_ld(const u32* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
 }
 __device__ __forceinline__ bool aborted() { return lds_ld(&g_abort) != 0; }
 
@@ -190,10 +196,10 @@ struct Watchdog {
     const uint64_t now = __builtin_amdgcn_s_memrealtime();
     if (t0 == 0) { t0 = now; return false; }
     if (now - t0 <= limit) return false;
-    if (lane_id() == 0) {
-      __hip_atomic_fetch_or(status, ST_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&g_abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
+    // every lane raises the (idempotent) flags: a lane-0 branch here gets merged into the
+    // caller's loop exit by the compiler, which turns every spin loop divergent
+    __hip_atomic_fetch_or(status, ST_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&g_abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     return true;
   }
 };
@@ -204,7 +210,7 @@ __device__ __forceinline__ bool cbar(const KArgs& A, u32& gen) {
   gen += NC;
   if (lane_id() == 0) __hip_atomic_fetch_add(&g_bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   Watchdog wd(A);
-  while (__hip_atomic_load(&g_bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < gen) {
+  while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(&g_bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < gen) {
     if (aborted() || wd.expired()) return false;
     __builtin_amdgcn_s_sleep(0);
   }
@@ -212,18 +218,18 @@ __device__ __forceinline__ bool cbar(const KArgs& A, u32& gen) {
 }
 
 // Wait until ring slot `seq` holds its bytes.  Returns false on abort.
-__device__ bool wait_full(const KArgs& A, u32 seq) {
-  const u32 pos = seq % NSLOT, want = seq / NSLOT + 1;
+__device__ __forceinline__ bool wait_full(const KArgs& A, u32 seq) {
   Watchdog wd(A);
-  while (lds_ld(&g_full[pos]) != want) {
+  while (lds_ld(&g_filled) <= seq) {
     if (aborted() || wd.expired()) return false;
     __builtin_amdgcn_s_sleep(0);
   }
   return true;
 }
-__device__ __forceinline__ void release_slot(u32 seq, u32 n) {
-  __builtin_amdgcn_s_waitcnt(MK_LGKMCNT0);  // this wave's reads of the slot are complete
-  if (lane_id() == 0) __hip_atomic_fetch_add(&g_done[seq % NSLOT], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+// Compute wave w will read no ring slot below `upto` again.  Monotonic per wave.
+__device__ __forceinline__ void release_upto(u32 w, u32 upto) {
+  __builtin_amdgcn_s_waitcnt(MK_LGKMCNT0);  // this wave's reads of those slots are complete
+  if (lane_id() == 0) __hip_atomic_store(&g_consumed[w], upto, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // ------------------------------------------------------------------ per-row validity
@@ -278,31 +284,55 @@ struct ItemCache {
     if (i != item) { it = attn_item(A, i, pps); item = i; }
     return it;
   }
+  __device__ void restate() {  // see compute(): the fields are uniform
+    item = __builtin_amdgcn_readfirstlane(item);
+    it.b = __builtin_amdgcn_readfirstlane(it.b);
+    it.kvh = __builtin_amdgcn_readfirstlane(it.kvh);
+    it.p0 = __builtin_amdgcn_readfirstlane(it.p0);
+    it.p1 = __builtin_amdgcn_readfirstlane(it.p1);
+    it.n_b = __builtin_amdgcn_readfirstlane(it.n_b);
+    it.first_item = __builtin_amdgcn_readfirstlane(it.first_item);
+    it.valid = __builtin_amdgcn_readfirstlane((int)it.valid) != 0;
+  }
 };
 
 __device__ __forceinline__ int attn_pps(int d) { return 4096 / (2 * d); }  // positions per ring slot
 
 // ------------------------------------------------------------------ loader
 
-// Publish "slot `seq` holds its bytes" (after the matching s_waitcnt vmcnt).  Written as an opaque
-// LDS store for the same reason as lds_ld_loader: the compiler would otherwise drain every DMA first.
-__device__ __forceinline__ void mark_full(u32 seq) {
-  const u32 addr = (u32)(uintptr_t)(__attribute__((address_space(3))) u32*)&g_full[seq % NSLOT];
-  const u32 v = seq / NSLOT + 1;
-  asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
+// Publish "slots below n hold their bytes" (after the matching s_waitcnt vmcnt).  Written as an
+// opaque LDS store for the same reason as lds_ld_loader: the compiler would otherwise drain every
+// DMA first.  No wait: LDS operations of a wave complete in order.
+__device__ __forceinline__ void publish_filled(u32 n) {
+  const u32 addr = (u32)(uintptr_t)(__attribute__((address_space(3))) u32*)&g_filled;
+  asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(n) : "memory");
 }
+// Smallest g_consumed over the compute waves: ring slots below it are free.
+__device__ __forceinline__ u32 min_consumed() {
+  const u32 addr = (u32)(uintptr_t)(__attribute__((address_space(3))) u32*)&g_consumed[0];
+  u32x4 a, b;
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+               : "=v"(a), "=v"(b) : "v"(addr) : "memory");
+  const u32 m = min(min(min(a.x, a.y), min(a.z, a.w)), min(min(b.x, b.y), min(b.z, b.w)));
+  return __builtin_amdgcn_readfirstlane(m);
+}
+static_assert(NC == 8, "min_consumed reads eight counters");
 
 // Wait until the oldest of n in-flight slots has landed (8 DMA instructions per slot).
+// n slots in flight (8 DMA instructions each, issued in order): wait until the oldest is complete
 __device__ __forceinline__ void wait_oldest(u32 n) {
   switch (n) {
     case 1: __builtin_amdgcn_s_waitcnt(MK_VMCNT(0)); break;
     case 2: __builtin_amdgcn_s_waitcnt(MK_VMCNT(8)); break;
     case 3: __builtin_amdgcn_s_waitcnt(MK_VMCNT(16)); break;
     case 4: __builtin_amdgcn_s_waitcnt(MK_VMCNT(24)); break;
-    default: __builtin_amdgcn_s_waitcnt(MK_VMCNT(32)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(MK_VMCNT(32)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(MK_VMCNT(40)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(MK_VMCNT(48)); break;
+    default: __builtin_amdgcn_s_waitcnt(MK_VMCNT(56)); break;
   }
 }
-static_assert(LOAD_DEPTH == 4, "wait_oldest covers LOAD_DEPTH + 1 in-flight slots");
+static_assert(LOAD_DEPTH >= 1 && LOAD_DEPTH <= 7, "wait_oldest covers LOAD_DEPTH + 1 in-flight slots (vmcnt <= 63)");
 
 // Every loader address is a uniform (scalar) base plus the lane's fixed 16-byte offset, so a
 // DMA costs only scalar work: no per-lane address arithmetic on the issue path.
@@ -458,7 +488,7 @@ __device__ u32 op_slots(const KArgs& A, const Op& o, ItemCache& ic) {
 }
 
 __device__ __forceinline__ void loader(const KArgs& A, u32 q0, u32 q1) {
-  u32 seq = 0, marked = 0;
+  u32 seq = 0, marked = 0, limit = NSLOT;  // slots below `limit` may be filled
   const u32 lane16 = lane_id() * 16;
   ItemCache ic;
   PageWindow pw;
@@ -476,34 +506,38 @@ __device__ __forceinline__ void loader(const KArgs& A, u32 q0, u32 q1) {
     if (o.opcode == OP_ATTN || o.opcode == OP_DELTA) Ld = sload(A.layers + o.layer);
     if (o.opcode == OP_ATTN) it = ic.get(A, o.row0, attn_pps(A.d));
     for (u32 s = 0; s < ns; ++s) {
-      const u32 pos = seq % NSLOT, round = seq / NSLOT;
-      Watchdog wd(A);
-      while (lds_ld_loader(&g_done[pos]) < round * NC) {  // slot still holds unconsumed bytes
-        if (marked < seq) {
-          wait_oldest(seq - marked);
-          mark_full(marked++);
-        } else {
-          if (aborted_loader() || wd.expired()) {
-            __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));
-            return;
+      if (seq >= limit) {  // the ring looks full: publish what has landed, then re-read the consumers
+        Watchdog wd(A);
+        while (true) {
+          if (marked < seq) {
+            wait_oldest(seq - marked);
+            publish_filled(++marked);
           }
-          __builtin_amdgcn_s_sleep(1);
+          limit = min_consumed() + NSLOT;
+          if (seq < limit) break;
+          if (marked == seq) {
+            if (aborted_loader() || wd.expired()) {
+              __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));
+              return;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
         }
       }
-      u32x4* dst = g_ring + pos * (SLOT / 16);
+      u32x4* dst = g_ring + (seq % NSLOT) * (SLOT / 16);
       if (o.opcode == OP_GEMV) issue_gemv(gsg, s, nrt, lgp, real_pieces, lane16, dst);
       else if (o.opcode == OP_ATTN) issue_attn(A, Ld, it, s, al, pw, lane16, dst);
       else issue_delta(A, Ld, o.row0, s, lane16, dst);
       ++seq;
       if (seq - marked > LOAD_DEPTH) {
         __builtin_amdgcn_s_waitcnt(MK_VMCNT(8 * LOAD_DEPTH));
-        mark_full(marked++);
+        publish_filled(++marked);
       }
     }
   }
   while (marked < seq) {
     wait_oldest(seq - marked);
-    mark_full(marked++);
+    publish_filled(++marked);
   }
 }
 
@@ -660,10 +694,7 @@ __device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32&
 #pragma unroll
     for (int i = 0; i < GEMV_BATCH; ++i)
       if ((u32)i < nb) wv[i] = g_ring[((seq + i) % NSLOT) * (SLOT / 16) + w * 64 + lane];
-    __builtin_amdgcn_s_waitcnt(MK_LGKMCNT0);
-    if (lane == 0)
-      for (u32 i = 0; i < nb; ++i)
-        __hip_atomic_fetch_add(&g_done[(seq + i) % NSLOT], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    release_upto(w, seq + nb);
     if constexpr (B >= 4) {
       // wide batches: one running sum per sequence, reduced four sequences at a time at each row end
 #pragma unroll
@@ -925,6 +956,7 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   for (int g = 0; g < GMAX; ++g)
 #pragma unroll
     for (int e = 0; e < DPL; ++e) ov[g][e] = 0.0f;
+  release_upto(w, seq0 + min(w, ns));  // slots before this wave's first belong to other waves
   for (u32 s = w; s < ns; s += NC) {
     const u32 sq = seq0 + s;
     if (!wait_full(A, sq)) return false;
@@ -1014,8 +1046,9 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
         for (int e = 0; e < DPL; ++e) ov[g][e] += pg * vv[e];
       }
     }
-    release_slot(sq, NC);
+    release_upto(w, seq0 + min(s + NC, ns));
   }
+  release_upto(w, seq0 + ns);
   if (!cbar(A, gen)) return false;  // every wave is done with the query / new-token areas
 
   // merge the waves of this workgroup
@@ -1059,7 +1092,7 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
     g_bcast[0] = (prev == (u32)it.n_b - 1) ? 1u : 0u;
   }
   if (!cbar(A, gen)) return false;
-  if (g_bcast[0]) {  // last chunk of (b, kvh): log-sum-exp merge of all its chunks
+  if (lds_ld(&g_bcast[0])) {  // last chunk of (b, kvh): log-sum-exp merge of all its chunks
     const int tid = (int)(w * 64 + lane);
     const float* part0 = (const float*)Ld.part + (size_t)it.first_item * GMAX * (D + 2);
     const size_t cstride = (size_t)A.Hkv * GMAX * (D + 2);  // floats between chunks of (b, kvh)
@@ -1127,9 +1160,12 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
     return silu(acc);
   };
 
-  for (u32 s = 0; s < (u32)NSL; ++s, ++seq) {
-    if (s % NC != w) continue;
-    if (!wait_full(A, seq)) return false;
+  const u32 seq0 = seq;
+  seq += NSL;
+  release_upto(w, seq0 + min(w, (u32)NSL));
+  for (u32 s = w; s < (u32)NSL; s += NC) {
+    const u32 sq = seq0 + s;
+    if (!wait_full(A, sq)) return false;
     float q[DPL], k[DPL], xq[DPL], xk[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
@@ -1141,9 +1177,9 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
 #pragma unroll
     for (int e = 0; e < DPL; ++e) { nq += q[e] * q[e]; nk += k[e] * k[e]; }
     nq = wave_sum(nq); nk = wave_sum(nk);
-    const float sq = 1.0f / sqrtf(nq + 1e-6f) / sqrtf((float)DK), sk = 1.0f / sqrtf(nk + 1e-6f);
+    const float rq = 1.0f / sqrtf(nq + 1e-6f) / sqrtf((float)DK), rk = 1.0f / sqrtf(nk + 1e-6f);
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) { q[e] *= sq; k[e] *= sk; }
+    for (int e = 0; e < DPL; ++e) { q[e] *= rq; k[e] *= rk; }
     const float gate = 1.0f / (1.0f + __expf(-ld_sc1(gts + h)));
     const float beta = 1.0f / (1.0f + __expf(-ld_sc1(gts + A.nh + h)));
     // value channels of this slot's rows: lane r < RPS computes row r's conv
@@ -1151,7 +1187,7 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
     const int vch = 2 * A.nh * DK + h * A.dv + j0 + (int)lane;
     float vx = 0.0f, vval = 0.0f;
     if ((int)lane < RPS) vval = conv(vch, &vx);
-    const float* srows = (const float*)(g_ring + (seq % NSLOT) * (SLOT / 16));
+    const float* srows = (const float*)(g_ring + (sq % NSLOT) * (SLOT / 16));
     float* sdst = (float*)Ld.delta_state + (((size_t)bh * A.dv + j0) * DK);
     for (int r = 0; r < RPS; ++r) {
       float sv[DPL];
@@ -1183,8 +1219,9 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
       st[W - 2] = vx;
     }
     (void)xq; (void)xk;
-    release_slot(seq, NC);
+    release_upto(w, seq0 + min(s + NC, (u32)NSL));
   }
+  release_upto(w, seq0 + NSL);
   // q / k conv states: written once all blocks of (b, h) have read them (ticket)
   __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));
   if (!cbar(A, gen)) return false;
@@ -1194,7 +1231,7 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
     g_bcast[0] = (prev == ncb - 1) ? 1u : 0u;
   }
   if (!cbar(A, gen)) return false;
-  if (g_bcast[0]) {
+  if (lds_ld(&g_bcast[0])) {
     if (ok) {
       for (int t = (int)(w * 64 + lane); t < 2 * DK; t += NC * 64) {
         const int c = t < DK ? h * DK + t : A.nh * DK + h * DK + (t - DK);
@@ -1230,6 +1267,13 @@ __device__ __forceinline__ void compute(const KArgs& A, u32 q0, u32 q1, u32 w) {
       case OP_DELTA: alive = A.dk == 128 ? op_delta<128>(A, o, w, seq, gen) : op_delta<64>(A, o, w, seq, gen); break;
       default: break;
     }
+    // Every value carried from op to op is wave-uniform.  The ops' lane-0 branches and early
+    // exits make the compiler's divergence analysis lose track of that, which would demote the
+    // carried state (and every loop around it) to vector registers; restate it.
+    alive = __builtin_amdgcn_readfirstlane((int)alive) != 0;
+    seq = __builtin_amdgcn_readfirstlane(seq);
+    gen = __builtin_amdgcn_readfirstlane(gen);
+    ic.restate();
     if (!alive || aborted()) return;
     __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));  // this wave's outputs are complete
     if (!cbar(A, gen)) return;
@@ -1240,7 +1284,8 @@ __device__ __forceinline__ void compute(const KArgs& A, u32 q0, u32 q1, u32 w) {
 template <int B>
 __device__ __forceinline__ void megakernel_body(const KArgs& A) {
   const u32 wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index: uniform per wave
-  if (threadIdx.x < NSLOT) { g_full[threadIdx.x] = 0; g_done[threadIdx.x] = 0; }
+  if (threadIdx.x < NC) g_consumed[threadIdx.x] = 0;
+  if (threadIdx.x == 0) g_filled = 0;
   if (threadIdx.x == 0) { g_bar = 0; g_abort = 0; }
   __syncthreads();
   const u32 q0 = A.queue_off[blockIdx.x], q1 = A.queue_off[blockIdx.x + 1];
