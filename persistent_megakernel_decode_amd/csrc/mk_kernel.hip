@@ -369,24 +369,45 @@ __device__ __forceinline__ const char* gemv_row(const GemvSeg& g, u32 rl) {
   return (const char*)(base + (uint64_t)r * g.rowbytes);
 }
 
+// 8 KB of one row into a slot: two address registers; each DMA's immediate offset moves the global
+// and the LDS address together, so a slot costs two M0 values and eight loads.
+__device__ __forceinline__ void dma_slot(const char* row, u32 lane16, u32x4* dst) {
+  const char* p0 = row + lane16;
+  const char* p1 = row + 4096 + lane16;
+  auto* l0 = (__attribute__((address_space(3))) void*)dst;
+  auto* l1 = (__attribute__((address_space(3))) void*)(dst + 256);
+  __builtin_amdgcn_global_load_lds(p0, l0, 16, 0, AUX_NT);
+  __builtin_amdgcn_global_load_lds(p0, l0, 16, 1024, AUX_NT);
+  __builtin_amdgcn_global_load_lds(p0, l0, 16, 2048, AUX_NT);
+  __builtin_amdgcn_global_load_lds(p0, l0, 16, 3072, AUX_NT);
+  __builtin_amdgcn_global_load_lds(p1, l1, 16, 0, AUX_NT);
+  __builtin_amdgcn_global_load_lds(p1, l1, 16, 1024, AUX_NT);
+  __builtin_amdgcn_global_load_lds(p1, l1, 16, 2048, AUX_NT);
+  __builtin_amdgcn_global_load_lds(p1, l1, 16, 3072, AUX_NT);
+}
+static_assert(SLOT == 8192 && SLOT_PIECES == 8 && PIECE == 1024, "dma_slot moves one 8 KB slot");
+
 // One ring slot of the GEMV stream.  With ppr >= 8 a slot is 8 consecutive pieces of one row
-// (one row lookup per slot); with ppr < 8 it is 8 / ppr whole rows.
-__device__ void issue_gemv(const GemvSeg& gsg, u32 s, u32 nrt, u32 lgp, u32 real_pieces, u32 lane16, u32x4* dst) {
+// (one row lookup per slot); with ppr < 8 it is 8 / ppr whole rows.  Pieces past the row's end
+// stream row 0 of the first weight (finite bytes whose products meet zero inputs); a partial last
+// piece reads only the lanes inside the row.
+__device__ __forceinline__ void issue_gemv(const GemvSeg& gsg, u32 s, u32 nrt, u32 lgp, u32 lane16, u32x4* dst) {
   const u32 rowbytes = gsg.rowbytes;
   const char* dummy = (const char*)gsg.wa;
   if (lgp >= 3) {
     const u32 lgm = lgp - 3;
     const u32 rl = s >> lgm, kp0 = (s & ((1u << lgm) - 1)) << 3;
-    if (rl >= nrt) {
-#pragma unroll
-      for (int i = 0; i < SLOT_PIECES; ++i) dma_at(dummy, lane16, dst + i * 64);
+    const u32 nfull = rowbytes / PIECE;
+    if (rl < nrt && kp0 + SLOT_PIECES <= nfull) {  // the common case: eight full pieces
+      dma_slot(gemv_row(gsg, rl) + kp0 * PIECE, lane16, dst);
       return;
     }
-    const char* row = gemv_row(gsg, rl) + kp0 * PIECE;
-    const u32 nreal = real_pieces > kp0 ? real_pieces - kp0 : 0u;  // full pieces: rowbytes % 1 KB == 0 here
+    const char* row = rl < nrt ? gemv_row(gsg, rl) : dummy;
 #pragma unroll
     for (int i = 0; i < SLOT_PIECES; ++i) {
-      if ((u32)i < nreal) dma_at(row + i * PIECE, lane16, dst + i * 64);
+      const u32 off = (kp0 + i) * PIECE;
+      if (rl < nrt && off + PIECE <= rowbytes) dma_at(row + off, lane16, dst + i * 64);
+      else if (rl < nrt && off < rowbytes) dma_at(row, off + lane16 < rowbytes ? off + lane16 : 0u, dst + i * 64);
       else dma_at(dummy, lane16, dst + i * 64);
     }
     return;
@@ -501,7 +522,6 @@ __device__ __forceinline__ void loader(const KArgs& A, u32 q0, u32 q1) {
     AttnItem it{};
     const u32 nrt = o.epi == EPI_SWIGLU ? 2 * o.nrows : o.nrows;
     const u32 lgp = o.opcode == OP_GEMV ? (u32)__builtin_ctz(o.ppr) : 0u;
-    const u32 real_pieces = (o.K + PIECE_ELEMS - 1) / PIECE_ELEMS;
     const GemvSeg gsg = gemv_seg(o);
     if (o.opcode == OP_ATTN || o.opcode == OP_DELTA) Ld = sload(A.layers + o.layer);
     if (o.opcode == OP_ATTN) it = ic.get(A, o.row0, attn_pps(A.d));
@@ -525,7 +545,7 @@ __device__ __forceinline__ void loader(const KArgs& A, u32 q0, u32 q1) {
         }
       }
       u32x4* dst = g_ring + (seq % NSLOT) * (SLOT / 16);
-      if (o.opcode == OP_GEMV) issue_gemv(gsg, s, nrt, lgp, real_pieces, lane16, dst);
+      if (o.opcode == OP_GEMV) issue_gemv(gsg, s, nrt, lgp, lane16, dst);
       else if (o.opcode == OP_ATTN) issue_attn(A, Ld, it, s, al, pw, lane16, dst);
       else issue_delta(A, Ld, o.row0, s, lane16, dst);
       ++seq;
