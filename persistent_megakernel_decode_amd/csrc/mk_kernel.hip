@@ -106,7 +106,14 @@ __device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even (f
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-__device__ __forceinline__ u32 lane_id() { return threadIdx.x & 63u; }
+// Lane index, recomputed at every use: an opaque instruction pair the compiler cannot hoist, so
+// lane-derived addresses are not kept alive across the whole persistent loop (which would crowd
+// out the registers the ops need).
+__device__ __forceinline__ u32 lane_id() {
+  u32 r;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
+  return r;
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dppf(float v) {
@@ -1113,29 +1120,40 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   }
   if (!cbar(A, gen)) return false;
   if (lds_ld(&g_bcast[0])) {  // last chunk of (b, kvh): log-sum-exp merge of all its chunks
-    const int tid = (int)(w * 64 + lane);
+    // Loads are issued ahead of their use: thread t owns output (head t / D, dim t % D) and loads
+    // that output of 16 chunks at a time; threads t < n_b * G also fetch one (m, l) pair for the
+    // LDS table every thread reads, in the same round trip as the first 16 outputs.
+    static_assert(GMAX * D <= NC * 64, "one merged output per thread");
+    const int tid = (int)(w * 64 + lane), nb = it.n_b;
     const float* part0 = (const float*)Ld.part + (size_t)it.first_item * GMAX * (D + 2);
     const size_t cstride = (size_t)A.Hkv * GMAX * (D + 2);  // floats between chunks of (b, kvh)
-    float* ml = g_red;                                         // [n_b][G][m, l]
-    for (int t = tid; t < it.n_b * G; t += NC * 64) {
-      const float* pc = part0 + (size_t)(t / G) * cstride + (t % G) * (D + 2);
-      ml[2 * t] = ld_sc1(pc);
-      ml[2 * t + 1] = ld_sc1(pc + 1);
+    const bool has_ml = tid < nb * G, has_o = tid < G * D;
+    const int g = has_o ? tid / D : 0, dim = tid % D;
+    float mv = 0.0f, lv = 0.0f;
+    if (has_ml) {
+      const float* pc = part0 + (size_t)(tid / G) * cstride + (tid % G) * (D + 2);
+      mv = ld_sc1(pc);
+      lv = ld_sc1(pc + 1);
     }
-    if (!cbar(A, gen)) return false;
-    for (int t = tid; t < G * D; t += NC * 64) {
-      const int g = t / D, dim = t % D;
-      float M = -INFINITY;
-      for (int c = 0; c < it.n_b; ++c) M = fmaxf(M, ml[2 * (c * G + g)]);
-      float den = 0.0f, num = 0.0f;
-      for (int c0 = 0; c0 < it.n_b; c0 += 16) {  // 16 chunks' outputs in flight at once
-        float oc[16];
+    const float* po = part0 + g * (D + 2) + 2 + dim;
+    float oc[16];
 #pragma unroll
-        for (int k = 0; k < 16; ++k)
-          oc[k] = c0 + k < it.n_b ? ld_sc1(part0 + (size_t)(c0 + k) * cstride + g * (D + 2) + 2 + dim) : 0.0f;
+    for (int k = 0; k < 16; ++k) oc[k] = has_o && k < nb ? ld_sc1(po + (size_t)k * cstride) : 0.0f;
+    float* ml = g_red;  // [n_b][G][m, l]
+    if (has_ml) { ml[2 * tid] = mv; ml[2 * tid + 1] = lv; }
+    if (!cbar(A, gen)) return false;
+    if (has_o) {
+      float M = -INFINITY;
+      for (int c = 0; c < nb; ++c) M = fmaxf(M, ml[2 * (c * G + g)]);
+      float den = 0.0f, num = 0.0f;
+      for (int c0 = 0; c0 < nb; c0 += 16) {
+        if (c0 > 0) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) oc[k] = c0 + k < nb ? ld_sc1(po + (size_t)(c0 + k) * cstride) : 0.0f;
+        }
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-          if (c0 + k < it.n_b) {
+          if (c0 + k < nb) {
             const float f = __expf(ml[2 * ((c0 + k) * G + g)] - M);
             den += f * ml[2 * ((c0 + k) * G + g) + 1];
             num += f * oc[k];
