@@ -69,6 +69,7 @@ struct mk_ctx {
   hipStream_t last_stream = nullptr;
   mk_status sticky = MK_OK;
   const void* kernel = nullptr;
+  bool plain_launch = false;
   std::mutex busy;
 };
 
@@ -261,6 +262,11 @@ mk_status mk_create(const mk_model_desc* desc, const mk_weights* w, const mk_kv_
   double ms = 2000.0;
   if (const char* s = getenv("MK_WATCHDOG_MS")) ms = std::max(1.0, atof(s));  // diagnostic only
   A.spin_limit = (uint64_t)(ms * 1e5);  // s_memrealtime runs at 100 MHz
+  // Diagnostic: MK_PLAIN_LAUNCH=1 launches with hipLaunchKernel instead of the cooperative launch
+  // (for tools that cannot follow cooperative dispatches).  mk_create has already checked that one
+  // workgroup per CU is resident; should some workgroup still not be scheduled, the spin-wait
+  // watchdog ends every wait and the step reports MK_ERR_TIMEOUT.
+  if (const char* s = getenv("MK_PLAIN_LAUNCH")) ctx->plain_launch = atoi(s) != 0;
   *out = ctx;
   return MK_OK;
 }
@@ -298,8 +304,10 @@ mk_status mk_decode_step(mk_ctx* ctx, const int32_t* tokens, const int32_t* posi
   A.batch = batch;
   A.epoch = ctx->epoch + 1;
   void* kargs[] = {&A};
-  hipError_t e = hipLaunchCooperativeKernel(ctx->kernel, dim3(ctx->plan.n_cus), dim3(mk::NTHREADS), kargs, 0, s);
-  if (e != hipSuccess) return hip_fail(e, "hipLaunchCooperativeKernel");
+  hipError_t e = ctx->plain_launch
+                     ? hipLaunchKernel(ctx->kernel, dim3(ctx->plan.n_cus), dim3(mk::NTHREADS), kargs, 0, s)
+                     : hipLaunchCooperativeKernel(ctx->kernel, dim3(ctx->plan.n_cus), dim3(mk::NTHREADS), kargs, 0, s);
+  if (e != hipSuccess) return hip_fail(e, ctx->plain_launch ? "hipLaunchKernel" : "hipLaunchCooperativeKernel");
   ctx->epoch += 1;
   ctx->last_stream = s;
   return MK_OK;
