@@ -1,0 +1,29 @@
+"""GPU parity at the full workload shapes, in the launch configuration the bench times.
+
+The oracle computes every logit of a full decode step (OpenMP over rows), so each case compares
+whole steps element by element: logits within 1e-2 max relative error, identical greedy ids where
+the oracle's top-2 gap exceeds 1e-2, and per-layer mid-states within 2e-3 normwise.  Two or three
+steps per case keep the oracle's share to seconds.
+"""
+import pytest
+
+import synth
+from gpu_harness import run_parity, say
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "0.6b": (synth.CONFIGS["0.6b"], 3),
+    "hybrid": (synth.CONFIGS["hybrid"], 2),
+    "8b": (synth.CONFIGS["8b"], 2),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_parity_full_size(case):
+    cfg, steps = CASES[case]
+    rep = run_parity(cfg, steps)
+    say(f"[{case}] {rep.steps} steps, worst logits rel {rep.worst_rel:.2e}, worst mid {rep.worst_mid:.2e}, "
+        f"greedy {rep.greedy_agree}/{rep.greedy_checked}")
+    assert not rep.failures, rep.failures
+    assert rep.steps == steps
