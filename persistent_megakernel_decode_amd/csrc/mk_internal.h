@@ -42,7 +42,7 @@ constexpr int PIECE_ELEMS = PIECE / 2; // bf16 weights per piece row-segment
 constexpr int MAX_M = 4;               // pieces of one row per compute wave (rows up to 16384 elements)
 constexpr int GEMV_BATCH = 4;          // ring slots a compute wave takes per wait
 
-enum Opcode : uint8_t { OP_NOP = 0, OP_EMBED = 1, OP_GEMV = 2, OP_ATTN = 3, OP_DELTA = 4 };
+enum Opcode : uint8_t { OP_NOP = 0, OP_EMBED = 1, OP_GEMV = 2, OP_ATTN = 3, OP_DELTA = 4, OP_MMV = 5 };
 enum Epi : uint8_t { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
 
 constexpr int16_t NO_STAGE = -1;
@@ -55,6 +55,14 @@ constexpr int16_t NO_STAGE = -1;
 // [0, b1) start at W (already offset to the op's first row) and stream rows
 // [b1, ...) start at W2.  EPI_SWIGLU streams the op's gate rows (W) then the
 // same rows of the up projection (W2, b1 = nrows) and writes silu(gate) * up.
+//
+// An MMV op (batch 8: the projection is a skinny GEMM on the matrix cores) covers the same row
+// space in tiles of 16 rows (SWIGLU: gate and up tiles interleaved, gate tile i = 2i, up tile
+// i = 2i + 1), at most MMV_TILES tiles, and streams K in segments of MMV_KSEG inputs: ring slot
+// s holds tile s % ntiles of segment s / ntiles (16 rows x 256 inputs, 8 KB); `ppr` holds the
+// number of segments K / MMV_KSEG.
+constexpr int MMV_KSEG = 256;
+constexpr int MMV_TILES = 8;
 struct alignas(16) Op {
   uint8_t opcode;
   uint8_t epi;

@@ -497,6 +497,29 @@ __device__ void issue_attn(const KArgs& A, const LayerDesc& Ld, const AttnItem& 
   (void)lane16;
 }
 
+// Matrix-core GEMV stream: slot s = 16 rows (tile s % nt) x 256 inputs (segment s / nt).  DMA j
+// carries input block j (32 inputs) of the 16 rows: lane i fills row i / 4, 16-byte chunk
+// position i % 4, which holds chunk (i % 4) ^ ((row / 4) % 4) of the block -- so the 16 rows a
+// matrix-core operand read touches fall in distinct LDS banks.  The immediate offset of DMA j
+// moves the global address by 64 j; M0 is set 64 j lower so the LDS side lands at 1024 j.
+// Rows past the op stream the tile's first row again (bytes that are never stored).
+__device__ __forceinline__ void issue_mmv(const GemvSeg& gsg, u32 s, u32 nt, u32 nrows, bool swiglu, u32 lane,
+                                          u32x4* dst) {
+  const u32 kseg = s / nt, t = s - kseg * nt;
+  const u32 lrow = lane >> 2;
+  const u32 chunk = (lane & 3) ^ ((lrow >> 2) & 3);
+  const u32 half0 = swiglu ? (t & 1) * nrows : 0u;     // stream row of the tile's half
+  const u32 trow = swiglu ? 16 * (t >> 1) : 16 * t;    // first row of the tile within its half
+  const u32 r = trow + lrow < nrows ? trow + lrow : trow;
+  const char* vaddr = gemv_row(gsg, half0 + r) + (size_t)kseg * (MMV_KSEG * 2) + chunk * 16;
+  char* lds = (char*)dst;
+#define MK_MMV_DMA(j) __builtin_amdgcn_global_load_lds(vaddr, (__attribute__((address_space(3))) void*)(lds + (j) * 960), 16, (j) * 64, AUX_NT)
+  MK_MMV_DMA(0); MK_MMV_DMA(1); MK_MMV_DMA(2); MK_MMV_DMA(3);
+  MK_MMV_DMA(4); MK_MMV_DMA(5); MK_MMV_DMA(6); MK_MMV_DMA(7);
+#undef MK_MMV_DMA
+}
+static_assert(MMV_KSEG == 256 && SLOT == 16 * MMV_KSEG * 2, "an MMV slot is 16 rows x 256 bf16");
+
 // Delta stream: rows of S^T (fp32) of one column block, contiguous.
 __device__ void issue_delta(const KArgs& A, const LayerDesc& Ld, u32 item, u32 s, u32 lane16, u32x4* dst) {
   const u32 ncb = (u32)A.dv / 32, cb = item % ncb, bh = item / ncb;  // bh = b * nh + h
@@ -530,6 +553,7 @@ __device__ __forceinline__ void loader(const KArgs& A, u32 q0, u32 q1) {
     const u32 nrt = o.epi == EPI_SWIGLU ? 2 * o.nrows : o.nrows;
     const u32 lgp = o.opcode == OP_GEMV ? (u32)__builtin_ctz(o.ppr) : 0u;
     const GemvSeg gsg = gemv_seg(o);
+    const u32 mmv_nt = (o.epi == EPI_SWIGLU ? 2u : 1u) * ((o.nrows + 15) / 16);
     if (o.opcode == OP_ATTN || o.opcode == OP_DELTA) Ld = sload(A.layers + o.layer);
     if (o.opcode == OP_ATTN) it = ic.get(A, o.row0, attn_pps(A.d));
     for (u32 s = 0; s < ns; ++s) {
@@ -553,6 +577,7 @@ __device__ __forceinline__ void loader(const KArgs& A, u32 q0, u32 q1) {
       }
       u32x4* dst = g_ring + (seq % NSLOT) * (SLOT / 16);
       if (o.opcode == OP_GEMV) issue_gemv(gsg, s, nrt, lgp, lane16, dst);
+      else if (o.opcode == OP_MMV) issue_mmv(gsg, s, mmv_nt, o.nrows, o.epi == EPI_SWIGLU, lane16 >> 4, dst);
       else if (o.opcode == OP_ATTN) issue_attn(A, Ld, it, s, al, pw, lane16, dst);
       else issue_delta(A, Ld, o.row0, s, lane16, dst);
       ++seq;
@@ -837,13 +862,7 @@ __device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32&
   return true;
 }
 
-// ------------------------------------------------------------------ ATTENTION (split-KV + merge)
-// One item = (sequence b, KV head, position chunk).  The G query heads sharing the KV head are
-// processed together.  Scores come from the matrix cores: Q (G heads, split into bf16 hi + lo so
-// the product keeps fp32 accuracy) times K^T, 16 positions per 16x16x32 tile.  Each compute wave
-// runs an online softmax over its ring slots and accumulates P V on the vector ALUs; the waves are
-// merged in LDS, the chunk's (m, l, o) partial goes to global memory, and the last chunk of
-// (b, kvh) to finish (a ticket) merges all chunks with the log-sum-exp rule.
+// ------------------------------------------------------------------ matrix-core and lane helpers
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -879,6 +898,146 @@ __device__ __forceinline__ void split_bf16x8(const float* x, u32x4& hi, u32x4& l
   lo = u32x4{l[0], l[1], l[2], l[3]};
 }
 
+// ------------------------------------------------------------------ MATRIX-CORE GEMV (batch 8)
+// With eight sequences a projection is a skinny GEMM: each 16-row tile is multiplied on the matrix
+// cores (16x16x32 bf16) by the 8 input columns (split into bf16 hi + lo, so the products keep fp32
+// accuracy).  Wave w takes input block w of every ring slot (k-outer: all tiles of one 256-input
+// segment, then the next segment) and keeps one 16x16 accumulator per tile; the eight waves'
+// partial sums are added in LDS, four tiles per pass.  RMSNorm factors out of the sum: the tiles
+// multiply x * gain, each lane accumulates x^2 on the side, and the epilogue scales by
+// (mean x^2 + eps)^-1/2.
+template <int B>
+__device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
+  static_assert(B <= 8 && NC == 8, "one pass holds 8 waves x 4 tiles x 16 rows x 8 columns");
+  static_assert(NC * 4 * 16 * 8 <= RED_FLOATS, "MMV partial-sum area");
+  const u32 lane = lane_id();
+  const bool swiglu = o.epi == EPI_SWIGLU;
+  const u32 nrows = o.nrows, ntg = (nrows + 15) / 16, nt = swiglu ? 2 * ntg : ntg, nks = o.ppr;
+  const u32 col = lane & 15, kq = lane >> 4;  // operand row / output column, and k-chunk of the lane
+  const bool cval = col < (u32)B;
+  const u32 aoff = w * 1024 + col * 64 + ((kq ^ ((col >> 2) & 3)) * 16);  // this lane's A bytes in a slot
+  const float* xin = (const float*)o.in + (size_t)(cval ? col : 0) * o.ld_in;
+  const uint16_t* gm = (const uint16_t*)o.gamma;
+
+  f32x4 acc[MMV_TILES];
+#pragma unroll
+  for (int t = 0; t < MMV_TILES; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float ssq = 0.0f;
+
+  // this lane's inputs of segment ks: x[col][ks*256 + 32 w + 8 kq .. + 8] and their gains
+  auto fetch = [&](u32 ks, float* xv, u32x4& gv) {
+    const u32 k0 = ks * MMV_KSEG + w * 32 + kq * 8;
+    if (cval && ks < nks) ld8_sc1(xin + k0, xv);
+    else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[e] = 0.0f;
+    }
+    gv = (o.norm && ks < nks) ? *(const u32x4*)(gm + k0) : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  };
+  auto consume = [&](const float* xv, const u32x4& gv) -> bool {
+    const float g[8] = {bflo(gv.x), bfhi(gv.x), bflo(gv.y), bfhi(gv.y), bflo(gv.z), bfhi(gv.z), bflo(gv.w), bfhi(gv.w)};
+    float xg[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ssq += xv[e] * xv[e];
+      xg[e] = xv[e] * g[e];
+    }
+    u32x4 hi, lo;
+    split_bf16x8(xg, hi, lo);
+    const bf16x8 bh = __builtin_bit_cast(bf16x8, hi), bl = __builtin_bit_cast(bf16x8, lo);
+    if (!wait_full(A, seq + nt - 1)) return false;
+#pragma unroll
+    for (int t = 0; t < MMV_TILES; ++t) {
+      if ((u32)t < nt) {
+        const char* slot = (const char*)(g_ring + ((seq + t) % NSLOT) * (SLOT / 16));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot + aoff));
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[t], 0, 0, 0);
+      }
+    }
+    release_upto(w, seq + nt);
+    seq += nt;
+    return true;
+  };
+
+  // segments two at a time, the inputs of each fetched two segments ahead
+  float xa[8], xb[8];
+  u32x4 ga, gb;
+  fetch(0, xa, ga);
+  fetch(1, xb, gb);
+  for (u32 ks = 0; ks < nks; ks += 2) {
+    if (!consume(xa, ga)) return false;
+    fetch(ks + 2, xa, ga);
+    if (ks + 1 < nks) {
+      if (!consume(xb, gb)) return false;
+      fetch(ks + 3, xb, gb);
+    }
+  }
+
+  // per-column sum of squares: lanes col, col + 16, col + 32, col + 48 of every wave
+  const float ss = add_swap32(add_swap16(ssq));
+  if (lane < 16) g_scr[w * 16 + lane] = ss;
+  const u32 tid = w * 64 + lane;
+#pragma unroll
+  for (int pp = 0; pp < MMV_TILES / 4; ++pp) {
+    if ((u32)(pp * 4) >= nt) break;
+    if (!cbar(A, gen)) return false;  // the previous pass's partials are read; g_scr is written
+    if (cval) {
+#pragma unroll
+      for (int tp = 0; tp < 4; ++tp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g_red[((w * 4 + tp) * 16 + kq * 4 + i) * B + col] = acc[pp * 4 + tp][i];
+    }
+    if (!cbar(A, gen)) return false;
+    auto colsum = [&](u32 tp, u32 row, u32 b) {
+      float v = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < NC; ++ww) v += g_red[((ww * 4 + tp) * 16 + row) * B + b];
+      if (o.norm) {
+        float tot = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NC; ++ww) tot += g_scr[ww * 16 + b];
+        v *= 1.0f / sqrtf(tot / (float)o.K + A.rms_eps);
+      }
+      return v;
+    };
+    const u32 row = (tid / B) % 16, b = tid % B;
+    if (swiglu) {
+      const u32 pr = tid / (16 * B);  // gate / up tile pair within the pass
+      if (pr < 2 && (u32)(pp * 4) + 2 * pr + 1 < nt) {
+        const float gv = colsum(2 * pr, row, b), uv = colsum(2 * pr + 1, row, b);
+        const u32 orow = 16 * ((u32)(pp * 2) + pr) + row;
+        if (orow < nrows) st_sc1((float*)o.out + (size_t)b * o.ld_out + o.row0 + orow, silu(gv) * uv);
+      }
+    } else {
+      const u32 tp = tid / (16 * B);
+      if (tp < 4 && (u32)(pp * 4) + tp < nt) {
+        const float v = colsum(tp, row, b);
+        const u32 orow = 16 * ((u32)(pp * 4) + tp) + row, grow = o.row0 + orow;
+        if (orow < nrows) {
+          if (o.epi == EPI_RESID) {
+            const float x = ld_sc1((const float*)o.res + (size_t)b * o.ld_out + grow);
+            st_sc1((float*)o.out + (size_t)b * o.ld_out + grow, x + v);
+          } else if (o.epi == EPI_STORE) {
+            st_sc1((float*)o.out + (size_t)b * o.ld_out + grow, v);
+          } else if ((int)b < A.batch) {  // EPI_LOGITS
+            const bool ok = ld_i32_sc1(A.row_ok + b) != 0;
+            A.logits[(size_t)b * A.V + grow] = ok ? v : __builtin_nanf("");
+          }
+        }
+      }
+    }
+  }
+  return true;
+}
+
+// ------------------------------------------------------------------ ATTENTION (split-KV + merge)
+// One item = (sequence b, KV head, position chunk).  The G query heads sharing the KV head are
+// processed together.  Scores come from the matrix cores: Q (G heads, split into bf16 hi + lo so
+// the product keeps fp32 accuracy) times K^T, 16 positions per 16x16x32 tile.  Each compute wave
+// runs an online softmax over its ring slots and accumulates P V on the vector ALUs; the waves are
+// merged in LDS, the chunk's (m, l, o) partial goes to global memory, and the last chunk of
+// (b, kvh) to finish (a ticket) merges all chunks with the log-sum-exp rule.
 template <int D>
 __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen, ItemCache& ic) {
   constexpr int DPL = D / 64;          // dims per lane in the vector layout
@@ -1300,7 +1459,12 @@ __device__ __forceinline__ void compute(const KArgs& A, u32 q0, u32 q1, u32 w) {
         if (!cbar(A, gen)) return;
         op_embed_finish(A, w, gen);
         break;
-      case OP_GEMV: alive = op_gemv<B>(A, o, w, seq, gen); break;
+      case OP_GEMV:
+        if constexpr (B < 8) alive = op_gemv<B>(A, o, w, seq, gen);
+        break;
+      case OP_MMV:
+        if constexpr (B == 8) alive = op_mmv<B>(A, o, w, seq, gen);
+        break;
       case OP_ATTN: alive = A.d == 128 ? op_attn<128>(A, o, w, seq, gen, ic) : op_attn<64>(A, o, w, seq, gen, ic); break;
       case OP_DELTA: alive = A.dk == 128 ? op_delta<128>(A, o, w, seq, gen) : op_delta<64>(A, o, w, seq, gen); break;
       default: break;

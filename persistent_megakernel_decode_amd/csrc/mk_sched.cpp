@@ -101,6 +101,10 @@ struct Builder {
             uint32_t ld_out, uint64_t res) {
     if (!err.empty()) return;
     const int B = P.kernel_batch;
+    if (B >= 8) {
+      mmv(stage, wait, layer, N, K, epi, norm, W, W2, W3, b1, b2, in, ld_in, gamma, out, ld_out, res);
+      return;
+    }
     const int ppr = pad_ppr((int)K);
     if (ppr >= 8 && ppr / 8 > mmax_for(B)) {
       err = fmt("projection with %u inputs is too long for batch width %d", K, B);
@@ -166,6 +170,73 @@ struct Builder {
       }
       o.in = in; o.gamma = gamma; o.out = out; o.res = res;
       stage_ops[stage].push_back(o);
+      }
+    }
+  }
+
+  // Matrix-core GEMV stage (batch 8): row tiles of 16, k-outer streaming.  Same row-space and
+  // weight-run conventions as gemv().
+  void mmv(int stage, int wait, int layer, uint32_t N, uint32_t K, uint8_t epi, bool norm, uint64_t W, uint64_t W2,
+           uint64_t W3, uint32_t b1, uint32_t b2, uint64_t in, uint32_t ld_in, uint64_t gamma, uint64_t out,
+           uint32_t ld_out, uint64_t res) {
+    if (K % MMV_KSEG) {
+      err = fmt("projection input length %u is not a multiple of %d (batch-8 matrix-core path)", K, MMV_KSEG);
+      return;
+    }
+    const bool swiglu = epi == EPI_SWIGLU;
+    const uint32_t maxrows = swiglu ? 16 * MMV_TILES / 2 : 16 * MMV_TILES;
+    uint32_t T = std::min<uint32_t>((uint32_t)n_cus, N);
+    if ((N + T - 1) / T > maxrows) {
+      T = (N + maxrows - 1) / maxrows;
+      T = (T + n_cus - 1) / n_cus * n_cus;
+    }
+    const uint32_t bnd[3] = {b1, b2, 0xFFFFFFFFu};
+    for (uint32_t t = 0; t < T; ++t) {
+      const uint32_t t0 = (uint32_t)((uint64_t)N * t / T), t1 = (uint32_t)((uint64_t)N * (t + 1) / T);
+      for (uint32_t r0 = t0, r1; r0 < t1; r0 = r1) {
+        r1 = t1;
+        if (!swiglu) {
+          const int sa = r0 < b1 ? 0 : (r0 < b2 ? 1 : 2);
+          if (sa < 2) r1 = std::min<uint32_t>(t1, bnd[sa + 1]);
+        }
+        Op o{};
+        o.opcode = OP_MMV;
+        o.epi = epi;
+        o.norm = norm ? 1 : 0;
+        o.wait_stage = (int16_t)wait;
+        o.sig_stage = (int16_t)stage;
+        o.layer = (uint32_t)layer;
+        o.row0 = r0;
+        o.nrows = r1 - r0;
+        o.K = K;
+        o.ppr = K / MMV_KSEG;
+        const uint32_t ntiles = (swiglu ? 2 : 1) * ((o.nrows + 15) / 16);
+        o.nslots = ntiles * o.ppr;
+        o.ld_in = ld_in;
+        o.ld_out = ld_out;
+        const uint64_t rb = (uint64_t)K * 2;
+        if (swiglu) {
+          o.W = W ? W + r0 * rb : 0;
+          o.W2 = W2 ? W2 + r0 * rb : 0;
+          o.b1 = o.nrows;
+        } else {
+          const uint64_t segs[3] = {W, W2, W3};
+          const uint32_t start[3] = {0u, b1, b2}, end[3] = {b1, b2, 0xFFFFFFFFu};
+          const int sa = r0 < b1 ? 0 : (r0 < b2 ? 1 : 2);
+          o.W = segs[sa] ? segs[sa] + (uint64_t)(r0 - start[sa]) * rb : 0;
+          const uint32_t na = std::min<uint32_t>(o.nrows, end[sa] - r0);
+          o.b1 = na;
+          o.W2 = 0;
+          if (na < o.nrows) {
+            if (sa == 2 || o.nrows - na > end[sa + 1] - start[sa + 1]) {
+              err = "a projection tile spans more than two weight tensors";
+              return;
+            }
+            o.W2 = segs[sa + 1];
+          }
+        }
+        o.in = in; o.gamma = gamma; o.out = out; o.res = res;
+        stage_ops[stage].push_back(o);
       }
     }
   }
@@ -317,7 +388,7 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
       Op o = ops[j];
       o.sig_index = (uint32_t)j;
       const int cu = (int)(j % (size_t)n_cus);
-      if (o.opcode == OP_GEMV) {
+      if (o.opcode == OP_GEMV || o.opcode == OP_MMV) {
         const double bytes = (double)o.nrows * (o.epi == EPI_SWIGLU ? 2 : 1) * o.K * 2;
         P.cu_bytes[cu] += bytes;
         P.weight_bytes += bytes;
@@ -385,6 +456,13 @@ int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
         if (o.nslots * SLOT_PIECES < o.nrows * mult * o.ppr) bad(fmt("cu %d op %u: too few slots", c, i));
         if (o.ppr * PIECE_ELEMS < o.K) bad(fmt("cu %d op %u: pieces do not cover a row", c, i));
       }
+      if (o.opcode == OP_MMV) {
+        const uint32_t ntiles = (o.epi == EPI_SWIGLU ? 2 : 1) * ((o.nrows + 15) / 16);
+        if (ntiles > (uint32_t)MMV_TILES) bad(fmt("cu %d op %u: %u row tiles, at most %d", c, i, ntiles, MMV_TILES));
+        if (o.K % MMV_KSEG || o.ppr * MMV_KSEG != o.K) bad(fmt("cu %d op %u: K segments do not cover a row", c, i));
+        if (o.nslots != ntiles * o.ppr) bad(fmt("cu %d op %u: slot count", c, i));
+        if (P.kernel_batch > 16) bad(fmt("cu %d op %u: batch wider than a matrix tile", c, i));
+      }
     }
   }
   for (int s = 0; s < S; ++s) {
@@ -397,7 +475,7 @@ int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
   // every GEMV stage covers its rows exactly once
   std::vector<std::vector<std::pair<uint32_t, uint32_t>>> rows(S);
   for (const Op& o : P.ops)
-    if (o.opcode == OP_GEMV) rows[o.sig_stage].push_back({o.row0, o.row0 + o.nrows});
+    if (o.opcode == OP_GEMV || o.opcode == OP_MMV) rows[o.sig_stage].push_back({o.row0, o.row0 + o.nrows});
   for (int s = 0; s < S; ++s) {
     auto& r = rows[s];
     if (r.empty()) continue;

@@ -41,7 +41,7 @@ def _desc(cfg, max_ctx):
                          s["conv_width"])
 
 
-@pytest.mark.parametrize("name", ["tiny", "0.6b", "8b", "hybrid"])
+@pytest.mark.parametrize("name", ["tiny", "0.6b", "8b", "13b", "hybrid"])
 def test_plan_is_valid_and_balanced(name):
     cfg = synth.CONFIGS[name]
     info = mkd.mk_plan(_desc(cfg, 4096 + 256), 256)
