@@ -16,6 +16,8 @@ CASES = {
     "0.6b": (synth.CONFIGS["0.6b"], 3),
     "hybrid": (synth.CONFIGS["hybrid"], 2),
     "8b": (synth.CONFIGS["8b"], 2),
+    # batch 8, ragged contexts 512-4096, shuffled pages, matrix-core projections
+    "13b": (synth.CONFIGS["13b"], 1),
 }
 
 
