@@ -144,32 +144,4 @@ struct KArgs {
 constexpr uint32_t ST_BAD_INPUT = 1u;
 constexpr uint32_t ST_TIMEOUT = 2u;
 
-// Positions per attention chunk: the smallest multiple of pps for which cutting every sequence's
-// context into chunks of that size gives at most n_items / Hkv chunks in all, so that one launch
-// has at most n_items (sequence, KV head, chunk) work items.  ctx(b) is the context length of
-// sequence b (0 = idle).  n_items >= batch * Hkv guarantees a solution (one chunk per sequence).
-template <class CtxFn>
-__host__ __device__ inline int32_t attn_chunk_size(CtxFn ctx, int32_t batch, int32_t Hkv, int32_t n_items,
-                                                   int32_t pps) {
-  const int64_t K = n_items / Hkv;
-  int64_t total = 0, maxc = 0;
-  for (int32_t b = 0; b < batch; ++b) {
-    const int64_t c = ctx(b);
-    total += c;
-    maxc = c > maxc ? c : maxc;
-  }
-  if (total == 0 || K < 1) return 0;
-  int64_t lo = ((total + K - 1) / K + pps - 1) / pps;  // in units of pps
-  int64_t hi = (maxc + pps - 1) / pps;
-  if (lo > hi) lo = hi;
-  while (lo < hi) {
-    const int64_t mid = (lo + hi) / 2, cs = mid * pps;
-    int64_t n = 0;
-    for (int32_t b = 0; b < batch; ++b) n += (ctx(b) + cs - 1) / cs;
-    if (n <= K) hi = mid;
-    else lo = mid + 1;
-  }
-  return (int32_t)(lo * pps);
-}
-
 }  // namespace mk

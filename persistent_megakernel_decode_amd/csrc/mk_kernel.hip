@@ -261,25 +261,76 @@ struct AttnItem {
 
 __device__ __forceinline__ int clamp_ctx(const KArgs& A, int c) { return (c >= 1 && c <= A.max_ctx) ? c : 0; }
 
-// Item i -> (sequence, KV head, position range).  Uniform; reads ctx_lens with scalar loads.
-// Depends only on the launch's context lengths, so callers keep it across layers.
+// The launch's attention split, built once per launch by the loader wave before it streams
+// anything and read from LDS by every wave.  Each KV head gets at most n_items / Hkv chunks, all
+// of one length (a multiple of the positions one ring slot holds; a sequence's last chunk may be
+// shorter).  Layout: [0] ready flag, [1 + b] context length of sequence b,
+// [9 + b] its chunk length, [17 + b] chunks of the sequences before b (b = 8: all chunks).
+constexpr int APLAN_MAXB = 8;
+__shared__ int g_aplan[1 + 3 * APLAN_MAXB + 1];
+
+__device__ __forceinline__ void attn_plan_build(const KArgs& A, int pps) {
+  int cv[APLAN_MAXB];
+  int total = 0, nz = 0;
+#pragma unroll
+  for (int b = 0; b < APLAN_MAXB; ++b) {
+    cv[b] = b < A.batch ? clamp_ctx(A, sload(A.ctx_lens + b)) : 0;
+    total += cv[b];
+    nz += cv[b] > 0 ? 1 : 0;
+  }
+  const int K = A.Hkv > 0 ? A.n_items / A.Hkv : 0;  // chunks per KV head; >= batch by construction
+  // one chunk length for the launch: the smallest multiple of pps that needs at most K chunks
+  // per KV head (binary search; one chunk per sequence always fits since K >= batch)
+  int cs_all = 0;
+  if (total > 0 && K >= nz) {
+    int maxc = 0;
+#pragma unroll
+    for (int b = 0; b < APLAN_MAXB; ++b) maxc = max(maxc, cv[b]);
+    int lo = ((total + K - 1) / K + pps - 1) / pps, hi = (maxc + pps - 1) / pps;
+    if (lo > hi) lo = hi;
+    while (lo < hi) {
+      const int mid = (lo + hi) / 2, c = mid * pps;
+      int n = 0;
+#pragma unroll
+      for (int b = 0; b < APLAN_MAXB; ++b) n += (cv[b] + c - 1) / c;
+      if (n <= K) hi = mid;
+      else lo = mid + 1;
+    }
+    cs_all = lo * pps;
+  }
+  if (lane_id() == 0) {
+    int acc = 0;
+#pragma unroll
+    for (int b = 0; b < APLAN_MAXB; ++b) {
+      const int cs = cv[b] > 0 ? cs_all : 0, nb = cs > 0 ? (cv[b] + cs - 1) / cs : 0;
+      g_aplan[1 + b] = cv[b];
+      g_aplan[9 + b] = cs;
+      g_aplan[17 + b] = acc;
+      acc += nb;
+    }
+    g_aplan[17 + APLAN_MAXB] = acc;
+    __hip_atomic_store(&g_aplan[0], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
+// Item i -> (sequence, KV head, position range), from the launch plan in LDS.  Uniform.
 __device__ AttnItem attn_item(const KArgs& A, u32 item, int pps) {
   AttnItem it{0, 0, 0, 0, 0, 0, false};
-  auto ctx = [&](int b) { return clamp_ctx(A, sload(A.ctx_lens + b)); };
-  const int cs = attn_chunk_size(ctx, A.batch, A.Hkv, A.n_items, pps);
-  if (cs == 0) return it;
+  (void)pps;
+  Watchdog wd(A);
+  while (lds_ld((const u32*)&g_aplan[0]) == 0) {
+    if (aborted() || wd.expired()) return it;
+    __builtin_amdgcn_s_sleep(1);
+  }
   const int bc = (int)(item / (u32)A.Hkv), kvh = (int)(item % (u32)A.Hkv);
-  int acc = 0;
-  for (int b = 0; b < A.batch; ++b) {
-    const int c = ctx(b);
-    const int nb = (c + cs - 1) / cs;
-    if (bc < acc + nb) {
-      const int k = bc - acc;
+  for (int b = 0; b < A.batch && b < APLAN_MAXB; ++b) {
+    const int c0 = (int)lds_ld((const u32*)&g_aplan[17 + b]), c1 = (int)lds_ld((const u32*)&g_aplan[18 + b]);
+    if (bc < c1) {
+      const int k = bc - c0, c = (int)lds_ld((const u32*)&g_aplan[1 + b]), cs = (int)lds_ld((const u32*)&g_aplan[9 + b]);
       it.b = b; it.kvh = kvh; it.p0 = k * cs; it.p1 = min(c, (k + 1) * cs);
-      it.n_b = nb; it.first_item = acc * A.Hkv + kvh; it.valid = true;
+      it.n_b = c1 - c0; it.first_item = c0 * A.Hkv + kvh; it.valid = true;
       return it;
     }
-    acc += nb;
   }
   return it;
 }
@@ -541,6 +592,7 @@ __device__ u32 op_slots(const KArgs& A, const Op& o, ItemCache& ic) {
 __device__ __forceinline__ void loader(const KArgs& A, u32 q0, u32 q1) {
   u32 seq = 0, marked = 0, limit = NSLOT;  // slots below `limit` may be filled
   const u32 lane16 = lane_id() * 16;
+  attn_plan_build(A, A.d == 64 ? 32 : 16);
   ItemCache ic;
   PageWindow pw;
   const AttnLanes al = attn_lanes(A.d == 64 ? 64u : 128u);
@@ -934,7 +986,8 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
     }
     gv = (o.norm && ks < nks) ? *(const u32x4*)(gm + k0) : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   };
-  auto consume = [&](const float* xv, const u32x4& gv) -> bool {
+  // one segment: this wave's input block times every tile of the segment (the slots must be full)
+  auto consume = [&](const float* xv, const u32x4& gv) {
     const float g[8] = {bflo(gv.x), bfhi(gv.x), bflo(gv.y), bfhi(gv.y), bflo(gv.z), bfhi(gv.z), bflo(gv.w), bfhi(gv.w)};
     float xg[8];
 #pragma unroll
@@ -945,7 +998,6 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
     u32x4 hi, lo;
     split_bf16x8(xg, hi, lo);
     const bf16x8 bh = __builtin_bit_cast(bf16x8, hi), bl = __builtin_bit_cast(bf16x8, lo);
-    if (!wait_full(A, seq + nt - 1)) return false;
 #pragma unroll
     for (int t = 0; t < MMV_TILES; ++t) {
       if ((u32)t < nt) {
@@ -955,22 +1007,27 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[t], 0, 0, 0);
       }
     }
-    release_upto(w, seq + nt);
     seq += nt;
-    return true;
   };
 
-  // segments two at a time, the inputs of each fetched two segments ahead
-  float xa[8], xb[8];
-  u32x4 ga, gb;
-  fetch(0, xa, ga);
-  fetch(1, xb, gb);
-  for (u32 ks = 0; ks < nks; ks += 2) {
-    if (!consume(xa, ga)) return false;
-    fetch(ks + 2, xa, ga);
-    if (ks + 1 < nks) {
-      if (!consume(xb, gb)) return false;
-      fetch(ks + 3, xb, gb);
+  // Segments four at a time, the inputs of each fetched four segments ahead (a segment of a
+  // 2-tile op streams in about half a microsecond; an input fetch takes longer).  Thin ops wait
+  // for and release several segments at once (gs segments, at most 8 slots), so the ring protocol
+  // is paid per 8 slots rather than per segment.
+  const u32 gs = nt <= 2 ? 4u : (nt <= 4 ? 2u : 1u);
+  float xr[4][8];
+  u32x4 gr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fetch(i, xr[i], gr[i]);
+  for (u32 ks = 0; ks < nks; ks += 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (ks + i < nks) {
+        if ((u32)i % gs == 0 && !wait_full(A, seq + min(gs, nks - (ks + i)) * nt - 1)) return false;
+        consume(xr[i], gr[i]);
+        if (((u32)i + 1) % gs == 0 || ks + i + 1 == nks) release_upto(w, seq);
+        fetch(ks + i + 4, xr[i], gr[i]);
+      }
     }
   }
 
@@ -1487,7 +1544,7 @@ template <int B>
 __device__ __forceinline__ void megakernel_body(const KArgs& A) {
   const u32 wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index: uniform per wave
   if (threadIdx.x < NC) g_consumed[threadIdx.x] = 0;
-  if (threadIdx.x == 0) g_filled = 0;
+  if (threadIdx.x == 0) { g_filled = 0; g_aplan[0] = 0; }
   if (threadIdx.x == 0) { g_bar = 0; g_abort = 0; }
   __syncthreads();
   const u32 q0 = A.queue_off[blockIdx.x], q1 = A.queue_off[blockIdx.x + 1];

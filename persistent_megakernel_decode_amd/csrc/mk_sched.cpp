@@ -17,6 +17,7 @@
 #include "mk_sched.h"
 
 #include <algorithm>
+#include <cstdlib>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -272,7 +273,13 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
   const int u_w = m.n_delta ? m.C + 2 * nh : 0;
   P.mix_dim = std::max(m.n_attn ? Hq * hd : 0, m.n_delta ? nh * dv : 0);
   // attention items per layer: a whole number of items per CU, at least one per (sequence, KV head)
-  P.n_items = m.n_attn ? n_cus * ((Hkv * d.max_batch + n_cus - 1) / n_cus) : 0;
+  {
+    // at least two chunks per (sequence, KV head) on average, so that chunks of one length
+    // balance across CUs for ragged contexts
+    int per_cu = (2 * Hkv * d.max_batch + n_cus - 1) / n_cus;
+    if (const char* e = getenv("MK_ATTN_ITEMS_PER_CU")) per_cu = std::max(per_cu, atoi(e));  // diagnostic
+    P.n_items = m.n_attn ? n_cus * per_cu : 0;
+  }
   // the merge of one (sequence, KV head) stages every chunk's (m, l) per query head in LDS
   if (m.n_attn && (int64_t)(P.n_items / Hkv) * (d.n_q_heads / Hkv) * 2 > RED_FLOATS)
     return fmt("too many attention chunks per KV head for the merge (%d items, %d KV heads)", P.n_items, Hkv);
