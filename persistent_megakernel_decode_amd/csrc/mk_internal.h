@@ -38,9 +38,8 @@ constexpr int NSUB = 16;               // split sub-counters per stage
 constexpr int CTR_STRIDE = 32;         // u32 between sub-counters (128 B, one cache line each)
 
 // ---- GEMV geometry ----
-constexpr int PIECE_ELEMS = PIECE / 2; // bf16 weights per piece row-segment
-constexpr int MAX_M = 4;               // pieces of one row per compute wave (rows up to 16384 elements)
-constexpr int GEMV_BATCH = 4;          // ring slots a compute wave takes per wait
+constexpr int PIECE_ELEMS = PIECE / 2; // bf16 weights per piece
+constexpr int GEMV_MAX_PG = 64;        // pieces per row group: a wave keeps at most 8 input fragments
 
 enum Opcode : uint8_t { OP_NOP = 0, OP_EMBED = 1, OP_GEMV = 2, OP_ATTN = 3, OP_DELTA = 4, OP_MMV = 5 };
 enum Epi : uint8_t { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
@@ -56,6 +55,13 @@ constexpr int16_t NO_STAGE = -1;
 // [b1, ...) start at W2.  EPI_SWIGLU streams the op's gate rows (W) then the
 // same rows of the up projection (W2, b1 = nrows) and writes silu(gate) * up.
 //
+// GEMV ops (batch <= 4) run on the matrix cores: the stream is cut into row
+// groups of R = 16 / part rows, each row split into pieces of 32 * part inputs
+// (a piece of one group is 16 x 32 bf16, one 16x16x32 operand).  `ppr` holds
+// the pieces per row group PG (1, 2, 4, or a multiple of 8 up to 64, padded
+// up from ceil(K / (32 part))); a ring slot holds 8 consecutive pieces, so a
+// group spans PG / 8 slots, or a slot holds 8 / PG groups.
+//
 // An MMV op (batch 8: the projection is a skinny GEMM on the matrix cores) covers the same row
 // space in tiles of 16 rows (SWIGLU: gate and up tiles interleaved, gate tile i = 2i, up tile
 // i = 2i + 1), at most MMV_TILES tiles, and streams K in segments of MMV_KSEG inputs: ring slot
@@ -67,7 +73,7 @@ struct alignas(16) Op {
   uint8_t opcode;
   uint8_t epi;
   uint8_t norm;        // GEMV: 1 = RMSNorm the input with `gamma`
-  uint8_t pad0;
+  uint8_t part;        // GEMV: input parts per matrix-core tile (4 or 8)
   int16_t wait_stage;  // stage this op waits for (NO_STAGE = none)
   int16_t sig_stage;   // stage this op counts towards (NO_STAGE = none)
   uint32_t sig_index;  // index of this op within sig_stage (selects the sub-counter)
@@ -75,7 +81,7 @@ struct alignas(16) Op {
   uint32_t row0;       // GEMV: first output row;  ATTN / DELTA: item index
   uint32_t nrows;      // GEMV: output rows
   uint32_t K;          // GEMV: input length
-  uint32_t ppr;        // GEMV: pieces per row, padded to a power of two (1 .. 32)
+  uint32_t ppr;        // GEMV: pieces per row group;  MMV: K segments
   uint32_t nslots;     // GEMV / DELTA: ring slots the op consumes (ATTN: computed at run time)
   uint32_t ld_in;      // floats between batch rows of `in`
   uint32_t ld_out;     // floats between batch rows of `out` / `res`

@@ -106,6 +106,24 @@ __device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even (f
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// x = hi + lo with both halves bf16 (hi rounded to nearest even by the hardware conversion, lo the
+// rounded remainder: hi + lo carries about 16 significant bits of x)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_bf16x8(const float* x, u32x4& hi, u32x4& lo) {
+  u32 h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const f32x2 v = {x[2 * e], x[2 * e + 1]};
+    const bf16x2 vh = __builtin_convertvector(v, bf16x2);
+    const bf16x2 vl = __builtin_convertvector(v - __builtin_convertvector(vh, f32x2), bf16x2);
+    h[e] = __builtin_bit_cast(u32, vh);
+    l[e] = __builtin_bit_cast(u32, vl);
+  }
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
 // Lane index, recomputed at every use: an opaque instruction pair the compiler cannot hoist, so
 // lane-derived addresses are not kept alive across the whole persistent loop (which would crowd
 // out the registers the ops need).
@@ -427,62 +445,119 @@ __device__ __forceinline__ const char* gemv_row(const GemvSeg& g, u32 rl) {
   return (const char*)(base + (uint64_t)r * g.rowbytes);
 }
 
-// 8 KB of one row into a slot: two address registers; each DMA's immediate offset moves the global
-// and the LDS address together, so a slot costs two M0 values and eight loads.
-__device__ __forceinline__ void dma_slot(const char* row, u32 lane16, u32x4* dst) {
-  const char* p0 = row + lane16;
-  const char* p1 = row + 4096 + lane16;
-  auto* l0 = (__attribute__((address_space(3))) void*)dst;
-  auto* l1 = (__attribute__((address_space(3))) void*)(dst + 256);
-  __builtin_amdgcn_global_load_lds(p0, l0, 16, 0, AUX_NT);
-  __builtin_amdgcn_global_load_lds(p0, l0, 16, 1024, AUX_NT);
-  __builtin_amdgcn_global_load_lds(p0, l0, 16, 2048, AUX_NT);
-  __builtin_amdgcn_global_load_lds(p0, l0, 16, 3072, AUX_NT);
-  __builtin_amdgcn_global_load_lds(p1, l1, 16, 0, AUX_NT);
-  __builtin_amdgcn_global_load_lds(p1, l1, 16, 1024, AUX_NT);
-  __builtin_amdgcn_global_load_lds(p1, l1, 16, 2048, AUX_NT);
-  __builtin_amdgcn_global_load_lds(p1, l1, 16, 3072, AUX_NT);
+// Loader-side walk over a GEMV op's slots (layout in the GEMV section below): the current row group
+// and the slot within it, advanced once per slot, so the issue path needs no divisions.
+// GEMV slot layout (batch <= 4; the compute side is described in the GEMV section).  A slot holds Rs
+// row segments of SB = 8 KB / Rs bytes in LDS order: segment j is stream row rho0 + j, inputs
+// [kappa0, kappa0 + SB / 2).  With PG >= 8 pieces per row group a slot is one group's R = 16 / P
+// rows (Rs = R) at kappa0 = t SB / 2 for its t-th slot; with PG < 8 it holds 8 / PG whole groups
+// (Rs = 8 R / PG, kappa0 = 0).  So the loader streams Rs contiguous runs per slot, one M0 value
+// each.  Within each 1 KB block of the slot, 16-byte chunk c sits at position gemv_pos(c): the
+// compute lanes' operand reads (which stride 64 bytes through a row, and with P = 4 cover two row
+// segments per eight lanes) then fall in eight distinct bank groups per eight lanes, while eight
+// consecutive DMA lanes still fetch one whole 128-byte line.
+__device__ __forceinline__ u32 gemv_lg_rs(u32 P, u32 pg) {  // log2 of the row segments per slot
+  const u32 lgR = P == 8 ? 1u : 2u;
+  return pg >= 8 ? lgR : lgR + 3 - (u32)__builtin_ctz(pg);
 }
-static_assert(SLOT == 8192 && SLOT_PIECES == 8 && PIECE == 1024, "dma_slot moves one 8 KB slot");
+__device__ __forceinline__ u32 gemv_pos(u32 c, u32 blk, u32 lgrs) {  // an involution on c
+  const u32 par = lgrs <= 3 ? (blk >> (3 - lgrs)) & 1 : 0u;  // parity of the segment holding the block
+  return c ^ ((c >> 3) & 3) ^ (par << 1);
+}
 
-// One ring slot of the GEMV stream.  With ppr >= 8 a slot is 8 consecutive pieces of one row
-// (one row lookup per slot); with ppr < 8 it is 8 / ppr whole rows.  Pieces past the row's end
-// stream row 0 of the first weight (finite bytes whose products meet zero inputs); a partial last
-// piece reads only the lanes inside the row.
-__device__ __forceinline__ void issue_gemv(const GemvSeg& gsg, u32 s, u32 nrt, u32 lgp, u32 lane16, u32x4* dst) {
-  const u32 rowbytes = gsg.rowbytes;
-  const char* dummy = (const char*)gsg.wa;
-  if (lgp >= 3) {
-    const u32 lgm = lgp - 3;
-    const u32 rl = s >> lgm, kp0 = (s & ((1u << lgm) - 1)) << 3;
-    const u32 nfull = rowbytes / PIECE;
-    if (rl < nrt && kp0 + SLOT_PIECES <= nfull) {  // the common case: eight full pieces
-      dma_slot(gemv_row(gsg, rl) + kp0 * PIECE, lane16, dst);
-      return;
-    }
-    const char* row = rl < nrt ? gemv_row(gsg, rl) : dummy;
+// Loader-side walk over a GEMV op's slots, advanced once per slot (no divisions on the issue path).
+struct GemvWalk {
+  u32 s, g, t;          // slot; PG >= 8: row group and its slot
+  u32 pg, nf, R, lgrs, nrt, K;
+  u32 voff0, voff1;     // this DMA lane's byte offset in a block of an even / odd segment
+  bool plain;           // every slot is R whole row segments (PG >= 8, no padding)
+  uint64_t grow;        // PG >= 8: address of the current group's first row
+};
+__device__ __forceinline__ GemvWalk gemv_walk(const Op& o, const GemvSeg& gsg, u32 lane) {
+  GemvWalk gw;
+  gw.s = gw.g = gw.t = 0;
+  gw.pg = o.ppr;
+  gw.nf = gw.pg >= 8 ? gw.pg / 8 : 1u;
+  gw.R = 16u / o.part;
+  gw.lgrs = gemv_lg_rs(o.part, gw.pg);
+  gw.nrt = o.epi == EPI_SWIGLU ? 2 * o.nrows : o.nrows;
+  gw.K = o.K;
+  // DMA lane d fills LDS chunk d of a block with the block's chunk gemv_pos(d)
+  gw.voff0 = 16 * (lane ^ ((lane >> 3) & 3));
+  gw.voff1 = 16 * (lane ^ ((lane >> 3) & 3) ^ 2u);
+  gw.plain = gw.pg >= 8 && gw.lgrs <= 3 && gw.nf * (4096u >> gw.lgrs) == gw.K;
+  gw.grow = uni64((uint64_t)gemv_row(gsg, 0));
+  return gw;
+}
+// Rs contiguous segments of BPS KB each: one scalar base per segment, the instruction offset
+// stepping both addresses through the segment's blocks.
+template <u32 BPS>
+__device__ __forceinline__ void dma_segments(const char* base, u32 rowbytes, u32 voff0, u32 voff1, u32x4* dst) {
+  constexpr u32 RS = 8 / BPS;
 #pragma unroll
-    for (int i = 0; i < SLOT_PIECES; ++i) {
-      const u32 off = (kp0 + i) * PIECE;
-      if (rl < nrt && off + PIECE <= rowbytes) dma_at(row + off, lane16, dst + i * 64);
-      else if (rl < nrt && off < rowbytes) dma_at(row, off + lane16 < rowbytes ? off + lane16 : 0u, dst + i * 64);
-      else dma_at(dummy, lane16, dst + i * 64);
+  for (u32 j = 0; j < RS; ++j) {
+    const char* p = base + (size_t)j * rowbytes + ((j & 1) ? voff1 : voff0);
+    auto* l = (__attribute__((address_space(3))) void*)((char*)dst + j * 1024 * BPS);
+    __builtin_amdgcn_global_load_lds(p, l, 16, 0, AUX_NT);
+    if constexpr (BPS >= 2) __builtin_amdgcn_global_load_lds(p, l, 16, 1024, AUX_NT);
+    if constexpr (BPS >= 4) {
+      __builtin_amdgcn_global_load_lds(p, l, 16, 2048, AUX_NT);
+      __builtin_amdgcn_global_load_lds(p, l, 16, 3072, AUX_NT);
     }
+  }
+}
+// One ring slot of a GEMV op.  Rows past the op and inputs past K (padding of the last group or
+// piece) re-read bytes of the op's rows: their products meet zero inputs, and nothing is stored for
+// rows past the op.
+__device__ __forceinline__ void issue_gemv(const GemvSeg& gsg, GemvWalk& gw, u32 lane, u32x4* dst) {
+  if (gw.plain) {  // the common case: R row segments of one group, base advanced per slot
+    const char* base = (const char*)gw.grow + gw.t * (8192u >> gw.lgrs);
+    if (gw.lgrs == 1) dma_segments<4>(base, gsg.rowbytes, gw.voff0, gw.voff1, dst);
+    else dma_segments<2>(base, gsg.rowbytes, gw.voff0, gw.voff1, dst);
+    if (++gw.t == gw.nf) {
+      gw.t = 0;
+      ++gw.g;
+      gw.grow = uni64((uint64_t)gemv_row(gsg, gw.g * gw.R));
+    }
+    ++gw.s;
     return;
   }
-  const u32 ppr = 1u << lgp;
+#ifdef MK_WALK_RESTATE
+  gw.s = __builtin_amdgcn_readfirstlane(gw.s);
+  gw.g = __builtin_amdgcn_readfirstlane(gw.g);
+  gw.t = __builtin_amdgcn_readfirstlane(gw.t);
+  gw.pg = __builtin_amdgcn_readfirstlane(gw.pg);
+  gw.nf = __builtin_amdgcn_readfirstlane(gw.nf);
+  gw.R = __builtin_amdgcn_readfirstlane(gw.R);
+  gw.lgrs = __builtin_amdgcn_readfirstlane(gw.lgrs);
+  gw.nrt = __builtin_amdgcn_readfirstlane(gw.nrt);
+  gw.K = __builtin_amdgcn_readfirstlane(gw.K);
+#endif
+  const u32 rho0 = gw.pg >= 8 ? gw.g * gw.R : gw.s << gw.lgrs;
+  const u32 rs = 1u << gw.lgrs, half = 4096u >> gw.lgrs;  // segments; inputs per segment
+  const u32 kappa0 = gw.pg >= 8 ? gw.t * half : 0u;
+  const bool one_run = rho0 + rs <= gsg.na || rho0 >= gsg.na;
+  if (gw.lgrs <= 3 && rho0 + rs <= gw.nrt && one_run && kappa0 + half <= gw.K) {  // the common case
+    const char* base = gemv_row(gsg, rho0) + 2 * kappa0;
+    if (gw.lgrs == 1) dma_segments<4>(base, gsg.rowbytes, gw.voff0, gw.voff1, dst);
+    else if (gw.lgrs == 2) dma_segments<2>(base, gsg.rowbytes, gw.voff0, gw.voff1, dst);
+    else dma_segments<1>(base, gsg.rowbytes, gw.voff0, gw.voff1, dst);
+  } else {
+    // per lane: each block's chunk gemv_pos(lane) -> segment, input; clamp rows and inputs
+    const u32 sb = 8192u >> gw.lgrs;
 #pragma unroll
-  for (int i = 0; i < SLOT_PIECES; ++i) {
-    const u32 p = s * SLOT_PIECES + i;
-    const u32 rl = p >> lgp, kp = p & (ppr - 1);
-    const u32 off = kp * PIECE;
-    if (rl < nrt && off < rowbytes) {
-      const char* row = gemv_row(gsg, rl);
-      if (off + PIECE <= rowbytes) dma_at(row + off, lane16, dst + i * 64);
-      else dma_at(row, off + lane16 < rowbytes ? off + lane16 : 0u, dst + i * 64);
-    } else {
-      dma_at(dummy, lane16, dst + i * 64);
+    for (int blk = 0; blk < SLOT_PIECES; ++blk) {
+      const u32 byte = (u32)blk * 1024 + 16 * gemv_pos(lane, blk, gw.lgrs);
+      u32 row = rho0 + byte / sb, k = kappa0 + (byte % sb) / 2;
+      if (row >= gw.nrt) row = gw.nrt - 1;
+      if (k >= gw.K) k = 0;
+      __builtin_amdgcn_global_load_lds(gemv_row(gsg, row) + 2 * k, (__attribute__((address_space(3))) void*)(dst + blk * 64), 16, 0, AUX_NT);
     }
+  }
+  ++gw.s;
+  if (gw.pg >= 8 && ++gw.t == gw.nf) {
+    gw.t = 0;
+    ++gw.g;
   }
 }
 
@@ -602,9 +677,9 @@ __device__ __forceinline__ void loader(const KArgs& A, u32 q0, u32 q1) {
     if (ns == 0) continue;
     LayerDesc Ld{};
     AttnItem it{};
-    const u32 nrt = o.epi == EPI_SWIGLU ? 2 * o.nrows : o.nrows;
-    const u32 lgp = o.opcode == OP_GEMV ? (u32)__builtin_ctz(o.ppr) : 0u;
     const GemvSeg gsg = gemv_seg(o);
+    GemvWalk gw{};
+    if (o.opcode == OP_GEMV) gw = gemv_walk(o, gsg, lane16 >> 4);
     const u32 mmv_nt = (o.epi == EPI_SWIGLU ? 2u : 1u) * ((o.nrows + 15) / 16);
     if (o.opcode == OP_ATTN || o.opcode == OP_DELTA) Ld = sload(A.layers + o.layer);
     if (o.opcode == OP_ATTN) it = ic.get(A, o.row0, attn_pps(A.d));
@@ -628,7 +703,7 @@ __device__ __forceinline__ void loader(const KArgs& A, u32 q0, u32 q1) {
         }
       }
       u32x4* dst = g_ring + (seq % NSLOT) * (SLOT / 16);
-      if (o.opcode == OP_GEMV) issue_gemv(gsg, s, nrt, lgp, lane16, dst);
+      if (o.opcode == OP_GEMV) issue_gemv(gsg, gw, lane16 >> 4, dst);
       else if (o.opcode == OP_MMV) issue_mmv(gsg, s, mmv_nt, o.nrows, o.epi == EPI_SWIGLU, lane16 >> 4, dst);
       else if (o.opcode == OP_ATTN) issue_attn(A, Ld, it, s, al, pw, lane16, dst);
       else issue_delta(A, Ld, o.row0, s, lane16, dst);
@@ -709,183 +784,270 @@ __device__ __forceinline__ void op_embed_finish(const KArgs& A, u32 w, u32& gen)
   }
 }
 
-// ------------------------------------------------------------------ GEMV (VALU, batch B)
+// ------------------------------------------------------------------ matrix-core and lane helpers
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Lane `l` of a float.  Takes the value by copy: clang's __builtin_bit_cast applied directly to an
+// element of an ext_vector (v[i]) reads element 0, so vector elements must never be its operand.
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+__device__ __forceinline__ float row_max16(float v) {  // max over the 16 lanes of a DPP row
+  v = fmaxf(v, dppf<0xB1>(v));
+  v = fmaxf(v, dppf<0x4E>(v));
+  v = fmaxf(v, dppf<0x141>(v));
+  return fmaxf(v, dppf<0x140>(v));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dppf<0xB1>(v);
+  v += dppf<0x4E>(v);
+  v += dppf<0x141>(v);
+  return v + dppf<0x140>(v);
+}
+
+// ------------------------------------------------------------------ GEMV (matrix cores, batch <= 4)
+// y_b = W x_b for B <= 4 sequences, on the matrix cores although the op is bound by the weight
+// stream: the 16x16x32 bf16 tiles take the multiply-adds off the vector ALUs (which are left with
+// the ring protocol) and cost the same for every B up to 4.  A tile's A operand is a row group of
+// R = 16 / P weight rows, each cut into P parts of 32 inputs (tile row m = r P + p); the B operand
+// holds the inputs cut the same way (column n = b P + p, x as bf16 hi + lo halves so that the
+// products keep fp32 accuracy).  Only the entries whose parts match belong to W x; each wave sums
+// them over p once per row group, after all of the group's pieces are accumulated.
+//
+// A lane's A and B elements sit at the same inputs: tile row / column block (lane & 15) / P (a
+// weight row of the group, or a sequence), inputs q 32 P + 32 ((lane & 15) % P) + 8 (lane >> 4)
+// + 0..7 of piece q.  The loader writes each piece in exactly that lane order.
 template <int B>
-struct MMax { static constexpr int v = B <= 2 ? 4 : (B <= 4 ? 2 : 1); };
+struct GemvWidth { static constexpr int P = B <= 2 ? 8 : 4; };
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-template <int B>
-__device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
-  constexpr int MM = MMax<B>::v;
-  const u32 lane = lane_id();
-  const u32 ppr = o.ppr, K = o.K;
-  const bool swiglu = o.epi == EPI_SWIGLU;
-  const u32 nrt = swiglu ? 2 * o.nrows : o.nrows;
-  const u32 M = ppr >= 8 ? ppr / 8 : 1;
-  const u32 RW = ppr >= 8 ? 8 : ppr;
+__device__ __forceinline__ u32 gemv_koff(u32 lane, u32 P) { return 32 * ((lane & 15) & (P - 1)) + 8 * (lane >> 4); }
 
-  // this wave's input fragments: piece kp covers elements [kp*512, kp*512+512), lane owns 8 of them
-  float xf[MM][B][8];
+// Wait until the ring holds slots below `need`; `avail` remembers how far g_filled had got, so a
+// batch already covered skips the LDS read.  Returns false on abort.
+#ifndef MK_POLL_SLEEP
+#define MK_POLL_SLEEP 0
+#endif
+__device__ __forceinline__ bool wait_avail(const KArgs& A, u32 need, u32& avail) {
+  Watchdog wd(A);
+  u32 f;
+  while ((f = lds_ld(&g_filled)) < need) {
+    if (aborted() || wd.expired()) return false;
+    __builtin_amdgcn_s_sleep(MK_POLL_SLEEP);
+  }
+  avail = f;
+  return true;
+}
+
+// d[i] for i = lane & 3: the entry of this lane whose tile row and column share their part (P = 4),
+// or may share it (P = 8).
+__device__ __forceinline__ float gemv_pick(const f32x4 d, u32 lane) {
+  const u32 j = lane & 3;
+  const float lo = (j & 1) ? d[1] : d[0], hi = (j & 1) ? d[3] : d[2];
+  return (j & 2) ? hi : lo;
+}
+
+// Sum one row group's matched entries over the parts and store this wave's partials: g_red[(row *
+// RW + j) * B + b] for the group's R rows and B sequences.
+template <int B, int P>
+__device__ __forceinline__ void gemv_extract(const f32x4 d, u32 lane, u32 g, u32 j, u32 RW, u32 nrt) {
+  constexpr u32 R = 16 / P;
+  float v = gemv_pick(d, lane);
+  if constexpr (P == 8) {
+    // tile row 4 (lane >> 4) + (lane & 3) is part 4 ((lane >> 4) & 1) + (lane & 3); the column is
+    // part lane & 7: they match in the low quad of each 8 lanes in even 16-lane rows and in the
+    // high quad in odd rows.  Mirror the odd rows' 8-lane halves so that both sit in the low quad.
+    if (((lane >> 2) ^ (lane >> 4)) & 1) v = 0.0f;
+    v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                              0x141, 0xA, 0xF, false));  // row_half_mirror, odd rows
+  }
+  v += dppf<0xB1>(v);  // quad sums
+  v += dppf<0x4E>(v);
+  if constexpr (P == 8) v = add_swap16(v);  // rows 2r and 2r + 1
+  // P = 4: lane 16 r + 4 b + q holds (row r, sequence b);  P = 8: lane 32 r + 8 b + q (q < 4)
+  const u32 r = P == 4 ? lane >> 4 : lane >> 5, b = P == 4 ? (lane >> 2) & 3 : (lane >> 3) & 1;
+  const bool mine = P == 4 ? (lane & 3) == 0 : (lane & 23) == 0;
+  const u32 row = g * R + r;
+  if (mine && b < (u32)B && row < nrt) g_red[(row * RW + j) * B + b] = v;
+}
+
+// One GEMV op with NF input fragments per wave (1, 2, or up to 8).  Row groups are taken GB at a
+// time (GB NF = 4 slots per wait for NF <= 2).  With PG < 8 pieces per group (NF = 1) a slot holds
+// 8 / PG groups and wave w works on group (slot 8 / PG + w / PG), piece w % PG.
+template <int B, int P, int NF>
+__device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
+  constexpr u32 R = 16 / P, KP = 32 * P;
+  constexpr u32 GB = NF == 1 ? 4 : (NF == 2 ? 2 : 1);
+  const u32 lane = lane_id();
+  const bool swiglu = o.epi == EPI_SWIGLU;
+  const u32 nrt = swiglu ? 2 * o.nrows : o.nrows;  // stream rows
+  const u32 nrg = nrt / R;                          // row groups
+  const u32 pg = o.ppr, K = o.K;
+  const u32 nf = pg >= 8 ? pg / 8 : 1;
+  const u32 RW = pg >= 8 ? 8 : pg;
+  const u32 bl = (lane & 15) / P;  // this lane's sequence in the B operand
+  const u32 koff = gemv_koff(lane, P);
+  // this lane's A operand in a slot: row segment seg, inputs piece * KP + koff of it, at the chunk's
+  // swizzled position in its 1 KB block
+  const u32 lgrs = gemv_lg_rs(P, pg), sb = 8192u >> lgrs;
+  const u32 seg = (pg >= 8 ? 0u : (w / pg) * R) + (lane & 15) / P;
+  const u32 abyte = seg * sb + 2 * ((pg >= 8 ? w : w % pg) * KP + koff);
+  const u32 achunk = (abyte >> 10) * 64 + gemv_pos((abyte & 1023) >> 4, abyte >> 10, lgrs);
+
+  // this wave's input fragments: fragment f is piece 8 f + w of every row group (w % PG if PG < 8)
+  float xf[NF][8];
 #pragma unroll
-  for (int t = 0; t < MM; ++t) {
-    const u32 kp = ppr >= 8 ? w + 8 * t : w % ppr;
-    const u32 k0 = kp * PIECE_ELEMS + lane * 8;
-    const bool valid = (u32)t < M && kp < ppr && k0 < K;
+  for (int f = 0; f < NF; ++f) {
+    const u32 q = pg >= 8 ? 8 * f + w : w % pg;
+    const u32 k0 = q * KP + koff;
+    if ((u32)f < nf && bl < (u32)B && k0 < K) ld8_sc1((const float*)o.in + (size_t)bl * o.ld_in + k0, xf[f]);
+    else {
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      if (valid) ld8_sc1((const float*)o.in + (size_t)b * o.ld_in + k0, xf[t][b]);
-      else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xf[t][b][e] = 0.0f;
-      }
+      for (int e = 0; e < 8; ++e) xf[f][e] = 0.0f;
     }
   }
   if (o.norm) {
-    const bool distinct = ppr >= 8 || w < ppr;
+    // sum of squares per sequence: each input appears once among the waves with distinct pieces
+    float ss = 0.0f;
+    if (pg >= 8 || w < pg) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += xf[f][e] * xf[f][e];
+    }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      float ss = 0.0f;
-      if (distinct) {
-#pragma unroll
-        for (int t = 0; t < MM; ++t)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ss += xf[t][b][e] * xf[t][b][e];
-      }
-      ss = wave_sum(ss);
-      if (lane == 0) g_scr[w * B + b] = ss;
+      const float t = wave_sum(bl == (u32)b ? ss : 0.0f);
+      if (lane == 0) g_scr[w * B + b] = t;
     }
     if (!cbar(A, gen)) return false;
-    float rstd[B];
+    float rstd = 1.0f;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       float tot = 0.0f;
       for (int j = 0; j < NC; ++j) tot += g_scr[j * B + b];
-      rstd[b] = 1.0f / sqrtf(tot / (float)K + A.rms_eps);
+      if (bl == (u32)b) rstd = 1.0f / sqrtf(tot / (float)K + A.rms_eps);
     }
     const uint16_t* gm = (const uint16_t*)o.gamma;
 #pragma unroll
-    for (int t = 0; t < MM; ++t) {
-      const u32 kp = ppr >= 8 ? w + 8 * t : w % ppr;
-      const u32 k0 = kp * PIECE_ELEMS + lane * 8;
-      if ((u32)t < M && kp < ppr && k0 < K) {
-        const u32x4 gv = *(const u32x4*)(gm + k0);
+    for (int f = 0; f < NF; ++f) {
+      const u32 q = pg >= 8 ? 8 * f + w : w % pg;
+      const u32 k0 = q * KP + koff;
+      if ((u32)f < nf && bl < (u32)B && k0 < K) {
+        const u32x4 gv = *(const __attribute__((address_space(1))) u32x4*)(gm + k0);
         const float g[8] = {bflo(gv.x), bfhi(gv.x), bflo(gv.y), bfhi(gv.y),
                             bflo(gv.z), bfhi(gv.z), bflo(gv.w), bfhi(gv.w)};
 #pragma unroll
-        for (int b = 0; b < B; ++b)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xf[t][b][e] *= rstd[b] * g[e];
+        for (int e = 0; e < 8; ++e) xf[f][e] *= rstd * g[e];
       }
     }
   }
+  bf16x8 xh[NF], xl[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    u32x4 h, l;
+    split_bf16x8(xf[f], h, l);
+    xh[f] = __builtin_bit_cast(bf16x8, h);
+    xl[f] = __builtin_bit_cast(bf16x8, l);
+  }
 
-  // stream the tile: wave w takes piece w of every slot, GEMV_BATCH slots at a time.
-  // Each slot gets its own partial sum; the batch then folds them by row shape:
-  //   ppr <= 8  (lgm 0): every slot ends one row of this wave -> four rows per reduction;
-  //   ppr == 16 (lgm 1): slot pairs form rows                  -> two rows per reduction;
-  //   ppr >= 32 (lgm 2+): a row spans whole batches           -> running sum, reduced at row end.
-  // With four or more sequences the four values folded together are the sequences of one row.
-  static_assert(GEMV_BATCH == 4, "the batched reduction folds four slots");
-  const u32 lgp = (u32)__builtin_ctz(ppr);  // ppr is a power of two
-  const u32 lgm = ppr >= 8 ? lgp - 3 : 0;   // log2(slots per row)
-  const u32 mmask = (1u << lgm) - 1;
-  float racc[B];
-  for (u32 s0 = 0; s0 < o.nslots; s0 += GEMV_BATCH) {
-    const u32 nb = min((u32)GEMV_BATCH, o.nslots - s0);
-    if (!wait_full(A, seq + nb - 1)) return false;  // slots are published in order
-    u32x4 wv[GEMV_BATCH];
+  u32 avail = seq;
+  if (NF > 1 || pg >= 8) {
+    // groups in order; a group's nf slots are consecutive and wave w takes piece w of each
+    u32 g0 = 0;
+    if constexpr (NF <= 2) {
+      // whole batches of GB groups (NF = nf here): straight-line code, so the groups' matrix-core
+      // chains and extractions interleave
+      constexpr u32 NS = GB * NF;
+      for (; g0 + GB <= nrg; g0 += GB) {
+        if (seq + NS > avail && !wait_avail(A, seq + NS, avail)) return false;
+        u32x4 wv[NS];
 #pragma unroll
-    for (int i = 0; i < GEMV_BATCH; ++i)
-      if ((u32)i < nb) wv[i] = g_ring[((seq + i) % NSLOT) * (SLOT / 16) + w * 64 + lane];
-    release_upto(w, seq + nb);
-    if constexpr (B >= 4) {
-      // wide batches: one running sum per sequence, reduced four sequences at a time at each row end
+        for (u32 i = 0; i < NS; ++i) wv[i] = g_ring[((seq + i) % NSLOT) * (SLOT / 16) + achunk];
+        release_upto(w, seq + NS);
+        f32x4 dh[GB], dl[GB];
 #pragma unroll
-      for (int i = 0; i < GEMV_BATCH; ++i) {
-        if ((u32)i < nb) {
-          const u32 s = s0 + i, t = s & mmask;
-          if (t == 0) {
+        for (u32 gb = 0; gb < GB; ++gb) {
+          dh[gb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          dl[gb] = dh[gb];
+        }
 #pragma unroll
-            for (int b = 0; b < B; ++b) racc[b] = 0.0f;
+        for (u32 f = 0; f < NF; ++f)
+#pragma unroll
+          for (u32 gb = 0; gb < GB; ++gb) {
+            const bf16x8 a = __builtin_bit_cast(bf16x8, wv[gb * NF + f]);
+            dh[gb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xh[f], dh[gb], 0, 0, 0);
+            dl[gb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl[f], dl[gb], 0, 0, 0);
           }
-          const u32x4 q = wv[i];
-          const float wf[8] = {bflo(q.x), bfhi(q.x), bflo(q.y), bfhi(q.y), bflo(q.z), bfhi(q.z), bflo(q.w), bfhi(q.w)};
 #pragma unroll
-          for (int tt = 0; tt < MM; ++tt) {
-            if ((u32)tt == t) {
-#pragma unroll
-              for (int b = 0; b < B; ++b)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) racc[b] += wf[e] * xf[tt][b][e];
-            }
-          }
-          if (t == mmask) {
-            const u32 rl = lgm == 0 ? (s * SLOT_PIECES + w) >> lgp : s >> lgm;
-            const u32 j = w & (RW - 1);
-#pragma unroll
-            for (int b0 = 0; b0 < B; b0 += 4) {
-              const float r = reduce4(racc[b0], racc[b0 + 1], racc[b0 + 2], racc[b0 + 3]);
-              if (lane < 4 && rl < nrt) g_red[(rl * RW + j) * B + b0 + lane] = r;
-            }
-          }
-        }
-      }
-    } else {
-      float acc[GEMV_BATCH][B];
-#pragma unroll
-      for (int i = 0; i < GEMV_BATCH; ++i) {
-#pragma unroll
-        for (int b = 0; b < B; ++b) acc[i][b] = 0.0f;
-        if ((u32)i < nb) {
-          // no lane or row test: inputs of lanes past the row's end are zero and every ring byte is
-          // a finite weight, so those products vanish; rows past the op are never stored
-          const u32 t = (s0 + i) & mmask;  // which 8-piece group of its row this slot holds
-          const u32x4 q = wv[i];
-          const float wf[8] = {bflo(q.x), bfhi(q.x), bflo(q.y), bfhi(q.y), bflo(q.z), bfhi(q.z), bflo(q.w), bfhi(q.w)};
-#pragma unroll
-          for (int tt = 0; tt < MM; ++tt) {
-            if ((u32)tt == t) {
-#pragma unroll
-              for (int b = 0; b < B; ++b)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[i][b] += wf[e] * xf[tt][b][e];
-            }
-          }
-        }
-      }
-      if (lgm == 0) {
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-          const float r = reduce4(acc[0][b], acc[1][b], acc[2][b], acc[3][b]);
-          if (lane < nb) {
-            const u32 rl = ((s0 + lane) * SLOT_PIECES + w) >> lgp;  // row of slot s0 + lane
-            const u32 j = w & (RW - 1);
-            if (rl < nrt) g_red[(rl * RW + j) * B + b] = r;
-          }
-        }
-      } else if (lgm == 1) {
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-          const float r = reduce4(acc[0][b] + acc[1][b], acc[2][b] + acc[3][b], 0.0f, 0.0f);
-          const u32 rl = (s0 >> 1) + lane;
-          if (lane < nb / 2 && rl < nrt) g_red[(rl * RW + w) * B + b] = r;
-        }
-      } else {
-        if ((s0 & mmask) == 0) {
-#pragma unroll
-          for (int b = 0; b < B; ++b) racc[b] = 0.0f;
-        }
-#pragma unroll
-        for (int b = 0; b < B; ++b) racc[b] += (acc[0][b] + acc[1][b]) + (acc[2][b] + acc[3][b]);
-        if (((s0 + nb) & mmask) == 0) {  // this batch ends the row
-          const u32 rl = s0 >> lgm;
-          const float r = reduce4(racc[0], B > 1 ? racc[B > 1 ? 1 : 0] : 0.0f, 0.0f, 0.0f);
-          if (lane < (u32)B && rl < nrt) g_red[(rl * RW + w) * B + lane] = r;
-        }
+        for (u32 gb = 0; gb < GB; ++gb) gemv_extract<B, P>(dh[gb] + dl[gb], lane, g0 + gb, w, RW, nrt);
+        seq += NS;
       }
     }
-    seq += nb;
+    // remaining groups one at a time (every group when NF = 8, with nf <= 8 slots each)
+    for (; g0 < nrg; ++g0) {
+      if (seq + nf > avail && !wait_avail(A, seq + nf, avail)) return false;
+      u32x4 wv[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        if ((u32)f < nf) wv[f] = g_ring[((seq + f) % NSLOT) * (SLOT / 16) + achunk];
+      release_upto(w, seq + nf);
+      // two accumulators per half (even / odd fragments) keep four chains in flight
+      f32x4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0, d2 = d0, d3 = d0;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        if ((u32)f < nf) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, wv[f]);
+          if (f & 1) {
+            d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xh[f], d1, 0, 0, 0);
+            d3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl[f], d3, 0, 0, 0);
+          } else {
+            d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xh[f], d0, 0, 0, 0);
+            d2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl[f], d2, 0, 0, 0);
+          }
+        }
+      }
+      gemv_extract<B, P>((d0 + d1) + (d2 + d3), lane, g0, w, RW, nrt);
+      seq += nf;
+    }
+  } else {
+    // PG < 8: each slot holds 8 / PG groups, one piece of a group per wave
+    const u32 lgpg = (u32)__builtin_ctz(pg);
+    const u32 gsub = w >> lgpg;          // this wave's group within a slot
+    const u32 full = nrg >> (3 - lgpg);  // slots whose groups all exist
+    u32 s0 = 0;
+    for (; s0 + 4 <= full; s0 += 4) {
+      if (seq + 4 > avail && !wait_avail(A, seq + 4, avail)) return false;
+      u32x4 wv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[i] = g_ring[((seq + i) % NSLOT) * (SLOT / 16) + achunk];
+      release_upto(w, seq + 4);
+      f32x4 d[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, wv[i]);
+        d[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xh[0], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        d[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl[0], d[i], 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gemv_extract<B, P>(d[i], lane, (((s0 + i) * 8) >> lgpg) + gsub, w & (pg - 1), RW, nrt);
+      seq += 4;
+    }
+    for (; s0 < o.nslots; ++s0) {
+      if (seq + 1 > avail && !wait_avail(A, seq + 1, avail)) return false;
+      const u32x4 wv = g_ring[(seq % NSLOT) * (SLOT / 16) + achunk];
+      release_upto(w, seq + 1);
+      const u32 g = ((s0 * 8) >> lgpg) + gsub;
+      if (g < nrg) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, wv);
+        f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xh[0], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl[0], d, 0, 0, 0);
+        gemv_extract<B, P>(d, lane, g, w & (pg - 1), RW, nrt);
+      }
+      seq += 1;
+    }
   }
   if (!cbar(A, gen)) return false;
 
@@ -914,40 +1076,13 @@ __device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32&
   return true;
 }
 
-// ------------------------------------------------------------------ matrix-core and lane helpers
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// Lane `l` of a float.  Takes the value by copy: clang's __builtin_bit_cast applied directly to an
-// element of an ext_vector (v[i]) reads element 0, so vector elements must never be its operand.
-__device__ __forceinline__ float readlane_f(float x, int l) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
-}
-__device__ __forceinline__ float row_max16(float v) {  // max over the 16 lanes of a DPP row
-  v = fmaxf(v, dppf<0xB1>(v));
-  v = fmaxf(v, dppf<0x4E>(v));
-  v = fmaxf(v, dppf<0x141>(v));
-  return fmaxf(v, dppf<0x140>(v));
-}
-__device__ __forceinline__ float row_sum16(float v) {
-  v += dppf<0xB1>(v);
-  v += dppf<0x4E>(v);
-  v += dppf<0x141>(v);
-  return v + dppf<0x140>(v);
-}
-// x = hi + lo with both halves bf16 (hi rounded to nearest, lo the rounded remainder)
-__device__ __forceinline__ void split_bf16x8(const float* x, u32x4& hi, u32x4& lo) {
-  u32 h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const u32 h0 = f2bf(x[2 * e]), h1 = f2bf(x[2 * e + 1]);
-    const u32 l0 = f2bf(x[2 * e] - __builtin_bit_cast(float, h0 << 16));
-    const u32 l1 = f2bf(x[2 * e + 1] - __builtin_bit_cast(float, h1 << 16));
-    h[e] = h0 | (h1 << 16);
-    l[e] = l0 | (l1 << 16);
-  }
-  hi = u32x4{h[0], h[1], h[2], h[3]};
-  lo = u32x4{l[0], l[1], l[2], l[3]};
+template <int B>
+__device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
+  constexpr int P = GemvWidth<B>::P;
+  const u32 pg = o.ppr;
+  if (pg <= 8) return op_gemv_nf<B, P, 1>(A, o, w, seq, gen);
+  if (pg == 16) return op_gemv_nf<B, P, 2>(A, o, w, seq, gen);
+  return op_gemv_nf<B, P, 8>(A, o, w, seq, gen);
 }
 
 // ------------------------------------------------------------------ MATRIX-CORE GEMV (batch 8)

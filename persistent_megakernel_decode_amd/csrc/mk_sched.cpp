@@ -74,14 +74,22 @@ std::string validate_desc(const mk_model_desc* desc, ModelShape* out, mk_status*
   return "";
 }
 
-// Pieces per row, rounded up to a power of two so the kernel indexes pieces with shifts.
-static int pad_ppr(int K) {
-  const int real = (K + PIECE_ELEMS - 1) / PIECE_ELEMS;
-  int p = 1;
-  while (p < real) p *= 2;
-  return p;
+// GEMV ops (batch <= 4) run on the matrix cores in row groups of R = 16 / P rows, each row cut into
+// pieces of 32 P inputs.  P = 8 for one or two sequences, 4 for up to four (P x batch <= 16).
+static int gemv_part(int B) { return B <= 2 ? 8 : 4; }
+// Pieces per row group: ceil(K / (32 P)) rounded up to 1, 2, 4, or a multiple of 8 (8 pieces fill a
+// ring slot, one per compute wave).
+static int gemv_pg(int K, int P) {
+  const int real = (K + 32 * P - 1) / (32 * P);
+  if (real <= 8) {
+    int p = 1;
+    while (p < real) p *= 2;
+    return p;
+  }
+  return (real + 7) / 8 * 8;
 }
-static int mmax_for(int B) { return B <= 2 ? 4 : (B <= 4 ? 2 : 1); }
+static bool gemv_pg_ok(uint32_t pg) { return pg == 1 || pg == 2 || pg == 4 || (pg % 8 == 0 && pg <= (uint32_t)GEMV_MAX_PG); }
+static uint32_t gemv_slots(uint32_t nrg, uint32_t pg) { return pg >= 8 ? nrg * (pg / 8) : (nrg * pg + 7) / 8; }
 
 namespace {
 struct Builder {
@@ -106,8 +114,9 @@ struct Builder {
       mmv(stage, wait, layer, N, K, epi, norm, W, W2, W3, b1, b2, in, ld_in, gamma, out, ld_out, res);
       return;
     }
-    const int ppr = pad_ppr((int)K);
-    if (ppr >= 8 && ppr / 8 > mmax_for(B)) {
+    const int Pp = gemv_part(B), R = 16 / Pp;
+    const int pg = gemv_pg((int)K, Pp);
+    if (pg > GEMV_MAX_PG) {
       err = fmt("projection with %u inputs is too long for batch width %d", K, B);
       return;
     }
@@ -115,17 +124,24 @@ struct Builder {
       err = fmt("projection input length %u is not a multiple of 8", K);
       return;
     }
-    const int RW = std::min(ppr, 8);
+    if (N % R || (b1 < N && b1 % R) || (b2 < N && b2 % R)) {
+      err = fmt("projection rows (%u, split at %u / %u) must come in groups of %d", N, b1, b2, R);
+      return;
+    }
+    const int RW = std::min(pg, 8);
     const int mult = epi == EPI_SWIGLU ? 2 : 1;
-    const uint32_t maxrows = (uint32_t)(RED_FLOATS / (RW * B * mult));
-    uint32_t T = std::min<uint32_t>((uint32_t)n_cus, N);
-    if ((N + T - 1) / T > maxrows) {
+    uint32_t maxrows = (uint32_t)(RED_FLOATS / (RW * B * mult));
+    maxrows -= maxrows % R;
+    // tiles of whole row groups, as even as the groups allow
+    const uint32_t NG = N / R;
+    uint32_t T = std::min<uint32_t>((uint32_t)n_cus, NG);
+    if ((NG + T - 1) / T * R > maxrows) {
       T = (N + maxrows - 1) / maxrows;
       T = (T + n_cus - 1) / n_cus * n_cus;
     }
     const uint32_t bnd[3] = {b1, b2, 0xFFFFFFFFu};
     for (uint32_t t = 0; t < T; ++t) {
-      const uint32_t t0 = (uint32_t)((uint64_t)N * t / T), t1 = (uint32_t)((uint64_t)N * (t + 1) / T);
+      const uint32_t t0 = R * (uint32_t)((uint64_t)NG * t / T), t1 = R * (uint32_t)((uint64_t)NG * (t + 1) / T);
       for (uint32_t r0 = t0, r1; r0 < t1; r0 = r1) {
       // an op streams at most two weight runs: cut a tile that would touch three tensors
       r1 = t1;
@@ -143,8 +159,9 @@ struct Builder {
       o.row0 = r0;
       o.nrows = r1 - r0;
       o.K = K;
-      o.ppr = (uint32_t)ppr;
-      o.nslots = (o.nrows * mult * ppr + SLOT_PIECES - 1) / SLOT_PIECES;
+      o.part = (uint8_t)Pp;
+      o.ppr = (uint32_t)pg;
+      o.nslots = gemv_slots(o.nrows * mult / R, (uint32_t)pg);
       o.ld_in = ld_in;
       o.ld_out = ld_out;
       // weight runs: at most two contiguous row runs per op
@@ -456,12 +473,19 @@ int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
       seen[o.sig_stage]++;
       idx[o.sig_stage].push_back(o.sig_index);
       if (o.opcode == OP_GEMV) {
-        const int mult = o.epi == EPI_SWIGLU ? 2 : 1;
-        const uint32_t RW = std::min<uint32_t>(o.ppr, 8);
+        const uint32_t mult = o.epi == EPI_SWIGLU ? 2 : 1;
+        const uint32_t Pp = o.part, R = Pp ? 16 / Pp : 1, pg = o.ppr;
+        const uint32_t RW = std::min<uint32_t>(pg, 8);
+        if (P.kernel_batch > 4) bad(fmt("cu %d op %u: matrix-core GEMV takes at most 4 sequences", c, i));
+        if (Pp != (uint32_t)gemv_part(P.kernel_batch)) bad(fmt("cu %d op %u: %u input parts for batch %d", c, i, Pp, P.kernel_batch));
+        if (!gemv_pg_ok(pg)) bad(fmt("cu %d op %u: %u pieces per row group", c, i, pg));
+        if ((uint64_t)pg * 32 * Pp < o.K) bad(fmt("cu %d op %u: pieces do not cover a row", c, i));
+        if (o.nrows == 0 || o.nrows % R) bad(fmt("cu %d op %u: %u rows, not whole groups of %u", c, i, o.nrows, R));
+        if (o.epi != EPI_SWIGLU && o.b1 < o.nrows && o.b1 % R) bad(fmt("cu %d op %u: weight runs split a row group", c, i));
+        if (o.epi == EPI_SWIGLU && o.b1 != o.nrows) bad(fmt("cu %d op %u: gate / up runs", c, i));
         if ((uint64_t)o.nrows * mult * RW * P.kernel_batch > (uint64_t)RED_FLOATS)
           bad(fmt("cu %d op %u: tile exceeds the partial-sum area", c, i));
-        if (o.nslots * SLOT_PIECES < o.nrows * mult * o.ppr) bad(fmt("cu %d op %u: too few slots", c, i));
-        if (o.ppr * PIECE_ELEMS < o.K) bad(fmt("cu %d op %u: pieces do not cover a row", c, i));
+        if (o.nslots != gemv_slots(o.nrows * mult / R, pg)) bad(fmt("cu %d op %u: slot count", c, i));
       }
       if (o.opcode == OP_MMV) {
         const uint32_t ntiles = (o.epi == EPI_SWIGLU ? 2 : 1) * ((o.nrows + 15) / 16);

@@ -47,8 +47,8 @@ def test_plan_is_valid_and_balanced(name):
     info = mkd.mk_plan(_desc(cfg, 4096 + 256), 256)
     assert info.errors == 0, mkd.mk_last_error()
     assert info.n_stages >= 3 * cfg.n_layers
-    if name != "tiny":  # every unit streams the same weight bytes to within a row per stage
-        assert info.max_cu_bytes <= 1.02 * info.mean_cu_bytes
+    if name != "tiny":  # every unit streams the same weight bytes to within a row group per stage
+        assert info.max_cu_bytes <= 1.03 * info.mean_cu_bytes
 
 
 def test_plan_for_other_unit_counts():
