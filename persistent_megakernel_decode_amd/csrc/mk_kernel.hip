@@ -896,20 +896,34 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   const u32 abyte = seg * sb + 2 * ((pg >= 8 ? w : w % pg) * KP + koff);
   const u32 achunk = (abyte >> 10) * 64 + gemv_pos((abyte & 1023) >> 4, abyte >> 10, lgrs);
 
-  // this wave's input fragments: fragment f is piece 8 f + w of every row group (w % PG if PG < 8)
+  // this wave's input fragments: fragment f is piece 8 f + w of every row group (w % PG if PG < 8).
+  // RMSNorm factors out of the sum: the tiles multiply x * gain (input and gain loads share one
+  // round trip) and the epilogue scales each output by (mean x^2 + eps)^-1/2, so no barrier stands
+  // between the loads and the stream.
   float xf[NF][8];
+  u32x4 gv[NF];
+  const uint16_t* gm = (const uint16_t*)o.gamma;
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const u32 q = pg >= 8 ? 8 * f + w : w % pg;
     const u32 k0 = q * KP + koff;
-    if ((u32)f < nf && bl < (u32)B && k0 < K) ld8_sc1((const float*)o.in + (size_t)bl * o.ld_in + k0, xf[f]);
+    const bool v = (u32)f < nf && bl < (u32)B && k0 < K;
+    if (v) ld8_sc1((const float*)o.in + (size_t)bl * o.ld_in + k0, xf[f]);
     else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) xf[f][e] = 0.0f;
     }
+    gv[f] = v && o.norm ? *(const __attribute__((address_space(1))) u32x4*)(gm + k0) : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   }
+  // residual rows of this thread (epilogue row r = thread index), fetched now, off the critical path
+  const u32 tid = w * 64 + lane;
+  float rv[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+    rv[b] = o.epi == EPI_RESID && tid < o.nrows ? ld_sc1((const float*)o.res + (size_t)b * o.ld_out + o.row0 + tid) : 0.0f;
   if (o.norm) {
-    // sum of squares per sequence: each input appears once among the waves with distinct pieces
+    // sum of squares per sequence (each input appears once among the waves with distinct pieces),
+    // read back in the epilogue
     float ss = 0.0f;
     if (pg >= 8 || w < pg) {
 #pragma unroll
@@ -922,26 +936,12 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
       const float t = wave_sum(bl == (u32)b ? ss : 0.0f);
       if (lane == 0) g_scr[w * B + b] = t;
     }
-    if (!cbar(A, gen)) return false;
-    float rstd = 1.0f;
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      float tot = 0.0f;
-      for (int j = 0; j < NC; ++j) tot += g_scr[j * B + b];
-      if (bl == (u32)b) rstd = 1.0f / sqrtf(tot / (float)K + A.rms_eps);
-    }
-    const uint16_t* gm = (const uint16_t*)o.gamma;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const u32 q = pg >= 8 ? 8 * f + w : w % pg;
-      const u32 k0 = q * KP + koff;
-      if ((u32)f < nf && bl < (u32)B && k0 < K) {
-        const u32x4 gv = *(const __attribute__((address_space(1))) u32x4*)(gm + k0);
-        const float g[8] = {bflo(gv.x), bfhi(gv.x), bflo(gv.y), bfhi(gv.y),
-                            bflo(gv.z), bfhi(gv.z), bflo(gv.w), bfhi(gv.w)};
+      const u32x4 g4 = gv[f];
+      const float g[8] = {bflo(g4.x), bfhi(g4.x), bflo(g4.y), bfhi(g4.y), bflo(g4.z), bfhi(g4.z), bflo(g4.w), bfhi(g4.w)};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xf[f][e] *= rstd * g[e];
-      }
+      for (int e = 0; e < 8; ++e) xf[f][e] *= g[e];
     }
   }
   bf16x8 xh[NF], xl[NF];
@@ -1052,18 +1052,29 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   if (!cbar(A, gen)) return false;
 
   // epilogue: one output row per compute thread
-  for (u32 r = w * 64 + lane; r < o.nrows; r += NC * 64) {
+  float rstd[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    rstd[b] = 1.0f;
+    if (o.norm) {
+      float tot = 0.0f;
+      for (int j = 0; j < NC; ++j) tot += g_scr[j * B + b];
+      rstd[b] = 1.0f / sqrtf(tot / (float)K + A.rms_eps);
+    }
+  }
+  for (u32 r = tid; r < o.nrows; r += NC * 64) {
     const u32 row = o.row0 + r;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       float v = 0.0f;
       for (u32 j = 0; j < RW; ++j) v += g_red[(r * RW + j) * B + b];
+      v *= rstd[b];
       if (o.epi == EPI_SWIGLU) {
         float u = 0.0f;
         for (u32 j = 0; j < RW; ++j) u += g_red[((r + o.nrows) * RW + j) * B + b];
-        st_sc1((float*)o.out + (size_t)b * o.ld_out + row, silu(v) * u);
+        st_sc1((float*)o.out + (size_t)b * o.ld_out + row, silu(v) * (u * rstd[b]));
       } else if (o.epi == EPI_RESID) {
-        const float x = ld_sc1((const float*)o.res + (size_t)b * o.ld_out + row);
+        const float x = r == tid ? rv[b] : ld_sc1((const float*)o.res + (size_t)b * o.ld_out + row);
         st_sc1((float*)o.out + (size_t)b * o.ld_out + row, x + v);
       } else if (o.epi == EPI_STORE) {
         st_sc1((float*)o.out + (size_t)b * o.ld_out + row, v);
@@ -1472,8 +1483,8 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   if (!cbar(A, gen)) return false;
   if (lds_ld(&g_bcast[0])) {  // last chunk of (b, kvh): log-sum-exp merge of all its chunks
     // Loads are issued ahead of their use: thread t owns output (head t / D, dim t % D) and loads
-    // that output of 16 chunks at a time; threads t < n_b * G also fetch one (m, l) pair for the
-    // LDS table every thread reads, in the same round trip as the first 16 outputs.
+    // that output of MC chunks at a time (one round trip for up to MC chunks); threads t < n_b * G
+    // also fetch one (m, l) pair for the LDS table every thread reads, in the same round trip.
     static_assert(GMAX * D <= NC * 64, "one merged output per thread");
     const int tid = (int)(w * 64 + lane), nb = it.n_b;
     const float* part0 = (const float*)Ld.part + (size_t)it.first_item * GMAX * (D + 2);
@@ -1487,9 +1498,10 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
       lv = ld_sc1(pc + 1);
     }
     const float* po = part0 + g * (D + 2) + 2 + dim;
-    float oc[16];
+    constexpr int MC = 16;
+    float oc[MC];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) oc[k] = has_o && k < nb ? ld_sc1(po + (size_t)k * cstride) : 0.0f;
+    for (int k = 0; k < MC; ++k) oc[k] = has_o && k < nb ? ld_sc1(po + (size_t)k * cstride) : 0.0f;
     float* ml = g_red;  // [n_b][G][m, l]
     if (has_ml) { ml[2 * tid] = mv; ml[2 * tid + 1] = lv; }
     if (!cbar(A, gen)) return false;
@@ -1497,13 +1509,13 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
       float M = -INFINITY;
       for (int c = 0; c < nb; ++c) M = fmaxf(M, ml[2 * (c * G + g)]);
       float den = 0.0f, num = 0.0f;
-      for (int c0 = 0; c0 < nb; c0 += 16) {
+      for (int c0 = 0; c0 < nb; c0 += MC) {
         if (c0 > 0) {
 #pragma unroll
-          for (int k = 0; k < 16; ++k) oc[k] = c0 + k < nb ? ld_sc1(po + (size_t)(c0 + k) * cstride) : 0.0f;
+          for (int k = 0; k < MC; ++k) oc[k] = c0 + k < nb ? ld_sc1(po + (size_t)(c0 + k) * cstride) : 0.0f;
         }
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < MC; ++k) {
           if (c0 + k < nb) {
             const float f = __expf(ml[2 * ((c0 + k) * G + g)] - M);
             den += f * ml[2 * ((c0 + k) * G + g) + 1];
