@@ -522,17 +522,6 @@ __device__ __forceinline__ void issue_gemv(const GemvSeg& gsg, GemvWalk& gw, u32
     ++gw.s;
     return;
   }
-#ifdef MK_WALK_RESTATE
-  gw.s = __builtin_amdgcn_readfirstlane(gw.s);
-  gw.g = __builtin_amdgcn_readfirstlane(gw.g);
-  gw.t = __builtin_amdgcn_readfirstlane(gw.t);
-  gw.pg = __builtin_amdgcn_readfirstlane(gw.pg);
-  gw.nf = __builtin_amdgcn_readfirstlane(gw.nf);
-  gw.R = __builtin_amdgcn_readfirstlane(gw.R);
-  gw.lgrs = __builtin_amdgcn_readfirstlane(gw.lgrs);
-  gw.nrt = __builtin_amdgcn_readfirstlane(gw.nrt);
-  gw.K = __builtin_amdgcn_readfirstlane(gw.K);
-#endif
   const u32 rho0 = gw.pg >= 8 ? gw.g * gw.R : gw.s << gw.lgrs;
   const u32 rs = 1u << gw.lgrs, half = 4096u >> gw.lgrs;  // segments; inputs per segment
   const u32 kappa0 = gw.pg >= 8 ? gw.t * half : 0u;
@@ -827,15 +816,12 @@ __device__ __forceinline__ u32 gemv_koff(u32 lane, u32 P) { return 32 * ((lane &
 
 // Wait until the ring holds slots below `need`; `avail` remembers how far g_filled had got, so a
 // batch already covered skips the LDS read.  Returns false on abort.
-#ifndef MK_POLL_SLEEP
-#define MK_POLL_SLEEP 0
-#endif
 __device__ __forceinline__ bool wait_avail(const KArgs& A, u32 need, u32& avail) {
   Watchdog wd(A);
   u32 f;
   while ((f = lds_ld(&g_filled)) < need) {
     if (aborted() || wd.expired()) return false;
-    __builtin_amdgcn_s_sleep(MK_POLL_SLEEP);
+    __builtin_amdgcn_s_sleep(0);
   }
   avail = f;
   return true;
