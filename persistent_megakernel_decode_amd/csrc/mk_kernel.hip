@@ -859,6 +859,67 @@ __device__ __forceinline__ void gemv_extract(const f32x4 d, u32 lane, u32 g, u32
   if (mine && b < (u32)B && row < nrt) g_red[(row * RW + j) * B + b] = v;
 }
 
+// Per-row-group accumulation.  Two or more sequences make the projection a (skinny) matrix
+// product: each piece is two 16x16x32 tiles on the matrix cores (inputs hi and lo) and the group
+// is extracted with gemv_extract.  One sequence makes it a matrix-vector product: each lane takes
+// the dot product of its 8 weights with its 8 inputs on the vector ALUs (v_dot2c_f32_bf16 against
+// the hi and lo halves), accumulates the group's pieces, and the group's two rows are reduced
+// across the wave once (wavefront shuffles).
+__device__ __forceinline__ float dot2(u32 wp, u32 xp, float acc) {  // acc + two bf16 products (exact in fp32)
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp), __builtin_bit_cast(bf16x2, xp), acc, false);
+}
+template <int B, int P>
+struct GemvAcc {
+  f32x4 h, l;
+  __device__ __forceinline__ void init() {
+    h = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    l = h;
+  }
+  __device__ __forceinline__ void add(const u32x4 wv, const bf16x8 xh, const bf16x8 xl) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, wv);
+    h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xh, h, 0, 0, 0);
+    l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl, l, 0, 0, 0);
+  }
+  __device__ __forceinline__ void merge(const GemvAcc& o) {
+    h += o.h;
+    l += o.l;
+  }
+  __device__ __forceinline__ void finish(u32 lane, u32 g, u32 j, u32 RW, u32 nrt) {
+    gemv_extract<B, P>(h + l, lane, g, j, RW, nrt);
+  }
+};
+template <>
+struct GemvAcc<1, 8> {
+  float h, l;
+  __device__ __forceinline__ void init() { h = l = 0.0f; }
+  __device__ __forceinline__ void add(const u32x4 wv, const bf16x8 xh8, const bf16x8 xl8) {
+    const u32x4 xh = __builtin_bit_cast(u32x4, xh8), xl = __builtin_bit_cast(u32x4, xl8);
+    h = dot2(wv.x, xh.x, h);
+    l = dot2(wv.x, xl.x, l);
+    h = dot2(wv.y, xh.y, h);
+    l = dot2(wv.y, xl.y, l);
+    h = dot2(wv.z, xh.z, h);
+    l = dot2(wv.z, xl.z, l);
+    h = dot2(wv.w, xh.w, h);
+    l = dot2(wv.w, xl.w, l);
+  }
+  __device__ __forceinline__ void merge(const GemvAcc& o) {
+    h += o.h;
+    l += o.l;
+  }
+  // Lane l holds row (l >> 3) & 1 of the group: fold lane bits 0-2 (quad steps and the half-row
+  // mirror), 4 and 5 (lane-16 and lane-32 swaps), keeping bit 3 apart; lanes 0 and 8 store.
+  __device__ __forceinline__ void finish(u32 lane, u32 g, u32 j, u32 RW, u32 nrt) {
+    float v = h + l;
+    v += dppf<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dppf<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dppf<0x141>(v);  // row_half_mirror: the other quad of the 8 lanes
+    v = add_swap32(add_swap16(v));
+    const u32 row = 2 * g + ((lane >> 3) & 1);
+    if ((lane & ~8u) == 0 && row < nrt) g_red[row * RW + j] = v;
+  }
+};
+
 // One GEMV op with NF input fragments per wave (1, 2, or up to 8).  Row groups are taken GB at a
 // time (GB NF = 4 slots per wait for NF <= 2).  With PG < 8 pieces per group (NF = 1) a slot holds
 // 8 / PG groups and wave w works on group (slot 8 / PG + w / PG), piece w % PG.
@@ -893,8 +954,8 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   for (int f = 0; f < NF; ++f) {
     const u32 q = pg >= 8 ? 8 * f + w : w % pg;
     const u32 k0 = q * KP + koff;
-    const bool v = (u32)f < nf && bl < (u32)B && k0 < K;
-    if (v) ld8_sc1((const float*)o.in + (size_t)bl * o.ld_in + k0, xf[f]);
+    const bool v = (u32)f < nf && (B == 1 || bl < (u32)B) && k0 < K;
+    if (v) ld8_sc1((const float*)o.in + (size_t)(B == 1 ? 0u : bl) * o.ld_in + k0, xf[f]);
     else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) xf[f][e] = 0.0f;
@@ -911,7 +972,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
     // sum of squares per sequence (each input appears once among the waves with distinct pieces),
     // read back in the epilogue
     float ss = 0.0f;
-    if (pg >= 8 || w < pg) {
+    if ((pg >= 8 || w < pg) && (B > 1 || bl == 0)) {  // (at B = 1 the row-1 lanes repeat the row-0 inputs)
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
@@ -953,22 +1014,15 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
         for (u32 i = 0; i < NS; ++i) wv[i] = g_ring[((seq + i) % NSLOT) * (SLOT / 16) + achunk];
         release_upto(w, seq + NS);
-        f32x4 dh[GB], dl[GB];
+        GemvAcc<B, P> acc[GB];
 #pragma unroll
-        for (u32 gb = 0; gb < GB; ++gb) {
-          dh[gb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-          dl[gb] = dh[gb];
-        }
+        for (u32 gb = 0; gb < GB; ++gb) acc[gb].init();
 #pragma unroll
         for (u32 f = 0; f < NF; ++f)
 #pragma unroll
-          for (u32 gb = 0; gb < GB; ++gb) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, wv[gb * NF + f]);
-            dh[gb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xh[f], dh[gb], 0, 0, 0);
-            dl[gb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl[f], dl[gb], 0, 0, 0);
-          }
+          for (u32 gb = 0; gb < GB; ++gb) acc[gb].add(wv[gb * NF + f], xh[f], xl[f]);
 #pragma unroll
-        for (u32 gb = 0; gb < GB; ++gb) gemv_extract<B, P>(dh[gb] + dl[gb], lane, g0 + gb, w, RW, nrt);
+        for (u32 gb = 0; gb < GB; ++gb) acc[gb].finish(lane, g0 + gb, w, RW, nrt);
         seq += NS;
       }
     }
@@ -980,22 +1034,19 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
       for (int f = 0; f < NF; ++f)
         if ((u32)f < nf) wv[f] = g_ring[((seq + f) % NSLOT) * (SLOT / 16) + achunk];
       release_upto(w, seq + nf);
-      // two accumulators per half (even / odd fragments) keep four chains in flight
-      f32x4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = d0, d2 = d0, d3 = d0;
+      // two accumulators (even / odd fragments) keep four chains in flight
+      GemvAcc<B, P> a0, a1;
+      a0.init();
+      a1.init();
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         if ((u32)f < nf) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, wv[f]);
-          if (f & 1) {
-            d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xh[f], d1, 0, 0, 0);
-            d3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl[f], d3, 0, 0, 0);
-          } else {
-            d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xh[f], d0, 0, 0, 0);
-            d2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl[f], d2, 0, 0, 0);
-          }
+          if (f & 1) a1.add(wv[f], xh[f], xl[f]);
+          else a0.add(wv[f], xh[f], xl[f]);
         }
       }
-      gemv_extract<B, P>((d0 + d1) + (d2 + d3), lane, g0, w, RW, nrt);
+      a0.merge(a1);
+      a0.finish(lane, g0, w, RW, nrt);
       seq += nf;
     }
   } else {
@@ -1010,15 +1061,14 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
       for (int i = 0; i < 4; ++i) wv[i] = g_ring[((seq + i) % NSLOT) * (SLOT / 16) + achunk];
       release_upto(w, seq + 4);
-      f32x4 d[4];
+      GemvAcc<B, P> acc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, wv[i]);
-        d[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xh[0], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-        d[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl[0], d[i], 0, 0, 0);
+        acc[i].init();
+        acc[i].add(wv[i], xh[0], xl[0]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) gemv_extract<B, P>(d[i], lane, (((s0 + i) * 8) >> lgpg) + gsub, w & (pg - 1), RW, nrt);
+      for (int i = 0; i < 4; ++i) acc[i].finish(lane, (((s0 + i) * 8) >> lgpg) + gsub, w & (pg - 1), RW, nrt);
       seq += 4;
     }
     for (; s0 < o.nslots; ++s0) {
@@ -1027,10 +1077,10 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
       release_upto(w, seq + 1);
       const u32 g = ((s0 * 8) >> lgpg) + gsub;
       if (g < nrg) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, wv);
-        f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xh[0], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl[0], d, 0, 0, 0);
-        gemv_extract<B, P>(d, lane, g, w & (pg - 1), RW, nrt);
+        GemvAcc<B, P> acc;
+        acc.init();
+        acc.add(wv, xh[0], xl[0]);
+        acc.finish(lane, g, w & (pg - 1), RW, nrt);
       }
       seq += 1;
     }
