@@ -65,6 +65,7 @@ struct mk_ctx {
   size_t ws_bytes = 0;
   mk::KArgs args{};
   uint32_t epoch = 0;
+  uint32_t tag = 0;  // launch tag of the last launch (activation parity = bit 0)
   uint32_t max_stage_ops = 1;
   hipStream_t last_stream = nullptr;
   mk_status sticky = MK_OK;
@@ -303,12 +304,15 @@ mk_status mk_decode_step(mk_ctx* ctx, const int32_t* tokens, const int32_t* posi
   A.logits = logits_out;
   A.batch = batch;
   A.epoch = ctx->epoch + 1;
+  // consecutive launches alternate the parity; the 31-bit tag restarts at 1 or 2 to keep it so
+  A.tag = ctx->tag + 1 <= 0x7FFFFFFFu ? ctx->tag + 1 : (ctx->tag & 1u) ? 2u : 1u;
   void* kargs[] = {&A};
   hipError_t e = ctx->plain_launch
                      ? hipLaunchKernel(ctx->kernel, dim3(ctx->plan.n_cus), dim3(mk::NTHREADS), kargs, 0, s)
                      : hipLaunchCooperativeKernel(ctx->kernel, dim3(ctx->plan.n_cus), dim3(mk::NTHREADS), kargs, 0, s);
   if (e != hipSuccess) return hip_fail(e, ctx->plain_launch ? "hipLaunchKernel" : "hipLaunchCooperativeKernel");
   ctx->epoch += 1;
+  ctx->tag = A.tag;
   ctx->last_stream = s;
   return MK_OK;
 }
@@ -335,9 +339,14 @@ mk_status mk_reset(mk_ctx* ctx) {
   for (const auto& Q : Y.layer)
     hipLaunchKernelGGL(fill_u32, dim3(1), dim3(256), 0, nullptr, (uint32_t*)(ctx->ws + Q.tickets),
                        Y.tickets_bytes_per_layer / 4, 0u);
+  // a stopped launch can leave activations of either parity: clear them (parity 0, row_ok tag 0)
+  // and restart the tags at 1
+  hipLaunchKernelGGL(fill_u32, dim3(256), dim3(256), 0, nullptr, (uint32_t*)(ctx->ws + Y.act_begin),
+                     (Y.act_end - Y.act_begin) / 4, 0u);
   MK_HIP(hipGetLastError());
   MK_HIP(hipDeviceSynchronize());
   ctx->epoch = 0;
+  ctx->tag = 0;
   ctx->sticky = MK_OK;
   return MK_OK;
 }

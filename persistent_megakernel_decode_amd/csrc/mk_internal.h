@@ -46,6 +46,14 @@ enum Epi : uint8_t { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 
 
 constexpr int16_t NO_STAGE = -1;
 
+// Op flags.  Activations written by EMBED and by the projections carry the launch's parity in
+// the lowest mantissa bit of every fp32 value (row_ok carries the launch tag itself), so an op
+// whose inputs all come from such writers can poll the inputs themselves instead of a stage
+// counter (OPF_TAGGED_IN).  A stage that no op waits on by counter skips its signal and the
+// store-completion wait before it (OPF_NO_SIGNAL).
+constexpr uint32_t OPF_TAGGED_IN = 1u;
+constexpr uint32_t OPF_NO_SIGNAL = 2u;
+
 // One queue entry (128 bytes).  Pointers are device addresses.
 //
 // A GEMV op computes output rows [row0, row0 + nrows) of a row space that may
@@ -86,7 +94,7 @@ struct alignas(16) Op {
   uint32_t ld_in;      // floats between batch rows of `in`
   uint32_t ld_out;     // floats between batch rows of `out` / `res`
   uint32_t b1;         // GEMV: stream rows taken from W before switching to W2
-  uint32_t pad1;
+  uint32_t flags;      // OPF_* bits
   uint64_t W, W2;      // GEMV weight runs, bf16 rows of K
   uint64_t pad3;
   uint64_t in;         // fp32 [batch][ld_in]
@@ -143,6 +151,7 @@ struct KArgs {
   float* logits;
   int32_t batch;
   uint32_t epoch;
+  uint32_t tag;               // launch tag: bit 0 is the activation parity, row_ok holds tag << 1 | ok
   uint64_t spin_limit;        // watchdog, in s_memrealtime ticks (100 MHz)
 };
 

@@ -97,6 +97,27 @@ __device__ __forceinline__ int32_t ld_i32_sc1(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Tagged activations: bit 0 of every fp32 value that EMBED or a projection writes holds the
+// launch parity (a relative change of at most 2^-23).  Each value is written once per launch and
+// consecutive launches differ in parity, so a value that shows the current parity is this
+// launch's: a reader can poll the data itself instead of a completion counter, and the writer
+// needs neither a store-completion wait nor a signal.
+__device__ __forceinline__ float tagv(float v, u32 par) {
+  return __builtin_bit_cast(float, (__builtin_bit_cast(u32, v) & ~1u) | par);
+}
+__device__ __forceinline__ bool tag_ok(float v, u32 par) { return (__builtin_bit_cast(u32, v) & 1u) == par; }
+__device__ __forceinline__ void st_tag(float* p, float v, u32 par) { st_sc1(p, tagv(v, par)); }
+template <int N>
+__device__ __forceinline__ bool tags_ok(const float* x, u32 par) {
+  u32 a = ~0u, o = 0u;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    a &= __builtin_bit_cast(u32, x[i]);
+    o |= __builtin_bit_cast(u32, x[i]);
+  }
+  return ((par ? a : o) & 1u) == par;
+}
+
 __device__ __forceinline__ float bf2f(uint16_t h) { return __builtin_bit_cast(float, (u32)h << 16); }
 __device__ __forceinline__ float bflo(u32 w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bfhi(u32 w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
@@ -251,6 +272,33 @@ __device__ __forceinline__ bool wait_full(const KArgs& A, u32 seq) {
   }
   return true;
 }
+// Bounded wait for a tagged value: returns `v` once it (or a re-read of `p`) shows this launch's
+// parity; past the watchdog limit the timeout is raised and the last value returned.
+__device__ __forceinline__ float tagged_fix(const KArgs& A, const float* p, float v) {
+  const u32 par = A.tag & 1u;
+  if (tag_ok(v, par)) return v;
+  Watchdog wd(A);
+  do {
+    if (aborted() || wd.expired()) break;
+    __builtin_amdgcn_s_sleep(1);
+    v = ld_sc1(p);
+  } while (!tag_ok(v, par));
+  return v;
+}
+__device__ __forceinline__ float ld_tagged(const KArgs& A, const float* p) { return tagged_fix(A, p, ld_sc1(p)); }
+// row_ok[b] holds tag << 1 | ok, written once per launch by EMBED: wait for this launch's entry.
+__device__ __forceinline__ bool row_ok_wait(const KArgs& A, int b) {
+  const u32 want = A.tag & 0x7FFFFFFFu;
+  u32 v = (u32)ld_i32_sc1(A.row_ok + b);
+  Watchdog wd(A);
+  while ((v >> 1) != want) {
+    if (aborted() || wd.expired()) return false;
+    __builtin_amdgcn_s_sleep(1);
+    v = (u32)ld_i32_sc1(A.row_ok + b);
+  }
+  return (v & 1u) != 0;
+}
+
 // Compute wave w will read no ring slot below `upto` again.  Monotonic per wave.
 __device__ __forceinline__ void release_upto(u32 w, u32 upto) {
   __builtin_amdgcn_s_waitcnt(MK_LGKMCNT0);  // this wave's reads of those slots are complete
@@ -731,16 +779,18 @@ __device__ __forceinline__ void signal_stage(const KArgs& A, int stage, u32 inde
 }
 
 // ------------------------------------------------------------------ EMBED
-// x0[b][h] = E[token_b][h] for this CU's slice of h (rows with b >= batch or a bad token are zero).
+// x0[b][h] = E[token_b][h] for this CU's slice of h, for all B activation rows (rows with
+// b >= batch or a bad token are zero), tagged.
+template <int B>
 __device__ __forceinline__ void op_embed(const KArgs& A, u32 w) {
-  const u32 t = w * 64 + lane_id();
+  const u32 t = w * 64 + lane_id(), par = A.tag & 1u;
   const int cu = (int)blockIdx.x;
   const int h0 = (int)((int64_t)A.H * cu / A.n_cus), h1 = (int)((int64_t)A.H * (cu + 1) / A.n_cus);
-  for (int b = 0; b < A.max_batch; ++b) {
+  for (int b = 0; b < B; ++b) {
     const int tok = b < A.batch ? A.tokens[b] : -1;
     const bool ok = tok >= 0 && tok < A.V;
     for (int h = h0 + (int)t; h < h1; h += NC * 64)
-      st_sc1(A.x0 + (size_t)b * A.H + h, ok ? bf2f(A.embed[(size_t)tok * A.H + h]) : 0.0f);
+      st_tag(A.x0 + (size_t)b * A.H + h, ok ? bf2f(A.embed[(size_t)tok * A.H + h]) : 0.0f, par);
   }
 }
 
@@ -766,7 +816,8 @@ __device__ __forceinline__ void op_embed_finish(const KArgs& A, u32 w, u32& gen)
       float any = 0.0f;
       for (int j = 0; j < NC; ++j) any = fmaxf(any, g_scr[j]);
       const bool final_ok = ok && any == 0.0f;
-      __hip_atomic_store(A.row_ok + b, final_ok ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(A.row_ok + b, (int32_t)((A.tag << 1) | (final_ok ? 1u : 0u)), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
       if (b < A.batch && !final_ok) raise_status(A, ST_BAD_INPUT);
     }
     if (!cbar(A, gen)) return;
@@ -950,12 +1001,15 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   float xf[NF][8];
   u32x4 gv[NF];
   const uint16_t* gm = (const uint16_t*)o.gamma;
+  const float* xin = (const float*)o.in + (size_t)(B == 1 ? 0u : bl) * o.ld_in;
+  u32 fv = 0;  // fragments this lane loads
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const u32 q = pg >= 8 ? 8 * f + w : w % pg;
     const u32 k0 = q * KP + koff;
     const bool v = (u32)f < nf && (B == 1 || bl < (u32)B) && k0 < K;
-    if (v) ld8_sc1((const float*)o.in + (size_t)(B == 1 ? 0u : bl) * o.ld_in + k0, xf[f]);
+    fv |= v ? 1u << f : 0u;
+    if (v) ld8_sc1(xin + k0, xf[f]);
     else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) xf[f][e] = 0.0f;
@@ -963,11 +1017,30 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
     gv[f] = v && o.norm ? *(const __attribute__((address_space(1))) u32x4*)(gm + k0) : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   }
   // residual rows of this thread (epilogue row r = thread index), fetched now, off the critical path
-  const u32 tid = w * 64 + lane;
+  const u32 tid = w * 64 + lane, par = A.tag & 1u;
   float rv[B];
 #pragma unroll
   for (int b = 0; b < B; ++b)
     rv[b] = o.epi == EPI_RESID && tid < o.nrows ? ld_sc1((const float*)o.res + (size_t)b * o.ld_out + o.row0 + tid) : 0.0f;
+  if (o.flags & OPF_TAGGED_IN) {
+    // poll the inputs themselves: re-read every fragment that does not yet show this launch's parity
+    u32 todo = 0;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) todo |= ((fv >> f) & 1u) && !tags_ok<8>(xf[f], par) ? 1u << f : 0u;
+    Watchdog wd(A);
+    while (__builtin_amdgcn_ballot_w64(todo != 0) != 0) {
+      if (aborted() || wd.expired()) return false;
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const u32 q = pg >= 8 ? 8 * f + w : w % pg;
+        if ((todo >> f) & 1u) ld8_sc1(xin + q * KP + koff, xf[f]);
+      }
+      todo = 0;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) todo |= ((fv >> f) & 1u) && !tags_ok<8>(xf[f], par) ? 1u << f : 0u;
+    }
+  }
   if (o.norm) {
     // sum of squares per sequence (each input appears once among the waves with distinct pieces),
     // read back in the epilogue
@@ -1108,14 +1181,15 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
       if (o.epi == EPI_SWIGLU) {
         float u = 0.0f;
         for (u32 j = 0; j < RW; ++j) u += g_red[((r + o.nrows) * RW + j) * B + b];
-        st_sc1((float*)o.out + (size_t)b * o.ld_out + row, silu(v) * (u * rstd[b]));
+        st_tag((float*)o.out + (size_t)b * o.ld_out + row, silu(v) * (u * rstd[b]), par);
       } else if (o.epi == EPI_RESID) {
-        const float x = r == tid ? rv[b] : ld_sc1((const float*)o.res + (size_t)b * o.ld_out + row);
-        st_sc1((float*)o.out + (size_t)b * o.ld_out + row, x + v);
+        const float* rp = (const float*)o.res + (size_t)b * o.ld_out + row;
+        const float x = tagged_fix(A, rp, r == tid ? rv[b] : ld_sc1(rp));
+        st_tag((float*)o.out + (size_t)b * o.ld_out + row, x + v, par);
       } else if (o.epi == EPI_STORE) {
-        st_sc1((float*)o.out + (size_t)b * o.ld_out + row, v);
+        st_tag((float*)o.out + (size_t)b * o.ld_out + row, v, par);
       } else if (b < A.batch) {  // EPI_LOGITS
-        const bool ok = ld_i32_sc1(A.row_ok + b) != 0;
+        const bool ok = row_ok_wait(A, b);
         A.logits[(size_t)b * A.V + row] = ok ? v : __builtin_nanf("");
       }
     }
@@ -1246,7 +1320,7 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
       if (pr < 2 && (u32)(pp * 4) + 2 * pr + 1 < nt) {
         const float gv = colsum(2 * pr, row, b), uv = colsum(2 * pr + 1, row, b);
         const u32 orow = 16 * ((u32)(pp * 2) + pr) + row;
-        if (orow < nrows) st_sc1((float*)o.out + (size_t)b * o.ld_out + o.row0 + orow, silu(gv) * uv);
+        if (orow < nrows) st_tag((float*)o.out + (size_t)b * o.ld_out + o.row0 + orow, silu(gv) * uv, A.tag & 1u);
       }
     } else {
       const u32 tp = tid / (16 * B);
@@ -1255,12 +1329,12 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
         const u32 orow = 16 * ((u32)(pp * 4) + tp) + row, grow = o.row0 + orow;
         if (orow < nrows) {
           if (o.epi == EPI_RESID) {
-            const float x = ld_sc1((const float*)o.res + (size_t)b * o.ld_out + grow);
-            st_sc1((float*)o.out + (size_t)b * o.ld_out + grow, x + v);
+            const float x = ld_tagged(A, (const float*)o.res + (size_t)b * o.ld_out + grow);
+            st_tag((float*)o.out + (size_t)b * o.ld_out + grow, x + v, A.tag & 1u);
           } else if (o.epi == EPI_STORE) {
-            st_sc1((float*)o.out + (size_t)b * o.ld_out + grow, v);
+            st_tag((float*)o.out + (size_t)b * o.ld_out + grow, v, A.tag & 1u);
           } else if ((int)b < A.batch) {  // EPI_LOGITS
-            const bool ok = ld_i32_sc1(A.row_ok + b) != 0;
+            const bool ok = row_ok_wait(A, (int)b);
             A.logits[(size_t)b * A.V + grow] = ok ? v : __builtin_nanf("");
           }
         }
@@ -1297,7 +1371,8 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   const LayerDesc Ld = sload(A.layers + o.layer);
   const int G = A.G, b = it.b, kvh = it.kvh;
   const int pos = A.positions[b];
-  const bool ok = ld_i32_sc1(A.row_ok + b) != 0;
+  const bool ok = row_ok_wait(A, b);
+  const bool tagged = (o.flags & OPF_TAGGED_IN) != 0;
   const int qkv_ld = (A.Hq + 2 * A.Hkv) * D;
   const float* qkv = (const float*)Ld.qkv + (size_t)b * qkv_ld;
   const float scale = 1.0f / sqrtf((float)D);
@@ -1332,8 +1407,13 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   for (int t = (int)w; t < ntask; t += NC) {
     const int row = t < G ? kvh * G + t : (t == G ? A.Hq + kvh : A.Hq + A.Hkv + kvh);
     float v[DPL];
+    const float* src = qkv + row * D + lane * DPL;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) v[e] = ld_sc1(qkv + row * D + lane * DPL + e);
+    for (int e = 0; e < DPL; ++e) v[e] = ld_sc1(src + e);
+    if (tagged) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) v[e] = tagged_fix(A, src + e, v[e]);
+    }
     if (t <= G) {
       if (A.qk_norm) headnorm(v, (const uint16_t*)(t < G ? Ld.q_norm : Ld.k_norm));
       rotate(v);
@@ -1585,13 +1665,15 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
   const int ldu = C + 2 * A.nh;
   const float* u = (const float*)Ld.qkv + (size_t)b * ldu;
   const float* gts = (const float*)Ld.gates + (size_t)b * ldu;
+  const bool tagged = (o.flags & OPF_TAGGED_IN) != 0;
+  auto rd = [&](const float* p) { return tagged ? ld_tagged(A, p) : ld_sc1(p); };
   float* cst = (float*)Ld.conv_state + (size_t)b * C * (W - 1);
   const uint16_t* cw = (const uint16_t*)Ld.conv_w;
 
   auto conv = [&](int c, float* newstate_last) -> float {  // causal conv of channel c with its window
     float acc = 0.0f;
     for (int j = 0; j < W - 1; ++j) acc += bf2f(cw[(size_t)c * W + j]) * cst[(size_t)c * (W - 1) + j];
-    const float x = ld_sc1(u + c);
+    const float x = rd(u + c);
     acc += bf2f(cw[(size_t)c * W + W - 1]) * x;
     *newstate_last = x;
     return silu(acc);
@@ -1617,8 +1699,8 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
     const float rq = 1.0f / sqrtf(nq + 1e-6f) / sqrtf((float)DK), rk = 1.0f / sqrtf(nk + 1e-6f);
 #pragma unroll
     for (int e = 0; e < DPL; ++e) { q[e] *= rq; k[e] *= rk; }
-    const float gate = 1.0f / (1.0f + __expf(-ld_sc1(gts + h)));
-    const float beta = 1.0f / (1.0f + __expf(-ld_sc1(gts + A.nh + h)));
+    const float gate = 1.0f / (1.0f + __expf(-rd(gts + h)));
+    const float beta = 1.0f / (1.0f + __expf(-rd(gts + A.nh + h)));
     // value channels of this slot's rows: lane r < RPS computes row r's conv
     const int j0 = (int)cb * 32 + (int)s * RPS;
     const int vch = 2 * A.nh * DK + h * A.dv + j0 + (int)lane;
@@ -1672,7 +1754,7 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
     if (ok) {
       for (int t = (int)(w * 64 + lane); t < 2 * DK; t += NC * 64) {
         const int c = t < DK ? h * DK + t : A.nh * DK + h * DK + (t - DK);
-        const float x = ld_sc1(u + c);
+        const float x = rd(u + c);
         float* st = cst + (size_t)c * (W - 1);
         for (int j = 0; j + 1 < W - 1; ++j) st[j] = st[j + 1];
         st[W - 2] = x;
@@ -1690,12 +1772,14 @@ __device__ __forceinline__ void compute(const KArgs& A, u32 q0, u32 q1, u32 w) {
   ItemCache ic;
   for (u32 oi = q0; oi < q1; ++oi) {
     const Op o = sload(A.ops + oi);
-    if (w == 0 && o.wait_stage != NO_STAGE) wait_stage(A, o.wait_stage);
-    if (!cbar(A, gen)) return;
+    if (o.wait_stage != NO_STAGE && !(o.flags & OPF_TAGGED_IN)) {  // inputs finished by counter
+      if (w == 0) wait_stage(A, o.wait_stage);
+      if (!cbar(A, gen)) return;
+    }
     bool alive = true;
     switch (o.opcode) {
       case OP_EMBED:
-        op_embed(A, w);
+        op_embed<B>(A, w);
         if (!cbar(A, gen)) return;
         op_embed_finish(A, w, gen);
         break;
@@ -1717,9 +1801,10 @@ __device__ __forceinline__ void compute(const KArgs& A, u32 q0, u32 q1, u32 w) {
     gen = __builtin_amdgcn_readfirstlane(gen);
     ic.restate();
     if (!alive || aborted()) return;
-    __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));  // this wave's outputs are complete
-    if (!cbar(A, gen)) return;
-    if (w == 0 && lane_id() == 0 && o.sig_stage != NO_STAGE) signal_stage(A, o.sig_stage, o.sig_index);
+    const bool sig = o.sig_stage != NO_STAGE && !(o.flags & OPF_NO_SIGNAL);
+    if (sig) __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));  // this wave's outputs are complete
+    if (!cbar(A, gen)) return;  // (also: the next op may overwrite this op's LDS areas)
+    if (sig && w == 0 && lane_id() == 0) signal_stage(A, o.sig_stage, o.sig_index);
   }
 }
 

@@ -327,6 +327,8 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
     Q.m = take((size_t)B * F * 4);
     Q.x_out = take((size_t)B * H * 4);
   }
+  Y.act_begin = Y.row_ok;
+  Y.act_end = off;
 
   // ---------------- stages and ops
   Builder bd{m, P, n_cus, {}, ""};
@@ -420,6 +422,26 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
       q[cu].push_back(o);
     }
   }
+  // Dependencies: an op whose wait stage was written by EMBED or a projection (tagged activations)
+  // polls its inputs; a stage is signalled only if some op waits on its counter.  The batch-8
+  // matrix-core path keeps the counters (MK_STAGE_COUNTERS=1 keeps them everywhere: diagnostic).
+  {
+    bool tags = P.kernel_batch <= 4;
+    if (const char* e = getenv("MK_STAGE_COUNTERS")) tags = tags && atoi(e) == 0;
+    std::vector<uint8_t> counted(S, 0);
+    for (auto& qc : q)
+      for (Op& o : qc) {
+        if (o.wait_stage == NO_STAGE) continue;
+        const uint8_t pop = bd.stage_ops[o.wait_stage][0].opcode;
+        const bool tagged_src = pop == OP_EMBED || pop == OP_GEMV;
+        const bool tagged_dst = o.opcode == OP_GEMV || o.opcode == OP_ATTN || o.opcode == OP_DELTA;
+        if (tags && tagged_src && tagged_dst) o.flags |= OPF_TAGGED_IN;
+        else counted[o.wait_stage] = 1;
+      }
+    for (auto& qc : q)
+      for (Op& o : qc)
+        if (o.sig_stage != NO_STAGE && !counted[o.sig_stage]) o.flags |= OPF_NO_SIGNAL;
+  }
   P.queue_off.assign(n_cus + 1, 0);
   for (int c2 = 0; c2 < n_cus; ++c2) {
     P.queue_off[c2 + 1] = P.queue_off[c2] + (uint32_t)q[c2].size();
@@ -470,6 +492,8 @@ int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
       last = o.sig_stage;
       if (o.wait_stage != NO_STAGE && o.wait_stage >= o.sig_stage)
         bad(fmt("cu %d op %u: waits on stage %d, not earlier than its own %d", c, i, o.wait_stage, o.sig_stage));
+      if ((o.flags & OPF_TAGGED_IN) && (o.opcode == OP_MMV || o.opcode == OP_EMBED || o.wait_stage == NO_STAGE))
+        bad(fmt("cu %d op %u: polls tagged inputs it cannot check", c, i));
       seen[o.sig_stage]++;
       idx[o.sig_stage].push_back(o.sig_index);
       if (o.opcode == OP_GEMV) {

@@ -20,6 +20,7 @@ struct Layout {
   };
   std::vector<PerLayer> layer;
   size_t counters_bytes = 0, tickets_bytes_per_layer = 0;
+  size_t act_begin = 0, act_end = 0;  // tagged activations (row_ok .. the last layer's sections)
   size_t total = 0;
 };
 
