@@ -53,6 +53,12 @@ constexpr int16_t NO_STAGE = -1;
 // store-completion wait before it (OPF_NO_SIGNAL).
 constexpr uint32_t OPF_TAGGED_IN = 1u;
 constexpr uint32_t OPF_NO_SIGNAL = 2u;
+// With OPF_TAGGED_IN: only rows that attention writes this launch (b < batch, context in range)
+// are polled; the others are never consumed.
+constexpr uint32_t OPF_LIVE_ROWS = 4u;
+// ATTN: the last chunk of each (sequence, KV head) in item order merges, polling the tagged
+// partials (one item per CU); without it the last chunk to finish merges (ticket).
+constexpr uint32_t OPF_POLL_MERGE = 8u;
 
 // One queue entry (128 bytes).  Pointers are device addresses.
 //

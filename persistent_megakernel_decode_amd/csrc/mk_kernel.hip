@@ -58,6 +58,24 @@ __shared__ u32 g_abort;         // set on watchdog expiry: every wave leaves
 __shared__ u32 g_bcast[4];
 
 // ------------------------------------------------------------------ helpers
+// An opaque copy of a uniform value in its own scalar register(s).
+template <typename T>
+__device__ __forceinline__ T opq(T v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+// The launch arguments, read through an opaque pointer to the kernel-argument segment: loads
+// through it cannot be hoisted past the point where it is taken, so a value is re-read (a cached
+// scalar load) in each op that needs it instead of being held -- and spilled -- for the whole
+// launch.  The arguments are the kernel's only parameter, at offset 0.
+__device__ __forceinline__ const KArgs& kargs() {
+  const __attribute__((address_space(4))) KArgs* p =
+      (const __attribute__((address_space(4))) KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return *(const KArgs*)p;
+}
+
 // Uniform, kernel-invariant data (queues, plan tables, inputs) read through the constant
 // address space, which the compiler turns into scalar loads.
 template <typename T>
@@ -297,6 +315,10 @@ __device__ __forceinline__ bool row_ok_wait(const KArgs& A, int b) {
     v = (u32)ld_i32_sc1(A.row_ok + b);
   }
   return (v & 1u) != 0;
+}
+// The same for an entry loaded earlier (`v`), so that the load overlaps other work.
+__device__ __forceinline__ bool row_ok_fix(const KArgs& A, int b, int32_t v) {
+  return ((u32)v >> 1) == (A.tag & 0x7FFFFFFFu) ? (v & 1) != 0 : row_ok_wait(A, b);
 }
 
 // Compute wave w will read no ring slot below `upto` again.  Monotonic per wave.
@@ -701,7 +723,8 @@ __device__ u32 op_slots(const KArgs& A, const Op& o, ItemCache& ic) {
   return o.nslots;
 }
 
-__device__ __forceinline__ void loader(const KArgs& A, u32 q0, u32 q1) {
+__device__ __forceinline__ void loader(const KArgs& A0, u32 q0, u32 q1) {
+  const KArgs& A = A0;
   u32 seq = 0, marked = 0, limit = NSLOT;  // slots below `limit` may be filled
   const u32 lane16 = lane_id() * 16;
   attn_plan_build(A, A.d == 64 ? 32 : 16);
@@ -709,6 +732,7 @@ __device__ __forceinline__ void loader(const KArgs& A, u32 q0, u32 q1) {
   PageWindow pw;
   const AttnLanes al = attn_lanes(A.d == 64 ? 64u : 128u);
   for (u32 oi = q0; oi < q1; ++oi) {
+    const KArgs& A = kargs();
     const Op o = sload(A.ops + oi);
     const u32 ns = op_slots(A, o, ic);
     if (ns == 0) continue;
@@ -979,10 +1003,14 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   constexpr u32 R = 16 / P, KP = 32 * P;
   constexpr u32 GB = NF == 1 ? 4 : (NF == 2 ? 2 : 1);
   const u32 lane = lane_id();
-  const bool swiglu = o.epi == EPI_SWIGLU;
-  const u32 nrt = swiglu ? 2 * o.nrows : o.nrows;  // stream rows
-  const u32 nrg = nrt / R;                          // row groups
-  const u32 pg = o.ppr, K = o.K;
+  // the Op's fields as independent scalars (see op_mmv)
+  const u32 epi = opq((u32)o.epi), norm = opq((u32)o.norm), flags = opq(o.flags), nrows = opq(o.nrows);
+  const u32 pg = opq(o.ppr), K = opq(o.K), nslots = opq(o.nslots), row0 = opq(o.row0);
+  const u32 ld_in = opq(o.ld_in), ld_out = opq(o.ld_out);
+  const uint64_t in = opq(o.in), gamma = opq(o.gamma), outp = opq(o.out), resp = opq(o.res);
+  const bool swiglu = epi == EPI_SWIGLU;
+  const u32 nrt = swiglu ? 2 * nrows : nrows;  // stream rows
+  const u32 nrg = nrt / R;                      // row groups
   const u32 nf = pg >= 8 ? pg / 8 : 1;
   const u32 RW = pg >= 8 ? 8 : pg;
   const u32 bl = (lane & 15) / P;  // this lane's sequence in the B operand
@@ -1000,8 +1028,8 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   // between the loads and the stream.
   float xf[NF][8];
   u32x4 gv[NF];
-  const uint16_t* gm = (const uint16_t*)o.gamma;
-  const float* xin = (const float*)o.in + (size_t)(B == 1 ? 0u : bl) * o.ld_in;
+  const uint16_t* gm = (const uint16_t*)gamma;
+  const float* xin = (const float*)in + (size_t)(B == 1 ? 0u : bl) * ld_in;
   u32 fv = 0;  // fragments this lane loads
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
@@ -1014,16 +1042,21 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
       for (int e = 0; e < 8; ++e) xf[f][e] = 0.0f;
     }
-    gv[f] = v && o.norm ? *(const __attribute__((address_space(1))) u32x4*)(gm + k0) : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    gv[f] = v && norm ? *(const __attribute__((address_space(1))) u32x4*)(gm + k0) : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   }
   // residual rows of this thread (epilogue row r = thread index), fetched now, off the critical path
   const u32 tid = w * 64 + lane, par = A.tag & 1u;
   float rv[B];
 #pragma unroll
   for (int b = 0; b < B; ++b)
-    rv[b] = o.epi == EPI_RESID && tid < o.nrows ? ld_sc1((const float*)o.res + (size_t)b * o.ld_out + o.row0 + tid) : 0.0f;
-  if (o.flags & OPF_TAGGED_IN) {
+    rv[b] = epi == EPI_RESID && tid < nrows ? ld_sc1((const float*)resp + (size_t)b * ld_out + row0 + tid)
+          : epi == EPI_LOGITS ? __builtin_bit_cast(float, ld_i32_sc1(A.row_ok + b)) : 0.0f;  // row_ok for logits
+  if (flags & OPF_TAGGED_IN) {
     // poll the inputs themselves: re-read every fragment that does not yet show this launch's parity
+    if (flags & OPF_LIVE_ROWS) {  // rows without attention this launch are never written: skip them
+      const int bb = B == 1 ? 0 : (int)min(bl, (u32)B - 1);
+      if (!(bb < A.batch && clamp_ctx(A, A.ctx_lens[bb]) > 0)) fv = 0;
+    }
     u32 todo = 0;
 #pragma unroll
     for (int f = 0; f < NF; ++f) todo |= ((fv >> f) & 1u) && !tags_ok<8>(xf[f], par) ? 1u << f : 0u;
@@ -1041,7 +1074,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
       for (int f = 0; f < NF; ++f) todo |= ((fv >> f) & 1u) && !tags_ok<8>(xf[f], par) ? 1u << f : 0u;
     }
   }
-  if (o.norm) {
+  if (norm) {
     // sum of squares per sequence (each input appears once among the waves with distinct pieces),
     // read back in the epilogue
     float ss = 0.0f;
@@ -1144,7 +1177,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
       for (int i = 0; i < 4; ++i) acc[i].finish(lane, (((s0 + i) * 8) >> lgpg) + gsub, w & (pg - 1), RW, nrt);
       seq += 4;
     }
-    for (; s0 < o.nslots; ++s0) {
+    for (; s0 < nslots; ++s0) {
       if (seq + 1 > avail && !wait_avail(A, seq + 1, avail)) return false;
       const u32x4 wv = g_ring[(seq % NSLOT) * (SLOT / 16) + achunk];
       release_upto(w, seq + 1);
@@ -1165,32 +1198,34 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
   for (int b = 0; b < B; ++b) {
     rstd[b] = 1.0f;
-    if (o.norm) {
+    if (norm) {
       float tot = 0.0f;
       for (int j = 0; j < NC; ++j) tot += g_scr[j * B + b];
       rstd[b] = 1.0f / sqrtf(tot / (float)K + A.rms_eps);
     }
   }
-  for (u32 r = tid; r < o.nrows; r += NC * 64) {
-    const u32 row = o.row0 + r;
+  bool okb[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) okb[b] = epi == EPI_LOGITS && b < A.batch && row_ok_fix(A, b, __builtin_bit_cast(int32_t, rv[b]));
+  for (u32 r = tid; r < nrows; r += NC * 64) {
+    const u32 row = row0 + r;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       float v = 0.0f;
       for (u32 j = 0; j < RW; ++j) v += g_red[(r * RW + j) * B + b];
       v *= rstd[b];
-      if (o.epi == EPI_SWIGLU) {
+      if (epi == EPI_SWIGLU) {
         float u = 0.0f;
-        for (u32 j = 0; j < RW; ++j) u += g_red[((r + o.nrows) * RW + j) * B + b];
-        st_tag((float*)o.out + (size_t)b * o.ld_out + row, silu(v) * (u * rstd[b]), par);
-      } else if (o.epi == EPI_RESID) {
-        const float* rp = (const float*)o.res + (size_t)b * o.ld_out + row;
+        for (u32 j = 0; j < RW; ++j) u += g_red[((r + nrows) * RW + j) * B + b];
+        st_tag((float*)outp + (size_t)b * ld_out + row, silu(v) * (u * rstd[b]), par);
+      } else if (epi == EPI_RESID) {
+        const float* rp = (const float*)resp + (size_t)b * ld_out + row;
         const float x = tagged_fix(A, rp, r == tid ? rv[b] : ld_sc1(rp));
-        st_tag((float*)o.out + (size_t)b * o.ld_out + row, x + v, par);
-      } else if (o.epi == EPI_STORE) {
-        st_tag((float*)o.out + (size_t)b * o.ld_out + row, v, par);
+        st_tag((float*)outp + (size_t)b * ld_out + row, x + v, par);
+      } else if (epi == EPI_STORE) {
+        st_tag((float*)outp + (size_t)b * ld_out + row, v, par);
       } else if (b < A.batch) {  // EPI_LOGITS
-        const bool ok = row_ok_wait(A, b);
-        A.logits[(size_t)b * A.V + row] = ok ? v : __builtin_nanf("");
+        A.logits[(size_t)b * A.V + row] = okb[b] ? v : __builtin_nanf("");
       }
     }
   }
@@ -1219,13 +1254,19 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
   static_assert(B <= 8 && NC == 8, "one pass holds 8 waves x 4 tiles x 16 rows x 8 columns");
   static_assert(NC * 4 * 16 * 8 <= RED_FLOATS, "MMV partial-sum area");
   const u32 lane = lane_id();
-  const bool swiglu = o.epi == EPI_SWIGLU;
-  const u32 nrows = o.nrows, ntg = (nrows + 15) / 16, nt = swiglu ? 2 * ntg : ntg, nks = o.ppr;
+  // the Op's fields as independent scalars: kept whole, its 8-dword load groups are what the
+  // compiler spills and reloads inside the stream loop
+  const u32 epi = opq((u32)o.epi), norm = opq((u32)o.norm), nrows = opq(o.nrows), nks = opq(o.ppr), K = opq(o.K);
+  const u32 row0 = opq(o.row0), ld_in = opq(o.ld_in), ld_out = opq(o.ld_out);
+  const uint64_t in = opq(o.in), gamma = opq(o.gamma), outp = opq(o.out), resp = opq(o.res);
+  const bool swiglu = epi == EPI_SWIGLU;
+  const u32 ntg = (nrows + 15) / 16, nt = swiglu ? 2 * ntg : ntg;
   const u32 col = lane & 15, kq = lane >> 4;  // operand row / output column, and k-chunk of the lane
   const bool cval = col < (u32)B;
   const u32 aoff = w * 1024 + col * 64 + ((kq ^ ((col >> 2) & 3)) * 16);  // this lane's A bytes in a slot
-  const float* xin = (const float*)o.in + (size_t)(cval ? col : 0) * o.ld_in;
-  const uint16_t* gm = (const uint16_t*)o.gamma;
+  const float* xin = (const float*)in + (size_t)(cval ? col : 0) * ld_in;
+  const uint16_t* gm = (const uint16_t*)gamma;
+  const int32_t rok = epi == EPI_LOGITS && lane < (u32)B ? ld_i32_sc1(A.row_ok + lane) : 0;  // lane b: row_ok[b]
 
   f32x4 acc[MMV_TILES];
 #pragma unroll
@@ -1240,7 +1281,7 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
 #pragma unroll
       for (int e = 0; e < 8; ++e) xv[e] = 0.0f;
     }
-    gv = (o.norm && ks < nks) ? *(const u32x4*)(gm + k0) : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    gv = (norm && ks < nks) ? *(const u32x4*)(gm + k0) : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   };
   // one segment: this wave's input block times every tile of the segment (the slots must be full)
   auto consume = [&](const float* xv, const u32x4& gv) {
@@ -1306,35 +1347,36 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
       float v = 0.0f;
 #pragma unroll
       for (int ww = 0; ww < NC; ++ww) v += g_red[((ww * 4 + tp) * 16 + row) * B + b];
-      if (o.norm) {
+      if (norm) {
         float tot = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < NC; ++ww) tot += g_scr[ww * 16 + b];
-        v *= 1.0f / sqrtf(tot / (float)o.K + A.rms_eps);
+        v *= 1.0f / sqrtf(tot / (float)K + A.rms_eps);
       }
       return v;
     };
     const u32 row = (tid / B) % 16, b = tid % B;
+    const int32_t rokb = __shfl(rok, (int)b, 64);  // row_ok[b] (all lanes active here)
     if (swiglu) {
       const u32 pr = tid / (16 * B);  // gate / up tile pair within the pass
       if (pr < 2 && (u32)(pp * 4) + 2 * pr + 1 < nt) {
         const float gv = colsum(2 * pr, row, b), uv = colsum(2 * pr + 1, row, b);
         const u32 orow = 16 * ((u32)(pp * 2) + pr) + row;
-        if (orow < nrows) st_tag((float*)o.out + (size_t)b * o.ld_out + o.row0 + orow, silu(gv) * uv, A.tag & 1u);
+        if (orow < nrows) st_tag((float*)outp + (size_t)b * ld_out + row0 + orow, silu(gv) * uv, A.tag & 1u);
       }
     } else {
       const u32 tp = tid / (16 * B);
       if (tp < 4 && (u32)(pp * 4) + tp < nt) {
         const float v = colsum(tp, row, b);
-        const u32 orow = 16 * ((u32)(pp * 4) + tp) + row, grow = o.row0 + orow;
+        const u32 orow = 16 * ((u32)(pp * 4) + tp) + row, grow = row0 + orow;
         if (orow < nrows) {
-          if (o.epi == EPI_RESID) {
-            const float x = ld_tagged(A, (const float*)o.res + (size_t)b * o.ld_out + grow);
-            st_tag((float*)o.out + (size_t)b * o.ld_out + grow, x + v, A.tag & 1u);
-          } else if (o.epi == EPI_STORE) {
-            st_tag((float*)o.out + (size_t)b * o.ld_out + grow, v, A.tag & 1u);
+          if (epi == EPI_RESID) {
+            const float x = ld_tagged(A, (const float*)resp + (size_t)b * ld_out + grow);
+            st_tag((float*)outp + (size_t)b * ld_out + grow, x + v, A.tag & 1u);
+          } else if (epi == EPI_STORE) {
+            st_tag((float*)outp + (size_t)b * ld_out + grow, v, A.tag & 1u);
           } else if ((int)b < A.batch) {  // EPI_LOGITS
-            const bool ok = row_ok_wait(A, (int)b);
+            const bool ok = row_ok_fix(A, (int)b, rokb);
             A.logits[(size_t)b * A.V + grow] = ok ? v : __builtin_nanf("");
           }
         }
@@ -1349,8 +1391,8 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
 // processed together.  Scores come from the matrix cores: Q (G heads, split into bf16 hi + lo so
 // the product keeps fp32 accuracy) times K^T, 16 positions per 16x16x32 tile.  Each compute wave
 // runs an online softmax over its ring slots and accumulates P V on the vector ALUs; the waves are
-// merged in LDS, the chunk's (m, l, o) partial goes to global memory, and the last chunk of
-// (b, kvh) to finish (a ticket) merges all chunks with the log-sum-exp rule.
+// merged in LDS, the chunk's (m, l, o) partial goes to global memory (tagged), and the last chunk
+// of (b, kvh) in item order merges all chunks with the log-sum-exp rule.
 template <int D>
 __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen, ItemCache& ic) {
   constexpr int DPL = D / 64;          // dims per lane in the vector layout
@@ -1361,7 +1403,8 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   constexpr int CPR = D / 8;           // 16-byte chunks per K row
   constexpr int RB = 2 * D;            // bytes per K or V row
   constexpr int QF = 768;              // query fragments: [KB][hi, lo][64 lanes] x 16 bytes
-  static_assert(QF + KB * 2 * 64 * 4 <= RED_FLOATS, "attention LDS areas");
+  constexpr int PA = QF + KB * 2 * 64 * 4;  // per-wave probabilities: [NC][PPS][GMAX]
+  static_assert(PA + NC * PPS * GMAX <= RED_FLOATS, "attention LDS areas");
   const u32 lane = lane_id();
   const AttnItem it = ic.get(A, o.row0, PPS);
   if (!it.valid) return true;
@@ -1371,7 +1414,7 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   const LayerDesc Ld = sload(A.layers + o.layer);
   const int G = A.G, b = it.b, kvh = it.kvh;
   const int pos = A.positions[b];
-  const bool ok = row_ok_wait(A, b);
+  const int32_t rok = ld_i32_sc1(A.row_ok + b);  // checked where it is used
   const bool tagged = (o.flags & OPF_TAGGED_IN) != 0;
   const int qkv_ld = (A.Hq + 2 * A.Hkv) * D;
   const float* qkv = (const float*)Ld.qkv + (size_t)b * qkv_ld;
@@ -1428,7 +1471,7 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
         hb[e] = f2bf(v[e]);
         kvn[(t - G) * D + lane * DPL + e] = bf2f(hb[e]);
       }
-      if (ok) {
+      if (row_ok_fix(A, b, rok)) {
         const int pg = A.page_table[(size_t)b * A.max_pages_per_seq + pos / 16];
         const size_t off = (((size_t)pg * A.Hkv + kvh) * 16 + pos % 16) * D + lane * DPL;
         uint16_t* dp = (uint16_t*)(t == G ? Ld.k_pages : Ld.v_pages) + off;
@@ -1521,17 +1564,15 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
       l[i] = l[i] * corr[i] + row_sum16(ps);
       m[i] = mn;
     }
-    // P V on the vector ALUs.  Lane owns DPL dims of every head; P[head][p] and the rescale
-    // factors are broadcast from their score-tile lanes with readlane.  Heads past G carry
-    // finite junk (zero queries) and are never stored.  Rows past the chunk are zeroed so that
-    // stale ring bytes cannot reach the sums.
-    u32 vw[PPS];
+    // P V on the vector ALUs.  Lane owns DPL dims of every head.  The probabilities go through
+    // this wave's LDS area as P[p][head] and come back as broadcast reads (every lane reads the
+    // same address); the rescale factors are broadcast with readlane.  Heads past G carry finite
+    // junk (zero queries) and are never stored.  Rows past the chunk are zeroed so that stale
+    // ring bytes cannot reach the sums.
+    float* pw = g_red + PA + w * (PPS * GMAX);
+    if (hr < GMAX) {
 #pragma unroll
-    for (int p = 0; p < PPS; ++p) {
-      u32 u;
-      if constexpr (DPL == 2) u = *(const u32*)(vslot + p * RB + lane * 4);
-      else u = *(const uint16_t*)(vslot + p * RB + lane * 2);
-      vw[p] = p < np ? u : 0u;
+      for (int blk = 0; blk < NB; ++blk) *(f32x4*)(pw + (blk * 16 + (int)(lane & 15)) * GMAX + hr) = sc[blk];
     }
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
@@ -1539,16 +1580,33 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
 #pragma unroll
       for (int e = 0; e < DPL; ++e) ov[g][e] *= cr;
     }
+    // four positions at a time: their V words and probabilities in flight together, then the
+    // products (a rolled loop: fully unrolled, every load would be hoisted and spilled)
+#pragma unroll 1
+    for (int p0 = 0; p0 < PPS; p0 += 4) {
+      u32 vw[4];
+      f32x4 pv[4][GMAX / 4];
 #pragma unroll
-    for (int p = 0; p < PPS; ++p) {
-      float vv[DPL];
-      if constexpr (DPL == 2) { vv[0] = bflo(vw[p]); vv[1] = bfhi(vw[p]); }
-      else vv[0] = bflo(vw[p]);
+      for (int j = 0; j < 4; ++j) {
+        const int p = p0 + j;
+        u32 u;
+        if constexpr (DPL == 2) u = *(const u32*)(vslot + p * RB + lane * 4);
+        else u = *(const uint16_t*)(vslot + p * RB + lane * 2);
+        vw[j] = p < np ? u : 0u;
 #pragma unroll
-      for (int g = 0; g < GMAX; ++g) {
-        const float pg = readlane_f(sc[p / 16][g & 3], (g >> 2) * 16 + p % 16);
+        for (int g4 = 0; g4 < GMAX / 4; ++g4) pv[j][g4] = *(const f32x4*)(pw + p * GMAX + 4 * g4);
+      }
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) ov[g][e] += pg * vv[e];
+      for (int j = 0; j < 4; ++j) {
+        float vv[DPL];
+        if constexpr (DPL == 2) { vv[0] = bflo(vw[j]); vv[1] = bfhi(vw[j]); }
+        else vv[0] = bflo(vw[j]);
+#pragma unroll
+        for (int g4 = 0; g4 < GMAX / 4; ++g4)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) ov[4 * g4 + i][e] += pv[j][g4][i] * vv[e];
       }
     }
     release_upto(w, seq0 + min(s + NC, ns));
@@ -1575,6 +1633,7 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   }
   if (!cbar(A, gen)) return false;
   float* part = (float*)Ld.part + (size_t)o.row0 * GMAX * (D + 2);
+  const u32 par = A.tag & 1u;
   for (int t = (int)(w * 64 + lane); t < G * D; t += NC * 64) {
     const int g = t / D, dim = t % D;
     float M = -INFINITY;
@@ -1586,49 +1645,69 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
       Ls += f * g_scr[(j * GMAX + g) * 2 + 1];
       Os += f * g_red[(j * GMAX + g) * D + dim];
     }
-    st_sc1(part + g * (D + 2) + 2 + dim, Os);
-    if (dim == 0) { st_sc1(part + g * (D + 2), M); st_sc1(part + g * (D + 2) + 1, Ls); }
+    // tagged (M is finite: a chunk holds at least one position, so some wave saw a score)
+    st_tag(part + g * (D + 2) + 2 + dim, Os, par);
+    if (dim == 0) { st_tag(part + g * (D + 2), M, par); st_tag(part + g * (D + 2) + 1, Ls, par); }
   }
-  __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));
-  if (!cbar(A, gen)) return false;
-  u32* ticket = (u32*)Ld.tickets + (size_t)b * A.Hkv + kvh;
-  if (w == 0 && lane == 0) {
-    const u32 prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    g_bcast[0] = (prev == (u32)it.n_b - 1) ? 1u : 0u;
+  // One chunk of (b, kvh) merges all of its chunks with the log-sum-exp rule.  With
+  // OPF_POLL_MERGE (one attention item per CU) it is the last chunk in item order, which polls the
+  // chunks' tagged partials: items go to CUs round-robin in item order, so every chunk it waits for
+  // sits at the same or an earlier position in its CU's queue and no two mergers wait on each
+  // other.  Otherwise the last chunk to finish merges (a ticket taken after its partial landed).
+  if (o.flags & OPF_POLL_MERGE) {
+    if (o.row0 != (u32)(it.first_item + (it.n_b - 1) * A.Hkv)) return true;
+    if (!cbar(A, gen)) return false;  // every thread is done with the wave partials in LDS
+  } else {
+    __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));
+    if (!cbar(A, gen)) return false;
+    u32* ticket = (u32*)Ld.tickets + (size_t)b * A.Hkv + kvh;
+    if (w == 0 && lane == 0) {
+      const u32 prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      g_bcast[0] = (prev == (u32)it.n_b - 1) ? 1u : 0u;
+      if (prev == (u32)it.n_b - 1) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!cbar(A, gen)) return false;
+    if (!lds_ld(&g_bcast[0])) return true;
   }
-  if (!cbar(A, gen)) return false;
-  if (lds_ld(&g_bcast[0])) {  // last chunk of (b, kvh): log-sum-exp merge of all its chunks
-    // Loads are issued ahead of their use: thread t owns output (head t / D, dim t % D) and loads
-    // that output of MC chunks at a time (one round trip for up to MC chunks); threads t < n_b * G
-    // also fetch one (m, l) pair for the LDS table every thread reads, in the same round trip.
+  {
+    // The (m, l) table goes to LDS first (one pair per thread and pass): polling it is where the
+    // merger waits for the last chunks.  Then thread t, owning output (head t / D, dim t % D),
+    // loads that output of MC chunks per round trip and re-reads together whichever of them
+    // still show the previous launch's parity.
     static_assert(GMAX * D <= NC * 64, "one merged output per thread");
     const int tid = (int)(w * 64 + lane), nb = it.n_b;
     const float* part0 = (const float*)Ld.part + (size_t)it.first_item * GMAX * (D + 2);
     const size_t cstride = (size_t)A.Hkv * GMAX * (D + 2);  // floats between chunks of (b, kvh)
-    const bool has_ml = tid < nb * G, has_o = tid < G * D;
+    const bool has_o = tid < G * D;
     const int g = has_o ? tid / D : 0, dim = tid % D;
-    float mv = 0.0f, lv = 0.0f;
-    if (has_ml) {
-      const float* pc = part0 + (size_t)(tid / G) * cstride + (tid % G) * (D + 2);
-      mv = ld_sc1(pc);
-      lv = ld_sc1(pc + 1);
-    }
     const float* po = part0 + g * (D + 2) + 2 + dim;
-    constexpr int MC = 16;
-    float oc[MC];
-#pragma unroll
-    for (int k = 0; k < MC; ++k) oc[k] = has_o && k < nb ? ld_sc1(po + (size_t)k * cstride) : 0.0f;
     float* ml = g_red;  // [n_b][G][m, l]
-    if (has_ml) { ml[2 * tid] = mv; ml[2 * tid + 1] = lv; }
+    for (int e = tid; e < nb * G; e += NC * 64) {
+      const float* pc = part0 + (size_t)(e / G) * cstride + (e % G) * (D + 2);
+      const float mv = ld_sc1(pc), lv = ld_sc1(pc + 1);
+      ml[2 * e] = tagged_fix(A, pc, mv);
+      ml[2 * e + 1] = tagged_fix(A, pc + 1, lv);
+    }
     if (!cbar(A, gen)) return false;
     if (has_o) {
       float M = -INFINITY;
       for (int c = 0; c < nb; ++c) M = fmaxf(M, ml[2 * (c * G + g)]);
       float den = 0.0f, num = 0.0f;
+      constexpr int MC = 16;
       for (int c0 = 0; c0 < nb; c0 += MC) {
-        if (c0 > 0) {
+        float oc[MC];
 #pragma unroll
-          for (int k = 0; k < MC; ++k) oc[k] = c0 + k < nb ? ld_sc1(po + (size_t)(c0 + k) * cstride) : 0.0f;
+        for (int k = 0; k < MC; ++k) oc[k] = c0 + k < nb ? ld_sc1(po + (size_t)(c0 + k) * cstride) : tagv(0.0f, par);
+        Watchdog wd(A);
+        while (true) {
+          u32 stale = 0;
+#pragma unroll
+          for (int k = 0; k < MC; ++k) stale |= tag_ok(oc[k], par) ? 0u : 1u << k;
+          if (stale == 0 || aborted() || wd.expired()) break;
+          __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+          for (int k = 0; k < MC; ++k)
+            if ((stale >> k) & 1u) oc[k] = ld_sc1(po + (size_t)(c0 + k) * cstride);
         }
 #pragma unroll
         for (int k = 0; k < MC; ++k) {
@@ -1639,9 +1718,8 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
           }
         }
       }
-      st_sc1((float*)Ld.mix_o + (size_t)b * A.mix + (kvh * G + g) * D + dim, num / den);
+      st_tag((float*)Ld.mix_o + (size_t)b * A.mix + (kvh * G + g) * D + dim, num / den, par);
     }
-    if (w == 0 && lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   return true;
 }
@@ -1767,10 +1845,11 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
 
 // ------------------------------------------------------------------ compute waves
 template <int B>
-__device__ __forceinline__ void compute(const KArgs& A, u32 q0, u32 q1, u32 w) {
+__device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
   u32 seq = 0, gen = 0;
   ItemCache ic;
   for (u32 oi = q0; oi < q1; ++oi) {
+    const KArgs& A = kargs();
     const Op o = sload(A.ops + oi);
     if (o.wait_stage != NO_STAGE && !(o.flags & OPF_TAGGED_IN)) {  // inputs finished by counter
       if (w == 0) wait_stage(A, o.wait_stage);
@@ -1817,7 +1896,7 @@ __device__ __forceinline__ void megakernel_body(const KArgs& A) {
   __syncthreads();
   const u32 q0 = A.queue_off[blockIdx.x], q1 = A.queue_off[blockIdx.x + 1];
   if (wv == 0) loader(A, q0, q1);
-  else compute<B>(A, q0, q1, wv - 1);
+  else compute<B>(q0, q1, wv - 1);
 }
 
 }  // namespace mk

@@ -422,8 +422,8 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
       q[cu].push_back(o);
     }
   }
-  // Dependencies: an op whose wait stage was written by EMBED or a projection (tagged activations)
-  // polls its inputs; a stage is signalled only if some op waits on its counter.  The batch-8
+  // Dependencies: an op whose wait stage was written by EMBED, a projection or attention (tagged
+  // activations) polls its inputs; a stage is signalled only if some op waits on its counter.  The batch-8
   // matrix-core path keeps the counters (MK_STAGE_COUNTERS=1 keeps them everywhere: diagnostic).
   {
     bool tags = P.kernel_batch <= 4;
@@ -433,14 +433,19 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
       for (Op& o : qc) {
         if (o.wait_stage == NO_STAGE) continue;
         const uint8_t pop = bd.stage_ops[o.wait_stage][0].opcode;
-        const bool tagged_src = pop == OP_EMBED || pop == OP_GEMV;
-        const bool tagged_dst = o.opcode == OP_GEMV || o.opcode == OP_ATTN || o.opcode == OP_DELTA;
-        if (tags && tagged_src && tagged_dst) o.flags |= OPF_TAGGED_IN;
+        const bool tagged_src = pop == OP_EMBED || pop == OP_GEMV || pop == OP_ATTN;
+        const bool tagged_dst = pop == OP_ATTN ? o.opcode == OP_GEMV
+                                               : o.opcode == OP_GEMV || o.opcode == OP_ATTN || o.opcode == OP_DELTA;
+        if (tags && tagged_src && tagged_dst) o.flags |= OPF_TAGGED_IN | (pop == OP_ATTN ? OPF_LIVE_ROWS : 0u);
         else counted[o.wait_stage] = 1;
       }
     for (auto& qc : q)
       for (Op& o : qc)
         if (o.sig_stage != NO_STAGE && !counted[o.sig_stage]) o.flags |= OPF_NO_SIGNAL;
+    if (tags && P.n_items == n_cus)
+      for (auto& qc : q)
+        for (Op& o : qc)
+          if (o.opcode == OP_ATTN) o.flags |= OPF_POLL_MERGE;
   }
   P.queue_off.assign(n_cus + 1, 0);
   for (int c2 = 0; c2 < n_cus; ++c2) {
