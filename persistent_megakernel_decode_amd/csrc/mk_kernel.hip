@@ -108,6 +108,20 @@ __device__ __forceinline__ void ld8_sc1(const float* p, float* out) {  // 8 cons
     out[2 * i + 1] = __builtin_bit_cast(float, (u32)(v >> 32));
   }
 }
+__device__ __forceinline__ void ld2_sc1(const float* p, float* out) {  // 2 consecutive floats, 8-B aligned
+  const uint64_t v = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  out[0] = __builtin_bit_cast(float, (u32)v);
+  out[1] = __builtin_bit_cast(float, (u32)(v >> 32));
+}
+__device__ __forceinline__ void ld4_sc1(const float* p, float* out) {  // 4 consecutive floats, 8-B aligned
+  const uint64_t* q = (const uint64_t*)p;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint64_t v = __hip_atomic_load(q + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    out[2 * i] = __builtin_bit_cast(float, (u32)v);
+    out[2 * i + 1] = __builtin_bit_cast(float, (u32)(v >> 32));
+  }
+}
 __device__ __forceinline__ u32 ld_u32_sc1(const u32* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1632,7 +1646,8 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
     }
   }
   if (!cbar(A, gen)) return false;
-  float* part = (float*)Ld.part + (size_t)o.row0 * GMAX * (D + 2);
+  // partial of item i, head g: part[(i * GMAX + g) * (D + 4)] = m, l, -, -, o[0..D) (o 16-B aligned)
+  float* part = (float*)Ld.part + (size_t)o.row0 * GMAX * (D + 4);
   const u32 par = A.tag & 1u;
   for (int t = (int)(w * 64 + lane); t < G * D; t += NC * 64) {
     const int g = t / D, dim = t % D;
@@ -1646,8 +1661,8 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
       Os += f * g_red[(j * GMAX + g) * D + dim];
     }
     // tagged (M is finite: a chunk holds at least one position, so some wave saw a score)
-    st_tag(part + g * (D + 2) + 2 + dim, Os, par);
-    if (dim == 0) { st_tag(part + g * (D + 2), M, par); st_tag(part + g * (D + 2) + 1, Ls, par); }
+    st_tag(part + g * (D + 4) + 4 + dim, Os, par);
+    if (dim == 0) { st_tag(part + g * (D + 4), M, par); st_tag(part + g * (D + 4) + 1, Ls, par); }
   }
   // One chunk of (b, kvh) merges all of its chunks with the log-sum-exp rule.  With
   // OPF_POLL_MERGE (one attention item per CU) it is the last chunk in item order, which polls the
@@ -1670,55 +1685,87 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
     if (!lds_ld(&g_bcast[0])) return true;
   }
   {
-    // The (m, l) table goes to LDS first (one pair per thread and pass): polling it is where the
-    // merger waits for the last chunks.  Then thread t, owning output (head t / D, dim t % D),
-    // loads that output of MC chunks per round trip and re-reads together whichever of them
-    // still show the previous launch's parity.
-    static_assert(GMAX * D <= NC * 64, "one merged output per thread");
+    // Thread t owns output quad t % NQ (head g, 4 dims) of chunks t / NQ, t / NQ + NG, ...: it
+    // reads each chunk's (m, l) pair and its quad (MQ chunks per round trip, re-reading together
+    // whichever still show the previous launch's parity) and folds them into a running
+    // (max, denominator, numerator); the NG chunk groups are then combined in LDS with the same
+    // log-sum-exp rule.
     const int tid = (int)(w * 64 + lane), nb = it.n_b;
-    const float* part0 = (const float*)Ld.part + (size_t)it.first_item * GMAX * (D + 2);
-    const size_t cstride = (size_t)A.Hkv * GMAX * (D + 2);  // floats between chunks of (b, kvh)
-    const bool has_o = tid < G * D;
-    const int g = has_o ? tid / D : 0, dim = tid % D;
-    const float* po = part0 + g * (D + 2) + 2 + dim;
-    float* ml = g_red;  // [n_b][G][m, l]
-    for (int e = tid; e < nb * G; e += NC * 64) {
-      const float* pc = part0 + (size_t)(e / G) * cstride + (e % G) * (D + 2);
-      const float mv = ld_sc1(pc), lv = ld_sc1(pc + 1);
-      ml[2 * e] = tagged_fix(A, pc, mv);
-      ml[2 * e + 1] = tagged_fix(A, pc + 1, lv);
-    }
-    if (!cbar(A, gen)) return false;
-    if (has_o) {
-      float M = -INFINITY;
-      for (int c = 0; c < nb; ++c) M = fmaxf(M, ml[2 * (c * G + g)]);
-      float den = 0.0f, num = 0.0f;
-      constexpr int MC = 16;
-      for (int c0 = 0; c0 < nb; c0 += MC) {
-        float oc[MC];
+    const float* part0 = (const float*)Ld.part + (size_t)it.first_item * GMAX * (D + 4);
+    const size_t cstride = (size_t)A.Hkv * GMAX * (D + 4);  // floats between chunks of (b, kvh)
+    const int NQ = G * D / 4, NG = NC * 64 / NQ;  // output quads; chunk groups
+    const int q = tid % NQ, cg = tid / NQ, g = q / (D / 4), d0 = 4 * (q % (D / 4));
+    const float* ph = part0 + g * (D + 4);  // this head's row in chunk 0
+    float Mt = -INFINITY, den = 0.0f, num[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int MQ = 8;
+    for (int c0 = cg; cg < NG && c0 < nb; c0 += MQ * NG) {  // (threads past NG x NQ idle)
+      float v[MQ][6];  // m, l, o[4]
 #pragma unroll
-        for (int k = 0; k < MC; ++k) oc[k] = c0 + k < nb ? ld_sc1(po + (size_t)(c0 + k) * cstride) : tagv(0.0f, par);
-        Watchdog wd(A);
-        while (true) {
-          u32 stale = 0;
+      for (int k = 0; k < MQ; ++k) {
+        const int c = c0 + k * NG;
+        if (c < nb) {
+          ld4_sc1(ph + (size_t)c * cstride + 4 + d0, v[k] + 2);
+          ld2_sc1(ph + (size_t)c * cstride, v[k]);
+        } else {
 #pragma unroll
-          for (int k = 0; k < MC; ++k) stale |= tag_ok(oc[k], par) ? 0u : 1u << k;
-          if (stale == 0 || aborted() || wd.expired()) break;
-          __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-          for (int k = 0; k < MC; ++k)
-            if ((stale >> k) & 1u) oc[k] = ld_sc1(po + (size_t)(c0 + k) * cstride);
-        }
-#pragma unroll
-        for (int k = 0; k < MC; ++k) {
-          if (c0 + k < nb) {
-            const float f = __expf(ml[2 * ((c0 + k) * G + g)] - M);
-            den += f * ml[2 * ((c0 + k) * G + g) + 1];
-            num += f * oc[k];
-          }
+          for (int e = 0; e < 6; ++e) v[k][e] = tagv(e == 0 ? -1.0e30f : 0.0f, par);
         }
       }
-      st_tag((float*)Ld.mix_o + (size_t)b * A.mix + (kvh * G + g) * D + dim, num / den, par);
+      Watchdog wd(A);
+      while (true) {
+        u32 stale = 0;
+#pragma unroll
+        for (int k = 0; k < MQ; ++k) stale |= tags_ok<6>(v[k], par) ? 0u : 1u << k;
+        if (stale == 0 || aborted() || wd.expired()) break;
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int k = 0; k < MQ; ++k)
+          if ((stale >> k) & 1u) {
+            ld4_sc1(ph + (size_t)(c0 + k * NG) * cstride + 4 + d0, v[k] + 2);
+            ld2_sc1(ph + (size_t)(c0 + k * NG) * cstride, v[k]);
+          }
+      }
+      float mr = Mt;
+#pragma unroll
+      for (int k = 0; k < MQ; ++k) mr = fmaxf(mr, v[k][0]);
+      const float sc = Mt == -INFINITY ? 0.0f : __expf(Mt - mr);
+      den *= sc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[e] *= sc;
+#pragma unroll
+      for (int k = 0; k < MQ; ++k) {
+        if (c0 + k * NG < nb) {
+          const float f = __expf(v[k][0] - mr);
+          den += f * v[k][1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) num[e] += f * v[k][2 + e];
+        }
+      }
+      Mt = mr;
+    }
+    // combine the chunk groups: acc[cg][q] = (max, den, num[4]) (a group with no chunk has max -inf)
+    float* acc = g_red;
+    if (cg < NG) {
+      float* a6 = acc + (cg * NQ + q) * 6;
+      a6[0] = Mt; a6[1] = den;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a6[2 + e] = num[e];
+    }
+    if (!cbar(A, gen)) return false;
+    if (tid < NQ) {
+      float M = -INFINITY;
+      for (int j = 0; j < NG; ++j) M = fmaxf(M, acc[(j * NQ + q) * 6]);
+      float dn = 0.0f, nm[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j = 0; j < NG; ++j) {
+        const float* a6 = acc + (j * NQ + q) * 6;
+        const float f = a6[0] == -INFINITY ? 0.0f : __expf(a6[0] - M);
+        dn += f * a6[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nm[e] += f * a6[2 + e];
+      }
+      float* dst = (float*)Ld.mix_o + (size_t)b * A.mix + (kvh * G + g) * D + d0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st_tag(dst + e, nm[e] / dn, par);
     }
   }
   return true;

@@ -297,9 +297,6 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
     if (const char* e = getenv("MK_ATTN_ITEMS_PER_CU")) per_cu = std::max(per_cu, atoi(e));  // diagnostic
     P.n_items = m.n_attn ? n_cus * per_cu : 0;
   }
-  // the merge of one (sequence, KV head) stages every chunk's (m, l) per query head in LDS
-  if (m.n_attn && (int64_t)(P.n_items / Hkv) * (d.n_q_heads / Hkv) * 2 > RED_FLOATS)
-    return fmt("too many attention chunks per KV head for the merge (%d items, %d KV heads)", P.n_items, Hkv);
   const int gmax = m.n_attn ? 512 / hd : 0;
 
   // ---------------- workspace layout (offsets; sizes of the queue sections are known after planning)
@@ -317,7 +314,7 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
     auto& Q = Y.layer[l];
     if (m.kinds[l] == MK_LAYER_ATTN) {
       Q.qkv = take((size_t)B * qkv_w * 4);
-      Q.part = take((size_t)P.n_items * gmax * (hd + 2) * 4);
+      Q.part = take((size_t)P.n_items * gmax * (hd + 4) * 4);
     } else {
       Q.qkv = take((size_t)B * u_w * 4);
     }
