@@ -53,8 +53,9 @@ constexpr int16_t NO_STAGE = -1;
 // store-completion wait before it (OPF_NO_SIGNAL).
 constexpr uint32_t OPF_TAGGED_IN = 1u;
 constexpr uint32_t OPF_NO_SIGNAL = 2u;
-// With OPF_TAGGED_IN: only rows that attention writes this launch (b < batch, context in range)
-// are polled; the others are never consumed.
+// With OPF_TAGGED_IN: only rows of live sequences (b < batch, context in range) are polled --
+// attention writes no others and the delta rule writes only b < max_batch; the rest are never
+// consumed.
 constexpr uint32_t OPF_LIVE_ROWS = 4u;
 // ATTN: the last chunk of each (sequence, KV head) in item order merges, polling the tagged
 // partials (one item per CU); without it the last chunk to finish merges (ticket).

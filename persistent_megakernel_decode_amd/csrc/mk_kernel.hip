@@ -1067,7 +1067,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
           : epi == EPI_LOGITS ? __builtin_bit_cast(float, ld_i32_sc1(A.row_ok + b)) : 0.0f;  // row_ok for logits
   if (flags & OPF_TAGGED_IN) {
     // poll the inputs themselves: re-read every fragment that does not yet show this launch's parity
-    if (flags & OPF_LIVE_ROWS) {  // rows without attention this launch are never written: skip them
+    if (flags & OPF_LIVE_ROWS) {  // rows of sequences not live this launch may be unwritten: skip them
       const int bb = B == 1 ? 0 : (int)min(bl, (u32)B - 1);
       if (!(bb < A.batch && clamp_ctx(A, A.ctx_lens[bb]) > 0)) fv = 0;
     }
@@ -1271,6 +1271,7 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
   // the Op's fields as independent scalars: kept whole, its 8-dword load groups are what the
   // compiler spills and reloads inside the stream loop
   const u32 epi = opq((u32)o.epi), norm = opq((u32)o.norm), nrows = opq(o.nrows), nks = opq(o.ppr), K = opq(o.K);
+  const u32 flags = opq(o.flags);
   const u32 row0 = opq(o.row0), ld_in = opq(o.ld_in), ld_out = opq(o.ld_out);
   const uint64_t in = opq(o.in), gamma = opq(o.gamma), outp = opq(o.out), resp = opq(o.res);
   const bool swiglu = epi == EPI_SWIGLU;
@@ -1296,6 +1297,21 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
       for (int e = 0; e < 8; ++e) xv[e] = 0.0f;
     }
     gv = (norm && ks < nks) ? *(const u32x4*)(gm + k0) : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  };
+  // tagged inputs: wait until this lane's block of segment ks shows this launch's parity (lanes of
+  // sequences that are not live are not checked with OPF_LIVE_ROWS)
+  const u32 par = A.tag & 1u;
+  const bool tcheck = (flags & OPF_TAGGED_IN) && cval &&
+                      (!(flags & OPF_LIVE_ROWS) || ((int)col < A.batch && clamp_ctx(A, A.ctx_lens[col]) > 0));
+  auto ready = [&](u32 ks, float* xv) -> bool {
+    const bool need = tcheck && ks < nks;
+    Watchdog wd(A);
+    while (__builtin_amdgcn_ballot_w64(need && !tags_ok<8>(xv, par)) != 0) {
+      if (aborted() || wd.expired()) return false;
+      __builtin_amdgcn_s_sleep(1);
+      if (need && !tags_ok<8>(xv, par)) ld8_sc1(xin + ks * MMV_KSEG + w * 32 + kq * 8, xv);
+    }
+    return true;
   };
   // one segment: this wave's input block times every tile of the segment (the slots must be full)
   auto consume = [&](const float* xv, const u32x4& gv) {
@@ -1335,6 +1351,7 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
     for (int i = 0; i < 4; ++i) {
       if (ks + i < nks) {
         if ((u32)i % gs == 0 && !wait_full(A, seq + min(gs, nks - (ks + i)) * nt - 1)) return false;
+        if ((flags & OPF_TAGGED_IN) && !ready(ks + i, xr[i])) return false;
         consume(xr[i], gr[i]);
         if (((u32)i + 1) % gs == 0 || ks + i + 1 == nks) release_upto(w, seq);
         fetch(ks + i + 4, xr[i], gr[i]);
@@ -1853,8 +1870,9 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
       if (ok) {
 #pragma unroll
         for (int e = 0; e < DPL; ++e) sdst[(size_t)r * DK + lane * DPL + e] = sv[e];
-        if (lane == 0) st_sc1((float*)Ld.mix_o + (size_t)b * A.mix + h * A.dv + j0 + r, oj);
       }
+      // every item writes its outputs (zero for a row out of contract), tagged
+      if (lane == 0) st_tag((float*)Ld.mix_o + (size_t)b * A.mix + h * A.dv + j0 + r, ok ? oj : 0.0f, A.tag & 1u);
     }
     // rolling conv state of this slot's value channels
     if (ok && (int)lane < RPS) {

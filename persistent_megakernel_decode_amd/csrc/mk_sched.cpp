@@ -419,21 +419,22 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
       q[cu].push_back(o);
     }
   }
-  // Dependencies: an op whose wait stage was written by EMBED, a projection or attention (tagged
-  // activations) polls its inputs; a stage is signalled only if some op waits on its counter.  The batch-8
-  // matrix-core path keeps the counters (MK_STAGE_COUNTERS=1 keeps them everywhere: diagnostic).
+  // Dependencies: an op whose wait stage was written by EMBED, a projection, attention or the
+  // delta rule (tagged activations) polls its inputs; a stage is signalled only if some op waits
+  // on its counter (MK_STAGE_COUNTERS=1 keeps the counters everywhere: diagnostic).
   {
-    bool tags = P.kernel_batch <= 4;
-    if (const char* e = getenv("MK_STAGE_COUNTERS")) tags = tags && atoi(e) == 0;
+    bool tags = true;
+    if (const char* e = getenv("MK_STAGE_COUNTERS")) tags = atoi(e) == 0;
     std::vector<uint8_t> counted(S, 0);
     for (auto& qc : q)
       for (Op& o : qc) {
         if (o.wait_stage == NO_STAGE) continue;
         const uint8_t pop = bd.stage_ops[o.wait_stage][0].opcode;
-        const bool tagged_src = pop == OP_EMBED || pop == OP_GEMV || pop == OP_ATTN;
-        const bool tagged_dst = pop == OP_ATTN ? o.opcode == OP_GEMV
-                                               : o.opcode == OP_GEMV || o.opcode == OP_ATTN || o.opcode == OP_DELTA;
-        if (tags && tagged_src && tagged_dst) o.flags |= OPF_TAGGED_IN | (pop == OP_ATTN ? OPF_LIVE_ROWS : 0u);
+        const bool mixer = pop == OP_ATTN || pop == OP_DELTA;  // rows written only for live sequences
+        const bool tagged_src = pop == OP_EMBED || pop == OP_GEMV || pop == OP_MMV || mixer;
+        const bool proj = o.opcode == OP_GEMV || o.opcode == OP_MMV;
+        const bool tagged_dst = mixer ? proj : proj || o.opcode == OP_ATTN || o.opcode == OP_DELTA;
+        if (tags && tagged_src && tagged_dst) o.flags |= OPF_TAGGED_IN | (mixer ? OPF_LIVE_ROWS : 0u);
         else counted[o.wait_stage] = 1;
       }
     for (auto& qc : q)
@@ -494,7 +495,7 @@ int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
       last = o.sig_stage;
       if (o.wait_stage != NO_STAGE && o.wait_stage >= o.sig_stage)
         bad(fmt("cu %d op %u: waits on stage %d, not earlier than its own %d", c, i, o.wait_stage, o.sig_stage));
-      if ((o.flags & OPF_TAGGED_IN) && (o.opcode == OP_MMV || o.opcode == OP_EMBED || o.wait_stage == NO_STAGE))
+      if ((o.flags & OPF_TAGGED_IN) && (o.opcode == OP_EMBED || o.wait_stage == NO_STAGE))
         bad(fmt("cu %d op %u: polls tagged inputs it cannot check", c, i));
       seen[o.sig_stage]++;
       idx[o.sig_stage].push_back(o.sig_index);
