@@ -57,9 +57,6 @@ constexpr uint32_t OPF_NO_SIGNAL = 2u;
 // attention writes no others and the delta rule writes only b < max_batch; the rest are never
 // consumed.
 constexpr uint32_t OPF_LIVE_ROWS = 4u;
-// ATTN: the last chunk of each (sequence, KV head) in item order merges, polling the tagged
-// partials (one item per CU); without it the last chunk to finish merges (ticket).
-constexpr uint32_t OPF_POLL_MERGE = 8u;
 
 // One queue entry (128 bytes).  Pointers are device addresses.
 //

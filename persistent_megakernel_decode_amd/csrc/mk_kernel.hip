@@ -1681,26 +1681,12 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
     st_tag(part + g * (D + 4) + 4 + dim, Os, par);
     if (dim == 0) { st_tag(part + g * (D + 4), M, par); st_tag(part + g * (D + 4) + 1, Ls, par); }
   }
-  // One chunk of (b, kvh) merges all of its chunks with the log-sum-exp rule.  With
-  // OPF_POLL_MERGE (one attention item per CU) it is the last chunk in item order, which polls the
-  // chunks' tagged partials: items go to CUs round-robin in item order, so every chunk it waits for
-  // sits at the same or an earlier position in its CU's queue and no two mergers wait on each
-  // other.  Otherwise the last chunk to finish merges (a ticket taken after its partial landed).
-  if (o.flags & OPF_POLL_MERGE) {
-    if (o.row0 != (u32)(it.first_item + (it.n_b - 1) * A.Hkv)) return true;
-    if (!cbar(A, gen)) return false;  // every thread is done with the wave partials in LDS
-  } else {
-    __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));
-    if (!cbar(A, gen)) return false;
-    u32* ticket = (u32*)Ld.tickets + (size_t)b * A.Hkv + kvh;
-    if (w == 0 && lane == 0) {
-      const u32 prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      g_bcast[0] = (prev == (u32)it.n_b - 1) ? 1u : 0u;
-      if (prev == (u32)it.n_b - 1) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (!cbar(A, gen)) return false;
-    if (!lds_ld(&g_bcast[0])) return true;
-  }
+  // The last chunk of (b, kvh) in item order merges all of its chunks with the log-sum-exp rule,
+  // polling their tagged partials.  Items go to CUs round-robin in item order, so every chunk it
+  // waits for sits at the same or an earlier position in its CU's queue: by induction on the item
+  // index every item completes, and no two mergers can wait on each other.
+  if (o.row0 != (u32)(it.first_item + (it.n_b - 1) * A.Hkv)) return true;
+  if (!cbar(A, gen)) return false;  // every thread is done with the wave partials in LDS
   {
     // Thread t owns output quad t % NQ (head g, 4 dims) of chunks t / NQ, t / NQ + NG, ...: it
     // reads each chunk's (m, l) pair and its quad (MQ chunks per round trip, re-reading together

@@ -440,10 +440,6 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
     for (auto& qc : q)
       for (Op& o : qc)
         if (o.sig_stage != NO_STAGE && !counted[o.sig_stage]) o.flags |= OPF_NO_SIGNAL;
-    if (tags && P.n_items == n_cus)
-      for (auto& qc : q)
-        for (Op& o : qc)
-          if (o.opcode == OP_ATTN) o.flags |= OPF_POLL_MERGE;
   }
   P.queue_off.assign(n_cus + 1, 0);
   for (int c2 = 0; c2 < n_cus; ++c2) {

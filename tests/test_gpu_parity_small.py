@@ -45,3 +45,15 @@ def test_parity_small(case):
         f"greedy {rep.greedy_agree}/{rep.greedy_checked}")
     assert not rep.failures, "\n".join(rep.failures[:20])
     assert rep.steps == steps
+
+
+@pytest.mark.parametrize("case", ["tiny-ragged", "tiny-hybrid", "small-b8"])
+def test_parity_small_counters(case, monkeypatch):
+    """The same checks with every dependency taken through the stage counters (the diagnostic
+    plan): the counter path stays correct while the tagged one is the default."""
+    monkeypatch.setenv("MK_STAGE_COUNTERS", "1")
+    cfg, steps = CASES[case]
+    rep = run_parity(cfg, steps)
+    say(f"[{case}, counters] {rep.steps} steps, worst logits rel {rep.worst_rel:.2e}, worst mid {rep.worst_mid:.2e}")
+    assert not rep.failures, "\n".join(rep.failures[:20])
+    assert rep.steps == steps
