@@ -32,6 +32,8 @@ namespace mk {
 typedef uint32_t u32;
 typedef uint64_t u64;
 typedef __attribute__((ext_vector_type(4))) u32 u32x4;
+typedef uint16_t __attribute__((may_alias)) u16_alias;  // partial writes into float / vector LDS areas
+typedef u32 __attribute__((may_alias)) u32_alias;
 typedef __attribute__((ext_vector_type(2))) u32 u32x2;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14])
@@ -1452,7 +1454,6 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   const float scale = 1.0f / sqrtf((float)D);
   const int posc = (pos >= 0 && pos < A.max_ctx) ? pos : 0;
   const float* rope = A.rope + (size_t)posc * (D / 2) * 2;
-  float* qs = g_red;                   // [G][D] rotated, scaled queries
   float* kvn = g_red + 512;            // [2][D] the new token's rotated K and its V, bf16-rounded
 
   // rotary embedding of a head held as dims [lane*DPL, lane*DPL + DPL): partner lane ^ 32
@@ -1475,8 +1476,14 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
     for (int e = 0; e < DPL; ++e) v[e] *= r * bf2f(gain[lane * DPL + e]);
   };
 
-  // 1. one task per wave: query heads 0..G-1, then (chunk holding the new token) its K and V
+  // 1. one task per wave: query heads 0..G-1, then (chunk holding the new token) its K and V.
+  //    A query head goes straight into the matrix-core A operand in LDS (row = head, split into
+  //    bf16 hi + lo): 16-byte chunk (kb, hi/lo, kc, row) holds dims 32 kb + 8 kc .. + 7.  Rows past
+  //    G are zeroed by every wave in the same pass.
+  u16_alias* qfh = (u16_alias*)(g_red + QF);
   const bool has_new = pos >= it.p0 && pos < it.p1;
+  for (int c = (int)(w * 64 + lane); c < KB * 2 * 4 * 16; c += NC * 64)
+    if ((c & 15) >= G) ((u32x4*)(g_red + QF))[c] = u32x4{0u, 0u, 0u, 0u};
   const int ntask = G + (has_new ? 2 : 0);
   for (int t = (int)w; t < ntask; t += NC) {
     const int row = t < G ? kvh * G + t : (t == G ? A.Hq + kvh : A.Hq + A.Hkv + kvh);
@@ -1493,8 +1500,21 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
       rotate(v);
     }
     if (t < G) {
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) qs[t * D + lane * DPL + e] = v[e] * scale;
+      const int i0 = (int)lane * DPL;  // this lane's first dim (DPL consecutive dims, one chunk)
+      const int chunk = ((i0 >> 5) * 2) * 64 + ((i0 >> 3) & 3) * 16 + t, j = i0 & 7;
+      if constexpr (DPL == 2) {
+        const f32x2 x = {v[0] * scale, v[1] * scale};
+        const bf16x2 xh = __builtin_convertvector(x, bf16x2);
+        const bf16x2 xl = __builtin_convertvector(x - __builtin_convertvector(xh, f32x2), bf16x2);
+        *(u32_alias*)(qfh + chunk * 8 + j) = __builtin_bit_cast(u32, xh);
+        *(u32_alias*)(qfh + (chunk + 64) * 8 + j) = __builtin_bit_cast(u32, xl);
+      } else {
+        const f32x2 x = {v[0] * scale, 0.0f};
+        const bf16x2 xh = __builtin_convertvector(x, bf16x2);
+        const bf16x2 xl = __builtin_convertvector(x - __builtin_convertvector(xh, f32x2), bf16x2);
+        qfh[chunk * 8 + j] = (uint16_t)__builtin_bit_cast(u32, xh);
+        qfh[(chunk + 64) * 8 + j] = (uint16_t)__builtin_bit_cast(u32, xl);
+      }
     } else {
       uint16_t hb[DPL];  // the cache holds bf16: attend to the rounded values
 #pragma unroll
@@ -1512,18 +1532,7 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
     }
   }
   if (!cbar(A, gen)) return false;
-
-  // 2. query fragments, built once into LDS by waves 0..KB-1: matrix-core A operand, row = head
-  //    lane % 16, k-chunk lane / 16, each split into bf16 hi + lo
-  u32x4* qf = (u32x4*)(g_red + QF);
-  if ((int)w < KB) {
-    const int kb = (int)w, gq = (int)(lane & 15), kc = (int)(lane >> 4);
-    float x[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = gq < G ? qs[gq * D + kb * 32 + kc * 8 + e] : 0.0f;
-    split_bf16x8(x, qf[(kb * 2) * 64 + lane], qf[(kb * 2 + 1) * 64 + lane]);
-  }
-  if (!cbar(A, gen)) return false;
+  const u32x4* qf = (const u32x4*)(g_red + QF);
 
   // 3. this wave's slots: w, w + NC, ...  Score tile lanes: position p = 16*blk + lane % 16,
   //    heads hr .. hr + 3 with hr = 4 * (lane / 16).

@@ -31,6 +31,10 @@ CASES = {
     "small-b8": (synth.Config("small-b8", n_layers=2, hidden=512, n_q_heads=4, n_kv_heads=4, head_dim=128,
                               ffn=1024, vocab=2048, batch=8, ctx=[5, 40, 0, 17, 100, 3, 64, 31], steps=3, seed=14,
                               shuffle_pages=True, gain_range=(0.5, 1.5)), 3),
+    # chunks of nine ring slots (one past a full round of the eight waves), the new token in a
+    # partly filled last slot
+    "small-split9": (synth.Config("small-split9", n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=8, head_dim=128,
+                                  ffn=1024, vocab=2048, batch=1, ctx=[4390], steps=3, seed=15), 3),
     # head_dim 64 with the largest group the kernel takes (8 query heads per KV head)
     "small-gqa8-d64": (synth.Config("small-gqa8-d64", n_layers=2, hidden=512, n_q_heads=16, n_kv_heads=2,
                                     head_dim=64, ffn=1024, vocab=2048, batch=1, ctx=[150], steps=3, seed=13), 3),
