@@ -34,6 +34,7 @@ typedef uint64_t u64;
 typedef __attribute__((ext_vector_type(4))) u32 u32x4;
 typedef uint16_t __attribute__((may_alias)) u16_alias;  // partial writes into float / vector LDS areas
 typedef u32 __attribute__((may_alias)) u32_alias;
+typedef u32x4 __attribute__((may_alias)) u32x4_alias;
 typedef __attribute__((ext_vector_type(2))) u32 u32x2;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14])
@@ -1555,8 +1556,8 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
     if (has_new && pos >= pbase && pos < pbase + PPS) {
       // the new token's K/V are not in the cache the loader read: put them into the slot
       const int r = pos - pbase, d0 = (int)lane * DPL, c = d0 / 8;
-      uint16_t* kd = (uint16_t*)(kslot + r * RB + ((c ^ (r % CPR)) * 16)) + (d0 % 8);
-      uint16_t* vd = (uint16_t*)(vslot + r * RB) + d0;
+      u16_alias* kd = (u16_alias*)(kslot + r * RB + ((c ^ (r % CPR)) * 16)) + (d0 % 8);
+      u16_alias* vd = (u16_alias*)(vslot + r * RB) + d0;
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
         kd[e] = f2bf(kvn[d0 + e]);
@@ -1571,7 +1572,7 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const int c = kb * 4 + (int)(lane >> 4);
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4*)(kslot + p * RB + ((c ^ (p % CPR)) * 16)));
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *(const u32x4_alias*)(kslot + p * RB + ((c ^ (p % CPR)) * 16)));
         const bf16x8 qh = __builtin_bit_cast(bf16x8, qf[(kb * 2) * 64 + lane]);
         const bf16x8 ql = __builtin_bit_cast(bf16x8, qf[(kb * 2 + 1) * 64 + lane]);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, kf, acc, 0, 0, 0);
@@ -1630,8 +1631,8 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
       for (int j = 0; j < 4; ++j) {
         const int p = p0 + j;
         u32 u;
-        if constexpr (DPL == 2) u = *(const u32*)(vslot + p * RB + lane * 4);
-        else u = *(const uint16_t*)(vslot + p * RB + lane * 2);
+        if constexpr (DPL == 2) u = *(const u32_alias*)(vslot + p * RB + lane * 4);
+        else u = *(const u16_alias*)(vslot + p * RB + lane * 2);
         vw[j] = p < np ? u : 0u;
 #pragma unroll
         for (int g4 = 0; g4 < GMAX / 4; ++g4) pv[j][g4] = *(const f32x4*)(pw + p * GMAX + 4 * g4);
