@@ -95,41 +95,37 @@ __device__ __forceinline__ T sload(const T* p) {
 }
 
 // Agent-coherent accesses for data that crosses compute units: relaxed agent-scope atomics,
-// i.e. global loads / stores with the sc1 cache-policy bit, with per-lane addresses.
+// i.e. global loads / stores with the sc1 cache-policy bit, with per-lane addresses.  The pointers
+// are cast to the global address space first: through a generic pointer they become FLAT
+// accesses, which also count against the LDS counter (every LDS wait then waits for them too).
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gptr(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
 __device__ __forceinline__ float ld_sc1(const float* p) {
-  return __builtin_bit_cast(float, __hip_atomic_load((const u32*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return __builtin_bit_cast(float, __hip_atomic_load(gptr((const u32*)p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 __device__ __forceinline__ void st_sc1(float* p, float v) {
-  __hip_atomic_store((u32*)p, __builtin_bit_cast(u32, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gptr((u32*)p), __builtin_bit_cast(u32, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void ld8_sc1(const float* p, float* out) {  // 8 consecutive floats, 8-B aligned
-  const uint64_t* q = (const uint64_t*)p;
+template <int N>  // N consecutive floats (N even), 8-B aligned
+__device__ __forceinline__ void ldn_sc1(const float* p, float* out) {
+  const auto q = gptr((const uint64_t*)p);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < N / 2; ++i) {
     const uint64_t v = __hip_atomic_load(q + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     out[2 * i] = __builtin_bit_cast(float, (u32)v);
     out[2 * i + 1] = __builtin_bit_cast(float, (u32)(v >> 32));
   }
 }
-__device__ __forceinline__ void ld2_sc1(const float* p, float* out) {  // 2 consecutive floats, 8-B aligned
-  const uint64_t v = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  out[0] = __builtin_bit_cast(float, (u32)v);
-  out[1] = __builtin_bit_cast(float, (u32)(v >> 32));
-}
-__device__ __forceinline__ void ld4_sc1(const float* p, float* out) {  // 4 consecutive floats, 8-B aligned
-  const uint64_t* q = (const uint64_t*)p;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint64_t v = __hip_atomic_load(q + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    out[2 * i] = __builtin_bit_cast(float, (u32)v);
-    out[2 * i + 1] = __builtin_bit_cast(float, (u32)(v >> 32));
-  }
-}
+__device__ __forceinline__ void ld8_sc1(const float* p, float* out) { ldn_sc1<8>(p, out); }
+__device__ __forceinline__ void ld4_sc1(const float* p, float* out) { ldn_sc1<4>(p, out); }
+__device__ __forceinline__ void ld2_sc1(const float* p, float* out) { ldn_sc1<2>(p, out); }
 __device__ __forceinline__ u32 ld_u32_sc1(const u32* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gptr(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int32_t ld_i32_sc1(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gptr(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Tagged activations: bit 0 of every fp32 value that EMBED or a projection writes holds the
