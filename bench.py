@@ -110,8 +110,9 @@ def calibrate_copy(nbytes: int) -> int:
     return 0
 
 
-def cpu_baseline(cfg, w, cache, ctx0, budget_s: float) -> dict:
-    """The oracle as it stands, on the host cores, over the same workload's first steps."""
+def cpu_baseline(cfg, w, cache, ctx0, budget_s: float, max_steps: int) -> dict:
+    """The oracle as it stands, on the host cores, over the same workload's first steps (at most
+    `max_steps`: the cache it is given has room for that many new positions)."""
     import oracle
     try:
         cores = len(os.sched_getaffinity(0))
@@ -129,7 +130,7 @@ def cpu_baseline(cfg, w, cache, ctx0, budget_s: float) -> dict:
         times.append(time.perf_counter() - t0)
         toks = [oracle.argmax(l) for l in logits]
         ctx = [c + 1 for c in ctx]
-        if time.time() - t_start > budget_s:
+        if time.time() - t_start > budget_s or len(times) >= max_steps:
             break
     step = float(np.mean(times))
     return {"value": cfg.batch / step, "unit": "tokens/s", "cores": min(threads, cores), "kind": "oracle",
@@ -249,7 +250,8 @@ def main() -> int:
         g.close()
         del g
         torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(cfg, w, synth.make_cache(cfg, ctx0, 8), ctx0, args.cpu_budget)
+        room = 64  # new positions the oracle's cache can take
+        out["cpu_baseline"] = cpu_baseline(cfg, w, synth.make_cache(cfg, ctx0, room), ctx0, args.cpu_budget, room)
     print(json.dumps(out), flush=True)
     return 0
 
