@@ -133,7 +133,16 @@ def cpu_baseline(cfg, w, cache, ctx0, budget_s: float, max_steps: int) -> dict:
         if time.time() - t_start > budget_s or len(times) >= max_steps:
             break
     step = float(np.mean(times))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    import resource
+    rss_gb = resource.getrusage(resource.RUSAGE_SELF).ru_maxrss / 2**20  # KiB -> GiB
     return {"value": cfg.batch / step, "unit": "tokens/s", "cores": min(threads, cores), "kind": "oracle",
+            "cpu_model": model, "host_peak_rss_gib": round(rss_gb, 1), "step_s_median": round(float(np.median(times)), 3),
             "sample": f"{len(times)} full decode steps of the same workload from its first position "
                       f"(mean {step:.3f} s/step, fp64-accumulating C oracle, OpenMP over output rows)"}
 
@@ -245,6 +254,33 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config)},
     }
+    # context: what a plain streaming read reaches on this GPU in the same run (torch's sum over a
+    # 2 GiB buffer, i.e. one read of every byte)
+    buf = torch.empty(1 << 29, dtype=torch.float32, device="cuda")
+    buf.fill_(1.0)
+    rd = []
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        buf.sum()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rd.append(e0.elapsed_time(e1))
+    stream_gbs = buf.numel() * 4 / (float(np.median(rd[1:])) * 1e-3) / 1e9
+    dst = torch.empty_like(buf)
+    cp = []
+    for _ in range(6):  # device-to-device copy (the runtime's blit kernel): read + write bytes
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(buf)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cp.append(e0.elapsed_time(e1))
+    copy_gbs = 2 * buf.numel() * 4 / (float(np.median(cp[1:])) * 1e-3) / 1e9
+    del buf, dst
+    out["stream_read"] = {"gbs": round(stream_gbs, 1), "kernel": "torch.sum over 2 GiB fp32",
+                          "achieved_frac": round(achieved / stream_gbs, 4),
+                          "copy_gbs": round(copy_gbs, 1), "copy": "2 GiB device-to-device copy, read + write bytes"}
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample")
         g.close()
