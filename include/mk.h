@@ -165,6 +165,20 @@ typedef enum {
  * fp32, `count` floats = batch * width), ordered on hip_stream. */
 mk_status mk_copy_midstate(mk_ctx* ctx, int32_t kind, int32_t layer, float* dst, size_t count, void* hip_stream);
 
+/* ---- per-op timing trace (diagnostic) ----
+ * With MK_TRACE=1 in the environment at mk_create, the kernel records for every queue entry the
+ * low 32 bits of the GPU's 100 MHz real-time clock when the op starts, when its inputs are in
+ * hand (projections and attention: after the input poll; other ops: = start) and when it ends
+ * (after the closing barrier of its workgroup), plus its opcode and stage.  The library owns the
+ * trace buffer (allocated at mk_create only in this mode).
+ * mk_copy_trace waits for the last step and copies into host memory `dst` (`count` uint32):
+ *   [0] n_ops, [1] n_cus, [2 .. 2+n_cus] queue offsets (op range of CU c: [off[c], off[c+1])),
+ *   then per op 4 words {opcode << 16 | stage, t_start, t_ready, t_end}.
+ * Returns MK_ERR_STATE when tracing is off and MK_ERR_INVALID_ARG when count is too small
+ * (mk_trace_words gives the size). */
+mk_status mk_trace_words(mk_ctx* ctx, size_t* count);
+mk_status mk_copy_trace(mk_ctx* ctx, uint32_t* dst, size_t count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -62,7 +62,7 @@ class mk_plan_info(ctypes.Structure):
 
 
 EXPORTED = ["mk_workspace_size", "mk_create", "mk_decode_step", "mk_sync_status", "mk_reset", "mk_last_error",
-            "mk_destroy", "mk_plan", "mk_copy_midstate"]
+            "mk_destroy", "mk_plan", "mk_copy_midstate", "mk_trace_words", "mk_copy_trace"]
 
 _lib = None
 
@@ -87,8 +87,10 @@ def lib() -> ctypes.CDLL:
         L.mk_destroy.restype = None
         L.mk_plan.argtypes = [ctypes.POINTER(mk_model_desc), I32, ctypes.POINTER(mk_plan_info)]
         L.mk_copy_midstate.argtypes = [P, I32, I32, P, ctypes.c_size_t, P]
+        L.mk_trace_words.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+        L.mk_copy_trace.argtypes = [P, P, ctypes.c_size_t]
         for f in ("mk_workspace_size", "mk_create", "mk_decode_step", "mk_sync_status", "mk_reset", "mk_plan",
-                  "mk_copy_midstate"):
+                  "mk_copy_midstate", "mk_trace_words", "mk_copy_trace"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -269,6 +271,22 @@ class DecodeContext:
         check(mk_copy_midstate(self.ctx, kind, layer, out.data_ptr(), batch * width, self.stream_ptr()),
               "mk_copy_midstate")
         return out
+
+    def trace(self) -> dict:
+        """Per-op timing of the last step (the context must have been created with MK_TRACE=1):
+        queue offsets per CU and, per op, opcode, stage and the start / inputs-ready / end stamps
+        (100 MHz GPU clock, low 32 bits)."""
+        import numpy as np
+        n = ctypes.c_size_t(0)
+        check(lib().mk_trace_words(self.ctx, ctypes.byref(n)), "mk_trace_words")
+        buf = np.zeros(n.value, np.uint32)
+        check(lib().mk_copy_trace(self.ctx, buf.ctypes.data, n.value), "mk_copy_trace")
+        n_ops, n_cus = int(buf[0]), int(buf[1])
+        off = buf[2:3 + n_cus].astype(np.int64)
+        rec = buf[3 + n_cus:].reshape(n_ops, 4)
+        cu = np.repeat(np.arange(n_cus), np.diff(off))
+        return {"n_cus": n_cus, "queue_off": off, "cu": cu, "opcode": rec[:, 0] >> 16,
+                "stage": (rec[:, 0] & 0xFFFF).astype(np.int16), "t": rec[:, 1:].astype(np.int64)}
 
     def close(self) -> None:
         if getattr(self, "ctx", None):

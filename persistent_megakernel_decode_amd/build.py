@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmk.so")
-SOURCES = ["mk_kernel.hip", "mk_api.cpp", "mk_sched.cpp"]
+SOURCES = ["mk_kernel.hip", "mk_kernel_trace.hip", "mk_api.cpp", "mk_sched.cpp"]
 HEADERS = ["mk_internal.h", "mk_sched.h", os.path.join("..", "..", "include", "mk.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -39,11 +39,19 @@ def build(force: bool = True, verbose: bool = False) -> str:
     if not force and not stale():
         return LIB
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *sources(), "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l and l.strip())
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    # one hipcc per source, in parallel (the two kernel translation units dominate), then link
+    procs = [subprocess.Popen([HIPCC, *FLAGS, "-c", src, "-o", obj], stdout=subprocess.PIPE,
+                              stderr=subprocess.STDOUT, text=True) for src, obj in zip(sources(), objs)]
+    results = [(p.communicate()[0], p.returncode) for p in procs]
+    link = subprocess.run([HIPCC, *[f for f in FLAGS if f not in ("-x", "hip")], *objs, "-o", tmp],
+                          capture_output=True, text=True)
+    results.append((link.stdout + link.stderr, link.returncode))
+    out = "\n".join(l for o, _ in results for l in o.splitlines() if "packed-fp32-ops" not in l and l.strip())
+    if any(rc != 0 for _, rc in results):
+        raise RuntimeError(f"hipcc failed:\n{out}")
     if verbose and out:
         print(out, file=sys.stderr)
     os.replace(tmp, LIB)

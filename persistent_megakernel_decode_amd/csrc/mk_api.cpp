@@ -20,6 +20,10 @@ extern "C" __global__ void mk_megakernel_b1(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_b2(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_b4(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_b8(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_b1_trace(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_b2_trace(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_b4_trace(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_b8_trace(mk::KArgs A);
 
 namespace {
 
@@ -42,12 +46,12 @@ mk_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-const void* kernel_for(int B) {
+const void* kernel_for(int B, bool traced) {
   switch (B) {
-    case 1: return (const void*)mk_megakernel_b1;
-    case 2: return (const void*)mk_megakernel_b2;
-    case 4: return (const void*)mk_megakernel_b4;
-    default: return (const void*)mk_megakernel_b8;
+    case 1: return traced ? (const void*)mk_megakernel_b1_trace : (const void*)mk_megakernel_b1;
+    case 2: return traced ? (const void*)mk_megakernel_b2_trace : (const void*)mk_megakernel_b2;
+    case 4: return traced ? (const void*)mk_megakernel_b4_trace : (const void*)mk_megakernel_b4;
+    default: return traced ? (const void*)mk_megakernel_b8_trace : (const void*)mk_megakernel_b8;
   }
 }
 
@@ -71,7 +75,11 @@ struct mk_ctx {
   mk_status sticky = MK_OK;
   const void* kernel = nullptr;
   bool plain_launch = false;
+  uint32_t* trace = nullptr;  // MK_TRACE=1: device buffer, 4 words per op (library-owned)
   std::mutex busy;
+  ~mk_ctx() {
+    if (trace) (void)hipFree(trace);
+  }
 };
 
 extern "C" {
@@ -201,7 +209,10 @@ mk_status mk_create(const mk_model_desc* desc, const mk_weights* w, const mk_kv_
   }
   ctx->ws = (char*)workspace;
   ctx->ws_bytes = workspace_bytes;
-  ctx->kernel = kernel_for(P.kernel_batch);
+  // MK_TRACE=1: the traced kernels (per-op timing stamps; diagnostic)
+  const char* trace_env = getenv("MK_TRACE");
+  const bool traced = trace_env && atoi(trace_env) != 0;
+  ctx->kernel = kernel_for(P.kernel_batch, traced);
 
   // one resident workgroup per compute unit is required by the persistent design
   int per_cu = 0;
@@ -268,6 +279,17 @@ mk_status mk_create(const mk_model_desc* desc, const mk_weights* w, const mk_kv_
   // workgroup per CU is resident; should some workgroup still not be scheduled, the spin-wait
   // watchdog ends every wait and the step reports MK_ERR_TIMEOUT.
   if (const char* s = getenv("MK_PLAIN_LAUNCH")) ctx->plain_launch = atoi(s) != 0;
+  A.trace = nullptr;
+  if (traced) {
+    const size_t bytes = P.ops.size() * 4 * sizeof(uint32_t);
+    he = hipMalloc((void**)&ctx->trace, bytes);
+    if (he == hipSuccess) he = hipMemset(ctx->trace, 0, bytes);
+    if (he != hipSuccess) {
+      delete ctx;
+      return hip_fail(he, "allocating the trace buffer");
+    }
+    A.trace = ctx->trace;
+  }
   *out = ctx;
   return MK_OK;
 }
@@ -352,6 +374,27 @@ mk_status mk_reset(mk_ctx* ctx) {
 }
 
 void mk_destroy(mk_ctx* ctx) { delete ctx; }
+
+mk_status mk_trace_words(mk_ctx* ctx, size_t* count) {
+  if (!ctx || !count) return fail(MK_ERR_INVALID_ARG, "null argument");
+  *count = 2 + (size_t)ctx->plan.n_cus + 1 + ctx->plan.ops.size() * 4;
+  return MK_OK;
+}
+
+mk_status mk_copy_trace(mk_ctx* ctx, uint32_t* dst, size_t count) {
+  if (!ctx || !dst) return fail(MK_ERR_INVALID_ARG, "null argument");
+  if (!ctx->trace) return fail(MK_ERR_STATE, "tracing is off (set MK_TRACE=1 before mk_create)");
+  size_t need = 0;
+  mk_trace_words(ctx, &need);
+  if (count < need) return fail(MK_ERR_INVALID_ARG, "trace buffer too small: need " + std::to_string(need) + " words");
+  MK_HIP(hipStreamSynchronize(ctx->last_stream));
+  const mk::Plan& P = ctx->plan;
+  dst[0] = (uint32_t)P.ops.size();
+  dst[1] = (uint32_t)P.n_cus;
+  for (int c = 0; c <= P.n_cus; ++c) dst[2 + c] = P.queue_off[c];
+  MK_HIP(hipMemcpy(dst + 3 + P.n_cus, ctx->trace, P.ops.size() * 4 * sizeof(uint32_t), hipMemcpyDeviceToHost));
+  return MK_OK;
+}
 
 mk_status mk_copy_midstate(mk_ctx* ctx, int32_t kind, int32_t layer, float* dst, size_t count, void* hip_stream) {
   if (!ctx || !dst) return fail(MK_ERR_INVALID_ARG, "null argument");

@@ -157,6 +157,7 @@ struct KArgs {
   uint32_t epoch;
   uint32_t tag;               // launch tag: bit 0 is the activation parity, row_ok holds tag << 1 | ok
   uint64_t spin_limit;        // watchdog, in s_memrealtime ticks (100 MHz)
+  uint32_t* trace;            // MK_TRACE=1: per op {opcode << 16 | stage, start, inputs ready, end}; else null
 };
 
 // status bits

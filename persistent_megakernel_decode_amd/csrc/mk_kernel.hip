@@ -41,6 +41,12 @@ typedef __attribute__((ext_vector_type(2))) u32 u32x2;
 #define MK_VMCNT(n) ((((n) & 0xF) | (((n) >> 4) << 14)) | 0x70 | 0xF00)
 #define MK_LGKMCNT0 (0xF | 0x70 | (0x3 << 14))
 
+// Per-op timing stamps are compiled into a second set of kernels only (built from a translation
+// unit that defines MK_TRACE_STAMPS=1), so the untraced kernels carry no trace code at all.
+#ifndef MK_TRACE_STAMPS
+#define MK_TRACE_STAMPS 0
+#endif
+
 constexpr int AUX_NT = 2;    // cache policy: non-temporal (streamed once)
 constexpr int AUX_SC1 = 16;  // cache policy: agent-scope coherent
 
@@ -59,6 +65,9 @@ __shared__ __attribute__((aligned(16))) u32 g_consumed[NC];
 __shared__ u32 g_bar;           // compute-wave barrier counter
 __shared__ u32 g_abort;         // set on watchdog expiry: every wave leaves
 __shared__ u32 g_bcast[4];
+#if MK_TRACE_STAMPS
+__shared__ u32 g_trace_oi;  // queue index of the running op (written and read by compute wave 0 only)
+#endif
 
 // ------------------------------------------------------------------ helpers
 // An opaque copy of a uniform value in its own scalar register(s).
@@ -332,6 +341,13 @@ __device__ __forceinline__ bool row_ok_wait(const KArgs& A, int b) {
 // The same for an entry loaded earlier (`v`), so that the load overlaps other work.
 __device__ __forceinline__ bool row_ok_fix(const KArgs& A, int b, int32_t v) {
   return ((u32)v >> 1) == (A.tag & 0x7FFFFFFFu) ? (v & 1) != 0 : row_ok_wait(A, b);
+}
+
+// Traced kernels: stamp "inputs in hand" for the running op (compute wave 0, lane 0 only).
+__device__ __forceinline__ void trace_ready(const KArgs& A, u32 w) {
+#if MK_TRACE_STAMPS
+  if (w == 0 && lane_id() == 0) A.trace[(size_t)g_trace_oi * 4 + 2] = (u32)__builtin_amdgcn_s_memrealtime();
+#endif
 }
 
 // Compute wave w will read no ring slot below `upto` again.  Monotonic per wave.
@@ -1087,6 +1103,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
       for (int f = 0; f < NF; ++f) todo |= ((fv >> f) & 1u) && !tags_ok<8>(xf[f], par) ? 1u << f : 0u;
     }
   }
+  trace_ready(A, w);
   if (norm) {
     // sum of squares per sequence (each input appears once among the waves with distinct pieces),
     // read back in the epilogue
@@ -1529,6 +1546,7 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
     }
   }
   if (!cbar(A, gen)) return false;
+  trace_ready(A, w);
   const u32x4* qf = (const u32x4*)(g_red + QF);
 
   // 3. this wave's slots: w, w + NC, ...  Score tile lanes: position p = 16*blk + lane % 16,
@@ -1908,6 +1926,16 @@ __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
   for (u32 oi = q0; oi < q1; ++oi) {
     const KArgs& A = kargs();
     const Op o = sload(A.ops + oi);
+#if MK_TRACE_STAMPS
+    if (w == 0 && lane_id() == 0) {
+      const u32 t = (u32)__builtin_amdgcn_s_memrealtime();
+      u32* tr = A.trace + (size_t)oi * 4;
+      tr[0] = ((u32)o.opcode << 16) | (u32)(uint16_t)o.sig_stage;
+      tr[1] = t;
+      tr[2] = t;
+      g_trace_oi = oi;
+    }
+#endif
     if (o.wait_stage != NO_STAGE && !(o.flags & OPF_TAGGED_IN)) {  // inputs finished by counter
       if (w == 0) wait_stage(A, o.wait_stage);
       if (!cbar(A, gen)) return;
@@ -1941,6 +1969,9 @@ __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
     if (sig) __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));  // this wave's outputs are complete
     if (!cbar(A, gen)) return;  // (also: the next op may overwrite this op's LDS areas)
     if (sig && w == 0 && lane_id() == 0) signal_stage(A, o.sig_stage, o.sig_index);
+#if MK_TRACE_STAMPS
+    if (w == 0 && lane_id() == 0) A.trace[(size_t)oi * 4 + 3] = (u32)__builtin_amdgcn_s_memrealtime();
+#endif
   }
 }
 
@@ -1958,7 +1989,12 @@ __device__ __forceinline__ void megakernel_body(const KArgs& A) {
 
 }  // namespace mk
 
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_b1(mk::KArgs A) { mk::megakernel_body<1>(A); }
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_b2(mk::KArgs A) { mk::megakernel_body<2>(A); }
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_b4(mk::KArgs A) { mk::megakernel_body<4>(A); }
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_b8(mk::KArgs A) { mk::megakernel_body<8>(A); }
+#if MK_TRACE_STAMPS
+#define MK_KNAME(b) mk_megakernel_##b##_trace
+#else
+#define MK_KNAME(b) mk_megakernel_##b
+#endif
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b1)(mk::KArgs A) { mk::megakernel_body<1>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b2)(mk::KArgs A) { mk::megakernel_body<2>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b4)(mk::KArgs A) { mk::megakernel_body<4>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b8)(mk::KArgs A) { mk::megakernel_body<8>(A); }

@@ -1,0 +1,49 @@
+"""Summaries of the per-op timing trace (contexts created with MK_TRACE=1).
+
+Times are the GPU's 100 MHz real-time clock (low 32 bits), so every figure is in microseconds
+after unwrapping against the first op.  A stage's time is measured from the previous stage's last
+op end to its own last op end; "waiting" is the median time its ops spend before their inputs are
+in hand, "tail" how long its last op ends after its median op.
+"""
+import numpy as np
+
+OPCODES = {1: "embed", 2: "gemv", 3: "attention", 4: "delta", 5: "mmv"}
+
+
+def unwrap(tr: dict) -> np.ndarray:
+    """Stamps [n_ops, 3] (start, ready, end) in us relative to the earliest start."""
+    t = tr["t"].astype(np.int64)
+    ref = int(t[:, 0].min())
+    d = (t - ref + (1 << 31)) % (1 << 32) - (1 << 31)
+    return d / 100.0
+
+
+def stage_table(tr: dict) -> list:
+    """One row per stage: opcode, ops, time from the previous stage's end, waiting, tail."""
+    us = unwrap(tr)
+    rows, prev_end = [], 0.0
+    for s in range(int(tr["stage"].max()) + 1):
+        m = tr["stage"] == s
+        if not m.any():
+            continue
+        end = us[m, 2]
+        rows.append({"stage": s, "op": OPCODES.get(int(tr["opcode"][m][0]), "?"), "ops": int(m.sum()),
+                     "us": float(end.max() - prev_end), "waiting_us": float(np.median(us[m, 1] - us[m, 0])),
+                     "tail_us": float(end.max() - np.median(end))})
+        prev_end = float(end.max())
+    return rows
+
+
+def check(tr: dict) -> list:
+    """Consistency problems: stamps out of order within an op or across a CU's queue."""
+    us = unwrap(tr)
+    bad = []
+    if np.any(us[:, 1] < us[:, 0]) or np.any(us[:, 2] < us[:, 1]):
+        bad.append("an op's stamps are out of order")
+    off = tr["queue_off"]
+    for c in range(tr["n_cus"]):
+        a, b = int(off[c]), int(off[c + 1])
+        if b - a > 1 and np.any(us[a + 1:b, 0] < us[a:b - 1, 2]):
+            bad.append(f"cu {c}: an op starts before the previous one ends")
+            break
+    return bad
