@@ -155,6 +155,8 @@ def main() -> int:
     ap.add_argument("--config", default="8b", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--trace", metavar="PATH", default="",
+                    help="run the traced kernels (per-op stamps) and write the last step as a Perfetto JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
@@ -165,6 +167,8 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
+    if args.trace:
+        os.environ["MK_TRACE"] = "1"  # read at context creation: selects the traced kernels
     import torch
     import synth
     import persistent_megakernel_decode_amd as mkd
@@ -281,6 +285,15 @@ def main() -> int:
     out["stream_read"] = {"gbs": round(stream_gbs, 1), "kernel": "torch.sum over 2 GiB fp32",
                           "achieved_frac": round(achieved / stream_gbs, 4),
                           "copy_gbs": round(copy_gbs, 1), "copy": "2 GiB device-to-device copy, read + write bytes"}
+    if args.trace:  # the last timed step, per op (the traced kernels were timed above)
+        from persistent_megakernel_decode_amd import trace as mktrace
+        tr = g.trace()
+        with open(args.trace, "w") as f:
+            json.dump(mktrace.chrome_trace(tr), f)
+        out["traced"] = {"path": args.trace, "per_op_kind_us": {
+            k: {kk: round(vv, 1) if isinstance(vv, float) else vv for kk, vv in v.items()}
+            for k, v in mktrace.op_summary(tr).items()}}
+        log(f"trace of the last step written to {args.trace}")
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample")
         g.close()

@@ -13,9 +13,9 @@ OPCODES = {1: "embed", 2: "gemv", 3: "attention", 4: "delta", 5: "mmv"}
 def unwrap(tr: dict) -> np.ndarray:
     """Stamps [n_ops, 3] (start, ready, end) in us relative to the earliest start."""
     t = tr["t"].astype(np.int64)
-    ref = int(t[:, 0].min())
-    d = (t - ref + (1 << 31)) % (1 << 32) - (1 << 31)
-    return d / 100.0
+    # differences to one stamp, taken modulo 2^32 (every stamp of a step lies within 21 s of it)
+    d = (t - int(t[0, 0]) + (1 << 31)) % (1 << 32) - (1 << 31)
+    return (d - d[:, 0].min()) / 100.0
 
 
 def stage_table(tr: dict) -> list:
@@ -47,3 +47,32 @@ def check(tr: dict) -> list:
             bad.append(f"cu {c}: an op starts before the previous one ends")
             break
     return bad
+
+
+def op_summary(tr: dict) -> dict:
+    """Stage time summed per op kind (embed / gemv / attention / delta / mmv) over the step, in us,
+    with the part of it the median op spent waiting for its inputs."""
+    out = {}
+    for r in stage_table(tr):
+        s = out.setdefault(r["op"], {"stages": 0, "us": 0.0, "waiting_us": 0.0, "tail_us": 0.0})
+        s["stages"] += 1
+        for k in ("us", "waiting_us", "tail_us"):
+            s[k] += r[k]
+    return out
+
+
+def chrome_trace(tr: dict) -> dict:
+    """The step as a Chrome / Perfetto trace (load the JSON in ui.perfetto.dev): one track per CU,
+    each op split into its input wait and its work."""
+    us = unwrap(tr)
+    ev = []
+    for i in range(len(us)):
+        name = f"{OPCODES.get(int(tr['opcode'][i]), '?')} s{int(tr['stage'][i])}"
+        cu = int(tr["cu"][i])
+        t0, t1, t2 = (float(x) for x in us[i])
+        if t1 > t0:
+            ev.append({"name": name + " wait", "ph": "X", "pid": 0, "tid": cu, "ts": t0, "dur": t1 - t0,
+                       "cat": "wait"})
+        ev.append({"name": name, "ph": "X", "pid": 0, "tid": cu, "ts": t1, "dur": max(t2 - t1, 0.0),
+                   "cat": "op", "args": {"queue_index": i}})
+    return {"traceEvents": ev, "displayTimeUnit": "ns"}
