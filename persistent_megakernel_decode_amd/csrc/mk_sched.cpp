@@ -294,7 +294,8 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
     // at least two chunks per (sequence, KV head) on average, so that chunks of one length
     // balance across CUs for ragged contexts
     int per_cu = (2 * Hkv * d.max_batch + n_cus - 1) / n_cus;
-    if (const char* e = getenv("MK_ATTN_ITEMS_PER_CU")) per_cu = std::max(per_cu, atoi(e));  // diagnostic
+    if (const char* e = getenv("MK_ATTN_ITEMS_PER_CU"))  // diagnostic: down to one chunk per (sequence, KV head)
+      per_cu = std::max((Hkv * d.max_batch + n_cus - 1) / n_cus, atoi(e));
     P.n_items = m.n_attn ? n_cus * per_cu : 0;
   }
   const int gmax = m.n_attn ? 512 / hd : 0;
