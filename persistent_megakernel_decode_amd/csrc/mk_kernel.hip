@@ -419,7 +419,11 @@ __device__ __forceinline__ void attn_plan_build(const KArgs& A, int pps) {
     int acc = 0;
 #pragma unroll
     for (int b = 0; b < APLAN_MAXB; ++b) {
-      const int cs = cv[b] > 0 ? cs_all : 0, nb = cs > 0 ? (cv[b] + cs - 1) / cs : 0;
+      // the sequence's chunk count at length cs_all, then its chunks evened out at that count
+      // (lengths a multiple of pps, at most cs_all; ceil(cv / cs) stays nb), so a ragged batch
+      // leaves no short last chunk per sequence
+      const int nb = cv[b] > 0 && cs_all > 0 ? (cv[b] + cs_all - 1) / cs_all : 0;
+      const int cs = nb > 0 ? ((cv[b] + nb - 1) / nb + pps - 1) / pps * pps : 0;
       g_aplan[1 + b] = cv[b];
       g_aplan[9 + b] = cs;
       g_aplan[17 + b] = acc;
