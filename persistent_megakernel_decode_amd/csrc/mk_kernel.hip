@@ -403,7 +403,9 @@ __device__ __forceinline__ void attn_plan_build(const KArgs& A, int pps) {
     int maxc = 0;
 #pragma unroll
     for (int b = 0; b < APLAN_MAXB; ++b) maxc = max(maxc, cv[b]);
-    int lo = ((total + K - 1) / K + pps - 1) / pps, hi = (maxc + pps - 1) / pps;
+    // and at least one ring slot per compute wave: shorter chunks leave waves idle and only add
+    // partials for the merger to fold
+    int lo = max(((total + K - 1) / K + pps - 1) / pps, (int)NC), hi = (maxc + pps - 1) / pps;
     if (lo > hi) lo = hi;
     while (lo < hi) {
       const int mid = (lo + hi) / 2, c = mid * pps;
