@@ -72,3 +72,14 @@ def test_host_rejects_out_of_contract_descriptions():
     with pytest.raises(mkd.MKError) as e:
         mkd.mk_plan(d, 256)
     assert e.value.status == mkd.MK_ERR_INVALID_ARG
+
+
+def test_trace_calls_reject_null_arguments():
+    """The trace entry points answer a null context or buffer with MK_ERR_INVALID_ARG before any
+    GPU call."""
+    L = mkd.lib()
+    n = ctypes.c_size_t(0)
+    assert L.mk_trace_words(None, ctypes.byref(n)) == mkd.MK_ERR_INVALID_ARG
+    assert L.mk_trace_words(None, None) == mkd.MK_ERR_INVALID_ARG
+    buf = (ctypes.c_uint32 * 8)()
+    assert L.mk_copy_trace(None, buf, 8) == mkd.MK_ERR_INVALID_ARG
