@@ -150,6 +150,42 @@ typedef struct {
 /* Run the scheduler and its checker on the host for n_cus compute units. */
 mk_status mk_plan(const mk_model_desc* desc, int32_t n_cus, mk_plan_info* info);
 
+/* ---- dependency-protocol emulator (host-only; no GPU needed) ----
+ * The abstract's megakernel replaces grid-wide synchronisation with dependencies between the
+ * compute units' instruction streams (ForgeMegakernel abstract, arxivdaily / arxiv.science); here
+ * a consumer polls its inputs for the launch's parity, which is sound only if every value it may
+ * poll is written exactly once per launch.  mk_emulate replays the queues mk_create would upload
+ * (the same scheduler, and the kernel's own attention planner) for n_cus compute units over
+ * n_launches launches, in a random interleaving drawn from `seed`, and reports what it found:
+ * polls satisfied by an earlier launch's value, reads after a counter wait that found unwritten
+ * data, values written twice or not at all in a launch, and launches in which every remaining
+ * unit waits (where the kernel's watchdog would end the step).  Positions are ctx_lens - 1.
+ * Returns MK_OK when the run completed (findings are in *rep; their text in mk_last_error()),
+ * MK_ERR_INVALID_ARG / MK_ERR_UNSUPPORTED for bad arguments or descriptions. */
+#define MK_EMU_COUNTERS 1u          /* every dependency through stage counters (the diagnostic plan) */
+#define MK_EMU_IDLE_ITEMS_SILENT 2u /* model a kernel whose attention items without a chunk write nothing */
+#define MK_EMU_DEAD_ROWS_SILENT 4u  /* model a kernel that writes no mixer rows for sequences outside the
+                                       step and polls only the rows of live sequences */
+#define MK_EMU_STALL_ONE_OP 8u      /* one op of the first launch never writes (a stuck producer) */
+typedef struct {
+  int32_t n_cus;            /* compute units to emulate (>= 1) */
+  int32_t n_launches;       /* launches in the sequence */
+  const int32_t* batch;     /* host [n_launches]: batch of each launch, in [1, max_batch] */
+  const int32_t* ctx_lens;  /* host [n_launches][max_batch]: context lengths; entries past batch ignored */
+  uint64_t seed;            /* interleaving seed */
+  uint32_t flags;           /* MK_EMU_* */
+} mk_emu_config;
+typedef struct {
+  int64_t ops_run, polls;   /* ops completed, polls satisfied */
+  int64_t stale_accepts;    /* polls that accepted a value written by an earlier launch */
+  int64_t unsynced_reads;   /* reads after a counter wait that found a value not written this launch */
+  int64_t double_writes;    /* tagged values written twice in one launch */
+  int64_t unwritten_cells;  /* pollable values not written in a launch */
+  int32_t deadlocks;        /* launches that stopped with every remaining unit waiting */
+  int32_t first_bad_launch; /* first launch with a finding, -1 if none */
+} mk_emu_report;
+mk_status mk_emulate(const mk_model_desc* desc, const mk_emu_config* cfg, mk_emu_report* rep);
+
 /* ---- mid-state access for checking against the oracle ---- */
 typedef enum {
   MK_MID_X_MIXER = 0, /* fp32 [batch][hidden] residual after layer l's attention / delta sub-layer */

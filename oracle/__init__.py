@@ -90,6 +90,8 @@ def lib():
         L.orc_conv_step.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, P]
         L.orc_delta_step.argtypes = [P, P, P, P, ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, P]
+        L.orc_delta_mixer.argtypes = [P, P, P, P, P, P, P]
+        L.orc_delta_mixer.restype = None
         L.orc_decode_step.argtypes = [P, P, P, P, P, P, ctypes.c_int, P, P]
         L.orc_decode_step.restype = ctypes.c_int
         L.orc_argmax.argtypes = [P, ctypes.c_int]
@@ -237,6 +239,18 @@ class DecodeOracle:
     def mix_dim(self) -> int:
         c = self.cfg
         return max(c.n_q_heads * c.head_dim, c.n_delta_heads * c.delta_dv)
+
+    def delta_mixer(self, layer: int, u, a, conv_state, delta_state):
+        """The delta-rule mixer of layer `layer` for one sequence, from given projections u [C] and gate
+        logits a [2 heads], conv state [C][W-1] and S^T [heads][dv][dk] (none modified).
+        Returns (o [heads*dv], new conv state, new S^T)."""
+        c = self.cfg
+        cs = _c(conv_state, np.float32).copy()
+        st = _c(delta_state, np.float32).copy()
+        o = np.empty(c.n_delta_heads * c.delta_dv, dtype=np.float32)
+        lib().orc_delta_mixer(ctypes.byref(self.m), self.w["layers"][layer]["conv_w"].ctypes.data,
+                              _ptr(_c(u, np.float32)), _ptr(_c(a, np.float32)), _ptr(cs), _ptr(st), _ptr(o))
+        return o, cs, st
 
     def step(self, tokens, positions, ctx_lens, dump: bool = False):
         """One decode step.  Returns logits [B, V] (and a dict of mid-states when dump)."""

@@ -200,17 +200,15 @@ static void attention_layer(const orc_model* m, const orc_layer* L, orc_cache* c
   free(kr); free(vr); free(q); free(k); free(v);
 }
 
-static void delta_layer(const orc_model* m, const orc_layer* L, orc_cache* c, int delta_layer_idx, int b,
-                        const float* r, float* o) {
+/* The delta-rule mixer of one sequence after its projections: conv step on u (rolling state cs),
+ * per-head L2 norm of q and k with q scaled by dk^-1/2, gates g = sigmoid(a_h), beta =
+ * sigmoid(a_{nh+h}), then the state update and readout of every head (st: S^T, [nh][dv][dk]). */
+void orc_delta_mixer(const orc_model* m, const uint16_t* conv_w, const float* u, const float* a, float* cs,
+                     float* st, float* o) {
   int nh = m->n_delta_heads, dk = m->delta_dk, dv = m->delta_dv, W = m->conv_width;
   int C = nh * (2 * dk + dv);
-  float* u = (float*)malloc(sizeof(float) * (size_t)C);
   float* y = (float*)malloc(sizeof(float) * (size_t)C);
-  float* a = (float*)malloc(sizeof(float) * (size_t)(2 * nh));
-  orc_matvec(L->w_qkv_delta, r, C, m->hidden, u);
-  orc_matvec(L->w_gates, r, 2 * nh, m->hidden, a);
-  float* cs = c->conv_state + ((size_t)delta_layer_idx * (size_t)c->max_batch + (size_t)b) * (size_t)C * (size_t)(W - 1);
-  orc_conv_step(u, L->conv_w, cs, C, W, y);
+  orc_conv_step(u, conv_w, cs, C, W, y);
   float* qh = (float*)malloc(sizeof(float) * (size_t)dk);
   float* kh = (float*)malloc(sizeof(float) * (size_t)dk);
   for (int h = 0; h < nh; ++h) {
@@ -222,11 +220,25 @@ static void delta_layer(const orc_model* m, const orc_layer* L, orc_cache* c, in
     double sq = 1.0 / sqrt(nq + 1e-6) / sqrt((double)dk), sk = 1.0 / sqrt(nk + 1e-6);
     for (int i = 0; i < dk; ++i) { qh[i] = (float)(yq[i] * sq); kh[i] = (float)(yk[i] * sk); }
     double g = orc_sigmoid(a[h]), beta = orc_sigmoid(a[nh + h]);
-    float* st = c->delta_state + (((size_t)delta_layer_idx * (size_t)c->max_batch + (size_t)b) * (size_t)nh + (size_t)h) *
-                                     (size_t)dv * (size_t)dk;
-    orc_delta_step(st, qh, kh, yv, g, beta, dk, dv, m->delta_decay_first, o + (size_t)h * dv);
+    orc_delta_step(st + (size_t)h * (size_t)dv * (size_t)dk, qh, kh, yv, g, beta, dk, dv, m->delta_decay_first,
+                   o + (size_t)h * dv);
   }
-  free(qh); free(kh); free(u); free(y); free(a);
+  free(qh); free(kh); free(y);
+}
+
+static void delta_layer(const orc_model* m, const orc_layer* L, orc_cache* c, int delta_layer_idx, int b,
+                        const float* r, float* o) {
+  int nh = m->n_delta_heads, dk = m->delta_dk, dv = m->delta_dv, W = m->conv_width;
+  int C = nh * (2 * dk + dv);
+  float* u = (float*)malloc(sizeof(float) * (size_t)C);
+  float* a = (float*)malloc(sizeof(float) * (size_t)(2 * nh));
+  orc_matvec(L->w_qkv_delta, r, C, m->hidden, u);
+  orc_matvec(L->w_gates, r, 2 * nh, m->hidden, a);
+  float* cs = c->conv_state + ((size_t)delta_layer_idx * (size_t)c->max_batch + (size_t)b) * (size_t)C * (size_t)(W - 1);
+  float* st = c->delta_state + ((size_t)delta_layer_idx * (size_t)c->max_batch + (size_t)b) * (size_t)nh *
+                                   (size_t)dv * (size_t)dk;
+  orc_delta_mixer(m, L->conv_w, u, a, cs, st, o);
+  free(u); free(a);
 }
 
 int orc_decode_step(const orc_model* m, const orc_weights* w, orc_cache* c, const int32_t* tokens,

@@ -88,6 +88,13 @@ void orc_conv_step(const float* u, const uint16_t* conv_w, float* state, int C, 
 void orc_delta_step(float* st, const float* q, const float* k, const float* v, double g, double beta,
                     int dk, int dv, int decay_first, float* o);
 
+/* the delta-rule mixer of one sequence from its projections u[C] (q | k | v) and gate logits a[2*heads]:
+ * conv step (cs = that sequence's conv state [C][W-1], updated), per-head L2 norm of q and k (q also
+ * scaled by dk^-1/2), g = sigmoid(a[h]), beta = sigmoid(a[heads+h]), state update and readout of every
+ * head (st = that sequence's S^T [heads][dv][dk], updated); o[heads*dv]. */
+void orc_delta_mixer(const orc_model* m, const uint16_t* conv_w, const float* u, const float* a, float* cs,
+                     float* st, float* o);
+
 /* ---- the decode step ----
  * For every b < batch: consume tokens[b] at position positions[b] (== ctx_lens[b]-1), append K/V
  * (or update the conv / delta states), write logits[b][vocab].  Returns 0 or a negative code for

@@ -61,8 +61,21 @@ class mk_plan_info(ctypes.Structure):
                 ("mean_cu_bytes", ctypes.c_double), ("errors", I32)]
 
 
+class mk_emu_config(ctypes.Structure):
+    _fields_ = [("n_cus", I32), ("n_launches", I32), ("batch", P), ("ctx_lens", P), ("seed", ctypes.c_uint64),
+                ("flags", ctypes.c_uint32)]
+
+
+class mk_emu_report(ctypes.Structure):
+    _fields_ = [("ops_run", ctypes.c_int64), ("polls", ctypes.c_int64), ("stale_accepts", ctypes.c_int64),
+                ("unsynced_reads", ctypes.c_int64), ("double_writes", ctypes.c_int64),
+                ("unwritten_cells", ctypes.c_int64), ("deadlocks", I32), ("first_bad_launch", I32)]
+
+
+MK_EMU_COUNTERS, MK_EMU_IDLE_ITEMS_SILENT, MK_EMU_DEAD_ROWS_SILENT, MK_EMU_STALL_ONE_OP = 1, 2, 4, 8
+
 EXPORTED = ["mk_workspace_size", "mk_create", "mk_decode_step", "mk_sync_status", "mk_reset", "mk_last_error",
-            "mk_destroy", "mk_plan", "mk_copy_midstate", "mk_trace_words", "mk_copy_trace"]
+            "mk_destroy", "mk_plan", "mk_emulate", "mk_copy_midstate", "mk_trace_words", "mk_copy_trace"]
 
 _lib = None
 
@@ -86,11 +99,13 @@ def lib() -> ctypes.CDLL:
         L.mk_destroy.argtypes = [P]
         L.mk_destroy.restype = None
         L.mk_plan.argtypes = [ctypes.POINTER(mk_model_desc), I32, ctypes.POINTER(mk_plan_info)]
+        L.mk_emulate.argtypes = [ctypes.POINTER(mk_model_desc), ctypes.POINTER(mk_emu_config),
+                                 ctypes.POINTER(mk_emu_report)]
         L.mk_copy_midstate.argtypes = [P, I32, I32, P, ctypes.c_size_t, P]
         L.mk_trace_words.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         L.mk_copy_trace.argtypes = [P, P, ctypes.c_size_t]
         for f in ("mk_workspace_size", "mk_create", "mk_decode_step", "mk_sync_status", "mk_reset", "mk_plan",
-                  "mk_copy_midstate", "mk_trace_words", "mk_copy_trace"):
+                  "mk_emulate", "mk_copy_midstate", "mk_trace_words", "mk_copy_trace"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -130,6 +145,23 @@ def mk_plan(desc: mk_model_desc, n_cus: int) -> mk_plan_info:
     info = mk_plan_info()
     check(lib().mk_plan(ctypes.byref(desc), n_cus, ctypes.byref(info)), "mk_plan")
     return info
+
+
+def mk_emulate(desc: mk_model_desc, n_cus: int, batches: Sequence[int], ctx_lens: Sequence[Sequence[int]],
+               seed: int = 0, flags: int = 0):
+    """Replay the compiled queues over a launch sequence on the CPU (no GPU).  ctx_lens[i] lists the
+    context lengths of launch i (at least batches[i] entries).  Returns (report, findings text)."""
+    import numpy as np
+    n = len(batches)
+    mb = desc.max_batch
+    bt = np.ascontiguousarray(batches, dtype=np.int32)
+    cl = np.zeros((max(n, 1), mb), dtype=np.int32)
+    for i, row in enumerate(ctx_lens):
+        cl[i, :min(len(row), mb)] = list(row)[:mb]
+    cfg = mk_emu_config(n_cus, n, bt.ctypes.data, cl.ctypes.data, seed, flags)
+    rep = mk_emu_report()
+    check(lib().mk_emulate(ctypes.byref(desc), ctypes.byref(cfg), ctypes.byref(rep)), "mk_emulate")
+    return rep, mk_last_error()
 
 
 def mk_create(desc, weights: mk_weights, cache: mk_kv_cache, workspace_ptr: int, workspace_bytes: int) -> int:

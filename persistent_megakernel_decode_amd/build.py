@@ -8,8 +8,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmk.so")
-SOURCES = ["mk_kernel.hip", "mk_kernel_trace.hip", "mk_api.cpp", "mk_sched.cpp"]
-HEADERS = ["mk_internal.h", "mk_sched.h", os.path.join("..", "..", "include", "mk.h")]
+SOURCES = ["mk_kernel.hip", "mk_kernel_trace.hip", "mk_api.cpp", "mk_sched.cpp", "mk_emu.cpp"]
+HEADERS = ["mk_internal.h", "mk_attn_plan.h", "mk_sched.h", os.path.join("..", "..", "include", "mk.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -75,11 +75,8 @@ struct mk_ctx {
   mk_status sticky = MK_OK;
   const void* kernel = nullptr;
   bool plain_launch = false;
-  uint32_t* trace = nullptr;  // MK_TRACE=1: device buffer, 4 words per op (library-owned)
+  uint32_t* trace = nullptr;  // MK_TRACE=1: the workspace's trace section, 4 words per op
   std::mutex busy;
-  ~mk_ctx() {
-    if (trace) (void)hipFree(trace);
-  }
 };
 
 extern "C" {
@@ -131,6 +128,22 @@ mk_status mk_plan(const mk_model_desc* desc, int32_t n_cus, mk_plan_info* info) 
   info->max_cu_bytes = mx;
   info->mean_cu_bytes = sum / n_cus;
   if (info->errors) g_last_error = why;
+  return MK_OK;
+}
+
+mk_status mk_emulate(const mk_model_desc* desc, const mk_emu_config* cfg, mk_emu_report* rep) {
+  if (!cfg || !rep) return fail(MK_ERR_INVALID_ARG, "cfg and rep must be non-null");
+  mk::ModelShape m;
+  mk_status st;
+  std::string e = mk::validate_desc(desc, &m, &st);
+  if (!e.empty()) return fail(st, e);
+  if (cfg->n_cus < 1 || cfg->n_launches < 0) return fail(MK_ERR_INVALID_ARG, "n_cus must be positive, n_launches >= 0");
+  if (cfg->n_launches > 0 && (!cfg->batch || !cfg->ctx_lens)) return fail(MK_ERR_INVALID_ARG, "batch and ctx_lens must be non-null");
+  for (int i = 0; i < cfg->n_launches; ++i)
+    if (cfg->batch[i] < 1 || cfg->batch[i] > m.d.max_batch)
+      return fail(MK_ERR_INVALID_ARG, "launch " + std::to_string(i) + ": batch outside [1, max_batch]");
+  std::string found = mk::emulate(m, *cfg, rep);
+  g_last_error = found;
   return MK_OK;
 }
 
@@ -264,7 +277,7 @@ mk_status mk_create(const mk_model_desc* desc, const mk_weights* w, const mk_kv_
   A.x0 = (float*)(ctx->ws + Y.x0);
   A.embed = (const uint16_t*)w->embed;
   A.page_table = m.n_attn ? c->page_table : nullptr;
-  A.H = d.hidden; A.V = d.vocab; A.Hq = d.n_q_heads; A.Hkv = d.n_kv_heads; A.d = d.head_dim; A.G = m.G;
+  A.n_layers = d.n_layers; A.H = d.hidden; A.V = d.vocab; A.Hq = d.n_q_heads; A.Hkv = d.n_kv_heads; A.d = d.head_dim; A.G = m.G;
   A.qk_norm = d.qk_norm; A.max_batch = d.max_batch; A.max_ctx = d.max_ctx; A.page_size = d.page_size;
   A.num_pages = m.n_attn ? c->num_pages : 0;
   A.max_pages_per_seq = m.n_attn ? c->max_pages_per_seq : 1;
@@ -272,24 +285,17 @@ mk_status mk_create(const mk_model_desc* desc, const mk_weights* w, const mk_kv_
   A.n_cus = ncu; A.n_items = P.n_items; A.mix = P.mix_dim;
   A.rms_eps = d.rms_eps;
   double ms = 2000.0;
-  if (const char* s = getenv("MK_WATCHDOG_MS")) ms = std::max(1.0, atof(s));  // diagnostic only
+  // diagnostic only; the tests set a tiny limit to force the timeout path from the host
+  if (const char* s = getenv("MK_WATCHDOG_MS")) ms = std::max(0.001, atof(s));
   A.spin_limit = (uint64_t)(ms * 1e5);  // s_memrealtime runs at 100 MHz
+  A.spin_check_mask = ms < 0.01 ? 0u : 63u;
   // Diagnostic: MK_PLAIN_LAUNCH=1 launches with hipLaunchKernel instead of the cooperative launch
   // (for tools that cannot follow cooperative dispatches).  mk_create has already checked that one
   // workgroup per CU is resident; should some workgroup still not be scheduled, the spin-wait
   // watchdog ends every wait and the step reports MK_ERR_TIMEOUT.
   if (const char* s = getenv("MK_PLAIN_LAUNCH")) ctx->plain_launch = atoi(s) != 0;
-  A.trace = nullptr;
-  if (traced) {
-    const size_t bytes = P.ops.size() * 4 * sizeof(uint32_t);
-    he = hipMalloc((void**)&ctx->trace, bytes);
-    if (he == hipSuccess) he = hipMemset(ctx->trace, 0, bytes);
-    if (he != hipSuccess) {
-      delete ctx;
-      return hip_fail(he, "allocating the trace buffer");
-    }
-    A.trace = ctx->trace;
-  }
+  ctx->trace = traced ? (uint32_t*)(ctx->ws + Y.trace) : nullptr;  // zeroed with the workspace
+  A.trace = ctx->trace;
   *out = ctx;
   return MK_OK;
 }

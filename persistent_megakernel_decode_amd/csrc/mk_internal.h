@@ -45,18 +45,15 @@ enum Opcode : uint8_t { OP_NOP = 0, OP_EMBED = 1, OP_GEMV = 2, OP_ATTN = 3, OP_D
 enum Epi : uint8_t { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
 
 constexpr int16_t NO_STAGE = -1;
+constexpr uint32_t LAYER_ATTN = 0, LAYER_DELTA = 1;  // the values of mk_layer_kind
 
-// Op flags.  Activations written by EMBED and by the projections carry the launch's parity in
-// the lowest mantissa bit of every fp32 value (row_ok carries the launch tag itself), so an op
-// whose inputs all come from such writers can poll the inputs themselves instead of a stage
-// counter (OPF_TAGGED_IN).  A stage that no op waits on by counter skips its signal and the
+// Op flags.  Every activation that crosses compute units carries the launch's parity in the
+// lowest mantissa bit of each fp32 value (row_ok carries the launch tag itself), and every such
+// value is written exactly once per launch, so an op can poll its inputs themselves instead of a
+// stage counter (OPF_TAGGED_IN).  A stage that no op waits on by counter skips its signal and the
 // store-completion wait before it (OPF_NO_SIGNAL).
 constexpr uint32_t OPF_TAGGED_IN = 1u;
 constexpr uint32_t OPF_NO_SIGNAL = 2u;
-// With OPF_TAGGED_IN: only rows of live sequences (b < batch, context in range) are polled --
-// attention writes no others and the delta rule writes only b < max_batch; the rest are never
-// consumed.
-constexpr uint32_t OPF_LIVE_ROWS = 4u;
 
 // One queue entry (128 bytes).  Pointers are device addresses.
 //
@@ -121,6 +118,8 @@ struct alignas(16) LayerDesc {
   uint64_t conv_w;       // delta: bf16 [C][W]
   uint64_t conv_state;   // delta: fp32 [B][C][W-1]
   uint64_t delta_state;  // delta: fp32 [B][heads][dv][dk]
+  uint32_t kind;         // LAYER_ATTN or LAYER_DELTA
+  uint32_t mix_width;    // floats of mix_o one row holds for this layer (Hq d, or heads dv)
 };
 
 struct Stage {
@@ -137,13 +136,13 @@ struct KArgs {
   uint32_t* counters;         // [n_stages][NSUB * CTR_STRIDE]
   const LayerDesc* layers;
   const float* rope;          // [max_ctx][d/2][2] (cos, sin)
-  uint32_t* status;           // [0] sticky error bits, [1] timeout flag
+  uint32_t* status;           // [0] sticky error bits, [1] tag of the first launch that raised any
   int32_t* row_ok;            // [max_batch]
   float* x0;                  // embedding output fp32 [max_batch][H]
   const uint16_t* embed;
   const int32_t* page_table;
   // model
-  int32_t H, V, Hq, Hkv, d, G, qk_norm, max_batch, max_ctx, page_size, num_pages, max_pages_per_seq;
+  int32_t n_layers, H, V, Hq, Hkv, d, G, qk_norm, max_batch, max_ctx, page_size, num_pages, max_pages_per_seq;
   int32_t nh, dk, dv, C, convw;
   int32_t n_cus, n_items;     // attention work items per attention layer
   int32_t mix;                // floats between batch rows of the attention / delta output
@@ -157,6 +156,7 @@ struct KArgs {
   uint32_t epoch;
   uint32_t tag;               // launch tag: bit 0 is the activation parity, row_ok holds tag << 1 | ok
   uint64_t spin_limit;        // watchdog, in s_memrealtime ticks (100 MHz)
+  uint32_t spin_check_mask;   // the watchdog reads the clock once every (mask + 1) polls
   uint32_t* trace;            // MK_TRACE=1: per op {opcode << 16 | stage, start, inputs ready, end}; else null
 };
 

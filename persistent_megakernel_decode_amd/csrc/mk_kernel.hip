@@ -25,6 +25,7 @@
 // No buffer_wbl2 / buffer_inv is issued anywhere on the path.
 #include <hip/hip_runtime.h>
 
+#include "mk_attn_plan.h"
 #include "mk_internal.h"
 
 namespace mk {
@@ -264,27 +265,45 @@ __device__ __forceinline__ u32 lds_ld_loader(const u32* p) {
 __device__ __forceinline__ bool aborted_loader() { return lds_ld_loader(&g_abort) != 0; }
 
 
-__device__ void raise_status(const KArgs& A, u32 bits) {
-  __hip_atomic_fetch_or(A.status, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Sticky status: status[0] holds the error bits, status[1] the tag of the first launch that raised
+// any.  The first raise stores both in one 64-bit compare-and-swap, so a reader sees either no
+// error or a complete (tag, bits) pair; later raises only add bits.
+__device__ __noinline__ void raise_status_at(u32* status, u32 tag, u32 bits) {
+  uint64_t expect = 0;
+  const uint64_t want = ((uint64_t)tag << 32) | bits;
+  if (!__hip_atomic_compare_exchange_strong(gptr((uint64_t*)status), &expect, want, __ATOMIC_RELAXED,
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+    __hip_atomic_fetch_or(gptr(status), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ void raise_status(const KArgs& A, u32 bits) { raise_status_at(A.status, A.tag, bits); }
+// A step queued behind one that raised an error (a timeout leaves tags and counters half-written)
+// does nothing: every workgroup reads the status at entry and leaves when an earlier launch raised.
+// Errors of this launch carry its own tag and do not stop it.
+__device__ __forceinline__ bool earlier_launch_failed(const KArgs& A) {
+  const uint64_t v = __hip_atomic_load(gptr((const uint64_t*)A.status), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v != 0 && (u32)(v >> 32) != A.tag;
 }
 
 // Every spin in the kernel is bounded: past the watchdog limit the waiting wave raises
 // ST_TIMEOUT and sets the workgroup abort flag, and every wave of the workgroup leaves.
-// The clock is read only once a wait has actually spun, and then every 64 polls: the fast path
+// The clock is read only once a wait has actually spun, and then every 64 polls (every poll under
+// a limit below 10 us, which only the tests that force the timeout path set): the fast path
 // (condition already true) costs nothing.
 struct Watchdog {
   uint64_t t0, limit;
   u32* status;
-  u32 polls;
-  __device__ explicit Watchdog(const KArgs& A) : t0(0), limit(A.spin_limit), status(A.status), polls(0) {}
+  u32 tag;
+  u32 polls, mask;
+  __device__ explicit Watchdog(const KArgs& A)
+      : t0(0), limit(A.spin_limit), status(A.status), tag(A.tag), polls(0), mask(A.spin_check_mask) {}
   __device__ bool expired() {
-    if ((polls++ & 63u) != 0) return false;
+    if ((polls++ & mask) != 0) return false;
     const uint64_t now = __builtin_amdgcn_s_memrealtime();
     if (t0 == 0) { t0 = now; return false; }
     if (now - t0 <= limit) return false;
     // every lane raises the (idempotent) flags: a lane-0 branch here gets merged into the
     // caller's loop exit by the compiler, which turns every spin loop divergent
-    __hip_atomic_fetch_or(status, ST_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    raise_status_at(status, tag, ST_TIMEOUT);
     __hip_atomic_store(&g_abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     return true;
   }
@@ -371,91 +390,35 @@ __device__ bool row_ok_local(const KArgs& A, int b) {
 }
 
 // ------------------------------------------------------------------ attention work split
-struct AttnItem {
-  int b, kvh, p0, p1, n_b, first_item;  // first_item: item index of chunk 0 of (b, kvh)
-  bool valid;
-};
+// The launch's attention split (mk_attn_plan.h), built once per launch by the loader wave before it
+// streams anything and read from LDS by every wave: [0] ready flag, then the APLAN_WORDS plan words.
+__shared__ int g_aplan[1 + APLAN_WORDS];
 
-__device__ __forceinline__ int clamp_ctx(const KArgs& A, int c) { return (c >= 1 && c <= A.max_ctx) ? c : 0; }
-
-// The launch's attention split, built once per launch by the loader wave before it streams
-// anything and read from LDS by every wave.  Each KV head gets at most n_items / Hkv chunks, all
-// of one length (a multiple of the positions one ring slot holds; a sequence's last chunk may be
-// shorter).  Layout: [0] ready flag, [1 + b] context length of sequence b,
-// [9 + b] its chunk length, [17 + b] chunks of the sequences before b (b = 8: all chunks).
-constexpr int APLAN_MAXB = 8;
-__shared__ int g_aplan[1 + 3 * APLAN_MAXB + 1];
+__device__ __forceinline__ int clamp_ctx(const KArgs& A, int c) { return attn_clamp_ctx(c, A.max_ctx); }
 
 __device__ __forceinline__ void attn_plan_build(const KArgs& A, int pps) {
   int cv[APLAN_MAXB];
-  int total = 0, nz = 0;
 #pragma unroll
-  for (int b = 0; b < APLAN_MAXB; ++b) {
-    cv[b] = b < A.batch ? clamp_ctx(A, sload(A.ctx_lens + b)) : 0;
-    total += cv[b];
-    nz += cv[b] > 0 ? 1 : 0;
-  }
+  for (int b = 0; b < APLAN_MAXB; ++b) cv[b] = b < A.batch ? clamp_ctx(A, sload(A.ctx_lens + b)) : 0;
   const int K = A.Hkv > 0 ? A.n_items / A.Hkv : 0;  // chunks per KV head; >= batch by construction
-  // one chunk length for the launch: the smallest multiple of pps that needs at most K chunks
-  // per KV head (binary search; one chunk per sequence always fits since K >= batch)
-  int cs_all = 0;
-  if (total > 0 && K >= nz) {
-    int maxc = 0;
-#pragma unroll
-    for (int b = 0; b < APLAN_MAXB; ++b) maxc = max(maxc, cv[b]);
-    // and at least one ring slot per compute wave: shorter chunks leave waves idle and only add
-    // partials for the merger to fold
-    int lo = max(((total + K - 1) / K + pps - 1) / pps, (int)NC), hi = (maxc + pps - 1) / pps;
-    if (lo > hi) lo = hi;
-    while (lo < hi) {
-      const int mid = (lo + hi) / 2, c = mid * pps;
-      int n = 0;
-#pragma unroll
-      for (int b = 0; b < APLAN_MAXB; ++b) n += (cv[b] + c - 1) / c;
-      if (n <= K) hi = mid;
-      else lo = mid + 1;
-    }
-    cs_all = lo * pps;
-  }
+  int plan[APLAN_WORDS];
+  attn_plan_make(cv, K, pps, NC, plan);
   if (lane_id() == 0) {
-    int acc = 0;
 #pragma unroll
-    for (int b = 0; b < APLAN_MAXB; ++b) {
-      // the sequence's chunk count at length cs_all, then its chunks evened out at that count
-      // (lengths a multiple of pps, at most cs_all; ceil(cv / cs) stays nb), so a ragged batch
-      // leaves no short last chunk per sequence
-      const int nb = cv[b] > 0 && cs_all > 0 ? (cv[b] + cs_all - 1) / cs_all : 0;
-      const int cs = nb > 0 ? ((cv[b] + nb - 1) / nb + pps - 1) / pps * pps : 0;
-      g_aplan[1 + b] = cv[b];
-      g_aplan[9 + b] = cs;
-      g_aplan[17 + b] = acc;
-      acc += nb;
-    }
-    g_aplan[17 + APLAN_MAXB] = acc;
+    for (int i = 0; i < APLAN_WORDS; ++i) g_aplan[1 + i] = plan[i];
     __hip_atomic_store(&g_aplan[0], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }
 
 // Item i -> (sequence, KV head, position range), from the launch plan in LDS.  Uniform.
 __device__ AttnItem attn_item(const KArgs& A, u32 item, int pps) {
-  AttnItem it{0, 0, 0, 0, 0, 0, false};
   (void)pps;
   Watchdog wd(A);
   while (lds_ld((const u32*)&g_aplan[0]) == 0) {
-    if (aborted() || wd.expired()) return it;
+    if (aborted() || wd.expired()) return AttnItem{0, 0, 0, 0, 0, 0, false};
     __builtin_amdgcn_s_sleep(1);
   }
-  const int bc = (int)(item / (u32)A.Hkv), kvh = (int)(item % (u32)A.Hkv);
-  for (int b = 0; b < A.batch && b < APLAN_MAXB; ++b) {
-    const int c0 = (int)lds_ld((const u32*)&g_aplan[17 + b]), c1 = (int)lds_ld((const u32*)&g_aplan[18 + b]);
-    if (bc < c1) {
-      const int k = bc - c0, c = (int)lds_ld((const u32*)&g_aplan[1 + b]), cs = (int)lds_ld((const u32*)&g_aplan[9 + b]);
-      it.b = b; it.kvh = kvh; it.p0 = k * cs; it.p1 = min(c, (k + 1) * cs);
-      it.n_b = c1 - c0; it.first_item = c0 * A.Hkv + kvh; it.valid = true;
-      return it;
-    }
-  }
-  return it;
+  return attn_item_from([](int i) { return (int)lds_ld((const u32*)&g_aplan[1 + i]); }, A.batch, A.Hkv, item);
 }
 // attn_item with a one-entry cache keyed by the item index
 struct ItemCache {
@@ -477,7 +440,6 @@ struct ItemCache {
   }
 };
 
-__device__ __forceinline__ int attn_pps(int d) { return 4096 / (2 * d); }  // positions per ring slot
 
 // ------------------------------------------------------------------ loader
 
@@ -851,6 +813,24 @@ __device__ __forceinline__ void op_embed(const KArgs& A, u32 w) {
     for (int h = h0 + (int)t; h < h1; h += NC * 64)
       st_tag(A.x0 + (size_t)b * A.H + h, ok ? bf2f(A.embed[(size_t)tok * A.H + h]) : 0.0f, par);
   }
+  // Rows of the attention / delta output that no mixer op writes this launch -- sequences that do
+  // not take part in an attention layer (past the batch, or a context out of range) and rows past
+  // max_batch of a delta layer -- get tagged zeros here, this CU's slice of each, so that every
+  // tagged value is written exactly once per launch and o_proj can poll every row.
+  bool live[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) live[b] = b < A.batch && clamp_ctx(A, A.ctx_lens[b]) > 0;
+  for (int l = 0; l < A.n_layers; ++l) {
+    const LayerDesc Ld = sload(A.layers + l);
+    const int wdt = (int)Ld.mix_width;
+    const int c0 = (int)((int64_t)wdt * cu / A.n_cus), c1 = (int)((int64_t)wdt * (cu + 1) / A.n_cus);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const bool written = Ld.kind == LAYER_ATTN ? live[b] : b < A.max_batch;
+      if (written) continue;
+      for (int c = c0 + (int)t; c < c1; c += NC * 64) st_tag((float*)Ld.mix_o + (size_t)b * A.mix + c, 0.0f, par);
+    }
+  }
 }
 
 // Second phase of EMBED, CU 0 only: validate every row (token, context, position, every page of
@@ -1088,10 +1068,6 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
           : epi == EPI_LOGITS ? __builtin_bit_cast(float, ld_i32_sc1(A.row_ok + b)) : 0.0f;  // row_ok for logits
   if (flags & OPF_TAGGED_IN) {
     // poll the inputs themselves: re-read every fragment that does not yet show this launch's parity
-    if (flags & OPF_LIVE_ROWS) {  // rows of sequences not live this launch may be unwritten: skip them
-      const int bb = B == 1 ? 0 : (int)min(bl, (u32)B - 1);
-      if (!(bb < A.batch && clamp_ctx(A, A.ctx_lens[bb]) > 0)) fv = 0;
-    }
     u32 todo = 0;
 #pragma unroll
     for (int f = 0; f < NF; ++f) todo |= ((fv >> f) & 1u) && !tags_ok<8>(xf[f], par) ? 1u << f : 0u;
@@ -1320,11 +1296,9 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
     }
     gv = (norm && ks < nks) ? *(const u32x4*)(gm + k0) : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   };
-  // tagged inputs: wait until this lane's block of segment ks shows this launch's parity (lanes of
-  // sequences that are not live are not checked with OPF_LIVE_ROWS)
+  // tagged inputs: wait until this lane's block of segment ks shows this launch's parity
   const u32 par = A.tag & 1u;
-  const bool tcheck = (flags & OPF_TAGGED_IN) && cval &&
-                      (!(flags & OPF_LIVE_ROWS) || ((int)col < A.batch && clamp_ctx(A, A.ctx_lens[col]) > 0));
+  const bool tcheck = (flags & OPF_TAGGED_IN) && cval;
   auto ready = [&](u32 ks, float* xv) -> bool {
     const bool need = tcheck && ks < nks;
     Watchdog wd(A);
@@ -1460,11 +1434,18 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   static_assert(PA + NC * PPS * GMAX <= RED_FLOATS, "attention LDS areas");
   const u32 lane = lane_id();
   const AttnItem it = ic.get(A, o.row0, PPS);
-  if (!it.valid) return true;
+  const LayerDesc Ld = sload(A.layers + o.layer);
+  if (!it.valid) {
+    // An item with no chunk this launch still writes its partial slot (tagged zeros), so that every
+    // tagged value is written exactly once per launch: a later launch whose plan gives this item a
+    // chunk then finds the previous launch's parity here until the real partial lands.
+    float* part = (float*)Ld.part + (size_t)o.row0 * GMAX * (D + 4);
+    for (int t = (int)(w * 64 + lane); t < A.G * (D + 4); t += NC * 64) st_tag(part + t, 0.0f, A.tag & 1u);
+    return true;
+  }
   const u32 ns = (u32)((it.p1 - it.p0 + PPS - 1) / PPS);
   const u32 seq0 = seq;
   seq += ns;
-  const LayerDesc Ld = sload(A.layers + o.layer);
   const int G = A.G, b = it.b, kvh = it.kvh;
   const int pos = A.positions[b];
   const int32_t rok = ld_i32_sc1(A.row_ok + b);  // checked where it is used
@@ -1715,7 +1696,7 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   // polling their tagged partials.  Items go to CUs round-robin in item order, so every chunk it
   // waits for sits at the same or an earlier position in its CU's queue: by induction on the item
   // index every item completes, and no two mergers can wait on each other.
-  if (o.row0 != (u32)(it.first_item + (it.n_b - 1) * A.Hkv)) return true;
+  if (!attn_is_merger(it, A.Hkv, o.row0)) return true;
   if (!cbar(A, gen)) return false;  // every thread is done with the wave partials in LDS
   {
     // Thread t owns output quad t % NQ (head g, 4 dims) of chunks t / NQ, t / NQ + NG, ...: it
@@ -1988,6 +1969,7 @@ __device__ __forceinline__ void megakernel_body(const KArgs& A) {
   if (threadIdx.x == 0) { g_filled = 0; g_aplan[0] = 0; }
   if (threadIdx.x == 0) { g_bar = 0; g_abort = 0; }
   __syncthreads();
+  if (earlier_launch_failed(A)) return;  // uniform: the same word for every wave of the grid
   const u32 q0 = A.queue_off[blockIdx.x], q1 = A.queue_off[blockIdx.x + 1];
   if (wv == 0) loader(A, q0, q1);
   else compute<B>(q0, q1, wv - 1);

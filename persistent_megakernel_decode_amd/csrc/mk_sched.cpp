@@ -274,7 +274,8 @@ struct Builder {
 };
 }  // namespace
 
-std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, const mk_kv_cache* c, Plan* plan) {
+std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, const mk_kv_cache* c, Plan* plan,
+                       int dep_mode) {
   const mk_model_desc& d = m.d;
   Plan& P = *plan;
   P = Plan{};
@@ -355,6 +356,8 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
         D.k_pages = wptr(c->k_pages) + per_layer * ia;
         D.v_pages = wptr(c->v_pages) + per_layer * ia;
       }
+      D.kind = LAYER_ATTN;
+      D.mix_width = (uint32_t)(Hq * hd);
       const int s_qkv = bd.new_stage();
       bd.gemv(s_qkv, prev, l, (uint32_t)qkv_w, (uint32_t)H, EPI_STORE, true, lw ? wptr(lw->wq) : 0,
               lw ? wptr(lw->wk) : 0, lw ? wptr(lw->wv) : 0, (uint32_t)(Hq * hd), (uint32_t)((Hq + Hkv) * hd), x_in,
@@ -366,6 +369,8 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
               (uint32_t)NONE, (uint32_t)NONE, ws(Q.mix_o), (uint32_t)P.mix_dim, 0, ws(Q.x_mix), (uint32_t)H, x_in);
       ++ia;
     } else {
+      D.kind = LAYER_DELTA;
+      D.mix_width = (uint32_t)(nh * dv);
       D.gates = ws(Q.qkv) + (uint64_t)m.C * 4;
       if (lw) D.conv_w = wptr(lw->conv_w);
       if (c) {
@@ -424,18 +429,17 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
   // delta rule (tagged activations) polls its inputs; a stage is signalled only if some op waits
   // on its counter (MK_STAGE_COUNTERS=1 keeps the counters everywhere: diagnostic).
   {
-    bool tags = true;
-    if (const char* e = getenv("MK_STAGE_COUNTERS")) tags = atoi(e) == 0;
+    bool tags = dep_mode != 1;
+    if (dep_mode < 0)
+      if (const char* e = getenv("MK_STAGE_COUNTERS")) tags = atoi(e) == 0;
     std::vector<uint8_t> counted(S, 0);
     for (auto& qc : q)
       for (Op& o : qc) {
         if (o.wait_stage == NO_STAGE) continue;
         const uint8_t pop = bd.stage_ops[o.wait_stage][0].opcode;
-        const bool mixer = pop == OP_ATTN || pop == OP_DELTA;  // rows written only for live sequences
-        const bool tagged_src = pop == OP_EMBED || pop == OP_GEMV || pop == OP_MMV || mixer;
-        const bool proj = o.opcode == OP_GEMV || o.opcode == OP_MMV;
-        const bool tagged_dst = mixer ? proj : proj || o.opcode == OP_ATTN || o.opcode == OP_DELTA;
-        if (tags && tagged_src && tagged_dst) o.flags |= OPF_TAGGED_IN | (mixer ? OPF_LIVE_ROWS : 0u);
+        const bool tagged_src = pop == OP_EMBED || pop == OP_GEMV || pop == OP_MMV || pop == OP_ATTN || pop == OP_DELTA;
+        const bool tagged_dst = o.opcode == OP_GEMV || o.opcode == OP_MMV || o.opcode == OP_ATTN || o.opcode == OP_DELTA;
+        if (tags && tagged_src && tagged_dst) o.flags |= OPF_TAGGED_IN;
         else counted[o.wait_stage] = 1;
       }
     for (auto& qc : q)
@@ -453,6 +457,9 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
   Y.counters_bytes = (size_t)S * NSUB * CTR_STRIDE * 4;
   Y.counters = take(Y.counters_bytes);
   Y.layers = take((size_t)L * sizeof(LayerDesc));
+  // per-op timing stamps of the traced kernels (MK_TRACE=1), 4 words per op; kept in every
+  // workspace so that tracing never needs memory of its own
+  Y.trace = take(P.ops.size() * 4 * sizeof(uint32_t));
   Y.total = off;
   return "";
 }

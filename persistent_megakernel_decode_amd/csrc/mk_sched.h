@@ -15,6 +15,7 @@ namespace mk {
 // Byte offsets of every workspace section (all 256-byte aligned).
 struct Layout {
   size_t ops = 0, queue_off = 0, stages = 0, counters = 0, layers = 0, rope = 0, status = 0, row_ok = 0, x0 = 0;
+  size_t trace = 0;  // per-op timing stamps (traced kernels only)
   struct PerLayer {
     size_t qkv = 0, part = 0, tickets = 0, mix_o = 0, x_mix = 0, m = 0, x_out = 0;
   };
@@ -51,7 +52,10 @@ std::string validate_desc(const mk_model_desc* desc, ModelShape* out, mk_status*
 // Builds the plan with device pointers expressed relative to:
 //   workspace base (bit 62 tag) -- relocated by relocate(); weights / cache pointers are taken
 //   verbatim from `w` / `c` when given (NULL = leave zero, for host-only planning).
-std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, const mk_kv_cache* c, Plan* plan);
+// dep_mode: 0 = tagged activations wherever possible (the default plan), 1 = every dependency
+// through the stage counters (diagnostic), -1 = from the MK_STAGE_COUNTERS environment variable.
+std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, const mk_kv_cache* c, Plan* plan,
+                       int dep_mode = -1);
 
 // Rewrites workspace-relative addresses in the plan into absolute device addresses.
 void relocate(Plan* plan, uint64_t workspace_base);
@@ -59,5 +63,9 @@ void relocate(Plan* plan, uint64_t workspace_base);
 // Structural checks (stage order, coverage, capacities).  Returns the number of violations and
 // appends their descriptions to `why`.
 int check_plan(const ModelShape& m, const Plan& plan, std::string* why);
+
+// Replays the compiled queues over a launch sequence on the CPU (mk_emu.cpp).  Fills *rep and
+// returns a description of the first problems found ("" when none).
+std::string emulate(const ModelShape& m, const mk_emu_config& cfg, mk_emu_report* rep);
 
 }  // namespace mk

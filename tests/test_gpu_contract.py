@@ -121,3 +121,47 @@ def test_shuffled_pages_match_identity_pages_bitwise():
         res.append(np.stack(lg))
         g.close()
     assert np.array_equal(res[0], res[1])
+
+
+def test_step_queued_behind_a_failed_step_does_nothing():
+    """A step enqueued before the host has seen a device error (no sync in between) leaves at
+    entry: it writes no logits, and the error is reported once the host syncs."""
+    import torch
+    cfg = synth.SMALL["tiny-gain"].replace(batch=2, ctx=[10, 20])
+    g, ctx0, _ = _ctx(cfg)
+    say("queued behind a failed step")
+    assert g.step([3, cfg.vocab + 1], [10, 20], [11, 21]) == 0   # row 1: token out of range
+    g.logits.fill_(123.0)                                        # stream-ordered between the launches
+    assert g.step([3, 4], [11, 21], [12, 22]) == 0               # accepted: the host does not know yet
+    torch.cuda.synchronize()
+    assert g.sync() == mkd.MK_ERR_DEVICE_INPUT
+    assert (g.logits[:2].cpu().numpy() == 123.0).all()
+    assert g.reset() == 0
+    assert g.step([3, 4], [11, 21], [12, 22]) == 0
+    torch.cuda.synchronize()
+    assert g.sync() == 0 and np.isfinite(g.logits[:2].cpu().numpy()).all()
+    g.close()
+
+
+def test_watchdog_timeout_is_reported_and_reset(monkeypatch):
+    """The timeout path forced from the host: a watchdog limit of 1 us ends the step's waits
+    (every wait in the kernel is bounded), the step reports MK_ERR_TIMEOUT, later steps are refused
+    until mk_reset, and a context with the normal limit works afterwards in the same process."""
+    import torch
+    cfg = synth.CONFIGS["tiny"]
+    monkeypatch.setenv("MK_WATCHDOG_MS", "0.001")
+    g, ctx0, _ = _ctx(cfg)
+    say("forced watchdog timeout")
+    assert g.step([1], [ctx0[0]], [ctx0[0] + 1]) == 0
+    torch.cuda.synchronize()
+    assert g.sync() == mkd.MK_ERR_TIMEOUT
+    assert g.step([1], [ctx0[0]], [ctx0[0] + 1]) == mkd.MK_ERR_STATE
+    assert g.reset() == 0
+    assert g.sync() == 0
+    g.close()
+    monkeypatch.delenv("MK_WATCHDOG_MS")
+    g, ctx0, _ = _ctx(cfg)
+    assert g.step([1], [ctx0[0]], [ctx0[0] + 1]) == 0
+    torch.cuda.synchronize()
+    assert g.sync() == 0 and np.isfinite(g.logits[:1].cpu().numpy()).all()
+    g.close()
