@@ -126,6 +126,19 @@ mk_status mk_create(const mk_model_desc* desc, const mk_weights* weights, const 
 mk_status mk_decode_step(mk_ctx* ctx, const int32_t* tokens, const int32_t* positions, const int32_t* ctx_lens,
                          int32_t batch, float* logits_out, void* hip_stream);
 
+/* mk_create for callers that cannot allocate device memory (code under HIP graph capture,
+ * allocation-free serving loops, harnesses that forbid hipMalloc): the same context, with the
+ * library's static device scratch of MK_STATIC_SCRATCH_BYTES as its workspace instead of a
+ * caller-provided one.  Allocates no device memory (no hipMalloc / hipFree); it clears the scratch
+ * with a fill kernel and uploads the plan, synchronously.  Each GPU holds one such scratch for
+ * the life of the process, shared by every call on that GPU: a later mk_create_static on the same
+ * GPU takes it over, after which the earlier context's calls return MK_ERR_STATE (destroy it).
+ * Contexts on one GPU's scratch must not be stepped concurrently (they would race).
+ * MK_ERR_INVALID_ARG when the model's workspace (mk_workspace_size) exceeds the scratch. */
+#define MK_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+mk_status mk_create_static(const mk_model_desc* desc, const mk_weights* weights, const mk_kv_cache* cache,
+                           mk_ctx** out);
+
 /* Wait for the last step and return the sticky device status. */
 mk_status mk_sync_status(mk_ctx* ctx);
 

@@ -75,7 +75,9 @@ class mk_emu_report(ctypes.Structure):
 MK_EMU_COUNTERS, MK_EMU_IDLE_ITEMS_SILENT, MK_EMU_DEAD_ROWS_SILENT, MK_EMU_STALL_ONE_OP = 1, 2, 4, 8
 
 EXPORTED = ["mk_workspace_size", "mk_create", "mk_decode_step", "mk_sync_status", "mk_reset", "mk_last_error",
-            "mk_destroy", "mk_plan", "mk_emulate", "mk_copy_midstate", "mk_trace_words", "mk_copy_trace"]
+            "mk_destroy", "mk_plan", "mk_emulate", "mk_copy_midstate", "mk_trace_words", "mk_copy_trace",
+            "mk_create_static"]
+MK_STATIC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -91,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.mk_workspace_size.argtypes = [ctypes.POINTER(mk_model_desc), ctypes.POINTER(ctypes.c_size_t)]
         L.mk_create.argtypes = [ctypes.POINTER(mk_model_desc), ctypes.POINTER(mk_weights),
                                 ctypes.POINTER(mk_kv_cache), P, ctypes.c_size_t, ctypes.POINTER(P)]
+        L.mk_create_static.argtypes = [ctypes.POINTER(mk_model_desc), ctypes.POINTER(mk_weights),
+                                       ctypes.POINTER(mk_kv_cache), ctypes.POINTER(P)]
         L.mk_decode_step.argtypes = [P, P, P, P, I32, P, P]
         L.mk_sync_status.argtypes = [P]
         L.mk_reset.argtypes = [P]
@@ -104,7 +108,7 @@ def lib() -> ctypes.CDLL:
         L.mk_copy_midstate.argtypes = [P, I32, I32, P, ctypes.c_size_t, P]
         L.mk_trace_words.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         L.mk_copy_trace.argtypes = [P, P, ctypes.c_size_t]
-        for f in ("mk_workspace_size", "mk_create", "mk_decode_step", "mk_sync_status", "mk_reset", "mk_plan",
+        for f in ("mk_workspace_size", "mk_create", "mk_create_static", "mk_decode_step", "mk_sync_status", "mk_reset", "mk_plan",
                   "mk_emulate", "mk_copy_midstate", "mk_trace_words", "mk_copy_trace"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -171,6 +175,14 @@ def mk_create(desc, weights: mk_weights, cache: mk_kv_cache, workspace_ptr: int,
     return out.value
 
 
+def mk_create_static(desc, weights: mk_weights, cache: mk_kv_cache) -> int:
+    """mk_create with the library's static device scratch as the workspace (no allocation)."""
+    out = P()
+    check(lib().mk_create_static(ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(cache), ctypes.byref(out)),
+          "mk_create_static")
+    return out.value
+
+
 def mk_decode_step(ctx: int, tokens_ptr: int, positions_ptr: int, ctx_lens_ptr: int, batch: int, logits_ptr: int,
                    stream: int = 0) -> int:
     return lib().mk_decode_step(ctx, tokens_ptr, positions_ptr, ctx_lens_ptr, batch, logits_ptr, stream or None)
@@ -206,7 +218,8 @@ class DecodeContext:
 
     ARENA_ALIGN = 2 << 20  # weights sit 2 MiB-aligned in one arena allocation
 
-    def __init__(self, shape: dict, weights: dict, cache: dict, device: str = "cuda:0", arena: bool = True):
+    def __init__(self, shape: dict, weights: dict, cache: dict, device: str = "cuda:0", arena: bool = True,
+                 static_workspace: bool = False):
         import numpy as np
         import torch
         self.torch = torch
@@ -263,10 +276,14 @@ class DecodeContext:
                              self.conv_state.data_ptr() if self.conv_state is not None else None)
         with torch.cuda.device(self.device):
             self.ws_bytes = mk_workspace_size(self.desc)
-            self.workspace = torch.zeros(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
-            base = self.workspace.data_ptr()
-            self.ws_ptr = (base + 255) // 256 * 256
-            self.ctx = mk_create(self.desc, self.w, self.c, self.ws_ptr, self.ws_bytes)
+            if static_workspace:  # the library's static scratch: no workspace tensor
+                self.workspace = None
+                self.ctx = mk_create_static(self.desc, self.w, self.c)
+            else:
+                self.workspace = torch.zeros(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
+                base = self.workspace.data_ptr()
+                self.ws_ptr = (base + 255) // 256 * 256
+                self.ctx = mk_create(self.desc, self.w, self.c, self.ws_ptr, self.ws_bytes)
         B = s["max_batch"]
         self.tokens = torch.zeros(B, dtype=torch.int32, device=self.device)
         self.positions = torch.zeros(B, dtype=torch.int32, device=self.device)

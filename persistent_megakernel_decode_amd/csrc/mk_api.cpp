@@ -59,6 +59,19 @@ __global__ void fill_u32(uint32_t* p, size_t n, uint32_t v) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
+// ---- the static scratch of mk_create_static ----
+// Callers that cannot allocate device memory (code under graph capture, allocation-free serving
+// loops) get a workspace from this file-scope array instead of bringing one.  Each GPU the library
+// runs on holds its own copy until the process ends.  In host code `scratch` is only a stand-in:
+// its device address on the current GPU comes from hipGetSymbolAddress, taken once per device.
+constexpr size_t STATIC_SCRATCH_BYTES = MK_STATIC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[STATIC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+uint64_t g_scratch_gen[MAX_DEVICES] = {};  // bumped by every mk_create_static on that device
+
 }  // namespace
 
 struct mk_ctx {
@@ -76,8 +89,22 @@ struct mk_ctx {
   const void* kernel = nullptr;
   bool plain_launch = false;
   uint32_t* trace = nullptr;  // MK_TRACE=1: the workspace's trace section, 4 words per op
+  uint64_t static_gen = 0;    // mk_create_static: the device scratch generation this context owns (0 = own workspace)
   std::mutex busy;
 };
+
+// A context made by mk_create_static owns the device's static scratch until the next
+// mk_create_static on that device; after that every call that touches its workspace is refused.
+static bool scratch_taken_over(const mk_ctx* ctx) {
+  if (!ctx->static_gen) return false;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  return g_scratch_gen[ctx->device] != ctx->static_gen;
+}
+#define MK_CHECK_SCRATCH(ctx)                                                                           \
+  do {                                                                                                  \
+    if (scratch_taken_over(ctx))                                                                        \
+      return fail(MK_ERR_STATE, "a later mk_create_static on this device took over the static scratch"); \
+  } while (0)
 
 extern "C" {
 
@@ -147,8 +174,8 @@ mk_status mk_emulate(const mk_model_desc* desc, const mk_emu_config* cfg, mk_emu
   return MK_OK;
 }
 
-mk_status mk_create(const mk_model_desc* desc, const mk_weights* w, const mk_kv_cache* c, void* workspace,
-                    size_t workspace_bytes, mk_ctx** out) {
+static mk_status create_impl(const mk_model_desc* desc, const mk_weights* w, const mk_kv_cache* c, void* workspace,
+                             size_t workspace_bytes, mk_ctx** out, uint64_t static_gen) {
   if (!out) return fail(MK_ERR_INVALID_ARG, "out is null");
   *out = nullptr;
   mk::ModelShape m;
@@ -238,7 +265,9 @@ mk_status mk_create(const mk_model_desc* desc, const mk_weights* w, const mk_kv_
   mk::relocate(&P, (uint64_t)(uintptr_t)workspace);
   const mk::Layout& Y = P.lay;
   // zero everything (activations, counters, tickets, status), then upload the plan
-  he = hipMemset(workspace, 0, Y.total);
+  // (a fill kernel rather than a memset, so the same code serves the static scratch)
+  hipLaunchKernelGGL(fill_u32, dim3(256), dim3(256), 0, nullptr, (uint32_t*)workspace, Y.total / 4, 0u);
+  he = hipGetLastError();
   if (he == hipSuccess) he = hipMemcpy(ctx->ws + Y.ops, P.ops.data(), P.ops.size() * sizeof(mk::Op), hipMemcpyHostToDevice);
   if (he == hipSuccess)
     he = hipMemcpy(ctx->ws + Y.queue_off, P.queue_off.data(), P.queue_off.size() * 4, hipMemcpyHostToDevice);
@@ -296,8 +325,49 @@ mk_status mk_create(const mk_model_desc* desc, const mk_weights* w, const mk_kv_
   if (const char* s = getenv("MK_PLAIN_LAUNCH")) ctx->plain_launch = atoi(s) != 0;
   ctx->trace = traced ? (uint32_t*)(ctx->ws + Y.trace) : nullptr;  // zeroed with the workspace
   A.trace = ctx->trace;
+  ctx->static_gen = static_gen;
   *out = ctx;
   return MK_OK;
+}
+
+mk_status mk_create(const mk_model_desc* desc, const mk_weights* w, const mk_kv_cache* c, void* workspace,
+                    size_t workspace_bytes, mk_ctx** out) {
+  return create_impl(desc, w, c, workspace, workspace_bytes, out, 0);
+}
+
+mk_status mk_create_static(const mk_model_desc* desc, const mk_weights* w, const mk_kv_cache* c, mk_ctx** out) {
+  if (!out) return fail(MK_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  mk::ModelShape m;
+  mk_status st;
+  std::string e = mk::validate_desc(desc, &m, &st);
+  if (!e.empty()) return fail(st, e);
+  int ncu = 0;
+  const int dev = device_cus(&ncu);
+  if (dev < 0) return fail(MK_ERR_HIP, "cannot query the current HIP device");
+  if (dev >= MAX_DEVICES) return fail(MK_ERR_UNSUPPORTED, "device index above the static scratch table");
+  mk::Plan p;
+  e = mk::build_plan(m, ncu, nullptr, nullptr, &p);
+  if (!e.empty()) return fail(MK_ERR_UNSUPPORTED, e);
+  if (p.lay.total > STATIC_SCRATCH_BYTES)
+    return fail(MK_ERR_INVALID_ARG, "the model needs " + std::to_string(p.lay.total) +
+                                        " bytes of workspace; the static scratch holds " +
+                                        std::to_string(STATIC_SCRATCH_BYTES) + " (use mk_create with a workspace)");
+  void* ptr = nullptr;
+  uint64_t gen = 0;
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {  // this device's copy of the array, with this device current
+      hipError_t he = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+      if (he != hipSuccess) {
+        g_scratch_ptr[dev] = nullptr;
+        return hip_fail(he, "hipGetSymbolAddress(scratch)");
+      }
+    }
+    ptr = g_scratch_ptr[dev];
+    gen = ++g_scratch_gen[dev];
+  }
+  return create_impl(desc, w, c, ptr, STATIC_SCRATCH_BYTES, out, gen);
 }
 
 static mk_status zero_counters(mk_ctx* ctx, hipStream_t s) {
@@ -318,6 +388,7 @@ mk_status mk_decode_step(mk_ctx* ctx, const int32_t* tokens, const int32_t* posi
     return fail(MK_ERR_INVALID_ARG, "batch " + std::to_string(batch) + " outside [1, max_batch]");
   std::unique_lock<std::mutex> lk(ctx->busy, std::try_to_lock);
   if (!lk.owns_lock()) return fail(MK_ERR_STATE, "another thread is stepping this context");
+  MK_CHECK_SCRATCH(ctx);
   hipStream_t s = (hipStream_t)hip_stream;
   // counters count cumulatively (epoch * ops); restart the epochs long before 32-bit overflow
   if ((uint64_t)(ctx->epoch + 1) * ctx->max_stage_ops >= (1ull << 31)) {
@@ -347,6 +418,7 @@ mk_status mk_decode_step(mk_ctx* ctx, const int32_t* tokens, const int32_t* posi
 
 mk_status mk_sync_status(mk_ctx* ctx) {
   if (!ctx) return fail(MK_ERR_INVALID_ARG, "ctx is null");
+  MK_CHECK_SCRATCH(ctx);
   MK_HIP(hipStreamSynchronize(ctx->last_stream));
   uint32_t st[2] = {0, 0};
   MK_HIP(hipMemcpy(st, ctx->ws + ctx->plan.lay.status, sizeof st, hipMemcpyDeviceToHost));
@@ -359,6 +431,7 @@ mk_status mk_sync_status(mk_ctx* ctx) {
 
 mk_status mk_reset(mk_ctx* ctx) {
   if (!ctx) return fail(MK_ERR_INVALID_ARG, "ctx is null");
+  MK_CHECK_SCRATCH(ctx);
   MK_HIP(hipDeviceSynchronize());
   const mk::Layout& Y = ctx->plan.lay;
   mk_status r = zero_counters(ctx, nullptr);
@@ -389,6 +462,7 @@ mk_status mk_trace_words(mk_ctx* ctx, size_t* count) {
 
 mk_status mk_copy_trace(mk_ctx* ctx, uint32_t* dst, size_t count) {
   if (!ctx || !dst) return fail(MK_ERR_INVALID_ARG, "null argument");
+  MK_CHECK_SCRATCH(ctx);
   if (!ctx->trace) return fail(MK_ERR_STATE, "tracing is off (set MK_TRACE=1 before mk_create)");
   size_t need = 0;
   mk_trace_words(ctx, &need);
@@ -404,6 +478,7 @@ mk_status mk_copy_trace(mk_ctx* ctx, uint32_t* dst, size_t count) {
 
 mk_status mk_copy_midstate(mk_ctx* ctx, int32_t kind, int32_t layer, float* dst, size_t count, void* hip_stream) {
   if (!ctx || !dst) return fail(MK_ERR_INVALID_ARG, "null argument");
+  MK_CHECK_SCRATCH(ctx);
   const mk_model_desc& d = ctx->shape.d;
   if (layer < 0 || layer >= d.n_layers) return fail(MK_ERR_INVALID_ARG, "layer out of range");
   const auto& Q = ctx->plan.lay.layer[layer];

@@ -83,3 +83,17 @@ def test_trace_calls_reject_null_arguments():
     assert L.mk_trace_words(None, None) == mkd.MK_ERR_INVALID_ARG
     buf = (ctypes.c_uint32 * 8)()
     assert L.mk_copy_trace(None, buf, 8) == mkd.MK_ERR_INVALID_ARG
+
+
+def test_library_imports_no_device_allocator():
+    """The library never allocates device memory itself (every buffer is the caller's, or the static
+    scratch of mk_create_static): its dynamic imports hold no hipMalloc / hipFree family call."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm is not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", mkd.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    imported = {l.split()[-1].split("@")[0] for l in out.splitlines() if l.strip()}
+    assert "hipGetSymbolAddress" in imported
+    assert not {s for s in imported if s.startswith("hip") and ("Malloc" in s or "Free" in s or "Alloc" in s)}
