@@ -222,7 +222,8 @@ mk_status mk_copy_midstate(mk_ctx* ctx, int32_t kind, int32_t layer, float* dst,
  * trace buffer (allocated at mk_create only in this mode).
  * mk_copy_trace waits for the last step and copies into host memory `dst` (`count` uint32):
  *   [0] n_ops, [1] n_cus, [2 .. 2+n_cus] queue offsets (op range of CU c: [off[c], off[c+1])),
- *   then per op 4 words {opcode << 16 | stage, t_start, t_ready, t_end}.
+ *   then per op 8 words {opcode << 16 | stage, t_start, t_ready, t_end, loader first issue, loader
+ *   last issue, loader ticks blocked on a full ring, 0} (the loader wave streams the op's bytes).
  * Returns MK_ERR_STATE when tracing is off and MK_ERR_INVALID_ARG when count is too small
  * (mk_trace_words gives the size). */
 mk_status mk_trace_words(mk_ctx* ctx, size_t* count);

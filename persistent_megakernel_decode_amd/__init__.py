@@ -78,6 +78,7 @@ EXPORTED = ["mk_workspace_size", "mk_create", "mk_decode_step", "mk_sync_status"
             "mk_destroy", "mk_plan", "mk_emulate", "mk_copy_midstate", "mk_trace_words", "mk_copy_trace",
             "mk_create_static"]
 MK_STATIC_SCRATCH_BYTES = 64 << 20
+TRACE_WORDS = 8  # per-op trace record (mk_internal.h)
 
 _lib = None
 
@@ -323,8 +324,9 @@ class DecodeContext:
 
     def trace(self) -> dict:
         """Per-op timing of the last step (the context must have been created with MK_TRACE=1):
-        queue offsets per CU and, per op, opcode, stage and the start / inputs-ready / end stamps
-        (100 MHz GPU clock, low 32 bits)."""
+        queue offsets per CU and, per op, opcode, stage, the compute waves' start / inputs-ready / end
+        stamps (100 MHz GPU clock, low 32 bits) and the loader wave's first-issue / last-issue stamps
+        and the ticks it spent blocked on a full ring while issuing the op."""
         import numpy as np
         n = ctypes.c_size_t(0)
         check(lib().mk_trace_words(self.ctx, ctypes.byref(n)), "mk_trace_words")
@@ -332,10 +334,11 @@ class DecodeContext:
         check(lib().mk_copy_trace(self.ctx, buf.ctypes.data, n.value), "mk_copy_trace")
         n_ops, n_cus = int(buf[0]), int(buf[1])
         off = buf[2:3 + n_cus].astype(np.int64)
-        rec = buf[3 + n_cus:].reshape(n_ops, 4)
+        rec = buf[3 + n_cus:].reshape(n_ops, TRACE_WORDS)
         cu = np.repeat(np.arange(n_cus), np.diff(off))
         return {"n_cus": n_cus, "queue_off": off, "cu": cu, "opcode": rec[:, 0] >> 16,
-                "stage": (rec[:, 0] & 0xFFFF).astype(np.int16), "t": rec[:, 1:].astype(np.int64)}
+                "stage": (rec[:, 0] & 0xFFFF).astype(np.int16), "t": rec[:, 1:4].astype(np.int64),
+                "loader": rec[:, 4:7].astype(np.int64)}
 
     def close(self) -> None:
         if getattr(self, "ctx", None):

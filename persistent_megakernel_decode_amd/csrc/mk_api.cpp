@@ -88,7 +88,7 @@ struct mk_ctx {
   mk_status sticky = MK_OK;
   const void* kernel = nullptr;
   bool plain_launch = false;
-  uint32_t* trace = nullptr;  // MK_TRACE=1: the workspace's trace section, 4 words per op
+  uint32_t* trace = nullptr;  // MK_TRACE=1: the workspace's trace section, TRACE_WORDS per op
   uint64_t static_gen = 0;    // mk_create_static: the device scratch generation this context owns (0 = own workspace)
   std::mutex busy;
 };
@@ -456,7 +456,7 @@ void mk_destroy(mk_ctx* ctx) { delete ctx; }
 
 mk_status mk_trace_words(mk_ctx* ctx, size_t* count) {
   if (!ctx || !count) return fail(MK_ERR_INVALID_ARG, "null argument");
-  *count = 2 + (size_t)ctx->plan.n_cus + 1 + ctx->plan.ops.size() * 4;
+  *count = 2 + (size_t)ctx->plan.n_cus + 1 + ctx->plan.ops.size() * mk::TRACE_WORDS;
   return MK_OK;
 }
 
@@ -472,7 +472,8 @@ mk_status mk_copy_trace(mk_ctx* ctx, uint32_t* dst, size_t count) {
   dst[0] = (uint32_t)P.ops.size();
   dst[1] = (uint32_t)P.n_cus;
   for (int c = 0; c <= P.n_cus; ++c) dst[2 + c] = P.queue_off[c];
-  MK_HIP(hipMemcpy(dst + 3 + P.n_cus, ctx->trace, P.ops.size() * 4 * sizeof(uint32_t), hipMemcpyDeviceToHost));
+  MK_HIP(hipMemcpy(dst + 3 + P.n_cus, ctx->trace, P.ops.size() * mk::TRACE_WORDS * sizeof(uint32_t),
+                   hipMemcpyDeviceToHost));
   return MK_OK;
 }
 

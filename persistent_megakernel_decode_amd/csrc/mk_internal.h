@@ -157,8 +157,12 @@ struct KArgs {
   uint32_t tag;               // launch tag: bit 0 is the activation parity, row_ok holds tag << 1 | ok
   uint64_t spin_limit;        // watchdog, in s_memrealtime ticks (100 MHz)
   uint32_t spin_check_mask;   // the watchdog reads the clock once every (mask + 1) polls
-  uint32_t* trace;            // MK_TRACE=1: per op {opcode << 16 | stage, start, inputs ready, end}; else null
+  uint32_t* trace;            // MK_TRACE=1: TRACE_WORDS per op (see below); else null
 };
+
+// Per-op trace record of the traced kernels: {opcode << 16 | stage, start, inputs ready, end,
+// loader first issue, loader last issue, loader ticks blocked on a full ring, 0} (100 MHz clock).
+constexpr int TRACE_WORDS = 8;
 
 // status bits
 constexpr uint32_t ST_BAD_INPUT = 1u;

@@ -68,6 +68,9 @@ __shared__ u32 g_abort;         // set on watchdog expiry: every wave leaves
 __shared__ u32 g_bcast[4];
 #if MK_TRACE_STAMPS
 __shared__ u32 g_trace_oi;  // queue index of the running op (written and read by compute wave 0 only)
+// loader stamps of op oi at [(oi % 64) * 3]: first issue, last issue, ticks blocked on a full ring
+constexpr int LDTR_OPS = 64;
+__shared__ u32 g_ldtr[LDTR_OPS * 3];
 #endif
 
 // ------------------------------------------------------------------ helpers
@@ -365,7 +368,7 @@ __device__ __forceinline__ bool row_ok_fix(const KArgs& A, int b, int32_t v) {
 // Traced kernels: stamp "inputs in hand" for the running op (compute wave 0, lane 0 only).
 __device__ __forceinline__ void trace_ready(const KArgs& A, u32 w) {
 #if MK_TRACE_STAMPS
-  if (w == 0 && lane_id() == 0) A.trace[(size_t)g_trace_oi * 4 + 2] = (u32)__builtin_amdgcn_s_memrealtime();
+  if (w == 0 && lane_id() == 0) A.trace[(size_t)g_trace_oi * TRACE_WORDS + 2] = (u32)__builtin_amdgcn_s_memrealtime();
 #endif
 }
 
@@ -619,27 +622,17 @@ __device__ __forceinline__ void issue_gemv(const GemvSeg& gsg, GemvWalk& gw, u32
 
 // Attention stream: slot s = PPS positions of K (pieces 0-3) then the same positions of V (4-7).
 // Chunks start on page boundaries and a slot holds one page (d = 128) or two (d = 64), so a slot
-// needs at most two page-table entries.  The loader keeps 64 consecutive entries of one sequence
-// in a VGPR (one per lane) and refills the window only when a page falls outside it.
+// needs at most two page-table entries.  They are read with scalar loads: a vector load would make
+// the loader wait for every DMA issued before it (the memory counter drains in order), while a
+// scalar load waits only for itself and mostly hits the scalar cache (16 entries per line).
 //
 // K rows are stored swizzled: 16-byte chunk c of row r sits at chunk position c ^ (r mod CPR)
 // (CPR = chunks per row), so the 16 rows one matrix-core operand read touches fall in distinct
 // LDS banks.  A DMA lane chooses its source address, so the swizzle costs nothing: lane i of
 // piece j fills row r = j*RPP + i/CPR, chunk position i mod CPR.
-struct PageWindow {
-  int b = -1;
-  u32 base = 0;
-  int v = 0;  // lane i: physical page of logical page base + i
-};
-__device__ __forceinline__ int page_lookup(const KArgs& A, PageWindow& pw, int b, u32 pi) {
-  if (b != pw.b || pi < pw.base || pi >= pw.base + 64) {
-    pw.b = b;
-    pw.base = pi;
-    const u32 lp = pi + lane_id();
-    int v = lp < (u32)A.max_pages_per_seq ? A.page_table[(size_t)b * A.max_pages_per_seq + lp] : 0;
-    pw.v = (v >= 0 && v < A.num_pages) ? v : 0;  // out-of-range entries stream page 0 (rows get masked)
-  }
-  return __builtin_amdgcn_readlane(pw.v, (int)(pi - pw.base));
+__device__ __forceinline__ int page_lookup(const KArgs& A, int b, u32 pi) {
+  const int v = sload(A.page_table + (size_t)b * A.max_pages_per_seq + pi);
+  return (v >= 0 && v < A.num_pages) ? v : 0;  // out-of-range entries stream page 0 (rows get masked)
 }
 struct AttnLanes {  // per-lane byte offsets of each piece within its page's (kv head) block
   u32 koff[4], voff[4];
@@ -658,7 +651,7 @@ __device__ AttnLanes attn_lanes(u32 d) {
   return L;
 }
 __device__ void issue_attn(const KArgs& A, const LayerDesc& Ld, const AttnItem& it, u32 s, const AttnLanes& L,
-                           PageWindow& pw, u32 lane16, u32x4* dst) {
+                           u32 lane16, u32x4* dst) {
   const u32 d = (u32)A.d, pps = 4096u / (2u * d);
   const size_t page_bytes = (size_t)A.Hkv * 16 * d * 2, head_off = (size_t)it.kvh * 16 * d * 2;
   const u32 pbase = (u32)it.p0 + s * pps, pi0 = pbase / 16;
@@ -668,7 +661,7 @@ __device__ void issue_attn(const KArgs& A, const LayerDesc& Ld, const AttnItem& 
 #pragma unroll
   for (u32 k = 0; k < 2; ++k) {
     const bool used = (pi0 + k) * 16 < (u32)it.p1 && (k == 0 || pps > 16);
-    off[k] = used ? (size_t)page_lookup(A, pw, it.b, pi0 + k) * page_bytes + head_off : 0;
+    off[k] = used ? (size_t)page_lookup(A, it.b, pi0 + k) * page_bytes + head_off : 0;
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -720,18 +713,34 @@ __device__ u32 op_slots(const KArgs& A, const Op& o, ItemCache& ic) {
   return o.nslots;
 }
 
+#if MK_TRACE_STAMPS
+// LDS store for the loader (opaque to the compiler's DMA tracking, like publish_filled)
+__device__ __forceinline__ void loader_lds_store(u32* p, u32 v) {
+  const u32 addr = (u32)(uintptr_t)(__attribute__((address_space(3))) u32*)p;
+  asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+#endif
+
 __device__ __forceinline__ void loader(const KArgs& A0, u32 q0, u32 q1) {
   const KArgs& A = A0;
   u32 seq = 0, marked = 0, limit = NSLOT;  // slots below `limit` may be filled
   const u32 lane16 = lane_id() * 16;
   attn_plan_build(A, A.d == 64 ? 32 : 16);
   ItemCache ic;
-  PageWindow pw;
   const AttnLanes al = attn_lanes(A.d == 64 ? 64u : 128u);
   for (u32 oi = q0; oi < q1; ++oi) {
     const KArgs& A = kargs();
     const Op o = sload(A.ops + oi);
     const u32 ns = op_slots(A, o, ic);
+#if MK_TRACE_STAMPS
+    u32 tr_first = (u32)__builtin_amdgcn_s_memrealtime(), tr_blocked = 0;
+    if (ns == 0) {
+      u32* ld = g_ldtr + (oi % LDTR_OPS) * 3;
+      loader_lds_store(ld, tr_first);
+      loader_lds_store(ld + 1, tr_first);
+      loader_lds_store(ld + 2, 0u);
+    }
+#endif
     if (ns == 0) continue;
     LayerDesc Ld{};
     AttnItem it{};
@@ -743,6 +752,9 @@ __device__ __forceinline__ void loader(const KArgs& A0, u32 q0, u32 q1) {
     if (o.opcode == OP_ATTN) it = ic.get(A, o.row0, attn_pps(A.d));
     for (u32 s = 0; s < ns; ++s) {
       if (seq >= limit) {  // the ring looks full: publish what has landed, then re-read the consumers
+#if MK_TRACE_STAMPS
+        const u32 tb0 = (u32)__builtin_amdgcn_s_memrealtime();
+#endif
         Watchdog wd(A);
         while (true) {
           if (marked < seq) {
@@ -759,11 +771,17 @@ __device__ __forceinline__ void loader(const KArgs& A0, u32 q0, u32 q1) {
             __builtin_amdgcn_s_sleep(1);
           }
         }
+#if MK_TRACE_STAMPS
+        tr_blocked += (u32)__builtin_amdgcn_s_memrealtime() - tb0;
+#endif
       }
+#if MK_TRACE_STAMPS
+      if (s == 0) tr_first = (u32)__builtin_amdgcn_s_memrealtime();
+#endif
       u32x4* dst = g_ring + (seq % NSLOT) * (SLOT / 16);
       if (o.opcode == OP_GEMV) issue_gemv(gsg, gw, lane16 >> 4, dst);
       else if (o.opcode == OP_MMV) issue_mmv(gsg, s, mmv_nt, o.nrows, o.epi == EPI_SWIGLU, lane16 >> 4, dst);
-      else if (o.opcode == OP_ATTN) issue_attn(A, Ld, it, s, al, pw, lane16, dst);
+      else if (o.opcode == OP_ATTN) issue_attn(A, Ld, it, s, al, lane16, dst);
       else issue_delta(A, Ld, o.row0, s, lane16, dst);
       ++seq;
       if (seq - marked > LOAD_DEPTH) {
@@ -771,6 +789,14 @@ __device__ __forceinline__ void loader(const KArgs& A0, u32 q0, u32 q1) {
         publish_filled(++marked);
       }
     }
+#if MK_TRACE_STAMPS
+    {
+      u32* ld = g_ldtr + (oi % LDTR_OPS) * 3;
+      loader_lds_store(ld, tr_first);
+      loader_lds_store(ld + 1, (u32)__builtin_amdgcn_s_memrealtime());
+      loader_lds_store(ld + 2, tr_blocked);
+    }
+#endif
   }
   while (marked < seq) {
     wait_oldest(seq - marked);
@@ -1916,7 +1942,7 @@ __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
 #if MK_TRACE_STAMPS
     if (w == 0 && lane_id() == 0) {
       const u32 t = (u32)__builtin_amdgcn_s_memrealtime();
-      u32* tr = A.trace + (size_t)oi * 4;
+      u32* tr = A.trace + (size_t)oi * TRACE_WORDS;
       tr[0] = ((u32)o.opcode << 16) | (u32)(uint16_t)o.sig_stage;
       tr[1] = t;
       tr[2] = t;
@@ -1957,7 +1983,14 @@ __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
     if (!cbar(A, gen)) return;  // (also: the next op may overwrite this op's LDS areas)
     if (sig && w == 0 && lane_id() == 0) signal_stage(A, o.sig_stage, o.sig_index);
 #if MK_TRACE_STAMPS
-    if (w == 0 && lane_id() == 0) A.trace[(size_t)oi * 4 + 3] = (u32)__builtin_amdgcn_s_memrealtime();
+    if (w == 0 && lane_id() == 0) {
+      u32* tr = A.trace + (size_t)oi * TRACE_WORDS;
+      tr[3] = (u32)__builtin_amdgcn_s_memrealtime();
+      const u32* ld = g_ldtr + (oi % LDTR_OPS) * 3;
+      tr[4] = ld[0];
+      tr[5] = ld[1];
+      tr[6] = ld[2];
+    }
 #endif
   }
 }

@@ -459,7 +459,7 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
   Y.layers = take((size_t)L * sizeof(LayerDesc));
   // per-op timing stamps of the traced kernels (MK_TRACE=1), 4 words per op; kept in every
   // workspace so that tracing never needs memory of its own
-  Y.trace = take(P.ops.size() * 4 * sizeof(uint32_t));
+  Y.trace = take(P.ops.size() * TRACE_WORDS * sizeof(uint32_t));
   Y.total = off;
   return "";
 }
