@@ -76,6 +76,9 @@ constexpr uint32_t OPF_NO_SIGNAL = 2u;
 // i = 2i + 1), at most MMV_TILES tiles, and streams K in segments of MMV_KSEG inputs: ring slot
 // s holds tile s % ntiles of segment s / ntiles (16 rows x 256 inputs, 8 KB); `ppr` holds the
 // number of segments K / MMV_KSEG.
+// A GEMV op (batch <= 4) with norm == 1 streams its RMSNorm gain first: gain_slots(K) ring slots
+// holding the K bf16 gains in order, then its weights (`nslots` counts both).
+constexpr uint32_t gain_slots(uint32_t K) { return (K * 2 + SLOT - 1) / SLOT; }
 constexpr int MMV_KSEG = 256;
 constexpr int MMV_TILES = 8;
 struct alignas(16) Op {

@@ -748,6 +748,7 @@ __device__ __forceinline__ void loader(const KArgs& A0, u32 q0, u32 q1) {
     GemvWalk gw{};
     if (o.opcode == OP_GEMV) gw = gemv_walk(o, gsg, lane16 >> 4);
     const u32 mmv_nt = (o.epi == EPI_SWIGLU ? 2u : 1u) * ((o.nrows + 15) / 16);
+    const u32 gs = o.opcode == OP_GEMV && o.norm ? gain_slots(o.K) : 0u;  // gain slots first
     if (o.opcode == OP_ATTN || o.opcode == OP_DELTA) Ld = sload(A.layers + o.layer);
     if (o.opcode == OP_ATTN) it = ic.get(A, o.row0, attn_pps(A.d));
     for (u32 s = 0; s < ns; ++s) {
@@ -779,7 +780,13 @@ __device__ __forceinline__ void loader(const KArgs& A0, u32 q0, u32 q1) {
       if (s == 0) tr_first = (u32)__builtin_amdgcn_s_memrealtime();
 #endif
       u32x4* dst = g_ring + (seq % NSLOT) * (SLOT / 16);
-      if (o.opcode == OP_GEMV) issue_gemv(gsg, gw, lane16 >> 4, dst);
+      if (s < gs) {  // the RMSNorm gain, in order; lanes past the gain re-read its first bytes
+#pragma unroll
+        for (u32 i = 0; i < SLOT_PIECES; ++i) {
+          const u32 off = s * SLOT + i * PIECE + lane16;
+          dma_at((const char*)o.gamma, off < o.K * 2 ? off : 0u, dst + i * 64);
+        }
+      } else if (o.opcode == OP_GEMV) issue_gemv(gsg, gw, lane16 >> 4, dst);
       else if (o.opcode == OP_MMV) issue_mmv(gsg, s, mmv_nt, o.nrows, o.epi == EPI_SWIGLU, lane16 >> 4, dst);
       else if (o.opcode == OP_ATTN) issue_attn(A, Ld, it, s, al, lane16, dst);
       else issue_delta(A, Ld, o.row0, s, lane16, dst);
@@ -951,8 +958,9 @@ __device__ __forceinline__ float gemv_pick(const f32x4 d, u32 lane) {
   return (j & 2) ? hi : lo;
 }
 
-// Sum one row group's matched entries over the parts and store this wave's partials: g_red[(row *
-// RW + j) * B + b] for the group's R rows and B sequences.
+// Sum one row group's matched entries over the parts and store this wave's partials: g_red[(j * B +
+// b) * nrt + row] for the group's R rows and B sequences (row innermost, so the epilogue's threads --
+// one per row -- read consecutive words, free of bank conflicts).
 template <int B, int P>
 __device__ __forceinline__ void gemv_extract(const f32x4 d, u32 lane, u32 g, u32 j, u32 RW, u32 nrt) {
   constexpr u32 R = 16 / P;
@@ -972,7 +980,7 @@ __device__ __forceinline__ void gemv_extract(const f32x4 d, u32 lane, u32 g, u32
   const u32 r = P == 4 ? lane >> 4 : lane >> 5, b = P == 4 ? (lane >> 2) & 3 : (lane >> 3) & 1;
   const bool mine = P == 4 ? (lane & 3) == 0 : (lane & 23) == 0;
   const u32 row = g * R + r;
-  if (mine && b < (u32)B && row < nrt) g_red[(row * RW + j) * B + b] = v;
+  if (mine && b < (u32)B && row < nrt) g_red[(j * B + b) * nrt + row] = v;
 }
 
 // Per-row-group accumulation.  Two or more sequences make the projection a (skinny) matrix
@@ -1032,7 +1040,7 @@ struct GemvAcc<1, 8> {
     v += dppf<0x141>(v);  // row_half_mirror: the other quad of the 8 lanes
     v = add_swap32(add_swap16(v));
     const u32 row = 2 * g + ((lane >> 3) & 1);
-    if ((lane & ~8u) == 0 && row < nrt) g_red[row * RW + j] = v;
+    if ((lane & ~8u) == 0 && row < nrt) g_red[j * nrt + row] = v;
   }
 };
 
@@ -1046,9 +1054,10 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   const u32 lane = lane_id();
   // the Op's fields as independent scalars (see op_mmv)
   const u32 epi = opq((u32)o.epi), norm = opq((u32)o.norm), flags = opq(o.flags), nrows = opq(o.nrows);
-  const u32 pg = opq(o.ppr), K = opq(o.K), nslots = opq(o.nslots), row0 = opq(o.row0);
+  const u32 pg = opq(o.ppr), K = opq(o.K), row0 = opq(o.row0);
+  const u32 nslots = opq(o.nslots) - (norm ? gain_slots(K) : 0u);  // weight slots (after the gain's)
   const u32 ld_in = opq(o.ld_in), ld_out = opq(o.ld_out);
-  const uint64_t in = opq(o.in), gamma = opq(o.gamma), outp = opq(o.out), resp = opq(o.res);
+  const uint64_t in = opq(o.in), outp = opq(o.out), resp = opq(o.res);
   const bool swiglu = epi == EPI_SWIGLU;
   const u32 nrt = swiglu ? 2 * nrows : nrows;  // stream rows
   const u32 nrg = nrt / R;                      // row groups
@@ -1069,7 +1078,6 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   // between the loads and the stream.
   float xf[NF][8];
   u32x4 gv[NF];
-  const uint16_t* gm = (const uint16_t*)gamma;
   const float* xin = (const float*)in + (size_t)(B == 1 ? 0u : bl) * ld_in;
   u32 fv = 0;  // fragments this lane loads
 #pragma unroll
@@ -1083,7 +1091,38 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
       for (int e = 0; e < 8; ++e) xf[f][e] = 0.0f;
     }
-    gv[f] = v && norm ? *(const __attribute__((address_space(1))) u32x4*)(gm + k0) : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  }
+  // the RMSNorm gain arrives in the op's first ring slots (streamed ahead by the loader like the
+  // weights): this lane's 8 gains per fragment, at byte 2 k0 of the gain stream
+  u32 avail = seq;
+  if (norm) {
+    const u32 gs = gain_slots(K);
+    if (seq + gs > avail && !wait_avail(A, seq + gs, avail)) return false;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const u32 q = pg >= 8 ? 8 * f + w : w % pg;
+      const u32 byte = 2 * (q * KP + koff);
+      gv[f] = ((fv >> f) & 1u) ? g_ring[((seq + byte / SLOT) % NSLOT) * (SLOT / 16) + (byte % SLOT) / 16]
+                               : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    }
+    release_upto(w, seq + gs);
+    seq += gs;
+  }
+  // Single-sequence projections stage their first SG row groups in registers and free those ring
+  // slots before waiting for their inputs: while this op waits (for the merged attention heads, the
+  // last SwiGLU rows) the loader keeps streaming the following bytes into the freed ring instead of
+  // idling this compute unit's share of HBM.
+  constexpr u32 SG = B != 1 ? 0u : (NF == 1 ? 16u : (NF == 2 ? 8u : 0u));  // staged row groups
+  constexpr u32 SS = SG * NF > 0 ? SG * NF : 1u;                          // their slot registers
+  u32x4 stg[SS];
+  const bool staged = SG > 0 && pg >= 8 && nrg >= SG;
+  if (staged) {
+    const u32 nst = SG * nf;
+    if (seq + nst > avail && !wait_avail(A, seq + nst, avail)) return false;
+#pragma unroll
+    for (u32 i = 0; i < SS; ++i)
+      if (i % NF < nf) stg[i] = g_ring[((seq + (i / NF) * nf + i % NF) % NSLOT) * (SLOT / 16) + achunk];
+    release_upto(w, seq + nst);
   }
   // residual rows of this thread (epilogue row r = thread index), fetched now, off the critical path
   const u32 tid = w * 64 + lane, par = A.tag & 1u;
@@ -1144,10 +1183,43 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
     xl[f] = __builtin_bit_cast(bf16x8, l);
   }
 
-  u32 avail = seq;
   if (NF > 1 || pg >= 8) {
     // groups in order; a group's nf slots are consecutive and wave w takes piece w of each
     u32 g0 = 0;
+    if (staged) {  // the staged groups first, from registers (the same arithmetic as below)
+      if constexpr (NF <= 2) {
+#pragma unroll
+        for (u32 bt = 0; bt < SG / GB; ++bt) {
+          GemvAcc<B, P> acc[GB];
+#pragma unroll
+          for (u32 gb = 0; gb < GB; ++gb) acc[gb].init();
+#pragma unroll
+          for (u32 f = 0; f < NF; ++f)
+#pragma unroll
+            for (u32 gb = 0; gb < GB; ++gb) acc[gb].add(stg[(bt * GB + gb) * NF + f], xh[f], xl[f]);
+#pragma unroll
+          for (u32 gb = 0; gb < GB; ++gb) acc[gb].finish(lane, bt * GB + gb, w, RW, nrt);
+        }
+      } else {
+#pragma unroll
+        for (u32 g = 0; g < SG; ++g) {
+          GemvAcc<B, P> a0, a1;
+          a0.init();
+          a1.init();
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            if ((u32)f < nf) {
+              if (f & 1) a1.add(stg[g * NF + f], xh[f], xl[f]);
+              else a0.add(stg[g * NF + f], xh[f], xl[f]);
+            }
+          }
+          a0.merge(a1);
+          a0.finish(lane, g, w, RW, nrt);
+        }
+      }
+      g0 = SG;
+      seq += SG * nf;
+    }
     if constexpr (NF <= 2) {
       // whole batches of GB groups (NF = nf here): straight-line code, so the groups' matrix-core
       // chains and extractions interleave
@@ -1250,11 +1322,11 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       float v = 0.0f;
-      for (u32 j = 0; j < RW; ++j) v += g_red[(r * RW + j) * B + b];
+      for (u32 j = 0; j < RW; ++j) v += g_red[(j * B + b) * nrt + r];
       v *= rstd[b];
       if (epi == EPI_SWIGLU) {
         float u = 0.0f;
-        for (u32 j = 0; j < RW; ++j) u += g_red[((r + nrows) * RW + j) * B + b];
+        for (u32 j = 0; j < RW; ++j) u += g_red[(j * B + b) * nrt + r + nrows];
         st_tag((float*)outp + (size_t)b * ld_out + row, silu(v) * (u * rstd[b]), par);
       } else if (epi == EPI_RESID) {
         const float* rp = (const float*)resp + (size_t)b * ld_out + row;

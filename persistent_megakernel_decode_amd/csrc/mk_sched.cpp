@@ -161,7 +161,7 @@ struct Builder {
       o.K = K;
       o.part = (uint8_t)Pp;
       o.ppr = (uint32_t)pg;
-      o.nslots = gemv_slots(o.nrows * mult / R, (uint32_t)pg);
+      o.nslots = gemv_slots(o.nrows * mult / R, (uint32_t)pg) + (norm ? gain_slots(K) : 0u);
       o.ld_in = ld_in;
       o.ld_out = ld_out;
       // weight runs: at most two contiguous row runs per op
@@ -516,7 +516,8 @@ int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
         if (o.epi == EPI_SWIGLU && o.b1 != o.nrows) bad(fmt("cu %d op %u: gate / up runs", c, i));
         if ((uint64_t)o.nrows * mult * RW * P.kernel_batch > (uint64_t)RED_FLOATS)
           bad(fmt("cu %d op %u: tile exceeds the partial-sum area", c, i));
-        if (o.nslots != gemv_slots(o.nrows * mult / R, pg)) bad(fmt("cu %d op %u: slot count", c, i));
+        if (o.nslots != gemv_slots(o.nrows * mult / R, pg) + (o.norm ? gain_slots(o.K) : 0u))
+          bad(fmt("cu %d op %u: slot count", c, i));
       }
       if (o.opcode == OP_MMV) {
         const uint32_t ntiles = (o.epi == EPI_SWIGLU ? 2 : 1) * ((o.nrows + 15) / 16);
