@@ -126,6 +126,23 @@ mk_status mk_create(const mk_model_desc* desc, const mk_weights* weights, const 
 mk_status mk_decode_step(mk_ctx* ctx, const int32_t* tokens, const int32_t* positions, const int32_t* ctx_lens,
                          int32_t batch, float* logits_out, void* hip_stream);
 
+/* n_steps greedy decode steps in ONE launch, the token fed back on the GPU.  The launch count
+ * per decoded token is what the Muse Spark megakernel posts (khabar-ai page, the post on SGLang
+ * megakernels: launches per decode step) cut; the greedy choice is the argmax the ForgeMegakernel
+ * abstract's decode produces token by token.  Step s (0 <= s < n_steps) of sequence b consumes
+ * tokens[b] (s = 0) or tokens_out[s-1][b] at position positions[b] + s with ctx_lens[b] + s cached
+ * tokens, exactly as n_steps calls of mk_decode_step would, and writes
+ *   logits_out[s][b][vocab]  fp32, device, 16-byte aligned, n_steps * batch * vocab floats;
+ *   tokens_out[s][b]         int32, device, 16-byte aligned: argmax of that step's logits (ties
+ *                            to the lowest index; -1 where the row was out of contract).
+ * Pages for positions[b] .. positions[b] + n_steps - 1 must be mapped.  1 <= n_steps <=
+ * MK_MAX_STEPS.  Asynchronous on hip_stream; errors as for mk_decode_step (a row that leaves the
+ * contract at some step -- its position past max_ctx, an unmapped page -- raises the sticky
+ * MK_ERR_DEVICE_INPUT and gets NaN logits from that step on). */
+#define MK_MAX_STEPS 4096
+mk_status mk_decode_steps(mk_ctx* ctx, const int32_t* tokens, const int32_t* positions, const int32_t* ctx_lens,
+                          int32_t batch, int32_t n_steps, float* logits_out, int32_t* tokens_out, void* hip_stream);
+
 /* mk_create for callers that cannot allocate device memory (code under HIP graph capture,
  * allocation-free serving loops, harnesses that forbid hipMalloc): the same context, with the
  * library's static device scratch of MK_STATIC_SCRATCH_BYTES as its workspace instead of a

@@ -76,8 +76,9 @@ MK_EMU_COUNTERS, MK_EMU_IDLE_ITEMS_SILENT, MK_EMU_DEAD_ROWS_SILENT, MK_EMU_STALL
 
 EXPORTED = ["mk_workspace_size", "mk_create", "mk_decode_step", "mk_sync_status", "mk_reset", "mk_last_error",
             "mk_destroy", "mk_plan", "mk_emulate", "mk_copy_midstate", "mk_trace_words", "mk_copy_trace",
-            "mk_create_static"]
+            "mk_create_static", "mk_decode_steps"]
 MK_STATIC_SCRATCH_BYTES = 64 << 20
+MK_MAX_STEPS = 4096
 TRACE_WORDS = 8  # per-op trace record (mk_internal.h)
 
 _lib = None
@@ -97,6 +98,7 @@ def lib() -> ctypes.CDLL:
         L.mk_create_static.argtypes = [ctypes.POINTER(mk_model_desc), ctypes.POINTER(mk_weights),
                                        ctypes.POINTER(mk_kv_cache), ctypes.POINTER(P)]
         L.mk_decode_step.argtypes = [P, P, P, P, I32, P, P]
+        L.mk_decode_steps.argtypes = [P, P, P, P, I32, I32, P, P, P]
         L.mk_sync_status.argtypes = [P]
         L.mk_reset.argtypes = [P]
         L.mk_last_error.argtypes = []
@@ -109,7 +111,7 @@ def lib() -> ctypes.CDLL:
         L.mk_copy_midstate.argtypes = [P, I32, I32, P, ctypes.c_size_t, P]
         L.mk_trace_words.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         L.mk_copy_trace.argtypes = [P, P, ctypes.c_size_t]
-        for f in ("mk_workspace_size", "mk_create", "mk_create_static", "mk_decode_step", "mk_sync_status", "mk_reset", "mk_plan",
+        for f in ("mk_workspace_size", "mk_create", "mk_create_static", "mk_decode_step", "mk_decode_steps", "mk_sync_status", "mk_reset", "mk_plan",
                   "mk_emulate", "mk_copy_midstate", "mk_trace_words", "mk_copy_trace"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -187,6 +189,12 @@ def mk_create_static(desc, weights: mk_weights, cache: mk_kv_cache) -> int:
 def mk_decode_step(ctx: int, tokens_ptr: int, positions_ptr: int, ctx_lens_ptr: int, batch: int, logits_ptr: int,
                    stream: int = 0) -> int:
     return lib().mk_decode_step(ctx, tokens_ptr, positions_ptr, ctx_lens_ptr, batch, logits_ptr, stream or None)
+
+
+def mk_decode_steps(ctx: int, tokens_ptr: int, positions_ptr: int, ctx_lens_ptr: int, batch: int, n_steps: int,
+                    logits_ptr: int, tokens_out_ptr: int, stream: int = 0) -> int:
+    return lib().mk_decode_steps(ctx, tokens_ptr, positions_ptr, ctx_lens_ptr, batch, n_steps, logits_ptr,
+                                 tokens_out_ptr, stream or None)
 
 
 def mk_sync_status(ctx: int) -> int:
@@ -309,6 +317,21 @@ class DecodeContext:
         """Enqueue one decode step reading the device arrays self.tokens / positions / ctx_lens as they are."""
         return mk_decode_step(self.ctx, self.tokens.data_ptr(), self.positions.data_ptr(), self.ctx_lens.data_ptr(),
                               batch, self.logits.data_ptr(), self.stream_ptr(stream))
+
+    def steps(self, tokens, positions, ctx_lens, n_steps: int, stream=None):
+        """Enqueue n_steps greedy decode steps in one launch from host lists.  Returns (status,
+        logits [n_steps][batch][vocab], tokens_out [n_steps][batch]): device tensors this call
+        allocates, valid once the stream has run the launch."""
+        B = len(tokens)
+        T = self.torch
+        self.tokens[:B].copy_(T.as_tensor(list(tokens), dtype=T.int32))
+        self.positions[:B].copy_(T.as_tensor(list(positions), dtype=T.int32))
+        self.ctx_lens[:B].copy_(T.as_tensor(list(ctx_lens), dtype=T.int32))
+        logits = T.empty((n_steps, B, self.shape["vocab"]), dtype=T.float32, device=self.device)
+        toks = T.empty((n_steps, B), dtype=T.int32, device=self.device)
+        rc = mk_decode_steps(self.ctx, self.tokens.data_ptr(), self.positions.data_ptr(), self.ctx_lens.data_ptr(),
+                             B, n_steps, logits.data_ptr(), toks.data_ptr(), self.stream_ptr(stream))
+        return rc, logits, toks
 
     def sync(self) -> int:
         return mk_sync_status(self.ctx)

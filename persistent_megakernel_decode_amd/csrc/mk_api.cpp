@@ -24,6 +24,10 @@ extern "C" __global__ void mk_megakernel_b1_trace(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_b2_trace(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_b4_trace(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_b8_trace(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_steps_b1(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_steps_b2(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_steps_b4(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_steps_b8(mk::KArgs A);
 
 namespace {
 
@@ -55,6 +59,15 @@ const void* kernel_for(int B, bool traced) {
   }
 }
 
+const void* steps_kernel_for(int B) {
+  switch (B) {
+    case 1: return (const void*)mk_megakernel_steps_b1;
+    case 2: return (const void*)mk_megakernel_steps_b2;
+    case 4: return (const void*)mk_megakernel_steps_b4;
+    default: return (const void*)mk_megakernel_steps_b8;
+  }
+}
+
 __global__ void fill_u32(uint32_t* p, size_t n, uint32_t v) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -82,11 +95,12 @@ struct mk_ctx {
   size_t ws_bytes = 0;
   mk::KArgs args{};
   uint32_t epoch = 0;
-  uint32_t tag = 0;  // launch tag of the last launch (activation parity = bit 0)
+  uint32_t tag = 0;  // tag of the last step run (activation parity = bit 0)
   uint32_t max_stage_ops = 1;
   hipStream_t last_stream = nullptr;
   mk_status sticky = MK_OK;
-  const void* kernel = nullptr;
+  const void* kernel = nullptr;        // one decode step per launch
+  const void* kernel_steps = nullptr;  // several steps per launch, tokens chosen on the device
   bool plain_launch = false;
   uint32_t* trace = nullptr;  // MK_TRACE=1: the workspace's trace section, TRACE_WORDS per op
   uint64_t static_gen = 0;    // mk_create_static: the device scratch generation this context owns (0 = own workspace)
@@ -253,11 +267,13 @@ static mk_status create_impl(const mk_model_desc* desc, const mk_weights* w, con
   const char* trace_env = getenv("MK_TRACE");
   const bool traced = trace_env && atoi(trace_env) != 0;
   ctx->kernel = kernel_for(P.kernel_batch, traced);
+  ctx->kernel_steps = steps_kernel_for(P.kernel_batch);
 
   // one resident workgroup per compute unit is required by the persistent design
-  int per_cu = 0;
+  int per_cu = 0, per_cu_steps = 0;
   hipError_t he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ctx->kernel, mk::NTHREADS, 0);
-  if (he != hipSuccess || per_cu < 1) {
+  if (he == hipSuccess) he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_steps, ctx->kernel_steps, mk::NTHREADS, 0);
+  if (he != hipSuccess || per_cu < 1 || per_cu_steps < 1) {
     delete ctx;
     return fail(MK_ERR_UNSUPPORTED, "the megakernel cannot be resident on a compute unit");
   }
@@ -313,6 +329,11 @@ static mk_status create_impl(const mk_model_desc* desc, const mk_weights* w, con
   A.nh = d.n_delta_heads; A.dk = d.delta_dk; A.dv = d.delta_dv; A.C = m.C; A.convw = d.conv_width;
   A.n_cus = ncu; A.n_items = P.n_items; A.mix = P.mix_dim;
   A.rms_eps = d.rms_eps;
+  A.n_steps = 1;  // mk_decode_steps overrides these four
+  A.n_lm = P.n_lm;
+  A.tokens_out = nullptr;
+  A.step_done = (uint32_t*)(ctx->ws + Y.step_done);
+  A.amax = nullptr;
   double ms = 2000.0;
   // diagnostic only; the tests set a tiny limit to force the timeout path from the host
   if (const char* s = getenv("MK_WATCHDOG_MS")) ms = std::max(0.001, atof(s));
@@ -377,8 +398,9 @@ static mk_status zero_counters(mk_ctx* ctx, hipStream_t s) {
   return MK_OK;
 }
 
-mk_status mk_decode_step(mk_ctx* ctx, const int32_t* tokens, const int32_t* positions, const int32_t* ctx_lens,
-                         int32_t batch, float* logits_out, void* hip_stream) {
+// Checks shared by both decode entry points.  Returns MK_OK or the failure (with its message set).
+static mk_status check_step_args(mk_ctx* ctx, const int32_t* tokens, const int32_t* positions, const int32_t* ctx_lens,
+                                 int32_t batch, const float* logits_out) {
   if (!ctx) return fail(MK_ERR_INVALID_ARG, "ctx is null");
   if (ctx->sticky != MK_OK) return fail(MK_ERR_STATE, "context holds a device error; call mk_reset");
   if (!tokens || !positions || !ctx_lens || !logits_out) return fail(MK_ERR_INVALID_ARG, "null input or output pointer");
@@ -386,34 +408,68 @@ mk_status mk_decode_step(mk_ctx* ctx, const int32_t* tokens, const int32_t* posi
     return fail(MK_ERR_INVALID_ARG, "inputs and logits must be 16-byte aligned");
   if (batch < 1 || batch > ctx->shape.d.max_batch)
     return fail(MK_ERR_INVALID_ARG, "batch " + std::to_string(batch) + " outside [1, max_batch]");
-  std::unique_lock<std::mutex> lk(ctx->busy, std::try_to_lock);
-  if (!lk.owns_lock()) return fail(MK_ERR_STATE, "another thread is stepping this context");
-  MK_CHECK_SCRATCH(ctx);
-  hipStream_t s = (hipStream_t)hip_stream;
+  return MK_OK;
+}
+
+// One launch of `n_steps` decode steps (the caller holds ctx->busy).  Step s of the launch uses tag
+// A.tag + s and counter epoch A.epoch + s.
+static mk_status launch_steps(mk_ctx* ctx, mk::KArgs& A, uint32_t n_steps, const void* kernel, hipStream_t s) {
   // counters count cumulatively (epoch * ops); restart the epochs long before 32-bit overflow
-  if ((uint64_t)(ctx->epoch + 1) * ctx->max_stage_ops >= (1ull << 31)) {
+  if ((uint64_t)(ctx->epoch + n_steps) * ctx->max_stage_ops >= (1ull << 31)) {
     mk_status r = zero_counters(ctx, s);
     if (r != MK_OK) return r;
     ctx->epoch = 0;
   }
+  A.epoch = ctx->epoch + 1;
+  // consecutive steps alternate the parity; the 31-bit tag restarts at 1 or 2 to keep it so
+  A.tag = (uint64_t)ctx->tag + n_steps <= 0x7FFFFFFFu ? ctx->tag + 1 : (ctx->tag & 1u) ? 2u : 1u;
+  void* kargs[] = {&A};
+  hipError_t e = ctx->plain_launch
+                     ? hipLaunchKernel(kernel, dim3(ctx->plan.n_cus), dim3(mk::NTHREADS), kargs, 0, s)
+                     : hipLaunchCooperativeKernel(kernel, dim3(ctx->plan.n_cus), dim3(mk::NTHREADS), kargs, 0, s);
+  if (e != hipSuccess) return hip_fail(e, ctx->plain_launch ? "hipLaunchKernel" : "hipLaunchCooperativeKernel");
+  ctx->epoch += n_steps;
+  ctx->tag = A.tag + n_steps - 1;
+  ctx->last_stream = s;
+  return MK_OK;
+}
+
+mk_status mk_decode_step(mk_ctx* ctx, const int32_t* tokens, const int32_t* positions, const int32_t* ctx_lens,
+                         int32_t batch, float* logits_out, void* hip_stream) {
+  mk_status r = check_step_args(ctx, tokens, positions, ctx_lens, batch, logits_out);
+  if (r != MK_OK) return r;
+  std::unique_lock<std::mutex> lk(ctx->busy, std::try_to_lock);
+  if (!lk.owns_lock()) return fail(MK_ERR_STATE, "another thread is stepping this context");
+  MK_CHECK_SCRATCH(ctx);
   mk::KArgs A = ctx->args;
   A.tokens = tokens;
   A.positions = positions;
   A.ctx_lens = ctx_lens;
   A.logits = logits_out;
   A.batch = batch;
-  A.epoch = ctx->epoch + 1;
-  // consecutive launches alternate the parity; the 31-bit tag restarts at 1 or 2 to keep it so
-  A.tag = ctx->tag + 1 <= 0x7FFFFFFFu ? ctx->tag + 1 : (ctx->tag & 1u) ? 2u : 1u;
-  void* kargs[] = {&A};
-  hipError_t e = ctx->plain_launch
-                     ? hipLaunchKernel(ctx->kernel, dim3(ctx->plan.n_cus), dim3(mk::NTHREADS), kargs, 0, s)
-                     : hipLaunchCooperativeKernel(ctx->kernel, dim3(ctx->plan.n_cus), dim3(mk::NTHREADS), kargs, 0, s);
-  if (e != hipSuccess) return hip_fail(e, ctx->plain_launch ? "hipLaunchKernel" : "hipLaunchCooperativeKernel");
-  ctx->epoch += 1;
-  ctx->tag = A.tag;
-  ctx->last_stream = s;
-  return MK_OK;
+  return launch_steps(ctx, A, 1, ctx->kernel, (hipStream_t)hip_stream);
+}
+
+mk_status mk_decode_steps(mk_ctx* ctx, const int32_t* tokens, const int32_t* positions, const int32_t* ctx_lens,
+                          int32_t batch, int32_t n_steps, float* logits_out, int32_t* tokens_out, void* hip_stream) {
+  mk_status r = check_step_args(ctx, tokens, positions, ctx_lens, batch, logits_out);
+  if (r != MK_OK) return r;
+  if (!tokens_out || !aligned16(tokens_out)) return fail(MK_ERR_INVALID_ARG, "tokens_out must be a 16-byte aligned device pointer");
+  if (n_steps < 1 || n_steps > MK_MAX_STEPS)
+    return fail(MK_ERR_INVALID_ARG, "n_steps " + std::to_string(n_steps) + " outside [1, MK_MAX_STEPS]");
+  std::unique_lock<std::mutex> lk(ctx->busy, std::try_to_lock);
+  if (!lk.owns_lock()) return fail(MK_ERR_STATE, "another thread is stepping this context");
+  MK_CHECK_SCRATCH(ctx);
+  mk::KArgs A = ctx->args;
+  A.tokens = tokens;
+  A.positions = positions;
+  A.ctx_lens = ctx_lens;
+  A.logits = logits_out;
+  A.batch = batch;
+  A.n_steps = n_steps;
+  A.tokens_out = tokens_out;
+  A.amax = (uint32_t*)(ctx->ws + ctx->plan.lay.amax);
+  return launch_steps(ctx, A, (uint32_t)n_steps, ctx->kernel_steps, (hipStream_t)hip_stream);
 }
 
 mk_status mk_sync_status(mk_ctx* ctx) {

@@ -47,10 +47,11 @@ enum Epi : uint8_t { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 
 constexpr int16_t NO_STAGE = -1;
 constexpr uint32_t LAYER_ATTN = 0, LAYER_DELTA = 1;  // the values of mk_layer_kind
 
-// Op flags.  Every activation that crosses compute units carries the launch's parity in the
-// lowest mantissa bit of each fp32 value (row_ok carries the launch tag itself), and every such
-// value is written exactly once per launch, so an op can poll its inputs themselves instead of a
-// stage counter (OPF_TAGGED_IN).  A stage that no op waits on by counter skips its signal and the
+// Op flags.  Every activation that crosses compute units carries its decode step's parity in the
+// lowest mantissa bit of each fp32 value (row_ok carries the step's tag itself), and every such
+// value is written exactly once per step, so an op can poll its inputs themselves instead of a
+// stage counter (OPF_TAGGED_IN).  Step s of a launch has tag `tag + s`; launches are serialized and
+// the next one starts at the following tag, so consecutive steps always alternate the parity.  A stage that no op waits on by counter skips its signal and the
 // store-completion wait before it (OPF_NO_SIGNAL).
 constexpr uint32_t OPF_TAGGED_IN = 1u;
 constexpr uint32_t OPF_NO_SIGNAL = 2u;
@@ -156,11 +157,19 @@ struct KArgs {
   const int32_t* ctx_lens;
   float* logits;
   int32_t batch;
-  uint32_t epoch;
-  uint32_t tag;               // launch tag: bit 0 is the activation parity, row_ok holds tag << 1 | ok
+  uint32_t epoch;             // stage counters reach (epoch + s) * count at the end of step s
+  uint32_t tag;               // tag of step 0: bit 0 is the activation parity, row_ok holds tag << 1 | ok
   uint64_t spin_limit;        // watchdog, in s_memrealtime ticks (100 MHz)
   uint32_t spin_check_mask;   // the watchdog reads the clock once every (mask + 1) polls
   uint32_t* trace;            // MK_TRACE=1: TRACE_WORDS per op (see below); else null
+  // multi-step launches (the token fed back on the device): step s consumes the argmax of step
+  // s - 1 at positions + s, writes logits + s * batch * V; tag + s is step s's activation tag
+  int32_t n_steps;            // steps in this launch (>= 1)
+  int32_t n_lm;               // LM-head ops (argmax partials per sequence)
+  int32_t* tokens_out;        // [n_steps][batch] greedy token of each step, or null
+  uint32_t* step_done;        // [n_cus] tag of the last step whose stores this CU has completed
+  uint32_t* amax;             // [2][n_lm][max batch width][2] per-op (value bits, index) of the LM head,
+                              // double-buffered by step parity
 };
 
 // Per-op trace record of the traced kernels: {opcode << 16 | stage, start, inputs ready, end,

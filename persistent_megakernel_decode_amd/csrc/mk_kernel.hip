@@ -66,6 +66,12 @@ __shared__ __attribute__((aligned(16))) u32 g_consumed[NC];
 __shared__ u32 g_bar;           // compute-wave barrier counter
 __shared__ u32 g_abort;         // set on watchdog expiry: every wave leaves
 __shared__ u32 g_bcast[4];
+// The step the compute waves are on (a launch may run several decode steps, each consuming the
+// previous step's greedy token): its activation tag, its index (the loader streams step s only once
+// the compute waves are on it) and its tokens.
+__shared__ u32 g_ctag;
+__shared__ u32 g_cstep;
+__shared__ int g_tok[APLAN_MAXB];
 #if MK_TRACE_STAMPS
 __shared__ u32 g_trace_oi;  // queue index of the running op (written and read by compute wave 0 only)
 // loader stamps of op oi at [(oi % 64) * 3]: first issue, last issue, ticks blocked on a full ring
@@ -254,6 +260,20 @@ __device__ __forceinline__ u32 lds_ld(const u32* p) {
   return __builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
 }
 __device__ __forceinline__ bool aborted() { return lds_ld(&g_abort) != 0; }
+__device__ __forceinline__ u32 ctag() { return lds_ld(&g_ctag); }
+__device__ __forceinline__ u32 cstep() { return lds_ld(&g_cstep); }
+// This step's context length, position and token of sequence b.  A launch value below the range
+// stays as it is and a sum past INT32_MAX saturates, so a row out of range at step 0 stays out of
+// range (and is rejected by the range checks) at every step.
+__device__ __forceinline__ int step_add(int v, int lo, u32 step) {
+  return v < lo ? v : (int)min((u32)v + step, 0x7FFFFFFFu);
+}
+__device__ __forceinline__ int step_ctx(const KArgs& A, int b) { return step_add(A.ctx_lens[b], 1, cstep()); }
+__device__ __forceinline__ int step_pos(const KArgs& A, int b) { return step_add(A.positions[b], 0, cstep()); }
+__device__ __forceinline__ int step_tok(int b) { return (int)lds_ld((const u32*)&g_tok[b]); }  // b uniform
+__device__ __forceinline__ int lane_tok(int b) {  // b may differ from lane to lane
+  return __hip_atomic_load(&g_tok[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
 // LDS read for the loader wave.  The compiler cannot tell that the ring (the only LDS the
 // DMA writes) and the control words are distinct, and would drain every outstanding DMA
@@ -337,7 +357,7 @@ __device__ __forceinline__ bool wait_full(const KArgs& A, u32 seq) {
 // Bounded wait for a tagged value: returns `v` once it (or a re-read of `p`) shows this launch's
 // parity; past the watchdog limit the timeout is raised and the last value returned.
 __device__ __forceinline__ float tagged_fix(const KArgs& A, const float* p, float v) {
-  const u32 par = A.tag & 1u;
+  const u32 par = ctag() & 1u;
   if (tag_ok(v, par)) return v;
   Watchdog wd(A);
   do {
@@ -350,7 +370,7 @@ __device__ __forceinline__ float tagged_fix(const KArgs& A, const float* p, floa
 __device__ __forceinline__ float ld_tagged(const KArgs& A, const float* p) { return tagged_fix(A, p, ld_sc1(p)); }
 // row_ok[b] holds tag << 1 | ok, written once per launch by EMBED: wait for this launch's entry.
 __device__ __forceinline__ bool row_ok_wait(const KArgs& A, int b) {
-  const u32 want = A.tag & 0x7FFFFFFFu;
+  const u32 want = ctag() & 0x7FFFFFFFu;
   u32 v = (u32)ld_i32_sc1(A.row_ok + b);
   Watchdog wd(A);
   while ((v >> 1) != want) {
@@ -362,7 +382,7 @@ __device__ __forceinline__ bool row_ok_wait(const KArgs& A, int b) {
 }
 // The same for an entry loaded earlier (`v`), so that the load overlaps other work.
 __device__ __forceinline__ bool row_ok_fix(const KArgs& A, int b, int32_t v) {
-  return ((u32)v >> 1) == (A.tag & 0x7FFFFFFFu) ? (v & 1) != 0 : row_ok_wait(A, b);
+  return ((u32)v >> 1) == (ctag() & 0x7FFFFFFFu) ? (v & 1) != 0 : row_ok_wait(A, b);
 }
 
 // Traced kernels: stamp "inputs in hand" for the running op (compute wave 0, lane 0 only).
@@ -382,7 +402,7 @@ __device__ __forceinline__ void release_upto(u32 w, u32 upto) {
 // A row is served only when its token, context length, position and current page are in range.
 __device__ bool row_ok_local(const KArgs& A, int b) {
   if (b >= A.batch) return false;
-  int tok = A.tokens[b], ctx = A.ctx_lens[b], pos = A.positions[b];
+  const int tok = step_tok(b), ctx = step_ctx(A, b), pos = step_pos(A, b);
   if (tok < 0 || tok >= A.V) return false;
   if (ctx < 1 || ctx > A.max_ctx || pos != ctx - 1) return false;
   if (!A.page_table) return true;  // no attention layers: no pages to check
@@ -393,23 +413,24 @@ __device__ bool row_ok_local(const KArgs& A, int b) {
 }
 
 // ------------------------------------------------------------------ attention work split
-// The launch's attention split (mk_attn_plan.h), built once per launch by the loader wave before it
-// streams anything and read from LDS by every wave: [0] ready flag, then the APLAN_WORDS plan words.
+// The step's attention split (mk_attn_plan.h), built once per step by the loader wave before it
+// streams the step and read from LDS by every wave: [0] step + 1 once ready, then the APLAN_WORDS
+// plan words.
 __shared__ int g_aplan[1 + APLAN_WORDS];
 
 __device__ __forceinline__ int clamp_ctx(const KArgs& A, int c) { return attn_clamp_ctx(c, A.max_ctx); }
 
-__device__ __forceinline__ void attn_plan_build(const KArgs& A, int pps) {
+__device__ __forceinline__ void attn_plan_build(const KArgs& A, int pps, u32 step) {
   int cv[APLAN_MAXB];
 #pragma unroll
-  for (int b = 0; b < APLAN_MAXB; ++b) cv[b] = b < A.batch ? clamp_ctx(A, sload(A.ctx_lens + b)) : 0;
+  for (int b = 0; b < APLAN_MAXB; ++b) cv[b] = b < A.batch ? clamp_ctx(A, step_add(sload(A.ctx_lens + b), 1, step)) : 0;
   const int K = A.Hkv > 0 ? A.n_items / A.Hkv : 0;  // chunks per KV head; >= batch by construction
   int plan[APLAN_WORDS];
   attn_plan_make(cv, K, pps, NC, plan);
   if (lane_id() == 0) {
 #pragma unroll
     for (int i = 0; i < APLAN_WORDS; ++i) g_aplan[1 + i] = plan[i];
-    __hip_atomic_store(&g_aplan[0], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_store(&g_aplan[0], (int)step + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }
 
@@ -417,7 +438,8 @@ __device__ __forceinline__ void attn_plan_build(const KArgs& A, int pps) {
 __device__ AttnItem attn_item(const KArgs& A, u32 item, int pps) {
   (void)pps;
   Watchdog wd(A);
-  while (lds_ld((const u32*)&g_aplan[0]) == 0) {
+  const u32 want = cstep() + 1;  // the plan of the compute waves' step
+  while (lds_ld((const u32*)&g_aplan[0]) != want) {
     if (aborted() || wd.expired()) return AttnItem{0, 0, 0, 0, 0, 0, false};
     __builtin_amdgcn_s_sleep(1);
   }
@@ -721,13 +743,30 @@ __device__ __forceinline__ void loader_lds_store(u32* p, u32 v) {
 }
 #endif
 
+template <bool MS>
 __device__ __forceinline__ void loader(const KArgs& A0, u32 q0, u32 q1) {
   const KArgs& A = A0;
   u32 seq = 0, marked = 0, limit = NSLOT;  // slots below `limit` may be filled
   const u32 lane16 = lane_id() * 16;
-  attn_plan_build(A, A.d == 64 ? 32 : 16);
-  ItemCache ic;
   const AttnLanes al = attn_lanes(A.d == 64 ? 64u : 128u);
+  const u32 nsteps = MS ? (u32)A.n_steps : 1u;
+  for (u32 step = 0; step < nsteps; ++step) {
+  if (step > 0) {
+    // Step s streams once the compute waves are on it: they reach it only when every compute unit
+    // has finished step s - 1, so the recurrent states this CU streams are the updated ones.  What
+    // has landed is published first (the compute waves need it to finish the previous step).
+    while (marked < seq) {
+      wait_oldest(seq - marked);
+      publish_filled(++marked);
+    }
+    Watchdog wd(A);
+    while (lds_ld_loader(&g_cstep) < step) {
+      if (aborted_loader() || wd.expired()) return;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  attn_plan_build(A, A.d == 64 ? 32 : 16, step);
+  ItemCache ic;
   for (u32 oi = q0; oi < q1; ++oi) {
     const KArgs& A = kargs();
     const Op o = sload(A.ops + oi);
@@ -805,6 +844,7 @@ __device__ __forceinline__ void loader(const KArgs& A0, u32 q0, u32 q1) {
     }
 #endif
   }
+  }
   while (marked < seq) {
     wait_oldest(seq - marked);
     publish_filled(++marked);
@@ -816,7 +856,7 @@ __device__ __forceinline__ bool wait_stage(const KArgs& A, int stage) {
   const u32 lane = lane_id();
   const Stage st = sload(A.stages + stage);
   const u32 per = st.nops / NSUB, rem = st.nops % NSUB;
-  const u32 tgt = A.epoch * (per + (lane < rem ? 1u : 0u));
+  const u32 tgt = (A.epoch + cstep()) * (per + (lane < rem ? 1u : 0u));  // counters count every step
   const u32* c = A.counters + (size_t)stage * NSUB * CTR_STRIDE + (size_t)(lane % NSUB) * CTR_STRIDE;
   Watchdog wd(A);
   while (true) {
@@ -837,11 +877,11 @@ __device__ __forceinline__ void signal_stage(const KArgs& A, int stage, u32 inde
 // b >= batch or a bad token are zero), tagged.
 template <int B>
 __device__ __forceinline__ void op_embed(const KArgs& A, u32 w) {
-  const u32 t = w * 64 + lane_id(), par = A.tag & 1u;
+  const u32 t = w * 64 + lane_id(), par = ctag() & 1u;
   const int cu = (int)blockIdx.x;
   const int h0 = (int)((int64_t)A.H * cu / A.n_cus), h1 = (int)((int64_t)A.H * (cu + 1) / A.n_cus);
   for (int b = 0; b < B; ++b) {
-    const int tok = b < A.batch ? A.tokens[b] : -1;
+    const int tok = b < A.batch ? step_tok(b) : -1;
     const bool ok = tok >= 0 && tok < A.V;
     for (int h = h0 + (int)t; h < h1; h += NC * 64)
       st_tag(A.x0 + (size_t)b * A.H + h, ok ? bf2f(A.embed[(size_t)tok * A.H + h]) : 0.0f, par);
@@ -852,7 +892,7 @@ __device__ __forceinline__ void op_embed(const KArgs& A, u32 w) {
   // tagged value is written exactly once per launch and o_proj can poll every row.
   bool live[B];
 #pragma unroll
-  for (int b = 0; b < B; ++b) live[b] = b < A.batch && clamp_ctx(A, A.ctx_lens[b]) > 0;
+  for (int b = 0; b < B; ++b) live[b] = b < A.batch && clamp_ctx(A, step_ctx(A, b)) > 0;
   for (int l = 0; l < A.n_layers; ++l) {
     const LayerDesc Ld = sload(A.layers + l);
     const int wdt = (int)Ld.mix_width;
@@ -866,6 +906,67 @@ __device__ __forceinline__ void op_embed(const KArgs& A, u32 w) {
   }
 }
 
+// The greedy token of each sequence from the LM head's per-op partials of a finished step: the
+// largest logit, ties to the lowest index; -1 when no op saw a valid row.  Every thread of the
+// compute waves takes part; the result is left in g_tok.  Runs while g_cstep still names the
+// finished step, whose partials sit in the half of amax of its parity: the next step's LM head
+// writes the other half, so a unit still reading them cannot see the next step's values, and the
+// step after that starts only once every unit has passed this point.  Passes two compute barriers
+// (the caller advances its barrier count by 2 NC, the count being taken by value); returns false
+// on abort.
+__device__ __forceinline__ bool argmax_tokens(const KArgs& A, u32 w, u32 gen) {
+  const u32 tid = w * 64 + lane_id();
+  for (int b = 0; b < A.batch; ++b) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int j = (int)tid; j < A.n_lm; j += NC * 64) {
+      const u32* e = A.amax + (((size_t)(cstep() & 1u) * A.n_lm + j) * APLAN_MAXB + b) * 2;
+      const float v = __builtin_bit_cast(float, ld_u32_sc1(e));
+      const int i = (int)ld_u32_sc1(e + 1);
+      if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if (lane_id() == 0) {
+      g_scr[(w * APLAN_MAXB + b) * 2] = bv;
+      g_scr[(w * APLAN_MAXB + b) * 2 + 1] = __builtin_bit_cast(float, bi);
+    }
+  }
+  if (!cbar(A, gen)) return false;
+  const int b = (int)lane_id();
+  if (w == 0 && b < A.batch) {
+    float v = g_scr[b * 2];
+    int i = __builtin_bit_cast(int, g_scr[b * 2 + 1]);
+    for (int j = 1; j < NC; ++j) {
+      const float ov = g_scr[(j * APLAN_MAXB + b) * 2];
+      const int oi = __builtin_bit_cast(int, g_scr[(j * APLAN_MAXB + b) * 2 + 1]);
+      if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+    }
+    g_tok[b] = v > -INFINITY && i < A.V ? i : -1;
+  }
+  return cbar(A, gen);
+}
+
+// Step s >= 1 starts when every compute unit has completed step s - 1 -- its stores included:
+// each one waits for its memory operations to finish and then publishes the step's tag in
+// step_done -- so that this step reads the states (KV rows, conv states) the previous one wrote,
+// and every activation cell holds the previous step's value until this step writes it.  Returns
+// false on abort.
+__device__ __forceinline__ bool step_barrier(const KArgs& A, u32 tag_prev) {
+  Watchdog wd(A);
+  for (int c = (int)lane_id(); c < A.n_cus; c += 64) {
+    while (ld_u32_sc1(A.step_done + c) != tag_prev) {
+      if (aborted() || wd.expired()) return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  return true;
+}
+
 // Second phase of EMBED, CU 0 only: validate every row (token, context, position, every page of
 // [0, ctx) mapped), publish row_ok and raise ST_BAD_INPUT for out-of-contract rows.
 __device__ __forceinline__ void op_embed_finish(const KArgs& A, u32 w, u32& gen) {
@@ -874,7 +975,7 @@ __device__ __forceinline__ void op_embed_finish(const KArgs& A, u32 w, u32& gen)
     bool ok = row_ok_local(A, b);
     float bad = 0.0f;
     if (ok && A.page_table) {
-      const int npg = (A.ctx_lens[b] + A.page_size - 1) / A.page_size;
+      const int npg = (step_ctx(A, b) + A.page_size - 1) / A.page_size;
       if (npg > A.max_pages_per_seq) bad = 1.0f;
       for (int p = (int)(w * 64 + lane_id()); p < npg && bad == 0.0f; p += NC * 64) {
         const int pg = A.page_table[(size_t)b * A.max_pages_per_seq + p];
@@ -888,7 +989,7 @@ __device__ __forceinline__ void op_embed_finish(const KArgs& A, u32 w, u32& gen)
       float any = 0.0f;
       for (int j = 0; j < NC; ++j) any = fmaxf(any, g_scr[j]);
       const bool final_ok = ok && any == 0.0f;
-      __hip_atomic_store(A.row_ok + b, (int32_t)((A.tag << 1) | (final_ok ? 1u : 0u)), __ATOMIC_RELAXED,
+      __hip_atomic_store(A.row_ok + b, (int32_t)((ctag() << 1) | (final_ok ? 1u : 0u)), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
       if (b < A.batch && !final_ok) raise_status(A, ST_BAD_INPUT);
     }
@@ -916,6 +1017,42 @@ __device__ __forceinline__ float row_sum16(float v) {
   v += dppf<0x4E>(v);
   v += dppf<0x141>(v);
   return v + dppf<0x140>(v);
+}
+
+// LM head: this op's largest logit per sequence (ties to the lowest row) into amax, for the next
+// step's token.  (v, i): this thread's candidate for sequence `b`, v = -inf when it has none; the
+// lanes holding candidates of one sequence are those equal modulo `lanes_mod` (1 or 8).  Uses g_scr
+// after a barrier.  Returns false on abort.
+__device__ __forceinline__ void amax_better(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+}
+template <int NB>  // sequences handled at once: candidates v[b], i[b] for b < NB
+__device__ __forceinline__ bool op_amax(const KArgs& A, const Op& o, u32 w, u32& gen, float* v, int* i, int lanes_mod) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    for (int off = 32; off >= lanes_mod; off >>= 1) amax_better(v[b], i[b], __shfl_xor(v[b], off, 64), __shfl_xor(i[b], off, 64));
+  if (!cbar(A, gen)) return false;  // g_scr may still be read by the epilogue
+  const u32 lane = lane_id();
+  constexpr int M = APLAN_MAXB;  // g_scr entries per wave: one (value, index) pair per sequence
+  if (lanes_mod == 1) {
+    if (lane == 0)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) { g_scr[(w * M + b) * 2] = v[b]; g_scr[(w * M + b) * 2 + 1] = __builtin_bit_cast(float, i[b]); }
+  } else if (lane < (u32)lanes_mod) {  // lane b holds sequence b
+    g_scr[(w * M + lane) * 2] = v[0];
+    g_scr[(w * M + lane) * 2 + 1] = __builtin_bit_cast(float, i[0]);
+  }
+  if (!cbar(A, gen)) return false;
+  const int nseq = lanes_mod == 1 ? NB : lanes_mod;
+  if (w == 0 && (int)lane < nseq && (int)lane < A.batch) {
+    float bv = g_scr[lane * 2];
+    int bi = __builtin_bit_cast(int, g_scr[lane * 2 + 1]);
+    for (int j = 1; j < NC; ++j) amax_better(bv, bi, g_scr[(j * M + lane) * 2], __builtin_bit_cast(int, g_scr[(j * M + lane) * 2 + 1]));
+    u32* e = A.amax + (((size_t)(cstep() & 1u) * A.n_lm + o.sig_index) * APLAN_MAXB + lane) * 2;
+    __hip_atomic_store(gptr(e), __builtin_bit_cast(u32, bv), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(gptr(e + 1), (u32)bi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return true;
 }
 
 // ------------------------------------------------------------------ GEMV (matrix cores, batch <= 4)
@@ -1047,7 +1184,7 @@ struct GemvAcc<1, 8> {
 // One GEMV op with NF input fragments per wave (1, 2, or up to 8).  Row groups are taken GB at a
 // time (GB NF = 4 slots per wait for NF <= 2).  With PG < 8 pieces per group (NF = 1) a slot holds
 // 8 / PG groups and wave w works on group (slot 8 / PG + w / PG), piece w % PG.
-template <int B, int P, int NF>
+template <int B, int P, int NF, bool AM>  // AM: track the LM head's greedy partials (multi-step kernels)
 __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
   constexpr u32 R = 16 / P, KP = 32 * P;
   constexpr u32 GB = NF == 1 ? 4 : (NF == 2 ? 2 : 1);
@@ -1125,7 +1262,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
     release_upto(w, seq + nst);
   }
   // residual rows of this thread (epilogue row r = thread index), fetched now, off the critical path
-  const u32 tid = w * 64 + lane, par = A.tag & 1u;
+  const u32 tid = w * 64 + lane, par = ctag() & 1u;
   float rv[B];
 #pragma unroll
   for (int b = 0; b < B; ++b)
@@ -1317,6 +1454,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   bool okb[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) okb[b] = epi == EPI_LOGITS && b < A.batch && row_ok_fix(A, b, __builtin_bit_cast(int32_t, rv[b]));
+  float* logits = A.logits + (size_t)cstep() * A.batch * A.V;  // this step's rows
   for (u32 r = tid; r < nrows; r += NC * 64) {
     const u32 row = row0 + r;
 #pragma unroll
@@ -1335,20 +1473,35 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
       } else if (epi == EPI_STORE) {
         st_tag((float*)outp + (size_t)b * ld_out + row, v, par);
       } else if (b < A.batch) {  // EPI_LOGITS
-        A.logits[(size_t)b * A.V + row] = okb[b] ? v : __builtin_nanf("");
+        logits[(size_t)b * A.V + row] = okb[b] ? v : __builtin_nanf("");
       }
     }
   }
-  return true;
+  if (!AM || epi != EPI_LOGITS || !A.amax) return true;
+  // on-device greedy choice: this thread's best row per sequence, from the sums still in LDS
+  float bv[B];
+  int bi[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    bv[b] = -INFINITY;
+    bi[b] = 0x7FFFFFFF;
+    if (!okb[b]) continue;
+    for (u32 r = tid; r < nrows; r += NC * 64) {
+      float v = 0.0f;
+      for (u32 j = 0; j < RW; ++j) v += g_red[(j * B + b) * nrt + r];
+      amax_better(bv[b], bi[b], v * rstd[b], (int)(row0 + r));
+    }
+  }
+  return op_amax<B>(A, o, w, gen, bv, bi, 1);
 }
 
-template <int B>
+template <int B, bool AM>
 __device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
   constexpr int P = GemvWidth<B>::P;
   const u32 pg = o.ppr;
-  if (pg <= 8) return op_gemv_nf<B, P, 1>(A, o, w, seq, gen);
-  if (pg == 16) return op_gemv_nf<B, P, 2>(A, o, w, seq, gen);
-  return op_gemv_nf<B, P, 8>(A, o, w, seq, gen);
+  if (pg <= 8) return op_gemv_nf<B, P, 1, AM>(A, o, w, seq, gen);
+  if (pg == 16) return op_gemv_nf<B, P, 2, AM>(A, o, w, seq, gen);
+  return op_gemv_nf<B, P, 8, AM>(A, o, w, seq, gen);
 }
 
 // ------------------------------------------------------------------ MATRIX-CORE GEMV (batch 8)
@@ -1359,7 +1512,7 @@ __device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32&
 // partial sums are added in LDS, four tiles per pass.  RMSNorm factors out of the sum: the tiles
 // multiply x * gain, each lane accumulates x^2 on the side, and the epilogue scales by
 // (mean x^2 + eps)^-1/2.
-template <int B>
+template <int B, bool AM>
 __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
   static_assert(B <= 8 && NC == 8, "one pass holds 8 waves x 4 tiles x 16 rows x 8 columns");
   static_assert(NC * 4 * 16 * 8 <= RED_FLOATS, "MMV partial-sum area");
@@ -1383,6 +1536,8 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
 #pragma unroll
   for (int t = 0; t < MMV_TILES; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   float ssq = 0.0f;
+  float mbv = -INFINITY;  // LM head: this thread's best logit of its sequence (tid % B) and its row
+  int mbi = 0x7FFFFFFF;
 
   // this lane's inputs of segment ks: x[col][ks*256 + 32 w + 8 kq .. + 8] and their gains
   auto fetch = [&](u32 ks, float* xv, u32x4& gv) {
@@ -1395,7 +1550,7 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
     gv = (norm && ks < nks) ? *(const u32x4*)(gm + k0) : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   };
   // tagged inputs: wait until this lane's block of segment ks shows this launch's parity
-  const u32 par = A.tag & 1u;
+  const u32 par = ctag() & 1u;
   const bool tcheck = (flags & OPF_TAGGED_IN) && cval;
   auto ready = [&](u32 ks, float* xv) -> bool {
     const bool need = tcheck && ks < nks;
@@ -1482,12 +1637,13 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
     };
     const u32 row = (tid / B) % 16, b = tid % B;
     const int32_t rokb = __shfl(rok, (int)b, 64);  // row_ok[b] (all lanes active here)
+    float* logits = A.logits + (size_t)cstep() * A.batch * A.V;
     if (swiglu) {
       const u32 pr = tid / (16 * B);  // gate / up tile pair within the pass
       if (pr < 2 && (u32)(pp * 4) + 2 * pr + 1 < nt) {
         const float gv = colsum(2 * pr, row, b), uv = colsum(2 * pr + 1, row, b);
         const u32 orow = 16 * ((u32)(pp * 2) + pr) + row;
-        if (orow < nrows) st_tag((float*)outp + (size_t)b * ld_out + row0 + orow, silu(gv) * uv, A.tag & 1u);
+        if (orow < nrows) st_tag((float*)outp + (size_t)b * ld_out + row0 + orow, silu(gv) * uv, ctag() & 1u);
       }
     } else {
       const u32 tp = tid / (16 * B);
@@ -1497,17 +1653,19 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
         if (orow < nrows) {
           if (epi == EPI_RESID) {
             const float x = ld_tagged(A, (const float*)resp + (size_t)b * ld_out + grow);
-            st_tag((float*)outp + (size_t)b * ld_out + grow, x + v, A.tag & 1u);
+            st_tag((float*)outp + (size_t)b * ld_out + grow, x + v, ctag() & 1u);
           } else if (epi == EPI_STORE) {
-            st_tag((float*)outp + (size_t)b * ld_out + grow, v, A.tag & 1u);
+            st_tag((float*)outp + (size_t)b * ld_out + grow, v, ctag() & 1u);
           } else if ((int)b < A.batch) {  // EPI_LOGITS
             const bool ok = row_ok_fix(A, (int)b, rokb);
-            A.logits[(size_t)b * A.V + grow] = ok ? v : __builtin_nanf("");
+            logits[(size_t)b * A.V + grow] = ok ? v : __builtin_nanf("");
+            if (AM && ok) amax_better(mbv, mbi, v, (int)grow);
           }
         }
       }
     }
   }
+  if (AM && epi == EPI_LOGITS && A.amax) return op_amax<1>(A, o, w, gen, &mbv, &mbi, B);
   return true;
 }
 
@@ -1538,14 +1696,15 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
     // tagged value is written exactly once per launch: a later launch whose plan gives this item a
     // chunk then finds the previous launch's parity here until the real partial lands.
     float* part = (float*)Ld.part + (size_t)o.row0 * GMAX * (D + 4);
-    for (int t = (int)(w * 64 + lane); t < A.G * (D + 4); t += NC * 64) st_tag(part + t, 0.0f, A.tag & 1u);
+    for (int t = (int)(w * 64 + lane); t < A.G * (D + 4); t += NC * 64) st_tag(part + t, 0.0f, ctag() & 1u);
     return true;
   }
   const u32 ns = (u32)((it.p1 - it.p0 + PPS - 1) / PPS);
   const u32 seq0 = seq;
   seq += ns;
   const int G = A.G, b = it.b, kvh = it.kvh;
-  const int pos = A.positions[b];
+  const int pos = step_pos(A, b);
+  const int pos0 = A.positions[b];  // the launch's first position: rows [pos0, pos) were appended by its earlier steps
   const int32_t rok = ld_i32_sc1(A.row_ok + b);  // checked where it is used
   const bool tagged = (o.flags & OPF_TAGGED_IN) != 0;
   const int qkv_ld = (A.Hq + 2 * A.Hkv) * D;
@@ -1622,11 +1781,15 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
         kvn[(t - G) * D + lane * DPL + e] = bf2f(hb[e]);
       }
       if (row_ok_fix(A, b, rok)) {
+        // agent-coherent stores: a later step of the same launch may read the row on another CU
         const int pg = A.page_table[(size_t)b * A.max_pages_per_seq + pos / 16];
         const size_t off = (((size_t)pg * A.Hkv + kvh) * 16 + pos % 16) * D + lane * DPL;
         uint16_t* dp = (uint16_t*)(t == G ? Ld.k_pages : Ld.v_pages) + off;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) dp[e] = hb[e];
+        if constexpr (DPL == 2) {
+          __hip_atomic_store(gptr((u32*)dp), (u32)hb[0] | ((u32)hb[1] << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          __hip_atomic_store(gptr(dp), hb[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
   }
@@ -1645,6 +1808,7 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
 #pragma unroll
     for (int e = 0; e < DPL; ++e) ov[g][e] = 0.0f;
   release_upto(w, seq0 + min(w, ns));  // slots before this wave's first belong to other waves
+  const bool rows_ok = pos0 < pos && pos0 < it.p1 && row_ok_fix(A, b, rok);  // earlier steps' rows in this chunk
   for (u32 s = w; s < ns; s += NC) {
     const u32 sq = seq0 + s;
     if (!wait_full(A, sq)) return false;
@@ -1652,6 +1816,25 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
     char* vslot = kslot + 4096;
     const int pbase = it.p0 + (int)s * PPS;
     const int np = min(PPS, it.p1 - pbase);
+    // rows appended by this launch's earlier steps (on any CU): the loader may have streamed them
+    // before they were written, so they are re-read with agent-coherent loads and put into the slot
+    const int q1 = rows_ok ? min(pbase + np, pos) : 0;  // (pages of rows out of contract are not read)
+    for (int q = max(pbase, pos0); q < q1; ++q) {
+      const int r = q - pbase, d0 = (int)lane * DPL, c = d0 / 8;
+      const int pg = A.page_table[(size_t)b * A.max_pages_per_seq + q / 16];
+      const size_t off = (((size_t)pg * A.Hkv + kvh) * 16 + q % 16) * D + d0;
+      u16_alias* kd = (u16_alias*)(kslot + r * RB + ((c ^ (r % CPR)) * 16)) + (d0 % 8);
+      u16_alias* vd = (u16_alias*)(vslot + r * RB) + d0;
+      if constexpr (DPL == 2) {
+        const u32 kw = __hip_atomic_load(gptr((const u32*)((const uint16_t*)Ld.k_pages + off)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const u32 vw = __hip_atomic_load(gptr((const u32*)((const uint16_t*)Ld.v_pages + off)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        kd[0] = (uint16_t)kw; kd[1] = (uint16_t)(kw >> 16);
+        vd[0] = (uint16_t)vw; vd[1] = (uint16_t)(vw >> 16);
+      } else {
+        kd[0] = __hip_atomic_load(gptr((const uint16_t*)Ld.k_pages + off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        vd[0] = __hip_atomic_load(gptr((const uint16_t*)Ld.v_pages + off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
     if (has_new && pos >= pbase && pos < pbase + PPS) {
       // the new token's K/V are not in the cache the loader read: put them into the slot
       const int r = pos - pbase, d0 = (int)lane * DPL, c = d0 / 8;
@@ -1774,7 +1957,7 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   if (!cbar(A, gen)) return false;
   // partial of item i, head g: part[(i * GMAX + g) * (D + 4)] = m, l, -, -, o[0..D) (o 16-B aligned)
   float* part = (float*)Ld.part + (size_t)o.row0 * GMAX * (D + 4);
-  const u32 par = A.tag & 1u;
+  const u32 par = ctag() & 1u;
   for (int t = (int)(w * 64 + lane); t < G * D; t += NC * 64) {
     const int g = t / D, dim = t % D;
     float M = -INFINITY;
@@ -1909,7 +2092,7 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
 
   auto conv = [&](int c, float* newstate_last) -> float {  // causal conv of channel c with its window
     float acc = 0.0f;
-    for (int j = 0; j < W - 1; ++j) acc += bf2f(cw[(size_t)c * W + j]) * cst[(size_t)c * (W - 1) + j];
+    for (int j = 0; j < W - 1; ++j) acc += bf2f(cw[(size_t)c * W + j]) * ld_sc1(cst + (size_t)c * (W - 1) + j);
     const float x = rd(u + c);
     acc += bf2f(cw[(size_t)c * W + W - 1]) * x;
     *newstate_last = x;
@@ -1964,16 +2147,16 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
       oj = wave_sum(oj);
       if (ok) {
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) sdst[(size_t)r * DK + lane * DPL + e] = sv[e];
+        for (int e = 0; e < DPL; ++e) st_sc1(sdst + (size_t)r * DK + lane * DPL + e, sv[e]);
       }
       // every item writes its outputs (zero for a row out of contract), tagged
-      if (lane == 0) st_tag((float*)Ld.mix_o + (size_t)b * A.mix + h * A.dv + j0 + r, ok ? oj : 0.0f, A.tag & 1u);
+      if (lane == 0) st_tag((float*)Ld.mix_o + (size_t)b * A.mix + h * A.dv + j0 + r, ok ? oj : 0.0f, ctag() & 1u);
     }
     // rolling conv state of this slot's value channels
-    if (ok && (int)lane < RPS) {
+    if (ok && (int)lane < RPS) {  // (agent-coherent: the next step may run this block elsewhere)
       float* st = cst + (size_t)vch * (W - 1);
-      for (int j = 0; j + 1 < W - 1; ++j) st[j] = st[j + 1];
-      st[W - 2] = vx;
+      for (int j = 0; j + 1 < W - 1; ++j) st_sc1(st + j, ld_sc1(st + j + 1));
+      st_sc1(st + W - 2, vx);
     }
     (void)xq; (void)xk;
     release_upto(w, seq0 + min(s + NC, (u32)NSL));
@@ -1994,8 +2177,8 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
         const int c = t < DK ? h * DK + t : A.nh * DK + h * DK + (t - DK);
         const float x = rd(u + c);
         float* st = cst + (size_t)c * (W - 1);
-        for (int j = 0; j + 1 < W - 1; ++j) st[j] = st[j + 1];
-        st[W - 2] = x;
+        for (int j = 0; j + 1 < W - 1; ++j) st_sc1(st + j, ld_sc1(st + j + 1));
+        st_sc1(st + W - 2, x);
       }
     }
     if (w == 0 && lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2004,11 +2187,32 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
 }
 
 // ------------------------------------------------------------------ compute waves
-template <int B>
+// MS: the multi-step kernels (n_steps decode steps per launch, on-device greedy tokens); the
+// single-step kernels are compiled without the step machinery.
+template <int B, bool MS>
 __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
   u32 seq = 0, gen = 0;
-  ItemCache ic;
-  for (u32 oi = q0; oi < q1; ++oi) {
+  const u32 nsteps = MS ? (u32)kargs().n_steps : 1u;
+  constexpr bool multi = MS;
+  for (u32 step = 0; step < nsteps; ++step) {
+    if (MS && step > 0) {  // step prologue
+      const KArgs& A = kargs();
+      {  // every compute unit has finished the previous step: take its greedy tokens
+        if (w == 0 && !step_barrier(A, A.tag + step - 1)) return;
+        if (!cbar(A, gen)) return;
+        if (!argmax_tokens(A, w, gen)) return;
+        gen += 2 * NC;
+        if (blockIdx.x == 0 && w == 0 && A.tokens_out && (int)lane_id() < A.batch)
+          A.tokens_out[(size_t)(step - 1) * A.batch + lane_id()] = lane_tok((int)lane_id());
+      }
+      if (w == 0 && lane_id() == 0) {  // this step's tag; publishing the step lets the loader stream it
+        __hip_atomic_store(&g_ctag, A.tag + step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_store(&g_cstep, step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      if (!cbar(A, gen)) return;
+    }
+    ItemCache ic;  // a new step has a new attention plan
+    for (u32 oi = q0; oi < q1; ++oi) {
     const KArgs& A = kargs();
     const Op o = sload(A.ops + oi);
 #if MK_TRACE_STAMPS
@@ -2033,10 +2237,10 @@ __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
         op_embed_finish(A, w, gen);
         break;
       case OP_GEMV:
-        if constexpr (B < 8) alive = op_gemv<B>(A, o, w, seq, gen);
+        if constexpr (B < 8) alive = op_gemv<B, MS>(A, o, w, seq, gen);
         break;
       case OP_MMV:
-        if constexpr (B == 8) alive = op_mmv<B>(A, o, w, seq, gen);
+        if constexpr (B == 8) alive = op_mmv<B, MS>(A, o, w, seq, gen);
         break;
       case OP_ATTN: alive = A.d == 128 ? op_attn<128>(A, o, w, seq, gen, ic) : op_attn<64>(A, o, w, seq, gen, ic); break;
       case OP_DELTA: alive = A.dk == 128 ? op_delta<128>(A, o, w, seq, gen) : op_delta<64>(A, o, w, seq, gen); break;
@@ -2064,20 +2268,39 @@ __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
       tr[6] = ld[2];
     }
 #endif
+    }
+    {  // step epilogue
+      if (multi) {  // this compute unit's stores of the step are complete: publish the step
+        const KArgs& A = kargs();
+        __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));
+        if (!cbar(A, gen)) return;
+        if (w == 0 && lane_id() == 0)
+          __hip_atomic_store(gptr(A.step_done + blockIdx.x), A.tag + step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  // the last step's greedy tokens
+  const KArgs& A = kargs();
+  if (MS && A.tokens_out && blockIdx.x == 0) {
+    if (w == 0 && !step_barrier(A, A.tag + nsteps - 1)) return;
+    if (!cbar(A, gen)) return;
+    if (!argmax_tokens(A, w, gen)) return;
+    if (w == 0 && (int)lane_id() < A.batch) A.tokens_out[(size_t)(nsteps - 1) * A.batch + lane_id()] = lane_tok((int)lane_id());
   }
 }
 
-template <int B>
+template <int B, bool MS>
 __device__ __forceinline__ void megakernel_body(const KArgs& A) {
   const u32 wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index: uniform per wave
   if (threadIdx.x < NC) g_consumed[threadIdx.x] = 0;
   if (threadIdx.x == 0) { g_filled = 0; g_aplan[0] = 0; }
-  if (threadIdx.x == 0) { g_bar = 0; g_abort = 0; }
+  if (threadIdx.x == 0) { g_bar = 0; g_abort = 0; g_ctag = A.tag; g_cstep = 0; }
+  if (threadIdx.x < (u32)A.batch && threadIdx.x < (u32)APLAN_MAXB) g_tok[threadIdx.x] = A.tokens[threadIdx.x];
   __syncthreads();
   if (earlier_launch_failed(A)) return;  // uniform: the same word for every wave of the grid
   const u32 q0 = A.queue_off[blockIdx.x], q1 = A.queue_off[blockIdx.x + 1];
-  if (wv == 0) loader(A, q0, q1);
-  else compute<B>(q0, q1, wv - 1);
+  if (wv == 0) loader<MS>(A, q0, q1);
+  else compute<B, MS>(q0, q1, wv - 1);
 }
 
 }  // namespace mk
@@ -2087,7 +2310,13 @@ __device__ __forceinline__ void megakernel_body(const KArgs& A) {
 #else
 #define MK_KNAME(b) mk_megakernel_##b
 #endif
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b1)(mk::KArgs A) { mk::megakernel_body<1>(A); }
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b2)(mk::KArgs A) { mk::megakernel_body<2>(A); }
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b4)(mk::KArgs A) { mk::megakernel_body<4>(A); }
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b8)(mk::KArgs A) { mk::megakernel_body<8>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b1)(mk::KArgs A) { mk::megakernel_body<1, false>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b2)(mk::KArgs A) { mk::megakernel_body<2, false>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b4)(mk::KArgs A) { mk::megakernel_body<4, false>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b8)(mk::KArgs A) { mk::megakernel_body<8, false>(A); }
+#if !MK_TRACE_STAMPS
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b1(mk::KArgs A) { mk::megakernel_body<1, true>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b2(mk::KArgs A) { mk::megakernel_body<2, true>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b4(mk::KArgs A) { mk::megakernel_body<4, true>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b8(mk::KArgs A) { mk::megakernel_body<8, true>(A); }
+#endif

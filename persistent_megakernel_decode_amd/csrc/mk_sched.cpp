@@ -326,6 +326,9 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
     Q.m = take((size_t)B * F * 4);
     Q.x_out = take((size_t)B * H * 4);
   }
+  // multi-step launches: the tag of the last step each CU has finished (cleared with the
+  // activations: a reset restarts the tags)
+  Y.step_done = take((size_t)n_cus * 4);
   Y.act_begin = Y.row_ok;
   Y.act_end = off;
 
@@ -404,6 +407,7 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
   bd.gemv(s_lm, prev, L, (uint32_t)d.vocab, (uint32_t)H, EPI_LOGITS, true, wptr(lm), 0, 0, (uint32_t)NONE,
           (uint32_t)NONE, x_in, (uint32_t)H, w ? wptr(w->final_norm) : 0, 0, (uint32_t)d.vocab, 0);
   if (!bd.err.empty()) return bd.err;
+  P.n_lm = (int)bd.stage_ops[s_lm].size();
 
   // ---------------- distribute ops to queues (op j of a stage -> CU j mod n_cus), in stage order
   const int S = (int)bd.stage_ops.size();
@@ -460,6 +464,9 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
   // per-op timing stamps of the traced kernels (MK_TRACE=1), 4 words per op; kept in every
   // workspace so that tracing never needs memory of its own
   Y.trace = take(P.ops.size() * TRACE_WORDS * sizeof(uint32_t));
+  // multi-step launches: per LM-head op and sequence, the (value, index) of its largest logit, one
+  // half per step parity (written every step before it is read: never cleared)
+  Y.amax = take((size_t)2 * P.n_lm * 8 * 2 * 4);
   Y.total = off;
   return "";
 }

@@ -16,6 +16,7 @@ namespace mk {
 struct Layout {
   size_t ops = 0, queue_off = 0, stages = 0, counters = 0, layers = 0, rope = 0, status = 0, row_ok = 0, x0 = 0;
   size_t trace = 0;  // per-op timing stamps (traced kernels only)
+  size_t step_done = 0, amax = 0;  // multi-step launches: per-CU step tags, LM-head greedy partials
   struct PerLayer {
     size_t qkv = 0, part = 0, tickets = 0, mix_o = 0, x_mix = 0, m = 0, x_out = 0;
   };
@@ -30,6 +31,7 @@ struct Plan {
   int kernel_batch = 1;          // compiled batch width of the kernel variant
   int n_items = 0;               // attention items per attention layer
   int mix_dim = 0;
+  int n_lm = 0;                  // LM-head ops (one greedy partial per op and sequence)
   std::vector<Op> ops;           // all queues concatenated (device pointers are offsets until relocated)
   std::vector<uint32_t> queue_off;
   std::vector<Stage> stages;
