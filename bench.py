@@ -8,9 +8,13 @@ synthetic weights and caches of the named shape, resident in HBM before the
 timed region; tokens and positions for every timed step are staged on the
 device beforehand, so nothing but launches happens between steps.
 
-Prints ONE JSON line: decode tokens/s (value), MBU, the roofline of the
-megakernel (algorithmic bytes per launch / measured launch time vs 8 TB/s)
-and the CPU oracle timed on a bounded sample of the same workload.
+Prints ONE JSON line: decode tokens/s of the headline workload (value), MBU,
+the roofline of the megakernel (algorithmic bytes per launch / measured launch
+time vs 8 TB/s), the same decode continued as launches of several steps with
+the greedy token chosen on the device (multistep), the CPU oracle timed on a
+bounded sample of the same workload, the read ceiling of this GPU measured in
+the same run (stream_read), and the same figures for the other workloads
+(per_config).
 """
 from __future__ import annotations
 
@@ -147,6 +151,192 @@ def cpu_baseline(cfg, w, cache, ctx0, budget_s: float, max_steps: int) -> dict:
                       f"(mean {step:.3f} s/step, fp64-accumulating C oracle, OpenMP over output rows)"}
 
 
+def stream_read_ceiling(mkd, torch, stream) -> dict:
+    """What a plain streaming read reaches on this GPU in the same run: the library's own read kernel
+    over a 2 GiB buffer (every byte once), best over a few grid sizes; and the runtime's
+    device-to-device copy for context."""
+    nbytes = 1 << 31
+    buf = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    buf.fill_(1.0)
+    out = torch.empty(65536, dtype=torch.int32, device="cuda")
+    sp = int(stream.cuda_stream)
+    best = (0.0, 0)
+    for blocks in (2048, 4096, 8192, 16384):
+        ts = []
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            mkd.check(mkd.mk_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), blocks, sp), "mk_stream_read")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        gbs = nbytes / (float(np.median(ts[1:])) * 1e-3) / 1e9
+        if gbs > best[0]:
+            best = (gbs, blocks)
+    dst = torch.empty_like(buf)
+    cp = []
+    for _ in range(6):  # read + write bytes
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(buf)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cp.append(e0.elapsed_time(e1))
+    copy_gbs = 2 * nbytes / (float(np.median(cp[1:])) * 1e-3) / 1e9
+    del buf, dst, out
+    torch.cuda.empty_cache()
+    return {"gbs": round(best[0], 1), "kernel": f"mk_stream_read over 2 GiB, {best[1]} workgroups x 256 threads, "
+            "non-temporal 16-byte loads, 8 in flight per thread, best of 2048/4096/8192/16384 workgroups",
+            "copy_gbs": round(copy_gbs, 1), "copy": "2 GiB device-to-device copy (runtime blit), read + write bytes"}
+
+
+def staged_inputs(torch, B, rows):
+    """Device int32 arrays [len(rows)][stride] (each row padded to 16 bytes) from host rows."""
+    stride = max(4, (B + 3) // 4 * 4)
+    a = np.zeros((len(rows), stride), np.int32)
+    for i, r in enumerate(rows):
+        a[i, :B] = r
+    return torch.from_numpy(a).cuda(), stride * 4
+
+
+def run_config(name: str, steps: int, warmup: int, multi_k: int, cpu_budget: float, trace_path: str = "") -> dict:
+    """Times `steps` single-step launches (after `warmup`), then `steps` decode steps as launches of
+    `multi_k` steps each (mk_decode_steps, tokens chosen on the device), on one seeded workload;
+    then the CPU oracle on a bounded sample (cpu_budget > 0)."""
+    import torch
+    import synth
+    import persistent_megakernel_decode_amd as mkd
+
+    cfg = synth.CONFIGS[name]
+    B = cfg.batch
+    n_launch = max(1, steps // multi_k) if multi_k else 0
+    room = warmup + steps + (multi_k * (1 + n_launch) if multi_k else 0)
+    ctx0 = synth.context_lengths(cfg)
+    t0 = time.time()
+    w = synth.make_weights(cfg)
+    cache = synth.make_cache(cfg, ctx0, room)
+    log(f"{name}: inputs generated in {time.time() - t0:.1f}s")
+    t0 = time.time()
+    max_ctx = int(cache["max_pages_per_seq"]) * cfg.page_size
+    g = mkd.DecodeContext(synth.shape_of(cfg, max_ctx), w, cache, "cuda:0")
+    del cache
+    entry = {}
+    try:
+        torch.cuda.synchronize()
+        log(f"{name}: device model ready in {time.time() - t0:.1f}s, workspace {g.ws_bytes / 2**20:.1f} MiB")
+        total = warmup + steps
+        draws = synth.u32(total * B, cfg.seed, "bench_tokens").reshape(total, B) % cfg.vocab
+        toks_d, row = staged_inputs(torch, B, [draws[s] for s in range(total)])
+        pos_d, _ = staged_inputs(torch, B, [[c + s for c in ctx0] for s in range(total)])
+        len_d, _ = staged_inputs(torch, B, [[c + s + 1 for c in ctx0] for s in range(total)])
+        stream = torch.cuda.current_stream()
+        sp = int(stream.cuda_stream)
+
+        def launch(s: int) -> None:
+            rc = mkd.mk_decode_step(g.ctx, toks_d.data_ptr() + s * row, pos_d.data_ptr() + s * row,
+                                    len_d.data_ptr() + s * row, B, g.logits.data_ptr(), sp)
+            if rc != 0:
+                raise mkd.MKError(rc, f"mk_decode_step (step {s})")
+
+        for s in range(warmup):
+            launch(s)
+        torch.cuda.synchronize()
+        mkd.check(g.sync(), "warm-up")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record(stream)
+            launch(warmup + i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+        mkd.check(g.sync(), "timed steps")
+        kms = np.array([a.elapsed_time(b) for a, b in ev])  # per-launch kernel time on its stream
+        log(f"{name}: timed {steps} steps: {elapsed * 1e3:.1f} ms wall, kernel median {np.median(kms) * 1e3:.1f} us")
+        step_bytes = [bytes_per_step(cfg, [c + warmup + i for c in ctx0]) for i in range(steps)]
+        mean_bytes = float(np.mean(step_bytes))
+        ms_per_step = elapsed * 1e3 / steps
+        kernel_s = float(np.mean(kms)) * 1e-3
+        achieved = mean_bytes / kernel_s / 1e9
+        entry = {
+            "workload": WORKLOADS[name], "batch": B, "ctx": ctx0 if B > 1 else ctx0[0], "steps": steps,
+            "warmup": warmup, "ms_per_step": round(ms_per_step, 4), "tokens_per_s": round(B * steps / elapsed, 2),
+            "mbu": round(mean_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+            "bytes_per_step": mean_bytes,
+            "kernel_us_mean": round(kernel_s * 1e6, 2),
+            "kernel_us_median": round(float(np.median(kms)) * 1e3, 2),
+            "kernel_us_p90": round(float(np.percentile(kms, 90)) * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name)},
+        }
+        if trace_path:  # the last timed step, per op (the traced kernels were timed above)
+            from persistent_megakernel_decode_amd import trace as mktrace
+            tr = g.trace()
+            with open(trace_path, "w") as f:
+                json.dump(mktrace.chrome_trace(tr), f)
+            entry["traced"] = {"path": trace_path, "per_op_kind_us": {
+                k: {kk: round(vv, 1) if isinstance(vv, float) else vv for kk, vv in v.items()}
+                for k, v in mktrace.op_summary(tr).items()}}
+            log(f"trace of the last step written to {trace_path}")
+        elif multi_k:
+            # the same decode continued as launches of multi_k steps (greedy tokens chosen on the device)
+            base = [c + total for c in ctx0]
+            first = [int(t) for t in draws[-1]]
+            starts = [[c + multi_k * j for c in base] for j in range(1 + n_launch)]
+            mtok_d, mrow = staged_inputs(torch, B, [first] * (1 + n_launch))
+            mpos_d, _ = staged_inputs(torch, B, starts)
+            mlen_d, _ = staged_inputs(torch, B, [[c + 1 for c in st] for st in starts])
+            mlogits = torch.empty((multi_k, B, cfg.vocab), dtype=torch.float32, device="cuda")
+            mtoks = torch.empty((multi_k, max(4, B)), dtype=torch.int32, device="cuda")
+
+            def mlaunch(j: int) -> None:
+                rc = mkd.mk_decode_steps(g.ctx, mtok_d.data_ptr() + j * mrow, mpos_d.data_ptr() + j * mrow,
+                                         mlen_d.data_ptr() + j * mrow, B, multi_k, mlogits.data_ptr(),
+                                         mtoks.data_ptr(), sp)
+                if rc != 0:
+                    raise mkd.MKError(rc, f"mk_decode_steps (launch {j})")
+
+            mlaunch(0)
+            torch.cuda.synchronize()
+            mkd.check(g.sync(), "multi-step warm-up")
+            mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_launch)]
+            t_start = time.perf_counter()
+            for j in range(n_launch):
+                mev[j][0].record(stream)
+                mlaunch(1 + j)
+                mev[j][1].record(stream)
+            torch.cuda.synchronize()
+            m_elapsed = time.perf_counter() - t_start
+            mkd.check(g.sync(), "multi-step launches")
+            mk_ms = np.array([a.elapsed_time(b) for a, b in mev])
+            m_steps = n_launch * multi_k
+            m_bytes = float(np.mean([bytes_per_step(cfg, [c + k for c in starts[1 + j]])
+                                     for j in range(n_launch) for k in range(multi_k)]))
+            m_ms = m_elapsed * 1e3 / m_steps
+            m_kernel_s = float(np.mean(mk_ms)) * 1e-3 / multi_k
+            entry["multistep"] = {
+                "steps_per_launch": multi_k, "launches": n_launch, "ms_per_step": round(m_ms, 4),
+                "tokens_per_s": round(B * m_steps / m_elapsed, 2),
+                "mbu": round(m_bytes / (m_ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                "kernel_us_per_step": round(m_kernel_s * 1e6, 2),
+                "roofline_frac": round(m_bytes / m_kernel_s / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"{name}: {n_launch} launches of {multi_k} steps: {m_ms * 1e3:.1f} us per step")
+    finally:
+        g.close()
+        del g
+        torch.cuda.empty_cache()
+    if cpu_budget > 0:
+        log(f"{name}: timing the CPU oracle on a bounded sample")
+        room = 64  # new positions the oracle's cache can take
+        entry["cpu_baseline"] = cpu_baseline(cfg, w, synth.make_cache(cfg, ctx0, room), ctx0, cpu_budget, room)
+    return entry
+
+
+PER_CONFIG = ("0.6b", "hybrid", "13b")   # measured beside the headline 8B workload
+RUN_STEPS = {"8b": 128, "0.6b": 64, "hybrid": 64, "13b": 64, "tiny": 8}  # decode steps of each workload's run
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,7 +344,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="8b", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--per-config-cpu-budget", type=float, default=6.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true", help="time the headline workload only")
+    ap.add_argument("--multi-k", type=int, default=8, help="steps per launch of the multi-step timing (0 = skip)")
     ap.add_argument("--trace", metavar="PATH", default="",
                     help="run the traced kernels (per-op stamps) and write the last step as a Perfetto JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -166,141 +359,42 @@ def main() -> int:
         print(f"bench.py runs on one GPU only: the megakernel is a single-GPU decode step (asked for {args.gpus})",
               file=sys.stderr)
         return 2
-
     if args.trace:
         os.environ["MK_TRACE"] = "1"  # read at context creation: selects the traced kernels
     import torch
-    import synth
     import persistent_megakernel_decode_amd as mkd
 
-    cfg = synth.CONFIGS[args.config]
-    B = cfg.batch
-    total = args.warmup + args.steps
-    ctx0 = synth.context_lengths(cfg)
-    t0 = time.time()
-    w = synth.make_weights(cfg)
-    cache = synth.make_cache(cfg, ctx0, total)
-    log(f"{args.config}: inputs generated in {time.time() - t0:.1f}s")
-    t0 = time.time()
-    max_ctx = int(cache["max_pages_per_seq"]) * cfg.page_size
-    g = mkd.DecodeContext(synth.shape_of(cfg, max_ctx), w, cache, "cuda:0")
-    torch.cuda.synchronize()
-    log(f"device model ready in {time.time() - t0:.1f}s, workspace {g.ws_bytes / 2**20:.1f} MiB")
-
-    # per-step device inputs, each row padded to 16 bytes
-    stride = max(4, (B + 3) // 4 * 4)
-    toks_h = np.zeros((total, stride), np.int32)
-    pos_h = np.zeros((total, stride), np.int32)
-    len_h = np.zeros((total, stride), np.int32)
-    draws = synth.u32(total * B, cfg.seed, "bench_tokens").reshape(total, B) % cfg.vocab
-    for s in range(total):
-        toks_h[s, :B] = draws[s]
-        pos_h[s, :B] = [c + s for c in ctx0]
-        len_h[s, :B] = [c + s + 1 for c in ctx0]
-    toks_d = torch.from_numpy(toks_h).cuda()
-    pos_d = torch.from_numpy(pos_h).cuda()
-    len_d = torch.from_numpy(len_h).cuda()
-    stream = torch.cuda.current_stream()
-    sp = int(stream.cuda_stream)
-    row = stride * 4
-
-    def launch(s: int) -> None:
-        rc = mkd.mk_decode_step(g.ctx, toks_d.data_ptr() + s * row, pos_d.data_ptr() + s * row,
-                                len_d.data_ptr() + s * row, B, g.logits.data_ptr(), sp)
-        if rc != 0:
-            raise mkd.MKError(rc, f"mk_decode_step (step {s})")
-
-    for s in range(args.warmup):
-        launch(s)
-    torch.cuda.synchronize()
-    mkd.check(g.sync(), "warm-up")
-    log(f"warm-up done ({args.warmup} steps)")
-
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        launch(args.warmup + i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    mkd.check(g.sync(), "timed steps")
-    kms = np.array([a.elapsed_time(b) for a, b in ev])  # per-launch kernel time on its stream
-    log(f"timed {args.steps} steps: {elapsed * 1e3:.1f} ms wall, kernel median {np.median(kms) * 1e3:.1f} us")
-
-    step_bytes = [bytes_per_step(cfg, [c + args.warmup + i for c in ctx0]) for i in range(args.steps)]
-    mean_bytes = float(np.mean(step_bytes))
-    ms_per_step = elapsed * 1e3 / args.steps
-    tok_s = B * args.steps / elapsed
-    kernel_s = float(np.mean(kms)) * 1e-3
-    achieved = mean_bytes / kernel_s / 1e9
+    head = run_config(args.config, args.steps, args.warmup, args.multi_k,
+                      0.0 if args.no_cpu else args.cpu_budget, args.trace)
+    B = head["batch"]
     out = {
         "metric": "decode tokens/s and MBU (% of HBM peak) per step, 8B-shape batch 1 ctx 4096"
         if args.config == "8b" else f"decode tokens/s and MBU (% of HBM peak) per step, {args.config}",
-        "value": round(tok_s, 2),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded random-init weights and KV cache of the named shape)",
-        "config": {"workload": WORKLOADS[args.config], "batch": B, "ctx": ctx0 if B > 1 else ctx0[0],
-                   "layers": cfg.n_layers, "hidden": cfg.hidden},
-        "mbu": round(mean_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
-        "bytes_per_step": mean_bytes,
-        "kernel_us_median": round(float(np.median(kms)) * 1e3, 2),
-        "kernel_us_p90": round(float(np.percentile(kms, 90)) * 1e3, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config)},
+        "config": {"workload": head["workload"], "batch": B, "ctx": head["ctx"]},
     }
-    # context: what a plain streaming read reaches on this GPU in the same run (torch's sum over a
-    # 2 GiB buffer, i.e. one read of every byte)
-    buf = torch.empty(1 << 29, dtype=torch.float32, device="cuda")
-    buf.fill_(1.0)
-    rd = []
-    for _ in range(6):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        buf.sum()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        rd.append(e0.elapsed_time(e1))
-    stream_gbs = buf.numel() * 4 / (float(np.median(rd[1:])) * 1e-3) / 1e9
-    dst = torch.empty_like(buf)
-    cp = []
-    for _ in range(6):  # device-to-device copy (the runtime's blit kernel): read + write bytes
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        dst.copy_(buf)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        cp.append(e0.elapsed_time(e1))
-    copy_gbs = 2 * buf.numel() * 4 / (float(np.median(cp[1:])) * 1e-3) / 1e9
-    del buf, dst
-    out["stream_read"] = {"gbs": round(stream_gbs, 1), "kernel": "torch.sum over 2 GiB fp32",
-                          "achieved_frac": round(achieved / stream_gbs, 4),
-                          "copy_gbs": round(copy_gbs, 1), "copy": "2 GiB device-to-device copy, read + write bytes"}
-    if args.trace:  # the last timed step, per op (the traced kernels were timed above)
-        from persistent_megakernel_decode_amd import trace as mktrace
-        tr = g.trace()
-        with open(args.trace, "w") as f:
-            json.dump(mktrace.chrome_trace(tr), f)
-        out["traced"] = {"path": args.trace, "per_op_kind_us": {
-            k: {kk: round(vv, 1) if isinstance(vv, float) else vv for kk, vv in v.items()}
-            for k, v in mktrace.op_summary(tr).items()}}
-        log(f"trace of the last step written to {args.trace}")
-    if not args.no_cpu:
-        log("timing the CPU oracle on a bounded sample")
-        g.close()
-        del g
-        torch.cuda.empty_cache()
-        room = 64  # new positions the oracle's cache can take
-        out["cpu_baseline"] = cpu_baseline(cfg, w, synth.make_cache(cfg, ctx0, room), ctx0, args.cpu_budget, room)
+    for k in ("mbu", "bytes_per_step", "kernel_us_mean", "kernel_us_median", "kernel_us_p90", "roofline",
+              "multistep", "traced", "cpu_baseline"):
+        if k in head:
+            out[k] = head[k]
+    out["stream_read"] = stream_read_ceiling(mkd, torch, torch.cuda.current_stream())
+    out["stream_read"]["achieved_frac"] = round(head["roofline"]["achieved"] / out["stream_read"]["gbs"], 4)
+    if not args.no_per_config and not args.trace and args.config == "8b":
+        out["per_config"] = {}
+        for name in PER_CONFIG:
+            n = min(args.steps, RUN_STEPS[name])
+            out["per_config"][name] = run_config(name, n, args.warmup, args.multi_k,
+                                                 0.0 if args.no_cpu else args.per_config_cpu_budget)
     print(json.dumps(out), flush=True)
     return 0
 

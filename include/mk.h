@@ -246,6 +246,14 @@ mk_status mk_copy_midstate(mk_ctx* ctx, int32_t kind, int32_t layer, float* dst,
 mk_status mk_trace_words(mk_ctx* ctx, size_t* count);
 mk_status mk_copy_trace(mk_ctx* ctx, uint32_t* dst, size_t count);
 
+/* Measurement aid: a plain streaming read of `bytes` (a multiple of 16) of device memory at `buf`
+ * (16-byte aligned), every byte once, by `blocks` workgroups of 256 threads (1..65536) in a
+ * grid-stride loop of non-temporal 16-byte loads, eight in flight per thread; `out` (device, `blocks` uint32) receives one XOR fold per
+ * workgroup so the loads cannot be dropped.  It is the achievable-read ceiling the decode kernel's
+ * HBM rate is set against (the roofline of a weight-streaming decode step, ForgeMegakernel
+ * abstract: decode is bound by the bytes it reads).  Asynchronous on hip_stream. */
+mk_status mk_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t blocks, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

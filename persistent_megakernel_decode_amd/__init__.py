@@ -76,7 +76,7 @@ MK_EMU_COUNTERS, MK_EMU_IDLE_ITEMS_SILENT, MK_EMU_DEAD_ROWS_SILENT, MK_EMU_STALL
 
 EXPORTED = ["mk_workspace_size", "mk_create", "mk_decode_step", "mk_sync_status", "mk_reset", "mk_last_error",
             "mk_destroy", "mk_plan", "mk_emulate", "mk_copy_midstate", "mk_trace_words", "mk_copy_trace",
-            "mk_create_static", "mk_decode_steps"]
+            "mk_create_static", "mk_decode_steps", "mk_stream_read"]
 MK_STATIC_SCRATCH_BYTES = 64 << 20
 MK_MAX_STEPS = 4096
 TRACE_WORDS = 8  # per-op trace record (mk_internal.h)
@@ -99,6 +99,7 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(mk_kv_cache), ctypes.POINTER(P)]
         L.mk_decode_step.argtypes = [P, P, P, P, I32, P, P]
         L.mk_decode_steps.argtypes = [P, P, P, P, I32, I32, P, P, P]
+        L.mk_stream_read.argtypes = [P, ctypes.c_size_t, P, I32, P]
         L.mk_sync_status.argtypes = [P]
         L.mk_reset.argtypes = [P]
         L.mk_last_error.argtypes = []
@@ -111,7 +112,7 @@ def lib() -> ctypes.CDLL:
         L.mk_copy_midstate.argtypes = [P, I32, I32, P, ctypes.c_size_t, P]
         L.mk_trace_words.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         L.mk_copy_trace.argtypes = [P, P, ctypes.c_size_t]
-        for f in ("mk_workspace_size", "mk_create", "mk_create_static", "mk_decode_step", "mk_decode_steps", "mk_sync_status", "mk_reset", "mk_plan",
+        for f in ("mk_workspace_size", "mk_create", "mk_create_static", "mk_decode_step", "mk_decode_steps", "mk_stream_read", "mk_sync_status", "mk_reset", "mk_plan",
                   "mk_emulate", "mk_copy_midstate", "mk_trace_words", "mk_copy_trace"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -195,6 +196,10 @@ def mk_decode_steps(ctx: int, tokens_ptr: int, positions_ptr: int, ctx_lens_ptr:
                     logits_ptr: int, tokens_out_ptr: int, stream: int = 0) -> int:
     return lib().mk_decode_steps(ctx, tokens_ptr, positions_ptr, ctx_lens_ptr, batch, n_steps, logits_ptr,
                                  tokens_out_ptr, stream or None)
+
+
+def mk_stream_read(buf_ptr: int, nbytes: int, out_ptr: int, blocks: int, stream: int = 0) -> int:
+    return lib().mk_stream_read(buf_ptr, nbytes, out_ptr, blocks, stream or None)
 
 
 def mk_sync_status(ctx: int) -> int:

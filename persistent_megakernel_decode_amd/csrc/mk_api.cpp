@@ -68,6 +68,31 @@ const void* steps_kernel_for(int B) {
   }
 }
 
+// Streaming read: every 16-byte word of [p, p + n) once, grid-stride, eight non-temporal 16-byte
+// loads in flight per thread (the cache policy the megakernel's weight stream uses).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__global__ void __launch_bounds__(256) stream_read_kernel(const u32x4_t* __restrict__ p, size_t n, uint32_t* out) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 7 * stride < n; i += 8 * stride) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n; i += stride) {
+    const u32x4_t a = __builtin_nontemporal_load(p + i);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  for (int o = 32; o >= 1; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
+  __shared__ uint32_t part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
 __global__ void fill_u32(uint32_t* p, size_t n, uint32_t v) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -509,6 +534,16 @@ mk_status mk_reset(mk_ctx* ctx) {
 }
 
 void mk_destroy(mk_ctx* ctx) { delete ctx; }
+
+mk_status mk_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t blocks, void* hip_stream) {
+  if (!buf || !out || !aligned16(buf) || bytes % 16 || bytes == 0)
+    return fail(MK_ERR_INVALID_ARG, "buf must be non-null and 16-byte aligned, bytes a positive multiple of 16");
+  if (blocks < 1 || blocks > 65536) return fail(MK_ERR_INVALID_ARG, "blocks outside [1, 65536]");
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)hip_stream, (const u32x4_t*)buf,
+                     bytes / 16, out);
+  MK_HIP(hipGetLastError());
+  return MK_OK;
+}
 
 mk_status mk_trace_words(mk_ctx* ctx, size_t* count) {
   if (!ctx || !count) return fail(MK_ERR_INVALID_ARG, "null argument");

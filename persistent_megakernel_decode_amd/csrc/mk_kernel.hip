@@ -91,11 +91,21 @@ __device__ __forceinline__ T opq(T v) {
 // through it cannot be hoisted past the point where it is taken, so a value is re-read (a cached
 // scalar load) in each op that needs it instead of being held -- and spilled -- for the whole
 // launch.  The arguments are the kernel's only parameter, at offset 0.
-__device__ __forceinline__ const KArgs& kargs() {
-  const __attribute__((address_space(4))) KArgs* p =
-      (const __attribute__((address_space(4))) KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+// The segment pointer exists in the kernel itself only: a called function gets null for it, so
+// the multi-step kernels pass it to their per-step calls (KPtr) explicitly.
+using KPtr = const __attribute__((address_space(4))) KArgs*;
+__device__ __forceinline__ KPtr kernarg_ptr() { return (KPtr)__builtin_amdgcn_kernarg_segment_ptr(); }
+__device__ __forceinline__ const KArgs& kref(KPtr p) {
   asm volatile("" : "+s"(p));
   return *(const KArgs*)p;
+}
+__device__ __forceinline__ const KArgs& kargs() { return kref(kernarg_ptr()); }
+// A KPtr received as a call argument (in vector registers): the same value in every lane.
+__device__ __forceinline__ KPtr uniform_kptr(KPtr p) {
+  const uint64_t v = (uint64_t)p;
+  const uint64_t lo = (u32)__builtin_amdgcn_readfirstlane((u32)v);  // (the builtin returns int)
+  const uint64_t hi = (u32)__builtin_amdgcn_readfirstlane((u32)(v >> 32));
+  return (KPtr)(lo | (hi << 32));
 }
 
 // Uniform, kernel-invariant data (queues, plan tables, inputs) read through the constant
@@ -743,32 +753,18 @@ __device__ __forceinline__ void loader_lds_store(u32* p, u32 v) {
 }
 #endif
 
-template <bool MS>
-__device__ __forceinline__ void loader(const KArgs& A0, u32 q0, u32 q1) {
-  const KArgs& A = A0;
-  u32 seq = 0, marked = 0, limit = NSLOT;  // slots below `limit` may be filled
+// One decode step's ring slots for this CU's queue [q0, q1): seq counts slots issued over the
+// launch.  Leaves every issued slot published (marked == seq) and returns the new seq, or ~0 on
+// abort.
+__device__ __forceinline__ u32 loader_ops(KPtr ap, u32 q0, u32 q1, u32 seq, u32 step) {
+  const KArgs& A = kref(ap);
+  u32 marked = seq, limit = seq + NSLOT;  // slots below `limit` may be filled: the ring is empty here
   const u32 lane16 = lane_id() * 16;
   const AttnLanes al = attn_lanes(A.d == 64 ? 64u : 128u);
-  const u32 nsteps = MS ? (u32)A.n_steps : 1u;
-  for (u32 step = 0; step < nsteps; ++step) {
-  if (step > 0) {
-    // Step s streams once the compute waves are on it: they reach it only when every compute unit
-    // has finished step s - 1, so the recurrent states this CU streams are the updated ones.  What
-    // has landed is published first (the compute waves need it to finish the previous step).
-    while (marked < seq) {
-      wait_oldest(seq - marked);
-      publish_filled(++marked);
-    }
-    Watchdog wd(A);
-    while (lds_ld_loader(&g_cstep) < step) {
-      if (aborted_loader() || wd.expired()) return;
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
   attn_plan_build(A, A.d == 64 ? 32 : 16, step);
   ItemCache ic;
   for (u32 oi = q0; oi < q1; ++oi) {
-    const KArgs& A = kargs();
+    const KArgs& A = kref(ap);
     const Op o = sload(A.ops + oi);
     const u32 ns = op_slots(A, o, ic);
 #if MK_TRACE_STAMPS
@@ -806,7 +802,7 @@ __device__ __forceinline__ void loader(const KArgs& A0, u32 q0, u32 q1) {
           if (marked == seq) {
             if (aborted_loader() || wd.expired()) {
               __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));
-              return;
+              return ~0u;
             }
             __builtin_amdgcn_s_sleep(1);
           }
@@ -844,10 +840,35 @@ __device__ __forceinline__ void loader(const KArgs& A0, u32 q0, u32 q1) {
     }
 #endif
   }
-  }
   while (marked < seq) {
     wait_oldest(seq - marked);
     publish_filled(++marked);
+  }
+  return seq;
+}
+
+template <bool MS>
+__device__ __forceinline__ void loader(u32 q0, u32 q1) {
+  if constexpr (!MS) {
+    loader_ops(kernarg_ptr(), q0, q1, 0, 0);
+  } else {
+    const KArgs& A = kargs();
+    const u32 nsteps = (u32)A.n_steps;
+    u32 seq = 0;
+    for (u32 step = 0; step < nsteps; ++step) {
+      if (step > 0) {
+        // Step s streams once the compute waves are on it: they reach it only when every compute
+        // unit has finished step s - 1 (and have acquired what the other units wrote), so the
+        // recurrent states and KV rows this CU streams are the updated ones.
+        Watchdog wd(A);
+        while (lds_ld_loader(&g_cstep) < step) {
+          if (aborted_loader() || wd.expired()) return;
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      seq = loader_ops(kernarg_ptr(), q0, q1, seq, step);
+      if (seq == ~0u) return;
+    }
   }
 }
 
@@ -1704,7 +1725,6 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   seq += ns;
   const int G = A.G, b = it.b, kvh = it.kvh;
   const int pos = step_pos(A, b);
-  const int pos0 = A.positions[b];  // the launch's first position: rows [pos0, pos) were appended by its earlier steps
   const int32_t rok = ld_i32_sc1(A.row_ok + b);  // checked where it is used
   const bool tagged = (o.flags & OPF_TAGGED_IN) != 0;
   const int qkv_ld = (A.Hq + 2 * A.Hkv) * D;
@@ -1808,7 +1828,6 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
 #pragma unroll
     for (int e = 0; e < DPL; ++e) ov[g][e] = 0.0f;
   release_upto(w, seq0 + min(w, ns));  // slots before this wave's first belong to other waves
-  const bool rows_ok = pos0 < pos && pos0 < it.p1 && row_ok_fix(A, b, rok);  // earlier steps' rows in this chunk
   for (u32 s = w; s < ns; s += NC) {
     const u32 sq = seq0 + s;
     if (!wait_full(A, sq)) return false;
@@ -1816,25 +1835,6 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
     char* vslot = kslot + 4096;
     const int pbase = it.p0 + (int)s * PPS;
     const int np = min(PPS, it.p1 - pbase);
-    // rows appended by this launch's earlier steps (on any CU): the loader may have streamed them
-    // before they were written, so they are re-read with agent-coherent loads and put into the slot
-    const int q1 = rows_ok ? min(pbase + np, pos) : 0;  // (pages of rows out of contract are not read)
-    for (int q = max(pbase, pos0); q < q1; ++q) {
-      const int r = q - pbase, d0 = (int)lane * DPL, c = d0 / 8;
-      const int pg = A.page_table[(size_t)b * A.max_pages_per_seq + q / 16];
-      const size_t off = (((size_t)pg * A.Hkv + kvh) * 16 + q % 16) * D + d0;
-      u16_alias* kd = (u16_alias*)(kslot + r * RB + ((c ^ (r % CPR)) * 16)) + (d0 % 8);
-      u16_alias* vd = (u16_alias*)(vslot + r * RB) + d0;
-      if constexpr (DPL == 2) {
-        const u32 kw = __hip_atomic_load(gptr((const u32*)((const uint16_t*)Ld.k_pages + off)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const u32 vw = __hip_atomic_load(gptr((const u32*)((const uint16_t*)Ld.v_pages + off)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        kd[0] = (uint16_t)kw; kd[1] = (uint16_t)(kw >> 16);
-        vd[0] = (uint16_t)vw; vd[1] = (uint16_t)(vw >> 16);
-      } else {
-        kd[0] = __hip_atomic_load(gptr((const uint16_t*)Ld.k_pages + off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        vd[0] = __hip_atomic_load(gptr((const uint16_t*)Ld.v_pages + off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
     if (has_new && pos >= pbase && pos < pbase + PPS) {
       // the new token's K/V are not in the cache the loader read: put them into the slot
       const int r = pos - pbase, d0 = (int)lane * DPL, c = d0 / 8;
@@ -2189,31 +2189,14 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
 // ------------------------------------------------------------------ compute waves
 // MS: the multi-step kernels (n_steps decode steps per launch, on-device greedy tokens); the
 // single-step kernels are compiled without the step machinery.
-template <int B, bool MS>
-__device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
-  u32 seq = 0, gen = 0;
-  const u32 nsteps = MS ? (u32)kargs().n_steps : 1u;
-  constexpr bool multi = MS;
-  for (u32 step = 0; step < nsteps; ++step) {
-    if (MS && step > 0) {  // step prologue
-      const KArgs& A = kargs();
-      {  // every compute unit has finished the previous step: take its greedy tokens
-        if (w == 0 && !step_barrier(A, A.tag + step - 1)) return;
-        if (!cbar(A, gen)) return;
-        if (!argmax_tokens(A, w, gen)) return;
-        gen += 2 * NC;
-        if (blockIdx.x == 0 && w == 0 && A.tokens_out && (int)lane_id() < A.batch)
-          A.tokens_out[(size_t)(step - 1) * A.batch + lane_id()] = lane_tok((int)lane_id());
-      }
-      if (w == 0 && lane_id() == 0) {  // this step's tag; publishing the step lets the loader stream it
-        __hip_atomic_store(&g_ctag, A.tag + step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        __hip_atomic_store(&g_cstep, step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-      if (!cbar(A, gen)) return;
-    }
-    ItemCache ic;  // a new step has a new attention plan
-    for (u32 oi = q0; oi < q1; ++oi) {
-    const KArgs& A = kargs();
+// One decode step's ops of this CU's queue, [q0, q1).  seq (ring slots consumed) and gen (compute
+// barrier count) carry over.  Returns false on abort.  AM: the LM head also leaves its greedy
+// partials (multi-step kernels).
+template <int B, bool AM>
+__device__ __forceinline__ bool op_loop(KPtr ap, u32 q0, u32 q1, u32 w, u32& seq, u32& gen) {
+  ItemCache ic;  // a new step has a new attention plan
+  for (u32 oi = q0; oi < q1; ++oi) {
+    const KArgs& A = kref(ap);
     const Op o = sload(A.ops + oi);
 #if MK_TRACE_STAMPS
     if (w == 0 && lane_id() == 0) {
@@ -2227,20 +2210,20 @@ __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
 #endif
     if (o.wait_stage != NO_STAGE && !(o.flags & OPF_TAGGED_IN)) {  // inputs finished by counter
       if (w == 0) wait_stage(A, o.wait_stage);
-      if (!cbar(A, gen)) return;
+      if (!cbar(A, gen)) return false;
     }
     bool alive = true;
     switch (o.opcode) {
       case OP_EMBED:
         op_embed<B>(A, w);
-        if (!cbar(A, gen)) return;
+        if (!cbar(A, gen)) return false;
         op_embed_finish(A, w, gen);
         break;
       case OP_GEMV:
-        if constexpr (B < 8) alive = op_gemv<B, MS>(A, o, w, seq, gen);
+        if constexpr (B < 8) alive = op_gemv<B, AM>(A, o, w, seq, gen);
         break;
       case OP_MMV:
-        if constexpr (B == 8) alive = op_mmv<B, MS>(A, o, w, seq, gen);
+        if constexpr (B == 8) alive = op_mmv<B, AM>(A, o, w, seq, gen);
         break;
       case OP_ATTN: alive = A.d == 128 ? op_attn<128>(A, o, w, seq, gen, ic) : op_attn<64>(A, o, w, seq, gen, ic); break;
       case OP_DELTA: alive = A.dk == 128 ? op_delta<128>(A, o, w, seq, gen) : op_delta<64>(A, o, w, seq, gen); break;
@@ -2253,10 +2236,10 @@ __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
     seq = __builtin_amdgcn_readfirstlane(seq);
     gen = __builtin_amdgcn_readfirstlane(gen);
     ic.restate();
-    if (!alive || aborted()) return;
+    if (!alive || aborted()) return false;
     const bool sig = o.sig_stage != NO_STAGE && !(o.flags & OPF_NO_SIGNAL);
     if (sig) __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));  // this wave's outputs are complete
-    if (!cbar(A, gen)) return;  // (also: the next op may overwrite this op's LDS areas)
+    if (!cbar(A, gen)) return false;  // (also: the next op may overwrite this op's LDS areas)
     if (sig && w == 0 && lane_id() == 0) signal_stage(A, o.sig_stage, o.sig_index);
 #if MK_TRACE_STAMPS
     if (w == 0 && lane_id() == 0) {
@@ -2268,14 +2251,74 @@ __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
       tr[6] = ld[2];
     }
 #endif
+  }
+  return true;
+}
+
+// The multi-step kernels run each step's op loop as a call: its registers are then allocated as
+// in a single-step kernel, instead of around a loop over steps (which costs spills throughout and
+// measured slower).  (The loader's step loop is inlined: as a call it measured slower.)
+// Arguments arrive in vector registers; they are uniform and restated so.  Returns seq | gen << 32,
+// or ~0 on abort.
+template <int B>
+__device__ __noinline__ uint64_t op_loop_call(KPtr ap, u32 q0, u32 q1, u32 w, u32 seq, u32 gen) {
+  q0 = __builtin_amdgcn_readfirstlane(q0);
+  q1 = __builtin_amdgcn_readfirstlane(q1);
+  w = __builtin_amdgcn_readfirstlane(w);
+  seq = __builtin_amdgcn_readfirstlane(seq);
+  gen = __builtin_amdgcn_readfirstlane(gen);
+  if (!op_loop<B, true>(uniform_kptr(ap), q0, q1, w, seq, gen)) return ~0ull;
+  return (uint64_t)seq | ((uint64_t)gen << 32);
+}
+
+template <int B, bool MS>
+__device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
+  u32 seq = 0, gen = 0;
+  const u32 nsteps = MS ? (u32)kargs().n_steps : 1u;
+  constexpr bool multi = MS;
+  for (u32 step = 0; step < nsteps; ++step) {
+    if (MS && step > 0) {  // step prologue
+      const KArgs& A = kargs();
+      {  // every compute unit has finished the previous step: take its greedy tokens
+        if (w == 0) {
+          if (!step_barrier(A, A.tag + step - 1)) return;
+          // acquire at agent scope: drops this CU's L1 lines and this XCD's L2 lines that other
+          // XCDs may have written since (KV rows appended by the previous step on any unit, which
+          // the loader streams with plain loads from here on)
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        if (!cbar(A, gen)) return;
+        if (!argmax_tokens(A, w, gen)) return;
+        gen += 2 * NC;
+        if (blockIdx.x == 0 && w == 0 && A.tokens_out && (int)lane_id() < A.batch)
+          A.tokens_out[(size_t)(step - 1) * A.batch + lane_id()] = lane_tok((int)lane_id());
+      }
+      if (w == 0 && lane_id() == 0) {  // this step's tag; publishing the step lets the loader stream it
+        __hip_atomic_store(&g_ctag, A.tag + step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_store(&g_cstep, step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      if (!cbar(A, gen)) return;
+    }
+    if constexpr (MS) {
+      const uint64_t r = op_loop_call<B>(kernarg_ptr(), q0, q1, w, seq, gen);
+      if (r == ~0ull) return;
+      seq = __builtin_amdgcn_readfirstlane((u32)r);
+      gen = __builtin_amdgcn_readfirstlane((u32)(r >> 32));
+    } else {
+      if (!op_loop<B, false>(kernarg_ptr(), q0, q1, w, seq, gen)) return;
     }
     {  // step epilogue
       if (multi) {  // this compute unit's stores of the step are complete: publish the step
         const KArgs& A = kargs();
         __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));
         if (!cbar(A, gen)) return;
-        if (w == 0 && lane_id() == 0)
-          __hip_atomic_store(gptr(A.step_done + blockIdx.x), A.tag + step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (w == 0) {
+          // release at agent scope: every wave's stores have completed (above); this writes this
+          // XCD's L2 back so that units on other XCDs read them after their acquire
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          if (lane_id() == 0)
+            __hip_atomic_store(gptr(A.step_done + blockIdx.x), A.tag + step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
   }
@@ -2299,7 +2342,7 @@ __device__ __forceinline__ void megakernel_body(const KArgs& A) {
   __syncthreads();
   if (earlier_launch_failed(A)) return;  // uniform: the same word for every wave of the grid
   const u32 q0 = A.queue_off[blockIdx.x], q1 = A.queue_off[blockIdx.x + 1];
-  if (wv == 0) loader<MS>(A, q0, q1);
+  if (wv == 0) loader<MS>(q0, q1);
   else compute<B, MS>(q0, q1, wv - 1);
 }
 
