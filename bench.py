@@ -71,13 +71,23 @@ def bytes_per_step(cfg, ctx_lens) -> float:
 PMC_FILE = os.path.join(ROOT, "profiles", "megakernel_8b_b1_ctx4096_pmc.txt")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the device sources the counters were taken with (kernel + shared header)."""
+def kernel_source_hash(texts=None) -> str:
+    """Hash of the device code the counters were taken with (kernel and the headers it includes),
+    comments and blank lines left out, so that a change to comments alone keeps the figure."""
     import hashlib
+    import re
     h = hashlib.sha256()
-    for f in ("mk_kernel.hip", "mk_internal.h"):
-        with open(os.path.join(ROOT, "persistent_megakernel_decode_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    if texts is None:
+        texts = []
+        for f in ("mk_kernel.hip", "mk_internal.h", "mk_attn_plan.h"):
+            with open(os.path.join(ROOT, "persistent_megakernel_decode_amd", "csrc", f)) as fh:
+                texts.append(fh.read())
+    for t in texts:
+        t = re.sub(r"/\*.*?\*/", "", t, flags=re.S)
+        for line in t.splitlines():
+            line = re.sub(r"//.*", "", line).rstrip()
+            if line:
+                h.update(line.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
@@ -92,7 +102,7 @@ def measured_traffic(config: str):
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+    if (vals.get("kernel_source_sha256_16", "").split() or [""])[0] != kernel_source_hash():
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])

@@ -105,16 +105,20 @@ typedef struct {
 typedef struct mk_ctx mk_ctx; /* opaque, library-owned host object */
 
 /* Bytes of device workspace mk_create needs for this model (queues, dependency
- * counters, RoPE table, inter-op activations, attention partials). */
+ * counters, RoPE table, inter-op activations, attention partials, the per-op trace
+ * section and the multi-step words): the instruction streams, dependency state and
+ * staging a decode megakernel keeps (ForgeMegakernel abstract). */
 mk_status mk_workspace_size(const mk_model_desc* desc, size_t* bytes);
 
-/* Compile the model into per-compute-unit instruction queues and upload them
- * into `workspace` (device memory of at least mk_workspace_size bytes, caller
+/* Compile the model into per-compute-unit instruction queues (the fine-grained
+ * instruction stream per compute unit of the ForgeMegakernel abstract) and upload
+ * them into `workspace` (device memory of at least mk_workspace_size bytes, caller
  * owned, 256-byte aligned).  Synchronous.  On success *out owns host state only. */
 mk_status mk_create(const mk_model_desc* desc, const mk_weights* weights, const mk_kv_cache* cache,
                     void* workspace, size_t workspace_bytes, mk_ctx** out);
 
-/* One decode step for sequences b < batch: consume tokens[b] at position
+/* One decode step -- the whole step in one persistent launch (the decode
+ * megakernel of the ForgeMegakernel abstract) -- for sequences b < batch: consume tokens[b] at position
  * positions[b] (== ctx_lens[b] - 1, ctx_lens counts cached tokens including
  * the new one), append its K/V (or update its conv / delta state) and write
  * fp32 logits_out[b][vocab].  tokens, positions, ctx_lens are device int32
@@ -156,15 +160,20 @@ mk_status mk_decode_steps(mk_ctx* ctx, const int32_t* tokens, const int32_t* pos
 mk_status mk_create_static(const mk_model_desc* desc, const mk_weights* weights, const mk_kv_cache* cache,
                            mk_ctx** out);
 
-/* Wait for the last step and return the sticky device status. */
+/* Wait for the last step and return the sticky device status: input-contract violations the
+ * kernel found (the contract the MK-KDA pull request's host check enforces, github
+ * choiceoh/stkernel #230) or a dependency wait that hit the watchdog. */
 mk_status mk_sync_status(mk_ctx* ctx);
 
-/* Clear the sticky error and all dependency counters (synchronous). */
+/* Clear the sticky error, the dependency counters and the tagged activations, and restart the
+ * step tags (synchronous): the recovery path after MK_ERR_DEVICE_INPUT or MK_ERR_TIMEOUT. */
 mk_status mk_reset(mk_ctx* ctx);
 
-/* Thread-local text for the last failing call on this thread ("" if none). */
+/* Thread-local text for the last failing call on this thread ("" if none).  (Library
+ * housekeeping; no passage of the pages defines it.) */
 const char* mk_last_error(void);
 
+/* Free the host state of a context (the caller's device buffers are untouched). */
 void mk_destroy(mk_ctx* ctx);
 
 /* ---- introspection (host-only; no GPU needed) ---- */
@@ -177,7 +186,9 @@ typedef struct {
   int32_t errors;           /* violations found by the plan checker (0 = valid) */
 } mk_plan_info;
 
-/* Run the scheduler and its checker on the host for n_cus compute units. */
+/* Run the scheduler -- the host side that compiles a model into per-unit instruction streams
+ * and dependency stages (ForgeMegakernel abstract) -- and its checker on the host for n_cus
+ * compute units. */
 mk_status mk_plan(const mk_model_desc* desc, int32_t n_cus, mk_plan_info* info);
 
 /* ---- dependency-protocol emulator (host-only; no GPU needed) ----
@@ -228,15 +239,16 @@ typedef enum {
 } mk_midstate;
 
 /* Copy mid-state `kind` of `layer` from the last step into dst (device memory,
- * fp32, `count` floats = batch * width), ordered on hip_stream. */
+ * fp32, `count` floats = batch * width), ordered on hip_stream: the intermediate states an
+ * independent mid-state oracle checks (ForgeMegakernel abstract). */
 mk_status mk_copy_midstate(mk_ctx* ctx, int32_t kind, int32_t layer, float* dst, size_t count, void* hip_stream);
 
 /* ---- per-op timing trace (diagnostic) ----
  * With MK_TRACE=1 in the environment at mk_create, the kernel records for every queue entry the
  * low 32 bits of the GPU's 100 MHz real-time clock when the op starts, when its inputs are in
  * hand (projections and attention: after the input poll; other ops: = start) and when it ends
- * (after the closing barrier of its workgroup), plus its opcode and stage.  The library owns the
- * trace buffer (allocated at mk_create only in this mode).
+ * (after the closing barrier of its workgroup), plus its opcode and stage, in a section of the
+ * caller's workspace (the multi-step kernels record none).
  * mk_copy_trace waits for the last step and copies into host memory `dst` (`count` uint32):
  *   [0] n_ops, [1] n_cus, [2 .. 2+n_cus] queue offsets (op range of CU c: [off[c], off[c+1])),
  *   then per op 8 words {opcode << 16 | stage, t_start, t_ready, t_end, loader first issue, loader
@@ -248,8 +260,8 @@ mk_status mk_copy_trace(mk_ctx* ctx, uint32_t* dst, size_t count);
 
 /* Measurement aid: a plain streaming read of `bytes` (a multiple of 16) of device memory at `buf`
  * (16-byte aligned), every byte once, by `blocks` workgroups of 256 threads (1..65536) in a
- * grid-stride loop of non-temporal 16-byte loads, eight in flight per thread; `out` (device, `blocks` uint32) receives one XOR fold per
- * workgroup so the loads cannot be dropped.  It is the achievable-read ceiling the decode kernel's
+ * grid-stride loop of non-temporal 16-byte loads, eight in flight per thread; `out` (device,
+ * `blocks` uint32) receives one XOR fold per workgroup so the loads cannot be dropped.  It is the achievable-read ceiling the decode kernel's
  * HBM rate is set against (the roofline of a weight-streaming decode step, ForgeMegakernel
  * abstract: decode is bound by the bytes it reads).  Asynchronous on hip_stream. */
 mk_status mk_stream_read(const void* buf, size_t bytes, uint32_t* out, int32_t blocks, void* hip_stream);

@@ -1,17 +1,17 @@
 // mk_attn_plan.h -- the decode step's split of every sequence's cached context into attention
-// chunks, shared by the gfx950 megakernel (which builds it once per launch in LDS) and the host
+// chunks, shared by the gfx950 megakernel (which builds it once per step in LDS) and the host
 // (the protocol emulator replays the kernel's own plan over launch sequences).
 //
 // Split-KV decode attention (paged GQA decode, the ForgeKernel blog post on ai6s.net, results
 // section) cuts each (sequence, KV head) context into chunks that run on different compute units
 // and are merged with the log-sum-exp rule.  Here every KV head gets at most K = n_items / Hkv
-// chunks per launch.  The launch picks one chunk length cs_all (a multiple of the positions one ring
+// chunks per step.  Each step picks one chunk length cs_all (a multiple of the positions one ring
 // slot holds, at least `min_slots` slots, the smallest such length that needs at most K chunks per
 // KV head); each sequence then keeps its chunk count at cs_all but evens its chunks out (lengths a
 // multiple of pps, at most cs_all), so a ragged batch leaves no short last chunk per sequence.
 //
 // Items: item i of a layer is chunk i / Hkv (counted over the sequences in order) of KV head
-// i % Hkv.  Chunks past the launch's total are items with no work.
+// i % Hkv.  Chunks past the step's total are items with no work.
 #pragma once
 #include <stdint.h>
 
@@ -29,7 +29,7 @@ constexpr int APLAN_MAXB = 8;
 // sequence, [16, 25) chunks of the sequences before b (entry 8 = all chunks).
 constexpr int APLAN_CTX = 0, APLAN_CS = 8, APLAN_FIRST = 16, APLAN_WORDS = 25;
 
-// A sequence takes part in attention this launch when it is in the batch and its context length
+// A sequence takes part in attention this step when it is in the batch and its context length
 // lies in [1, max_ctx].
 MK_HD int attn_clamp_ctx(int c, int max_ctx) { return (c >= 1 && c <= max_ctx) ? c : 0; }
 

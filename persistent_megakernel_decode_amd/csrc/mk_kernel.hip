@@ -158,10 +158,10 @@ __device__ __forceinline__ int32_t ld_i32_sc1(const int32_t* p) {
 }
 
 // Tagged activations: bit 0 of every fp32 value that EMBED or a projection writes holds the
-// launch parity (a relative change of at most 2^-23).  Each value is written once per launch and
-// consecutive launches differ in parity, so a value that shows the current parity is this
-// launch's: a reader can poll the data itself instead of a completion counter, and the writer
-// needs neither a store-completion wait nor a signal.
+// decode step's parity (a relative change of at most 2^-23).  Each value is written once per step
+// and consecutive steps differ in parity (within a launch and across launches), so a value that
+// shows the current parity is this step's: a reader can poll the data itself instead of a
+// completion counter, and the writer needs neither a store-completion wait nor a signal.
 __device__ __forceinline__ float tagv(float v, u32 par) {
   return __builtin_bit_cast(float, (__builtin_bit_cast(u32, v) & ~1u) | par);
 }
@@ -378,7 +378,7 @@ __device__ __forceinline__ float tagged_fix(const KArgs& A, const float* p, floa
   return v;
 }
 __device__ __forceinline__ float ld_tagged(const KArgs& A, const float* p) { return tagged_fix(A, p, ld_sc1(p)); }
-// row_ok[b] holds tag << 1 | ok, written once per launch by EMBED: wait for this launch's entry.
+// row_ok[b] holds tag << 1 | ok, written once per step by EMBED: wait for this step's entry.
 __device__ __forceinline__ bool row_ok_wait(const KArgs& A, int b) {
   const u32 want = ctag() & 0x7FFFFFFFu;
   u32 v = (u32)ld_i32_sc1(A.row_ok + b);
@@ -910,7 +910,7 @@ __device__ __forceinline__ void op_embed(const KArgs& A, u32 w) {
   // Rows of the attention / delta output that no mixer op writes this launch -- sequences that do
   // not take part in an attention layer (past the batch, or a context out of range) and rows past
   // max_batch of a delta layer -- get tagged zeros here, this CU's slice of each, so that every
-  // tagged value is written exactly once per launch and o_proj can poll every row.
+  // tagged value is written exactly once per step and o_proj can poll every row.
   bool live[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) live[b] = b < A.batch && clamp_ctx(A, step_ctx(A, b)) > 0;
@@ -1713,9 +1713,9 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   const AttnItem it = ic.get(A, o.row0, PPS);
   const LayerDesc Ld = sload(A.layers + o.layer);
   if (!it.valid) {
-    // An item with no chunk this launch still writes its partial slot (tagged zeros), so that every
-    // tagged value is written exactly once per launch: a later launch whose plan gives this item a
-    // chunk then finds the previous launch's parity here until the real partial lands.
+    // An item with no chunk this step still writes its partial slot (tagged zeros), so that every
+    // tagged value is written exactly once per step: a later step whose plan gives this item a
+    // chunk then finds the previous step's parity here until the real partial lands.
     float* part = (float*)Ld.part + (size_t)o.row0 * GMAX * (D + 4);
     for (int t = (int)(w * 64 + lane); t < A.G * (D + 4); t += NC * 64) st_tag(part + t, 0.0f, ctag() & 1u);
     return true;
