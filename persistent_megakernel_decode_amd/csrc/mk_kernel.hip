@@ -2073,115 +2073,168 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
 // The q / k conv state is shared by the blocks of (b, h): the last block to finish writes it.
 template <int DK>
 __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
+  // Item = (sequence, head, block of 32 value columns, i.e. 32 rows of S^T).  Wave w takes rows
+  // 4w .. 4w + 3.  Every input the wave needs (the q / k conv windows and new inputs of the whole
+  // head, its four value channels, the gates) is loaded at once, so the op pays one memory round
+  // trip before its rows rather than one per dependent load.
   constexpr int DPL = DK / 64;
   constexpr int RPS = SLOT / (DK * 4);  // S^T rows per slot
   constexpr int NSL = 32 / RPS;
+  constexpr int RPW = 32 / NC;          // rows per wave
+  constexpr int CW = 4;                 // conv width (the host accepts 4 only)
+  (void)gen;
   const u32 lane = lane_id();
   const u32 ncb = (u32)A.dv / 32, cb = o.row0 % ncb, bh = o.row0 / ncb;
   const int b = (int)(bh / (u32)A.nh), h = (int)(bh % (u32)A.nh);
   const LayerDesc Ld = sload(A.layers + o.layer);
   const bool ok = row_ok_local(A, b);
-  const int C = A.C, W = A.convw;
+  const int C = A.C;
   const int ldu = C + 2 * A.nh;
   const float* u = (const float*)Ld.qkv + (size_t)b * ldu;
   const float* gts = (const float*)Ld.gates + (size_t)b * ldu;
   const bool tagged = (o.flags & OPF_TAGGED_IN) != 0;
-  auto rd = [&](const float* p) { return tagged ? ld_tagged(A, p) : ld_sc1(p); };
-  float* cst = (float*)Ld.conv_state + (size_t)b * C * (W - 1);
+  float* cst = (float*)Ld.conv_state + (size_t)b * C * (CW - 1);
   const uint16_t* cw = (const uint16_t*)Ld.conv_w;
+  const int jw = (int)cb * 32 + (int)w * RPW;  // this wave's first row (value column)
+  const u32 ws = (w * RPW) / RPS;               // the slot holding its rows
+  const int r0 = (int)(w * RPW) % RPS;
 
-  auto conv = [&](int c, float* newstate_last) -> float {  // causal conv of channel c with its window
-    float acc = 0.0f;
-    for (int j = 0; j < W - 1; ++j) acc += bf2f(cw[(size_t)c * W + j]) * ld_sc1(cst + (size_t)c * (W - 1) + j);
-    const float x = rd(u + c);
-    acc += bf2f(cw[(size_t)c * W + W - 1]) * x;
-    *newstate_last = x;
-    return silu(acc);
-  };
-
-  const u32 seq0 = seq;
-  seq += NSL;
-  release_upto(w, seq0 + min(w, (u32)NSL));
-  for (u32 s = w; s < (u32)NSL; s += NC) {
-    const u32 sq = seq0 + s;
-    if (!wait_full(A, sq)) return false;
-    float q[DPL], k[DPL], xq[DPL], xk[DPL];
+  // all loads first
+  float qs[DPL][CW - 1], ks[DPL][CW - 1], qx[DPL], kx[DPL], vs[CW - 1], vx = 0.0f;
+  uint2 cq[DPL], ck[DPL], cv = {0u, 0u};
+  const int vch = 2 * A.nh * DK + h * A.dv + jw + (int)(lane % RPW);
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    const int chq = h * DK + (int)lane * DPL + e, chk = A.nh * DK + chq;
+#pragma unroll
+    for (int j = 0; j < CW - 1; ++j) {
+      qs[e][j] = ld_sc1(cst + (size_t)chq * (CW - 1) + j);
+      ks[e][j] = ld_sc1(cst + (size_t)chk * (CW - 1) + j);
+    }
+    qx[e] = ld_sc1(u + chq);
+    kx[e] = ld_sc1(u + chk);
+    cq[e] = *(const uint2*)(cw + (size_t)chq * CW);
+    ck[e] = *(const uint2*)(cw + (size_t)chk * CW);
+  }
+#pragma unroll
+  for (int j = 0; j < CW - 1; ++j) vs[j] = lane < (u32)RPW ? ld_sc1(cst + (size_t)vch * (CW - 1) + j) : 0.0f;
+  if (lane < (u32)RPW) {
+    vx = ld_sc1(u + vch);
+    cv = *(const uint2*)(cw + (size_t)vch * CW);
+  }
+  float ga = ld_sc1(gts + h), be = ld_sc1(gts + A.nh + h);
+  if (tagged) {  // inputs written this step by the in-projection: wait for any not yet landed
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
-      const int i = (int)lane * DPL + e;
-      q[e] = conv(h * DK + i, &xq[e]);
-      k[e] = conv(A.nh * DK + h * DK + i, &xk[e]);
+      qx[e] = tagged_fix(A, u + h * DK + (int)lane * DPL + e, qx[e]);
+      kx[e] = tagged_fix(A, u + A.nh * DK + h * DK + (int)lane * DPL + e, kx[e]);
     }
-    float nq = 0.0f, nk = 0.0f;
+    if (lane < (u32)RPW) vx = tagged_fix(A, u + vch, vx);
+    ga = tagged_fix(A, gts + h, ga);
+    be = tagged_fix(A, gts + A.nh + h, be);
+  }
+  auto conv = [](const uint2 wts, const float* st, float x) {  // causal conv of one channel, then SiLU
+    float acc = 0.0f;
+    acc += bflo(wts.x) * st[0];
+    acc += bfhi(wts.x) * st[1];
+    acc += bflo(wts.y) * st[2];
+    acc += bfhi(wts.y) * x;
+    return silu(acc);
+  };
+  float q[DPL], k[DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) { nq += q[e] * q[e]; nk += k[e] * k[e]; }
-    nq = wave_sum(nq); nk = wave_sum(nk);
-    const float rq = 1.0f / sqrtf(nq + 1e-6f) / sqrtf((float)DK), rk = 1.0f / sqrtf(nk + 1e-6f);
+  for (int e = 0; e < DPL; ++e) {
+    q[e] = conv(cq[e], qs[e], qx[e]);
+    k[e] = conv(ck[e], ks[e], kx[e]);
+  }
+  float nq = 0.0f, nk = 0.0f;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) { q[e] *= rq; k[e] *= rk; }
-    const float gate = 1.0f / (1.0f + __expf(-rd(gts + h)));
-    const float beta = 1.0f / (1.0f + __expf(-rd(gts + A.nh + h)));
-    // value channels of this slot's rows: lane r < RPS computes row r's conv
-    const int j0 = (int)cb * 32 + (int)s * RPS;
-    const int vch = 2 * A.nh * DK + h * A.dv + j0 + (int)lane;
-    float vx = 0.0f, vval = 0.0f;
-    if ((int)lane < RPS) vval = conv(vch, &vx);
-    const float* srows = (const float*)(g_ring + (sq % NSLOT) * (SLOT / 16));
-    float* sdst = (float*)Ld.delta_state + (((size_t)bh * A.dv + j0) * DK);
-    for (int r = 0; r < RPS; ++r) {
-      float sv[DPL];
+  for (int e = 0; e < DPL; ++e) { nq += q[e] * q[e]; nk += k[e] * k[e]; }
+  nq = wave_sum(nq);
+  nk = wave_sum(nk);
+  const float rq = 1.0f / sqrtf(nq + 1e-6f) / sqrtf((float)DK), rk = 1.0f / sqrtf(nk + 1e-6f);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) sv[e] = srows[r * DK + lane * DPL + e];
-      float kS = 0.0f;
+  for (int e = 0; e < DPL; ++e) { q[e] *= rq; k[e] *= rk; }
+  const float gate = 1.0f / (1.0f + __expf(-ga));
+  const float beta = 1.0f / (1.0f + __expf(-be));
+  const float vval = lane < (u32)RPW ? conv(cv, vs, vx) : 0.0f;  // lane r: value of row jw + r
+
+  // this wave's rows of S^T
+  const u32 seq0 = seq;
+  seq += NSL;
+  release_upto(w, seq0 + ws);  // slots before this wave's own are other waves'
+  if (!wait_full(A, seq0 + ws)) return false;
+  const float* srows = (const float*)(g_ring + ((seq0 + ws) % NSLOT) * (SLOT / 16)) + r0 * DK;
+  float sv[RPW][DPL], kS[RPW], oj[RPW];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) kS += sv[e] * k[e];
-      kS = wave_sum(kS);
-      const float vj = __shfl(vval, r, 64);
-      const float err = vj - kS;
-      float oj = 0.0f;
+  for (int r = 0; r < RPW; ++r) {
+    kS[r] = 0.0f;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        sv[e] = gate * sv[e] + beta * k[e] * err;
-        oj += sv[e] * q[e];
-      }
-      oj = wave_sum(oj);
-      if (ok) {
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) st_sc1(sdst + (size_t)r * DK + lane * DPL + e, sv[e]);
-      }
-      // every item writes its outputs (zero for a row out of contract), tagged
-      if (lane == 0) st_tag((float*)Ld.mix_o + (size_t)b * A.mix + h * A.dv + j0 + r, ok ? oj : 0.0f, ctag() & 1u);
+    for (int e = 0; e < DPL; ++e) {
+      sv[r][e] = srows[r * DK + lane * DPL + e];
+      kS[r] += sv[r][e] * k[e];
     }
-    // rolling conv state of this slot's value channels
-    if (ok && (int)lane < RPS) {  // (agent-coherent: the next step may run this block elsewhere)
-      float* st = cst + (size_t)vch * (W - 1);
-      for (int j = 0; j + 1 < W - 1; ++j) st_sc1(st + j, ld_sc1(st + j + 1));
-      st_sc1(st + W - 2, vx);
-    }
-    (void)xq; (void)xk;
-    release_upto(w, seq0 + min(s + NC, (u32)NSL));
   }
   release_upto(w, seq0 + NSL);
-  // q / k conv states: written once all blocks of (b, h) have read them (ticket)
-  __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));
-  if (!cbar(A, gen)) return false;
-  u32* ticket = (u32*)Ld.tickets + bh;
-  if (w == 0 && lane == 0) {
-    const u32 prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    g_bcast[0] = (prev == ncb - 1) ? 1u : 0u;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) kS[r] = wave_sum(kS[r]);
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const float err = __shfl(vval, r, 64) - kS[r];
+    oj[r] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      sv[r][e] = gate * sv[r][e] + beta * k[e] * err;
+      oj[r] += sv[r][e] * q[e];
+    }
   }
-  if (!cbar(A, gen)) return false;
-  if (lds_ld(&g_bcast[0])) {
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) oj[r] = wave_sum(oj[r]);
+  float* sdst = (float*)Ld.delta_state + (((size_t)bh * A.dv + jw) * DK);
+  if (ok) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) st_sc1(sdst + (size_t)r * DK + lane * DPL + e, sv[r][e]);
+  }
+  // every item writes its outputs (zero for a row out of contract), tagged
+  if (lane < (u32)RPW) {
+    float mine = oj[0];
+#pragma unroll
+    for (int r = 1; r < RPW; ++r) mine = lane == (u32)r ? oj[r] : mine;
+    st_tag((float*)Ld.mix_o + (size_t)b * A.mix + h * A.dv + jw + lane, ok ? mine : 0.0f, ctag() & 1u);
+    // rolling conv window of this row's value channel (agent-coherent: the next step may run
+    // this block on another CU)
     if (ok) {
-      for (int t = (int)(w * 64 + lane); t < 2 * DK; t += NC * 64) {
-        const int c = t < DK ? h * DK + t : A.nh * DK + h * DK + (t - DK);
-        const float x = rd(u + c);
-        float* st = cst + (size_t)c * (W - 1);
-        for (int j = 0; j + 1 < W - 1; ++j) st_sc1(st + j, ld_sc1(st + j + 1));
-        st_sc1(st + W - 2, x);
+      float* st = cst + (size_t)vch * (CW - 1);
+      st_sc1(st, vs[1]);
+      st_sc1(st + 1, vs[2]);
+      st_sc1(st + 2, vx);
+    }
+  }
+  // The q / k conv windows are read by every wave of the head's ncb items; the last of those
+  // waves to take a ticket (all the others have their window values in hand by then) writes the
+  // new windows from its registers and resets the ticket for the next step.
+  u32* ticket = (u32*)Ld.tickets + bh;
+  u32 prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  if (prev == ncb * NC - 1) {
+    if (ok) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const int chq = h * DK + (int)lane * DPL + e, chk = A.nh * DK + chq;
+        float* sq = cst + (size_t)chq * (CW - 1);
+        float* sk = cst + (size_t)chk * (CW - 1);
+        st_sc1(sq, qs[e][1]);
+        st_sc1(sq + 1, qs[e][2]);
+        st_sc1(sq + 2, qx[e]);
+        st_sc1(sk, ks[e][1]);
+        st_sc1(sk + 1, ks[e][2]);
+        st_sc1(sk + 2, kx[e]);
       }
     }
-    if (w == 0 && lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(gptr(ticket), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   return true;
 }
