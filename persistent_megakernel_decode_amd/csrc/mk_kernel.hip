@@ -720,7 +720,9 @@ __device__ __forceinline__ void issue_mmv(const GemvSeg& gsg, u32 s, u32 nt, u32
   const u32 r = trow + lrow < nrows ? trow + lrow : trow;
   const char* vaddr = gemv_row(gsg, half0 + r) + (size_t)kseg * (MMV_KSEG * 2) + chunk * 16;
   char* lds = (char*)dst;
-#define MK_MMV_DMA(j) __builtin_amdgcn_global_load_lds(vaddr, (__attribute__((address_space(3))) void*)(lds + (j) * 960), 16, (j) * 64, AUX_NT)
+  // plain (cacheable) loads: each instruction touches 16 rows x 64 bytes, half of a 128-byte line,
+  // whose other half the next instruction reads; as non-temporal loads the 13B step was 4 % slower
+#define MK_MMV_DMA(j) __builtin_amdgcn_global_load_lds(vaddr, (__attribute__((address_space(3))) void*)(lds + (j) * 960), 16, (j) * 64, 0)
   MK_MMV_DMA(0); MK_MMV_DMA(1); MK_MMV_DMA(2); MK_MMV_DMA(3);
   MK_MMV_DMA(4); MK_MMV_DMA(5); MK_MMV_DMA(6); MK_MMV_DMA(7);
 #undef MK_MMV_DMA
