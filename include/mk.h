@@ -147,6 +147,21 @@ mk_status mk_decode_step(mk_ctx* ctx, const int32_t* tokens, const int32_t* posi
 mk_status mk_decode_steps(mk_ctx* ctx, const int32_t* tokens, const int32_t* positions, const int32_t* ctx_lens,
                           int32_t batch, int32_t n_steps, float* logits_out, int32_t* tokens_out, void* hip_stream);
 
+/* A speculative-decoding verify window: `window` consecutive tokens of each sequence in ONE step,
+ * as the MK-KDA pull request's multi-token window runs (github choiceoh/stkernel #230, commit
+ * message: a spec window of at most 8 query tokens, the host refusing wider ones).  Token t
+ * (0 <= t < window) of sequence b is tokens[b * window + t] at position positions[b] + t and sees
+ * ctx_lens[b] + t cached tokens (positions[b] == ctx_lens[b] - 1): the cache up to positions[b]
+ * and the window's earlier tokens, exactly as `window` calls of mk_decode_step fed these tokens
+ * would.  Every window token's K/V is appended.  logits_out[b][t][vocab] fp32 (device, 16-byte
+ * aligned).  1 <= window <= MK_MAX_WINDOW, batch * window <= max_batch (the window's tokens run
+ * as rows of the batched projections).  Pages for positions[b] .. positions[b] + window - 1 must
+ * be mapped.  MK_ERR_UNSUPPORTED for models with delta-rule layers (their recurrence over the
+ * window is not built).  Asynchronous on hip_stream; errors as for mk_decode_step. */
+#define MK_MAX_WINDOW 8
+mk_status mk_decode_window(mk_ctx* ctx, const int32_t* tokens, const int32_t* positions, const int32_t* ctx_lens,
+                           int32_t batch, int32_t window, float* logits_out, void* hip_stream);
+
 /* mk_create for callers that cannot allocate device memory (code under HIP graph capture,
  * allocation-free serving loops, harnesses that forbid hipMalloc): the same context, with the
  * library's static device scratch of MK_STATIC_SCRATCH_BYTES as its workspace instead of a

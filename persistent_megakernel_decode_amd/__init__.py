@@ -76,9 +76,10 @@ MK_EMU_COUNTERS, MK_EMU_IDLE_ITEMS_SILENT, MK_EMU_DEAD_ROWS_SILENT, MK_EMU_STALL
 
 EXPORTED = ["mk_workspace_size", "mk_create", "mk_decode_step", "mk_sync_status", "mk_reset", "mk_last_error",
             "mk_destroy", "mk_plan", "mk_emulate", "mk_copy_midstate", "mk_trace_words", "mk_copy_trace",
-            "mk_create_static", "mk_decode_steps", "mk_stream_read"]
+            "mk_create_static", "mk_decode_steps", "mk_stream_read", "mk_decode_window"]
 MK_STATIC_SCRATCH_BYTES = 64 << 20
 MK_MAX_STEPS = 4096
+MK_MAX_WINDOW = 8
 TRACE_WORDS = 8  # per-op trace record (mk_internal.h)
 
 _lib = None
@@ -100,6 +101,7 @@ def lib() -> ctypes.CDLL:
         L.mk_decode_step.argtypes = [P, P, P, P, I32, P, P]
         L.mk_decode_steps.argtypes = [P, P, P, P, I32, I32, P, P, P]
         L.mk_stream_read.argtypes = [P, ctypes.c_size_t, P, I32, P]
+        L.mk_decode_window.argtypes = [P, P, P, P, I32, I32, P, P]
         L.mk_sync_status.argtypes = [P]
         L.mk_reset.argtypes = [P]
         L.mk_last_error.argtypes = []
@@ -112,7 +114,7 @@ def lib() -> ctypes.CDLL:
         L.mk_copy_midstate.argtypes = [P, I32, I32, P, ctypes.c_size_t, P]
         L.mk_trace_words.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         L.mk_copy_trace.argtypes = [P, P, ctypes.c_size_t]
-        for f in ("mk_workspace_size", "mk_create", "mk_create_static", "mk_decode_step", "mk_decode_steps", "mk_stream_read", "mk_sync_status", "mk_reset", "mk_plan",
+        for f in ("mk_workspace_size", "mk_create", "mk_create_static", "mk_decode_step", "mk_decode_steps", "mk_stream_read", "mk_decode_window", "mk_sync_status", "mk_reset", "mk_plan",
                   "mk_emulate", "mk_copy_midstate", "mk_trace_words", "mk_copy_trace"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -196,6 +198,12 @@ def mk_decode_steps(ctx: int, tokens_ptr: int, positions_ptr: int, ctx_lens_ptr:
                     logits_ptr: int, tokens_out_ptr: int, stream: int = 0) -> int:
     return lib().mk_decode_steps(ctx, tokens_ptr, positions_ptr, ctx_lens_ptr, batch, n_steps, logits_ptr,
                                  tokens_out_ptr, stream or None)
+
+
+def mk_decode_window(ctx: int, tokens_ptr: int, positions_ptr: int, ctx_lens_ptr: int, batch: int, window: int,
+                     logits_ptr: int, stream: int = 0) -> int:
+    return lib().mk_decode_window(ctx, tokens_ptr, positions_ptr, ctx_lens_ptr, batch, window, logits_ptr,
+                                  stream or None)
 
 
 def mk_stream_read(buf_ptr: int, nbytes: int, out_ptr: int, blocks: int, stream: int = 0) -> int:
@@ -337,6 +345,23 @@ class DecodeContext:
         rc = mk_decode_steps(self.ctx, self.tokens.data_ptr(), self.positions.data_ptr(), self.ctx_lens.data_ptr(),
                              B, n_steps, logits.data_ptr(), toks.data_ptr(), self.stream_ptr(stream))
         return rc, logits, toks
+
+    def window(self, tokens, positions, ctx_lens, stream=None):
+        """Enqueue one verify-window step from host data: tokens [batch][window], positions and
+        ctx_lens [batch] (of window token 0).  Returns (status, logits [batch][window][vocab]), the
+        logits a device tensor this call allocates."""
+        T = self.torch
+        tk = T.as_tensor(tokens, dtype=T.int32)
+        B, W = int(tk.shape[0]), int(tk.shape[1])
+        toks = T.zeros(max(4, B * W), dtype=T.int32, device=self.device)
+        toks[:B * W].copy_(tk.reshape(-1))
+        self.positions[:B].copy_(T.as_tensor(list(positions), dtype=T.int32))
+        self.ctx_lens[:B].copy_(T.as_tensor(list(ctx_lens), dtype=T.int32))
+        logits = T.empty((B, W, self.shape["vocab"]), dtype=T.float32, device=self.device)
+        self._window_tokens = toks  # kept alive until the launch has run
+        rc = mk_decode_window(self.ctx, toks.data_ptr(), self.positions.data_ptr(), self.ctx_lens.data_ptr(), B, W,
+                              logits.data_ptr(), self.stream_ptr(stream))
+        return rc, logits
 
     def sync(self) -> int:
         return mk_sync_status(self.ctx)

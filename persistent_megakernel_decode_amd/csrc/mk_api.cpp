@@ -354,6 +354,7 @@ static mk_status create_impl(const mk_model_desc* desc, const mk_weights* w, con
   A.nh = d.n_delta_heads; A.dk = d.delta_dk; A.dv = d.delta_dv; A.C = m.C; A.convw = d.conv_width;
   A.n_cus = ncu; A.n_items = P.n_items; A.mix = P.mix_dim;
   A.rms_eps = d.rms_eps;
+  A.win = 1;      // mk_decode_window overrides it
   A.n_steps = 1;  // mk_decode_steps overrides these four
   A.n_lm = P.n_lm;
   A.tokens_out = nullptr;
@@ -472,6 +473,31 @@ mk_status mk_decode_step(mk_ctx* ctx, const int32_t* tokens, const int32_t* posi
   A.ctx_lens = ctx_lens;
   A.logits = logits_out;
   A.batch = batch;
+  return launch_steps(ctx, A, 1, ctx->kernel, (hipStream_t)hip_stream);
+}
+
+mk_status mk_decode_window(mk_ctx* ctx, const int32_t* tokens, const int32_t* positions, const int32_t* ctx_lens,
+                           int32_t batch, int32_t window, float* logits_out, void* hip_stream) {
+  if (!ctx) return fail(MK_ERR_INVALID_ARG, "ctx is null");
+  if (window < 1 || window > MK_MAX_WINDOW)
+    return fail(MK_ERR_INVALID_ARG, "window " + std::to_string(window) + " outside [1, MK_MAX_WINDOW]");
+  if (batch < 1 || (int64_t)batch * window > ctx->shape.d.max_batch)
+    return fail(MK_ERR_INVALID_ARG, "batch * window = " + std::to_string((int64_t)batch * window) +
+                                        " outside [1, max_batch]");
+  if (ctx->shape.n_delta > 0)
+    return fail(MK_ERR_UNSUPPORTED, "verify windows are not built for models with delta-rule layers");
+  mk_status r = check_step_args(ctx, tokens, positions, ctx_lens, batch * window, logits_out);
+  if (r != MK_OK) return r;
+  std::unique_lock<std::mutex> lk(ctx->busy, std::try_to_lock);
+  if (!lk.owns_lock()) return fail(MK_ERR_STATE, "another thread is stepping this context");
+  MK_CHECK_SCRATCH(ctx);
+  mk::KArgs A = ctx->args;
+  A.tokens = tokens;
+  A.positions = positions;
+  A.ctx_lens = ctx_lens;
+  A.logits = logits_out;
+  A.batch = batch * window;  // rows
+  A.win = window;
   return launch_steps(ctx, A, 1, ctx->kernel, (hipStream_t)hip_stream);
 }
 
