@@ -156,8 +156,10 @@ mk_status mk_decode_steps(mk_ctx* ctx, const int32_t* tokens, const int32_t* pos
  * would.  Every window token's K/V is appended.  logits_out[b][t][vocab] fp32 (device, 16-byte
  * aligned).  1 <= window <= MK_MAX_WINDOW, batch * window <= max_batch (the window's tokens run
  * as rows of the batched projections).  Pages for positions[b] .. positions[b] + window - 1 must
- * be mapped.  MK_ERR_UNSUPPORTED for models with delta-rule layers (their recurrence over the
- * window is not built).  Asynchronous on hip_stream; errors as for mk_decode_step. */
+ * be mapped.  Delta-rule layers run their recurrence over the window's tokens in order (the conv
+ * window rolling through them, the state written back after the last); a sequence with any window
+ * token out of contract gets zero outputs and no state write.  Asynchronous on hip_stream; errors
+ * as for mk_decode_step. */
 #define MK_MAX_WINDOW 8
 mk_status mk_decode_window(mk_ctx* ctx, const int32_t* tokens, const int32_t* positions, const int32_t* ctx_lens,
                            int32_t batch, int32_t window, float* logits_out, void* hip_stream);

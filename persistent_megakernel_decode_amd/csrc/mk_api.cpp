@@ -484,8 +484,6 @@ mk_status mk_decode_window(mk_ctx* ctx, const int32_t* tokens, const int32_t* po
   if (batch < 1 || (int64_t)batch * window > ctx->shape.d.max_batch)
     return fail(MK_ERR_INVALID_ARG, "batch * window = " + std::to_string((int64_t)batch * window) +
                                         " outside [1, max_batch]");
-  if (ctx->shape.n_delta > 0)
-    return fail(MK_ERR_UNSUPPORTED, "verify windows are not built for models with delta-rule layers");
   mk_status r = check_step_args(ctx, tokens, positions, ctx_lens, batch * window, logits_out);
   if (r != MK_OK) return r;
   std::unique_lock<std::mutex> lk(ctx->busy, std::try_to_lock);

@@ -2117,9 +2117,10 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
 template <int DK>
 __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
   // Item = (sequence, head, block of 32 value columns, i.e. 32 rows of S^T).  Wave w takes rows
-  // 4w .. 4w + 3.  Every input the wave needs (the q / k conv windows and new inputs of the whole
-  // head, its four value channels, the gates) is loaded at once, so the op pays one memory round
-  // trip before its rows rather than one per dependent load.
+  // 4w .. 4w + 3.  A verify window of T tokens runs the recurrence over the window's rows in
+  // order: the conv windows roll through the tokens in registers, S stays in registers, and the
+  // state written back is the one after the last token.  A token's inputs (its rows' conv inputs
+  // and gates) are loaded together, the first token's before the op waits for its S rows.
   constexpr int DPL = DK / 64;
   constexpr int RPS = SLOT / (DK * 4);  // S^T rows per slot
   constexpr int NSL = 32 / RPS;
@@ -2130,77 +2131,68 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
   const u32 ncb = (u32)A.dv / 32, cb = o.row0 % ncb, bh = o.row0 / ncb;
   const int b = (int)(bh / (u32)A.nh), h = (int)(bh % (u32)A.nh);
   const LayerDesc Ld = sload(A.layers + o.layer);
-  const bool ok = row_ok_local(A, b);
+  const int T = A.win;
+  const int nseq = T == 1 ? A.batch : A.batch / T;
   const int C = A.C;
   const int ldu = C + 2 * A.nh;
-  const float* u = (const float*)Ld.qkv + (size_t)b * ldu;
-  const float* gts = (const float*)Ld.gates + (size_t)b * ldu;
   const bool tagged = (o.flags & OPF_TAGGED_IN) != 0;
   float* cst = (float*)Ld.conv_state + (size_t)b * C * (CW - 1);
   const uint16_t* cw = (const uint16_t*)Ld.conv_w;
   const int jw = (int)cb * 32 + (int)w * RPW;  // this wave's first row (value column)
   const u32 ws = (w * RPW) / RPS;               // the slot holding its rows
   const int r0 = (int)(w * RPW) % RPS;
+  const u32 par = ctag() & 1u;
+  float* mix = (float*)Ld.mix_o + h * A.dv + jw;
+  // This item is sequence b's if b < nseq.  Otherwise it writes the zero outputs of row b when b
+  // lies past the batch (rows [nseq, batch) of a window are its sequences' tokens).
+  bool ok = b < nseq;
+  for (int t = 0; t < T && ok; ++t) ok = row_ok_local(A, b * T + t);
 
-  // all loads first
-  float qs[DPL][CW - 1], ks[DPL][CW - 1], qx[DPL], kx[DPL], vs[CW - 1], vx = 0.0f;
+  float qw[DPL][CW - 1], kw[DPL][CW - 1], vw[CW - 1];  // conv windows, oldest first
   uint2 cq[DPL], ck[DPL], cv = {0u, 0u};
   const int vch = 2 * A.nh * DK + h * A.dv + jw + (int)(lane % RPW);
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) {
-    const int chq = h * DK + (int)lane * DPL + e, chk = A.nh * DK + chq;
-#pragma unroll
-    for (int j = 0; j < CW - 1; ++j) {
-      qs[e][j] = ld_sc1(cst + (size_t)chq * (CW - 1) + j);
-      ks[e][j] = ld_sc1(cst + (size_t)chk * (CW - 1) + j);
-    }
-    qx[e] = ld_sc1(u + chq);
-    kx[e] = ld_sc1(u + chk);
-    cq[e] = *(const uint2*)(cw + (size_t)chq * CW);
-    ck[e] = *(const uint2*)(cw + (size_t)chk * CW);
-  }
-#pragma unroll
-  for (int j = 0; j < CW - 1; ++j) vs[j] = lane < (u32)RPW ? ld_sc1(cst + (size_t)vch * (CW - 1) + j) : 0.0f;
-  if (lane < (u32)RPW) {
-    vx = ld_sc1(u + vch);
-    cv = *(const uint2*)(cw + (size_t)vch * CW);
-  }
-  float ga = ld_sc1(gts + h), be = ld_sc1(gts + A.nh + h);
-  if (tagged) {  // inputs written this step by the in-projection: wait for any not yet landed
+  if (b < nseq) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
-      qx[e] = tagged_fix(A, u + h * DK + (int)lane * DPL + e, qx[e]);
-      kx[e] = tagged_fix(A, u + A.nh * DK + h * DK + (int)lane * DPL + e, kx[e]);
+      const int chq = h * DK + (int)lane * DPL + e, chk = A.nh * DK + chq;
+#pragma unroll
+      for (int j = 0; j < CW - 1; ++j) {
+        qw[e][j] = ld_sc1(cst + (size_t)chq * (CW - 1) + j);
+        kw[e][j] = ld_sc1(cst + (size_t)chk * (CW - 1) + j);
+      }
+      cq[e] = *(const uint2*)(cw + (size_t)chq * CW);
+      ck[e] = *(const uint2*)(cw + (size_t)chk * CW);
     }
-    if (lane < (u32)RPW) vx = tagged_fix(A, u + vch, vx);
-    ga = tagged_fix(A, gts + h, ga);
-    be = tagged_fix(A, gts + A.nh + h, be);
+#pragma unroll
+    for (int j = 0; j < CW - 1; ++j) vw[j] = lane < (u32)RPW ? ld_sc1(cst + (size_t)vch * (CW - 1) + j) : 0.0f;
+    if (lane < (u32)RPW) cv = *(const uint2*)(cw + (size_t)vch * CW);
   }
-  auto conv = [](const uint2 wts, const float* st, float x) {  // causal conv of one channel, then SiLU
-    float acc = 0.0f;
-    acc += bflo(wts.x) * st[0];
-    acc += bfhi(wts.x) * st[1];
-    acc += bflo(wts.y) * st[2];
-    acc += bfhi(wts.y) * x;
-    return silu(acc);
+  // token t's conv inputs and gates (row b T + t)
+  float qx[DPL], kx[DPL], vx = 0.0f, ga = 0.0f, be = 0.0f;
+  auto load_token = [&](int t) {
+    const int row = b * T + t;
+    const float* u = (const float*)Ld.qkv + (size_t)row * ldu;
+    const float* gts = (const float*)Ld.gates + (size_t)row * ldu;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      qx[e] = ld_sc1(u + h * DK + (int)lane * DPL + e);
+      kx[e] = ld_sc1(u + A.nh * DK + h * DK + (int)lane * DPL + e);
+    }
+    if (lane < (u32)RPW) vx = ld_sc1(u + vch);
+    ga = ld_sc1(gts + h);
+    be = ld_sc1(gts + A.nh + h);
+    if (tagged) {  // inputs written this step by the in-projection: wait for any not yet landed
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        qx[e] = tagged_fix(A, u + h * DK + (int)lane * DPL + e, qx[e]);
+        kx[e] = tagged_fix(A, u + A.nh * DK + h * DK + (int)lane * DPL + e, kx[e]);
+      }
+      if (lane < (u32)RPW) vx = tagged_fix(A, u + vch, vx);
+      ga = tagged_fix(A, gts + h, ga);
+      be = tagged_fix(A, gts + A.nh + h, be);
+    }
   };
-  float q[DPL], k[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) {
-    q[e] = conv(cq[e], qs[e], qx[e]);
-    k[e] = conv(ck[e], ks[e], kx[e]);
-  }
-  float nq = 0.0f, nk = 0.0f;
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) { nq += q[e] * q[e]; nk += k[e] * k[e]; }
-  nq = wave_sum(nq);
-  nk = wave_sum(nk);
-  const float rq = 1.0f / sqrtf(nq + 1e-6f) / sqrtf((float)DK), rk = 1.0f / sqrtf(nk + 1e-6f);
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) { q[e] *= rq; k[e] *= rk; }
-  const float gate = 1.0f / (1.0f + __expf(-ga));
-  const float beta = 1.0f / (1.0f + __expf(-be));
-  const float vval = lane < (u32)RPW ? conv(cv, vs, vx) : 0.0f;  // lane r: value of row jw + r
+  if (b < nseq) load_token(0);
 
   // this wave's rows of S^T
   const u32 seq0 = seq;
@@ -2208,51 +2200,87 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
   release_upto(w, seq0 + ws);  // slots before this wave's own are other waves'
   if (!wait_full(A, seq0 + ws)) return false;
   const float* srows = (const float*)(g_ring + ((seq0 + ws) % NSLOT) * (SLOT / 16)) + r0 * DK;
-  float sv[RPW][DPL], kS[RPW], oj[RPW];
+  float sv[RPW][DPL];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    kS[r] = 0.0f;
+  for (int r = 0; r < RPW; ++r)
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      sv[r][e] = srows[r * DK + lane * DPL + e];
-      kS[r] += sv[r][e] * k[e];
-    }
-  }
+    for (int e = 0; e < DPL; ++e) sv[r][e] = srows[r * DK + lane * DPL + e];
   release_upto(w, seq0 + NSL);
+
+  if (b >= nseq) {
+    if (b >= A.batch && lane < (u32)RPW) st_tag(mix + (size_t)b * A.mix + lane, 0.0f, par);
+  } else {
+    auto conv = [](const uint2 wts, float* win, float x) {  // causal conv of one channel, then SiLU
+      float acc = 0.0f;
+      acc += bflo(wts.x) * win[0];
+      acc += bfhi(wts.x) * win[1];
+      acc += bflo(wts.y) * win[2];
+      acc += bfhi(wts.y) * x;
+      win[0] = win[1];  // the window rolls on to this token's input
+      win[1] = win[2];
+      win[2] = x;
+      return silu(acc);
+    };
+    for (int t = 0; t < T; ++t) {
+      if (t > 0) load_token(t);
+      float q[DPL], k[DPL];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) kS[r] = wave_sum(kS[r]);
+      for (int e = 0; e < DPL; ++e) {
+        q[e] = conv(cq[e], qw[e], qx[e]);
+        k[e] = conv(ck[e], kw[e], kx[e]);
+      }
+      float nq = 0.0f, nk = 0.0f;
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const float err = __shfl(vval, r, 64) - kS[r];
-    oj[r] = 0.0f;
+      for (int e = 0; e < DPL; ++e) { nq += q[e] * q[e]; nk += k[e] * k[e]; }
+      nq = wave_sum(nq);
+      nk = wave_sum(nk);
+      const float rq = 1.0f / sqrtf(nq + 1e-6f) / sqrtf((float)DK), rk = 1.0f / sqrtf(nk + 1e-6f);
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      sv[r][e] = gate * sv[r][e] + beta * k[e] * err;
-      oj[r] += sv[r][e] * q[e];
+      for (int e = 0; e < DPL; ++e) { q[e] *= rq; k[e] *= rk; }
+      const float gate = 1.0f / (1.0f + __expf(-ga));
+      const float beta = 1.0f / (1.0f + __expf(-be));
+      float vval = 0.0f;  // lane r: value of row jw + r
+      if (lane < (u32)RPW) vval = conv(cv, vw, vx);
+      float kS[RPW], oj[RPW];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        kS[r] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) kS[r] += sv[r][e] * k[e];
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) kS[r] = wave_sum(kS[r]);
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const float err = __shfl(vval, r, 64) - kS[r];
+        oj[r] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+          sv[r][e] = gate * sv[r][e] + beta * k[e] * err;
+          oj[r] += sv[r][e] * q[e];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) oj[r] = wave_sum(oj[r]);
+      // every sequence item writes its rows' outputs (zero for a window out of contract), tagged
+      if (lane < (u32)RPW) {
+        float mine = oj[0];
+#pragma unroll
+        for (int r = 1; r < RPW; ++r) mine = lane == (u32)r ? oj[r] : mine;
+        st_tag(mix + (size_t)(b * T + t) * A.mix + lane, ok ? mine : 0.0f, par);
+      }
     }
-  }
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) oj[r] = wave_sum(oj[r]);
-  float* sdst = (float*)Ld.delta_state + (((size_t)bh * A.dv + jw) * DK);
-  if (ok) {
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) st_sc1(sdst + (size_t)r * DK + lane * DPL + e, sv[r][e]);
-  }
-  // every item writes its outputs (zero for a row out of contract), tagged
-  if (lane < (u32)RPW) {
-    float mine = oj[0];
-#pragma unroll
-    for (int r = 1; r < RPW; ++r) mine = lane == (u32)r ? oj[r] : mine;
-    st_tag((float*)Ld.mix_o + (size_t)b * A.mix + h * A.dv + jw + lane, ok ? mine : 0.0f, ctag() & 1u);
-    // rolling conv window of this row's value channel (agent-coherent: the next step may run
-    // this block on another CU)
     if (ok) {
-      float* st = cst + (size_t)vch * (CW - 1);
-      st_sc1(st, vs[1]);
-      st_sc1(st + 1, vs[2]);
-      st_sc1(st + 2, vx);
+      float* sdst = (float*)Ld.delta_state + (((size_t)bh * A.dv + jw) * DK);
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) st_sc1(sdst + (size_t)r * DK + lane * DPL + e, sv[r][e]);
+      if (lane < (u32)RPW) {  // this row's value-channel window (agent-coherent: the next step may
+        float* st = cst + (size_t)vch * (CW - 1);  // run this block on another CU)
+#pragma unroll
+        for (int j = 0; j < CW - 1; ++j) st_sc1(st + j, vw[j]);
+      }
     }
   }
   // The q / k conv windows are read by every wave of the head's ncb items; the last of those
@@ -2267,14 +2295,11 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
         const int chq = h * DK + (int)lane * DPL + e, chk = A.nh * DK + chq;
-        float* sq = cst + (size_t)chq * (CW - 1);
-        float* sk = cst + (size_t)chk * (CW - 1);
-        st_sc1(sq, qs[e][1]);
-        st_sc1(sq + 1, qs[e][2]);
-        st_sc1(sq + 2, qx[e]);
-        st_sc1(sk, ks[e][1]);
-        st_sc1(sk + 1, ks[e][2]);
-        st_sc1(sk + 2, kx[e]);
+#pragma unroll
+        for (int j = 0; j < CW - 1; ++j) {
+          st_sc1(cst + (size_t)chq * (CW - 1) + j, qw[e][j]);
+          st_sc1(cst + (size_t)chk * (CW - 1) + j, kw[e][j]);
+        }
       }
     }
     if (lane == 0) __hip_atomic_store(gptr(ticket), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

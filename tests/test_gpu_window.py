@@ -5,15 +5,16 @@ window tokens one step at a time (the window's semantics: a speculative draft ve
 pass): logits within 1e-2 max relative error, the oracle's greedy id wherever its top-2 gap exceeds
 1e-2.  A decode step after the window then checks the K/V rows the window appended.  Cases: batch
 1 and 2, windows of 2 to 8 tokens (the rows run on the batch-2, batch-4 and batch-8 kernels),
-head_dim 64 and 128, windows that cross a page and a chunk boundary, and a one-token window equal
-bit for bit to mk_decode_step.
+head_dim 64 and 128, windows that cross a page and a chunk boundary, the delta-rule hybrid with
+windows shorter and longer than its conv history (its recurrent and conv states checked against the
+oracle's after the window), and a one-token window equal bit for bit to mk_decode_step.
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from gpu_harness import GREEDY_GAP, LOGIT_REL_TOL, make_pair, say, top2_gap
+from gpu_harness import GREEDY_GAP, LOGIT_REL_TOL, STATE_RUN_TOL, make_pair, say, top2_gap
 
 pytestmark = pytest.mark.gpu
 
@@ -28,6 +29,13 @@ CASES = {
                                ffn=1024, vocab=2048, batch=4, ctx=[150, 31, 7, 7], steps=3, seed=22), 2, 2),
     "d128-b1-w5-chunks": (synth.Config("d128-w5", n_layers=2, hidden=512, n_q_heads=4, n_kv_heads=4, head_dim=128,
                                        ffn=1024, vocab=2048, batch=8, ctx=[1700] * 8, steps=3, seed=23), 1, 5),
+    # delta-rule hybrid (dk = dv = 64): windows shorter and longer than the conv history of 3
+    "hybrid-b1-w2": (synth.SMALL["tiny-hybrid"].replace(name="hyb-w2", delta_dk=64, delta_dv=64, batch=2, ctx=[16, 16]), 1, 2),
+    "hybrid-b2-w2": (synth.SMALL["tiny-hybrid"].replace(name="hyb-b2-w2", delta_dk=64, delta_dv=64, batch=4, ctx=[16, 40, 9, 9]), 2, 2),
+    "hybrid-d128-b2-w4": (synth.SMALL["tiny-hybrid"].replace(name="hyb-d128-w4", delta_dk=128, delta_dv=128, batch=8,
+                                                             ctx=[16, 40] + [9] * 6), 2, 4),
+    "hybrid-d128-b1-w8": (synth.SMALL["tiny-hybrid"].replace(name="hyb-d128-w8", delta_dk=128, delta_dv=128, batch=8,
+                                                             ctx=[33] * 8), 1, 8),
 }
 
 
@@ -85,6 +93,12 @@ def test_window_parity(case):
             worst = max(worst, rel)
             if rel > LOGIT_REL_TOL:
                 errs.append(f"step after the window, seq {b}: logits rel err {rel:.3e}")
+        if gpu.delta_state is not None:  # the states after the window and the step after it
+            for name, gv, ov in (("S", gpu.delta_state, orc.delta_state), ("conv state", gpu.conv_state, orc.conv_state)):
+                g, o = gv.cpu().numpy()[:, :B], np.asarray(ov)[:, :B]
+                e = float(np.linalg.norm(g.astype(np.float64) - o) / np.linalg.norm(o))
+                if e > STATE_RUN_TOL:
+                    errs.append(f"{name} normwise err {e:.3e} against the oracle run")
         say(f"[{case}] worst logits rel {worst:.2e}, greedy checked {checked}")
         assert not errs, "\n".join(errs[:20])
     finally:
@@ -124,12 +138,5 @@ def test_window_rejects_bad_arguments():
         assert mkd.mk_decode_window(gpu.ctx, *a, 1, mkd.MK_MAX_WINDOW + 1, lg) == mkd.MK_ERR_INVALID_ARG
         assert mkd.mk_decode_window(gpu.ctx, *a, 1, 0, lg) == mkd.MK_ERR_INVALID_ARG
         assert mkd.mk_decode_window(gpu.ctx, *a, 2, 3, lg) == mkd.MK_ERR_INVALID_ARG  # 6 rows > max_batch 4
-    finally:
-        gpu.close()
-    hy = synth.SMALL["tiny-hybrid"].replace(delta_dk=64, delta_dv=64, batch=4, ctx=[16] * 4)
-    w, cache, orc, gpu, ctx0 = make_pair(hy, 2)
-    try:
-        a = (gpu.tokens.data_ptr(), gpu.positions.data_ptr(), gpu.ctx_lens.data_ptr())
-        assert mkd.mk_decode_window(gpu.ctx, *a, 1, 2, gpu.logits.data_ptr()) == mkd.MK_ERR_UNSUPPORTED
     finally:
         gpu.close()
