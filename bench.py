@@ -13,8 +13,8 @@ the roofline of the megakernel (algorithmic bytes per launch / measured launch
 time vs 8 TB/s), the same decode continued as launches of several steps with
 the greedy token chosen on the device (multistep), the CPU oracle timed on a
 bounded sample of the same workload, the read ceiling of this GPU measured in
-the same run (stream_read), and the same figures for the other workloads
-(per_config).
+the same run (stream_read), the same figures for the other workloads
+(per_config), and verify windows of 8 tokens (verify_window).
 """
 from __future__ import annotations
 
@@ -343,7 +343,67 @@ def run_config(name: str, steps: int, warmup: int, multi_k: int, cpu_budget: flo
     return entry
 
 
+def run_window(name: str, window: int, launches: int, warmup: int) -> dict:
+    """Verify windows (mk_decode_window): `window` tokens of each sequence per step, the same
+    workload's weights and cache, a context compiled for batch x window rows."""
+    import torch
+    import synth
+    import persistent_megakernel_decode_amd as mkd
+
+    cfg = synth.CONFIGS[name]
+    B = cfg.batch
+    total = warmup + launches
+    ctx0 = synth.context_lengths(cfg)
+    w = synth.make_weights(cfg)
+    cache = synth.make_cache(cfg, ctx0, total * window)
+    max_ctx = int(cache["max_pages_per_seq"]) * cfg.page_size
+    shape = synth.shape_of(cfg, max_ctx)
+    shape["max_batch"] = B * window
+    g = mkd.DecodeContext(shape, w, cache, "cuda:0")
+    del cache
+    try:
+        draws = synth.u32(total * B * window, cfg.seed, "bench_window_tokens").reshape(total, B * window) % cfg.vocab
+        toks_d, trow = staged_inputs(torch, B * window, [draws[i] for i in range(total)])
+        pos_d, row = staged_inputs(torch, B, [[c + i * window for c in ctx0] for i in range(total)])
+        len_d, _ = staged_inputs(torch, B, [[c + i * window + 1 for c in ctx0] for i in range(total)])
+        logits = torch.empty((B, window, cfg.vocab), dtype=torch.float32, device="cuda")
+        stream = torch.cuda.current_stream()
+        sp = int(stream.cuda_stream)
+
+        def launch(i: int) -> None:
+            rc = mkd.mk_decode_window(g.ctx, toks_d.data_ptr() + i * trow, pos_d.data_ptr() + i * row,
+                                      len_d.data_ptr() + i * row, B, window, logits.data_ptr(), sp)
+            if rc != 0:
+                raise mkd.MKError(rc, f"mk_decode_window (launch {i})")
+
+        for i in range(warmup):
+            launch(i)
+        torch.cuda.synchronize()
+        mkd.check(g.sync(), "window warm-up")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+        t_start = time.perf_counter()
+        for i in range(launches):
+            ev[i][0].record(stream)
+            launch(warmup + i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+        mkd.check(g.sync(), "window launches")
+        kms = np.array([a.elapsed_time(b) for a, b in ev])
+    finally:
+        g.close()
+        del g
+        torch.cuda.empty_cache()
+    ms = elapsed * 1e3 / launches
+    log(f"{name}: {launches} windows of {window}: {ms * 1e3:.1f} us per window")
+    return {"window": window, "sequences": B, "launches": launches, "ms_per_window": round(ms, 4),
+            "tokens_per_s": round(B * window * launches / elapsed, 2),
+            "kernel_us_median": round(float(np.median(kms)) * 1e3, 2),
+            "note": "tokens verified per second: every window token's logits per launch"}
+
+
 PER_CONFIG = ("0.6b", "hybrid", "13b")   # measured beside the headline 8B workload
+WINDOWS = {"8b": 8, "0.6b": 8}            # verify windows timed beside them
 RUN_STEPS = {"8b": 128, "0.6b": 64, "hybrid": 64, "13b": 64, "tiny": 8}  # decode steps of each workload's run
 
 
@@ -400,6 +460,7 @@ def main() -> int:
     out["stream_read"] = stream_read_ceiling(mkd, torch, torch.cuda.current_stream())
     out["stream_read"]["achieved_frac"] = round(head["roofline"]["achieved"] / out["stream_read"]["gbs"], 4)
     if not args.no_per_config and not args.trace and args.config == "8b":
+        out["verify_window"] = {name: run_window(name, win, 16, 2) for name, win in WINDOWS.items()}
         out["per_config"] = {}
         for name in PER_CONFIG:
             n = min(args.steps, RUN_STEPS[name])
