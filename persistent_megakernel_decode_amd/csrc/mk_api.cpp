@@ -93,6 +93,28 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const u32x4_t* __restr
   if (threadIdx.x == 0) out[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
+// Verify windows: row r = b * win + t gets position positions[b] + t, context ctx_lens[b] + t (a
+// value out of range at t = 0 stays out of range) and sequence b's page-table row.
+__global__ void expand_window(const int32_t* pos, const int32_t* ctx, const int32_t* pt, int mpps_src, int batch,
+                              int win, int32_t* rpos, int32_t* rctx, int32_t* rpt, int mpps_dst) {
+  const int rows = batch * win, per = 2 + (pt ? mpps_dst : 0);
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < rows * per; i += gridDim.x * blockDim.x) {
+    const int r = i / per, k = i % per, b = r / win, t = r % win;
+    if (k == 0) {
+      const int p = pos[b];
+      const int64_t q = (int64_t)p + t;
+      rpos[r] = p < 0 ? p : (int)(q < 0x7FFFFFFF ? q : 0x7FFFFFFF);
+    } else if (k == 1) {
+      const int c = ctx[b];
+      const int64_t q = (int64_t)c + t;
+      rctx[r] = c < 1 ? c : (int)(q < 0x7FFFFFFF ? q : 0x7FFFFFFF);
+    } else {
+      const int p = k - 2;
+      rpt[(size_t)r * mpps_dst + p] = p < mpps_src ? pt[(size_t)b * mpps_src + p] : -1;
+    }
+  }
+}
+
 __global__ void fill_u32(uint32_t* p, size_t n, uint32_t v) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -489,14 +511,24 @@ mk_status mk_decode_window(mk_ctx* ctx, const int32_t* tokens, const int32_t* po
   std::unique_lock<std::mutex> lk(ctx->busy, std::try_to_lock);
   if (!lk.owns_lock()) return fail(MK_ERR_STATE, "another thread is stepping this context");
   MK_CHECK_SCRATCH(ctx);
+  const mk::Layout& Y = ctx->plan.lay;
   mk::KArgs A = ctx->args;
   A.tokens = tokens;
-  A.positions = positions;
-  A.ctx_lens = ctx_lens;
+  A.positions = (const int32_t*)(ctx->ws + Y.win_pos);
+  A.ctx_lens = (const int32_t*)(ctx->ws + Y.win_ctx);
+  if (A.page_table) {
+    A.page_table = (const int32_t*)(ctx->ws + Y.win_pages);
+    A.max_pages_per_seq = Y.win_pages_per_row;
+  }
   A.logits = logits_out;
   A.batch = batch * window;  // rows
   A.win = window;
-  return launch_steps(ctx, A, 1, ctx->kernel, (hipStream_t)hip_stream);
+  hipStream_t s = (hipStream_t)hip_stream;
+  hipLaunchKernelGGL(expand_window, dim3(4), dim3(256), 0, s, positions, ctx_lens, ctx->args.page_table,
+                     ctx->args.max_pages_per_seq, batch, window, (int32_t*)(ctx->ws + Y.win_pos),
+                     (int32_t*)(ctx->ws + Y.win_ctx), (int32_t*)(ctx->ws + Y.win_pages), Y.win_pages_per_row);
+  MK_HIP(hipGetLastError());
+  return launch_steps(ctx, A, 1, ctx->kernel, s);
 }
 
 mk_status mk_decode_steps(mk_ctx* ctx, const int32_t* tokens, const int32_t* positions, const int32_t* ctx_lens,

@@ -167,9 +167,10 @@ struct KArgs {
   int32_t n_steps;            // steps in this launch (>= 1)
   int32_t n_lm;               // LM-head ops (argmax partials per sequence)
   int32_t* tokens_out;        // [n_steps][batch] greedy token of each step, or null
-  // verify windows: rows b*win .. b*win + win - 1 are tokens 0 .. win - 1 of sequence b, at
-  // positions[b] + t with ctx_lens[b] + t cached tokens (page-table and state row b); win = 1 is
-  // one token per sequence.  `batch` counts rows.
+  // verify windows: rows b*win .. b*win + win - 1 are tokens 0 .. win - 1 of sequence b; the host
+  // expands positions, context lengths and page-table rows per row (positions / ctx_lens /
+  // page_table then point at that copy), and the delta-rule items run sequence b's window with
+  // state row b.  win = 1 is one token per sequence.  `batch` counts rows.
   int32_t win;
   uint32_t* step_done;        // [n_cus] tag of the last step whose stores this CU has completed
   uint32_t* amax;             // [2][n_lm][max batch width][2] per-op (value bits, index) of the LM head,

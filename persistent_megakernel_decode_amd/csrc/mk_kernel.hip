@@ -278,15 +278,10 @@ __device__ __forceinline__ u32 cstep() { return lds_ld(&g_cstep); }
 __device__ __forceinline__ int step_add(int v, int lo, u32 step) {
   return v < lo ? v : (int)min((u32)v + step, 0x7FFFFFFFu);
 }
-// Row b's sequence (its page-table row) and its token's place in the verify window.
-__device__ __forceinline__ int row_seq(const KArgs& A, int b) { return A.win == 1 ? b : b / A.win; }
+__device__ __forceinline__ int step_ctx(const KArgs& A, int b) { return step_add(A.ctx_lens[b], 1, cstep()); }
+__device__ __forceinline__ int step_pos(const KArgs& A, int b) { return step_add(A.positions[b], 0, cstep()); }
+// Row b's place in its verify window (the window's earlier tokens are rows b - 1, b - 2, ...).
 __device__ __forceinline__ u32 row_tok(const KArgs& A, int b) { return A.win == 1 ? 0u : (u32)(b % A.win); }
-__device__ __forceinline__ int step_ctx(const KArgs& A, int b) {
-  return step_add(A.ctx_lens[row_seq(A, b)], 1, cstep() + row_tok(A, b));
-}
-__device__ __forceinline__ int step_pos(const KArgs& A, int b) {
-  return step_add(A.positions[row_seq(A, b)], 0, cstep() + row_tok(A, b));
-}
 __device__ __forceinline__ int step_tok(int b) { return (int)lds_ld((const u32*)&g_tok[b]); }  // b uniform
 __device__ __forceinline__ int lane_tok(int b) {  // b may differ from lane to lane
   return __hip_atomic_load(&g_tok[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -425,7 +420,7 @@ __device__ bool row_ok_local(const KArgs& A, int b) {
   if (!A.page_table) return true;  // no attention layers: no pages to check
   int pi = pos / A.page_size;
   if (pi >= A.max_pages_per_seq) return false;
-  int pg = A.page_table[(size_t)row_seq(A, b) * A.max_pages_per_seq + pi];
+  int pg = A.page_table[(size_t)b * A.max_pages_per_seq + pi];
   return pg >= 0 && pg < A.num_pages;
 }
 
@@ -440,8 +435,7 @@ __device__ __forceinline__ int clamp_ctx(const KArgs& A, int c) { return attn_cl
 __device__ __forceinline__ void attn_plan_build(const KArgs& A, int pps, u32 step) {
   int cv[APLAN_MAXB];
 #pragma unroll
-  for (int b = 0; b < APLAN_MAXB; ++b)
-    cv[b] = b < A.batch ? clamp_ctx(A, step_add(sload(A.ctx_lens + row_seq(A, b)), 1, step + row_tok(A, b))) : 0;
+  for (int b = 0; b < APLAN_MAXB; ++b) cv[b] = b < A.batch ? clamp_ctx(A, step_add(sload(A.ctx_lens + b), 1, step)) : 0;
   const int K = A.Hkv > 0 ? A.n_items / A.Hkv : 0;  // chunks per KV head; >= batch by construction
   int plan[APLAN_WORDS];
   attn_plan_make(cv, K, pps, NC, plan);
@@ -671,7 +665,7 @@ __device__ __forceinline__ void issue_gemv(const GemvSeg& gsg, GemvWalk& gw, u32
 // LDS banks.  A DMA lane chooses its source address, so the swizzle costs nothing: lane i of
 // piece j fills row r = j*RPP + i/CPR, chunk position i mod CPR.
 __device__ __forceinline__ int page_lookup(const KArgs& A, int b, u32 pi) {
-  const int v = sload(A.page_table + (size_t)row_seq(A, b) * A.max_pages_per_seq + pi);
+  const int v = sload(A.page_table + (size_t)b * A.max_pages_per_seq + pi);
   return (v >= 0 && v < A.num_pages) ? v : 0;  // out-of-range entries stream page 0 (rows get masked)
 }
 struct AttnLanes {  // per-lane byte offsets of each piece within its page's (kv head) block
@@ -1009,7 +1003,7 @@ __device__ __forceinline__ void op_embed_finish(const KArgs& A, u32 w, u32& gen)
       const int npg = (step_ctx(A, b) + A.page_size - 1) / A.page_size;
       if (npg > A.max_pages_per_seq) bad = 1.0f;
       for (int p = (int)(w * 64 + lane_id()); p < npg && bad == 0.0f; p += NC * 64) {
-        const int pg = A.page_table[(size_t)row_seq(A, b) * A.max_pages_per_seq + p];
+        const int pg = A.page_table[(size_t)b * A.max_pages_per_seq + p];
         if (pg < 0 || pg >= A.num_pages) bad = 1.0f;
       }
     }
@@ -1735,6 +1729,7 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
   seq += ns;
   const int G = A.G, b = it.b, kvh = it.kvh;
   const int pos = step_pos(A, b);
+  const int wt = (int)row_tok(A, b);  // earlier tokens of this row's verify window
   const int32_t rok = ld_i32_sc1(A.row_ok + b);  // checked where it is used
   const bool tagged = (o.flags & OPF_TAGGED_IN) != 0;
   const int qkv_ld = (A.Hq + 2 * A.Hkv) * D;
@@ -1813,7 +1808,7 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
       }
       if (row_ok_fix(A, b, rok)) {
         // agent-coherent stores: a later step of the same launch may read the row on another CU
-        const int pg = A.page_table[(size_t)row_seq(A, b) * A.max_pages_per_seq + pos / 16];
+        const int pg = A.page_table[(size_t)b * A.max_pages_per_seq + pos / 16];
         const size_t off = (((size_t)pg * A.Hkv + kvh) * 16 + pos % 16) * D + lane * DPL;
         uint16_t* dp = (uint16_t*)(t == G ? Ld.k_pages : Ld.v_pages) + off;
         if constexpr (DPL == 2) {
@@ -1850,7 +1845,7 @@ __device__ __forceinline__ bool op_attn(const KArgs& A, const Op& o, u32 w, u32&
     // sequence) are appended by their own rows in this step, so the loader may have read their
     // positions before they were written.  Their K/V are computed here from those rows'
     // projections exactly as their owners compute them, and put into the slot.
-    for (int q = max(pbase, pos - (int)row_tok(A, b)), q1 = min(pbase + np, pos); q < q1; ++q) {
+    for (int q = max(pbase, pos - wt), q1 = min(pbase + np, pos); q < q1; ++q) {
       const int rq = b - (pos - q);
       const float* ks = (const float*)Ld.qkv + (size_t)rq * qkv_ld + (A.Hq + kvh) * D + lane * DPL;
       const float* vs = ks + A.Hkv * D;

@@ -464,6 +464,12 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
   // per-op timing stamps of the traced kernels (MK_TRACE=1), 4 words per op; kept in every
   // workspace so that tracing never needs memory of its own
   Y.trace = take(P.ops.size() * TRACE_WORDS * sizeof(uint32_t));
+  // verify windows: the launch's per-row positions, context lengths and page-table rows (pages
+  // covering max_ctx), expanded from the per-sequence inputs before the launch
+  Y.win_pages_per_row = (d.max_ctx + d.page_size - 1) / d.page_size;
+  Y.win_pos = take((size_t)B * 4);
+  Y.win_ctx = take((size_t)B * 4);
+  Y.win_pages = take((size_t)B * Y.win_pages_per_row * 4);
   // multi-step launches: per LM-head op and sequence, the (value, index) of its largest logit, one
   // half per step parity (written every step before it is read: never cleared)
   Y.amax = take((size_t)2 * P.n_lm * 8 * 2 * 4);

@@ -17,6 +17,8 @@ struct Layout {
   size_t ops = 0, queue_off = 0, stages = 0, counters = 0, layers = 0, rope = 0, status = 0, row_ok = 0, x0 = 0;
   size_t trace = 0;  // per-op timing stamps (traced kernels only)
   size_t step_done = 0, amax = 0;  // multi-step launches: per-CU step tags, LM-head greedy partials
+  size_t win_pos = 0, win_ctx = 0, win_pages = 0;  // verify windows: per-row positions, contexts, page rows
+  int win_pages_per_row = 0;
   struct PerLayer {
     size_t qkv = 0, part = 0, tickets = 0, mix_o = 0, x_mix = 0, m = 0, x_out = 0;
   };
