@@ -9,7 +9,8 @@ The launch feeds each step's argmax back on the device.  Per step and sequence:
 and at the end of the run the delta-rule states against the oracle's trajectory (normwise <= 1e-4)
 and, bit for bit, against the step-by-step context.  Cases cover batch widths 1 / 2 / 4 / 8, GQA and
 MHA, head_dim 64 and 128, contexts that cross page and chunk boundaries within a launch (rows appended
-by earlier steps of the launch on other compute units), and several launches in a row.
+by earlier steps of the launch on other compute units), several launches in a row, and the
+0.6B-shape workload at full size.
 """
 import numpy as np
 import pytest
@@ -39,6 +40,8 @@ CASES = {
     # one long context split over many chunks: the rows the launch appends land in its last chunk
     "small-split9": (synth.Config("small-split9", n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=8, head_dim=128,
                                   ffn=1024, vocab=2048, batch=1, ctx=[4390], steps=3, seed=15), 5, 1),
+    # the 0.6B-shape workload at full size (28 layers, tied LM head over 151936 rows): 8 steps per launch
+    "0.6b": (synth.CONFIGS["0.6b"], 8, 1),
 }
 
 

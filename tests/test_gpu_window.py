@@ -36,6 +36,8 @@ CASES = {
                                                              ctx=[16, 40] + [9] * 6), 2, 4),
     "hybrid-d128-b1-w8": (synth.SMALL["tiny-hybrid"].replace(name="hyb-d128-w8", delta_dk=128, delta_dv=128, batch=8,
                                                              ctx=[33] * 8), 1, 8),
+    # the 0.6B-shape workload at full size, a window of 8 drafted tokens
+    "0.6b-w8": (synth.CONFIGS["0.6b"].replace(name="0.6b-w8", batch=8, ctx=[1024] * 8), 1, 8),
 }
 
 
