@@ -45,15 +45,22 @@ class OrcModel(ctypes.Structure):
                 ("rms_eps", ctypes.c_double), ("rope_base", ctypes.c_double),
                 ("n_delta_heads", ctypes.c_int), ("delta_dk", ctypes.c_int), ("delta_dv", ctypes.c_int),
                 ("conv_width", ctypes.c_int), ("layer_kind", P), ("page_size", ctypes.c_int),
-                ("delta_decay_first", ctypes.c_int)]
+                ("delta_decay_first", ctypes.c_int), ("weight_format", ctypes.c_int)]
+
+
+W_BF16, W_FP8 = 0, 1  # orc_model.weight_format
 
 
 _LAYER_FIELDS = ["attn_norm", "wq", "wk", "wv", "wo", "q_norm", "k_norm", "w_qkv_delta", "w_gates", "conv_w",
                  "wo_delta", "mlp_norm", "w_gate", "w_up", "w_down"]
 
 
+# projections that are fp8 codes with fp32 row scales ("<name>_scale") when the weights are fp8
+PROJ_FIELDS = ["wq", "wk", "wv", "wo", "w_qkv_delta", "w_gates", "wo_delta", "w_gate", "w_up", "w_down"]
+
+
 class OrcLayer(ctypes.Structure):
-    _fields_ = [(f, P) for f in _LAYER_FIELDS]
+    _fields_ = [(f, P) for f in _LAYER_FIELDS] + [("s_" + f, P) for f in PROJ_FIELDS]
 
 
 class OrcWeights(ctypes.Structure):
@@ -81,6 +88,10 @@ def lib():
         L.orc_f32_to_bf16.restype = ctypes.c_uint16
         L.orc_rmsnorm.argtypes = [P, P, ctypes.c_int, ctypes.c_double, P]
         L.orc_matvec.argtypes = [P, P, ctypes.c_int, ctypes.c_int, P]
+        L.orc_matvec_fp8.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, P]
+        L.orc_matvec_fp8.restype = None
+        L.orc_e4m3.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3.restype = ctypes.c_double
         L.orc_rope.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_double]
         L.orc_attend.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, P, P]
         L.orc_silu.argtypes = [ctypes.c_double]
@@ -124,6 +135,21 @@ def matvec(W_bf16, x) -> np.ndarray:
     x = _c(x, np.float32)
     y = np.empty(W.shape[0], dtype=np.float32)
     lib().orc_matvec(_ptr(W), _ptr(x), W.shape[0], W.shape[1], _ptr(y))
+    return y
+
+
+def e4m3(code: int) -> float:
+    """The value of one OCP E4M3 fp8 code (NaN for 0x7F / 0xFF)."""
+    return lib().orc_e4m3(int(code))
+
+
+def matvec_fp8(W_codes, scale, x) -> np.ndarray:
+    """y[r] = scale[r] * sum_k e4m3(W[r][k]) x[k]."""
+    W = _c(W_codes, np.uint8)
+    s = _c(scale, np.float32)
+    x = _c(x, np.float32)
+    y = np.empty(W.shape[0], dtype=np.float32)
+    lib().orc_matvec_fp8(_ptr(W), _ptr(s), _ptr(x), W.shape[0], W.shape[1], _ptr(y))
     return y
 
 
@@ -209,12 +235,24 @@ class DecodeOracle:
         m.layer_kind = self.kinds.ctypes.data
         m.page_size = cfg.page_size
         m.delta_decay_first = decay_first
+        fp8 = weights.get("format", "bf16") == "fp8"
+        m.weight_format = W_FP8 if fp8 else W_BF16
         self.m = m
         self.layers = (OrcLayer * cfg.n_layers)()
         for l, L in enumerate(weights["layers"]):
             for f in _LAYER_FIELDS:
                 if f in L:
+                    want = np.uint8 if fp8 and f in PROJ_FIELDS else np.uint16
+                    if L[f].dtype != want:
+                        raise TypeError(f"layer {l} {f}: {L[f].dtype}, expected {np.dtype(want)}")
                     setattr(self.layers[l], f, L[f].ctypes.data)
+            if fp8:
+                for f in PROJ_FIELDS:
+                    if f in L:
+                        sc = L[f + "_scale"]
+                        if sc.dtype != np.float32 or sc.shape != (L[f].shape[0],):
+                            raise TypeError(f"layer {l} {f}_scale: fp32 [{L[f].shape[0]}] expected")
+                        setattr(self.layers[l], "s_" + f, sc.ctypes.data)
         ow = OrcWeights()
         ow.embed = weights["embed"].ctypes.data
         ow.final_norm = weights["final_norm"].ctypes.data

@@ -60,6 +60,34 @@ void orc_matvec(const uint16_t* W, const float* x, int rows, int cols, float* y)
 }
 
 /* Rotate-half: pairs (i, i + d/2), angle pos * base^(-2i/d). */
+/* OCP 8-bit floating point specification, E4M3 encoding: the low-bit weight format of the MK-KDA
+ * pull request's weight stream (github choiceoh/stkernel #230, PR summary) taken at 8 bits, in the
+ * variant gfx950 reads natively. */
+double orc_e4m3(uint8_t code) {
+  int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  double mag = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -mag : mag;
+}
+
+void orc_matvec_fp8(const uint8_t* W, const float* scale, const float* x, int rows, int cols, float* y) {
+  double lut[256];
+  for (int c = 0; c < 256; ++c) lut[c] = orc_e4m3((uint8_t)c);
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < rows; ++r) {
+    const uint8_t* wr = W + (size_t)r * (size_t)cols;
+    double acc = 0.0;
+    for (int k = 0; k < cols; ++k) acc += lut[wr[k]] * (double)x[k];
+    y[r] = (float)((double)scale[r] * acc);
+  }
+}
+
+/* one projection of the model, in its weight format */
+static void proj(const orc_model* m, const void* W, const float* scale, const float* x, int rows, int cols, float* y) {
+  if (m->weight_format == ORC_W_FP8) orc_matvec_fp8((const uint8_t*)W, scale, x, rows, cols, y);
+  else orc_matvec((const uint16_t*)W, x, rows, cols, y);
+}
+
 void orc_rope(float* u, int d, int pos, double base) {
   int half = d / 2;
   for (int i = 0; i < half; ++i) {
@@ -168,9 +196,9 @@ static void attention_layer(const orc_model* m, const orc_layer* L, orc_cache* c
   float* q = (float*)malloc(sizeof(float) * (size_t)Hq * d);
   float* k = (float*)malloc(sizeof(float) * (size_t)Hkv * d);
   float* v = (float*)malloc(sizeof(float) * (size_t)Hkv * d);
-  orc_matvec(L->wq, r, Hq * d, m->hidden, q);
-  orc_matvec(L->wk, r, Hkv * d, m->hidden, k);
-  orc_matvec(L->wv, r, Hkv * d, m->hidden, v);
+  proj(m, L->wq, L->s_wq, r, Hq * d, m->hidden, q);
+  proj(m, L->wk, L->s_wk, r, Hkv * d, m->hidden, k);
+  proj(m, L->wv, L->s_wv, r, Hkv * d, m->hidden, v);
   if (m->qk_norm) {
     for (int h = 0; h < Hq; ++h) orc_rmsnorm(q + (size_t)h * d, L->q_norm, d, m->rms_eps, q + (size_t)h * d);
     for (int h = 0; h < Hkv; ++h) orc_rmsnorm(k + (size_t)h * d, L->k_norm, d, m->rms_eps, k + (size_t)h * d);
@@ -232,8 +260,8 @@ static void delta_layer(const orc_model* m, const orc_layer* L, orc_cache* c, in
   int C = nh * (2 * dk + dv);
   float* u = (float*)malloc(sizeof(float) * (size_t)C);
   float* a = (float*)malloc(sizeof(float) * (size_t)(2 * nh));
-  orc_matvec(L->w_qkv_delta, r, C, m->hidden, u);
-  orc_matvec(L->w_gates, r, 2 * nh, m->hidden, a);
+  proj(m, L->w_qkv_delta, L->s_w_qkv_delta, r, C, m->hidden, u);
+  proj(m, L->w_gates, L->s_w_gates, r, 2 * nh, m->hidden, a);
   float* cs = c->conv_state + ((size_t)delta_layer_idx * (size_t)c->max_batch + (size_t)b) * (size_t)C * (size_t)(W - 1);
   float* st = c->delta_state + ((size_t)delta_layer_idx * (size_t)c->max_batch + (size_t)b) * (size_t)nh *
                                    (size_t)dv * (size_t)dk;
@@ -264,20 +292,20 @@ int orc_decode_step(const orc_model* m, const orc_weights* w, orc_cache* c, cons
       orc_rmsnorm(x, L->attn_norm, H, m->rms_eps, r);
       if (m->layer_kind[l] == ORC_ATTN) {
         attention_layer(m, L, c, ia++, b, pos, ctx, r, o);
-        orc_matvec(L->wo, o, H, m->n_q_heads * m->head_dim, t);
+        proj(m, L->wo, L->s_wo, o, H, m->n_q_heads * m->head_dim, t);
       } else {
         delta_layer(m, L, c, id++, b, r, o);
-        orc_matvec(L->wo_delta, o, H, m->n_delta_heads * m->delta_dv, t);
+        proj(m, L->wo_delta, L->s_wo_delta, o, H, m->n_delta_heads * m->delta_dv, t);
       }
       add_into(x, t, H);
       if (dump && dump->mixer_o) memcpy(dump->mixer_o + ((size_t)l * batch + b) * (size_t)mix, o, sizeof(float) * (size_t)mix);
       if (dump && dump->x_mixer) memcpy(dump->x_mixer + ((size_t)l * batch + b) * (size_t)H, x, sizeof(float) * (size_t)H);
       /* SwiGLU MLP */
       orc_rmsnorm(x, L->mlp_norm, H, m->rms_eps, r);
-      orc_matvec(L->w_gate, r, F, H, gt);
-      orc_matvec(L->w_up, r, F, H, up);
+      proj(m, L->w_gate, L->s_w_gate, r, F, H, gt);
+      proj(m, L->w_up, L->s_w_up, r, F, H, up);
       for (int i = 0; i < F; ++i) gt[i] = (float)(orc_silu(gt[i]) * (double)up[i]);
-      orc_matvec(L->w_down, gt, H, F, t);
+      proj(m, L->w_down, L->s_w_down, gt, H, F, t);
       add_into(x, t, H);
       if (dump && dump->mlp_m) memcpy(dump->mlp_m + ((size_t)l * batch + b) * (size_t)F, gt, sizeof(float) * (size_t)F);
       if (dump && dump->x_mlp) memcpy(dump->x_mlp + ((size_t)l * batch + b) * (size_t)H, x, sizeof(float) * (size_t)H);

@@ -33,12 +33,25 @@ typedef struct {
   const int32_t* layer_kind; /* [n_layers]: ORC_ATTN or ORC_DELTA */
   int page_size;
   int delta_decay_first;     /* 0: S <- gS + b k(v^T - k^T S) with the old S throughout; 1: decay first */
+  int weight_format;         /* ORC_W_BF16, or ORC_W_FP8: every projection matrix is fp8 codes + row scales */
 } orc_model;
 
-typedef struct { /* bf16 bit patterns, [out][in] row-major */
-  const uint16_t *attn_norm, *wq, *wk, *wv, *wo, *q_norm, *k_norm;
-  const uint16_t *w_qkv_delta, *w_gates, *conv_w, *wo_delta;
-  const uint16_t *mlp_norm, *w_gate, *w_up, *w_down;
+/* Projection weights (wq wk wv wo w_qkv_delta w_gates wo_delta w_gate w_up w_down): bf16 bit
+ * patterns, or with ORC_W_FP8 one OCP E4M3 byte per weight and one fp32 scale per output row,
+ * W[r][k] = scale[r] * e4m3(code[r][k]).  Norm gains, conv_w, embedding and LM head stay bf16. */
+enum { ORC_W_BF16 = 0, ORC_W_FP8 = 1 };
+
+typedef struct { /* [out][in] row-major; projections bf16 or fp8 (weight_format), the rest bf16 */
+  const uint16_t *attn_norm;
+  const void *wq, *wk, *wv, *wo;
+  const uint16_t *q_norm, *k_norm;
+  const void *w_qkv_delta, *w_gates;
+  const uint16_t *conv_w;
+  const void *wo_delta;
+  const uint16_t *mlp_norm;
+  const void *w_gate, *w_up, *w_down;
+  /* ORC_W_FP8: fp32 [out] row scales of the projection of the same name (unused otherwise) */
+  const float *s_wq, *s_wk, *s_wv, *s_wo, *s_w_qkv_delta, *s_w_gates, *s_wo_delta, *s_w_gate, *s_w_up, *s_w_down;
 } orc_layer;
 
 typedef struct {
@@ -73,6 +86,11 @@ uint16_t orc_f32_to_bf16(float f);
 void orc_rmsnorm(const float* x, const uint16_t* gain, int n, double eps, float* y);
 /* y[r] = sum_k W[r][k] x[k], W bf16 [rows][cols] */
 void orc_matvec(const uint16_t* W, const float* x, int rows, int cols, float* y);
+/* value of an OCP 8-bit floating-point E4M3 code (sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; exponent 0 is subnormal; 0x7F and 0xFF are NaN; no infinities; largest finite 448) */
+double orc_e4m3(uint8_t code);
+/* y[r] = scale[r] * sum_k e4m3(W[r][k]) x[k], W fp8 codes [rows][cols] */
+void orc_matvec_fp8(const uint8_t* W, const float* scale, const float* x, int rows, int cols, float* y);
 /* rotate-half rotary embedding of one head vector u[d] at position pos */
 void orc_rope(float* u, int d, int pos, double base);
 /* single-head attention over n keys: o = softmax(q.K^T / sqrt(d)) V; K, V bf16 rows [n][d]

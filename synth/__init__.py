@@ -49,7 +49,9 @@ def lib():
         L.synth_uniform_bf16.argtypes = [vp, sz, u64, u64, dbl, dbl]
         L.synth_u32.argtypes = [vp, sz, u64, u64]
         L.synth_philox4x32_10.argtypes = [vp, vp, vp]
-        for f in (L.synth_normal_bf16, L.synth_normal_f32, L.synth_uniform_bf16, L.synth_u32, L.synth_philox4x32_10):
+        L.synth_fp8_codes.argtypes = [vp, sz, u64, u64]
+        for f in (L.synth_normal_bf16, L.synth_normal_f32, L.synth_uniform_bf16, L.synth_u32, L.synth_philox4x32_10,
+                  L.synth_fp8_codes):
             f.restype = None
         _lib = L
     return _lib
@@ -81,6 +83,13 @@ def uniform_bf16(shape, seed: int, name: str, lo: float, hi: float) -> np.ndarra
 def u32(n: int, seed: int, name: str) -> np.ndarray:
     out = np.empty(n, dtype=np.uint32)
     lib().synth_u32(out.ctypes.data, n, seed, stream_id(name))
+    return out
+
+
+def fp8_codes(shape, seed: int, name: str) -> np.ndarray:
+    """Random E4M3 fp8 weight codes (uint8; no NaN codes), see synth_fp8_codes in gen.c."""
+    out = np.empty(shape, dtype=np.uint8)
+    lib().synth_fp8_codes(out.ctypes.data, out.size, seed, stream_id(name))
     return out
 
 
@@ -128,6 +137,7 @@ class Config:
     page_size: int = 16
     shuffle_pages: bool = False
     gain_range: Optional[tuple] = None       # None = unit norm gains
+    weights: str = "bf16"                    # projection matrices: "bf16", or "fp8" codes + fp32 row scales
 
     def kinds(self) -> List[int]:
         return list(self.layer_kinds) if self.layer_kinds is not None else [ATTN] * self.n_layers
@@ -202,34 +212,53 @@ def _gain(cfg: Config, n: int, name: str) -> np.ndarray:
     return uniform_bf16(n, cfg.seed, name, lo, hi)
 
 
+# fp8 projections: the drawn codes' values have an RMS of about 142 (the exponent spread of
+# synth_fp8_codes), so row scales of FP8_SCALE * U[0.5, 1.5) give weights of about WEIGHT_STD.
+FP8_SCALE = WEIGHT_STD / 142.0
+
+
+def _proj(cfg: Config, L: dict, name: str, rows: int, cols: int, prefix: str) -> None:
+    """One projection matrix: bf16 N(0, WEIGHT_STD), or fp8 codes with one fp32 scale per row."""
+    if cfg.weights == "fp8":
+        L[name] = fp8_codes((rows, cols), cfg.seed, prefix + name)
+        u = u32(rows, cfg.seed, prefix + name + "_scale").astype(np.float64) / 4294967296.0
+        L[name + "_scale"] = (FP8_SCALE * (0.5 + u)).astype(np.float32)
+    else:
+        L[name] = normal_bf16((rows, cols), cfg.seed, prefix + name, WEIGHT_STD)
+
+
 def make_weights(cfg: Config) -> dict:
-    """Host (numpy) weights in PyTorch Linear layout [out, in], bf16 bit patterns."""
+    """Host (numpy) weights in PyTorch Linear layout [out, in]: bf16 bit patterns, except that with
+    cfg.weights == "fp8" every projection matrix is E4M3 codes (uint8) with fp32 row scales
+    ("<name>_scale"); embedding, LM head, norm gains and conv taps stay bf16."""
+    if cfg.weights not in ("bf16", "fp8"):
+        raise ValueError(f"weight format {cfg.weights!r}")
     s, H, d = cfg.seed, cfg.hidden, cfg.head_dim
     w = {"embed": normal_bf16((cfg.vocab, H), s, "embed", WEIGHT_STD),
-         "final_norm": _gain(cfg, H, "final_norm")}
+         "final_norm": _gain(cfg, H, "final_norm"), "format": cfg.weights}
     w["lm_head"] = w["embed"] if cfg.tied else normal_bf16((cfg.vocab, H), s, "lm_head", WEIGHT_STD)
     layers = []
     for l, kind in enumerate(cfg.kinds()):
         p = f"layer{l}."
-        L = {"attn_norm": _gain(cfg, H, p + "attn_norm"), "mlp_norm": _gain(cfg, H, p + "mlp_norm"),
-             "w_gate": normal_bf16((cfg.ffn, H), s, p + "w_gate", WEIGHT_STD),
-             "w_up": normal_bf16((cfg.ffn, H), s, p + "w_up", WEIGHT_STD),
-             "w_down": normal_bf16((H, cfg.ffn), s, p + "w_down", WEIGHT_STD)}
+        L = {"attn_norm": _gain(cfg, H, p + "attn_norm"), "mlp_norm": _gain(cfg, H, p + "mlp_norm")}
+        _proj(cfg, L, "w_gate", cfg.ffn, H, p)
+        _proj(cfg, L, "w_up", cfg.ffn, H, p)
+        _proj(cfg, L, "w_down", H, cfg.ffn, p)
         if kind == ATTN:
-            L["wq"] = normal_bf16((cfg.n_q_heads * d, H), s, p + "wq", WEIGHT_STD)
-            L["wk"] = normal_bf16((cfg.n_kv_heads * d, H), s, p + "wk", WEIGHT_STD)
-            L["wv"] = normal_bf16((cfg.n_kv_heads * d, H), s, p + "wv", WEIGHT_STD)
-            L["wo"] = normal_bf16((H, cfg.n_q_heads * d), s, p + "wo", WEIGHT_STD)
+            _proj(cfg, L, "wq", cfg.n_q_heads * d, H, p)
+            _proj(cfg, L, "wk", cfg.n_kv_heads * d, H, p)
+            _proj(cfg, L, "wv", cfg.n_kv_heads * d, H, p)
+            _proj(cfg, L, "wo", H, cfg.n_q_heads * d, p)
             if cfg.qk_norm:
                 L["q_norm"] = _gain(cfg, d, p + "q_norm")
                 L["k_norm"] = _gain(cfg, d, p + "k_norm")
         else:
             nh, dk, dv = cfg.n_delta_heads, cfg.delta_dk, cfg.delta_dv
             C = nh * (2 * dk + dv)
-            L["w_qkv_delta"] = normal_bf16((C, H), s, p + "w_qkv_delta", WEIGHT_STD)
-            L["w_gates"] = normal_bf16((2 * nh, H), s, p + "w_gates", WEIGHT_STD)
+            _proj(cfg, L, "w_qkv_delta", C, H, p)
+            _proj(cfg, L, "w_gates", 2 * nh, H, p)
             L["conv_w"] = normal_bf16((C, cfg.conv_width), s, p + "conv_w", WEIGHT_STD)
-            L["wo_delta"] = normal_bf16((H, nh * dv), s, p + "wo_delta", WEIGHT_STD)
+            _proj(cfg, L, "wo_delta", H, nh * dv, p)
         layers.append(L)
     w["layers"] = layers
     return w
@@ -306,4 +335,4 @@ def shape_of(cfg: Config, max_ctx: int) -> dict:
                 n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, qk_norm=cfg.qk_norm, tied=cfg.tied,
                 rms_eps=cfg.rms_eps, rope_base=cfg.rope_base, layer_kinds=cfg.kinds(), max_batch=cfg.batch,
                 max_ctx=max_ctx, n_delta_heads=cfg.n_delta_heads, delta_dk=cfg.delta_dk, delta_dv=cfg.delta_dv,
-                conv_width=cfg.conv_width, page_size=cfg.page_size)
+                conv_width=cfg.conv_width, page_size=cfg.page_size, weights=cfg.weights)

@@ -114,6 +114,26 @@ void synth_u32(uint32_t* out, size_t n, uint64_t seed, uint64_t stream) {
   }
 }
 
+/* Random OCP E4M3 fp8 weight codes, one 32-bit draw x each: sign = bit 31, mantissa = bits 28-30,
+ * exponent field 14 - t with t the number of trailing zero bits of x (capped at 14), so field e has
+ * probability 2^(e-15) -- a magnitude spread falling off by halves below the top, as a zero-mean
+ * bell-shaped draw does -- reaching zero and subnormal codes at field 0 and never field 15 (no
+ * NaN codes).  The generator only assembles bits; it decodes nothing. */
+void synth_fp8_codes(uint8_t* out, size_t n, uint64_t seed, uint64_t stream) {
+  size_t nb = (n + 3) / 4;
+#pragma omp parallel for schedule(static)
+  for (size_t j = 0; j < nb; ++j) {
+    uint32_t x[4];
+    block4(seed, stream, j, x);
+    for (int c = 0; c < 4; ++c) {
+      size_t i = j * 4 + c;
+      if (i >= n) continue;
+      uint32_t t = (uint32_t)__builtin_ctz(x[c] | (1u << 14));
+      out[i] = (uint8_t)(((x[c] >> 31) << 7) | ((14u - t) << 3) | ((x[c] >> 28) & 7u));
+    }
+  }
+}
+
 /* Philox block for known-answer tests of the generator itself. */
 void synth_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
   philox4x32_10(ctr, key[0], key[1], out);
