@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 1u
+#define MK_ABI_VERSION 2u
 
 typedef enum {
   MK_OK = 0,
@@ -47,6 +47,21 @@ typedef enum {
 } mk_status;
 
 typedef enum { MK_LAYER_ATTN = 0, MK_LAYER_DELTA = 1 } mk_layer_kind;
+
+/* Projection weight formats.  Low-bit weight streaming is how the MK-KDA pull request (github
+ * choiceoh/stkernel #230, PR summary: its W4 weight stream; fp8 o_proj operands) cuts the bytes a
+ * decode step moves; at 8 bits it halves them against bf16.
+ *   MK_WEIGHTS_BF16     every projection bf16.
+ *   MK_WEIGHTS_FP8_E4M3 every projection matrix (wq wk wv wo w_qkv_delta w_gates wo_delta w_gate
+ *                       w_up w_down) is one OCP 8-bit floating-point E4M3 code per weight (sign,
+ *                       4 exponent bits with bias 7, 3 mantissa bits, exponent 0 subnormal, 0x7F /
+ *                       0xFF NaN, no infinities), [out][in] row-major, with one fp32 scale per
+ *                       output row: W[r][k] = scale[r] * e4m3(code[r][k]).  Embedding, LM head,
+ *                       norm gains, conv taps and the KV cache stay bf16.  Supported for
+ *                       max_batch == 1 (the batch-1 vector path) with every projection input
+ *                       length (hidden, ffn, n_q_heads * head_dim, n_delta_heads * delta_dv) a
+ *                       multiple of 16; otherwise mk_create / mk_plan return MK_ERR_UNSUPPORTED. */
+typedef enum { MK_WEIGHTS_BF16 = 0, MK_WEIGHTS_FP8_E4M3 = 1 } mk_weight_format;
 
 /* Model description (host memory; copied by mk_create).
  *   hidden % 8 == 0, head_dim in {64, 128}, n_q_heads % n_kv_heads == 0,
@@ -68,18 +83,22 @@ typedef struct {
   int32_t n_delta_heads, delta_dk, delta_dv, conv_width; /* 0 when there are no delta layers */
   const int32_t* layer_kind; /* host array [n_layers] of mk_layer_kind */
   int32_t max_batch, max_ctx, page_size;
+  int32_t weight_format;     /* mk_weight_format of the projection matrices */
 } mk_model_desc;
 
-/* Per-layer weights: device pointers to bf16.  Attention layers set attn_norm,
- * wq [Hq*d][H], wk [Hkv*d][H], wv [Hkv*d][H], wo [H][Hq*d] and, with qk_norm,
- * q_norm [d], k_norm [d].  Delta layers set attn_norm, w_qkv_delta [C][H],
+/* Per-layer weights: device pointers to bf16 (projections in the model's weight_format).
+ * Attention layers set attn_norm, wq [Hq*d][H], wk [Hkv*d][H], wv [Hkv*d][H], wo [H][Hq*d] and,
+ * with qk_norm, q_norm [d], k_norm [d].  Delta layers set attn_norm, w_qkv_delta [C][H],
  * w_gates [2*heads][H], conv_w [C][conv_width], wo_delta [H][heads*dv].
  * Every layer sets mlp_norm [H], w_gate [F][H], w_up [F][H], w_down [H][F].
- * Unused fields may be NULL. */
+ * With MK_WEIGHTS_FP8_E4M3 each projection the layer sets also sets its <name>_scale: fp32 [out]
+ * row scales (device, 16-byte aligned).  Unused fields may be NULL. */
 typedef struct {
   const void *attn_norm, *wq, *wk, *wv, *wo, *q_norm, *k_norm;
   const void *w_qkv_delta, *w_gates, *conv_w, *wo_delta;
   const void *mlp_norm, *w_gate, *w_up, *w_down;
+  const float *wq_scale, *wk_scale, *wv_scale, *wo_scale, *w_qkv_delta_scale, *w_gates_scale, *wo_delta_scale;
+  const float *w_gate_scale, *w_up_scale, *w_down_scale;
 } mk_layer_weights;
 
 typedef struct {

@@ -16,7 +16,8 @@ from typing import Dict, List, Optional, Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmk.so")
 
-MK_ABI_VERSION = 1
+MK_ABI_VERSION = 2
+MK_WEIGHTS_BF16, MK_WEIGHTS_FP8_E4M3 = 0, 1
 MK_OK, MK_ERR_INVALID_ARG, MK_ERR_UNSUPPORTED, MK_ERR_HIP, MK_ERR_DEVICE_INPUT, MK_ERR_TIMEOUT, MK_ERR_STATE = \
     0, -1, -2, -3, -4, -5, -6
 MK_LAYER_ATTN, MK_LAYER_DELTA = 0, 1
@@ -35,15 +36,20 @@ class mk_model_desc(ctypes.Structure):
                 ("n_q_heads", I32), ("n_kv_heads", I32), ("head_dim", I32), ("qk_norm", I32),
                 ("tied_embeddings", I32), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
                 ("n_delta_heads", I32), ("delta_dk", I32), ("delta_dv", I32), ("conv_width", I32),
-                ("layer_kind", P), ("max_batch", I32), ("max_ctx", I32), ("page_size", I32)]
+                ("layer_kind", P), ("max_batch", I32), ("max_ctx", I32), ("page_size", I32),
+                ("weight_format", I32)]
 
 
 LAYER_FIELDS = ["attn_norm", "wq", "wk", "wv", "wo", "q_norm", "k_norm", "w_qkv_delta", "w_gates", "conv_w",
                 "wo_delta", "mlp_norm", "w_gate", "w_up", "w_down"]
 
 
+# projection matrices: bf16, or fp8 E4M3 codes with fp32 row scales "<name>_scale"
+PROJ_FIELDS = ["wq", "wk", "wv", "wo", "w_qkv_delta", "w_gates", "wo_delta", "w_gate", "w_up", "w_down"]
+
+
 class mk_layer_weights(ctypes.Structure):
-    _fields_ = [(f, P) for f in LAYER_FIELDS]
+    _fields_ = [(f, P) for f in LAYER_FIELDS] + [(f + "_scale", P) for f in PROJ_FIELDS]
 
 
 class mk_weights(ctypes.Structure):
@@ -136,11 +142,11 @@ def check(status: int, where: str) -> None:
 # ---------------------------------------------------------------- C-ABI wrappers (same names)
 def make_desc(n_layers, hidden, vocab, ffn, n_q_heads, n_kv_heads, head_dim, qk_norm, tied_embeddings, rms_eps,
               rope_base, layer_kinds: Sequence[int], max_batch, max_ctx, n_delta_heads=0, delta_dk=0, delta_dv=0,
-              conv_width=0, page_size=16):
+              conv_width=0, page_size=16, weight_format=MK_WEIGHTS_BF16):
     kinds = (I32 * n_layers)(*layer_kinds)
     d = mk_model_desc(MK_ABI_VERSION, ctypes.sizeof(mk_model_desc), n_layers, hidden, vocab, ffn, n_q_heads,
                       n_kv_heads, head_dim, qk_norm, tied_embeddings, rms_eps, rope_base, n_delta_heads, delta_dk,
-                      delta_dv, conv_width, ctypes.cast(kinds, P), max_batch, max_ctx, page_size)
+                      delta_dv, conv_width, ctypes.cast(kinds, P), max_batch, max_ctx, page_size, weight_format)
     d._kinds = kinds  # keep the array alive with the struct
     return d
 
@@ -234,8 +240,10 @@ def mk_copy_midstate(ctx: int, kind: int, layer: int, dst_ptr: int, count: int, 
 class DecodeContext:
     """Owns the device tensors of one model and its mk_ctx.
 
-    `weights` / `cache` are dicts of host numpy arrays (bf16 as uint16) in the layout include/mk.h
-    documents; they are copied to `device` once.  Only memory and the stream come from PyTorch.
+    `weights` / `cache` are dicts of host numpy arrays (bf16 as uint16; with shape["weights"] ==
+    "fp8" the projections as uint8 E4M3 codes with float32 "<name>_scale" row scales) in the layout
+    include/mk.h documents; they are copied to `device` once.  Only memory and the stream come from
+    PyTorch.
     """
 
     ARENA_ALIGN = 2 << 20  # weights sit 2 MiB-aligned in one arena allocation
@@ -251,22 +259,27 @@ class DecodeContext:
         self.tensors: Dict[str, "torch.Tensor"] = {}
         keep: List = self.tensors.setdefault("_all", [])
         self.arena = None
-        if arena:  # one allocation for every weight tensor (bf16 bit patterns)
+        fp8 = shape.get("weights", "bf16") == "fp8"
+        if arena:  # one allocation for every weight tensor
             arrays = [weights["embed"], weights["final_norm"]] + ([] if shape["tied"] else [weights["lm_head"]])
             for L in weights["layers"]:
                 arrays += [L[f] for f in LAYER_FIELDS if f in L]
+                if fp8:
+                    arrays += [L[f + "_scale"] for f in PROJ_FIELDS if f in L]
             A = self.ARENA_ALIGN
             total = sum((a.nbytes + A - 1) // A * A for a in arrays) + A
             self.arena = torch.empty(total, dtype=torch.uint8, device=self.device)
             self._arena_off = (-self.arena.data_ptr()) % A
 
         def dev(a, dt=None):
-            if self.arena is not None and dt is i16:
+            if self.arena is not None and dt in (i16, "raw"):
                 n = a.nbytes
                 view = self.arena[self._arena_off:self._arena_off + n]
                 self._arena_off += (n + self.ARENA_ALIGN - 1) // self.ARENA_ALIGN * self.ARENA_ALIGN
                 view.copy_(torch.from_numpy(np.ascontiguousarray(a).reshape(-1).view(np.uint8)))
-                x = view.view(torch.int16)
+                x = view.view(torch.int16) if dt is i16 else view
+            elif dt == "raw":
+                x = torch.from_numpy(np.ascontiguousarray(a)).to(self.device)
             else:
                 x = torch.from_numpy(a).to(self.device) if dt is None else torch.from_numpy(a).view(dt).to(self.device)
             keep.append(x)
@@ -276,7 +289,8 @@ class DecodeContext:
         self.desc = make_desc(s["n_layers"], s["hidden"], s["vocab"], s["ffn"], s["n_q_heads"], s["n_kv_heads"],
                               s["head_dim"], s["qk_norm"], s["tied"], s["rms_eps"], s["rope_base"], s["layer_kinds"],
                               s["max_batch"], s["max_ctx"], s.get("n_delta_heads", 0), s.get("delta_dk", 0),
-                              s.get("delta_dv", 0), s.get("conv_width", 0), s.get("page_size", 16))
+                              s.get("delta_dv", 0), s.get("conv_width", 0), s.get("page_size", 16),
+                              MK_WEIGHTS_FP8_E4M3 if fp8 else MK_WEIGHTS_BF16)
         self.embed = dev(weights["embed"], i16)
         final_norm = dev(weights["final_norm"], i16)
         lm = self.embed if s["tied"] else dev(weights["lm_head"], i16)
@@ -284,7 +298,13 @@ class DecodeContext:
         for l, L in enumerate(weights["layers"]):
             for f in LAYER_FIELDS:
                 if f in L:
-                    setattr(self.layers[l], f, dev(L[f], i16).data_ptr())
+                    if fp8 and f in PROJ_FIELDS:
+                        if L[f].dtype != np.uint8 or L[f + "_scale"].dtype != np.float32:
+                            raise TypeError(f"layer {l} {f}: fp8 weights are uint8 codes with float32 row scales")
+                        setattr(self.layers[l], f, dev(L[f], "raw").data_ptr())
+                        setattr(self.layers[l], f + "_scale", dev(L[f + "_scale"], "raw").data_ptr())
+                    else:
+                        setattr(self.layers[l], f, dev(L[f], i16).data_ptr())
         self.w = mk_weights(self.embed.data_ptr(), final_norm.data_ptr(), lm.data_ptr(), ctypes.cast(self.layers, P))
         self.k_pages = torch.from_numpy(cache["k_pages"]).view(i16).to(self.device)
         self.v_pages = torch.from_numpy(cache["v_pages"]).view(i16).to(self.device)

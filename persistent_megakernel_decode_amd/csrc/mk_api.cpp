@@ -28,6 +28,9 @@ extern "C" __global__ void mk_megakernel_steps_b1(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_steps_b2(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_steps_b4(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_steps_b8(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_b1_f8(mk::KArgs A);  // fp8 projections (batch 1)
+extern "C" __global__ void mk_megakernel_b1_f8_trace(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_steps_b1_f8(mk::KArgs A);
 
 namespace {
 
@@ -50,7 +53,8 @@ mk_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-const void* kernel_for(int B, bool traced) {
+const void* kernel_for(int B, bool traced, bool f8) {
+  if (f8) return traced ? (const void*)mk_megakernel_b1_f8_trace : (const void*)mk_megakernel_b1_f8;
   switch (B) {
     case 1: return traced ? (const void*)mk_megakernel_b1_trace : (const void*)mk_megakernel_b1;
     case 2: return traced ? (const void*)mk_megakernel_b2_trace : (const void*)mk_megakernel_b2;
@@ -59,7 +63,8 @@ const void* kernel_for(int B, bool traced) {
   }
 }
 
-const void* steps_kernel_for(int B) {
+const void* steps_kernel_for(int B, bool f8) {
+  if (f8) return (const void*)mk_megakernel_steps_b1_f8;
   switch (B) {
     case 1: return (const void*)mk_megakernel_steps_b1;
     case 2: return (const void*)mk_megakernel_steps_b2;
@@ -257,25 +262,31 @@ static mk_status create_impl(const mk_model_desc* desc, const mk_weights* w, con
   if (pe.empty()) pe = need(w->final_norm, "final_norm");
   if (pe.empty() && !d.tied_embeddings) pe = need(w->lm_head, "lm_head");
   if (pe.empty() && !w->layers) pe = "layers is null";
+  const bool f8 = d.weight_format == MK_WEIGHTS_FP8_E4M3;
   for (int l = 0; pe.empty() && l < d.n_layers; ++l) {
     const mk_layer_weights& L = w->layers[l];
+    // a projection and, for fp8 weights, its row scales
+    auto proj = [&](const void* p, const float* sc, const char* name, const char* sname) {
+      if (pe.empty()) pe = need(p, name);
+      if (pe.empty() && f8) pe = need(sc, sname);
+    };
     pe = need(L.attn_norm, "attn_norm");
     if (pe.empty()) pe = need(L.mlp_norm, "mlp_norm");
-    if (pe.empty()) pe = need(L.w_gate, "w_gate");
-    if (pe.empty()) pe = need(L.w_up, "w_up");
-    if (pe.empty()) pe = need(L.w_down, "w_down");
+    proj(L.w_gate, L.w_gate_scale, "w_gate", "w_gate_scale");
+    proj(L.w_up, L.w_up_scale, "w_up", "w_up_scale");
+    proj(L.w_down, L.w_down_scale, "w_down", "w_down_scale");
     if (m.kinds[l] == MK_LAYER_ATTN) {
-      if (pe.empty()) pe = need(L.wq, "wq");
-      if (pe.empty()) pe = need(L.wk, "wk");
-      if (pe.empty()) pe = need(L.wv, "wv");
-      if (pe.empty()) pe = need(L.wo, "wo");
+      proj(L.wq, L.wq_scale, "wq", "wq_scale");
+      proj(L.wk, L.wk_scale, "wk", "wk_scale");
+      proj(L.wv, L.wv_scale, "wv", "wv_scale");
+      proj(L.wo, L.wo_scale, "wo", "wo_scale");
       if (pe.empty() && d.qk_norm) pe = need(L.q_norm, "q_norm");
       if (pe.empty() && d.qk_norm) pe = need(L.k_norm, "k_norm");
     } else {
-      if (pe.empty()) pe = need(L.w_qkv_delta, "w_qkv_delta");
-      if (pe.empty()) pe = need(L.w_gates, "w_gates");
+      proj(L.w_qkv_delta, L.w_qkv_delta_scale, "w_qkv_delta", "w_qkv_delta_scale");
+      proj(L.w_gates, L.w_gates_scale, "w_gates", "w_gates_scale");
       if (pe.empty()) pe = need(L.conv_w, "conv_w");
-      if (pe.empty()) pe = need(L.wo_delta, "wo_delta");
+      proj(L.wo_delta, L.wo_delta_scale, "wo_delta", "wo_delta_scale");
     }
     if (!pe.empty()) pe = "layer " + std::to_string(l) + ": " + pe;
   }
@@ -313,8 +324,9 @@ static mk_status create_impl(const mk_model_desc* desc, const mk_weights* w, con
   // MK_TRACE=1: the traced kernels (per-op timing stamps; diagnostic)
   const char* trace_env = getenv("MK_TRACE");
   const bool traced = trace_env && atoi(trace_env) != 0;
-  ctx->kernel = kernel_for(P.kernel_batch, traced);
-  ctx->kernel_steps = steps_kernel_for(P.kernel_batch);
+  const bool f8_kernels = d.weight_format == MK_WEIGHTS_FP8_E4M3;  // (batch 1 only: validate_desc)
+  ctx->kernel = kernel_for(P.kernel_batch, traced, f8_kernels);
+  ctx->kernel_steps = steps_kernel_for(P.kernel_batch, f8_kernels);
 
   // one resident workgroup per compute unit is required by the persistent design
   int per_cu = 0, per_cu_steps = 0;

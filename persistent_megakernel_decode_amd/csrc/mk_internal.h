@@ -55,6 +55,11 @@ constexpr uint32_t LAYER_ATTN = 0, LAYER_DELTA = 1;  // the values of mk_layer_k
 // store-completion wait before it (OPF_NO_SIGNAL).
 constexpr uint32_t OPF_TAGGED_IN = 1u;
 constexpr uint32_t OPF_NO_SIGNAL = 2u;
+// A GEMV op whose weights are fp8 (E4M3 codes, one byte each, with fp32 row scales Ws / Ws2): the
+// loader streams a row of K codes exactly as a bf16 row of K / 2 weights (gemv_kv), so slots,
+// pieces and row groups are counted in those 16-bit units; the compute waves read 16 codes per
+// 16-byte chunk against 16 inputs.
+constexpr uint32_t OPF_FP8 = 4u;
 
 // One queue entry (128 bytes).  Pointers are device addresses.
 //
@@ -100,15 +105,17 @@ struct alignas(16) Op {
   uint32_t ld_out;     // floats between batch rows of `out` / `res`
   uint32_t b1;         // GEMV: stream rows taken from W before switching to W2
   uint32_t flags;      // OPF_* bits
-  uint64_t W, W2;      // GEMV weight runs, bf16 rows of K
-  uint64_t pad3;
+  uint64_t W, W2;      // GEMV weight runs, bf16 rows of K (OPF_FP8: fp8 rows of K)
+  uint64_t Ws;         // OPF_FP8: fp32 row scales of the W run (at the op's first row)
   uint64_t in;         // fp32 [batch][ld_in]
   uint64_t gamma;      // bf16 [K] norm gain (norm == 1)
   uint64_t out;        // fp32 [batch][ld_out] (EPI_LOGITS writes the launch's logits instead)
   uint64_t res;        // fp32 [batch][ld_out] residual (EPI_RESID)
-  uint64_t pad2;
+  uint64_t Ws2;        // OPF_FP8: fp32 row scales of the W2 run
 };
 static_assert(sizeof(Op) == 128, "Op must stay 128 bytes");
+// stream elements per row of a GEMV op: 16-bit weights, or pairs of fp8 codes
+constexpr uint32_t gemv_kv(uint32_t K, uint32_t flags) { return (flags & OPF_FP8) ? K / 2 : K; }
 
 // Per-layer device pointers used by ATTN / DELTA ops.
 struct alignas(16) LayerDesc {

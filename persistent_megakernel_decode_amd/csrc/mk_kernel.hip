@@ -539,7 +539,7 @@ __device__ __forceinline__ GemvSeg gemv_seg(const Op& o) {
   g.wa = uni64(o.W);
   g.wb = uni64(o.W2);
   g.na = __builtin_amdgcn_readfirstlane(o.b1);
-  g.rowbytes = __builtin_amdgcn_readfirstlane(o.K * 2);
+  g.rowbytes = __builtin_amdgcn_readfirstlane(gemv_kv(o.K, o.flags) * 2);
   return g;
 }
 __device__ __forceinline__ const char* gemv_row(const GemvSeg& g, u32 rl) {
@@ -585,7 +585,7 @@ __device__ __forceinline__ GemvWalk gemv_walk(const Op& o, const GemvSeg& gsg, u
   gw.R = 16u / o.part;
   gw.lgrs = gemv_lg_rs(o.part, gw.pg);
   gw.nrt = o.epi == EPI_SWIGLU ? 2 * o.nrows : o.nrows;
-  gw.K = o.K;
+  gw.K = gemv_kv(o.K, o.flags);  // in 16-bit stream elements
   // DMA lane d fills LDS chunk d of a block with the block's chunk gemv_pos(d)
   gw.voff0 = 16 * (lane ^ ((lane >> 3) & 3));
   gw.voff1 = 16 * (lane ^ ((lane >> 3) & 3) ^ 2u);
@@ -1189,6 +1189,19 @@ struct GemvAcc<1, 8> {
     h = dot2(wv.w, xh.w, h);
     l = dot2(wv.w, xl.w, l);
   }
+  // fp8 weights: 16 E4M3 codes (byte j of word i is input 4 i + j) against 16 fp32 inputs, each
+  // code widened exactly to fp32 by the hardware conversion (two per instruction)
+  __device__ __forceinline__ void add8(const u32x4 wv, const float* x) {
+    const u32 wd[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], false), c = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], true);
+      h = __builtin_fmaf(a.x, x[4 * i], h);
+      l = __builtin_fmaf(a.y, x[4 * i + 1], l);
+      h = __builtin_fmaf(c.x, x[4 * i + 2], h);
+      l = __builtin_fmaf(c.y, x[4 * i + 3], l);
+    }
+  }
   __device__ __forceinline__ void merge(const GemvAcc& o) {
     h += o.h;
     l += o.l;
@@ -1209,14 +1222,21 @@ struct GemvAcc<1, 8> {
 // One GEMV op with NF input fragments per wave (1, 2, or up to 8).  Row groups are taken GB at a
 // time (GB NF = 4 slots per wait for NF <= 2).  With PG < 8 pieces per group (NF = 1) a slot holds
 // 8 / PG groups and wave w works on group (slot 8 / PG + w / PG), piece w % PG.
-template <int B, int P, int NF, bool AM>  // AM: track the LM head's greedy partials (multi-step kernels)
+// F8 (batch 1): fp8 weights.  The slot layout is the bf16 one over K / 2 16-bit stream elements
+// (a row's codes in pairs), so a lane's 16-byte chunk at stream element k holds the codes of inputs
+// 2k .. 2k + 15: each fragment is 16 inputs (fp32, multiplied without a bf16 split) and every
+// output row is scaled by its fp32 row scale in the epilogue.
+template <int B, int P, int NF, bool AM, bool F8 = false>  // AM: track the LM head's greedy partials (multi-step kernels)
 __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
+  static_assert(!F8 || (B == 1 && P == 8 && NF <= 4), "fp8 weights: batch-1 vector path, at most 4 fragments");
   constexpr u32 R = 16 / P, KP = 32 * P;
   constexpr u32 GB = NF == 1 ? 4 : (NF == 2 ? 2 : 1);
+  constexpr u32 XN = F8 ? 16 : 8;  // inputs per fragment
   const u32 lane = lane_id();
   // the Op's fields as independent scalars (see op_mmv)
   const u32 epi = opq((u32)o.epi), norm = opq((u32)o.norm), flags = opq(o.flags), nrows = opq(o.nrows);
   const u32 pg = opq(o.ppr), K = opq(o.K), row0 = opq(o.row0);
+  const u32 kv = F8 ? K / 2 : K;  // stream elements per row
   const u32 nslots = opq(o.nslots) - (norm ? gain_slots(K) : 0u);  // weight slots (after the gain's)
   const u32 ld_in = opq(o.ld_in), ld_out = opq(o.ld_out);
   const uint64_t in = opq(o.in), outp = opq(o.out), resp = opq(o.res);
@@ -1238,20 +1258,20 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   // RMSNorm factors out of the sum: the tiles multiply x * gain (input and gain loads share one
   // round trip) and the epilogue scales each output by (mean x^2 + eps)^-1/2, so no barrier stands
   // between the loads and the stream.
-  float xf[NF][8];
-  u32x4 gv[NF];
+  float xf[NF][XN];
+  u32x4 gv[NF], gv2[NF];  // gv2: the second 8 gains of an fp8 fragment
   const float* xin = (const float*)in + (size_t)(B == 1 ? 0u : bl) * ld_in;
   u32 fv = 0;  // fragments this lane loads
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const u32 q = pg >= 8 ? 8 * f + w : w % pg;
     const u32 k0 = q * KP + koff;
-    const bool v = (u32)f < nf && (B == 1 || bl < (u32)B) && k0 < K;
+    const bool v = (u32)f < nf && (B == 1 || bl < (u32)B) && k0 < kv;
     fv |= v ? 1u << f : 0u;
-    if (v) ld8_sc1(xin + k0, xf[f]);
+    if (v) ldn_sc1<XN>(xin + (F8 ? 2 * k0 : k0), xf[f]);
     else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xf[f][e] = 0.0f;
+      for (int e = 0; e < (int)XN; ++e) xf[f][e] = 0.0f;
     }
   }
   // the RMSNorm gain arrives in the op's first ring slots (streamed ahead by the loader like the
@@ -1263,9 +1283,11 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const u32 q = pg >= 8 ? 8 * f + w : w % pg;
-      const u32 byte = 2 * (q * KP + koff);
-      gv[f] = ((fv >> f) & 1u) ? g_ring[((seq + byte / SLOT) % NSLOT) * (SLOT / 16) + (byte % SLOT) / 16]
-                               : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+      const u32 byte = 2 * (F8 ? 2 : 1) * (q * KP + koff);  // (fp8: 32 bytes of gains, one slot)
+      const u32 at = ((seq + byte / SLOT) % NSLOT) * (SLOT / 16) + (byte % SLOT) / 16;
+      const u32x4 one = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+      gv[f] = ((fv >> f) & 1u) ? g_ring[at] : one;
+      if constexpr (F8) gv2[f] = ((fv >> f) & 1u) ? g_ring[at + 1] : one;
     }
     release_upto(w, seq + gs);
     seq += gs;
@@ -1288,6 +1310,20 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   }
   // residual rows of this thread (epilogue row r = thread index), fetched now, off the critical path
   const u32 tid = w * 64 + lane, par = ctag() & 1u;
+  // fp8: the row scales of this op's runs (gate / up rows: W / W2 at the same row)
+  const u32 b1 = F8 ? opq(o.b1) : 0u;
+  const float* ws1 = F8 ? (const float*)opq(o.Ws) : nullptr;
+  const float* ws2 = F8 ? (const float*)opq(o.Ws2) : nullptr;
+  auto row_scale = [&](u32 r, bool up) -> float {
+    return up ? ws2[r] : (r < b1 || epi == EPI_SWIGLU ? ws1[r] : ws2[r - b1]);
+  };
+  float sc0 = 1.0f, sc1 = 1.0f;  // this thread's first epilogue row
+  if constexpr (F8) {
+    if (tid < nrows) {
+      sc0 = row_scale(tid, false);
+      if (epi == EPI_SWIGLU) sc1 = row_scale(tid, true);
+    }
+  }
   float rv[B];
 #pragma unroll
   for (int b = 0; b < B; ++b)
@@ -1297,7 +1333,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
     // poll the inputs themselves: re-read every fragment that does not yet show this launch's parity
     u32 todo = 0;
 #pragma unroll
-    for (int f = 0; f < NF; ++f) todo |= ((fv >> f) & 1u) && !tags_ok<8>(xf[f], par) ? 1u << f : 0u;
+    for (int f = 0; f < NF; ++f) todo |= ((fv >> f) & 1u) && !tags_ok<XN>(xf[f], par) ? 1u << f : 0u;
     Watchdog wd(A);
     while (__builtin_amdgcn_ballot_w64(todo != 0) != 0) {
       if (aborted() || wd.expired()) return false;
@@ -1305,11 +1341,11 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const u32 q = pg >= 8 ? 8 * f + w : w % pg;
-        if ((todo >> f) & 1u) ld8_sc1(xin + q * KP + koff, xf[f]);
+        if ((todo >> f) & 1u) ldn_sc1<XN>(xin + (F8 ? 2 : 1) * (q * KP + koff), xf[f]);
       }
       todo = 0;
 #pragma unroll
-      for (int f = 0; f < NF; ++f) todo |= ((fv >> f) & 1u) && !tags_ok<8>(xf[f], par) ? 1u << f : 0u;
+      for (int f = 0; f < NF; ++f) todo |= ((fv >> f) & 1u) && !tags_ok<XN>(xf[f], par) ? 1u << f : 0u;
     }
   }
   trace_ready(A, w);
@@ -1321,7 +1357,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss += xf[f][e] * xf[f][e];
+        for (int e = 0; e < (int)XN; ++e) ss += xf[f][e] * xf[f][e];
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
@@ -1330,20 +1366,31 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
     }
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const u32x4 g4 = gv[f];
-      const float g[8] = {bflo(g4.x), bfhi(g4.x), bflo(g4.y), bfhi(g4.y), bflo(g4.z), bfhi(g4.z), bflo(g4.w), bfhi(g4.w)};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xf[f][e] *= g[e];
+      for (int hf = 0; hf < (int)XN / 8; ++hf) {
+        const u32x4 g4 = hf ? gv2[f] : gv[f];
+        const float g[8] = {bflo(g4.x), bfhi(g4.x), bflo(g4.y), bfhi(g4.y), bflo(g4.z), bfhi(g4.z), bflo(g4.w), bfhi(g4.w)};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xf[f][8 * hf + e] *= g[e];
+      }
     }
   }
   bf16x8 xh[NF], xl[NF];
+  if constexpr (!F8) {
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    u32x4 h, l;
-    split_bf16x8(xf[f], h, l);
-    xh[f] = __builtin_bit_cast(bf16x8, h);
-    xl[f] = __builtin_bit_cast(bf16x8, l);
+    for (int f = 0; f < NF; ++f) {
+      u32x4 h, l;
+      split_bf16x8(xf[f], h, l);
+      xh[f] = __builtin_bit_cast(bf16x8, h);
+      xl[f] = __builtin_bit_cast(bf16x8, l);
+    }
   }
+  // one weight chunk of fragment f into an accumulator
+#define MK_GEMV_ADD(acc, wv, f)                          \
+  do {                                                   \
+    if constexpr (F8) (acc).add8((wv), xf[f]);           \
+    else (acc).add((wv), xh[f], xl[f]);                  \
+  } while (0)
 
   if (NF > 1 || pg >= 8) {
     // groups in order; a group's nf slots are consecutive and wave w takes piece w of each
@@ -1358,7 +1405,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
           for (u32 f = 0; f < NF; ++f)
 #pragma unroll
-            for (u32 gb = 0; gb < GB; ++gb) acc[gb].add(stg[(bt * GB + gb) * NF + f], xh[f], xl[f]);
+            for (u32 gb = 0; gb < GB; ++gb) MK_GEMV_ADD(acc[gb], stg[(bt * GB + gb) * NF + f], f);
 #pragma unroll
           for (u32 gb = 0; gb < GB; ++gb) acc[gb].finish(lane, bt * GB + gb, w, RW, nrt);
         }
@@ -1371,8 +1418,8 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
           for (int f = 0; f < NF; ++f) {
             if ((u32)f < nf) {
-              if (f & 1) a1.add(stg[g * NF + f], xh[f], xl[f]);
-              else a0.add(stg[g * NF + f], xh[f], xl[f]);
+              if (f & 1) MK_GEMV_ADD(a1, stg[g * NF + f], f);
+              else MK_GEMV_ADD(a0, stg[g * NF + f], f);
             }
           }
           a0.merge(a1);
@@ -1398,7 +1445,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
         for (u32 f = 0; f < NF; ++f)
 #pragma unroll
-          for (u32 gb = 0; gb < GB; ++gb) acc[gb].add(wv[gb * NF + f], xh[f], xl[f]);
+          for (u32 gb = 0; gb < GB; ++gb) MK_GEMV_ADD(acc[gb], wv[gb * NF + f], f);
 #pragma unroll
         for (u32 gb = 0; gb < GB; ++gb) acc[gb].finish(lane, g0 + gb, w, RW, nrt);
         seq += NS;
@@ -1419,8 +1466,8 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         if ((u32)f < nf) {
-          if (f & 1) a1.add(wv[f], xh[f], xl[f]);
-          else a0.add(wv[f], xh[f], xl[f]);
+          if (f & 1) MK_GEMV_ADD(a1, wv[f], f);
+          else MK_GEMV_ADD(a0, wv[f], f);
         }
       }
       a0.merge(a1);
@@ -1443,7 +1490,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[i].init();
-        acc[i].add(wv[i], xh[0], xl[0]);
+        MK_GEMV_ADD(acc[i], wv[i], 0);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i].finish(lane, (((s0 + i) * 8) >> lgpg) + gsub, w & (pg - 1), RW, nrt);
@@ -1457,7 +1504,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
       if (g < nrg) {
         GemvAcc<B, P> acc;
         acc.init();
-        acc.add(wv, xh[0], xl[0]);
+        MK_GEMV_ADD(acc, wv, 0);
         acc.finish(lane, g, w & (pg - 1), RW, nrt);
       }
       seq += 1;
@@ -1487,9 +1534,11 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
       float v = 0.0f;
       for (u32 j = 0; j < RW; ++j) v += g_red[(j * B + b) * nrt + r];
       v *= rstd[b];
+      if constexpr (F8) v *= r == tid ? sc0 : row_scale(r, false);
       if (epi == EPI_SWIGLU) {
         float u = 0.0f;
         for (u32 j = 0; j < RW; ++j) u += g_red[(j * B + b) * nrt + r + nrows];
+        if constexpr (F8) u *= r == tid ? sc1 : row_scale(r, true);
         st_tag((float*)outp + (size_t)b * ld_out + row, silu(v) * (u * rstd[b]), par);
       } else if (epi == EPI_RESID) {
         const float* rp = (const float*)resp + (size_t)b * ld_out + row;
@@ -1514,16 +1563,25 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
     for (u32 r = tid; r < nrows; r += NC * 64) {
       float v = 0.0f;
       for (u32 j = 0; j < RW; ++j) v += g_red[(j * B + b) * nrt + r];
+      if constexpr (F8) v *= row_scale(r, false);
       amax_better(bv[b], bi[b], v * rstd[b], (int)(row0 + r));
     }
   }
   return op_amax<B>(A, o, w, gen, bv, bi, 1);
+#undef MK_GEMV_ADD
 }
 
-template <int B, bool AM>
+template <int B, bool AM, bool F8>  // F8: kernels for models with fp8 projections (the LM head stays bf16)
 __device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
   constexpr int P = GemvWidth<B>::P;
   const u32 pg = o.ppr;
+  if constexpr (F8 && B == 1) {
+    if (o.flags & OPF_FP8) {  // at most 32 pieces per row group (the host checks)
+      if (pg <= 8) return op_gemv_nf<B, P, 1, AM, true>(A, o, w, seq, gen);
+      if (pg == 16) return op_gemv_nf<B, P, 2, AM, true>(A, o, w, seq, gen);
+      return op_gemv_nf<B, P, 4, AM, true>(A, o, w, seq, gen);
+    }
+  }
   if (pg <= 8) return op_gemv_nf<B, P, 1, AM>(A, o, w, seq, gen);
   if (pg == 16) return op_gemv_nf<B, P, 2, AM>(A, o, w, seq, gen);
   return op_gemv_nf<B, P, 8, AM>(A, o, w, seq, gen);
@@ -2308,7 +2366,7 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
 // One decode step's ops of this CU's queue, [q0, q1).  seq (ring slots consumed) and gen (compute
 // barrier count) carry over.  Returns false on abort.  AM: the LM head also leaves its greedy
 // partials (multi-step kernels).
-template <int B, bool AM>
+template <int B, bool AM, bool F8>
 __device__ __forceinline__ bool op_loop(KPtr ap, u32 q0, u32 q1, u32 w, u32& seq, u32& gen) {
   ItemCache ic;  // a new step has a new attention plan
   for (u32 oi = q0; oi < q1; ++oi) {
@@ -2336,7 +2394,7 @@ __device__ __forceinline__ bool op_loop(KPtr ap, u32 q0, u32 q1, u32 w, u32& seq
         op_embed_finish(A, w, gen);
         break;
       case OP_GEMV:
-        if constexpr (B < 8) alive = op_gemv<B, AM>(A, o, w, seq, gen);
+        if constexpr (B < 8) alive = op_gemv<B, AM, F8>(A, o, w, seq, gen);
         break;
       case OP_MMV:
         if constexpr (B == 8) alive = op_mmv<B, AM>(A, o, w, seq, gen);
@@ -2376,18 +2434,18 @@ __device__ __forceinline__ bool op_loop(KPtr ap, u32 q0, u32 q1, u32 w, u32& seq
 // measured slower).  (The loader's step loop is inlined: as a call it measured slower.)
 // Arguments arrive in vector registers; they are uniform and restated so.  Returns seq | gen << 32,
 // or ~0 on abort.
-template <int B>
+template <int B, bool F8>
 __device__ __noinline__ uint64_t op_loop_call(KPtr ap, u32 q0, u32 q1, u32 w, u32 seq, u32 gen) {
   q0 = __builtin_amdgcn_readfirstlane(q0);
   q1 = __builtin_amdgcn_readfirstlane(q1);
   w = __builtin_amdgcn_readfirstlane(w);
   seq = __builtin_amdgcn_readfirstlane(seq);
   gen = __builtin_amdgcn_readfirstlane(gen);
-  if (!op_loop<B, true>(uniform_kptr(ap), q0, q1, w, seq, gen)) return ~0ull;
+  if (!op_loop<B, true, F8>(uniform_kptr(ap), q0, q1, w, seq, gen)) return ~0ull;
   return (uint64_t)seq | ((uint64_t)gen << 32);
 }
 
-template <int B, bool MS>
+template <int B, bool MS, bool F8>
 __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
   u32 seq = 0, gen = 0;
   const u32 nsteps = MS ? (u32)kargs().n_steps : 1u;
@@ -2416,12 +2474,12 @@ __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
       if (!cbar(A, gen)) return;
     }
     if constexpr (MS) {
-      const uint64_t r = op_loop_call<B>(kernarg_ptr(), q0, q1, w, seq, gen);
+      const uint64_t r = op_loop_call<B, F8>(kernarg_ptr(), q0, q1, w, seq, gen);
       if (r == ~0ull) return;
       seq = __builtin_amdgcn_readfirstlane((u32)r);
       gen = __builtin_amdgcn_readfirstlane((u32)(r >> 32));
     } else {
-      if (!op_loop<B, false>(kernarg_ptr(), q0, q1, w, seq, gen)) return;
+      if (!op_loop<B, false, F8>(kernarg_ptr(), q0, q1, w, seq, gen)) return;
     }
     {  // step epilogue
       if (multi) {  // this compute unit's stores of the step are complete: publish the step
@@ -2448,7 +2506,7 @@ __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
   }
 }
 
-template <int B, bool MS>
+template <int B, bool MS, bool F8 = false>  // F8: models with fp8 projections (batch 1)
 __device__ __forceinline__ void megakernel_body(const KArgs& A) {
   const u32 wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index: uniform per wave
   if (threadIdx.x < NC) g_consumed[threadIdx.x] = 0;
@@ -2459,7 +2517,7 @@ __device__ __forceinline__ void megakernel_body(const KArgs& A) {
   if (earlier_launch_failed(A)) return;  // uniform: the same word for every wave of the grid
   const u32 q0 = A.queue_off[blockIdx.x], q1 = A.queue_off[blockIdx.x + 1];
   if (wv == 0) loader<MS>(q0, q1);
-  else compute<B, MS>(q0, q1, wv - 1);
+  else compute<B, MS, F8>(q0, q1, wv - 1);
 }
 
 }  // namespace mk
@@ -2473,9 +2531,11 @@ extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b1)(mk::K
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b2)(mk::KArgs A) { mk::megakernel_body<2, false>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b4)(mk::KArgs A) { mk::megakernel_body<4, false>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b8)(mk::KArgs A) { mk::megakernel_body<8, false>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b1_f8)(mk::KArgs A) { mk::megakernel_body<1, false, true>(A); }
 #if !MK_TRACE_STAMPS
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b1(mk::KArgs A) { mk::megakernel_body<1, true>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b2(mk::KArgs A) { mk::megakernel_body<2, true>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b4(mk::KArgs A) { mk::megakernel_body<4, true>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b8(mk::KArgs A) { mk::megakernel_body<8, true>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b1_f8(mk::KArgs A) { mk::megakernel_body<1, true, true>(A); }
 #endif

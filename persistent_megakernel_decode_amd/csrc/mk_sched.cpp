@@ -44,11 +44,17 @@ std::string validate_desc(const mk_model_desc* desc, ModelShape* out, mk_status*
   if (d.n_layers < 1 || d.hidden < 8 || d.vocab < 1 || d.ffn < 8) return "n_layers, hidden, vocab and ffn must be positive";
   if (!d.layer_kind) return "layer_kind is null";
   if (d.max_batch < 1 || d.max_ctx < 1) return "max_batch and max_ctx must be positive";
+  if (d.weight_format != MK_WEIGHTS_BF16 && d.weight_format != MK_WEIGHTS_FP8_E4M3)
+    return fmt("weight_format %d is not a mk_weight_format", d.weight_format);
   *st = MK_ERR_UNSUPPORTED;
   if (d.max_batch > 8) return "max_batch above 8 is not supported";
   if (d.hidden % 8 || d.ffn % 8) return "hidden and ffn must be multiples of 8";
   if (d.page_size != 16) return "page_size must be 16";
   if (!(d.rms_eps > 0.0f) || !(d.rope_base > 1.0f)) return "rms_eps must be > 0 and rope_base > 1";
+  if (d.weight_format == MK_WEIGHTS_FP8_E4M3) {
+    if (d.max_batch != 1) return "fp8 weights run on the batch-1 path only (max_batch must be 1)";
+    if (d.hidden % 16 || d.ffn % 16) return "fp8 weights need hidden and ffn to be multiples of 16";
+  }
   out->d = d;
   out->kinds.assign(d.layer_kind, d.layer_kind + d.n_layers);
   out->n_attn = out->n_delta = 0;
@@ -92,6 +98,12 @@ static bool gemv_pg_ok(uint32_t pg) { return pg == 1 || pg == 2 || pg == 4 || (p
 static uint32_t gemv_slots(uint32_t nrg, uint32_t pg) { return pg >= 8 ? nrg * (pg / 8) : (nrg * pg + 7) / 8; }
 
 namespace {
+// fp32 row scales of a projection's (up to three) weight runs, for fp8 weights
+struct RowScales {
+  bool f8 = false;
+  uint64_t s[3] = {0, 0, 0};
+};
+
 struct Builder {
   const ModelShape& m;
   Plan& P;
@@ -104,19 +116,26 @@ struct Builder {
     return (int)stage_ops.size() - 1;
   }
 
-  // Row-tiled GEMV stage over N output rows of length K.
+  // Row-tiled GEMV stage over N output rows of length K.  With sc.f8 the weight runs W / W2 / W3
+  // are fp8 codes and sc.s the fp32 row scales of each run.
   void gemv(int stage, int wait, int layer, uint32_t N, uint32_t K, uint8_t epi, bool norm, uint64_t W, uint64_t W2,
             uint64_t W3, uint32_t b1, uint32_t b2, uint64_t in, uint32_t ld_in, uint64_t gamma, uint64_t out,
-            uint32_t ld_out, uint64_t res) {
+            uint32_t ld_out, uint64_t res, const RowScales& sc = RowScales{}) {
     if (!err.empty()) return;
     const int B = P.kernel_batch;
+    if (sc.f8 && (B != 1 || K % 16)) {
+      err = fmt("fp8 projection with %u inputs at batch width %d (needs batch 1, inputs a multiple of 16)", K, B);
+      return;
+    }
     if (B >= 8) {
       mmv(stage, wait, layer, N, K, epi, norm, W, W2, W3, b1, b2, in, ld_in, gamma, out, ld_out, res);
       return;
     }
     const int Pp = gemv_part(B), R = 16 / Pp;
-    const int pg = gemv_pg((int)K, Pp);
-    if (pg > GEMV_MAX_PG) {
+    const uint32_t flags = sc.f8 ? OPF_FP8 : 0u;
+    const uint32_t kv = gemv_kv(K, flags);  // stream elements per row
+    const int pg = gemv_pg((int)kv, Pp);
+    if (pg > GEMV_MAX_PG || (sc.f8 && pg > 32)) {  // (fp8: at most 4 input fragments of 16 per wave)
       err = fmt("projection with %u inputs is too long for batch width %d", K, B);
       return;
     }
@@ -159,22 +178,26 @@ struct Builder {
       o.row0 = r0;
       o.nrows = r1 - r0;
       o.K = K;
+      o.flags = flags;
       o.part = (uint8_t)Pp;
       o.ppr = (uint32_t)pg;
       o.nslots = gemv_slots(o.nrows * mult / R, (uint32_t)pg) + (norm ? gain_slots(K) : 0u);
       o.ld_in = ld_in;
       o.ld_out = ld_out;
-      // weight runs: at most two contiguous row runs per op
-      const uint64_t rb = (uint64_t)K * 2;
+      // weight runs: at most two contiguous row runs per op (fp8 row scales: the same runs)
+      const uint64_t rb = (uint64_t)kv * 2;
       if (epi == EPI_SWIGLU) {
         o.W = W ? W + r0 * rb : 0;
         o.W2 = W2 ? W2 + r0 * rb : 0;
+        o.Ws = sc.s[0] ? sc.s[0] + r0 * 4ull : 0;
+        o.Ws2 = sc.s[1] ? sc.s[1] + r0 * 4ull : 0;
         o.b1 = o.nrows;
       } else {
         const uint64_t segs[3] = {W, W2, W3};
         const uint32_t start[3] = {0u, b1, b2}, end[3] = {b1, b2, 0xFFFFFFFFu};
         int sa = r0 < b1 ? 0 : (r0 < b2 ? 1 : 2);
         o.W = segs[sa] ? segs[sa] + (uint64_t)(r0 - start[sa]) * rb : 0;
+        o.Ws = sc.s[sa] ? sc.s[sa] + (uint64_t)(r0 - start[sa]) * 4 : 0;
         const uint32_t na = std::min<uint32_t>(o.nrows, end[sa] - r0);
         o.b1 = na;
         o.W2 = 0;
@@ -184,6 +207,7 @@ struct Builder {
             return;
           }
           o.W2 = segs[sa + 1];
+          o.Ws2 = sc.s[sa + 1];
         }
       }
       o.in = in; o.gamma = gamma; o.out = out; o.res = res;
@@ -335,6 +359,17 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
   // ---------------- stages and ops
   Builder bd{m, P, n_cus, {}, ""};
   auto wptr = [&](const void* p) -> uint64_t { return (uint64_t)(uintptr_t)p; };
+  const bool f8 = d.weight_format == MK_WEIGHTS_FP8_E4M3;
+  auto scales = [&](const float* a, const float* b = nullptr, const float* c3 = nullptr) {
+    RowScales r;
+    r.f8 = f8;
+    if (f8) {
+      r.s[0] = wptr(a);
+      r.s[1] = wptr(b);
+      r.s[2] = wptr(c3);
+    }
+    return r;
+  };
   const mk_layer_weights* LW = w ? w->layers : nullptr;
   const uint64_t NONE = ~0u;
   const int s_embed = bd.new_stage();
@@ -364,12 +399,14 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
       const int s_qkv = bd.new_stage();
       bd.gemv(s_qkv, prev, l, (uint32_t)qkv_w, (uint32_t)H, EPI_STORE, true, lw ? wptr(lw->wq) : 0,
               lw ? wptr(lw->wk) : 0, lw ? wptr(lw->wv) : 0, (uint32_t)(Hq * hd), (uint32_t)((Hq + Hkv) * hd), x_in,
-              (uint32_t)H, lw ? wptr(lw->attn_norm) : 0, ws(Q.qkv), (uint32_t)qkv_w, 0);
+              (uint32_t)H, lw ? wptr(lw->attn_norm) : 0, ws(Q.qkv), (uint32_t)qkv_w, 0,
+              scales(lw ? lw->wq_scale : nullptr, lw ? lw->wk_scale : nullptr, lw ? lw->wv_scale : nullptr));
       const int s_attn = bd.new_stage();
       bd.items(s_attn, s_qkv, l, OP_ATTN, P.n_items, 0);
       s_mix = bd.new_stage();
       bd.gemv(s_mix, s_attn, l, (uint32_t)H, (uint32_t)(Hq * hd), EPI_RESID, false, lw ? wptr(lw->wo) : 0, 0, 0,
-              (uint32_t)NONE, (uint32_t)NONE, ws(Q.mix_o), (uint32_t)P.mix_dim, 0, ws(Q.x_mix), (uint32_t)H, x_in);
+              (uint32_t)NONE, (uint32_t)NONE, ws(Q.mix_o), (uint32_t)P.mix_dim, 0, ws(Q.x_mix), (uint32_t)H, x_in,
+              scales(lw ? lw->wo_scale : nullptr));
       ++ia;
     } else {
       D.kind = LAYER_DELTA;
@@ -383,22 +420,26 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
       const int s_in = bd.new_stage();
       bd.gemv(s_in, prev, l, (uint32_t)u_w, (uint32_t)H, EPI_STORE, true, lw ? wptr(lw->w_qkv_delta) : 0,
               lw ? wptr(lw->w_gates) : 0, 0, (uint32_t)m.C, (uint32_t)NONE, x_in, (uint32_t)H,
-              lw ? wptr(lw->attn_norm) : 0, ws(Q.qkv), (uint32_t)u_w, 0);
+              lw ? wptr(lw->attn_norm) : 0, ws(Q.qkv), (uint32_t)u_w, 0,
+              scales(lw ? lw->w_qkv_delta_scale : nullptr, lw ? lw->w_gates_scale : nullptr));
       const int s_delta = bd.new_stage();
       const int n_items = d.max_batch * nh * (dv / 32);
       bd.items(s_delta, s_in, l, OP_DELTA, n_items, (uint32_t)(32 * dk * 4 / SLOT));
       s_mix = bd.new_stage();
       bd.gemv(s_mix, s_delta, l, (uint32_t)H, (uint32_t)(nh * dv), EPI_RESID, false, lw ? wptr(lw->wo_delta) : 0, 0,
-              0, (uint32_t)NONE, (uint32_t)NONE, ws(Q.mix_o), (uint32_t)P.mix_dim, 0, ws(Q.x_mix), (uint32_t)H, x_in);
+              0, (uint32_t)NONE, (uint32_t)NONE, ws(Q.mix_o), (uint32_t)P.mix_dim, 0, ws(Q.x_mix), (uint32_t)H, x_in,
+              scales(lw ? lw->wo_delta_scale : nullptr));
       ++id;
     }
     const int s_gu = bd.new_stage();
     bd.gemv(s_gu, s_mix, l, (uint32_t)F, (uint32_t)H, EPI_SWIGLU, true, lw ? wptr(lw->w_gate) : 0,
             lw ? wptr(lw->w_up) : 0, 0, (uint32_t)NONE, (uint32_t)NONE, ws(Q.x_mix), (uint32_t)H,
-            lw ? wptr(lw->mlp_norm) : 0, ws(Q.m), (uint32_t)F, 0);
+            lw ? wptr(lw->mlp_norm) : 0, ws(Q.m), (uint32_t)F, 0,
+            scales(lw ? lw->w_gate_scale : nullptr, lw ? lw->w_up_scale : nullptr));
     const int s_down = bd.new_stage();
     bd.gemv(s_down, s_gu, l, (uint32_t)H, (uint32_t)F, EPI_RESID, false, lw ? wptr(lw->w_down) : 0, 0, 0,
-            (uint32_t)NONE, (uint32_t)NONE, ws(Q.m), (uint32_t)F, 0, ws(Q.x_out), (uint32_t)H, ws(Q.x_mix));
+            (uint32_t)NONE, (uint32_t)NONE, ws(Q.m), (uint32_t)F, 0, ws(Q.x_out), (uint32_t)H, ws(Q.x_mix),
+            scales(lw ? lw->w_down_scale : nullptr));
     prev = s_down;
     x_in = ws(Q.x_out);
   }
@@ -422,7 +463,9 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
       o.sig_index = (uint32_t)j;
       const int cu = (int)(j % (size_t)n_cus);
       if (o.opcode == OP_GEMV || o.opcode == OP_MMV) {
-        const double bytes = (double)o.nrows * (o.epi == EPI_SWIGLU ? 2 : 1) * o.K * 2;
+        // streamed weight bytes: 2 per bf16 weight; 1 per fp8 code plus 4 per fp32 row scale
+        const double rows = (double)o.nrows * (o.epi == EPI_SWIGLU ? 2 : 1);
+        const double bytes = (o.flags & OPF_FP8) ? rows * (o.K + 4.0) : rows * o.K * 2;
         P.cu_bytes[cu] += bytes;
         P.weight_bytes += bytes;
       }
@@ -523,7 +566,9 @@ int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
         if (P.kernel_batch > 4) bad(fmt("cu %d op %u: matrix-core GEMV takes at most 4 sequences", c, i));
         if (Pp != (uint32_t)gemv_part(P.kernel_batch)) bad(fmt("cu %d op %u: %u input parts for batch %d", c, i, Pp, P.kernel_batch));
         if (!gemv_pg_ok(pg)) bad(fmt("cu %d op %u: %u pieces per row group", c, i, pg));
-        if ((uint64_t)pg * 32 * Pp < o.K) bad(fmt("cu %d op %u: pieces do not cover a row", c, i));
+        if ((uint64_t)pg * 32 * Pp < gemv_kv(o.K, o.flags)) bad(fmt("cu %d op %u: pieces do not cover a row", c, i));
+        if ((o.flags & OPF_FP8) && (P.kernel_batch != 1 || o.K % 16 || o.epi == EPI_LOGITS || pg > 32))
+          bad(fmt("cu %d op %u: fp8 weights off the batch-1 projection path", c, i));
         if (o.nrows == 0 || o.nrows % R) bad(fmt("cu %d op %u: %u rows, not whole groups of %u", c, i, o.nrows, R));
         if (o.epi != EPI_SWIGLU && o.b1 < o.nrows && o.b1 % R) bad(fmt("cu %d op %u: weight runs split a row group", c, i));
         if (o.epi == EPI_SWIGLU && o.b1 != o.nrows) bad(fmt("cu %d op %u: gate / up runs", c, i));
@@ -562,13 +607,17 @@ int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
   }
   // streamed weight bytes == the model's projection bytes
   const mk_model_desc& d = m.d;
-  double want = (double)d.vocab * d.hidden * 2;
+  // (a projection of rows x cols: 2 bytes per bf16 weight, or 1 per fp8 code and 4 per row scale)
+  const bool f8 = d.weight_format == MK_WEIGHTS_FP8_E4M3;
+  auto pbytes = [&](double rows, double cols) { return f8 ? rows * (cols + 4.0) : rows * cols * 2; };
+  double want = (double)d.vocab * d.hidden * 2;  // the LM head stays bf16
   for (int l = 0; l < d.n_layers; ++l) {
-    want += 3.0 * d.ffn * d.hidden * 2;
+    want += 2 * pbytes(d.ffn, d.hidden) + pbytes(d.hidden, d.ffn);
     if (m.kinds[l] == MK_LAYER_ATTN)
-      want += 2.0 * d.hidden * d.head_dim * (d.n_q_heads + d.n_kv_heads) * 2;
+      want += pbytes((double)(d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim, d.hidden) +
+              pbytes(d.hidden, (double)d.n_q_heads * d.head_dim);
     else
-      want += ((double)m.C + 2.0 * d.n_delta_heads + (double)d.n_delta_heads * d.delta_dv) * d.hidden * 2;
+      want += pbytes((double)m.C + 2.0 * d.n_delta_heads, d.hidden) + pbytes(d.hidden, (double)d.n_delta_heads * d.delta_dv);
   }
   if (std::fabs(want - P.weight_bytes) > 0.5) bad(fmt("streamed %.0f weight bytes, model has %.0f", P.weight_bytes, want));
   return errors;

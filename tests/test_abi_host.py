@@ -26,10 +26,11 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header_layout():
-    # mk_model_desc is 92 bytes of fields padded to 96; the library itself rejects any struct_size
-    # other than its own sizeof (see test_host_rejects_out_of_contract_descriptions / mk_plan calls)
+    # mk_model_desc is 96 bytes (weight_format last, at 92); the library itself rejects any
+    # struct_size other than its own sizeof (see test_host_rejects_out_of_contract_descriptions)
     assert ctypes.sizeof(mkd.mk_model_desc) == 96
-    assert ctypes.sizeof(mkd.mk_layer_weights) == 15 * 8
+    assert mkd.mk_model_desc.weight_format.offset == 92
+    assert ctypes.sizeof(mkd.mk_layer_weights) == (15 + 10) * 8  # 15 tensors, 10 fp8 row-scale pointers
     assert ctypes.sizeof(mkd.mk_kv_cache) == 48
 
 
@@ -38,7 +39,44 @@ def _desc(cfg, max_ctx):
     return mkd.make_desc(s["n_layers"], s["hidden"], s["vocab"], s["ffn"], s["n_q_heads"], s["n_kv_heads"],
                          s["head_dim"], s["qk_norm"], s["tied"], s["rms_eps"], s["rope_base"], s["layer_kinds"],
                          s["max_batch"], s["max_ctx"], s["n_delta_heads"], s["delta_dk"], s["delta_dv"],
-                         s["conv_width"])
+                         s["conv_width"], weight_format=mkd.MK_WEIGHTS_FP8_E4M3 if cfg.weights == "fp8" else 0)
+
+
+def _proj_bytes(cfg, per_weight, per_row):
+    """The model's projection bytes (attention models), per_weight bytes a weight plus per_row a row."""
+    H, F, d = cfg.hidden, cfg.ffn, cfg.head_dim
+    mats = [(cfg.n_q_heads * d, H), (cfg.n_kv_heads * d, H), (cfg.n_kv_heads * d, H), (H, cfg.n_q_heads * d),
+            (F, H), (F, H), (H, F)]
+    return cfg.n_layers * sum(r * (c * per_weight + per_row) for r, c in mats)
+
+
+@pytest.mark.parametrize("name", ["tiny", "0.6b", "8b"])
+def test_fp8_plan_streams_one_byte_per_weight(name):
+    """fp8 projections: the plan checks, and streams one byte per weight plus a 4-byte scale per row
+    (the LM head stays bf16), against 2 bytes per weight for the bf16 model."""
+    cfg = synth.CONFIGS[name]
+    lm = cfg.vocab * cfg.hidden * 2
+    for c, per_weight, per_row in ((cfg, 2, 0), (cfg.replace(weights="fp8"), 1, 4)):
+        info = mkd.mk_plan(_desc(c, 4096 + 256), 256)
+        assert info.errors == 0, mkd.mk_last_error()
+        assert info.weight_bytes == lm + _proj_bytes(c, per_weight, per_row)
+        if name != "tiny":
+            assert info.max_cu_bytes <= 1.03 * info.mean_cu_bytes
+
+
+def test_fp8_out_of_contract_descriptions():
+    """fp8 weights run on the batch-1 path: a wider batch, or an input length that is not a multiple
+    of 16, is MK_ERR_UNSUPPORTED; an unknown weight format is MK_ERR_INVALID_ARG."""
+    cfg = synth.CONFIGS["tiny"].replace(weights="fp8")
+    for c in (cfg.replace(batch=2, ctx=[128, 128]), cfg.replace(hidden=264)):
+        with pytest.raises(mkd.MKError) as e:
+            mkd.mk_plan(_desc(c, 512), 256)
+        assert e.value.status == mkd.MK_ERR_UNSUPPORTED
+    d = _desc(cfg, 512)
+    d.weight_format = 7
+    with pytest.raises(mkd.MKError) as e:
+        mkd.mk_plan(d, 256)
+    assert e.value.status == mkd.MK_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("name", ["tiny", "0.6b", "8b", "13b", "hybrid"])
