@@ -37,6 +37,8 @@ WORKLOADS = {
     "hybrid": "hybrid decoder (24 layers, hidden 2048, 6 GQA + 18 gated delta-rule layers, FFN 6144, vocab 65536), batch 4, ctx 2048",
     "13b": "13B-shape MHA decoder (40 layers, hidden 5120, 40 heads, FFN 13824, vocab 32000), batch 8, ctx U[512,4096], paged",
     "tiny": "tiny decoder (2 layers, hidden 256, GQA 4/2, head_dim 64, FFN 768, vocab 1024), batch 1, ctx 128",
+    "8b-fp8": "8B-shape decoder with fp8 E4M3 projections (fp32 row scales; bf16 embedding, LM head and KV "
+              "cache), batch 1, ctx 4096",
 }
 
 
@@ -45,20 +47,26 @@ def log(msg: str) -> None:
 
 
 def bytes_per_step(cfg, ctx_lens) -> float:
-    """Algorithmic HBM bytes of one decode step: every projection weight once, one embedding row per
-    sequence, the LM head once, K/V of every cached position per attention layer (plus the append),
-    the delta-rule and conv states read and written, and the logits written."""
+    """Algorithmic HBM bytes of one decode step: every projection weight once (2 bytes a bf16 weight,
+    or 1 an fp8 code plus 4 a row scale), one embedding row per sequence, the LM head once, K/V of
+    every cached position per attention layer (plus the append), the delta-rule and conv states read
+    and written, and the logits written."""
     H, F, V, B = cfg.hidden, cfg.ffn, cfg.vocab, cfg.batch
+    fp8 = cfg.weights == "fp8"
+
+    def proj(rows, cols):
+        return rows * (cols + 4.0) if fp8 else rows * cols * 2.0
+
     w = 0.0
     attn_kv = 0.0
     for kind in cfg.kinds():
-        w += 3.0 * F * H * 2
+        w += 2 * proj(F, H) + proj(H, F)
         if kind == 0:
-            w += 2.0 * H * cfg.head_dim * (cfg.n_q_heads + cfg.n_kv_heads) * 2
+            w += proj((cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim, H) + proj(H, cfg.n_q_heads * cfg.head_dim)
             attn_kv += sum(2.0 * c * cfg.n_kv_heads * cfg.head_dim * 2 for c in ctx_lens)  # read K and V
         else:
             C = cfg.n_delta_heads * (2 * cfg.delta_dk + cfg.delta_dv)
-            w += (C + 2.0 * cfg.n_delta_heads + cfg.n_delta_heads * cfg.delta_dv) * H * 2
+            w += proj(C + 2.0 * cfg.n_delta_heads, H) + proj(H, cfg.n_delta_heads * cfg.delta_dv)
             w += C * cfg.conv_width * 2
             attn_kv += B * cfg.n_delta_heads * cfg.delta_dk * cfg.delta_dv * 4 * 2     # S read + write
             attn_kv += B * C * (cfg.conv_width - 1) * 4 * 2                             # conv state
@@ -270,7 +278,8 @@ def run_config(name: str, steps: int, warmup: int, multi_k: int, cpu_budget: flo
         kernel_s = float(np.mean(kms)) * 1e-3
         achieved = mean_bytes / kernel_s / 1e9
         entry = {
-            "workload": WORKLOADS[name], "batch": B, "ctx": ctx0 if B > 1 else ctx0[0], "steps": steps,
+            "workload": WORKLOADS[name], "weights": cfg.weights, "batch": B, "ctx": ctx0 if B > 1 else ctx0[0],
+            "steps": steps,
             "warmup": warmup, "ms_per_step": round(ms_per_step, 4), "tokens_per_s": round(B * steps / elapsed, 2),
             "mbu": round(mean_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
             "bytes_per_step": mean_bytes,
@@ -402,9 +411,9 @@ def run_window(name: str, window: int, launches: int, warmup: int) -> dict:
             "note": "tokens verified per second: every window token's logits per launch"}
 
 
-PER_CONFIG = ("0.6b", "hybrid", "13b")   # measured beside the headline 8B workload
+PER_CONFIG = ("0.6b", "hybrid", "13b", "8b-fp8")  # measured beside the headline 8B workload
 WINDOWS = {"8b": 8, "0.6b": 8}            # verify windows timed beside them
-RUN_STEPS = {"8b": 128, "0.6b": 64, "hybrid": 64, "13b": 64, "tiny": 8}  # decode steps of each workload's run
+RUN_STEPS = {"8b": 128, "0.6b": 64, "hybrid": 64, "13b": 64, "tiny": 8, "8b-fp8": 128}  # decode steps per run
 
 
 def main() -> int:
@@ -449,7 +458,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if head["weights"] == "fp8" else "bf16",
         "data": "synthetic (seeded random-init weights and KV cache of the named shape)",
         "config": {"workload": head["workload"], "batch": B, "ctx": head["ctx"]},
     }

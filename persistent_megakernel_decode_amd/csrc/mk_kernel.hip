@@ -612,7 +612,9 @@ __device__ __forceinline__ void dma_segments(const char* base, u32 rowbytes, u32
 }
 // One ring slot of a GEMV op.  Rows past the op and inputs past K (padding of the last group or
 // piece) re-read bytes of the op's rows: their products meet zero inputs, and nothing is stored for
-// rows past the op.
+// rows past the op.  A padded input wraps to the start of its row (k - K), so the lanes of a padded
+// block fetch distinct, consecutive bytes.  Every slot is 8 DMA instructions, padded or not: the
+// loader's completion tracking counts them.
 __device__ __forceinline__ void issue_gemv(const GemvSeg& gsg, GemvWalk& gw, u32 lane, u32x4* dst) {
   if (gw.plain) {  // the common case: R row segments of one group, base advanced per slot
     const char* base = (const char*)gw.grow + gw.t * (8192u >> gw.lgrs);
@@ -643,7 +645,8 @@ __device__ __forceinline__ void issue_gemv(const GemvSeg& gsg, GemvWalk& gw, u32
       const u32 byte = (u32)blk * 1024 + 16 * gemv_pos(lane, blk, gw.lgrs);
       u32 row = rho0 + byte / sb, k = kappa0 + (byte % sb) / 2;
       if (row >= gw.nrt) row = gw.nrt - 1;
-      if (k >= gw.K) k = 0;
+      if (k >= gw.K) k -= gw.K;
+      if (k >= gw.K) k = 0;  // (rows shorter than the padding)
       __builtin_amdgcn_global_load_lds(gemv_row(gsg, row) + 2 * k, (__attribute__((address_space(3))) void*)(dst + blk * 64), 16, 0, AUX_NT);
     }
   }
