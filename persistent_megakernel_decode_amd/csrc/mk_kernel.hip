@@ -1157,6 +1157,18 @@ __device__ __forceinline__ void gemv_extract(const f32x4 d, u32 lane, u32 g, u32
 __device__ __forceinline__ float dot2(u32 wp, u32 xp, float acc) {  // acc + two bf16 products (exact in fp32)
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp), __builtin_bit_cast(bf16x2, xp), acc, false);
 }
+// 8 E4M3 codes (byte j of w0: code j; of w1: code 4 + j) as bf16, exactly (an E4M3 value has at
+// most 4 significant bits and its exponent range fits bf16's): the top halves of their fp32 values
+__device__ __forceinline__ bf16x8 fp8x8_bf16(u32 w0, u32 w1) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+  auto pk = [](float lo, float hi) {
+    return __builtin_amdgcn_perm(__builtin_bit_cast(u32, hi), __builtin_bit_cast(u32, lo), 0x07060302u);
+  };
+  const u32x4 r = {pk(a.x, a.y), pk(b.x, b.y), pk(c.x, c.y), pk(d.x, d.y)};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 template <int B, int P>
 struct GemvAcc {
   f32x4 h, l;
@@ -1598,9 +1610,18 @@ __device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32&
 // partial sums are added in LDS, four tiles per pass.  RMSNorm factors out of the sum: the tiles
 // multiply x * gain, each lane accumulates x^2 on the side, and the epilogue scales by
 // (mean x^2 + eps)^-1/2.
-template <int B, bool AM>
+// F8: fp8 weights.  The slot is the same 16 rows x 512 bytes, now 512 codes of one segment: wave w
+// takes codes 64 w .. 64 w + 63 of each row, a lane 16 of them, widened exactly to two bf16x8
+// operands (inputs 16 kq .. 16 kq + 7 and 16 kq + 8 .. 16 kq + 15 of the wave's block), each
+// multiplied by the matching halves of the lane's 16 inputs (hi + lo): four tiles' products per
+// chunk.  Inputs are fetched two segments ahead (the same registers as four bf16 segments), and
+// every output row is scaled by its fp32 row scale.
+template <int B, bool AM, bool F8 = false>
 __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
   static_assert(B <= 8 && NC == 8, "one pass holds 8 waves x 4 tiles x 16 rows x 8 columns");
+  constexpr u32 XN = F8 ? 16u : 8u;                    // inputs per lane per segment
+  constexpr u32 KS = F8 ? 2u * MMV_KSEG : MMV_KSEG;    // inputs per segment
+  constexpr int LA = F8 ? 2 : 4;                       // segments whose inputs are fetched ahead
   static_assert(NC * 4 * 16 * 8 <= RED_FLOATS, "MMV partial-sum area");
   const u32 lane = lane_id();
   // the Op's fields as independent scalars: kept whole, its 8-dword load groups are what the
@@ -1609,6 +1630,9 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
   const u32 flags = opq(o.flags);
   const u32 row0 = opq(o.row0), ld_in = opq(o.ld_in), ld_out = opq(o.ld_out);
   const uint64_t in = opq(o.in), gamma = opq(o.gamma), outp = opq(o.out), resp = opq(o.res);
+  const float* ws1 = F8 ? (const float*)opq(o.Ws) : nullptr;  // fp8 row scales of the W / W2 runs
+  const float* ws2 = F8 ? (const float*)opq(o.Ws2) : nullptr;
+  const u32 wb1 = F8 ? opq(o.b1) : 0u;
   const bool swiglu = epi == EPI_SWIGLU;
   const u32 ntg = (nrows + 15) / 16, nt = swiglu ? 2 * ntg : ntg;
   const u32 col = lane & 15, kq = lane >> 4;  // operand row / output column, and k-chunk of the lane
@@ -1625,15 +1649,18 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
   float mbv = -INFINITY;  // LM head: this thread's best logit of its sequence (tid % B) and its row
   int mbi = 0x7FFFFFFF;
 
-  // this lane's inputs of segment ks: x[col][ks*256 + 32 w + 8 kq .. + 8] and their gains
-  auto fetch = [&](u32 ks, float* xv, u32x4& gv) {
-    const u32 k0 = ks * MMV_KSEG + w * 32 + kq * 8;
-    if (cval && ks < nks) ld8_sc1(xin + k0, xv);
+  // this lane's inputs of segment ks: x[col][ks KS + w KS / 8 + kq XN .. + XN] and their gains
+  // (gv2: the second 8 gains of 16, fp8)
+  auto fetch = [&](u32 ks, float* xv, u32x4& gv, u32x4& gv2) {
+    const u32 k0 = ks * KS + w * (KS / 8) + kq * XN;
+    if (cval && ks < nks) ldn_sc1<XN>(xin + k0, xv);
     else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xv[e] = 0.0f;
+      for (int e = 0; e < (int)XN; ++e) xv[e] = 0.0f;
     }
-    gv = (norm && ks < nks) ? *(const u32x4*)(gm + k0) : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const u32x4 one = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    gv = (norm && ks < nks) ? *(const u32x4*)(gm + k0) : one;
+    if constexpr (F8) gv2 = (norm && ks < nks) ? *(const u32x4*)(gm + k0 + 8) : one;
   };
   // tagged inputs: wait until this lane's block of segment ks shows this launch's parity
   const u32 par = ctag() & 1u;
@@ -1641,32 +1668,50 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
   auto ready = [&](u32 ks, float* xv) -> bool {
     const bool need = tcheck && ks < nks;
     Watchdog wd(A);
-    while (__builtin_amdgcn_ballot_w64(need && !tags_ok<8>(xv, par)) != 0) {
+    while (__builtin_amdgcn_ballot_w64(need && !tags_ok<XN>(xv, par)) != 0) {
       if (aborted() || wd.expired()) return false;
       __builtin_amdgcn_s_sleep(1);
-      if (need && !tags_ok<8>(xv, par)) ld8_sc1(xin + ks * MMV_KSEG + w * 32 + kq * 8, xv);
+      if (need && !tags_ok<XN>(xv, par)) ldn_sc1<XN>(xin + ks * KS + w * (KS / 8) + kq * XN, xv);
     }
     return true;
   };
   // one segment: this wave's input block times every tile of the segment (the slots must be full)
-  auto consume = [&](const float* xv, const u32x4& gv) {
-    const float g[8] = {bflo(gv.x), bfhi(gv.x), bflo(gv.y), bfhi(gv.y), bflo(gv.z), bfhi(gv.z), bflo(gv.w), bfhi(gv.w)};
-    float xg[8];
+  auto consume = [&](const float* xv, const u32x4& gv, const u32x4& gv2) {
+    float xg[XN];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ssq += xv[e] * xv[e];
-      xg[e] = xv[e] * g[e];
+    for (int hf = 0; hf < (int)XN / 8; ++hf) {
+      const u32x4 g4 = hf ? gv2 : gv;
+      const float g[8] = {bflo(g4.x), bfhi(g4.x), bflo(g4.y), bfhi(g4.y), bflo(g4.z), bfhi(g4.z), bflo(g4.w), bfhi(g4.w)};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ssq += xv[8 * hf + e] * xv[8 * hf + e];
+        xg[8 * hf + e] = xv[8 * hf + e] * g[e];
+      }
     }
-    u32x4 hi, lo;
-    split_bf16x8(xg, hi, lo);
-    const bf16x8 bh = __builtin_bit_cast(bf16x8, hi), bl = __builtin_bit_cast(bf16x8, lo);
+    bf16x8 bh[XN / 8], bl[XN / 8];
+#pragma unroll
+    for (int hf = 0; hf < (int)XN / 8; ++hf) {
+      u32x4 hi, lo;
+      split_bf16x8(xg + 8 * hf, hi, lo);
+      bh[hf] = __builtin_bit_cast(bf16x8, hi);
+      bl[hf] = __builtin_bit_cast(bf16x8, lo);
+    }
 #pragma unroll
     for (int t = 0; t < MMV_TILES; ++t) {
       if ((u32)t < nt) {
         const char* slot = (const char*)(g_ring + ((seq + t) % NSLOT) * (SLOT / 16));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(slot + aoff));
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[t], 0, 0, 0);
+        const u32x4 c = *(const u32x4*)(slot + aoff);
+        if constexpr (F8) {
+          const bf16x8 a0 = fp8x8_bf16(c.x, c.y), a1 = fp8x8_bf16(c.z, c.w);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bh[0], acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl[0], acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bh[1], acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl[1], acc[t], 0, 0, 0);
+        } else {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, c);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[0], acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[0], acc[t], 0, 0, 0);
+        }
       }
     }
     seq += nt;
@@ -1676,20 +1721,21 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
   // 2-tile op streams in about half a microsecond; an input fetch takes longer).  Thin ops wait
   // for and release several segments at once (gs segments, at most 8 slots), so the ring protocol
   // is paid per 8 slots rather than per segment.
-  const u32 gs = nt <= 2 ? 4u : (nt <= 4 ? 2u : 1u);
-  float xr[4][8];
-  u32x4 gr[4];
+  // (gs divides LA: a wave releases its slots within every batch of LA segments)
+  const u32 gs = nt <= 2 ? (u32)LA : (nt <= 4 ? 2u : 1u);
+  float xr[LA][XN];
+  u32x4 gr[LA], gr2[LA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) fetch(i, xr[i], gr[i]);
-  for (u32 ks = 0; ks < nks; ks += 4) {
+  for (int i = 0; i < LA; ++i) fetch(i, xr[i], gr[i], gr2[i]);
+  for (u32 ks = 0; ks < nks; ks += LA) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < LA; ++i) {
       if (ks + i < nks) {
         if ((u32)i % gs == 0 && !wait_full(A, seq + min(gs, nks - (ks + i)) * nt - 1)) return false;
         if ((flags & OPF_TAGGED_IN) && !ready(ks + i, xr[i])) return false;
-        consume(xr[i], gr[i]);
+        consume(xr[i], gr[i], gr2[i]);
         if (((u32)i + 1) % gs == 0 || ks + i + 1 == nks) release_upto(w, seq);
-        fetch(ks + i + 4, xr[i], gr[i]);
+        fetch(ks + i + LA, xr[i], gr[i], gr2[i]);
       }
     }
   }
@@ -1727,16 +1773,23 @@ __device__ __forceinline__ bool op_mmv(const KArgs& A, const Op& o, u32 w, u32& 
     if (swiglu) {
       const u32 pr = tid / (16 * B);  // gate / up tile pair within the pass
       if (pr < 2 && (u32)(pp * 4) + 2 * pr + 1 < nt) {
-        const float gv = colsum(2 * pr, row, b), uv = colsum(2 * pr + 1, row, b);
+        float gv = colsum(2 * pr, row, b), uv = colsum(2 * pr + 1, row, b);
         const u32 orow = 16 * ((u32)(pp * 2) + pr) + row;
-        if (orow < nrows) st_tag((float*)outp + (size_t)b * ld_out + row0 + orow, silu(gv) * uv, ctag() & 1u);
+        if (orow < nrows) {
+          if constexpr (F8) {  // gate / up row scales
+            gv *= ws1[orow];
+            uv *= ws2[orow];
+          }
+          st_tag((float*)outp + (size_t)b * ld_out + row0 + orow, silu(gv) * uv, ctag() & 1u);
+        }
       }
     } else {
       const u32 tp = tid / (16 * B);
       if (tp < 4 && (u32)(pp * 4) + tp < nt) {
-        const float v = colsum(tp, row, b);
+        float v = colsum(tp, row, b);
         const u32 orow = 16 * ((u32)(pp * 4) + tp) + row, grow = row0 + orow;
         if (orow < nrows) {
+          if constexpr (F8) v *= orow < wb1 ? ws1[orow] : ws2[orow - wb1];  // the row's run's scale
           if (epi == EPI_RESID) {
             const float x = ld_tagged(A, (const float*)resp + (size_t)b * ld_out + grow);
             st_tag((float*)outp + (size_t)b * ld_out + grow, x + v, ctag() & 1u);
@@ -2400,7 +2453,10 @@ __device__ __forceinline__ bool op_loop(KPtr ap, u32 q0, u32 q1, u32 w, u32& seq
         if constexpr (B < 8) alive = op_gemv<B, AM, F8>(A, o, w, seq, gen);
         break;
       case OP_MMV:
-        if constexpr (B == 8) alive = op_mmv<B, AM>(A, o, w, seq, gen);
+        if constexpr (B == 8) {
+          if (F8 && (o.flags & OPF_FP8)) alive = op_mmv<B, AM, F8>(A, o, w, seq, gen);
+          else alive = op_mmv<B, AM>(A, o, w, seq, gen);
+        }
         break;
       case OP_ATTN: alive = A.d == 128 ? op_attn<128>(A, o, w, seq, gen, ic) : op_attn<64>(A, o, w, seq, gen, ic); break;
       case OP_DELTA: alive = A.dk == 128 ? op_delta<128>(A, o, w, seq, gen) : op_delta<64>(A, o, w, seq, gen); break;
@@ -2535,10 +2591,12 @@ extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b2)(mk::K
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b4)(mk::KArgs A) { mk::megakernel_body<4, false>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b8)(mk::KArgs A) { mk::megakernel_body<8, false>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b1_f8)(mk::KArgs A) { mk::megakernel_body<1, false, true>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b8_f8)(mk::KArgs A) { mk::megakernel_body<8, false, true>(A); }
 #if !MK_TRACE_STAMPS
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b1(mk::KArgs A) { mk::megakernel_body<1, true>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b2(mk::KArgs A) { mk::megakernel_body<2, true>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b4(mk::KArgs A) { mk::megakernel_body<4, true>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b8(mk::KArgs A) { mk::megakernel_body<8, true>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b1_f8(mk::KArgs A) { mk::megakernel_body<1, true, true>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b8_f8(mk::KArgs A) { mk::megakernel_body<8, true, true>(A); }
 #endif

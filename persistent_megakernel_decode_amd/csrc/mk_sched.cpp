@@ -52,7 +52,7 @@ std::string validate_desc(const mk_model_desc* desc, ModelShape* out, mk_status*
   if (d.page_size != 16) return "page_size must be 16";
   if (!(d.rms_eps > 0.0f) || !(d.rope_base > 1.0f)) return "rms_eps must be > 0 and rope_base > 1";
   if (d.weight_format == MK_WEIGHTS_FP8_E4M3) {
-    if (d.max_batch != 1) return "fp8 weights run on the batch-1 path only (max_batch must be 1)";
+    if (d.max_batch > 1 && d.max_batch <= 4) return "fp8 weights run at batch width 1 or 8 (max_batch 1, or 5 to 8)";
     if (d.hidden % 16 || d.ffn % 16) return "fp8 weights need hidden and ffn to be multiples of 16";
   }
   out->d = d;
@@ -123,12 +123,12 @@ struct Builder {
             uint32_t ld_out, uint64_t res, const RowScales& sc = RowScales{}) {
     if (!err.empty()) return;
     const int B = P.kernel_batch;
-    if (sc.f8 && (B != 1 || K % 16)) {
-      err = fmt("fp8 projection with %u inputs at batch width %d (needs batch 1, inputs a multiple of 16)", K, B);
+    if (sc.f8 && ((B != 1 && B != 8) || K % 16)) {
+      err = fmt("fp8 projection with %u inputs at batch width %d (needs batch 1 or 8, inputs a multiple of 16)", K, B);
       return;
     }
     if (B >= 8) {
-      mmv(stage, wait, layer, N, K, epi, norm, W, W2, W3, b1, b2, in, ld_in, gamma, out, ld_out, res);
+      mmv(stage, wait, layer, N, K, epi, norm, W, W2, W3, b1, b2, in, ld_in, gamma, out, ld_out, res, sc);
       return;
     }
     const int Pp = gemv_part(B), R = 16 / Pp;
@@ -220,9 +220,12 @@ struct Builder {
   // weight-run conventions as gemv().
   void mmv(int stage, int wait, int layer, uint32_t N, uint32_t K, uint8_t epi, bool norm, uint64_t W, uint64_t W2,
            uint64_t W3, uint32_t b1, uint32_t b2, uint64_t in, uint32_t ld_in, uint64_t gamma, uint64_t out,
-           uint32_t ld_out, uint64_t res) {
-    if (K % MMV_KSEG) {
-      err = fmt("projection input length %u is not a multiple of %d (batch-8 matrix-core path)", K, MMV_KSEG);
+           uint32_t ld_out, uint64_t res, const RowScales& sc) {
+    const uint32_t flags = sc.f8 ? OPF_FP8 : 0u;
+    const uint32_t kv = gemv_kv(K, flags);  // stream elements per row (fp8: a segment is 512 codes)
+    if (K % 16 || kv % MMV_KSEG) {
+      err = fmt("projection input length %u is not a multiple of %d (batch-8 matrix-core path)", K,
+                sc.f8 ? 2 * MMV_KSEG : MMV_KSEG);
       return;
     }
     const bool swiglu = epi == EPI_SWIGLU;
@@ -251,21 +254,25 @@ struct Builder {
         o.row0 = r0;
         o.nrows = r1 - r0;
         o.K = K;
-        o.ppr = K / MMV_KSEG;
+        o.flags = flags;
+        o.ppr = kv / MMV_KSEG;
         const uint32_t ntiles = (swiglu ? 2 : 1) * ((o.nrows + 15) / 16);
         o.nslots = ntiles * o.ppr;
         o.ld_in = ld_in;
         o.ld_out = ld_out;
-        const uint64_t rb = (uint64_t)K * 2;
+        const uint64_t rb = (uint64_t)kv * 2;
         if (swiglu) {
           o.W = W ? W + r0 * rb : 0;
           o.W2 = W2 ? W2 + r0 * rb : 0;
+          o.Ws = sc.s[0] ? sc.s[0] + r0 * 4ull : 0;
+          o.Ws2 = sc.s[1] ? sc.s[1] + r0 * 4ull : 0;
           o.b1 = o.nrows;
         } else {
           const uint64_t segs[3] = {W, W2, W3};
           const uint32_t start[3] = {0u, b1, b2}, end[3] = {b1, b2, 0xFFFFFFFFu};
           const int sa = r0 < b1 ? 0 : (r0 < b2 ? 1 : 2);
           o.W = segs[sa] ? segs[sa] + (uint64_t)(r0 - start[sa]) * rb : 0;
+          o.Ws = sc.s[sa] ? sc.s[sa] + (uint64_t)(r0 - start[sa]) * 4 : 0;
           const uint32_t na = std::min<uint32_t>(o.nrows, end[sa] - r0);
           o.b1 = na;
           o.W2 = 0;
@@ -275,6 +282,7 @@ struct Builder {
               return;
             }
             o.W2 = segs[sa + 1];
+            o.Ws2 = sc.s[sa + 1];
           }
         }
         o.in = in; o.gamma = gamma; o.out = out; o.res = res;
@@ -580,7 +588,9 @@ int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
       if (o.opcode == OP_MMV) {
         const uint32_t ntiles = (o.epi == EPI_SWIGLU ? 2 : 1) * ((o.nrows + 15) / 16);
         if (ntiles > (uint32_t)MMV_TILES) bad(fmt("cu %d op %u: %u row tiles, at most %d", c, i, ntiles, MMV_TILES));
-        if (o.K % MMV_KSEG || o.ppr * MMV_KSEG != o.K) bad(fmt("cu %d op %u: K segments do not cover a row", c, i));
+        const uint32_t kv = gemv_kv(o.K, o.flags);
+        if (kv % MMV_KSEG || o.ppr * MMV_KSEG != kv) bad(fmt("cu %d op %u: K segments do not cover a row", c, i));
+        if ((o.flags & OPF_FP8) && (o.K % 16 || o.epi == EPI_LOGITS)) bad(fmt("cu %d op %u: fp8 operands", c, i));
         if (o.nslots != ntiles * o.ppr) bad(fmt("cu %d op %u: slot count", c, i));
         if (P.kernel_batch > 16) bad(fmt("cu %d op %u: batch wider than a matrix tile", c, i));
       }

@@ -178,6 +178,7 @@ CONFIGS: Dict[str, Config] = {
 # the 8B shape with every projection in fp8 (E4M3 codes, fp32 row scales); LM head, embedding and
 # KV cache bf16
 CONFIGS["8b-fp8"] = CONFIGS["8b"].replace(name="8b-fp8", weights="fp8")
+CONFIGS["13b-fp8"] = CONFIGS["13b"].replace(name="13b-fp8", weights="fp8")
 
 
 def context_lengths(cfg: Config) -> List[int]:

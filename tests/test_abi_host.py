@@ -50,7 +50,7 @@ def _proj_bytes(cfg, per_weight, per_row):
     return cfg.n_layers * sum(r * (c * per_weight + per_row) for r, c in mats)
 
 
-@pytest.mark.parametrize("name", ["tiny", "0.6b", "8b"])
+@pytest.mark.parametrize("name", ["tiny", "0.6b", "8b", "13b"])
 def test_fp8_plan_streams_one_byte_per_weight(name):
     """fp8 projections: the plan checks, and streams one byte per weight plus a 4-byte scale per row
     (the LM head stays bf16), against 2 bytes per weight for the bf16 model."""
@@ -65,10 +65,12 @@ def test_fp8_plan_streams_one_byte_per_weight(name):
 
 
 def test_fp8_out_of_contract_descriptions():
-    """fp8 weights run on the batch-1 path: a wider batch, or an input length that is not a multiple
-    of 16, is MK_ERR_UNSUPPORTED; an unknown weight format is MK_ERR_INVALID_ARG."""
+    """fp8 weights run at batch width 1 or 8: a batch of 2-4, an input length that is not a multiple
+    of 16 (or of 512 at batch width 8) is MK_ERR_UNSUPPORTED; an unknown weight format is
+    MK_ERR_INVALID_ARG."""
     cfg = synth.CONFIGS["tiny"].replace(weights="fp8")
-    for c in (cfg.replace(batch=2, ctx=[128, 128]), cfg.replace(hidden=264)):
+    for c in (cfg.replace(batch=2, ctx=[128, 128]), cfg.replace(batch=4, ctx=[128] * 4), cfg.replace(hidden=264),
+              cfg.replace(batch=8, ctx=[128] * 8)):  # (hidden 256: not a multiple of 512)
         with pytest.raises(mkd.MKError) as e:
             mkd.mk_plan(_desc(c, 512), 256)
         assert e.value.status == mkd.MK_ERR_UNSUPPORTED

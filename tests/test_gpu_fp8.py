@@ -6,7 +6,8 @@ and for the delta-rule layers the recurrent and conv states.  The cases cover ev
 batch-1 fp8 projection: pieces per row group 1, 2 and 4 (slots holding several row groups), 8 with
 and without row groups staged in registers, 16 (two input fragments per wave, padded pieces) and
 24 / 32 (four fragments), the RMSNorm gains, q/k norm with a tied bf16 LM head, the delta-rule
-projections, and the 8B shape at full size.
+projections, and the 8B shape at full size; and the batch-8 matrix-core path (batches 6 and 8,
+ragged contexts, shuffled pages) up to the 13B shape.
 """
 import numpy as np
 import pytest
@@ -32,6 +33,17 @@ CASES = {
     # the 8B shape (QKV / o_proj / gate-up over 4096 inputs: 8 pieces, gate-up staged; down over
     # 14336: 32 pieces), bf16 LM head over 128256 rows
     "8b-fp8": (synth.CONFIGS["8b"].replace(name="8b-fp8", weights="fp8"), 4),
+    # batch 8 (the matrix-core k-outer path, 512 codes per segment), ragged contexts incl. an empty
+    # cache, shuffled pages, gains
+    "small-b8-fp8": (synth.Config("small-b8-fp8", n_layers=2, hidden=512, n_q_heads=4, n_kv_heads=4, head_dim=128,
+                                  ffn=1536, vocab=2048, batch=8, ctx=[5, 40, 0, 17, 100, 3, 64, 31], steps=3, seed=32,
+                                  shuffle_pages=True, gain_range=(0.5, 1.5), weights="fp8"), 3),
+    # batch 6 on the batch-8 kernel, GQA
+    "small-b6-fp8": (synth.Config("small-b6-fp8", n_layers=2, hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                  ffn=2048, vocab=4096, batch=6, ctx=[7, 300, 33, 1, 90, 129], steps=3, seed=33,
+                                  weights="fp8"), 3),
+    # the 13B shape at batch 8 (ragged contexts 512-4096, shuffled pages)
+    "13b-fp8": (synth.CONFIGS["13b"].replace(name="13b-fp8", weights="fp8"), 2),
 }
 
 

@@ -38,6 +38,10 @@ CASES = {
                                                              ctx=[33] * 8), 1, 8),
     # the 0.6B-shape workload at full size, a window of 8 drafted tokens
     "0.6b-w8": (synth.CONFIGS["0.6b"].replace(name="0.6b-w8", batch=8, ctx=[1024] * 8), 1, 8),
+    # fp8 projections: the window's 8 rows on the batch-8 fp8 kernel
+    "d128-fp8-b1-w8": (synth.Config("d128-fp8-w8", n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                    ffn=1024, vocab=2048, batch=8, ctx=[60] * 8, steps=3, seed=34,
+                                    gain_range=(0.5, 1.5), weights="fp8"), 1, 8),
 }
 
 
