@@ -76,7 +76,8 @@ def bytes_per_step(cfg, ctx_lens) -> float:
     return w + attn_kv + norms + B * V * 4
 
 
-PMC_FILE = os.path.join(ROOT, "profiles", "megakernel_8b_b1_ctx4096_pmc.txt")
+PMC_FILES = {"8b": os.path.join(ROOT, "profiles", "megakernel_8b_b1_ctx4096_pmc.txt"),
+             "8b-fp8": os.path.join(ROOT, "profiles", "megakernel_8b_fp8_b1_ctx4096_pmc.txt")}
 
 
 def kernel_source_hash(texts=None) -> str:
@@ -102,10 +103,11 @@ def kernel_source_hash(texts=None) -> str:
 def measured_traffic(config: str):
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary, calibrated against a
     plain copy kernel; None when the summary is missing, for another workload, or for other sources."""
-    if config != "8b" or not os.path.exists(PMC_FILE):
+    path = PMC_FILES.get(config)
+    if path is None or not os.path.exists(path):
         return None
     vals = {}
-    with open(PMC_FILE) as fh:
+    with open(path) as fh:
         for line in fh:
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
