@@ -58,10 +58,9 @@ typedef enum { MK_LAYER_ATTN = 0, MK_LAYER_DELTA = 1 } mk_layer_kind;
  *                       0xFF NaN, no infinities), [out][in] row-major, with one fp32 scale per
  *                       output row: W[r][k] = scale[r] * e4m3(code[r][k]).  Embedding, LM head,
  *                       norm gains, conv taps and the KV cache stay bf16.  Codes must not be
- *                       NaN.  Supported for max_batch 1 (every projection input length -- hidden,
- *                       ffn, n_q_heads * head_dim, n_delta_heads * delta_dv -- a multiple of 16)
- *                       and max_batch 5 to 8 (those lengths multiples of 512); otherwise
- *                       mk_create / mk_plan return MK_ERR_UNSUPPORTED. */
+ *                       NaN.  Every projection input length (hidden, ffn, n_q_heads * head_dim,
+ *                       n_delta_heads * delta_dv) must be a multiple of 16, of 512 when max_batch
+ *                       is 5 to 8; otherwise mk_create / mk_plan return MK_ERR_UNSUPPORTED. */
 typedef enum { MK_WEIGHTS_BF16 = 0, MK_WEIGHTS_FP8_E4M3 = 1 } mk_weight_format;
 
 /* Model description (host memory; copied by mk_create).

@@ -28,11 +28,17 @@ extern "C" __global__ void mk_megakernel_steps_b1(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_steps_b2(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_steps_b4(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_steps_b8(mk::KArgs A);
-extern "C" __global__ void mk_megakernel_b1_f8(mk::KArgs A);  // fp8 projections (batch 1 and 8)
+extern "C" __global__ void mk_megakernel_b1_f8(mk::KArgs A);  // fp8 projections
+extern "C" __global__ void mk_megakernel_b2_f8(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_b4_f8(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_b8_f8(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_b1_f8_trace(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_b2_f8_trace(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_b4_f8_trace(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_b8_f8_trace(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_steps_b1_f8(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_steps_b2_f8(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_steps_b4_f8(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_steps_b8_f8(mk::KArgs A);
 
 namespace {
@@ -57,8 +63,14 @@ mk_status hip_fail(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 const void* kernel_for(int B, bool traced, bool f8) {
-  if (f8 && B == 1) return traced ? (const void*)mk_megakernel_b1_f8_trace : (const void*)mk_megakernel_b1_f8;
-  if (f8) return traced ? (const void*)mk_megakernel_b8_f8_trace : (const void*)mk_megakernel_b8_f8;
+  if (f8) {
+    switch (B) {
+      case 1: return traced ? (const void*)mk_megakernel_b1_f8_trace : (const void*)mk_megakernel_b1_f8;
+      case 2: return traced ? (const void*)mk_megakernel_b2_f8_trace : (const void*)mk_megakernel_b2_f8;
+      case 4: return traced ? (const void*)mk_megakernel_b4_f8_trace : (const void*)mk_megakernel_b4_f8;
+      default: return traced ? (const void*)mk_megakernel_b8_f8_trace : (const void*)mk_megakernel_b8_f8;
+    }
+  }
   switch (B) {
     case 1: return traced ? (const void*)mk_megakernel_b1_trace : (const void*)mk_megakernel_b1;
     case 2: return traced ? (const void*)mk_megakernel_b2_trace : (const void*)mk_megakernel_b2;
@@ -68,7 +80,14 @@ const void* kernel_for(int B, bool traced, bool f8) {
 }
 
 const void* steps_kernel_for(int B, bool f8) {
-  if (f8) return B == 1 ? (const void*)mk_megakernel_steps_b1_f8 : (const void*)mk_megakernel_steps_b8_f8;
+  if (f8) {
+    switch (B) {
+      case 1: return (const void*)mk_megakernel_steps_b1_f8;
+      case 2: return (const void*)mk_megakernel_steps_b2_f8;
+      case 4: return (const void*)mk_megakernel_steps_b4_f8;
+      default: return (const void*)mk_megakernel_steps_b8_f8;
+    }
+  }
   switch (B) {
     case 1: return (const void*)mk_megakernel_steps_b1;
     case 2: return (const void*)mk_megakernel_steps_b2;
@@ -328,7 +347,7 @@ static mk_status create_impl(const mk_model_desc* desc, const mk_weights* w, con
   // MK_TRACE=1: the traced kernels (per-op timing stamps; diagnostic)
   const char* trace_env = getenv("MK_TRACE");
   const bool traced = trace_env && atoi(trace_env) != 0;
-  const bool f8_kernels = d.weight_format == MK_WEIGHTS_FP8_E4M3;  // (batch width 1 or 8: validate_desc)
+  const bool f8_kernels = d.weight_format == MK_WEIGHTS_FP8_E4M3;
   ctx->kernel = kernel_for(P.kernel_batch, traced, f8_kernels);
   ctx->kernel_steps = steps_kernel_for(P.kernel_batch, f8_kernels);
 

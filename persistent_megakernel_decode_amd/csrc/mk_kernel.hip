@@ -1181,6 +1181,15 @@ struct GemvAcc {
     h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xh, h, 0, 0, 0);
     l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xl, l, 0, 0, 0);
   }
+  // fp8 weights: 16 codes, widened exactly to two bf16x8 operands, times the two input halves
+  __device__ __forceinline__ void add8m(const u32x4 wv, const bf16x8 xh0, const bf16x8 xl0, const bf16x8 xh1,
+                                        const bf16x8 xl1) {
+    const bf16x8 a0 = fp8x8_bf16(wv.x, wv.y), a1 = fp8x8_bf16(wv.z, wv.w);
+    h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, xh0, h, 0, 0, 0);
+    l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, xl0, l, 0, 0, 0);
+    h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, xh1, h, 0, 0, 0);
+    l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, xl1, l, 0, 0, 0);
+  }
   __device__ __forceinline__ void merge(const GemvAcc& o) {
     h += o.h;
     l += o.l;
@@ -1237,13 +1246,16 @@ struct GemvAcc<1, 8> {
 // One GEMV op with NF input fragments per wave (1, 2, or up to 8).  Row groups are taken GB at a
 // time (GB NF = 4 slots per wait for NF <= 2).  With PG < 8 pieces per group (NF = 1) a slot holds
 // 8 / PG groups and wave w works on group (slot 8 / PG + w / PG), piece w % PG.
-// F8 (batch 1): fp8 weights.  The slot layout is the bf16 one over K / 2 16-bit stream elements
-// (a row's codes in pairs), so a lane's 16-byte chunk at stream element k holds the codes of inputs
-// 2k .. 2k + 15: each fragment is 16 inputs (fp32, multiplied without a bf16 split) and every
-// output row is scaled by its fp32 row scale in the epilogue.
+// F8: fp8 weights.  The slot layout is the bf16 one over K / 2 16-bit stream elements (a row's
+// codes in pairs), so a lane's 16-byte chunk at stream element k holds the codes of inputs 2k ..
+// 2k + 15: each fragment is 16 inputs, and every output row is scaled by its fp32 row scale in the
+// epilogue.  One sequence multiplies the widened codes by the fp32 inputs on the vector ALUs; two
+// to four widen the chunk to two bf16x8 operands (codes 0-7 and 8-15), each taken with the matching
+// half of the lane's inputs (hi + lo) on the matrix cores: A and B lanes of one (part, k-group)
+// then index the same 16 inputs, so the matched-part extraction is unchanged.
 template <int B, int P, int NF, bool AM, bool F8 = false>  // AM: track the LM head's greedy partials (multi-step kernels)
 __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
-  static_assert(!F8 || (B == 1 && P == 8 && NF <= 4), "fp8 weights: batch-1 vector path, at most 4 fragments");
+  static_assert(!F8 || NF <= 4, "fp8 weights: at most 4 input fragments per wave");
   constexpr u32 R = 16 / P, KP = 32 * P;
   constexpr u32 GB = NF == 1 ? 4 : (NF == 2 ? 2 : 1);
   constexpr u32 XN = F8 ? 16 : 8;  // inputs per fragment
@@ -1390,21 +1402,26 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
       }
     }
   }
-  bf16x8 xh[NF], xl[NF];
-  if constexpr (!F8) {
+  // bf16 hi + lo operands of the inputs: per fragment, or per half fragment for fp8 codes at B > 1
+  constexpr int XH = F8 ? (B == 1 ? 1 : 2) : 1;
+  bf16x8 xh[NF][XH], xl[NF][XH];
+  if constexpr (!F8 || B > 1) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      u32x4 h, l;
-      split_bf16x8(xf[f], h, l);
-      xh[f] = __builtin_bit_cast(bf16x8, h);
-      xl[f] = __builtin_bit_cast(bf16x8, l);
-    }
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int hf = 0; hf < XH; ++hf) {
+        u32x4 h, l;
+        split_bf16x8(xf[f] + 8 * hf, h, l);
+        xh[f][hf] = __builtin_bit_cast(bf16x8, h);
+        xl[f][hf] = __builtin_bit_cast(bf16x8, l);
+      }
   }
   // one weight chunk of fragment f into an accumulator
-#define MK_GEMV_ADD(acc, wv, f)                          \
-  do {                                                   \
-    if constexpr (F8) (acc).add8((wv), xf[f]);           \
-    else (acc).add((wv), xh[f], xl[f]);                  \
+#define MK_GEMV_ADD(acc, wv, f)                                                              \
+  do {                                                                                       \
+    if constexpr (F8 && B == 1) (acc).add8((wv), xf[f]);                                     \
+    else if constexpr (F8) (acc).add8m((wv), xh[f][0], xl[f][0], xh[f][XH - 1], xl[f][XH - 1]); \
+    else (acc).add((wv), xh[f][0], xl[f][0]);                                                \
   } while (0)
 
   if (NF > 1 || pg >= 8) {
@@ -1590,7 +1607,7 @@ template <int B, bool AM, bool F8>  // F8: kernels for models with fp8 projectio
 __device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
   constexpr int P = GemvWidth<B>::P;
   const u32 pg = o.ppr;
-  if constexpr (F8 && B == 1) {
+  if constexpr (F8) {
     if (o.flags & OPF_FP8) {  // at most 32 pieces per row group (the host checks)
       if (pg <= 8) return op_gemv_nf<B, P, 1, AM, true>(A, o, w, seq, gen);
       if (pg == 16) return op_gemv_nf<B, P, 2, AM, true>(A, o, w, seq, gen);
@@ -2591,6 +2608,8 @@ extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b2)(mk::K
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b4)(mk::KArgs A) { mk::megakernel_body<4, false>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b8)(mk::KArgs A) { mk::megakernel_body<8, false>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b1_f8)(mk::KArgs A) { mk::megakernel_body<1, false, true>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b2_f8)(mk::KArgs A) { mk::megakernel_body<2, false, true>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b4_f8)(mk::KArgs A) { mk::megakernel_body<4, false, true>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b8_f8)(mk::KArgs A) { mk::megakernel_body<8, false, true>(A); }
 #if !MK_TRACE_STAMPS
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b1(mk::KArgs A) { mk::megakernel_body<1, true>(A); }
@@ -2598,5 +2617,7 @@ extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_step
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b4(mk::KArgs A) { mk::megakernel_body<4, true>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b8(mk::KArgs A) { mk::megakernel_body<8, true>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b1_f8(mk::KArgs A) { mk::megakernel_body<1, true, true>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b2_f8(mk::KArgs A) { mk::megakernel_body<2, true, true>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b4_f8(mk::KArgs A) { mk::megakernel_body<4, true, true>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b8_f8(mk::KArgs A) { mk::megakernel_body<8, true, true>(A); }
 #endif

@@ -52,7 +52,6 @@ std::string validate_desc(const mk_model_desc* desc, ModelShape* out, mk_status*
   if (d.page_size != 16) return "page_size must be 16";
   if (!(d.rms_eps > 0.0f) || !(d.rope_base > 1.0f)) return "rms_eps must be > 0 and rope_base > 1";
   if (d.weight_format == MK_WEIGHTS_FP8_E4M3) {
-    if (d.max_batch > 1 && d.max_batch <= 4) return "fp8 weights run at batch width 1 or 8 (max_batch 1, or 5 to 8)";
     if (d.hidden % 16 || d.ffn % 16) return "fp8 weights need hidden and ffn to be multiples of 16";
   }
   out->d = d;
@@ -123,8 +122,8 @@ struct Builder {
             uint32_t ld_out, uint64_t res, const RowScales& sc = RowScales{}) {
     if (!err.empty()) return;
     const int B = P.kernel_batch;
-    if (sc.f8 && ((B != 1 && B != 8) || K % 16)) {
-      err = fmt("fp8 projection with %u inputs at batch width %d (needs batch 1 or 8, inputs a multiple of 16)", K, B);
+    if (sc.f8 && K % 16) {
+      err = fmt("fp8 projection with %u inputs (needs a multiple of 16)", K);
       return;
     }
     if (B >= 8) {
@@ -575,7 +574,7 @@ int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
         if (Pp != (uint32_t)gemv_part(P.kernel_batch)) bad(fmt("cu %d op %u: %u input parts for batch %d", c, i, Pp, P.kernel_batch));
         if (!gemv_pg_ok(pg)) bad(fmt("cu %d op %u: %u pieces per row group", c, i, pg));
         if ((uint64_t)pg * 32 * Pp < gemv_kv(o.K, o.flags)) bad(fmt("cu %d op %u: pieces do not cover a row", c, i));
-        if ((o.flags & OPF_FP8) && (P.kernel_batch != 1 || o.K % 16 || o.epi == EPI_LOGITS || pg > 32))
+        if ((o.flags & OPF_FP8) && (o.K % 16 || o.epi == EPI_LOGITS || pg > 32))
           bad(fmt("cu %d op %u: fp8 weights off the batch-1 projection path", c, i));
         if (o.nrows == 0 || o.nrows % R) bad(fmt("cu %d op %u: %u rows, not whole groups of %u", c, i, o.nrows, R));
         if (o.epi != EPI_SWIGLU && o.b1 < o.nrows && o.b1 % R) bad(fmt("cu %d op %u: weight runs split a row group", c, i));

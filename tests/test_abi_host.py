@@ -65,12 +65,12 @@ def test_fp8_plan_streams_one_byte_per_weight(name):
 
 
 def test_fp8_out_of_contract_descriptions():
-    """fp8 weights run at batch width 1 or 8: a batch of 2-4, an input length that is not a multiple
-    of 16 (or of 512 at batch width 8) is MK_ERR_UNSUPPORTED; an unknown weight format is
-    MK_ERR_INVALID_ARG."""
+    """fp8 weights: an input length that is not a multiple of 16 (of 512 at batch width 8) is
+    MK_ERR_UNSUPPORTED; an unknown weight format is MK_ERR_INVALID_ARG; every batch width plans."""
     cfg = synth.CONFIGS["tiny"].replace(weights="fp8")
-    for c in (cfg.replace(batch=2, ctx=[128, 128]), cfg.replace(batch=4, ctx=[128] * 4), cfg.replace(hidden=264),
-              cfg.replace(batch=8, ctx=[128] * 8)):  # (hidden 256: not a multiple of 512)
+    for b in (2, 3, 4):
+        assert mkd.mk_plan(_desc(cfg.replace(batch=b, ctx=[128] * b), 512), 256).errors == 0
+    for c in (cfg.replace(hidden=264), cfg.replace(batch=8, ctx=[128] * 8)):  # (hidden 256: not a multiple of 512)
         with pytest.raises(mkd.MKError) as e:
             mkd.mk_plan(_desc(c, 512), 256)
         assert e.value.status == mkd.MK_ERR_UNSUPPORTED

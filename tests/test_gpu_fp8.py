@@ -6,8 +6,9 @@ and for the delta-rule layers the recurrent and conv states.  The cases cover ev
 batch-1 fp8 projection: pieces per row group 1, 2 and 4 (slots holding several row groups), 8 with
 and without row groups staged in registers, 16 (two input fragments per wave, padded pieces) and
 24 / 32 (four fragments), the RMSNorm gains, q/k norm with a tied bf16 LM head, the delta-rule
-projections, and the 8B shape at full size; and the batch-8 matrix-core path (batches 6 and 8,
-ragged contexts, shuffled pages) up to the 13B shape.
+projections, and the 8B shape at full size; the row-group matrix-core path at batches 2 to 4
+(dense and delta-rule, up to the hybrid workload's shape); and the batch-8 matrix-core path
+(batches 6 and 8, ragged contexts, shuffled pages) up to the 13B shape.
 """
 import numpy as np
 import pytest
@@ -44,6 +45,14 @@ CASES = {
                                   weights="fp8"), 3),
     # the 13B shape at batch 8 (ragged contexts 512-4096, shuffled pages)
     "13b-fp8": (synth.CONFIGS["13b"].replace(name="13b-fp8", weights="fp8"), 2),
+    # batch 2 and 3 (the row-group matrix-core path: 8 and 4 input parts per tile)
+    "tiny-b2-fp8": (synth.SMALL["tiny-gain"].replace(name="tiny-b2-fp8", batch=2, ctx=[128, 33], weights="fp8"), 4),
+    "tiny-ragged-fp8": (synth.SMALL["tiny-gain"].replace(name="tiny-ragged-fp8", batch=3, ctx=[0, 77, 19],
+                                                         shuffle_pages=True, weights="fp8"), 4),
+    # delta-rule hybrid at batch 4, and the hybrid workload's shape at full size
+    "hybrid-b4-fp8": (synth.SMALL["tiny-hybrid"].replace(name="hybrid-b4-fp8", weights="fp8", delta_dk=64, delta_dv=64,
+                                                         batch=4, ctx=[16, 40, 9, 9]), 4),
+    "hybrid-full-fp8": (synth.CONFIGS["hybrid"].replace(name="hybrid-full-fp8", weights="fp8"), 4),
 }
 
 

@@ -42,6 +42,9 @@ CASES = {
                                   ffn=1024, vocab=2048, batch=1, ctx=[4390], steps=3, seed=15), 5, 1),
     # the 0.6B-shape workload at full size (28 layers, tied LM head over 151936 rows): 8 steps per launch
     "0.6b": (synth.CONFIGS["0.6b"], 8, 1),
+    # fp8 projections at batch 3 on the width-4 kernel, ragged contexts across page boundaries
+    "tiny-ragged-fp8": (synth.SMALL["tiny-gain"].replace(name="tiny-ragged-fp8", batch=3, ctx=[14, 77, 30],
+                                                         shuffle_pages=True, weights="fp8"), 5, 1),
     # fp8 projections at batch 8 (the batch-8 fp8 multi-step kernel)
     "small-b8-fp8": (synth.Config("small-b8-fp8", n_layers=2, hidden=512, n_q_heads=4, n_kv_heads=4, head_dim=128,
                                   ffn=1024, vocab=2048, batch=8, ctx=[5, 40, 1, 17, 100, 3, 64, 31], steps=3, seed=35,
