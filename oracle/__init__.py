@@ -48,14 +48,15 @@ class OrcModel(ctypes.Structure):
                 ("delta_decay_first", ctypes.c_int), ("weight_format", ctypes.c_int)]
 
 
-W_BF16, W_FP8 = 0, 1  # orc_model.weight_format
+W_BF16, W_FP8, W_FP4 = 0, 1, 2  # orc_model.weight_format
 
 
 _LAYER_FIELDS = ["attn_norm", "wq", "wk", "wv", "wo", "q_norm", "k_norm", "w_qkv_delta", "w_gates", "conv_w",
                  "wo_delta", "mlp_norm", "w_gate", "w_up", "w_down"]
 
 
-# projections that are fp8 codes with fp32 row scales ("<name>_scale") when the weights are fp8
+# projections that are fp8 codes with fp32 row scales ("<name>_scale") when the weights are fp8, or
+# packed E2M1 codes with E8M0 block scales ("<name>_scale", uint8 [rows][cols / 32]) when fp4
 PROJ_FIELDS = ["wq", "wk", "wv", "wo", "w_qkv_delta", "w_gates", "wo_delta", "w_gate", "w_up", "w_down"]
 
 
@@ -92,6 +93,12 @@ def lib():
         L.orc_matvec_fp8.restype = None
         L.orc_e4m3.argtypes = [ctypes.c_uint8]
         L.orc_e4m3.restype = ctypes.c_double
+        L.orc_e2m1.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1.restype = ctypes.c_double
+        L.orc_e8m0.argtypes = [ctypes.c_uint8]
+        L.orc_e8m0.restype = ctypes.c_double
+        L.orc_matvec_fp4.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, P]
+        L.orc_matvec_fp4.restype = None
         L.orc_rope.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_double]
         L.orc_attend.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, P, P]
         L.orc_silu.argtypes = [ctypes.c_double]
@@ -150,6 +157,26 @@ def matvec_fp8(W_codes, scale, x) -> np.ndarray:
     x = _c(x, np.float32)
     y = np.empty(W.shape[0], dtype=np.float32)
     lib().orc_matvec_fp8(_ptr(W), _ptr(s), _ptr(x), W.shape[0], W.shape[1], _ptr(y))
+    return y
+
+
+def e2m1(code: int) -> float:
+    """The value of one MX E2M1 code (low 4 bits)."""
+    return lib().orc_e2m1(int(code))
+
+
+def e8m0(e: int) -> float:
+    """The value of one MX E8M0 scale byte (NaN for 0xFF)."""
+    return lib().orc_e8m0(int(e))
+
+
+def matvec_fp4(W_packed, S, x) -> np.ndarray:
+    """y[r] = sum_k e8m0(S[r][k // 32]) e2m1(code(r, k)) x[k], codes packed two per byte, low nibble first."""
+    W = _c(W_packed, np.uint8)
+    S = _c(S, np.uint8)
+    x = _c(x, np.float32)
+    y = np.empty(W.shape[0], dtype=np.float32)
+    lib().orc_matvec_fp4(_ptr(W), _ptr(S), _ptr(x), W.shape[0], x.size, _ptr(y))
     return y
 
 
@@ -235,23 +262,25 @@ class DecodeOracle:
         m.layer_kind = self.kinds.ctypes.data
         m.page_size = cfg.page_size
         m.delta_decay_first = decay_first
-        fp8 = weights.get("format", "bf16") == "fp8"
-        m.weight_format = W_FP8 if fp8 else W_BF16
+        fmt = weights.get("format", "bf16")
+        fp8, fp4 = fmt == "fp8", fmt == "fp4"
+        m.weight_format = W_FP8 if fp8 else (W_FP4 if fp4 else W_BF16)
         self.m = m
         self.layers = (OrcLayer * cfg.n_layers)()
         for l, L in enumerate(weights["layers"]):
             for f in _LAYER_FIELDS:
                 if f in L:
-                    want = np.uint8 if fp8 and f in PROJ_FIELDS else np.uint16
+                    want = np.uint8 if (fp8 or fp4) and f in PROJ_FIELDS else np.uint16
                     if L[f].dtype != want:
                         raise TypeError(f"layer {l} {f}: {L[f].dtype}, expected {np.dtype(want)}")
                     setattr(self.layers[l], f, L[f].ctypes.data)
-            if fp8:
+            if fp8 or fp4:
                 for f in PROJ_FIELDS:
                     if f in L:
                         sc = L[f + "_scale"]
-                        if sc.dtype != np.float32 or sc.shape != (L[f].shape[0],):
-                            raise TypeError(f"layer {l} {f}_scale: fp32 [{L[f].shape[0]}] expected")
+                        shape = (L[f].shape[0],) if fp8 else (L[f].shape[0], L[f].shape[1] * 2 // 32)
+                        if sc.dtype != (np.float32 if fp8 else np.uint8) or sc.shape != shape:
+                            raise TypeError(f"layer {l} {f}_scale: {'fp32' if fp8 else 'uint8'} {list(shape)} expected")
                         setattr(self.layers[l], "s_" + f, sc.ctypes.data)
         ow = OrcWeights()
         ow.embed = weights["embed"].ctypes.data

@@ -82,9 +82,38 @@ void orc_matvec_fp8(const uint8_t* W, const float* scale, const float* x, int ro
   }
 }
 
+/* OCP Microscaling (MX) formats specification: MXFP4 elements are E2M1, scaled per block of 32 by
+ * an E8M0 power of two -- the 4-bit weight stream with block scales of the MK-KDA pull request
+ * (github choiceoh/stkernel #230, PR summary), in the MX encoding gfx950 reads natively. */
+double orc_e2m1(uint8_t code) {
+  int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -mag : mag;
+}
+
+double orc_e8m0(uint8_t e) { return e == 0xFF ? NAN : ldexp(1.0, (int)e - 127); }
+
+void orc_matvec_fp4(const uint8_t* W, const uint8_t* S, const float* x, int rows, int cols, float* y) {
+  double lut[16];
+  for (int c = 0; c < 16; ++c) lut[c] = orc_e2m1((uint8_t)c);
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < rows; ++r) {
+    const uint8_t* wr = W + (size_t)r * (size_t)(cols / 2);
+    const uint8_t* sr = S + (size_t)r * (size_t)(cols / 32);
+    double acc = 0.0;
+    for (int k = 0; k < cols; ++k) {
+      const uint8_t byte = wr[k / 2];
+      const double w = orc_e8m0(sr[k / 32]) * lut[(k & 1) ? byte >> 4 : byte & 15];
+      acc += w * (double)x[k];
+    }
+    y[r] = (float)acc;
+  }
+}
+
 /* one projection of the model, in its weight format */
-static void proj(const orc_model* m, const void* W, const float* scale, const float* x, int rows, int cols, float* y) {
-  if (m->weight_format == ORC_W_FP8) orc_matvec_fp8((const uint8_t*)W, scale, x, rows, cols, y);
+static void proj(const orc_model* m, const void* W, const void* scale, const float* x, int rows, int cols, float* y) {
+  if (m->weight_format == ORC_W_FP8) orc_matvec_fp8((const uint8_t*)W, (const float*)scale, x, rows, cols, y);
+  else if (m->weight_format == ORC_W_FP4) orc_matvec_fp4((const uint8_t*)W, (const uint8_t*)scale, x, rows, cols, y);
   else orc_matvec((const uint16_t*)W, x, rows, cols, y);
 }
 

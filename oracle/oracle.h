@@ -33,13 +33,16 @@ typedef struct {
   const int32_t* layer_kind; /* [n_layers]: ORC_ATTN or ORC_DELTA */
   int page_size;
   int delta_decay_first;     /* 0: S <- gS + b k(v^T - k^T S) with the old S throughout; 1: decay first */
-  int weight_format;         /* ORC_W_BF16, or ORC_W_FP8: every projection matrix is fp8 codes + row scales */
+  int weight_format;         /* ORC_W_BF16, ORC_W_FP8 or ORC_W_FP4: the projection matrices' format */
 } orc_model;
 
 /* Projection weights (wq wk wv wo w_qkv_delta w_gates wo_delta w_gate w_up w_down): bf16 bit
- * patterns, or with ORC_W_FP8 one OCP E4M3 byte per weight and one fp32 scale per output row,
- * W[r][k] = scale[r] * e4m3(code[r][k]).  Norm gains, conv_w, embedding and LM head stay bf16. */
-enum { ORC_W_BF16 = 0, ORC_W_FP8 = 1 };
+ * patterns; or with ORC_W_FP8 one OCP E4M3 byte per weight and one fp32 scale per output row,
+ * W[r][k] = scale[r] * e4m3(code[r][k]); or with ORC_W_FP4 OCP MX FP4: E2M1 codes two per byte
+ * (weight 2i in the low nibble of byte i of the row, 2i + 1 in the high nibble) and one E8M0 scale
+ * byte per block of 32 consecutive weights of a row, W[r][k] = e8m0(S[r][k / 32]) * e2m1(code).
+ * Norm gains, conv_w, embedding and LM head stay bf16. */
+enum { ORC_W_BF16 = 0, ORC_W_FP8 = 1, ORC_W_FP4 = 2 };
 
 typedef struct { /* [out][in] row-major; projections bf16 or fp8 (weight_format), the rest bf16 */
   const uint16_t *attn_norm;
@@ -50,8 +53,9 @@ typedef struct { /* [out][in] row-major; projections bf16 or fp8 (weight_format)
   const void *wo_delta;
   const uint16_t *mlp_norm;
   const void *w_gate, *w_up, *w_down;
-  /* ORC_W_FP8: fp32 [out] row scales of the projection of the same name (unused otherwise) */
-  const float *s_wq, *s_wk, *s_wv, *s_wo, *s_w_qkv_delta, *s_w_gates, *s_wo_delta, *s_w_gate, *s_w_up, *s_w_down;
+  /* the projection of the same name's scales: ORC_W_FP8 fp32 [out] row scales, ORC_W_FP4 E8M0
+   * bytes [out][in / 32]; unused for bf16 */
+  const void *s_wq, *s_wk, *s_wv, *s_wo, *s_w_qkv_delta, *s_w_gates, *s_wo_delta, *s_w_gate, *s_w_up, *s_w_down;
 } orc_layer;
 
 typedef struct {
@@ -91,6 +95,14 @@ void orc_matvec(const uint16_t* W, const float* x, int rows, int cols, float* y)
 double orc_e4m3(uint8_t code);
 /* y[r] = scale[r] * sum_k e4m3(W[r][k]) x[k], W fp8 codes [rows][cols] */
 void orc_matvec_fp8(const uint8_t* W, const float* scale, const float* x, int rows, int cols, float* y);
+/* value of an OCP MX E2M1 code (low 4 bits: sign, 2 exponent bits with bias 1, 1 mantissa bit;
+ * exponent 0 is subnormal; no infinities or NaN; largest 6) */
+double orc_e2m1(uint8_t code);
+/* value of an OCP MX E8M0 scale byte: 2^(e - 127); 0xFF is NaN */
+double orc_e8m0(uint8_t e);
+/* y[r] = sum_k e8m0(S[r][k / 32]) e2m1(W[r][k]) x[k]; W packed E2M1 [rows][cols / 2], S E8M0
+ * [rows][cols / 32]; cols a multiple of 32 */
+void orc_matvec_fp4(const uint8_t* W, const uint8_t* S, const float* x, int rows, int cols, float* y);
 /* rotate-half rotary embedding of one head vector u[d] at position pos */
 void orc_rope(float* u, int d, int pos, double base);
 /* single-head attention over n keys: o = softmax(q.K^T / sqrt(d)) V; K, V bf16 rows [n][d]

@@ -137,7 +137,7 @@ class Config:
     page_size: int = 16
     shuffle_pages: bool = False
     gain_range: Optional[tuple] = None       # None = unit norm gains
-    weights: str = "bf16"                    # projection matrices: "bf16", or "fp8" codes + fp32 row scales
+    weights: str = "bf16"                    # projections: "bf16", "fp8" (+ fp32 row scales), "fp4" (+ E8M0 block scales)
 
     def kinds(self) -> List[int]:
         return list(self.layer_kinds) if self.layer_kinds is not None else [ATTN] * self.n_layers
@@ -179,6 +179,8 @@ CONFIGS: Dict[str, Config] = {
 # KV cache bf16
 CONFIGS["8b-fp8"] = CONFIGS["8b"].replace(name="8b-fp8", weights="fp8")
 CONFIGS["13b-fp8"] = CONFIGS["13b"].replace(name="13b-fp8", weights="fp8")
+# the 8B shape with MX fp4 projections (E2M1, E8M0 scales per 32 weights)
+CONFIGS["8b-fp4"] = CONFIGS["8b"].replace(name="8b-fp4", weights="fp4")
 
 
 def context_lengths(cfg: Config) -> List[int]:
@@ -223,9 +225,21 @@ def _gain(cfg: Config, n: int, name: str) -> np.ndarray:
 FP8_SCALE = WEIGHT_STD / 142.0
 
 
+# fp4 projections: uniform random E2M1 nibbles (RMS of their values about 2.93) with E8M0 block scales
+# 2^-8 .. 2^-6 drawn per block of 32 weights, so the weights have about the bf16 models' scale.
+FP4_SCALE_E = (119, 120, 121)
+
+
 def _proj(cfg: Config, L: dict, name: str, rows: int, cols: int, prefix: str) -> None:
-    """One projection matrix: bf16 N(0, WEIGHT_STD), or fp8 codes with one fp32 scale per row."""
-    if cfg.weights == "fp8":
+    """One projection matrix: bf16 N(0, WEIGHT_STD); fp8 codes with one fp32 scale per row; or fp4
+    E2M1 codes packed two per byte (low nibble first) with one E8M0 scale byte per 32 weights."""
+    if cfg.weights == "fp4":
+        if cols % 32:
+            raise ValueError(f"{name}: fp4 rows of {cols} weights are not whole blocks of 32")
+        L[name] = u32(rows * cols // 8, cfg.seed, prefix + name).view(np.uint8).reshape(rows, cols // 2)
+        e = u32(rows * cols // 32, cfg.seed, prefix + name + "_scale") % len(FP4_SCALE_E)
+        L[name + "_scale"] = (np.uint8(FP4_SCALE_E[0]) + e.astype(np.uint8)).reshape(rows, cols // 32)
+    elif cfg.weights == "fp8":
         L[name] = fp8_codes((rows, cols), cfg.seed, prefix + name)
         u = u32(rows, cfg.seed, prefix + name + "_scale").astype(np.float64) / 4294967296.0
         L[name + "_scale"] = (FP8_SCALE * (0.5 + u)).astype(np.float32)
@@ -237,7 +251,7 @@ def make_weights(cfg: Config) -> dict:
     """Host (numpy) weights in PyTorch Linear layout [out, in]: bf16 bit patterns, except that with
     cfg.weights == "fp8" every projection matrix is E4M3 codes (uint8) with fp32 row scales
     ("<name>_scale"); embedding, LM head, norm gains and conv taps stay bf16."""
-    if cfg.weights not in ("bf16", "fp8"):
+    if cfg.weights not in ("bf16", "fp8", "fp4"):
         raise ValueError(f"weight format {cfg.weights!r}")
     s, H, d = cfg.seed, cfg.hidden, cfg.head_dim
     w = {"embed": normal_bf16((cfg.vocab, H), s, "embed", WEIGHT_STD),

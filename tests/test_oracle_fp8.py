@@ -1,4 +1,5 @@
-"""Pins of the oracle's fp8 weight path (E4M3 codes with fp32 row scales).
+"""Pins of the oracle's low-bit weight paths: fp8 (E4M3 codes with fp32 row scales) and MX fp4 (E2M1
+codes with E8M0 scales per block of 32).
 
 The code table is pinned to PyTorch's own float8_e4m3fn type (a library decoding of the same OCP
 format, independent of oracle.c) and to values the format fixes; the projection to a brute-force
@@ -6,7 +7,10 @@ product of those library-decoded values; and the whole decode step to the bf16 p
 by oracle_pins and the brute-force recomputation): with power-of-two row scales every fp8 weight is
 exactly a bf16 number, and the fp8 model must give the bf16 model's logits bit for bit.  A slip in
 the code table, a scale applied by column or to the wrong projection, or a projection left on the
-bf16 path fails one of these.
+bf16 path fails one of these.  fp4: the E2M1 table against the format's eight magnitudes, E8M0
+against PyTorch's float8_e8m0fnu, the block-scaled product against a float64 product of weights
+unpacked here, one block scale moving one row by that block's share, and the decode step bit for bit
+against the bf16 model holding the same (exactly representable) weights.
 """
 import numpy as np
 import pytest
@@ -141,3 +145,83 @@ def test_fp8_scales_are_per_row_of_each_projection():
         assert not np.array_equal(moved, base), f
         again = oracle.DecodeOracle(cfg, w, cache).step(toks, ctx, [c + 1 for c in ctx])
         assert np.array_equal(again, base)
+
+
+# ------------------------------------------------------------------ MX fp4 (E2M1 + E8M0 block scales)
+def test_e2m1_values_the_format_fixes():
+    # OCP Microscaling formats, E2M1: the eight magnitudes 0, 0.5 (the one subnormal), 1, 1.5, 2, 3, 4, 6
+    # and their negatives (the sign bit is bit 3); no infinities, no NaN
+    want = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    got = [oracle.e2m1(c) for c in range(16)]
+    assert got[:8] == want and got[8:] == [-v for v in want]
+    assert np.signbit(oracle.e2m1(8)) and not np.signbit(oracle.e2m1(0))
+    assert oracle.e2m1(0x17) == oracle.e2m1(0x7)  # only the low 4 bits count
+
+
+def test_e8m0_matches_pytorch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = np.array([oracle.e8m0(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.isnan(got[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert oracle.e8m0(127) == 1.0 and oracle.e8m0(0) == 2.0 ** -127
+
+
+def fp4_values(W_packed, S) -> np.ndarray:
+    """Weights of an fp4 matrix in float64, unpacked here by nibble (low first) with the format's value
+    table and PyTorch's E8M0 decoding."""
+    table = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float64)
+    W = np.asarray(W_packed, np.uint8)
+    codes = np.stack([W & 15, W >> 4], axis=-1).reshape(W.shape[0], -1)
+    v = table[codes & 7] * np.where(codes & 8, -1.0, 1.0)
+    sc = torch.from_numpy(np.ascontiguousarray(S)).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    return v * np.repeat(sc, 32, axis=1)
+
+
+def test_matvec_fp4_is_the_block_scaled_product():
+    rng = np.random.default_rng(9)
+    cfg = synth.CONFIGS["tiny"].replace(weights="fp4")
+    L = {}
+    synth._proj(cfg, L, "w", 7, 96, "pin.")
+    x = rng.standard_normal(96).astype(np.float32)
+    want = fp4_values(L["w"], L["w_scale"]) @ x.astype(np.float64)
+    assert np.allclose(oracle.matvec_fp4(L["w"], L["w_scale"], x), want, rtol=1e-6, atol=0)
+    # one block's scale doubled moves only that row, by that block's share
+    S2 = L["w_scale"].copy()
+    S2[3, 1] += 1
+    d = oracle.matvec_fp4(L["w"], S2, x).astype(np.float64) - oracle.matvec_fp4(L["w"], L["w_scale"], x)
+    blk = fp4_values(L["w"], L["w_scale"])[3, 32:64] @ x[32:64].astype(np.float64)
+    assert np.allclose(d[3], blk, rtol=1e-5) and np.count_nonzero(d) == 1
+
+
+def _fp4_as_bf16(w: dict) -> dict:
+    """The fp4 model with every projection widened to bf16 (exact: an E2M1 value times a power of two)."""
+    out = dict(w, format="bf16")
+    out["layers"] = []
+    for L in w["layers"]:
+        L = dict(L)
+        for f in oracle.PROJ_FIELDS:
+            if f in L:
+                v = fp4_values(L[f], L.pop(f + "_scale"))
+                b = torch.from_numpy(v).to(torch.bfloat16)
+                assert np.array_equal(b.to(torch.float64).numpy(), v)
+                L[f] = b.view(torch.int16).numpy().view(np.uint16)
+        out["layers"].append(L)
+    return out
+
+
+@pytest.mark.parametrize("name", ["tiny-gain", "tiny-qknorm"])
+def test_fp4_step_equals_bf16_step(name):
+    cfg = synth.SMALL[name].replace(weights="fp4")
+    w4 = synth.make_weights(cfg)
+    wb = _fp4_as_bf16(w4)
+    ctx = synth.context_lengths(cfg)
+    cache = synth.make_cache(cfg, ctx, 2)
+    o4, ob = oracle.DecodeOracle(cfg, w4, cache), oracle.DecodeOracle(cfg.replace(weights="bf16"), wb, cache)
+    toks = [int(t) for t in synth.first_tokens(cfg)]
+    for s in range(2):
+        pos = [c + s for c in ctx]
+        a = o4.step(toks, pos, [p + 1 for p in pos])
+        b = ob.step(toks, pos, [p + 1 for p in pos])
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"step {s}"
+        toks = [oracle.argmax(r) for r in a]
