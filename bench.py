@@ -39,6 +39,8 @@ WORKLOADS = {
     "tiny": "tiny decoder (2 layers, hidden 256, GQA 4/2, head_dim 64, FFN 768, vocab 1024), batch 1, ctx 128",
     "8b-fp8": "8B-shape decoder with fp8 E4M3 projections (fp32 row scales; bf16 embedding, LM head and KV "
               "cache), batch 1, ctx 4096",
+    "8b-fp4": "8B-shape decoder with MX fp4 projections (E2M1 codes, E8M0 scales per 32 weights; bf16 "
+              "embedding, LM head and KV cache), batch 1, ctx 4096",
 }
 
 
@@ -48,13 +50,16 @@ def log(msg: str) -> None:
 
 def bytes_per_step(cfg, ctx_lens) -> float:
     """Algorithmic HBM bytes of one decode step: every projection weight once (2 bytes a bf16 weight,
-    or 1 an fp8 code plus 4 a row scale), one embedding row per sequence, the LM head once, K/V of
+    or 1 an fp8 code plus 4 a row scale, or half a byte an fp4 code plus 1 a block scale of 32),
+    one embedding row per sequence, the LM head once, K/V of
     every cached position per attention layer (plus the append), the delta-rule and conv states read
     and written, and the logits written."""
     H, F, V, B = cfg.hidden, cfg.ffn, cfg.vocab, cfg.batch
-    fp8 = cfg.weights == "fp8"
+    fp8, fp4 = cfg.weights == "fp8", cfg.weights == "fp4"
 
     def proj(rows, cols):
+        if fp4:
+            return rows * (cols / 2.0 + cols / 32.0)
         return rows * (cols + 4.0) if fp8 else rows * cols * 2.0
 
     w = 0.0
@@ -413,9 +418,9 @@ def run_window(name: str, window: int, launches: int, warmup: int) -> dict:
             "note": "tokens verified per second: every window token's logits per launch"}
 
 
-PER_CONFIG = ("0.6b", "hybrid", "13b", "8b-fp8")  # measured beside the headline 8B workload
+PER_CONFIG = ("0.6b", "hybrid", "13b", "8b-fp8", "8b-fp4")  # measured beside the headline 8B workload
 WINDOWS = {"8b": 8, "0.6b": 8}            # verify windows timed beside them
-RUN_STEPS = {"8b": 128, "0.6b": 64, "hybrid": 64, "13b": 64, "tiny": 8, "8b-fp8": 128}  # decode steps per run
+RUN_STEPS = {"8b": 128, "0.6b": 64, "hybrid": 64, "13b": 64, "tiny": 8, "8b-fp8": 128, "8b-fp4": 128}  # decode steps per run
 
 
 def main() -> int:
@@ -460,7 +465,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if head["weights"] == "fp8" else "bf16",
+        "dtype": head["weights"] if head["weights"] in ("fp8", "fp4") else "bf16",
         "data": "synthetic (seeded random-init weights and KV cache of the named shape)",
         "config": {"workload": head["workload"], "batch": B, "ctx": head["ctx"]},
     }

@@ -60,8 +60,18 @@ typedef enum { MK_LAYER_ATTN = 0, MK_LAYER_DELTA = 1 } mk_layer_kind;
  *                       norm gains, conv taps and the KV cache stay bf16.  Codes must not be
  *                       NaN.  Every projection input length (hidden, ffn, n_q_heads * head_dim,
  *                       n_delta_heads * delta_dv) must be a multiple of 16, of 512 when max_batch
- *                       is 5 to 8; otherwise mk_create / mk_plan return MK_ERR_UNSUPPORTED. */
-typedef enum { MK_WEIGHTS_BF16 = 0, MK_WEIGHTS_FP8_E4M3 = 1 } mk_weight_format;
+ *                       is 5 to 8; otherwise mk_create / mk_plan return MK_ERR_UNSUPPORTED.
+ *   MK_WEIGHTS_FP4_MX   every projection matrix is OCP MX fp4: E2M1 codes (sign, 2 exponent bits
+ *                       with bias 1, 1 mantissa bit, exponent 0 subnormal; values 0 .. 6, no
+ *                       infinities or NaN) packed two per byte, weight 2i of a row in the low
+ *                       nibble of byte i and 2i + 1 in the high nibble, uint8 [out][in / 2]; with
+ *                       one E8M0 scale byte (2^(e - 127), 0xFF NaN: not allowed) per block of 32
+ *                       consecutive weights of a row, uint8 [out][in / 32]:
+ *                       W[r][k] = 2^(S[r][k / 32] - 127) * e2m1(code(r, k)).  The same tensors
+ *                       stay bf16 as for fp8.  One sequence per step: max_batch must be 1, and
+ *                       every projection input length a multiple of 32 (at most 16384);
+ *                       otherwise MK_ERR_UNSUPPORTED. */
+typedef enum { MK_WEIGHTS_BF16 = 0, MK_WEIGHTS_FP8_E4M3 = 1, MK_WEIGHTS_FP4_MX = 2 } mk_weight_format;
 
 /* Model description (host memory; copied by mk_create).
  *   hidden % 8 == 0, head_dim in {64, 128}, n_q_heads % n_kv_heads == 0,
@@ -92,13 +102,14 @@ typedef struct {
  * w_gates [2*heads][H], conv_w [C][conv_width], wo_delta [H][heads*dv].
  * Every layer sets mlp_norm [H], w_gate [F][H], w_up [F][H], w_down [H][F].
  * With MK_WEIGHTS_FP8_E4M3 each projection the layer sets also sets its <name>_scale: fp32 [out]
- * row scales (device, 16-byte aligned).  Unused fields may be NULL. */
+ * row scales (device, 16-byte aligned); with MK_WEIGHTS_FP4_MX its E8M0 block scales, uint8
+ * [out][in / 32] (device, 16-byte aligned).  Unused fields may be NULL. */
 typedef struct {
   const void *attn_norm, *wq, *wk, *wv, *wo, *q_norm, *k_norm;
   const void *w_qkv_delta, *w_gates, *conv_w, *wo_delta;
   const void *mlp_norm, *w_gate, *w_up, *w_down;
-  const float *wq_scale, *wk_scale, *wv_scale, *wo_scale, *w_qkv_delta_scale, *w_gates_scale, *wo_delta_scale;
-  const float *w_gate_scale, *w_up_scale, *w_down_scale;
+  const void *wq_scale, *wk_scale, *wv_scale, *wo_scale, *w_qkv_delta_scale, *w_gates_scale, *wo_delta_scale;
+  const void *w_gate_scale, *w_up_scale, *w_down_scale;
 } mk_layer_weights;
 
 typedef struct {

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmk.so")
 
 MK_ABI_VERSION = 2
-MK_WEIGHTS_BF16, MK_WEIGHTS_FP8_E4M3 = 0, 1
+MK_WEIGHTS_BF16, MK_WEIGHTS_FP8_E4M3, MK_WEIGHTS_FP4_MX = 0, 1, 2
 MK_OK, MK_ERR_INVALID_ARG, MK_ERR_UNSUPPORTED, MK_ERR_HIP, MK_ERR_DEVICE_INPUT, MK_ERR_TIMEOUT, MK_ERR_STATE = \
     0, -1, -2, -3, -4, -5, -6
 MK_LAYER_ATTN, MK_LAYER_DELTA = 0, 1
@@ -241,7 +241,8 @@ class DecodeContext:
     """Owns the device tensors of one model and its mk_ctx.
 
     `weights` / `cache` are dicts of host numpy arrays (bf16 as uint16; with shape["weights"] ==
-    "fp8" the projections as uint8 E4M3 codes with float32 "<name>_scale" row scales) in the layout
+    "fp8" the projections as uint8 E4M3 codes with float32 "<name>_scale" row scales; "fp4" as packed
+    uint8 E2M1 codes with uint8 E8M0 "<name>_scale" block scales) in the layout
     include/mk.h documents; they are copied to `device` once.  Only memory and the stream come from
     PyTorch.
     """
@@ -259,12 +260,13 @@ class DecodeContext:
         self.tensors: Dict[str, "torch.Tensor"] = {}
         keep: List = self.tensors.setdefault("_all", [])
         self.arena = None
-        fp8 = shape.get("weights", "bf16") == "fp8"
+        wfmt = shape.get("weights", "bf16")
+        fp8, fp4 = wfmt == "fp8", wfmt == "fp4"
         if arena:  # one allocation for every weight tensor
             arrays = [weights["embed"], weights["final_norm"]] + ([] if shape["tied"] else [weights["lm_head"]])
             for L in weights["layers"]:
                 arrays += [L[f] for f in LAYER_FIELDS if f in L]
-                if fp8:
+                if fp8 or fp4:
                     arrays += [L[f + "_scale"] for f in PROJ_FIELDS if f in L]
             A = self.ARENA_ALIGN
             total = sum((a.nbytes + A - 1) // A * A for a in arrays) + A
@@ -290,7 +292,7 @@ class DecodeContext:
                               s["head_dim"], s["qk_norm"], s["tied"], s["rms_eps"], s["rope_base"], s["layer_kinds"],
                               s["max_batch"], s["max_ctx"], s.get("n_delta_heads", 0), s.get("delta_dk", 0),
                               s.get("delta_dv", 0), s.get("conv_width", 0), s.get("page_size", 16),
-                              MK_WEIGHTS_FP8_E4M3 if fp8 else MK_WEIGHTS_BF16)
+                              MK_WEIGHTS_FP8_E4M3 if fp8 else (MK_WEIGHTS_FP4_MX if fp4 else MK_WEIGHTS_BF16))
         self.embed = dev(weights["embed"], i16)
         final_norm = dev(weights["final_norm"], i16)
         lm = self.embed if s["tied"] else dev(weights["lm_head"], i16)
@@ -298,9 +300,10 @@ class DecodeContext:
         for l, L in enumerate(weights["layers"]):
             for f in LAYER_FIELDS:
                 if f in L:
-                    if fp8 and f in PROJ_FIELDS:
-                        if L[f].dtype != np.uint8 or L[f + "_scale"].dtype != np.float32:
-                            raise TypeError(f"layer {l} {f}: fp8 weights are uint8 codes with float32 row scales")
+                    if (fp8 or fp4) and f in PROJ_FIELDS:
+                        if L[f].dtype != np.uint8 or L[f + "_scale"].dtype != (np.float32 if fp8 else np.uint8):
+                            raise TypeError(f"layer {l} {f}: {wfmt} weights are uint8 codes with "
+                                            f"{'float32 row' if fp8 else 'uint8 E8M0 block'} scales")
                         setattr(self.layers[l], f, dev(L[f], "raw").data_ptr())
                         setattr(self.layers[l], f + "_scale", dev(L[f + "_scale"], "raw").data_ptr())
                     else:

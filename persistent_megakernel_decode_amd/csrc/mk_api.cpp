@@ -40,6 +40,9 @@ extern "C" __global__ void mk_megakernel_steps_b1_f8(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_steps_b2_f8(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_steps_b4_f8(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_steps_b8_f8(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_b1_f4(mk::KArgs A);  // MX fp4 projections (one sequence)
+extern "C" __global__ void mk_megakernel_b1_f4_trace(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_steps_b1_f4(mk::KArgs A);
 
 namespace {
 
@@ -62,8 +65,9 @@ mk_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-const void* kernel_for(int B, bool traced, bool f8) {
-  if (f8) {
+const void* kernel_for(int B, bool traced, int32_t wf) {
+  if (wf == MK_WEIGHTS_FP4_MX) return traced ? (const void*)mk_megakernel_b1_f4_trace : (const void*)mk_megakernel_b1_f4;
+  if (wf == MK_WEIGHTS_FP8_E4M3) {
     switch (B) {
       case 1: return traced ? (const void*)mk_megakernel_b1_f8_trace : (const void*)mk_megakernel_b1_f8;
       case 2: return traced ? (const void*)mk_megakernel_b2_f8_trace : (const void*)mk_megakernel_b2_f8;
@@ -79,8 +83,9 @@ const void* kernel_for(int B, bool traced, bool f8) {
   }
 }
 
-const void* steps_kernel_for(int B, bool f8) {
-  if (f8) {
+const void* steps_kernel_for(int B, int32_t wf) {
+  if (wf == MK_WEIGHTS_FP4_MX) return (const void*)mk_megakernel_steps_b1_f4;
+  if (wf == MK_WEIGHTS_FP8_E4M3) {
     switch (B) {
       case 1: return (const void*)mk_megakernel_steps_b1_f8;
       case 2: return (const void*)mk_megakernel_steps_b2_f8;
@@ -285,13 +290,13 @@ static mk_status create_impl(const mk_model_desc* desc, const mk_weights* w, con
   if (pe.empty()) pe = need(w->final_norm, "final_norm");
   if (pe.empty() && !d.tied_embeddings) pe = need(w->lm_head, "lm_head");
   if (pe.empty() && !w->layers) pe = "layers is null";
-  const bool f8 = d.weight_format == MK_WEIGHTS_FP8_E4M3;
+  const bool scaled = d.weight_format == MK_WEIGHTS_FP8_E4M3 || d.weight_format == MK_WEIGHTS_FP4_MX;
   for (int l = 0; pe.empty() && l < d.n_layers; ++l) {
     const mk_layer_weights& L = w->layers[l];
-    // a projection and, for fp8 weights, its row scales
-    auto proj = [&](const void* p, const float* sc, const char* name, const char* sname) {
+    // a projection and, for fp8 / fp4 weights, its scales
+    auto proj = [&](const void* p, const void* sc, const char* name, const char* sname) {
       if (pe.empty()) pe = need(p, name);
-      if (pe.empty() && f8) pe = need(sc, sname);
+      if (pe.empty() && scaled) pe = need(sc, sname);
     };
     pe = need(L.attn_norm, "attn_norm");
     if (pe.empty()) pe = need(L.mlp_norm, "mlp_norm");
@@ -347,9 +352,8 @@ static mk_status create_impl(const mk_model_desc* desc, const mk_weights* w, con
   // MK_TRACE=1: the traced kernels (per-op timing stamps; diagnostic)
   const char* trace_env = getenv("MK_TRACE");
   const bool traced = trace_env && atoi(trace_env) != 0;
-  const bool f8_kernels = d.weight_format == MK_WEIGHTS_FP8_E4M3;
-  ctx->kernel = kernel_for(P.kernel_batch, traced, f8_kernels);
-  ctx->kernel_steps = steps_kernel_for(P.kernel_batch, f8_kernels);
+  ctx->kernel = kernel_for(P.kernel_batch, traced, d.weight_format);
+  ctx->kernel_steps = steps_kernel_for(P.kernel_batch, d.weight_format);
 
   // one resident workgroup per compute unit is required by the persistent design
   int per_cu = 0, per_cu_steps = 0;

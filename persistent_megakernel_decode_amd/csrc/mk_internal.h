@@ -60,6 +60,13 @@ constexpr uint32_t OPF_NO_SIGNAL = 2u;
 // pieces and row groups are counted in those 16-bit units; the compute waves read 16 codes per
 // 16-byte chunk against 16 inputs.
 constexpr uint32_t OPF_FP8 = 4u;
+// A GEMV op whose weights are MX fp4 (E2M1 codes packed two per byte, low nibble first, with one
+// E8M0 scale byte per 32 weights: Ws / Ws2 point at the runs' scale rows of K / 32 bytes): the
+// loader streams a row of K codes as a bf16 row of K / 4 weights, and every 16-byte chunk the
+// compute waves read is one 32-weight block.
+constexpr uint32_t OPF_FP4 = 8u;
+// The projection weight format a kernel is compiled for (OPF_FP8 / OPF_FP4 ops need it)
+constexpr int WF_BF16 = 0, WF_FP8 = 1, WF_FP4 = 2;
 
 // One queue entry (128 bytes).  Pointers are device addresses.
 //
@@ -106,16 +113,18 @@ struct alignas(16) Op {
   uint32_t b1;         // GEMV: stream rows taken from W before switching to W2
   uint32_t flags;      // OPF_* bits
   uint64_t W, W2;      // GEMV weight runs, bf16 rows of K (OPF_FP8: fp8 rows of K)
-  uint64_t Ws;         // OPF_FP8: fp32 row scales of the W run (at the op's first row)
+  uint64_t Ws;         // OPF_FP8: fp32 row scales of the W run (at the op's first row); OPF_FP4: E8M0 scale rows
   uint64_t in;         // fp32 [batch][ld_in]
   uint64_t gamma;      // bf16 [K] norm gain (norm == 1)
   uint64_t out;        // fp32 [batch][ld_out] (EPI_LOGITS writes the launch's logits instead)
   uint64_t res;        // fp32 [batch][ld_out] residual (EPI_RESID)
-  uint64_t Ws2;        // OPF_FP8: fp32 row scales of the W2 run
+  uint64_t Ws2;        // OPF_FP8: fp32 row scales of the W2 run; OPF_FP4: its E8M0 scale rows
 };
 static_assert(sizeof(Op) == 128, "Op must stay 128 bytes");
-// stream elements per row of a GEMV op: 16-bit weights, or pairs of fp8 codes
-constexpr uint32_t gemv_kv(uint32_t K, uint32_t flags) { return (flags & OPF_FP8) ? K / 2 : K; }
+// stream elements per row of a GEMV op: 16-bit weights, pairs of fp8 codes, or quads of fp4 codes
+constexpr uint32_t gemv_kv(uint32_t K, uint32_t flags) {
+  return (flags & OPF_FP4) ? K / 4 : ((flags & OPF_FP8) ? K / 2 : K);
+}
 
 // Per-layer device pointers used by ATTN / DELTA ops.
 struct alignas(16) LayerDesc {

@@ -1226,6 +1226,31 @@ struct GemvAcc<1, 8> {
       l = __builtin_fmaf(c.y, x[4 * i + 3], l);
     }
   }
+  // MX fp4 weights: 32 E2M1 codes, one block (byte j of word i: input 8 i + 2 j in the low nibble,
+  // 8 i + 2 j + 1 in the high one) against 32 fp32 inputs.  Each code is widened exactly to fp32 by
+  // the hardware conversion (two per instruction, unscaled); the block's two partial sums are then
+  // multiplied by the block's E8M0 scale, a power of two, so scaling the sum equals scaling each code.
+  __device__ __forceinline__ void add4(const u32x4 wv, const float* x, float sc) {
+    const u32 wd[4] = {wv.x, wv.y, wv.z, wv.w};
+    float p = 0.0f, q = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[i], 1.0f, 0);
+      const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[i], 1.0f, 1);
+      const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[i], 1.0f, 2);
+      const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[i], 1.0f, 3);
+      p = __builtin_fmaf(a.x, x[8 * i], p);
+      q = __builtin_fmaf(a.y, x[8 * i + 1], q);
+      p = __builtin_fmaf(b.x, x[8 * i + 2], p);
+      q = __builtin_fmaf(b.y, x[8 * i + 3], q);
+      p = __builtin_fmaf(c.x, x[8 * i + 4], p);
+      q = __builtin_fmaf(c.y, x[8 * i + 5], q);
+      p = __builtin_fmaf(d.x, x[8 * i + 6], p);
+      q = __builtin_fmaf(d.y, x[8 * i + 7], q);
+    }
+    h = __builtin_fmaf(p, sc, h);
+    l = __builtin_fmaf(q, sc, l);
+  }
   __device__ __forceinline__ void merge(const GemvAcc& o) {
     h += o.h;
     l += o.l;
@@ -1243,6 +1268,11 @@ struct GemvAcc<1, 8> {
   }
 };
 
+// An MX E8M0 scale byte as fp32: 2^(e - 127); 0 is 2^-127 (an fp32 subnormal), 0xFF NaN
+__device__ __forceinline__ float e8m0f(u32 e) {
+  return e == 0xFFu ? __builtin_nanf("") : __builtin_bit_cast(float, e ? e << 23 : 0x00400000u);
+}
+
 // One GEMV op with NF input fragments per wave (1, 2, or up to 8).  Row groups are taken GB at a
 // time (GB NF = 4 slots per wait for NF <= 2).  With PG < 8 pieces per group (NF = 1) a slot holds
 // 8 / PG groups and wave w works on group (slot 8 / PG + w / PG), piece w % PG.
@@ -1253,17 +1283,24 @@ struct GemvAcc<1, 8> {
 // to four widen the chunk to two bf16x8 operands (codes 0-7 and 8-15), each taken with the matching
 // half of the lane's inputs (hi + lo) on the matrix cores: A and B lanes of one (part, k-group)
 // then index the same 16 inputs, so the matched-part extraction is unchanged.
-template <int B, int P, int NF, bool AM, bool F8 = false>  // AM: track the LM head's greedy partials (multi-step kernels)
+// F4: MX fp4 weights (one sequence).  The slot layout is the bf16 one over K / 4 16-bit stream
+// elements, so a lane's 16-byte chunk at stream element k holds the E2M1 codes of inputs 4k ..
+// 4k + 31: exactly one 32-weight block of one row, whose E8M0 scale byte the lane reads from the
+// op's scale rows (one byte per block; a batch of groups' scales is fetched while the batch before
+// it computes).  Each fragment is 32 fp32 inputs; the block sum is scaled inside the loop.
+template <int B, int P, int NF, bool AM, bool F8 = false, bool F4 = false>  // AM: track the LM head's greedy partials (multi-step kernels)
 __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
   static_assert(!F8 || NF <= 4, "fp8 weights: at most 4 input fragments per wave");
+  static_assert(!F4 || (B == 1 && NF <= 2 && !F8), "fp4 weights: one sequence, at most 2 input fragments per wave");
   constexpr u32 R = 16 / P, KP = 32 * P;
   constexpr u32 GB = NF == 1 ? 4 : (NF == 2 ? 2 : 1);
-  constexpr u32 XN = F8 ? 16 : 8;  // inputs per fragment
+  constexpr u32 EM = F4 ? 4u : (F8 ? 2u : 1u);  // inputs per 16-bit stream element
+  constexpr u32 XN = 8 * EM;                    // inputs per fragment
   const u32 lane = lane_id();
   // the Op's fields as independent scalars (see op_mmv)
   const u32 epi = opq((u32)o.epi), norm = opq((u32)o.norm), flags = opq(o.flags), nrows = opq(o.nrows);
   const u32 pg = opq(o.ppr), K = opq(o.K), row0 = opq(o.row0);
-  const u32 kv = F8 ? K / 2 : K;  // stream elements per row
+  const u32 kv = K / EM;  // stream elements per row
   const u32 nslots = opq(o.nslots) - (norm ? gain_slots(K) : 0u);  // weight slots (after the gain's)
   const u32 ld_in = opq(o.ld_in), ld_out = opq(o.ld_out);
   const uint64_t in = opq(o.in), outp = opq(o.out), resp = opq(o.res);
@@ -1286,7 +1323,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   // round trip) and the epilogue scales each output by (mean x^2 + eps)^-1/2, so no barrier stands
   // between the loads and the stream.
   float xf[NF][XN];
-  u32x4 gv[NF], gv2[NF];  // gv2: the second 8 gains of an fp8 fragment
+  u32x4 gv[NF][XN / 8];  // the fragment's gains, 8 per vector
   const float* xin = (const float*)in + (size_t)(B == 1 ? 0u : bl) * ld_in;
   u32 fv = 0;  // fragments this lane loads
 #pragma unroll
@@ -1295,7 +1332,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
     const u32 k0 = q * KP + koff;
     const bool v = (u32)f < nf && (B == 1 || bl < (u32)B) && k0 < kv;
     fv |= v ? 1u << f : 0u;
-    if (v) ldn_sc1<XN>(xin + (F8 ? 2 * k0 : k0), xf[f]);
+    if (v) ldn_sc1<XN>(xin + EM * k0, xf[f]);
     else {
 #pragma unroll
       for (int e = 0; e < (int)XN; ++e) xf[f][e] = 0.0f;
@@ -1310,20 +1347,36 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const u32 q = pg >= 8 ? 8 * f + w : w % pg;
-      const u32 byte = 2 * (F8 ? 2 : 1) * (q * KP + koff);  // (fp8: 32 bytes of gains, one slot)
+      const u32 byte = 2 * EM * (q * KP + koff);  // (fp8 / fp4: 32 / 64 bytes of gains, in one slot)
       const u32 at = ((seq + byte / SLOT) % NSLOT) * (SLOT / 16) + (byte % SLOT) / 16;
       const u32x4 one = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-      gv[f] = ((fv >> f) & 1u) ? g_ring[at] : one;
-      if constexpr (F8) gv2[f] = ((fv >> f) & 1u) ? g_ring[at + 1] : one;
+#pragma unroll
+      for (u32 hf = 0; hf < XN / 8; ++hf) gv[f][hf] = ((fv >> f) & 1u) ? g_ring[at + hf] : one;
     }
     release_upto(w, seq + gs);
     seq += gs;
   }
+  // fp4: the E8M0 block scales of the op's runs, K / 32 bytes per stream row (stream rows from b1
+  // on are W2's, as in the weight stream).  This lane's byte for group g, piece q; the rows and
+  // blocks of padding read an in-bounds byte of the op (their inputs are zero).
+  const u32 nbk = K / 32;
+  const uint8_t* sq1 = F4 ? (const uint8_t*)opq(o.Ws) : nullptr;
+  const uint8_t* sq2 = F4 ? (const uint8_t*)opq(o.Ws2) : nullptr;
+  const u32 sb1 = F4 ? opq(o.b1) : 0u;
+  auto s4ld = [&](u32 g, u32 q) -> u32 {
+    u32 rho = g * R + (lane & 15) / P;
+    rho = rho < nrt ? rho : nrt - 1;
+    u32 blk = (q * KP + koff) / 8;
+    blk = blk < nbk ? blk : nbk - 1;
+    const uint8_t* p = rho < sb1 ? sq1 + (size_t)rho * nbk : sq2 + (size_t)(rho - sb1) * nbk;
+    return (u32)p[blk];
+  };
   // Single-sequence projections stage their first SG row groups in registers and free those ring
   // slots before waiting for their inputs: while this op waits (for the merged attention heads, the
   // last SwiGLU rows) the loader keeps streaming the following bytes into the freed ring instead of
   // idling this compute unit's share of HBM.
-  constexpr u32 SG = B != 1 ? 0u : (NF == 1 ? 16u : (NF == 2 ? 8u : 0u));  // staged row groups
+  // (fp4 fragments hold four times the inputs: half the staged groups keep the registers in bounds)
+  constexpr u32 SG = B != 1 ? 0u : (F4 ? (NF == 1 ? 8u : 4u) : (NF == 1 ? 16u : (NF == 2 ? 8u : 0u)));  // staged row groups
   constexpr u32 SS = SG * NF > 0 ? SG * NF : 1u;                          // their slot registers
   u32x4 stg[SS];
   const bool staged = SG > 0 && pg >= 8 && nrg >= SG;
@@ -1334,6 +1387,13 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
     for (u32 i = 0; i < SS; ++i)
       if (i % NF < nf) stg[i] = g_ring[((seq + (i / NF) * nf + i % NF) % NSLOT) * (SLOT / 16) + achunk];
     release_upto(w, seq + nst);
+  }
+  u32 sst[F4 ? SS : 1];  // fp4: the staged groups' scale bytes, fetched while the inputs are awaited
+  if constexpr (F4) {
+    if (staged) {
+#pragma unroll
+      for (u32 i = 0; i < SS; ++i) sst[i] = i % NF < nf ? s4ld(i / NF, 8 * (i % NF) + w) : 0x7Fu;
+    }
   }
   // residual rows of this thread (epilogue row r = thread index), fetched now, off the critical path
   const u32 tid = w * 64 + lane, par = ctag() & 1u;
@@ -1368,7 +1428,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const u32 q = pg >= 8 ? 8 * f + w : w % pg;
-        if ((todo >> f) & 1u) ldn_sc1<XN>(xin + (F8 ? 2 : 1) * (q * KP + koff), xf[f]);
+        if ((todo >> f) & 1u) ldn_sc1<XN>(xin + EM * (q * KP + koff), xf[f]);
       }
       todo = 0;
 #pragma unroll
@@ -1395,7 +1455,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
     for (int f = 0; f < NF; ++f) {
 #pragma unroll
       for (int hf = 0; hf < (int)XN / 8; ++hf) {
-        const u32x4 g4 = hf ? gv2[f] : gv[f];
+        const u32x4 g4 = gv[f][hf];
         const float g[8] = {bflo(g4.x), bfhi(g4.x), bflo(g4.y), bfhi(g4.y), bflo(g4.z), bfhi(g4.z), bflo(g4.w), bfhi(g4.w)};
 #pragma unroll
         for (int e = 0; e < 8; ++e) xf[f][8 * hf + e] *= g[e];
@@ -1405,7 +1465,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   // bf16 hi + lo operands of the inputs: per fragment, or per half fragment for fp8 codes at B > 1
   constexpr int XH = F8 ? (B == 1 ? 1 : 2) : 1;
   bf16x8 xh[NF][XH], xl[NF][XH];
-  if constexpr (!F8 || B > 1) {
+  if constexpr (!(F8 || F4) || B > 1) {
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
@@ -1416,10 +1476,11 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
         xl[f][hf] = __builtin_bit_cast(bf16x8, l);
       }
   }
-  // one weight chunk of fragment f into an accumulator
-#define MK_GEMV_ADD(acc, wv, f)                                                              \
+  // one weight chunk of fragment f into an accumulator (SC: the chunk's fp4 block scale)
+#define MK_GEMV_ADD(acc, wv, f, SC)                                                          \
   do {                                                                                       \
-    if constexpr (F8 && B == 1) (acc).add8((wv), xf[f]);                                     \
+    if constexpr (F4) (acc).add4((wv), xf[f], (SC));                                         \
+    else if constexpr (F8 && B == 1) (acc).add8((wv), xf[f]);                                \
     else if constexpr (F8) (acc).add8m((wv), xh[f][0], xl[f][0], xh[f][XH - 1], xl[f][XH - 1]); \
     else (acc).add((wv), xh[f][0], xl[f][0]);                                                \
   } while (0)
@@ -1437,7 +1498,8 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
           for (u32 f = 0; f < NF; ++f)
 #pragma unroll
-            for (u32 gb = 0; gb < GB; ++gb) MK_GEMV_ADD(acc[gb], stg[(bt * GB + gb) * NF + f], f);
+            for (u32 gb = 0; gb < GB; ++gb)
+              MK_GEMV_ADD(acc[gb], stg[(bt * GB + gb) * NF + f], f, e8m0f(sst[F4 ? (bt * GB + gb) * NF + f : 0]));
 #pragma unroll
           for (u32 gb = 0; gb < GB; ++gb) acc[gb].finish(lane, bt * GB + gb, w, RW, nrt);
         }
@@ -1450,8 +1512,8 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
           for (int f = 0; f < NF; ++f) {
             if ((u32)f < nf) {
-              if (f & 1) MK_GEMV_ADD(a1, stg[g * NF + f], f);
-              else MK_GEMV_ADD(a0, stg[g * NF + f], f);
+              if (f & 1) MK_GEMV_ADD(a1, stg[g * NF + f], f, 1.0f);
+              else MK_GEMV_ADD(a0, stg[g * NF + f], f, 1.0f);
             }
           }
           a0.merge(a1);
@@ -1465,7 +1527,20 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
       // whole batches of GB groups (NF = nf here): straight-line code, so the groups' matrix-core
       // chains and extractions interleave
       constexpr u32 NS = GB * NF;
+      u32 snx[F4 ? NS : 1];  // fp4: the next batch's scale bytes
+      if constexpr (F4) {
+#pragma unroll
+        for (u32 i = 0; i < NS; ++i) snx[i] = s4ld(g0 + i / NF, 8 * (i % NF) + w);
+      }
       for (; g0 + GB <= nrg; g0 += GB) {
+        u32 scu[F4 ? NS : 1];
+        if constexpr (F4) {
+#pragma unroll
+          for (u32 i = 0; i < NS; ++i) {
+            scu[i] = snx[i];
+            snx[i] = s4ld(g0 + GB + i / NF, 8 * (i % NF) + w);
+          }
+        }
         if (seq + NS > avail && !wait_avail(A, seq + NS, avail)) return false;
         u32x4 wv[NS];
 #pragma unroll
@@ -1477,7 +1552,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
         for (u32 f = 0; f < NF; ++f)
 #pragma unroll
-          for (u32 gb = 0; gb < GB; ++gb) MK_GEMV_ADD(acc[gb], wv[gb * NF + f], f);
+          for (u32 gb = 0; gb < GB; ++gb) MK_GEMV_ADD(acc[gb], wv[gb * NF + f], f, e8m0f(scu[F4 ? gb * NF + f : 0]));
 #pragma unroll
         for (u32 gb = 0; gb < GB; ++gb) acc[gb].finish(lane, g0 + gb, w, RW, nrt);
         seq += NS;
@@ -1498,8 +1573,9 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         if ((u32)f < nf) {
-          if (f & 1) MK_GEMV_ADD(a1, wv[f], f);
-          else MK_GEMV_ADD(a0, wv[f], f);
+          const float sc = F4 ? e8m0f(s4ld(g0, 8 * f + w)) : 1.0f;
+          if (f & 1) MK_GEMV_ADD(a1, wv[f], f, sc);
+          else MK_GEMV_ADD(a0, wv[f], f, sc);
         }
       }
       a0.merge(a1);
@@ -1512,7 +1588,21 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
     const u32 gsub = w >> lgpg;          // this wave's group within a slot
     const u32 full = nrg >> (3 - lgpg);  // slots whose groups all exist
     u32 s0 = 0;
+    const u32 qp = w & (pg - 1);  // this wave's piece of its group
+    u32 snx[F4 ? 4 : 1];          // fp4: the next batch's scale bytes
+    if constexpr (F4) {
+#pragma unroll
+      for (u32 i = 0; i < 4; ++i) snx[i] = s4ld(((i * 8) >> lgpg) + gsub, qp);
+    }
     for (; s0 + 4 <= full; s0 += 4) {
+      u32 scu[F4 ? 4 : 1];
+      if constexpr (F4) {
+#pragma unroll
+        for (u32 i = 0; i < 4; ++i) {
+          scu[i] = snx[i];
+          snx[i] = s4ld((((s0 + 4 + i) * 8) >> lgpg) + gsub, qp);
+        }
+      }
       if (seq + 4 > avail && !wait_avail(A, seq + 4, avail)) return false;
       u32x4 wv[4];
 #pragma unroll
@@ -1522,7 +1612,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[i].init();
-        MK_GEMV_ADD(acc[i], wv[i], 0);
+        MK_GEMV_ADD(acc[i], wv[i], 0, e8m0f(scu[F4 ? i : 0]));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i].finish(lane, (((s0 + i) * 8) >> lgpg) + gsub, w & (pg - 1), RW, nrt);
@@ -1536,7 +1626,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
       if (g < nrg) {
         GemvAcc<B, P> acc;
         acc.init();
-        MK_GEMV_ADD(acc, wv, 0);
+        MK_GEMV_ADD(acc, wv, 0, F4 ? e8m0f(s4ld(g, qp)) : 1.0f);
         acc.finish(lane, g, w & (pg - 1), RW, nrt);
       }
       seq += 1;
@@ -1603,11 +1693,18 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 #undef MK_GEMV_ADD
 }
 
-template <int B, bool AM, bool F8>  // F8: kernels for models with fp8 projections (the LM head stays bf16)
+// WF: the kernel's projection weight format (WF_BF16, WF_FP8, WF_FP4); the LM head stays bf16
+template <int B, bool AM, int WF>
 __device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
   constexpr int P = GemvWidth<B>::P;
   const u32 pg = o.ppr;
-  if constexpr (F8) {
+  if constexpr (WF == WF_FP4 && B == 1) {
+    if (o.flags & OPF_FP4) {  // at most 16 pieces per row group (the host checks)
+      if (pg <= 8) return op_gemv_nf<B, P, 1, AM, false, true>(A, o, w, seq, gen);
+      return op_gemv_nf<B, P, 2, AM, false, true>(A, o, w, seq, gen);
+    }
+  }
+  if constexpr (WF == WF_FP8) {
     if (o.flags & OPF_FP8) {  // at most 32 pieces per row group (the host checks)
       if (pg <= 8) return op_gemv_nf<B, P, 1, AM, true>(A, o, w, seq, gen);
       if (pg == 16) return op_gemv_nf<B, P, 2, AM, true>(A, o, w, seq, gen);
@@ -2439,7 +2536,7 @@ __device__ __forceinline__ bool op_delta(const KArgs& A, const Op& o, u32 w, u32
 // One decode step's ops of this CU's queue, [q0, q1).  seq (ring slots consumed) and gen (compute
 // barrier count) carry over.  Returns false on abort.  AM: the LM head also leaves its greedy
 // partials (multi-step kernels).
-template <int B, bool AM, bool F8>
+template <int B, bool AM, int WF>
 __device__ __forceinline__ bool op_loop(KPtr ap, u32 q0, u32 q1, u32 w, u32& seq, u32& gen) {
   ItemCache ic;  // a new step has a new attention plan
   for (u32 oi = q0; oi < q1; ++oi) {
@@ -2467,11 +2564,11 @@ __device__ __forceinline__ bool op_loop(KPtr ap, u32 q0, u32 q1, u32 w, u32& seq
         op_embed_finish(A, w, gen);
         break;
       case OP_GEMV:
-        if constexpr (B < 8) alive = op_gemv<B, AM, F8>(A, o, w, seq, gen);
+        if constexpr (B < 8) alive = op_gemv<B, AM, WF>(A, o, w, seq, gen);
         break;
       case OP_MMV:
         if constexpr (B == 8) {
-          if (F8 && (o.flags & OPF_FP8)) alive = op_mmv<B, AM, F8>(A, o, w, seq, gen);
+          if (WF == WF_FP8 && (o.flags & OPF_FP8)) alive = op_mmv<B, AM, WF == WF_FP8>(A, o, w, seq, gen);
           else alive = op_mmv<B, AM>(A, o, w, seq, gen);
         }
         break;
@@ -2510,18 +2607,18 @@ __device__ __forceinline__ bool op_loop(KPtr ap, u32 q0, u32 q1, u32 w, u32& seq
 // measured slower).  (The loader's step loop is inlined: as a call it measured slower.)
 // Arguments arrive in vector registers; they are uniform and restated so.  Returns seq | gen << 32,
 // or ~0 on abort.
-template <int B, bool F8>
+template <int B, int WF>
 __device__ __noinline__ uint64_t op_loop_call(KPtr ap, u32 q0, u32 q1, u32 w, u32 seq, u32 gen) {
   q0 = __builtin_amdgcn_readfirstlane(q0);
   q1 = __builtin_amdgcn_readfirstlane(q1);
   w = __builtin_amdgcn_readfirstlane(w);
   seq = __builtin_amdgcn_readfirstlane(seq);
   gen = __builtin_amdgcn_readfirstlane(gen);
-  if (!op_loop<B, true, F8>(uniform_kptr(ap), q0, q1, w, seq, gen)) return ~0ull;
+  if (!op_loop<B, true, WF>(uniform_kptr(ap), q0, q1, w, seq, gen)) return ~0ull;
   return (uint64_t)seq | ((uint64_t)gen << 32);
 }
 
-template <int B, bool MS, bool F8>
+template <int B, bool MS, int WF>
 __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
   u32 seq = 0, gen = 0;
   const u32 nsteps = MS ? (u32)kargs().n_steps : 1u;
@@ -2550,12 +2647,12 @@ __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
       if (!cbar(A, gen)) return;
     }
     if constexpr (MS) {
-      const uint64_t r = op_loop_call<B, F8>(kernarg_ptr(), q0, q1, w, seq, gen);
+      const uint64_t r = op_loop_call<B, WF>(kernarg_ptr(), q0, q1, w, seq, gen);
       if (r == ~0ull) return;
       seq = __builtin_amdgcn_readfirstlane((u32)r);
       gen = __builtin_amdgcn_readfirstlane((u32)(r >> 32));
     } else {
-      if (!op_loop<B, false, F8>(kernarg_ptr(), q0, q1, w, seq, gen)) return;
+      if (!op_loop<B, false, WF>(kernarg_ptr(), q0, q1, w, seq, gen)) return;
     }
     {  // step epilogue
       if (multi) {  // this compute unit's stores of the step are complete: publish the step
@@ -2582,7 +2679,7 @@ __device__ __forceinline__ void compute(u32 q0, u32 q1, u32 w) {
   }
 }
 
-template <int B, bool MS, bool F8 = false>  // F8: models with fp8 projections (batch 1)
+template <int B, bool MS, int WF = WF_BF16>  // WF: the projections' weight format
 __device__ __forceinline__ void megakernel_body(const KArgs& A) {
   const u32 wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index: uniform per wave
   if (threadIdx.x < NC) g_consumed[threadIdx.x] = 0;
@@ -2593,7 +2690,7 @@ __device__ __forceinline__ void megakernel_body(const KArgs& A) {
   if (earlier_launch_failed(A)) return;  // uniform: the same word for every wave of the grid
   const u32 q0 = A.queue_off[blockIdx.x], q1 = A.queue_off[blockIdx.x + 1];
   if (wv == 0) loader<MS>(q0, q1);
-  else compute<B, MS, F8>(q0, q1, wv - 1);
+  else compute<B, MS, WF>(q0, q1, wv - 1);
 }
 
 }  // namespace mk
@@ -2607,17 +2704,19 @@ extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b1)(mk::K
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b2)(mk::KArgs A) { mk::megakernel_body<2, false>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b4)(mk::KArgs A) { mk::megakernel_body<4, false>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b8)(mk::KArgs A) { mk::megakernel_body<8, false>(A); }
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b1_f8)(mk::KArgs A) { mk::megakernel_body<1, false, true>(A); }
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b2_f8)(mk::KArgs A) { mk::megakernel_body<2, false, true>(A); }
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b4_f8)(mk::KArgs A) { mk::megakernel_body<4, false, true>(A); }
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b8_f8)(mk::KArgs A) { mk::megakernel_body<8, false, true>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b1_f8)(mk::KArgs A) { mk::megakernel_body<1, false, mk::WF_FP8>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b2_f8)(mk::KArgs A) { mk::megakernel_body<2, false, mk::WF_FP8>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b4_f8)(mk::KArgs A) { mk::megakernel_body<4, false, mk::WF_FP8>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b8_f8)(mk::KArgs A) { mk::megakernel_body<8, false, mk::WF_FP8>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b1_f4)(mk::KArgs A) { mk::megakernel_body<1, false, mk::WF_FP4>(A); }
 #if !MK_TRACE_STAMPS
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b1(mk::KArgs A) { mk::megakernel_body<1, true>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b2(mk::KArgs A) { mk::megakernel_body<2, true>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b4(mk::KArgs A) { mk::megakernel_body<4, true>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b8(mk::KArgs A) { mk::megakernel_body<8, true>(A); }
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b1_f8(mk::KArgs A) { mk::megakernel_body<1, true, true>(A); }
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b2_f8(mk::KArgs A) { mk::megakernel_body<2, true, true>(A); }
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b4_f8(mk::KArgs A) { mk::megakernel_body<4, true, true>(A); }
-extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b8_f8(mk::KArgs A) { mk::megakernel_body<8, true, true>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b1_f8(mk::KArgs A) { mk::megakernel_body<1, true, mk::WF_FP8>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b2_f8(mk::KArgs A) { mk::megakernel_body<2, true, mk::WF_FP8>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b4_f8(mk::KArgs A) { mk::megakernel_body<4, true, mk::WF_FP8>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b8_f8(mk::KArgs A) { mk::megakernel_body<8, true, mk::WF_FP8>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b1_f4(mk::KArgs A) { mk::megakernel_body<1, true, mk::WF_FP4>(A); }
 #endif

@@ -44,7 +44,7 @@ std::string validate_desc(const mk_model_desc* desc, ModelShape* out, mk_status*
   if (d.n_layers < 1 || d.hidden < 8 || d.vocab < 1 || d.ffn < 8) return "n_layers, hidden, vocab and ffn must be positive";
   if (!d.layer_kind) return "layer_kind is null";
   if (d.max_batch < 1 || d.max_ctx < 1) return "max_batch and max_ctx must be positive";
-  if (d.weight_format != MK_WEIGHTS_BF16 && d.weight_format != MK_WEIGHTS_FP8_E4M3)
+  if (d.weight_format != MK_WEIGHTS_BF16 && d.weight_format != MK_WEIGHTS_FP8_E4M3 && d.weight_format != MK_WEIGHTS_FP4_MX)
     return fmt("weight_format %d is not a mk_weight_format", d.weight_format);
   *st = MK_ERR_UNSUPPORTED;
   if (d.max_batch > 8) return "max_batch above 8 is not supported";
@@ -53,6 +53,10 @@ std::string validate_desc(const mk_model_desc* desc, ModelShape* out, mk_status*
   if (!(d.rms_eps > 0.0f) || !(d.rope_base > 1.0f)) return "rms_eps must be > 0 and rope_base > 1";
   if (d.weight_format == MK_WEIGHTS_FP8_E4M3) {
     if (d.hidden % 16 || d.ffn % 16) return "fp8 weights need hidden and ffn to be multiples of 16";
+  }
+  if (d.weight_format == MK_WEIGHTS_FP4_MX) {
+    if (d.max_batch != 1) return "fp4 weights run one sequence per step (max_batch 1)";
+    if (d.hidden % 32 || d.ffn % 32) return "fp4 weights need hidden and ffn to be multiples of 32";
   }
   out->d = d;
   out->kinds.assign(d.layer_kind, d.layer_kind + d.n_layers);
@@ -97,9 +101,10 @@ static bool gemv_pg_ok(uint32_t pg) { return pg == 1 || pg == 2 || pg == 4 || (p
 static uint32_t gemv_slots(uint32_t nrg, uint32_t pg) { return pg >= 8 ? nrg * (pg / 8) : (nrg * pg + 7) / 8; }
 
 namespace {
-// fp32 row scales of a projection's (up to three) weight runs, for fp8 weights
+// scales of a projection's (up to three) weight runs: fp32 row scales for fp8 weights, E8M0 block
+// scale rows (K / 32 bytes per row) for fp4 weights
 struct RowScales {
-  bool f8 = false;
+  bool f8 = false, f4 = false;
   uint64_t s[3] = {0, 0, 0};
 };
 
@@ -126,15 +131,20 @@ struct Builder {
       err = fmt("fp8 projection with %u inputs (needs a multiple of 16)", K);
       return;
     }
+    if (sc.f4 && (K % 32 || B != 1)) {
+      err = fmt("fp4 projection with %u inputs at batch width %d (needs a multiple of 32, one sequence)", K, B);
+      return;
+    }
     if (B >= 8) {
       mmv(stage, wait, layer, N, K, epi, norm, W, W2, W3, b1, b2, in, ld_in, gamma, out, ld_out, res, sc);
       return;
     }
     const int Pp = gemv_part(B), R = 16 / Pp;
-    const uint32_t flags = sc.f8 ? OPF_FP8 : 0u;
+    const uint32_t flags = sc.f8 ? OPF_FP8 : (sc.f4 ? OPF_FP4 : 0u);
     const uint32_t kv = gemv_kv(K, flags);  // stream elements per row
     const int pg = gemv_pg((int)kv, Pp);
-    if (pg > GEMV_MAX_PG || (sc.f8 && pg > 32)) {  // (fp8: at most 4 input fragments of 16 per wave)
+    // (fp8: at most 4 input fragments of 16 per wave; fp4: 2 of 32)
+    if (pg > GEMV_MAX_PG || (sc.f8 && pg > 32) || (sc.f4 && pg > 16)) {
       err = fmt("projection with %u inputs is too long for batch width %d", K, B);
       return;
     }
@@ -183,20 +193,20 @@ struct Builder {
       o.nslots = gemv_slots(o.nrows * mult / R, (uint32_t)pg) + (norm ? gain_slots(K) : 0u);
       o.ld_in = ld_in;
       o.ld_out = ld_out;
-      // weight runs: at most two contiguous row runs per op (fp8 row scales: the same runs)
-      const uint64_t rb = (uint64_t)kv * 2;
+      // weight runs: at most two contiguous row runs per op (scales: the same runs, srb bytes a row)
+      const uint64_t rb = (uint64_t)kv * 2, srb = sc.f4 ? K / 32 : 4;
       if (epi == EPI_SWIGLU) {
         o.W = W ? W + r0 * rb : 0;
         o.W2 = W2 ? W2 + r0 * rb : 0;
-        o.Ws = sc.s[0] ? sc.s[0] + r0 * 4ull : 0;
-        o.Ws2 = sc.s[1] ? sc.s[1] + r0 * 4ull : 0;
+        o.Ws = sc.s[0] ? sc.s[0] + r0 * srb : 0;
+        o.Ws2 = sc.s[1] ? sc.s[1] + r0 * srb : 0;
         o.b1 = o.nrows;
       } else {
         const uint64_t segs[3] = {W, W2, W3};
         const uint32_t start[3] = {0u, b1, b2}, end[3] = {b1, b2, 0xFFFFFFFFu};
         int sa = r0 < b1 ? 0 : (r0 < b2 ? 1 : 2);
         o.W = segs[sa] ? segs[sa] + (uint64_t)(r0 - start[sa]) * rb : 0;
-        o.Ws = sc.s[sa] ? sc.s[sa] + (uint64_t)(r0 - start[sa]) * 4 : 0;
+        o.Ws = sc.s[sa] ? sc.s[sa] + (uint64_t)(r0 - start[sa]) * srb : 0;
         const uint32_t na = std::min<uint32_t>(o.nrows, end[sa] - r0);
         o.b1 = na;
         o.W2 = 0;
@@ -220,6 +230,10 @@ struct Builder {
   void mmv(int stage, int wait, int layer, uint32_t N, uint32_t K, uint8_t epi, bool norm, uint64_t W, uint64_t W2,
            uint64_t W3, uint32_t b1, uint32_t b2, uint64_t in, uint32_t ld_in, uint64_t gamma, uint64_t out,
            uint32_t ld_out, uint64_t res, const RowScales& sc) {
+    if (sc.f4) {
+      err = "fp4 weights on the batch-8 path";
+      return;
+    }
     const uint32_t flags = sc.f8 ? OPF_FP8 : 0u;
     const uint32_t kv = gemv_kv(K, flags);  // stream elements per row (fp8: a segment is 512 codes)
     if (K % 16 || kv % MMV_KSEG) {
@@ -366,11 +380,12 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
   // ---------------- stages and ops
   Builder bd{m, P, n_cus, {}, ""};
   auto wptr = [&](const void* p) -> uint64_t { return (uint64_t)(uintptr_t)p; };
-  const bool f8 = d.weight_format == MK_WEIGHTS_FP8_E4M3;
-  auto scales = [&](const float* a, const float* b = nullptr, const float* c3 = nullptr) {
+  const bool f8 = d.weight_format == MK_WEIGHTS_FP8_E4M3, f4 = d.weight_format == MK_WEIGHTS_FP4_MX;
+  auto scales = [&](const void* a, const void* b = nullptr, const void* c3 = nullptr) {
     RowScales r;
     r.f8 = f8;
-    if (f8) {
+    r.f4 = f4;
+    if (f8 || f4) {
       r.s[0] = wptr(a);
       r.s[1] = wptr(b);
       r.s[2] = wptr(c3);
@@ -470,9 +485,11 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
       o.sig_index = (uint32_t)j;
       const int cu = (int)(j % (size_t)n_cus);
       if (o.opcode == OP_GEMV || o.opcode == OP_MMV) {
-        // streamed weight bytes: 2 per bf16 weight; 1 per fp8 code plus 4 per fp32 row scale
+        // streamed weight bytes: 2 per bf16 weight; 1 per fp8 code plus 4 per fp32 row scale; half
+        // a byte per fp4 code plus one scale byte per 32 codes
         const double rows = (double)o.nrows * (o.epi == EPI_SWIGLU ? 2 : 1);
-        const double bytes = (o.flags & OPF_FP8) ? rows * (o.K + 4.0) : rows * o.K * 2;
+        const double bytes = (o.flags & OPF_FP8) ? rows * (o.K + 4.0)
+                           : (o.flags & OPF_FP4) ? rows * (o.K / 2.0 + o.K / 32.0) : rows * o.K * 2;
         P.cu_bytes[cu] += bytes;
         P.weight_bytes += bytes;
       }
@@ -576,6 +593,8 @@ int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
         if ((uint64_t)pg * 32 * Pp < gemv_kv(o.K, o.flags)) bad(fmt("cu %d op %u: pieces do not cover a row", c, i));
         if ((o.flags & OPF_FP8) && (o.K % 16 || o.epi == EPI_LOGITS || pg > 32))
           bad(fmt("cu %d op %u: fp8 weights off the batch-1 projection path", c, i));
+        if ((o.flags & OPF_FP4) && (o.K % 32 || o.epi == EPI_LOGITS || pg > 16 || P.kernel_batch != 1 || (o.flags & OPF_FP8)))
+          bad(fmt("cu %d op %u: fp4 weights off the batch-1 projection path", c, i));
         if (o.nrows == 0 || o.nrows % R) bad(fmt("cu %d op %u: %u rows, not whole groups of %u", c, i, o.nrows, R));
         if (o.epi != EPI_SWIGLU && o.b1 < o.nrows && o.b1 % R) bad(fmt("cu %d op %u: weight runs split a row group", c, i));
         if (o.epi == EPI_SWIGLU && o.b1 != o.nrows) bad(fmt("cu %d op %u: gate / up runs", c, i));
@@ -590,6 +609,7 @@ int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
         const uint32_t kv = gemv_kv(o.K, o.flags);
         if (kv % MMV_KSEG || o.ppr * MMV_KSEG != kv) bad(fmt("cu %d op %u: K segments do not cover a row", c, i));
         if ((o.flags & OPF_FP8) && (o.K % 16 || o.epi == EPI_LOGITS)) bad(fmt("cu %d op %u: fp8 operands", c, i));
+        if (o.flags & OPF_FP4) bad(fmt("cu %d op %u: fp4 weights on the batch-8 path", c, i));
         if (o.nslots != ntiles * o.ppr) bad(fmt("cu %d op %u: slot count", c, i));
         if (P.kernel_batch > 16) bad(fmt("cu %d op %u: batch wider than a matrix tile", c, i));
       }
@@ -616,9 +636,12 @@ int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
   }
   // streamed weight bytes == the model's projection bytes
   const mk_model_desc& d = m.d;
-  // (a projection of rows x cols: 2 bytes per bf16 weight, or 1 per fp8 code and 4 per row scale)
-  const bool f8 = d.weight_format == MK_WEIGHTS_FP8_E4M3;
-  auto pbytes = [&](double rows, double cols) { return f8 ? rows * (cols + 4.0) : rows * cols * 2; };
+  // (a projection of rows x cols: 2 bytes per bf16 weight, or 1 per fp8 code and 4 per row scale, or
+  // half a byte per fp4 code and one per 32-code block scale)
+  const bool f8 = d.weight_format == MK_WEIGHTS_FP8_E4M3, f4 = d.weight_format == MK_WEIGHTS_FP4_MX;
+  auto pbytes = [&](double rows, double cols) {
+    return f8 ? rows * (cols + 4.0) : (f4 ? rows * (cols / 2 + cols / 32) : rows * cols * 2);
+  };
   double want = (double)d.vocab * d.hidden * 2;  // the LM head stays bf16
   for (int l = 0; l < d.n_layers; ++l) {
     want += 2 * pbytes(d.ffn, d.hidden) + pbytes(d.hidden, d.ffn);

@@ -39,7 +39,8 @@ def _desc(cfg, max_ctx):
     return mkd.make_desc(s["n_layers"], s["hidden"], s["vocab"], s["ffn"], s["n_q_heads"], s["n_kv_heads"],
                          s["head_dim"], s["qk_norm"], s["tied"], s["rms_eps"], s["rope_base"], s["layer_kinds"],
                          s["max_batch"], s["max_ctx"], s["n_delta_heads"], s["delta_dk"], s["delta_dv"],
-                         s["conv_width"], weight_format=mkd.MK_WEIGHTS_FP8_E4M3 if cfg.weights == "fp8" else 0)
+                         s["conv_width"], weight_format={"fp8": mkd.MK_WEIGHTS_FP8_E4M3,
+                                                         "fp4": mkd.MK_WEIGHTS_FP4_MX}.get(cfg.weights, 0))
 
 
 def _proj_bytes(cfg, per_weight, per_row):
@@ -137,3 +138,23 @@ def test_library_imports_no_device_allocator():
     imported = {l.split()[-1].split("@")[0] for l in out.splitlines() if l.strip()}
     assert "hipGetSymbolAddress" in imported
     assert not {s for s in imported if s.startswith("hip") and ("Malloc" in s or "Free" in s or "Alloc" in s)}
+
+
+@pytest.mark.parametrize("name", ["tiny", "0.6b", "8b"])
+def test_fp4_plan_streams_half_a_byte_per_weight(name):
+    """MX fp4 projections (one sequence): the plan checks, and streams half a byte per weight plus one
+    E8M0 scale byte per 32 weights (the LM head stays bf16)."""
+    cfg = synth.CONFIGS[name].replace(weights="fp4")
+    lm = cfg.vocab * cfg.hidden * 2
+    info = mkd.mk_plan(_desc(cfg, 4096 + 256), 256)
+    assert info.weight_bytes == lm + _proj_bytes(cfg, 0.5 + 1 / 32, 0)
+
+
+def test_fp4_refuses_more_than_one_sequence_and_partial_blocks():
+    cfg = synth.CONFIGS["tiny"].replace(weights="fp4")
+    with pytest.raises(mkd.MKError) as e:
+        mkd.mk_plan(_desc(cfg.replace(batch=2, ctx=[128, 128]), 512), 256)
+    assert e.value.status == mkd.MK_ERR_UNSUPPORTED and "max_batch" in str(e.value)
+    with pytest.raises(mkd.MKError) as e:  # hidden 272: rows of 272 weights are not whole blocks of 32
+        mkd.mk_plan(_desc(cfg.replace(hidden=272), 512), 256)
+    assert e.value.status == mkd.MK_ERR_UNSUPPORTED
