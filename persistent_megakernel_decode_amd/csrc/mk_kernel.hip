@@ -1388,11 +1388,30 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
       if (i % NF < nf) stg[i] = g_ring[((seq + (i / NF) * nf + i % NF) % NSLOT) * (SLOT / 16) + achunk];
     release_upto(w, seq + nst);
   }
+  // With PG < 8 pieces per row group a slot holds 8 / PG groups, one piece of one group per wave:
+  // the first SGS slots (whole groups only) are staged the same way.
+  constexpr u32 SGS = (B == 1 && NF == 1) ? 8u : 0u;
+  static_assert(SGS <= SS, "staged slots fit the staging registers");
+  const u32 lgpg = pg < 8 ? (u32)__builtin_ctz(pg) : 0u;
+  const u32 gsub = w >> lgpg;                        // (PG < 8) this wave's group within a slot
+  const u32 qp = w & (pg - 1);                       // (PG < 8) this wave's piece of its group
+  const u32 full = pg < 8 ? nrg >> (3 - lgpg) : 0u;  // (PG < 8) slots whose groups all exist
+  const bool staged_s = SGS > 0 && pg < 8 && full >= SGS;
+  if (staged_s) {
+    if (seq + SGS > avail && !wait_avail(A, seq + SGS, avail)) return false;
+#pragma unroll
+    for (u32 i = 0; i < SGS; ++i) stg[i] = g_ring[((seq + i) % NSLOT) * (SLOT / 16) + achunk];
+    release_upto(w, seq + SGS);
+  }
   u32 sst[F4 ? SS : 1];  // fp4: the staged groups' scale bytes, fetched while the inputs are awaited
   if constexpr (F4) {
     if (staged) {
 #pragma unroll
       for (u32 i = 0; i < SS; ++i) sst[i] = i % NF < nf ? s4ld(i / NF, 8 * (i % NF) + w) : 0x7Fu;
+    }
+    if (staged_s) {
+#pragma unroll
+      for (u32 i = 0; i < SGS; ++i) sst[i] = s4ld(((i * 8) >> lgpg) + gsub, qp);
     }
   }
   // residual rows of this thread (epilogue row r = thread index), fetched now, off the critical path
@@ -1584,15 +1603,26 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
     }
   } else {
     // PG < 8: each slot holds 8 / PG groups, one piece of a group per wave
-    const u32 lgpg = (u32)__builtin_ctz(pg);
-    const u32 gsub = w >> lgpg;          // this wave's group within a slot
-    const u32 full = nrg >> (3 - lgpg);  // slots whose groups all exist
     u32 s0 = 0;
-    const u32 qp = w & (pg - 1);  // this wave's piece of its group
-    u32 snx[F4 ? 4 : 1];          // fp4: the next batch's scale bytes
+    if (staged_s) {  // the staged slots first, from registers (the same arithmetic as below)
+#pragma unroll
+      for (u32 bt = 0; bt < SGS / 4; ++bt) {
+        GemvAcc<B, P> acc[4];
+#pragma unroll
+        for (u32 i = 0; i < 4; ++i) {
+          acc[i].init();
+          MK_GEMV_ADD(acc[i], stg[bt * 4 + i], 0, e8m0f(sst[F4 ? bt * 4 + i : 0]));
+        }
+#pragma unroll
+        for (u32 i = 0; i < 4; ++i) acc[i].finish(lane, (((bt * 4 + i) * 8) >> lgpg) + gsub, qp, RW, nrt);
+      }
+      s0 = SGS;
+      seq += SGS;
+    }
+    u32 snx[F4 ? 4 : 1];  // fp4: the next batch's scale bytes
     if constexpr (F4) {
 #pragma unroll
-      for (u32 i = 0; i < 4; ++i) snx[i] = s4ld(((i * 8) >> lgpg) + gsub, qp);
+      for (u32 i = 0; i < 4; ++i) snx[i] = s4ld((((s0 + i) * 8) >> lgpg) + gsub, qp);
     }
     for (; s0 + 4 <= full; s0 += 4) {
       u32 scu[F4 ? 4 : 1];
@@ -1615,7 +1645,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
         MK_GEMV_ADD(acc[i], wv[i], 0, e8m0f(scu[F4 ? i : 0]));
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i].finish(lane, (((s0 + i) * 8) >> lgpg) + gsub, w & (pg - 1), RW, nrt);
+      for (int i = 0; i < 4; ++i) acc[i].finish(lane, (((s0 + i) * 8) >> lgpg) + gsub, qp, RW, nrt);
       seq += 4;
     }
     for (; s0 < nslots; ++s0) {
@@ -1627,7 +1657,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
         GemvAcc<B, P> acc;
         acc.init();
         MK_GEMV_ADD(acc, wv, 0, F4 ? e8m0f(s4ld(g, qp)) : 1.0f);
-        acc.finish(lane, g, w & (pg - 1), RW, nrt);
+        acc.finish(lane, g, qp, RW, nrt);
       }
       seq += 1;
     }
