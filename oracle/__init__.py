@@ -45,7 +45,8 @@ class OrcModel(ctypes.Structure):
                 ("rms_eps", ctypes.c_double), ("rope_base", ctypes.c_double),
                 ("n_delta_heads", ctypes.c_int), ("delta_dk", ctypes.c_int), ("delta_dv", ctypes.c_int),
                 ("conv_width", ctypes.c_int), ("layer_kind", P), ("page_size", ctypes.c_int),
-                ("delta_decay_first", ctypes.c_int), ("weight_format", ctypes.c_int)]
+                ("delta_decay_first", ctypes.c_int), ("weight_format", ctypes.c_int),
+                ("n_experts", ctypes.c_int), ("top_k", ctypes.c_int)]
 
 
 W_BF16, W_FP8, W_FP4 = 0, 1, 2  # orc_model.weight_format
@@ -61,7 +62,7 @@ PROJ_FIELDS = ["wq", "wk", "wv", "wo", "w_qkv_delta", "w_gates", "wo_delta", "w_
 
 
 class OrcLayer(ctypes.Structure):
-    _fields_ = [(f, P) for f in _LAYER_FIELDS] + [("s_" + f, P) for f in PROJ_FIELDS]
+    _fields_ = [(f, P) for f in _LAYER_FIELDS] + [("s_" + f, P) for f in PROJ_FIELDS] + [("w_router", P)]
 
 
 class OrcWeights(ctypes.Structure):
@@ -74,7 +75,8 @@ class OrcCache(ctypes.Structure):
 
 
 class OrcDump(ctypes.Structure):
-    _fields_ = [("x_mixer", P), ("x_mlp", P), ("mixer_o", P), ("mlp_m", P), ("final_r", P)]
+    _fields_ = [("x_mixer", P), ("x_mlp", P), ("mixer_o", P), ("mlp_m", P), ("final_r", P), ("router", P),
+                ("sel", P), ("force", P)]
 
 
 def lib():
@@ -99,6 +101,10 @@ def lib():
         L.orc_e8m0.restype = ctypes.c_double
         L.orc_matvec_fp4.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, P]
         L.orc_matvec_fp4.restype = None
+        L.orc_moe_select.argtypes = [P, ctypes.c_int, ctypes.c_int, P]
+        L.orc_moe_select.restype = None
+        L.orc_moe_weights.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P]
+        L.orc_moe_weights.restype = None
         L.orc_rope.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_double]
         L.orc_attend.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, P, P]
         L.orc_silu.argtypes = [ctypes.c_double]
@@ -178,6 +184,23 @@ def matvec_fp4(W_packed, S, x) -> np.ndarray:
     y = np.empty(W.shape[0], dtype=np.float32)
     lib().orc_matvec_fp4(_ptr(W), _ptr(S), _ptr(x), W.shape[0], x.size, _ptr(y))
     return y
+
+
+def moe_select(logits, k: int) -> np.ndarray:
+    """The k largest router logits' experts, descending, ties to the lower index."""
+    v = _c(logits, np.float32)
+    sel = np.empty(k, dtype=np.int32)
+    lib().orc_moe_select(_ptr(v), v.size, k, _ptr(sel))
+    return sel
+
+
+def moe_weights(logits, sel) -> np.ndarray:
+    """softmax over all router logits, renormalised over the chosen experts `sel`."""
+    v = _c(logits, np.float32)
+    sel = _c(sel, np.int32)
+    w = np.empty(sel.size, dtype=np.float64)
+    lib().orc_moe_weights(_ptr(v), v.size, sel.size, _ptr(sel), _ptr(w))
+    return w
 
 
 def rope(u, pos: int, base: float) -> np.ndarray:
@@ -265,6 +288,7 @@ class DecodeOracle:
         fmt = weights.get("format", "bf16")
         fp8, fp4 = fmt == "fp8", fmt == "fp4"
         m.weight_format = W_FP8 if fp8 else (W_FP4 if fp4 else W_BF16)
+        m.n_experts, m.top_k = getattr(cfg, "n_experts", 0), getattr(cfg, "top_k", 0)
         self.m = m
         self.layers = (OrcLayer * cfg.n_layers)()
         for l, L in enumerate(weights["layers"]):
@@ -282,6 +306,12 @@ class DecodeOracle:
                         if sc.dtype != (np.float32 if fp8 else np.uint8) or sc.shape != shape:
                             raise TypeError(f"layer {l} {f}_scale: {'fp32' if fp8 else 'uint8'} {list(shape)} expected")
                         setattr(self.layers[l], "s_" + f, sc.ctypes.data)
+            if m.n_experts:
+                E, F, H = m.n_experts, cfg.ffn, cfg.hidden
+                for f, shape in (("w_router", (E, H)), ("w_gate", (E, F, H)), ("w_up", (E, F, H)), ("w_down", (E, H, F))):
+                    if L[f].dtype != np.uint16 or L[f].shape != shape or not L[f].flags.c_contiguous:
+                        raise TypeError(f"layer {l} {f}: bf16 {list(shape)} expected")
+                self.layers[l].w_router = L["w_router"].ctypes.data
         ow = OrcWeights()
         ow.embed = weights["embed"].ctypes.data
         ow.final_norm = weights["final_norm"].ctypes.data
@@ -319,8 +349,11 @@ class DecodeOracle:
                               _ptr(_c(u, np.float32)), _ptr(_c(a, np.float32)), _ptr(cs), _ptr(st), _ptr(o))
         return o, cs, st
 
-    def step(self, tokens, positions, ctx_lens, dump: bool = False):
-        """One decode step.  Returns logits [B, V] (and a dict of mid-states when dump)."""
+    def step(self, tokens, positions, ctx_lens, dump: bool = False, force_experts=None):
+        """One decode step.  Returns logits [B, V] (and a dict of mid-states when dump).  For
+        mixture-of-experts models the mid-states include the router logits "router" [L, B, E] and the
+        oracle's own expert choice "sel" [L, B, k]; force_experts [L, B, k] makes it use those experts
+        instead of its own choice."""
         c = self.cfg
         tokens = _c(tokens, np.int32)
         positions = _c(positions, np.int32)
@@ -335,7 +368,17 @@ class DecodeOracle:
                     "mixer_o": np.zeros((c.n_layers, B, self.mix_dim), np.float32),
                     "mlp_m": np.zeros((c.n_layers, B, c.ffn), np.float32),
                     "final_r": np.zeros((B, c.hidden), np.float32)}
+            if self.m.n_experts:
+                arrs["router"] = np.zeros((c.n_layers, B, self.m.n_experts), np.float32)
+                arrs["sel"] = np.zeros((c.n_layers, B, self.m.top_k), np.int32)
+        if arrs or force_experts is not None:
             d = OrcDump(**{k: v.ctypes.data for k, v in arrs.items()})
+            if force_experts is not None:
+                fe = np.ascontiguousarray(force_experts, dtype=np.int32)
+                if fe.shape != (c.n_layers, B, self.m.top_k) or fe.min() < 0 or fe.max() >= self.m.n_experts:
+                    raise ValueError("force_experts: [n_layers, batch, top_k] expert ids expected")
+                d.force = fe.ctypes.data
+                self._force_keep = fe
         rc = lib().orc_decode_step(ctypes.byref(self.m), ctypes.byref(self.ow), ctypes.byref(self.oc),
                                    tokens.ctypes.data, positions.ctypes.data, ctx_lens.ctypes.data, B,
                                    logits.ctypes.data, ctypes.byref(d) if d is not None else None)

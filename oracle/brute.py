@@ -12,7 +12,10 @@ floor(h * Hkv / Hq); cached K/V rounded to bf16 before use.  Delta-rule
 layer (MK-KDA pull request, github choiceoh/stkernel #230, phase chain;
 update S <- g S + beta k (v^T - k^T S)): SiLU after a causal depthwise conv,
 per-head L2 norm of q and k, q scaled by dk^-1/2, g and beta sigmoids of
-the gates projection [g | beta].
+the gates projection [g | beta].  Mixture-of-experts MLP (top-k gating as in
+Mixtral / OLMoE): router logits of the normalised input, the k largest (ties
+to the lower index), softmax weights renormalised over those k, and the sum of
+the chosen SwiGLU experts' outputs weighted by them.
 """
 from __future__ import annotations
 
@@ -125,6 +128,24 @@ def delta_layer(cfg, L, R, S0=None, conv0=None, decay_first=False):
     return out, S_final, conv_final
 
 
+def moe_mlp(cfg, L, R):
+    """Mixture-of-experts MLP of every position of R [T, H]: each row routed on its own."""
+    E, k = cfg.n_experts, cfg.top_k
+    Z = R @ _f(L["w_router"]).T                  # [T, E] router logits
+    Wg, Wu, Wd = _f(L["w_gate"]), _f(L["w_up"]), _f(L["w_down"])
+    out = np.zeros_like(R)
+    for t in range(R.shape[0]):
+        z = Z[t]
+        chosen = np.lexsort((np.arange(E), -z))[:k]   # descending logit, ties to the lower index
+        p = np.exp(z - z.max())
+        p = p / p.sum()
+        g = p[chosen] / p[chosen].sum()
+        for e, ge in zip(chosen, g):
+            m = silu(Wg[e] @ R[t]) * (Wu[e] @ R[t])
+            out[t] += ge * (Wd[e] @ m)
+    return out
+
+
 def forward(cfg, w, tokens, S0=None, conv0=None, decay_first=False):
     """Logits of the last position after running the whole sequence `tokens` (prompt mode).
 
@@ -148,8 +169,11 @@ def forward(cfg, w, tokens, S0=None, conv0=None, decay_first=False):
             idx += 1
             X = X + O @ _f(L["wo_delta"]).T
         R = rms(X, _f(L["mlp_norm"]), cfg.rms_eps)
-        M = silu(R @ _f(L["w_gate"]).T) * (R @ _f(L["w_up"]).T)
-        X = X + M @ _f(L["w_down"]).T
+        if getattr(cfg, "n_experts", 0):
+            X = X + moe_mlp(cfg, L, R)
+        else:
+            M = silu(R @ _f(L["w_gate"]).T) * (R @ _f(L["w_up"]).T)
+            X = X + M @ _f(L["w_down"]).T
         xs.append(X[-1].copy())
     r = rms(X[-1], _f(w["final_norm"]), cfg.rms_eps)
     logits = _f(w["lm_head"]) @ r

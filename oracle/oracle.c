@@ -298,6 +298,67 @@ static void delta_layer(const orc_model* m, const orc_layer* L, orc_cache* c, in
   free(u); free(a);
 }
 
+/* Router of a mixture-of-experts MLP: the top-k experts by logit (Mixtral / OLMoE style top-k gating),
+ * repeated selection of the largest remaining logit, ties to the lower index. */
+void orc_moe_select(const float* logits, int n, int k, int32_t* sel) {
+  for (int j = 0; j < k; ++j) {
+    int best = -1;
+    for (int e = 0; e < n; ++e) {
+      int taken = 0;
+      for (int i = 0; i < j; ++i) taken |= sel[i] == e;
+      if (!taken && (best < 0 || logits[e] > logits[best])) best = e;
+    }
+    sel[j] = best;
+  }
+}
+
+/* gate probabilities p = softmax(logits) over every expert, then the chosen k renormalised */
+void orc_moe_weights(const float* logits, int n, int k, const int32_t* sel, double* w) {
+  double mx = logits[0];
+  for (int e = 1; e < n; ++e) mx = logits[e] > mx ? logits[e] : mx;
+  double z = 0.0;
+  for (int e = 0; e < n; ++e) z += exp((double)logits[e] - mx);
+  double s = 0.0;
+  for (int j = 0; j < k; ++j) {
+    w[j] = exp((double)logits[sel[j]] - mx) / z;
+    s += w[j];
+  }
+  for (int j = 0; j < k; ++j) w[j] /= s;
+}
+
+/* The MoE MLP of one sequence (layer l, sequence b of `batch`): r = RMSNorm(x) * gain, router
+ * logits, top-k experts (or the forced ones), x += sum_j w_j down_e(silu(gate_e r) * up_e r). */
+static void moe_mlp(const orc_model* m, const orc_layer* L, int l, int b, int batch, float* x, orc_dump* dump) {
+  int H = m->hidden, F = m->ffn, E = m->n_experts, k = m->top_k;
+  float* r = (float*)malloc(sizeof(float) * (size_t)H);
+  float* rl = (float*)malloc(sizeof(float) * (size_t)E);
+  float* gt = (float*)malloc(sizeof(float) * (size_t)F);
+  float* up = (float*)malloc(sizeof(float) * (size_t)F);
+  float* y = (float*)malloc(sizeof(float) * (size_t)H);
+  double* acc = (double*)calloc((size_t)H, sizeof(double));
+  int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  double* wt = (double*)malloc(sizeof(double) * (size_t)k);
+  orc_rmsnorm(x, L->mlp_norm, H, m->rms_eps, r);
+  orc_matvec(L->w_router, r, E, H, rl);
+  orc_moe_select(rl, E, k, sel);
+  size_t at = ((size_t)l * batch + b);
+  if (dump && dump->router) memcpy(dump->router + at * (size_t)E, rl, sizeof(float) * (size_t)E);
+  if (dump && dump->sel) memcpy(dump->sel + at * (size_t)k, sel, sizeof(int32_t) * (size_t)k);
+  if (dump && dump->force) memcpy(sel, dump->force + at * (size_t)k, sizeof(int32_t) * (size_t)k);
+  orc_moe_weights(rl, E, k, sel, wt);
+  const uint16_t *wg = (const uint16_t*)L->w_gate, *wu = (const uint16_t*)L->w_up, *wd = (const uint16_t*)L->w_down;
+  for (int j = 0; j < k; ++j) {
+    size_t e = (size_t)sel[j];
+    orc_matvec(wg + e * (size_t)F * H, r, F, H, gt);
+    orc_matvec(wu + e * (size_t)F * H, r, F, H, up);
+    for (int i = 0; i < F; ++i) gt[i] = (float)(orc_silu(gt[i]) * (double)up[i]);
+    orc_matvec(wd + e * (size_t)H * F, gt, H, F, y);
+    for (int i = 0; i < H; ++i) acc[i] += wt[j] * (double)y[i];
+  }
+  for (int i = 0; i < H; ++i) x[i] = (float)((double)x[i] + acc[i]);
+  free(r); free(rl); free(gt); free(up); free(y); free(acc); free(sel); free(wt);
+}
+
 int orc_decode_step(const orc_model* m, const orc_weights* w, orc_cache* c, const int32_t* tokens,
                     const int32_t* positions, const int32_t* ctx_lens, int batch, float* logits, orc_dump* dump) {
   int rc = check_inputs(m, c, tokens, positions, ctx_lens, batch);
@@ -329,6 +390,11 @@ int orc_decode_step(const orc_model* m, const orc_weights* w, orc_cache* c, cons
       add_into(x, t, H);
       if (dump && dump->mixer_o) memcpy(dump->mixer_o + ((size_t)l * batch + b) * (size_t)mix, o, sizeof(float) * (size_t)mix);
       if (dump && dump->x_mixer) memcpy(dump->x_mixer + ((size_t)l * batch + b) * (size_t)H, x, sizeof(float) * (size_t)H);
+      if (m->n_experts > 0) {
+        moe_mlp(m, L, l, b, batch, x, dump);
+        if (dump && dump->x_mlp) memcpy(dump->x_mlp + ((size_t)l * batch + b) * (size_t)H, x, sizeof(float) * (size_t)H);
+        continue;
+      }
       /* SwiGLU MLP */
       orc_rmsnorm(x, L->mlp_norm, H, m->rms_eps, r);
       proj(m, L->w_gate, L->s_w_gate, r, F, H, gt);

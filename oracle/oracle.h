@@ -34,6 +34,9 @@ typedef struct {
   int page_size;
   int delta_decay_first;     /* 0: S <- gS + b k(v^T - k^T S) with the old S throughout; 1: decay first */
   int weight_format;         /* ORC_W_BF16, ORC_W_FP8 or ORC_W_FP4: the projection matrices' format */
+  /* Mixture of experts (0 = dense MLPs): with n_experts > 0 every layer's MLP is top_k of n_experts
+   * SwiGLU experts of width ffn, chosen per sequence by a router (bf16 weights only). */
+  int n_experts, top_k;
 } orc_model;
 
 /* Projection weights (wq wk wv wo w_qkv_delta w_gates wo_delta w_gate w_up w_down): bf16 bit
@@ -56,6 +59,9 @@ typedef struct { /* [out][in] row-major; projections bf16 or fp8 (weight_format)
   /* the projection of the same name's scales: ORC_W_FP8 fp32 [out] row scales, ORC_W_FP4 E8M0
    * bytes [out][in / 32]; unused for bf16 */
   const void *s_wq, *s_wk, *s_wv, *s_wo, *s_w_qkv_delta, *s_w_gates, *s_wo_delta, *s_w_gate, *s_w_up, *s_w_down;
+  /* n_experts > 0: router bf16 [n_experts][hidden]; w_gate / w_up are then [n_experts][ffn][hidden]
+   * and w_down [n_experts][hidden][ffn], expert-major */
+  const uint16_t* w_router;
 } orc_layer;
 
 typedef struct {
@@ -78,9 +84,18 @@ typedef struct {
  *   mixer_o [L][B][mix_dim]  attention output o (Hq*d) or delta readout (heads*dv), before o_proj
  *   mlp_m   [L][B][ffn]      silu(gate) * up
  *   final_r [B][hidden]      normalised input of the LM head
- * mix_dim = max(n_q_heads*head_dim, n_delta_heads*delta_dv). */
+ * mix_dim = max(n_q_heads*head_dim, n_delta_heads*delta_dv).  mlp_m is left untouched for MoE layers.
+ * Mixture of experts (n_experts > 0):
+ *   router  [L][B][n_experts] router logits
+ *   sel     [L][B][top_k]     the experts this oracle's own routing chooses (descending logit,
+ *                             ties to the lower index)
+ *   force   [L][B][top_k]     input: when set, these experts are used instead of its own choice
+ *                             (their weights still come from its own logits) */
 typedef struct {
   float *x_mixer, *x_mlp, *mixer_o, *mlp_m, *final_r;
+  float* router;
+  int32_t* sel;
+  const int32_t* force;
 } orc_dump;
 
 /* ---- building blocks (exported so the tests can pin each one) ---- */
@@ -132,6 +147,13 @@ void orc_delta_mixer(const orc_model* m, const uint16_t* conv_w, const float* u,
 int orc_decode_step(const orc_model* m, const orc_weights* w, orc_cache* c, const int32_t* tokens,
                     const int32_t* positions, const int32_t* ctx_lens, int batch, float* logits,
                     orc_dump* dump);
+
+/* Mixture-of-experts routing of one sequence: the k largest of n router logits (ties to the lower
+ * index), in descending order, into sel[k]. */
+void orc_moe_select(const float* logits, int n, int k, int32_t* sel);
+/* the weights of the k chosen experts: softmax over all n logits, renormalised over the chosen k
+ * (so they sum to 1) */
+void orc_moe_weights(const float* logits, int n, int k, const int32_t* sel, double* w);
 
 /* greedy choice: argmax, ties to the lowest index */
 int orc_argmax(const float* v, int n);

@@ -138,6 +138,8 @@ class Config:
     shuffle_pages: bool = False
     gain_range: Optional[tuple] = None       # None = unit norm gains
     weights: str = "bf16"                    # projections: "bf16", "fp8" (+ fp32 row scales), "fp4" (+ E8M0 block scales)
+    n_experts: int = 0                       # > 0: every MLP is top_k of n_experts experts of width ffn
+    top_k: int = 0
 
     def kinds(self) -> List[int]:
         return list(self.layer_kinds) if self.layer_kinds is not None else [ATTN] * self.n_layers
@@ -179,6 +181,10 @@ CONFIGS: Dict[str, Config] = {
 # KV cache bf16
 CONFIGS["8b-fp8"] = CONFIGS["8b"].replace(name="8b-fp8", weights="fp8")
 CONFIGS["13b-fp8"] = CONFIGS["13b"].replace(name="13b-fp8", weights="fp8")
+# a mixture-of-experts decoder: 16 layers, hidden 2048, GQA 16/4, every MLP 8 of 64 experts of
+# width 1024 (the layer shape of the small open MoE models), batch 1, ctx 4096
+CONFIGS["moe"] = Config("moe", n_layers=16, hidden=2048, n_q_heads=16, n_kv_heads=4, head_dim=128, ffn=1024,
+                        vocab=50304, rope_base=1e4, batch=1, ctx=[4096], steps=64, seed=5, n_experts=64, top_k=8)
 # the 8B shape with MX fp4 projections (E2M1, E8M0 scales per 32 weights)
 CONFIGS["8b-fp4"] = CONFIGS["8b"].replace(name="8b-fp4", weights="fp4")
 
@@ -262,9 +268,18 @@ def make_weights(cfg: Config) -> dict:
     for l, kind in enumerate(cfg.kinds()):
         p = f"layer{l}."
         L = {"attn_norm": _gain(cfg, H, p + "attn_norm"), "mlp_norm": _gain(cfg, H, p + "mlp_norm")}
-        _proj(cfg, L, "w_gate", cfg.ffn, H, p)
-        _proj(cfg, L, "w_up", cfg.ffn, H, p)
-        _proj(cfg, L, "w_down", H, cfg.ffn, p)
+        if cfg.n_experts:  # router and expert-major expert weights (bf16)
+            if cfg.weights != "bf16":
+                raise ValueError("mixture-of-experts models take bf16 weights")
+            E, F = cfg.n_experts, cfg.ffn
+            L["w_router"] = normal_bf16((E, H), s, p + "w_router", WEIGHT_STD)
+            L["w_gate"] = normal_bf16((E, F, H), s, p + "w_gate", WEIGHT_STD)
+            L["w_up"] = normal_bf16((E, F, H), s, p + "w_up", WEIGHT_STD)
+            L["w_down"] = normal_bf16((E, H, F), s, p + "w_down", WEIGHT_STD)
+        else:
+            _proj(cfg, L, "w_gate", cfg.ffn, H, p)
+            _proj(cfg, L, "w_up", cfg.ffn, H, p)
+            _proj(cfg, L, "w_down", H, cfg.ffn, p)
         if kind == ATTN:
             _proj(cfg, L, "wq", cfg.n_q_heads * d, H, p)
             _proj(cfg, L, "wk", cfg.n_kv_heads * d, H, p)
@@ -347,6 +362,9 @@ SMALL: Dict[str, Config] = {
     "tiny-hybrid": Config("tiny-hybrid", n_layers=4, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=512,
                           vocab=512, layer_kinds=hybrid_kinds(4), n_delta_heads=2, delta_dk=32, delta_dv=32,
                           conv_width=4, batch=2, ctx=[16, 16], steps=4, seed=5, gain_range=(0.5, 1.5)),
+    # mixture of experts: 8 experts of width 256, top 2
+    "tiny-moe": CONFIGS["tiny"].replace(name="tiny-moe", ffn=256, n_experts=8, top_k=2, gain_range=(0.5, 1.5),
+                                        seed=6),
 }
 
 
@@ -356,4 +374,5 @@ def shape_of(cfg: Config, max_ctx: int) -> dict:
                 n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, qk_norm=cfg.qk_norm, tied=cfg.tied,
                 rms_eps=cfg.rms_eps, rope_base=cfg.rope_base, layer_kinds=cfg.kinds(), max_batch=cfg.batch,
                 max_ctx=max_ctx, n_delta_heads=cfg.n_delta_heads, delta_dk=cfg.delta_dk, delta_dv=cfg.delta_dv,
-                conv_width=cfg.conv_width, page_size=cfg.page_size, weights=cfg.weights)
+                conv_width=cfg.conv_width, page_size=cfg.page_size, weights=cfg.weights, n_experts=cfg.n_experts,
+                top_k=cfg.top_k)

@@ -137,3 +137,19 @@ def test_out_of_contract_inputs_are_rejected():
     for toks, pos, ctx in (([cfg.vocab], [128], [129]), ([1], [127], [129]), ([1], [500], [501]), ([-1], [128], [129])):
         with pytest.raises(ValueError):
             orc.step(toks, pos, ctx)
+
+
+def test_moe_decode_matches_full_sequence():
+    """Mixture-of-experts MLPs: the incremental oracle against the full-sequence recomputation.  The
+    router's choice is discrete, so the prompt is also checked to keep every top-k margin well above
+    the two sides' rounding (no near-tie decides between them)."""
+    cfg = synth.SMALL["tiny-moe"]
+    T = 24
+    tokens = (synth.u32(T, cfg.seed, "prompt") % cfg.vocab).astype(int).tolist()
+    w, orc, (logits, mid) = _run_prompt(cfg, tokens, dump=True)
+    want, xs, _ = brute.forward(cfg, w, tokens)
+    srt = np.sort(mid["router"][:, 0], axis=-1)[:, ::-1]
+    assert float(np.min(srt[:, cfg.top_k - 1] - srt[:, cfg.top_k])) > 1e-4
+    assert _rel(logits[0], want) < 1e-5
+    for l in range(cfg.n_layers):
+        assert _rel(mid["x_mlp"][l, 0], xs[l]) < 1e-5
