@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 2u
+#define MK_ABI_VERSION 3u
 
 typedef enum {
   MK_OK = 0,
@@ -94,6 +94,14 @@ typedef struct {
   const int32_t* layer_kind; /* host array [n_layers] of mk_layer_kind */
   int32_t max_batch, max_ctx, page_size;
   int32_t weight_format;     /* mk_weight_format of the projection matrices */
+  /* Mixture of experts (0 = dense MLPs).  With n_experts > 0 every layer's MLP is top_k of
+   * n_experts SwiGLU experts of width ffn: router logits z = w_router RMSNorm(x), the top_k experts
+   * of each sequence by logit (ties to the lower index), weights softmax(z) renormalised over the
+   * chosen, and x += sum of the chosen experts' outputs times their weights (the "full layer (MoE +
+   * Attention) megakernel" of the Muse Spark post, LMSYS, as summarised on the khabar-ai page).
+   * n_experts <= 64, 1 <= top_k <= min(8, n_experts), bf16 weights, max_batch <= 4, no verify
+   * windows; otherwise MK_ERR_UNSUPPORTED. */
+  int32_t n_experts, top_k;
 } mk_model_desc;
 
 /* Per-layer weights: device pointers to bf16 (projections in the model's weight_format).
@@ -110,6 +118,9 @@ typedef struct {
   const void *mlp_norm, *w_gate, *w_up, *w_down;
   const void *wq_scale, *wk_scale, *wv_scale, *wo_scale, *w_qkv_delta_scale, *w_gates_scale, *wo_delta_scale;
   const void *w_gate_scale, *w_up_scale, *w_down_scale;
+  /* n_experts > 0: router bf16 [n_experts][H]; w_gate and w_up are then [n_experts][F][H] and
+   * w_down [n_experts][H][F], expert-major, each one allocation */
+  const void* w_router;
 } mk_layer_weights;
 
 typedef struct {
@@ -282,7 +293,8 @@ typedef enum {
   MK_MID_MLP_M = 3,   /* fp32 [batch][ffn] silu(gate) * up */
   MK_MID_PROJ = 4,    /* fp32 [batch][(Hq+2Hkv)*d] raw q|k|v of an attention layer (before norm / RoPE),
                          or [batch][C + 2*heads] in_proj|gates of a delta layer (before the conv) */
-  MK_MID_EMBED = 5    /* fp32 [batch][hidden] embedding rows (layer ignored) */
+  MK_MID_EMBED = 5,   /* fp32 [batch][hidden] embedding rows (layer ignored) */
+  MK_MID_ROUTER = 6   /* fp32 [batch][n_experts] router logits of a mixture-of-experts layer */
 } mk_midstate;
 
 /* Copy mid-state `kind` of `layer` from the last step into dst (device memory,

@@ -16,12 +16,12 @@ from typing import Dict, List, Optional, Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmk.so")
 
-MK_ABI_VERSION = 2
+MK_ABI_VERSION = 3
 MK_WEIGHTS_BF16, MK_WEIGHTS_FP8_E4M3, MK_WEIGHTS_FP4_MX = 0, 1, 2
 MK_OK, MK_ERR_INVALID_ARG, MK_ERR_UNSUPPORTED, MK_ERR_HIP, MK_ERR_DEVICE_INPUT, MK_ERR_TIMEOUT, MK_ERR_STATE = \
     0, -1, -2, -3, -4, -5, -6
 MK_LAYER_ATTN, MK_LAYER_DELTA = 0, 1
-MK_MID_X_MIXER, MK_MID_X_MLP, MK_MID_MIXER_O, MK_MID_MLP_M, MK_MID_PROJ, MK_MID_EMBED = 0, 1, 2, 3, 4, 5
+MK_MID_X_MIXER, MK_MID_X_MLP, MK_MID_MIXER_O, MK_MID_MLP_M, MK_MID_PROJ, MK_MID_EMBED, MK_MID_ROUTER = 0, 1, 2, 3, 4, 5, 6
 
 STATUS_NAMES = {0: "MK_OK", -1: "MK_ERR_INVALID_ARG", -2: "MK_ERR_UNSUPPORTED", -3: "MK_ERR_HIP",
                 -4: "MK_ERR_DEVICE_INPUT", -5: "MK_ERR_TIMEOUT", -6: "MK_ERR_STATE"}
@@ -37,7 +37,7 @@ class mk_model_desc(ctypes.Structure):
                 ("tied_embeddings", I32), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
                 ("n_delta_heads", I32), ("delta_dk", I32), ("delta_dv", I32), ("conv_width", I32),
                 ("layer_kind", P), ("max_batch", I32), ("max_ctx", I32), ("page_size", I32),
-                ("weight_format", I32)]
+                ("weight_format", I32), ("n_experts", I32), ("top_k", I32)]
 
 
 LAYER_FIELDS = ["attn_norm", "wq", "wk", "wv", "wo", "q_norm", "k_norm", "w_qkv_delta", "w_gates", "conv_w",
@@ -49,7 +49,7 @@ PROJ_FIELDS = ["wq", "wk", "wv", "wo", "w_qkv_delta", "w_gates", "wo_delta", "w_
 
 
 class mk_layer_weights(ctypes.Structure):
-    _fields_ = [(f, P) for f in LAYER_FIELDS] + [(f + "_scale", P) for f in PROJ_FIELDS]
+    _fields_ = [(f, P) for f in LAYER_FIELDS] + [(f + "_scale", P) for f in PROJ_FIELDS] + [("w_router", P)]
 
 
 class mk_weights(ctypes.Structure):
@@ -142,11 +142,12 @@ def check(status: int, where: str) -> None:
 # ---------------------------------------------------------------- C-ABI wrappers (same names)
 def make_desc(n_layers, hidden, vocab, ffn, n_q_heads, n_kv_heads, head_dim, qk_norm, tied_embeddings, rms_eps,
               rope_base, layer_kinds: Sequence[int], max_batch, max_ctx, n_delta_heads=0, delta_dk=0, delta_dv=0,
-              conv_width=0, page_size=16, weight_format=MK_WEIGHTS_BF16):
+              conv_width=0, page_size=16, weight_format=MK_WEIGHTS_BF16, n_experts=0, top_k=0):
     kinds = (I32 * n_layers)(*layer_kinds)
     d = mk_model_desc(MK_ABI_VERSION, ctypes.sizeof(mk_model_desc), n_layers, hidden, vocab, ffn, n_q_heads,
                       n_kv_heads, head_dim, qk_norm, tied_embeddings, rms_eps, rope_base, n_delta_heads, delta_dk,
-                      delta_dv, conv_width, ctypes.cast(kinds, P), max_batch, max_ctx, page_size, weight_format)
+                      delta_dv, conv_width, ctypes.cast(kinds, P), max_batch, max_ctx, page_size, weight_format,
+                      n_experts, top_k)
     d._kinds = kinds  # keep the array alive with the struct
     return d
 
@@ -265,7 +266,7 @@ class DecodeContext:
         if arena:  # one allocation for every weight tensor
             arrays = [weights["embed"], weights["final_norm"]] + ([] if shape["tied"] else [weights["lm_head"]])
             for L in weights["layers"]:
-                arrays += [L[f] for f in LAYER_FIELDS if f in L]
+                arrays += [L[f] for f in LAYER_FIELDS + ["w_router"] if f in L]
                 if fp8 or fp4:
                     arrays += [L[f + "_scale"] for f in PROJ_FIELDS if f in L]
             A = self.ARENA_ALIGN
@@ -292,7 +293,8 @@ class DecodeContext:
                               s["head_dim"], s["qk_norm"], s["tied"], s["rms_eps"], s["rope_base"], s["layer_kinds"],
                               s["max_batch"], s["max_ctx"], s.get("n_delta_heads", 0), s.get("delta_dk", 0),
                               s.get("delta_dv", 0), s.get("conv_width", 0), s.get("page_size", 16),
-                              MK_WEIGHTS_FP8_E4M3 if fp8 else (MK_WEIGHTS_FP4_MX if fp4 else MK_WEIGHTS_BF16))
+                              MK_WEIGHTS_FP8_E4M3 if fp8 else (MK_WEIGHTS_FP4_MX if fp4 else MK_WEIGHTS_BF16),
+                              s.get("n_experts", 0), s.get("top_k", 0))
         self.embed = dev(weights["embed"], i16)
         final_norm = dev(weights["final_norm"], i16)
         lm = self.embed if s["tied"] else dev(weights["lm_head"], i16)
@@ -308,6 +310,8 @@ class DecodeContext:
                         setattr(self.layers[l], f + "_scale", dev(L[f + "_scale"], "raw").data_ptr())
                     else:
                         setattr(self.layers[l], f, dev(L[f], i16).data_ptr())
+            if "w_router" in L:  # mixture of experts: expert-major w_gate / w_up / w_down above
+                self.layers[l].w_router = dev(L["w_router"], i16).data_ptr()
         self.w = mk_weights(self.embed.data_ptr(), final_norm.data_ptr(), lm.data_ptr(), ctypes.cast(self.layers, P))
         self.k_pages = torch.from_numpy(cache["k_pages"]).view(i16).to(self.device)
         self.v_pages = torch.from_numpy(cache["v_pages"]).view(i16).to(self.device)

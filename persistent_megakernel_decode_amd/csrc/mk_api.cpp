@@ -43,6 +43,15 @@ extern "C" __global__ void mk_megakernel_steps_b8_f8(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_b1_f4(mk::KArgs A);  // MX fp4 projections (one sequence)
 extern "C" __global__ void mk_megakernel_b1_f4_trace(mk::KArgs A);
 extern "C" __global__ void mk_megakernel_steps_b1_f4(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_b1_moe(mk::KArgs A);  // mixture-of-experts MLPs (bf16)
+extern "C" __global__ void mk_megakernel_b2_moe(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_b4_moe(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_b1_moe_trace(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_b2_moe_trace(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_b4_moe_trace(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_steps_b1_moe(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_steps_b2_moe(mk::KArgs A);
+extern "C" __global__ void mk_megakernel_steps_b4_moe(mk::KArgs A);
 
 namespace {
 
@@ -65,7 +74,14 @@ mk_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-const void* kernel_for(int B, bool traced, int32_t wf) {
+const void* kernel_for(int B, bool traced, int32_t wf, bool moe) {
+  if (moe) {  // (at most 4 sequences)
+    switch (B) {
+      case 1: return traced ? (const void*)mk_megakernel_b1_moe_trace : (const void*)mk_megakernel_b1_moe;
+      case 2: return traced ? (const void*)mk_megakernel_b2_moe_trace : (const void*)mk_megakernel_b2_moe;
+      default: return traced ? (const void*)mk_megakernel_b4_moe_trace : (const void*)mk_megakernel_b4_moe;
+    }
+  }
   if (wf == MK_WEIGHTS_FP4_MX) return traced ? (const void*)mk_megakernel_b1_f4_trace : (const void*)mk_megakernel_b1_f4;
   if (wf == MK_WEIGHTS_FP8_E4M3) {
     switch (B) {
@@ -83,7 +99,14 @@ const void* kernel_for(int B, bool traced, int32_t wf) {
   }
 }
 
-const void* steps_kernel_for(int B, int32_t wf) {
+const void* steps_kernel_for(int B, int32_t wf, bool moe) {
+  if (moe) {
+    switch (B) {
+      case 1: return (const void*)mk_megakernel_steps_b1_moe;
+      case 2: return (const void*)mk_megakernel_steps_b2_moe;
+      default: return (const void*)mk_megakernel_steps_b4_moe;
+    }
+  }
   if (wf == MK_WEIGHTS_FP4_MX) return (const void*)mk_megakernel_steps_b1_f4;
   if (wf == MK_WEIGHTS_FP8_E4M3) {
     switch (B) {
@@ -237,6 +260,15 @@ mk_status mk_plan(const mk_model_desc* desc, int32_t n_cus, mk_plan_info* info) 
   if (!e.empty()) return fail(MK_ERR_UNSUPPORTED, e);
   std::string why;
   info->errors = mk::check_plan(m, p, &why);
+  {  // every workspace reference becomes a device address at mk_create
+    mk::Plan r = p;
+    mk::relocate(&r, 1ull << 40);
+    const std::string u = mk::unrelocated(r);
+    if (!u.empty()) {
+      why += u + "\n";
+      ++info->errors;
+    }
+  }
   info->n_cus = n_cus;
   info->n_ops = (int32_t)p.ops.size();
   info->n_stages = (int32_t)p.stages.size();
@@ -300,6 +332,7 @@ static mk_status create_impl(const mk_model_desc* desc, const mk_weights* w, con
     };
     pe = need(L.attn_norm, "attn_norm");
     if (pe.empty()) pe = need(L.mlp_norm, "mlp_norm");
+    if (pe.empty() && d.n_experts > 0) pe = need(L.w_router, "w_router");
     proj(L.w_gate, L.w_gate_scale, "w_gate", "w_gate_scale");
     proj(L.w_up, L.w_up_scale, "w_up", "w_up_scale");
     proj(L.w_down, L.w_down_scale, "w_down", "w_down_scale");
@@ -352,8 +385,8 @@ static mk_status create_impl(const mk_model_desc* desc, const mk_weights* w, con
   // MK_TRACE=1: the traced kernels (per-op timing stamps; diagnostic)
   const char* trace_env = getenv("MK_TRACE");
   const bool traced = trace_env && atoi(trace_env) != 0;
-  ctx->kernel = kernel_for(P.kernel_batch, traced, d.weight_format);
-  ctx->kernel_steps = steps_kernel_for(P.kernel_batch, d.weight_format);
+  ctx->kernel = kernel_for(P.kernel_batch, traced, d.weight_format, d.n_experts > 0);
+  ctx->kernel_steps = steps_kernel_for(P.kernel_batch, d.weight_format, d.n_experts > 0);
 
   // one resident workgroup per compute unit is required by the persistent design
   int per_cu = 0, per_cu_steps = 0;
@@ -365,6 +398,13 @@ static mk_status create_impl(const mk_model_desc* desc, const mk_weights* w, con
   }
 
   mk::relocate(&P, (uint64_t)(uintptr_t)workspace);
+  {
+    const std::string u = mk::unrelocated(P);
+    if (!u.empty()) {
+      delete ctx;
+      return fail(MK_ERR_STATE, "plan: " + u);
+    }
+  }
   const mk::Layout& Y = P.lay;
   // zero everything (activations, counters, tickets, status), then upload the plan
   // (a fill kernel rather than a memset, so the same code serves the static scratch)
@@ -414,6 +454,7 @@ static mk_status create_impl(const mk_model_desc* desc, const mk_weights* w, con
   A.max_pages_per_seq = m.n_attn ? c->max_pages_per_seq : 1;
   A.nh = d.n_delta_heads; A.dk = d.delta_dk; A.dv = d.delta_dv; A.C = m.C; A.convw = d.conv_width;
   A.n_cus = ncu; A.n_items = P.n_items; A.mix = P.mix_dim;
+  A.n_experts = d.n_experts; A.top_k = d.top_k;
   A.rms_eps = d.rms_eps;
   A.win = 1;      // mk_decode_window overrides it
   A.n_steps = 1;  // mk_decode_steps overrides these four
@@ -542,6 +583,8 @@ mk_status mk_decode_window(mk_ctx* ctx, const int32_t* tokens, const int32_t* po
   if (!ctx) return fail(MK_ERR_INVALID_ARG, "ctx is null");
   if (window < 1 || window > MK_MAX_WINDOW)
     return fail(MK_ERR_INVALID_ARG, "window " + std::to_string(window) + " outside [1, MK_MAX_WINDOW]");
+  if (ctx->shape.d.n_experts > 0 && window > 1)
+    return fail(MK_ERR_UNSUPPORTED, "verify windows are not supported for mixture-of-experts models");
   if (batch < 1 || (int64_t)batch * window > ctx->shape.d.max_batch)
     return fail(MK_ERR_INVALID_ARG, "batch * window = " + std::to_string((int64_t)batch * window) +
                                         " outside [1, max_batch]");
@@ -674,7 +717,16 @@ mk_status mk_copy_midstate(mk_ctx* ctx, int32_t kind, int32_t layer, float* dst,
     case MK_MID_X_MIXER: off = Q.x_mix; width = d.hidden; break;
     case MK_MID_X_MLP: off = Q.x_out; width = d.hidden; break;
     case MK_MID_MIXER_O: off = Q.mix_o; width = ctx->plan.mix_dim; break;
-    case MK_MID_MLP_M: off = Q.m; width = d.ffn; break;
+    case MK_MID_MLP_M:
+      if (d.n_experts > 0) return fail(MK_ERR_UNSUPPORTED, "mixture-of-experts layers keep one MLP state per expert");
+      off = Q.m;
+      width = d.ffn;
+      break;
+    case MK_MID_ROUTER:
+      if (d.n_experts < 1) return fail(MK_ERR_INVALID_ARG, "the model has no router");
+      off = Q.router;
+      width = d.n_experts;
+      break;
     case MK_MID_PROJ:
       off = Q.qkv;
       width = ctx->shape.kinds[layer] == MK_LAYER_ATTN ? (size_t)(d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim

@@ -137,7 +137,8 @@ struct Emu {
       const size_t width = P.layers[l].mix_width;
       for (size_t i = 0; i < bufs[L.mix_o].floats; ++i) bufs[L.mix_o].pollable[i] = (i % P.mix_dim) < width;
       L.x_mix = add_buf(Q.x_mix, (size_t)B * d.hidden);
-      L.m = add_buf(Q.m, (size_t)B * d.ffn);
+      L.m = add_buf(Q.m, (size_t)std::max(1, d.n_experts) * B * d.ffn);  // (one row block per expert)
+      if (d.n_experts > 0) add_buf(Q.router, (size_t)B * d.n_experts);
       L.x_out = add_buf(Q.x_out, (size_t)B * d.hidden);
     }
   }
@@ -218,6 +219,26 @@ struct Emu {
           for (int b = 0; b < B; ++b) w.r.push_back(at(o.out, b * o.ld_out + o.row0, o.nrows));
           ph.push_back(w);
         }
+        break;
+      }
+      case OP_MOE_GU:
+      case OP_MOE_DOWN: {
+        // a row tile of every expert: the router logits, then (gate / up) the normalised input and a
+        // write of every expert's rows (the chosen ones computed, the others zero), or (down) every
+        // expert's SwiGLU rows, whichever the router chose, and the residual
+        const bool gu = o.opcode == OP_MOE_GU;
+        const uint32_t E = (uint32_t)d.n_experts, xs = o.moe_xstride / 4;
+        Phase in{in_kind, {}, -1};
+        for (int b = 0; b < B; ++b) in.r.push_back(at(o.Ws, b * E, E));
+        for (uint32_t e = 0; e < (gu ? 1u : E); ++e)
+          for (int b = 0; b < B; ++b) in.r.push_back(at(o.in, e * xs + b * o.ld_in, o.K));
+        if (!gu)
+          for (int b = 0; b < B; ++b) in.r.push_back(at(o.res, b * o.ld_out + o.row0, o.nrows));
+        ph.push_back(in);
+        Phase w{PH_WRITE, {}, -1};
+        for (uint32_t e = 0; e < (gu ? E : 1u); ++e)
+          for (int b = 0; b < B; ++b) w.r.push_back(at(o.out, e * xs + b * o.ld_out + o.row0, o.nrows));
+        ph.push_back(w);
         break;
       }
       case OP_ATTN: {

@@ -41,8 +41,9 @@ constexpr int CTR_STRIDE = 32;         // u32 between sub-counters (128 B, one c
 constexpr int PIECE_ELEMS = PIECE / 2; // bf16 weights per piece
 constexpr int GEMV_MAX_PG = 64;        // pieces per row group: a wave keeps at most 8 input fragments
 
-enum Opcode : uint8_t { OP_NOP = 0, OP_EMBED = 1, OP_GEMV = 2, OP_ATTN = 3, OP_DELTA = 4, OP_MMV = 5 };
-enum Epi : uint8_t { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+enum Opcode : uint8_t { OP_NOP = 0, OP_EMBED = 1, OP_GEMV = 2, OP_ATTN = 3, OP_DELTA = 4, OP_MMV = 5, OP_MOE_GU = 6,
+                       OP_MOE_DOWN = 7 };
+enum Epi : uint8_t { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_MOE_ACC = 4 };
 
 constexpr int16_t NO_STAGE = -1;
 constexpr uint32_t LAYER_ATTN = 0, LAYER_DELTA = 1;  // the values of mk_layer_kind
@@ -65,8 +66,9 @@ constexpr uint32_t OPF_FP8 = 4u;
 // loader streams a row of K codes as a bf16 row of K / 4 weights, and every 16-byte chunk the
 // compute waves read is one 32-weight block.
 constexpr uint32_t OPF_FP4 = 8u;
-// The projection weight format a kernel is compiled for (OPF_FP8 / OPF_FP4 ops need it)
-constexpr int WF_BF16 = 0, WF_FP8 = 1, WF_FP4 = 2;
+// The projection weight format a kernel is compiled for (OPF_FP8 / OPF_FP4 ops need it); WF_MOE:
+// bf16 weights with mixture-of-experts ops (OP_MOE_GU / OP_MOE_DOWN)
+constexpr int WF_BF16 = 0, WF_FP8 = 1, WF_FP4 = 2, WF_MOE = 3;
 
 // One queue entry (128 bytes).  Pointers are device addresses.
 //
@@ -112,6 +114,7 @@ struct alignas(16) Op {
   uint32_t ld_out;     // floats between batch rows of `out` / `res`
   uint32_t b1;         // GEMV: stream rows taken from W before switching to W2
   uint32_t flags;      // OPF_* bits
+  uint32_t moe_xstride;  // OP_MOE_*: bytes between experts' SwiGLU outputs (m [n_experts][B][F])
   uint64_t W, W2;      // GEMV weight runs, bf16 rows of K (OPF_FP8: fp8 rows of K)
   uint64_t Ws;         // OPF_FP8: fp32 row scales of the W run (at the op's first row); OPF_FP4: E8M0 scale rows
   uint64_t in;         // fp32 [batch][ld_in]
@@ -119,6 +122,7 @@ struct alignas(16) Op {
   uint64_t out;        // fp32 [batch][ld_out] (EPI_LOGITS writes the launch's logits instead)
   uint64_t res;        // fp32 [batch][ld_out] residual (EPI_RESID)
   uint64_t Ws2;        // OPF_FP8: fp32 row scales of the W2 run; OPF_FP4: its E8M0 scale rows
+  uint64_t moe_wstride;  // OP_MOE_*: bytes between experts' weight matrices (W / W2 are expert 0's)
 };
 static_assert(sizeof(Op) == 128, "Op must stay 128 bytes");
 // stream elements per row of a GEMV op: 16-bit weights, pairs of fp8 codes, or quads of fp4 codes
@@ -166,6 +170,7 @@ struct KArgs {
   int32_t nh, dk, dv, C, convw;
   int32_t n_cus, n_items;     // attention work items per attention layer
   int32_t mix;                // floats between batch rows of the attention / delta output
+  int32_t n_experts, top_k;   // mixture-of-experts MLPs (0: dense)
   float rms_eps;
   // per launch
   const int32_t* tokens;

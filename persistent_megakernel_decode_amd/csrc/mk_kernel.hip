@@ -69,6 +69,10 @@ __shared__ u32 g_bcast[4];
 // The step the compute waves are on (a launch may run several decode steps, each consuming the
 // previous step's greedy token): its activation tag, its index (the loader streams step s only once
 // the compute waves are on it) and its tokens.
+// mixture of experts: the running expert's weight per sequence, and the down projection's sums over
+// the chosen experts (sequence b, row r of the op at [b * 64 NC + r]; each row owned by one thread)
+__shared__ float g_moew[4];
+__shared__ __attribute__((aligned(16))) float g_moeacc[4 * 64 * NC];
 __shared__ u32 g_ctag;
 __shared__ u32 g_cstep;
 __shared__ int g_tok[APLAN_MAXB];
@@ -380,6 +384,45 @@ __device__ __forceinline__ float tagged_fix(const KArgs& A, const float* p, floa
   return v;
 }
 __device__ __forceinline__ float ld_tagged(const KArgs& A, const float* p) { return tagged_fix(A, p, ld_sc1(p)); }
+
+// Mixture-of-experts routing of one sequence.  Lane e holds expert e's router logit z (valid: e <
+// n_experts): the k largest are chosen one at a time (the lowest lane among equal maxima), and the
+// chosen experts' weights are the softmax of their logits, i.e. the softmax over every expert
+// renormalised over the chosen.  Returns the chosen lanes as a mask and this lane's weight in *wl
+// (0 unless chosen).  NaN logits are never chosen.
+__device__ __forceinline__ uint64_t moe_choose(float z, bool valid, int k, float* wl) {
+  const u32 lane = lane_id();
+  uint64_t chosen = 0;
+  for (int j = 0; j < k; ++j) {
+    const bool open = valid && !((chosen >> lane) & 1ull);
+    const float mx = wave_max(open ? z : -INFINITY);
+    const uint64_t at = __builtin_amdgcn_ballot_w64(open && z == mx);
+    if (at == 0) break;
+    chosen |= at & (~at + 1ull);
+  }
+  const bool mine = (chosen >> lane) & 1ull;
+  const float top = wave_max(mine ? z : -INFINITY);
+  const float ex = mine ? __expf(z - top) : 0.0f;
+  const float s = wave_sum(ex);
+  *wl = mine ? ex / s : 0.0f;
+  return chosen;
+}
+// Sequence b's router logits of this step: lane e reads expert e's, re-reading until every one shows
+// the step's parity.  Returns false at the watchdog limit or on abort.
+template <bool LOADER>
+__device__ __forceinline__ bool moe_logits(const KArgs& A, const float* router, int b, u32 par, float* z) {
+  const u32 lane = lane_id(), E = (u32)A.n_experts;
+  const float* p = router + (size_t)b * E + lane;
+  float v = lane < E ? ld_sc1(p) : 0.0f;
+  Watchdog wd(A);
+  while (__builtin_amdgcn_ballot_w64(lane < E && !tag_ok(v, par)) != 0) {
+    if ((LOADER ? aborted_loader() : aborted()) || wd.expired()) return false;
+    __builtin_amdgcn_s_sleep(1);
+    if (lane < E) v = ld_sc1(p);
+  }
+  *z = v;
+  return true;
+}
 // row_ok[b] holds tag << 1 | ok, written once per step by EMBED: wait for this step's entry.
 __device__ __forceinline__ bool row_ok_wait(const KArgs& A, int b) {
   const u32 want = ctag() & 0x7FFFFFFFu;
@@ -770,20 +813,11 @@ __device__ __forceinline__ u32 loader_ops(KPtr ap, u32 q0, u32 q1, u32 seq, u32 
   const AttnLanes al = attn_lanes(A.d == 64 ? 64u : 128u);
   attn_plan_build(A, A.d == 64 ? 32 : 16, step);
   ItemCache ic;
-  for (u32 oi = q0; oi < q1; ++oi) {
-    const KArgs& A = kref(ap);
-    const Op o = sload(A.ops + oi);
-    const u32 ns = op_slots(A, o, ic);
 #if MK_TRACE_STAMPS
-    u32 tr_first = (u32)__builtin_amdgcn_s_memrealtime(), tr_blocked = 0;
-    if (ns == 0) {
-      u32* ld = g_ldtr + (oi % LDTR_OPS) * 3;
-      loader_lds_store(ld, tr_first);
-      loader_lds_store(ld + 1, tr_first);
-      loader_lds_store(ld + 2, 0u);
-    }
+  u32 tr_first = 0, tr_blocked = 0;
 #endif
-    if (ns == 0) continue;
+  // every ring slot of one op (an expert's GEMV for a mixture-of-experts op); false on abort
+  auto issue_op = [&](const KArgs& A, const Op& o, u32 ns) -> bool {
     LayerDesc Ld{};
     AttnItem it{};
     const GemvSeg gsg = gemv_seg(o);
@@ -809,7 +843,7 @@ __device__ __forceinline__ u32 loader_ops(KPtr ap, u32 q0, u32 q1, u32 seq, u32 
           if (marked == seq) {
             if (aborted_loader() || wd.expired()) {
               __builtin_amdgcn_s_waitcnt(MK_VMCNT(0));
-              return ~0u;
+              return false;
             }
             __builtin_amdgcn_s_sleep(1);
           }
@@ -837,6 +871,51 @@ __device__ __forceinline__ u32 loader_ops(KPtr ap, u32 q0, u32 q1, u32 seq, u32 
         __builtin_amdgcn_s_waitcnt(MK_VMCNT(8 * LOAD_DEPTH));
         publish_filled(++marked);
       }
+    }
+    return true;
+  };
+  for (u32 oi = q0; oi < q1; ++oi) {
+    const KArgs& A = kref(ap);
+    const Op o = sload(A.ops + oi);
+    const bool moe = o.opcode == OP_MOE_GU || o.opcode == OP_MOE_DOWN;
+    const u32 ns = moe ? 0u : op_slots(A, o, ic);
+#if MK_TRACE_STAMPS
+    tr_first = (u32)__builtin_amdgcn_s_memrealtime();
+    tr_blocked = 0;
+    if (ns == 0) {
+      u32* ld = g_ldtr + (oi % LDTR_OPS) * 3;
+      loader_lds_store(ld, tr_first);
+      loader_lds_store(ld + 1, tr_first);
+      loader_lds_store(ld + 2, 0u);
+    }
+#endif
+    if (moe) {
+      // The router's choice decides which experts' rows to stream.  Publish every slot issued so far
+      // first (a compute wave may need them to finish the router itself), then wait for the logits.
+      while (marked < seq) {
+        wait_oldest(seq - marked);
+        publish_filled(++marked);
+      }
+      const u32 par = lds_ld_loader(&g_ctag) & 1u;
+      uint64_t any = 0;
+      for (int b = 0; b < A.batch && b < 4; ++b) {
+        float z, wl;
+        const bool ok = moe_logits<true>(A, (const float*)o.Ws, b, par, &z);
+        if (!__builtin_amdgcn_readfirstlane((int)ok)) return ~0u;
+        any |= moe_choose(z, lane_id() < (u32)A.n_experts, A.top_k, &wl);
+      }
+      any = uni64(any);
+      for (uint64_t mset = any; mset; mset &= mset - 1) {
+        const u32 e = __builtin_amdgcn_readfirstlane((u32)__builtin_ctzll(mset));
+        Op oe = o;
+        oe.opcode = OP_GEMV;
+        oe.W = o.W + e * o.moe_wstride;
+        oe.W2 = o.W2 ? o.W2 + e * o.moe_wstride : 0;
+        if (!issue_op(A, oe, op_slots(A, oe, ic))) return ~0u;
+      }
+    } else {
+      if (ns == 0) continue;
+      if (!issue_op(A, o, ns)) return ~0u;
     }
 #if MK_TRACE_STAMPS
     {
@@ -1268,6 +1347,14 @@ struct GemvAcc<1, 8> {
   }
 };
 
+// A mixture-of-experts op's run of one expert through the GEMV path: byte offsets of that expert's
+// input and output blocks, and acc = 1 for the down projection's weighted sum in LDS (EPI_MOE_ACC).
+// (The loader applies the expert's weight offset itself; uniform values.)
+struct MoeX {
+  uint64_t din = 0, dout = 0;
+  u32 acc = 0;
+};
+
 // An MX E8M0 scale byte as fp32: 2^(e - 127); 0 is 2^-127 (an fp32 subnormal), 0xFF NaN
 __device__ __forceinline__ float e8m0f(u32 e) {
   return e == 0xFFu ? __builtin_nanf("") : __builtin_bit_cast(float, e ? e << 23 : 0x00400000u);
@@ -1289,7 +1376,7 @@ __device__ __forceinline__ float e8m0f(u32 e) {
 // op's scale rows (one byte per block; a batch of groups' scales is fetched while the batch before
 // it computes).  Each fragment is 32 fp32 inputs; the block sum is scaled inside the loop.
 template <int B, int P, int NF, bool AM, bool F8 = false, bool F4 = false>  // AM: track the LM head's greedy partials (multi-step kernels)
-__device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
+__device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen, const MoeX mx = MoeX{}) {
   static_assert(!F8 || NF <= 4, "fp8 weights: at most 4 input fragments per wave");
   static_assert(!F4 || (B == 1 && NF <= 2 && !F8), "fp4 weights: one sequence, at most 2 input fragments per wave");
   constexpr u32 R = 16 / P, KP = 32 * P;
@@ -1298,12 +1385,12 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   constexpr u32 XN = 8 * EM;                    // inputs per fragment
   const u32 lane = lane_id();
   // the Op's fields as independent scalars (see op_mmv)
-  const u32 epi = opq((u32)o.epi), norm = opq((u32)o.norm), flags = opq(o.flags), nrows = opq(o.nrows);
-  const u32 pg = opq(o.ppr), K = opq(o.K), row0 = opq(o.row0);
+  const u32 epi = mx.acc ? (u32)EPI_MOE_ACC : opq((u32)o.epi), norm = opq((u32)o.norm), flags = opq(o.flags);
+  const u32 nrows = opq(o.nrows), pg = opq(o.ppr), K = opq(o.K), row0 = opq(o.row0);
   const u32 kv = K / EM;  // stream elements per row
   const u32 nslots = opq(o.nslots) - (norm ? gain_slots(K) : 0u);  // weight slots (after the gain's)
   const u32 ld_in = opq(o.ld_in), ld_out = opq(o.ld_out);
-  const uint64_t in = opq(o.in), outp = opq(o.out), resp = opq(o.res);
+  const uint64_t in = opq(o.in) + mx.din, outp = opq(o.out) + mx.dout, resp = opq(o.res);
   const bool swiglu = epi == EPI_SWIGLU;
   const u32 nrt = swiglu ? 2 * nrows : nrows;  // stream rows
   const u32 nrg = nrt / R;                      // row groups
@@ -1696,6 +1783,8 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
         const float* rp = (const float*)resp + (size_t)b * ld_out + row;
         const float x = tagged_fix(A, rp, r == tid ? rv[b] : ld_sc1(rp));
         st_tag((float*)outp + (size_t)b * ld_out + row, x + v, par);
+      } else if (epi == EPI_MOE_ACC) {  // this expert's share of the rows (one thread per row)
+        g_moeacc[b * 64 * NC + r] += g_moew[b] * v;
       } else if (epi == EPI_STORE) {
         st_tag((float*)outp + (size_t)b * ld_out + row, v, par);
       } else if (b < A.batch) {  // EPI_LOGITS
@@ -1725,7 +1814,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
 
 // WF: the kernel's projection weight format (WF_BF16, WF_FP8, WF_FP4); the LM head stays bf16
 template <int B, bool AM, int WF>
-__device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
+__device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen, const MoeX mx = MoeX{}) {
   constexpr int P = GemvWidth<B>::P;
   const u32 pg = o.ppr;
   if constexpr (WF == WF_FP4 && B == 1) {
@@ -1741,9 +1830,78 @@ __device__ __forceinline__ bool op_gemv(const KArgs& A, const Op& o, u32 w, u32&
       return op_gemv_nf<B, P, 4, AM, true>(A, o, w, seq, gen);
     }
   }
-  if (pg <= 8) return op_gemv_nf<B, P, 1, AM>(A, o, w, seq, gen);
-  if (pg == 16) return op_gemv_nf<B, P, 2, AM>(A, o, w, seq, gen);
-  return op_gemv_nf<B, P, 8, AM>(A, o, w, seq, gen);
+  if (pg <= 8) return op_gemv_nf<B, P, 1, AM>(A, o, w, seq, gen, mx);
+  if (pg == 16) return op_gemv_nf<B, P, 2, AM>(A, o, w, seq, gen, mx);
+  return op_gemv_nf<B, P, 8, AM>(A, o, w, seq, gen, mx);
+}
+
+// Mixture-of-experts op: a row tile of every expert, run for the experts the router chose (the
+// loader streams exactly their rows, in the same order).  Gate / up: each chosen expert's SwiGLU rows
+// by an ordinary GEMV, and zeros for the experts nobody chose, so that every expert's rows are
+// written once per step (a later step's poll then never meets an earlier step's value).  Down: each
+// chosen expert's rows times its weight per sequence summed in LDS, then x = residual + sum, tagged.
+template <int B, bool AM, int WF>
+__device__ __forceinline__ bool op_moe(const KArgs& A, const Op& o, u32 w, u32& seq, u32& gen) {
+  static_assert(B <= 4, "mixture-of-experts ops run at most 4 sequences");
+  const bool gu = o.opcode == OP_MOE_GU;
+  const u32 lane = lane_id(), tid = w * 64 + lane, par = ctag() & 1u;
+  const u32 nrows = o.nrows, row0 = o.row0, ld_out = o.ld_out;
+  uint64_t any = 0;
+  float wl[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    wl[b] = 0.0f;
+    if (b >= A.batch) continue;
+    float z;
+    const bool ok = moe_logits<false>(A, (const float*)o.Ws, b, par, &z);
+    if (!__builtin_amdgcn_readfirstlane((int)ok)) return false;
+    any |= moe_choose(z, lane < (u32)A.n_experts, A.top_k, &wl[b]);
+  }
+  any = uni64(any);  // (a ballot: uniform; restated for the divergence analysis)
+  if (gu) {
+    for (u32 e = 0; e < (u32)A.n_experts; ++e) {
+      if ((any >> e) & 1ull) continue;
+      float* out = (float*)(o.out + (uint64_t)e * o.moe_xstride);
+      for (u32 r = tid; r < nrows; r += NC * 64)
+#pragma unroll
+        for (int b = 0; b < B; ++b) st_tag(out + (size_t)b * ld_out + row0 + r, 0.0f, par);
+    }
+    for (uint64_t mset = any; mset; mset &= mset - 1) {
+      const u32 e = __builtin_amdgcn_readfirstlane((u32)__builtin_ctzll(mset));
+      MoeX mx;
+      mx.dout = (uint64_t)e * opq(o.moe_xstride);
+      const bool alive = op_gemv<B, AM, WF>(A, o, w, seq, gen, mx);
+      seq = __builtin_amdgcn_readfirstlane(seq);
+      gen = __builtin_amdgcn_readfirstlane(gen);
+      if (!__builtin_amdgcn_readfirstlane((int)alive) || !cbar(A, gen)) return false;
+    }
+    return true;
+  }
+  if (tid < nrows)
+#pragma unroll
+    for (int b = 0; b < B; ++b) g_moeacc[b * 64 * NC + tid] = 0.0f;
+  for (uint64_t mset = any; mset; mset &= mset - 1) {
+    const u32 e = __builtin_amdgcn_readfirstlane((u32)__builtin_ctzll(mset));
+    if (w == 0 && lane == 0)
+#pragma unroll
+      for (int b = 0; b < B; ++b) g_moew[b] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl[b]), e));
+    MoeX mx;
+    mx.din = (uint64_t)e * opq(o.moe_xstride);
+    mx.acc = 1;
+    const bool alive = op_gemv<B, AM, WF>(A, o, w, seq, gen, mx);
+    seq = __builtin_amdgcn_readfirstlane(seq);
+    gen = __builtin_amdgcn_readfirstlane(gen);
+    if (!__builtin_amdgcn_readfirstlane((int)alive) || !cbar(A, gen)) return false;
+  }
+  if (tid < nrows) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float* rp = (const float*)o.res + (size_t)b * ld_out + row0 + tid;
+      const float x = ld_tagged(A, rp);
+      st_tag((float*)o.out + (size_t)b * ld_out + row0 + tid, x + g_moeacc[b * 64 * NC + tid], par);
+    }
+  }
+  return true;
 }
 
 // ------------------------------------------------------------------ MATRIX-CORE GEMV (batch 8)
@@ -2602,6 +2760,10 @@ __device__ __forceinline__ bool op_loop(KPtr ap, u32 q0, u32 q1, u32 w, u32& seq
           else alive = op_mmv<B, AM>(A, o, w, seq, gen);
         }
         break;
+      case OP_MOE_GU:
+      case OP_MOE_DOWN:
+        if constexpr (WF == WF_MOE && B <= 4) alive = op_moe<B, AM, WF_BF16>(A, o, w, seq, gen);
+        break;
       case OP_ATTN: alive = A.d == 128 ? op_attn<128>(A, o, w, seq, gen, ic) : op_attn<64>(A, o, w, seq, gen, ic); break;
       case OP_DELTA: alive = A.dk == 128 ? op_delta<128>(A, o, w, seq, gen) : op_delta<64>(A, o, w, seq, gen); break;
       default: break;
@@ -2739,6 +2901,9 @@ extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b2_f8)(mk
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b4_f8)(mk::KArgs A) { mk::megakernel_body<4, false, mk::WF_FP8>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b8_f8)(mk::KArgs A) { mk::megakernel_body<8, false, mk::WF_FP8>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b1_f4)(mk::KArgs A) { mk::megakernel_body<1, false, mk::WF_FP4>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b1_moe)(mk::KArgs A) { mk::megakernel_body<1, false, mk::WF_MOE>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b2_moe)(mk::KArgs A) { mk::megakernel_body<2, false, mk::WF_MOE>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) MK_KNAME(b4_moe)(mk::KArgs A) { mk::megakernel_body<4, false, mk::WF_MOE>(A); }
 #if !MK_TRACE_STAMPS
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b1(mk::KArgs A) { mk::megakernel_body<1, true>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b2(mk::KArgs A) { mk::megakernel_body<2, true>(A); }
@@ -2749,4 +2914,7 @@ extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_step
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b4_f8(mk::KArgs A) { mk::megakernel_body<4, true, mk::WF_FP8>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b8_f8(mk::KArgs A) { mk::megakernel_body<8, true, mk::WF_FP8>(A); }
 extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b1_f4(mk::KArgs A) { mk::megakernel_body<1, true, mk::WF_FP4>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b1_moe(mk::KArgs A) { mk::megakernel_body<1, true, mk::WF_MOE>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b2_moe(mk::KArgs A) { mk::megakernel_body<2, true, mk::WF_MOE>(A); }
+extern "C" __global__ void __launch_bounds__(mk::NTHREADS, 1) mk_megakernel_steps_b4_moe(mk::KArgs A) { mk::megakernel_body<4, true, mk::WF_MOE>(A); }
 #endif

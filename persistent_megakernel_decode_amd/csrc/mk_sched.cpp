@@ -54,6 +54,13 @@ std::string validate_desc(const mk_model_desc* desc, ModelShape* out, mk_status*
   if (d.weight_format == MK_WEIGHTS_FP8_E4M3) {
     if (d.hidden % 16 || d.ffn % 16) return "fp8 weights need hidden and ffn to be multiples of 16";
   }
+  if (d.n_experts < 0 || d.n_experts > 64) return "n_experts must be 0 to 64";
+  if (d.n_experts > 0) {
+    if (d.top_k < 1 || d.top_k > 8 || d.top_k > d.n_experts) return "top_k must be 1 to min(8, n_experts)";
+    if (d.n_experts % 4) return "n_experts must be a multiple of 4";
+    if (d.weight_format != MK_WEIGHTS_BF16) return "mixture-of-experts models take bf16 weights";
+    if (d.max_batch > 4) return "mixture-of-experts models run at most 4 sequences per step";
+  }
   if (d.weight_format == MK_WEIGHTS_FP4_MX) {
     if (d.max_batch != 1) return "fp4 weights run one sequence per step (max_batch 1)";
     if (d.hidden % 32 || d.ffn % 32) return "fp4 weights need hidden and ffn to be multiples of 32";
@@ -108,6 +115,14 @@ struct RowScales {
   uint64_t s[3] = {0, 0, 0};
 };
 
+// A mixture-of-experts stage: each op is one row tile of every expert (W / W2 expert 0's rows, the
+// others moe_wstride bytes apart); the kernel runs it for the experts the router chose.
+struct MoeOp {
+  uint8_t opcode = 0;  // OP_MOE_GU or OP_MOE_DOWN (0: an ordinary GEMV stage)
+  uint64_t router = 0, wstride = 0;
+  uint32_t xstride = 0;
+};
+
 struct Builder {
   const ModelShape& m;
   Plan& P;
@@ -124,7 +139,7 @@ struct Builder {
   // are fp8 codes and sc.s the fp32 row scales of each run.
   void gemv(int stage, int wait, int layer, uint32_t N, uint32_t K, uint8_t epi, bool norm, uint64_t W, uint64_t W2,
             uint64_t W3, uint32_t b1, uint32_t b2, uint64_t in, uint32_t ld_in, uint64_t gamma, uint64_t out,
-            uint32_t ld_out, uint64_t res, const RowScales& sc = RowScales{}) {
+            uint32_t ld_out, uint64_t res, const RowScales& sc = RowScales{}, const MoeOp& moe = MoeOp{}) {
     if (!err.empty()) return;
     const int B = P.kernel_batch;
     if (sc.f8 && K % 16) {
@@ -159,6 +174,7 @@ struct Builder {
     const int RW = std::min(pg, 8);
     const int mult = epi == EPI_SWIGLU ? 2 : 1;
     uint32_t maxrows = (uint32_t)(RED_FLOATS / (RW * B * mult));
+    if (moe.opcode) maxrows = std::min<uint32_t>(maxrows, 64 * NC);  // (one accumulator row per compute thread)
     maxrows -= maxrows % R;
     // tiles of whole row groups, as even as the groups allow
     const uint32_t NG = N / R;
@@ -220,6 +236,12 @@ struct Builder {
         }
       }
       o.in = in; o.gamma = gamma; o.out = out; o.res = res;
+      if (moe.opcode) {
+        o.opcode = moe.opcode;
+        o.Ws = moe.router;
+        o.moe_wstride = moe.wstride;
+        o.moe_xstride = moe.xstride;
+      }
       stage_ops[stage].push_back(o);
       }
     }
@@ -368,7 +390,8 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
     Q.tickets = take(Y.tickets_bytes_per_layer);
     Q.mix_o = take((size_t)B * P.mix_dim * 4);
     Q.x_mix = take((size_t)B * H * 4);
-    Q.m = take((size_t)B * F * 4);
+    Q.m = take((size_t)std::max(1, d.n_experts) * B * F * 4);  // (one row block per expert)
+    Q.router = take((size_t)B * std::max(1, d.n_experts) * 4);
     Q.x_out = take((size_t)B * H * 4);
   }
   // multi-step launches: the tag of the last step each CU has finished (cleared with the
@@ -453,6 +476,30 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
               scales(lw ? lw->wo_delta_scale : nullptr));
       ++id;
     }
+    if (d.n_experts > 0) {
+      // mixture of experts: router logits, then every chosen expert's gate / up and down rows
+      const uint32_t E = (uint32_t)d.n_experts;
+      const int s_rt = bd.new_stage();
+      bd.gemv(s_rt, s_mix, l, E, (uint32_t)H, EPI_STORE, true, lw ? wptr(lw->w_router) : 0, 0, 0, (uint32_t)NONE,
+              (uint32_t)NONE, ws(Q.x_mix), (uint32_t)H, lw ? wptr(lw->mlp_norm) : 0, ws(Q.router), E, 0);
+      MoeOp mo;
+      mo.router = ws(Q.router);
+      mo.wstride = (uint64_t)F * H * 2;
+      mo.xstride = (uint32_t)((size_t)B * F * 4);
+      mo.opcode = OP_MOE_GU;
+      const int s_gu = bd.new_stage();
+      bd.gemv(s_gu, s_rt, l, (uint32_t)F, (uint32_t)H, EPI_SWIGLU, true, lw ? wptr(lw->w_gate) : 0,
+              lw ? wptr(lw->w_up) : 0, 0, (uint32_t)NONE, (uint32_t)NONE, ws(Q.x_mix), (uint32_t)H,
+              lw ? wptr(lw->mlp_norm) : 0, ws(Q.m), (uint32_t)F, 0, RowScales{}, mo);
+      mo.opcode = OP_MOE_DOWN;
+      const int s_down = bd.new_stage();
+      bd.gemv(s_down, s_gu, l, (uint32_t)H, (uint32_t)F, EPI_RESID, false, lw ? wptr(lw->w_down) : 0, 0, 0,
+              (uint32_t)NONE, (uint32_t)NONE, ws(Q.m), (uint32_t)F, 0, ws(Q.x_out), (uint32_t)H, ws(Q.x_mix),
+              RowScales{}, mo);
+      prev = s_down;
+      x_in = ws(Q.x_out);
+      continue;
+    }
     const int s_gu = bd.new_stage();
     bd.gemv(s_gu, s_mix, l, (uint32_t)F, (uint32_t)H, EPI_SWIGLU, true, lw ? wptr(lw->w_gate) : 0,
             lw ? wptr(lw->w_up) : 0, 0, (uint32_t)NONE, (uint32_t)NONE, ws(Q.x_mix), (uint32_t)H,
@@ -484,14 +531,15 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
       Op o = ops[j];
       o.sig_index = (uint32_t)j;
       const int cu = (int)(j % (size_t)n_cus);
-      if (o.opcode == OP_GEMV || o.opcode == OP_MMV) {
+      if (o.opcode == OP_GEMV || o.opcode == OP_MMV || o.opcode == OP_MOE_GU || o.opcode == OP_MOE_DOWN) {
         // streamed weight bytes: 2 per bf16 weight; 1 per fp8 code plus 4 per fp32 row scale; half
         // a byte per fp4 code plus one scale byte per 32 codes
         const double rows = (double)o.nrows * (o.epi == EPI_SWIGLU ? 2 : 1);
         const double bytes = (o.flags & OPF_FP8) ? rows * (o.K + 4.0)
                            : (o.flags & OPF_FP4) ? rows * (o.K / 2.0 + o.K / 32.0) : rows * o.K * 2;
-        P.cu_bytes[cu] += bytes;
-        P.weight_bytes += bytes;
+        const bool moe = o.opcode == OP_MOE_GU || o.opcode == OP_MOE_DOWN;  // (every expert's rows)
+        P.cu_bytes[cu] += moe ? bytes * m.d.n_experts : bytes;
+        P.weight_bytes += moe ? bytes * m.d.n_experts : bytes;
       }
       q[cu].push_back(o);
     }
@@ -508,8 +556,10 @@ std::string build_plan(const ModelShape& m, int n_cus, const mk_weights* w, cons
       for (Op& o : qc) {
         if (o.wait_stage == NO_STAGE) continue;
         const uint8_t pop = bd.stage_ops[o.wait_stage][0].opcode;
-        const bool tagged_src = pop == OP_EMBED || pop == OP_GEMV || pop == OP_MMV || pop == OP_ATTN || pop == OP_DELTA;
-        const bool tagged_dst = o.opcode == OP_GEMV || o.opcode == OP_MMV || o.opcode == OP_ATTN || o.opcode == OP_DELTA;
+        const bool tagged_src = pop == OP_EMBED || pop == OP_GEMV || pop == OP_MMV || pop == OP_ATTN || pop == OP_DELTA ||
+                                pop == OP_MOE_GU || pop == OP_MOE_DOWN;
+        const bool tagged_dst = o.opcode == OP_GEMV || o.opcode == OP_MMV || o.opcode == OP_ATTN || o.opcode == OP_DELTA ||
+                                o.opcode == OP_MOE_GU || o.opcode == OP_MOE_DOWN;
         if (tags && tagged_src && tagged_dst) o.flags |= OPF_TAGGED_IN;
         else counted[o.wait_stage] = 1;
       }
@@ -551,6 +601,7 @@ void relocate(Plan* plan, uint64_t base) {
     o.in = reloc(o.in, base);
     o.out = reloc(o.out, base);
     o.res = reloc(o.res, base);
+    if (o.opcode == OP_MOE_GU || o.opcode == OP_MOE_DOWN) o.Ws = reloc(o.Ws, base);  // the router logits
   }
   for (LayerDesc& D : plan->layers) {
     D.qkv = reloc(D.qkv, base);
@@ -559,6 +610,21 @@ void relocate(Plan* plan, uint64_t base) {
     D.tickets = reloc(D.tickets, base);
     D.mix_o = reloc(D.mix_o, base);
   }
+}
+
+std::string unrelocated(const Plan& P) {
+  for (size_t i = 0; i < P.ops.size(); ++i) {
+    const Op& o = P.ops[i];
+    for (uint64_t v : {o.W, o.W2, o.Ws, o.Ws2, o.in, o.gamma, o.out, o.res})
+      if (v & WS_TAG) return fmt("op %zu (opcode %u) keeps a workspace-relative address", i, (unsigned)o.opcode);
+  }
+  for (size_t l = 0; l < P.layers.size(); ++l) {
+    const LayerDesc& D = P.layers[l];
+    for (uint64_t v : {D.qkv, D.gates, D.q_norm, D.k_norm, D.k_pages, D.v_pages, D.part, D.tickets, D.mix_o, D.conv_w,
+                       D.conv_state, D.delta_state})
+      if (v & WS_TAG) return fmt("layer %zu keeps a workspace-relative address", l);
+  }
+  return "";
 }
 
 int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
@@ -583,7 +649,13 @@ int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
         bad(fmt("cu %d op %u: polls tagged inputs it cannot check", c, i));
       seen[o.sig_stage]++;
       idx[o.sig_stage].push_back(o.sig_index);
-      if (o.opcode == OP_GEMV) {
+      if (o.opcode == OP_MOE_GU || o.opcode == OP_MOE_DOWN) {
+        const bool gu = o.opcode == OP_MOE_GU;
+        if (m.d.n_experts < 1 || !o.Ws || (gu ? o.epi != EPI_SWIGLU : o.epi != EPI_RESID) || o.nrows > 64u * NC ||
+            (o.flags & (OPF_FP8 | OPF_FP4)) || o.moe_xstride < (uint64_t)P.kernel_batch * m.d.ffn * 4)
+          bad(fmt("cu %d op %u: mixture-of-experts op", c, i));
+      }
+      if (o.opcode == OP_GEMV || o.opcode == OP_MOE_GU || o.opcode == OP_MOE_DOWN) {
         const uint32_t mult = o.epi == EPI_SWIGLU ? 2 : 1;
         const uint32_t Pp = o.part, R = Pp ? 16 / Pp : 1, pg = o.ppr;
         const uint32_t RW = std::min<uint32_t>(pg, 8);
@@ -644,7 +716,10 @@ int check_plan(const ModelShape& m, const Plan& P, std::string* why) {
   };
   double want = (double)d.vocab * d.hidden * 2;  // the LM head stays bf16
   for (int l = 0; l < d.n_layers; ++l) {
-    want += 2 * pbytes(d.ffn, d.hidden) + pbytes(d.hidden, d.ffn);
+    if (d.n_experts > 0)  // router plus every expert
+      want += pbytes(d.n_experts, d.hidden) + d.n_experts * (2 * pbytes(d.ffn, d.hidden) + pbytes(d.hidden, d.ffn));
+    else
+      want += 2 * pbytes(d.ffn, d.hidden) + pbytes(d.hidden, d.ffn);
     if (m.kinds[l] == MK_LAYER_ATTN)
       want += pbytes((double)(d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim, d.hidden) +
               pbytes(d.hidden, (double)d.n_q_heads * d.head_dim);

@@ -21,6 +21,7 @@ struct Layout {
   int win_pages_per_row = 0;
   struct PerLayer {
     size_t qkv = 0, part = 0, tickets = 0, mix_o = 0, x_mix = 0, m = 0, x_out = 0;
+    size_t router = 0;  // mixture of experts: router logits fp32 [B][n_experts]
   };
   std::vector<PerLayer> layer;
   size_t counters_bytes = 0, tickets_bytes_per_layer = 0;
@@ -67,6 +68,8 @@ void relocate(Plan* plan, uint64_t workspace_base);
 // Structural checks (stage order, coverage, capacities).  Returns the number of violations and
 // appends their descriptions to `why`.
 int check_plan(const ModelShape& m, const Plan& plan, std::string* why);
+// After relocate(): the first op or layer field still holding a workspace-relative address, or "".
+std::string unrelocated(const Plan& plan);
 
 // Replays the compiled queues over a launch sequence on the CPU (mk_emu.cpp).  Fills *rep and
 // returns a description of the first problems found ("" when none).

@@ -36,6 +36,9 @@ GREEDY_GAP = 1e-2      # greedy ids must agree wherever the oracle's top-2 logit
 MID_TOL = 2e-3         # normwise relative error of per-layer mid-states (fp32 activations)
 STATE_OP_TOL = 1e-5    # delta-rule S from the GPU's own inputs (fp32 update of fp32 state)
 STATE_RUN_TOL = 1e-4   # GPU S / conv state against the oracle's own trajectory
+ROUTE_GAP = 1e-2       # mixture of experts: the oracle's own top-k choice must be the GPU's wherever its
+                       # k-th and (k+1)-th router logits differ by more than this (the oracle then runs
+                       # the GPU's choice, as both sides consume the GPU's greedy token)
 
 
 def say(msg: str) -> None:
@@ -65,6 +68,8 @@ class ParityReport:
     conv_checked: int = 0
     greedy_checked: int = 0
     greedy_agree: int = 0
+    route_checked: int = 0   # (layer, sequence) routing choices compared (oracle's k-th margin > ROUTE_GAP)
+    route_agree: int = 0
     failures: List[str] = field(default_factory=list)
 
 
@@ -127,20 +132,41 @@ def run_parity(cfg: synth.Config, steps: int, mid: bool = True, device: str = "c
         g = gpu.logits[:nb].cpu().numpy()
         gmid = {}
         do_mid = mid and step % mid_every == 0
+        moe = cfg.n_experts > 0
+        if moe:  # the GPU's router logits and the experts it chose from them, fed to the oracle
+            E, k = cfg.n_experts, cfg.top_k
+            glog = np.stack([gpu.midstate(6, l, E, nb).cpu().numpy() for l in range(cfg.n_layers)])
+            gsel = np.array([[oracle.moe_select(glog[l, b], k) for b in range(nb)] for l in range(cfg.n_layers)],
+                            dtype=np.int32)
         if do_mid:
             H, F, X = cfg.hidden, cfg.ffn, orc.mix_dim
             for l in range(cfg.n_layers):
                 gmid[("x_mixer", l)] = gpu.midstate(0, l, H, nb).cpu().numpy()
                 gmid[("x_mlp", l)] = gpu.midstate(1, l, H, nb).cpu().numpy()
                 gmid[("mixer_o", l)] = gpu.midstate(2, l, X, nb).cpu().numpy()
-                gmid[("mlp_m", l)] = gpu.midstate(3, l, F, nb).cpu().numpy()
+                if moe:
+                    gmid[("router", l)] = glog[l]
+                else:
+                    gmid[("mlp_m", l)] = gpu.midstate(3, l, F, nb).cpu().numpy()
         if dls:
             s_new = gpu.delta_state.cpu().numpy()
             c_new = gpu.conv_state.cpu().numpy()
             proj = {l: gpu.midstate(4, l, C + 2 * cfg.n_delta_heads, nb).cpu().numpy() for l in dls}
             mixo = {l: gpu.midstate(2, l, orc.mix_dim, nb).cpu().numpy() for l in dls}
         t0 = time.time()
-        o, omid = orc.step(toks[:nb], pos, lens, dump=True)
+        o, omid = orc.step(toks[:nb], pos, lens, dump=True, force_experts=gsel if moe else None)
+        if moe:  # where the oracle's own choice is clear, it must be the GPU's
+            for l in range(cfg.n_layers):
+                for b in range(nb):
+                    srt = np.sort(omid["router"][l, b])[::-1]
+                    if k < E and float(srt[k - 1] - srt[k]) <= ROUTE_GAP:
+                        continue
+                    rep.route_checked += 1
+                    if sorted(omid["sel"][l, b].tolist()) == sorted(gsel[l, b].tolist()):
+                        rep.route_agree += 1
+                    else:
+                        rep.failures.append(f"step {step} layer {l} row {b}: experts {sorted(gsel[l, b].tolist())} "
+                                            f"!= the oracle's {sorted(omid['sel'][l, b].tolist())}")
         say(f"[{cfg.name}] step {step}: oracle {time.time() - t0:.2f}s")
         for b in range(nb):
             rel = float(np.max(np.abs(g[b].astype(np.float64) - o[b])) / np.max(np.abs(o[b])))

@@ -26,11 +26,11 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header_layout():
-    # mk_model_desc is 96 bytes (weight_format last, at 92); the library itself rejects any
-    # struct_size other than its own sizeof (see test_host_rejects_out_of_contract_descriptions)
-    assert ctypes.sizeof(mkd.mk_model_desc) == 96
-    assert mkd.mk_model_desc.weight_format.offset == 92
-    assert ctypes.sizeof(mkd.mk_layer_weights) == (15 + 10) * 8  # 15 tensors, 10 fp8 row-scale pointers
+    # mk_model_desc is 104 bytes (weight_format at 92, n_experts and top_k last); the library itself
+    # rejects any struct_size other than its own sizeof (see test_host_rejects_out_of_contract_descriptions)
+    assert ctypes.sizeof(mkd.mk_model_desc) == 104
+    assert mkd.mk_model_desc.weight_format.offset == 92 and mkd.mk_model_desc.top_k.offset == 100
+    assert ctypes.sizeof(mkd.mk_layer_weights) == (15 + 10 + 1) * 8  # 15 tensors, 10 scale pointers, the router
     assert ctypes.sizeof(mkd.mk_kv_cache) == 48
 
 
@@ -40,7 +40,8 @@ def _desc(cfg, max_ctx):
                          s["head_dim"], s["qk_norm"], s["tied"], s["rms_eps"], s["rope_base"], s["layer_kinds"],
                          s["max_batch"], s["max_ctx"], s["n_delta_heads"], s["delta_dk"], s["delta_dv"],
                          s["conv_width"], weight_format={"fp8": mkd.MK_WEIGHTS_FP8_E4M3,
-                                                         "fp4": mkd.MK_WEIGHTS_FP4_MX}.get(cfg.weights, 0))
+                                                         "fp4": mkd.MK_WEIGHTS_FP4_MX}.get(cfg.weights, 0),
+                         n_experts=cfg.n_experts, top_k=cfg.top_k)
 
 
 def _proj_bytes(cfg, per_weight, per_row):
@@ -158,3 +159,25 @@ def test_fp4_refuses_more_than_one_sequence_and_partial_blocks():
     with pytest.raises(mkd.MKError) as e:  # hidden 272: rows of 272 weights are not whole blocks of 32
         mkd.mk_plan(_desc(cfg.replace(hidden=272), 512), 256)
     assert e.value.status == mkd.MK_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name,batch", [("tiny-moe", 1), ("tiny-moe", 4), ("moe", 1)])
+def test_moe_plan_checks_and_streams_every_expert_once(name, batch):
+    """Mixture-of-experts layers: a router stage and one gate / up and one down op per compute unit
+    that cover a row tile of every expert; the plan checks and accounts every expert's bytes once."""
+    cfg = (synth.SMALL.get(name) or synth.CONFIGS[name]).replace(batch=batch)
+    info = mkd.mk_plan(_desc(cfg, 4096 + 256), 256)
+    assert info.errors == 0, mkd.mk_last_error()  # (includes: every workspace address relocatable)
+    H, F, d, E = cfg.hidden, cfg.ffn, cfg.head_dim, cfg.n_experts
+    per_layer = (E * H + E * 3 * F * H + (cfg.n_q_heads + 2 * cfg.n_kv_heads) * d * H + H * cfg.n_q_heads * d) * 2
+    assert info.weight_bytes == cfg.vocab * H * 2 + cfg.n_layers * per_layer
+    assert info.max_cu_bytes <= 1.05 * info.weight_bytes / 256 + 2 * E * 3 * F * 2 * 4
+
+
+def test_moe_refuses_unsupported_shapes():
+    cfg = synth.SMALL["tiny-moe"]
+    for bad in (cfg.replace(batch=8, ctx=[128] * 8), cfg.replace(top_k=9, n_experts=12), cfg.replace(n_experts=6),
+                cfg.replace(n_experts=68, top_k=2)):
+        with pytest.raises(mkd.MKError) as e:
+            mkd.mk_plan(_desc(bad, 512), 256)
+        assert e.value.status == mkd.MK_ERR_UNSUPPORTED

@@ -23,7 +23,7 @@ def _desc(cfg, max_ctx=MAX_CTX):
     return mkd.make_desc(s["n_layers"], s["hidden"], s["vocab"], s["ffn"], s["n_q_heads"], s["n_kv_heads"],
                          s["head_dim"], s["qk_norm"], s["tied"], s["rms_eps"], s["rope_base"], s["layer_kinds"],
                          s["max_batch"], s["max_ctx"], s["n_delta_heads"], s["delta_dk"], s["delta_dv"],
-                         s["conv_width"])
+                         s["conv_width"], n_experts=s["n_experts"], top_k=s["top_k"])
 
 
 def _clean(rep):
@@ -59,6 +59,8 @@ SHAPES = {
     "gqa8-d64": synth.Config("gqa8-d64", n_layers=2, hidden=512, n_q_heads=16, n_kv_heads=2, head_dim=64,
                              ffn=1024, vocab=2048, batch=2),
     "tiny-hybrid": synth.SMALL["tiny-hybrid"].replace(batch=3, delta_dk=64, delta_dv=64),
+    # mixture of experts: every expert's SwiGLU rows written each launch (zeros when not chosen)
+    "tiny-moe-b4": synth.SMALL["tiny-moe"].replace(batch=4),
 }
 
 
