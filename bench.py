@@ -41,6 +41,8 @@ WORKLOADS = {
               "cache), batch 1, ctx 4096",
     "8b-fp4": "8B-shape decoder with MX fp4 projections (E2M1 codes, E8M0 scales per 32 weights; bf16 "
               "embedding, LM head and KV cache), batch 1, ctx 4096",
+    "moe": "mixture-of-experts decoder (16 layers, hidden 2048, GQA 16/4, every MLP top-8 of 64 SwiGLU experts "
+           "of width 1024, vocab 50304), batch 1, ctx 4096",
 }
 
 
@@ -65,7 +67,11 @@ def bytes_per_step(cfg, ctx_lens) -> float:
     w = 0.0
     attn_kv = 0.0
     for kind in cfg.kinds():
-        w += 2 * proj(F, H) + proj(H, F)
+        if cfg.n_experts:  # the router, and the chosen experts' rows (exactly top_k of them at batch 1;
+            # at larger batches the union of the sequences' choices, bounded here by top_k * batch)
+            w += cfg.n_experts * H * 2 + min(cfg.n_experts, cfg.top_k * B) * (2 * proj(F, H) + proj(H, F))
+        else:
+            w += 2 * proj(F, H) + proj(H, F)
         if kind == 0:
             w += proj((cfg.n_q_heads + 2 * cfg.n_kv_heads) * cfg.head_dim, H) + proj(H, cfg.n_q_heads * cfg.head_dim)
             attn_kv += sum(2.0 * c * cfg.n_kv_heads * cfg.head_dim * 2 for c in ctx_lens)  # read K and V
@@ -418,9 +424,9 @@ def run_window(name: str, window: int, launches: int, warmup: int) -> dict:
             "note": "tokens verified per second: every window token's logits per launch"}
 
 
-PER_CONFIG = ("0.6b", "hybrid", "13b", "8b-fp8", "8b-fp4")  # measured beside the headline 8B workload
+PER_CONFIG = ("0.6b", "hybrid", "13b", "8b-fp8", "8b-fp4", "moe")  # measured beside the headline 8B workload
 WINDOWS = {"8b": 8, "0.6b": 8}            # verify windows timed beside them
-RUN_STEPS = {"8b": 128, "0.6b": 64, "hybrid": 64, "13b": 64, "tiny": 8, "8b-fp8": 128, "8b-fp4": 128}  # decode steps per run
+RUN_STEPS = {"8b": 128, "0.6b": 64, "hybrid": 64, "13b": 64, "tiny": 8, "8b-fp8": 128, "8b-fp4": 128, "moe": 64}  # decode steps per run
 
 
 def main() -> int:
