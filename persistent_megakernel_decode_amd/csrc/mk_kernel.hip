@@ -817,7 +817,7 @@ __device__ __forceinline__ u32 loader_ops(KPtr ap, u32 q0, u32 q1, u32 seq, u32 
   u32 tr_first = 0, tr_blocked = 0;
 #endif
   // every ring slot of one op (an expert's GEMV for a mixture-of-experts op); false on abort
-  auto issue_op = [&](const KArgs& A, const Op& o, u32 ns) -> bool {
+  auto issue_op = [&](const KArgs& A, const Op& o, u32 ns, u32 s_begin) -> bool {
     LayerDesc Ld{};
     AttnItem it{};
     const GemvSeg gsg = gemv_seg(o);
@@ -827,7 +827,7 @@ __device__ __forceinline__ u32 loader_ops(KPtr ap, u32 q0, u32 q1, u32 seq, u32 
     const u32 gs = o.opcode == OP_GEMV && o.norm ? gain_slots(o.K) : 0u;  // gain slots first
     if (o.opcode == OP_ATTN || o.opcode == OP_DELTA) Ld = sload(A.layers + o.layer);
     if (o.opcode == OP_ATTN) it = ic.get(A, o.row0, attn_pps(A.d));
-    for (u32 s = 0; s < ns; ++s) {
+    for (u32 s = s_begin; s < ns; ++s) {
       if (seq >= limit) {  // the ring looks full: publish what has landed, then re-read the consumers
 #if MK_TRACE_STAMPS
         const u32 tb0 = (u32)__builtin_amdgcn_s_memrealtime();
@@ -853,7 +853,7 @@ __device__ __forceinline__ u32 loader_ops(KPtr ap, u32 q0, u32 q1, u32 seq, u32 
 #endif
       }
 #if MK_TRACE_STAMPS
-      if (s == 0) tr_first = (u32)__builtin_amdgcn_s_memrealtime();
+      if (s == s_begin) tr_first = (u32)__builtin_amdgcn_s_memrealtime();
 #endif
       u32x4* dst = g_ring + (seq % NSLOT) * (SLOT / 16);
       if (s < gs) {  // the RMSNorm gain, in order; lanes past the gain re-read its first bytes
@@ -905,17 +905,19 @@ __device__ __forceinline__ u32 loader_ops(KPtr ap, u32 q0, u32 q1, u32 seq, u32 
         any |= moe_choose(z, lane_id() < (u32)A.n_experts, A.top_k, &wl);
       }
       any = uni64(any);
+      // (gate / up: the chosen experts share one pass's inputs, so the RMSNorm gain is streamed once)
+      const u32 gskip = o.opcode == OP_MOE_GU && o.norm ? gain_slots(o.K) : 0u;
       for (uint64_t mset = any; mset; mset &= mset - 1) {
         const u32 e = __builtin_amdgcn_readfirstlane((u32)__builtin_ctzll(mset));
         Op oe = o;
         oe.opcode = OP_GEMV;
         oe.W = o.W + e * o.moe_wstride;
         oe.W2 = o.W2 ? o.W2 + e * o.moe_wstride : 0;
-        if (!issue_op(A, oe, op_slots(A, oe, ic))) return ~0u;
+        if (!issue_op(A, oe, op_slots(A, oe, ic), mset == any ? 0u : gskip)) return ~0u;
       }
     } else {
       if (ns == 0) continue;
-      if (!issue_op(A, o, ns)) return ~0u;
+      if (!issue_op(A, o, ns, 0u)) return ~0u;
     }
 #if MK_TRACE_STAMPS
     {
@@ -1350,9 +1352,13 @@ struct GemvAcc<1, 8> {
 // A mixture-of-experts op's run of one expert through the GEMV path: byte offsets of that expert's
 // input and output blocks, and acc = 1 for the down projection's weighted sum in LDS (EPI_MOE_ACC).
 // (The loader applies the expert's weight offset itself; uniform values.)
+// emask (gate / up): the chosen experts, run as successive passes over the shared inputs, the output
+// blocks xstride bytes apart.
 struct MoeX {
   uint64_t din = 0, dout = 0;
   u32 acc = 0;
+  uint64_t emask = 0;
+  u32 xstride = 0;
 };
 
 // An MX E8M0 scale byte as fp32: 2^(e - 127); 0 is 2^-127 (an fp32 subnormal), 0xFF NaN
@@ -1466,7 +1472,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   constexpr u32 SG = B != 1 ? 0u : (F4 ? (NF == 1 ? 8u : 4u) : (NF == 1 ? 16u : (NF == 2 ? 8u : 0u)));  // staged row groups
   constexpr u32 SS = SG * NF > 0 ? SG * NF : 1u;                          // their slot registers
   u32x4 stg[SS];
-  const bool staged = SG > 0 && pg >= 8 && nrg >= SG;
+  bool staged = SG > 0 && pg >= 8 && nrg >= SG;
   if (staged) {
     const u32 nst = SG * nf;
     if (seq + nst > avail && !wait_avail(A, seq + nst, avail)) return false;
@@ -1483,7 +1489,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   const u32 gsub = w >> lgpg;                        // (PG < 8) this wave's group within a slot
   const u32 qp = w & (pg - 1);                       // (PG < 8) this wave's piece of its group
   const u32 full = pg < 8 ? nrg >> (3 - lgpg) : 0u;  // (PG < 8) slots whose groups all exist
-  const bool staged_s = SGS > 0 && pg < 8 && full >= SGS;
+  bool staged_s = SGS > 0 && pg < 8 && full >= SGS;
   if (staged_s) {
     if (seq + SGS > avail && !wait_avail(A, seq + SGS, avail)) return false;
 #pragma unroll
@@ -1591,206 +1597,218 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
     else (acc).add((wv), xh[f][0], xl[f][0]);                                                \
   } while (0)
 
-  if (NF > 1 || pg >= 8) {
-    // groups in order; a group's nf slots are consecutive and wave w takes piece w of each
-    u32 g0 = 0;
-    if (staged) {  // the staged groups first, from registers (the same arithmetic as below)
-      if constexpr (NF <= 2) {
+  // Several experts' gate / up rows over the same inputs (mixture of experts): one pass per chosen
+  // expert, the inputs, gains and RMS factor shared; otherwise one pass.
+  uint64_t em = uni64(mx.emask);
+  uint64_t dout = em ? uni64((uint64_t)__builtin_ctzll(em) * mx.xstride) : 0ull;
+  float rstd[B];
+  bool okb[B];
+  for (;;) {
+    if (NF > 1 || pg >= 8) {
+      // groups in order; a group's nf slots are consecutive and wave w takes piece w of each
+      u32 g0 = 0;
+      if (staged) {  // the staged groups first, from registers (the same arithmetic as below)
+        if constexpr (NF <= 2) {
 #pragma unroll
-        for (u32 bt = 0; bt < SG / GB; ++bt) {
+          for (u32 bt = 0; bt < SG / GB; ++bt) {
+            GemvAcc<B, P> acc[GB];
+#pragma unroll
+            for (u32 gb = 0; gb < GB; ++gb) acc[gb].init();
+#pragma unroll
+            for (u32 f = 0; f < NF; ++f)
+#pragma unroll
+              for (u32 gb = 0; gb < GB; ++gb)
+                MK_GEMV_ADD(acc[gb], stg[(bt * GB + gb) * NF + f], f, e8m0f(sst[F4 ? (bt * GB + gb) * NF + f : 0]));
+#pragma unroll
+            for (u32 gb = 0; gb < GB; ++gb) acc[gb].finish(lane, bt * GB + gb, w, RW, nrt);
+          }
+        } else {
+#pragma unroll
+          for (u32 g = 0; g < SG; ++g) {
+            GemvAcc<B, P> a0, a1;
+            a0.init();
+            a1.init();
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+              if ((u32)f < nf) {
+                if (f & 1) MK_GEMV_ADD(a1, stg[g * NF + f], f, 1.0f);
+                else MK_GEMV_ADD(a0, stg[g * NF + f], f, 1.0f);
+              }
+            }
+            a0.merge(a1);
+            a0.finish(lane, g, w, RW, nrt);
+          }
+        }
+        g0 = SG;
+        seq += SG * nf;
+      }
+      if constexpr (NF <= 2) {
+        // whole batches of GB groups (NF = nf here): straight-line code, so the groups' matrix-core
+        // chains and extractions interleave
+        constexpr u32 NS = GB * NF;
+        u32 snx[F4 ? NS : 1];  // fp4: the next batch's scale bytes
+        if constexpr (F4) {
+#pragma unroll
+          for (u32 i = 0; i < NS; ++i) snx[i] = s4ld(g0 + i / NF, 8 * (i % NF) + w);
+        }
+        for (; g0 + GB <= nrg; g0 += GB) {
+          u32 scu[F4 ? NS : 1];
+          if constexpr (F4) {
+#pragma unroll
+            for (u32 i = 0; i < NS; ++i) {
+              scu[i] = snx[i];
+              snx[i] = s4ld(g0 + GB + i / NF, 8 * (i % NF) + w);
+            }
+          }
+          if (seq + NS > avail && !wait_avail(A, seq + NS, avail)) return false;
+          u32x4 wv[NS];
+#pragma unroll
+          for (u32 i = 0; i < NS; ++i) wv[i] = g_ring[((seq + i) % NSLOT) * (SLOT / 16) + achunk];
+          release_upto(w, seq + NS);
           GemvAcc<B, P> acc[GB];
 #pragma unroll
           for (u32 gb = 0; gb < GB; ++gb) acc[gb].init();
 #pragma unroll
           for (u32 f = 0; f < NF; ++f)
 #pragma unroll
-            for (u32 gb = 0; gb < GB; ++gb)
-              MK_GEMV_ADD(acc[gb], stg[(bt * GB + gb) * NF + f], f, e8m0f(sst[F4 ? (bt * GB + gb) * NF + f : 0]));
+            for (u32 gb = 0; gb < GB; ++gb) MK_GEMV_ADD(acc[gb], wv[gb * NF + f], f, e8m0f(scu[F4 ? gb * NF + f : 0]));
 #pragma unroll
-          for (u32 gb = 0; gb < GB; ++gb) acc[gb].finish(lane, bt * GB + gb, w, RW, nrt);
-        }
-      } else {
-#pragma unroll
-        for (u32 g = 0; g < SG; ++g) {
-          GemvAcc<B, P> a0, a1;
-          a0.init();
-          a1.init();
-#pragma unroll
-          for (int f = 0; f < NF; ++f) {
-            if ((u32)f < nf) {
-              if (f & 1) MK_GEMV_ADD(a1, stg[g * NF + f], f, 1.0f);
-              else MK_GEMV_ADD(a0, stg[g * NF + f], f, 1.0f);
-            }
-          }
-          a0.merge(a1);
-          a0.finish(lane, g, w, RW, nrt);
+          for (u32 gb = 0; gb < GB; ++gb) acc[gb].finish(lane, g0 + gb, w, RW, nrt);
+          seq += NS;
         }
       }
-      g0 = SG;
-      seq += SG * nf;
-    }
-    if constexpr (NF <= 2) {
-      // whole batches of GB groups (NF = nf here): straight-line code, so the groups' matrix-core
-      // chains and extractions interleave
-      constexpr u32 NS = GB * NF;
-      u32 snx[F4 ? NS : 1];  // fp4: the next batch's scale bytes
+      // remaining groups one at a time (every group when NF = 8, with nf <= 8 slots each)
+      for (; g0 < nrg; ++g0) {
+        if (seq + nf > avail && !wait_avail(A, seq + nf, avail)) return false;
+        u32x4 wv[NF];
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          if ((u32)f < nf) wv[f] = g_ring[((seq + f) % NSLOT) * (SLOT / 16) + achunk];
+        release_upto(w, seq + nf);
+        // two accumulators (even / odd fragments) keep four chains in flight
+        GemvAcc<B, P> a0, a1;
+        a0.init();
+        a1.init();
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if ((u32)f < nf) {
+            const float sc = F4 ? e8m0f(s4ld(g0, 8 * f + w)) : 1.0f;
+            if (f & 1) MK_GEMV_ADD(a1, wv[f], f, sc);
+            else MK_GEMV_ADD(a0, wv[f], f, sc);
+          }
+        }
+        a0.merge(a1);
+        a0.finish(lane, g0, w, RW, nrt);
+        seq += nf;
+      }
+    } else {
+      // PG < 8: each slot holds 8 / PG groups, one piece of a group per wave
+      u32 s0 = 0;
+      if (staged_s) {  // the staged slots first, from registers (the same arithmetic as below)
+#pragma unroll
+        for (u32 bt = 0; bt < SGS / 4; ++bt) {
+          GemvAcc<B, P> acc[4];
+#pragma unroll
+          for (u32 i = 0; i < 4; ++i) {
+            acc[i].init();
+            MK_GEMV_ADD(acc[i], stg[bt * 4 + i], 0, e8m0f(sst[F4 ? bt * 4 + i : 0]));
+          }
+#pragma unroll
+          for (u32 i = 0; i < 4; ++i) acc[i].finish(lane, (((bt * 4 + i) * 8) >> lgpg) + gsub, qp, RW, nrt);
+        }
+        s0 = SGS;
+        seq += SGS;
+      }
+      u32 snx[F4 ? 4 : 1];  // fp4: the next batch's scale bytes
       if constexpr (F4) {
 #pragma unroll
-        for (u32 i = 0; i < NS; ++i) snx[i] = s4ld(g0 + i / NF, 8 * (i % NF) + w);
+        for (u32 i = 0; i < 4; ++i) snx[i] = s4ld((((s0 + i) * 8) >> lgpg) + gsub, qp);
       }
-      for (; g0 + GB <= nrg; g0 += GB) {
-        u32 scu[F4 ? NS : 1];
+      for (; s0 + 4 <= full; s0 += 4) {
+        u32 scu[F4 ? 4 : 1];
         if constexpr (F4) {
 #pragma unroll
-          for (u32 i = 0; i < NS; ++i) {
+          for (u32 i = 0; i < 4; ++i) {
             scu[i] = snx[i];
-            snx[i] = s4ld(g0 + GB + i / NF, 8 * (i % NF) + w);
+            snx[i] = s4ld((((s0 + 4 + i) * 8) >> lgpg) + gsub, qp);
           }
         }
-        if (seq + NS > avail && !wait_avail(A, seq + NS, avail)) return false;
-        u32x4 wv[NS];
+        if (seq + 4 > avail && !wait_avail(A, seq + 4, avail)) return false;
+        u32x4 wv[4];
 #pragma unroll
-        for (u32 i = 0; i < NS; ++i) wv[i] = g_ring[((seq + i) % NSLOT) * (SLOT / 16) + achunk];
-        release_upto(w, seq + NS);
-        GemvAcc<B, P> acc[GB];
-#pragma unroll
-        for (u32 gb = 0; gb < GB; ++gb) acc[gb].init();
-#pragma unroll
-        for (u32 f = 0; f < NF; ++f)
-#pragma unroll
-          for (u32 gb = 0; gb < GB; ++gb) MK_GEMV_ADD(acc[gb], wv[gb * NF + f], f, e8m0f(scu[F4 ? gb * NF + f : 0]));
-#pragma unroll
-        for (u32 gb = 0; gb < GB; ++gb) acc[gb].finish(lane, g0 + gb, w, RW, nrt);
-        seq += NS;
-      }
-    }
-    // remaining groups one at a time (every group when NF = 8, with nf <= 8 slots each)
-    for (; g0 < nrg; ++g0) {
-      if (seq + nf > avail && !wait_avail(A, seq + nf, avail)) return false;
-      u32x4 wv[NF];
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        if ((u32)f < nf) wv[f] = g_ring[((seq + f) % NSLOT) * (SLOT / 16) + achunk];
-      release_upto(w, seq + nf);
-      // two accumulators (even / odd fragments) keep four chains in flight
-      GemvAcc<B, P> a0, a1;
-      a0.init();
-      a1.init();
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        if ((u32)f < nf) {
-          const float sc = F4 ? e8m0f(s4ld(g0, 8 * f + w)) : 1.0f;
-          if (f & 1) MK_GEMV_ADD(a1, wv[f], f, sc);
-          else MK_GEMV_ADD(a0, wv[f], f, sc);
-        }
-      }
-      a0.merge(a1);
-      a0.finish(lane, g0, w, RW, nrt);
-      seq += nf;
-    }
-  } else {
-    // PG < 8: each slot holds 8 / PG groups, one piece of a group per wave
-    u32 s0 = 0;
-    if (staged_s) {  // the staged slots first, from registers (the same arithmetic as below)
-#pragma unroll
-      for (u32 bt = 0; bt < SGS / 4; ++bt) {
+        for (int i = 0; i < 4; ++i) wv[i] = g_ring[((seq + i) % NSLOT) * (SLOT / 16) + achunk];
+        release_upto(w, seq + 4);
         GemvAcc<B, P> acc[4];
 #pragma unroll
-        for (u32 i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i) {
           acc[i].init();
-          MK_GEMV_ADD(acc[i], stg[bt * 4 + i], 0, e8m0f(sst[F4 ? bt * 4 + i : 0]));
+          MK_GEMV_ADD(acc[i], wv[i], 0, e8m0f(scu[F4 ? i : 0]));
         }
 #pragma unroll
-        for (u32 i = 0; i < 4; ++i) acc[i].finish(lane, (((bt * 4 + i) * 8) >> lgpg) + gsub, qp, RW, nrt);
+        for (int i = 0; i < 4; ++i) acc[i].finish(lane, (((s0 + i) * 8) >> lgpg) + gsub, qp, RW, nrt);
+        seq += 4;
       }
-      s0 = SGS;
-      seq += SGS;
-    }
-    u32 snx[F4 ? 4 : 1];  // fp4: the next batch's scale bytes
-    if constexpr (F4) {
-#pragma unroll
-      for (u32 i = 0; i < 4; ++i) snx[i] = s4ld((((s0 + i) * 8) >> lgpg) + gsub, qp);
-    }
-    for (; s0 + 4 <= full; s0 += 4) {
-      u32 scu[F4 ? 4 : 1];
-      if constexpr (F4) {
-#pragma unroll
-        for (u32 i = 0; i < 4; ++i) {
-          scu[i] = snx[i];
-          snx[i] = s4ld((((s0 + 4 + i) * 8) >> lgpg) + gsub, qp);
+      for (; s0 < nslots; ++s0) {
+        if (seq + 1 > avail && !wait_avail(A, seq + 1, avail)) return false;
+        const u32x4 wv = g_ring[(seq % NSLOT) * (SLOT / 16) + achunk];
+        release_upto(w, seq + 1);
+        const u32 g = ((s0 * 8) >> lgpg) + gsub;
+        if (g < nrg) {
+          GemvAcc<B, P> acc;
+          acc.init();
+          MK_GEMV_ADD(acc, wv, 0, F4 ? e8m0f(s4ld(g, qp)) : 1.0f);
+          acc.finish(lane, g, qp, RW, nrt);
         }
+        seq += 1;
       }
-      if (seq + 4 > avail && !wait_avail(A, seq + 4, avail)) return false;
-      u32x4 wv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wv[i] = g_ring[((seq + i) % NSLOT) * (SLOT / 16) + achunk];
-      release_upto(w, seq + 4);
-      GemvAcc<B, P> acc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i].init();
-        MK_GEMV_ADD(acc[i], wv[i], 0, e8m0f(scu[F4 ? i : 0]));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i].finish(lane, (((s0 + i) * 8) >> lgpg) + gsub, qp, RW, nrt);
-      seq += 4;
     }
-    for (; s0 < nslots; ++s0) {
-      if (seq + 1 > avail && !wait_avail(A, seq + 1, avail)) return false;
-      const u32x4 wv = g_ring[(seq % NSLOT) * (SLOT / 16) + achunk];
-      release_upto(w, seq + 1);
-      const u32 g = ((s0 * 8) >> lgpg) + gsub;
-      if (g < nrg) {
-        GemvAcc<B, P> acc;
-        acc.init();
-        MK_GEMV_ADD(acc, wv, 0, F4 ? e8m0f(s4ld(g, qp)) : 1.0f);
-        acc.finish(lane, g, qp, RW, nrt);
-      }
-      seq += 1;
-    }
-  }
-  if (!cbar(A, gen)) return false;
+    if (!cbar(A, gen)) return false;
 
-  // epilogue: one output row per compute thread
-  float rstd[B];
-#pragma unroll
-  for (int b = 0; b < B; ++b) {
-    rstd[b] = 1.0f;
-    if (norm) {
-      float tot = 0.0f;
-      for (int j = 0; j < NC; ++j) tot += g_scr[j * B + b];
-      rstd[b] = 1.0f / sqrtf(tot / (float)K + A.rms_eps);
-    }
-  }
-  bool okb[B];
-#pragma unroll
-  for (int b = 0; b < B; ++b) okb[b] = epi == EPI_LOGITS && b < A.batch && row_ok_fix(A, b, __builtin_bit_cast(int32_t, rv[b]));
-  float* logits = A.logits + (size_t)cstep() * A.batch * A.V;  // this step's rows
-  for (u32 r = tid; r < nrows; r += NC * 64) {
-    const u32 row = row0 + r;
+    // epilogue: one output row per compute thread
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      float v = 0.0f;
-      for (u32 j = 0; j < RW; ++j) v += g_red[(j * B + b) * nrt + r];
-      v *= rstd[b];
-      if constexpr (F8) v *= r == tid ? sc0 : row_scale(r, false);
-      if (epi == EPI_SWIGLU) {
-        float u = 0.0f;
-        for (u32 j = 0; j < RW; ++j) u += g_red[(j * B + b) * nrt + r + nrows];
-        if constexpr (F8) u *= r == tid ? sc1 : row_scale(r, true);
-        st_tag((float*)outp + (size_t)b * ld_out + row, silu(v) * (u * rstd[b]), par);
-      } else if (epi == EPI_RESID) {
-        const float* rp = (const float*)resp + (size_t)b * ld_out + row;
-        const float x = tagged_fix(A, rp, r == tid ? rv[b] : ld_sc1(rp));
-        st_tag((float*)outp + (size_t)b * ld_out + row, x + v, par);
-      } else if (epi == EPI_MOE_ACC) {  // this expert's share of the rows (one thread per row)
-        g_moeacc[b * 64 * NC + r] += g_moew[b] * v;
-      } else if (epi == EPI_STORE) {
-        st_tag((float*)outp + (size_t)b * ld_out + row, v, par);
-      } else if (b < A.batch) {  // EPI_LOGITS
-        logits[(size_t)b * A.V + row] = okb[b] ? v : __builtin_nanf("");
+      rstd[b] = 1.0f;
+      if (norm) {
+        float tot = 0.0f;
+        for (int j = 0; j < NC; ++j) tot += g_scr[j * B + b];
+        rstd[b] = 1.0f / sqrtf(tot / (float)K + A.rms_eps);
       }
     }
+#pragma unroll
+    for (int b = 0; b < B; ++b) okb[b] = epi == EPI_LOGITS && b < A.batch && row_ok_fix(A, b, __builtin_bit_cast(int32_t, rv[b]));
+    float* logits = A.logits + (size_t)cstep() * A.batch * A.V;  // this step's rows
+    for (u32 r = tid; r < nrows; r += NC * 64) {
+      const u32 row = row0 + r;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        float v = 0.0f;
+        for (u32 j = 0; j < RW; ++j) v += g_red[(j * B + b) * nrt + r];
+        v *= rstd[b];
+        if constexpr (F8) v *= r == tid ? sc0 : row_scale(r, false);
+        if (epi == EPI_SWIGLU) {
+          float u = 0.0f;
+          for (u32 j = 0; j < RW; ++j) u += g_red[(j * B + b) * nrt + r + nrows];
+          if constexpr (F8) u *= r == tid ? sc1 : row_scale(r, true);
+          st_tag((float*)(outp + dout) + (size_t)b * ld_out + row, silu(v) * (u * rstd[b]), par);
+        } else if (epi == EPI_RESID) {
+          const float* rp = (const float*)resp + (size_t)b * ld_out + row;
+          const float x = tagged_fix(A, rp, r == tid ? rv[b] : ld_sc1(rp));
+          st_tag((float*)outp + (size_t)b * ld_out + row, x + v, par);
+        } else if (epi == EPI_MOE_ACC) {  // this expert's share of the rows (one thread per row)
+          g_moeacc[b * 64 * NC + r] += g_moew[b] * v;
+        } else if (epi == EPI_STORE) {
+          st_tag((float*)outp + (size_t)b * ld_out + row, v, par);
+        } else if (b < A.batch) {  // EPI_LOGITS
+          logits[(size_t)b * A.V + row] = okb[b] ? v : __builtin_nanf("");
+        }
+      }
+    }
+    if (em == 0) break;
+    em &= em - 1;
+    if (em == 0) break;
+    dout = uni64((uint64_t)__builtin_ctzll(em) * mx.xstride);
+    staged = staged_s = false;  // (the staged registers held the first pass's slots)
+    if (!cbar(A, gen)) return false;  // the next pass rewrites the partial sums
   }
   if (!AM || epi != EPI_LOGITS || !A.amax) return true;
   // on-device greedy choice: this thread's best row per sequence, from the sums still in LDS
@@ -1866,10 +1884,10 @@ __device__ __forceinline__ bool op_moe(const KArgs& A, const Op& o, u32 w, u32& 
 #pragma unroll
         for (int b = 0; b < B; ++b) st_tag(out + (size_t)b * ld_out + row0 + r, 0.0f, par);
     }
-    for (uint64_t mset = any; mset; mset &= mset - 1) {
-      const u32 e = __builtin_amdgcn_readfirstlane((u32)__builtin_ctzll(mset));
+    if (any) {  // every chosen expert in one GEMV: the inputs, gains and RMS factor read once
       MoeX mx;
-      mx.dout = (uint64_t)e * opq(o.moe_xstride);
+      mx.emask = any;
+      mx.xstride = opq(o.moe_xstride);
       const bool alive = op_gemv<B, AM, WF>(A, o, w, seq, gen, mx);
       seq = __builtin_amdgcn_readfirstlane(seq);
       gen = __builtin_amdgcn_readfirstlane(gen);
