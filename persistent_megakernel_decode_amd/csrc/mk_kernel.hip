@@ -71,7 +71,7 @@ __shared__ u32 g_bcast[4];
 // the compute waves are on it) and its tokens.
 // mixture of experts: the running expert's weight per sequence, and the down projection's sums over
 // the chosen experts (sequence b, row r of the op at [b * 64 NC + r]; each row owned by one thread)
-__shared__ float g_moew[4];
+__shared__ float g_moew[4 * 64];  // [sequence][expert]
 __shared__ __attribute__((aligned(16))) float g_moeacc[4 * 64 * NC];
 __shared__ u32 g_ctag;
 __shared__ u32 g_cstep;
@@ -1349,11 +1349,11 @@ struct GemvAcc<1, 8> {
   }
 };
 
-// A mixture-of-experts op's run of one expert through the GEMV path: byte offsets of that expert's
-// input and output blocks, and acc = 1 for the down projection's weighted sum in LDS (EPI_MOE_ACC).
-// (The loader applies the expert's weight offset itself; uniform values.)
-// emask (gate / up): the chosen experts, run as successive passes over the shared inputs, the output
-// blocks xstride bytes apart.
+// A mixture-of-experts op's run of its chosen experts (emask) through the GEMV path, one pass per
+// expert: gate / up over shared inputs into output blocks xstride bytes apart, or (acc = 1) down
+// over each expert's own input block (xstride apart), its rows times the expert's routing weight
+// per sequence (g_moew) summed in LDS (EPI_MOE_ACC).  din / dout: fixed byte offsets of the input /
+// output.  (The loader applies each expert's weight offset itself; uniform values.)
 struct MoeX {
   uint64_t din = 0, dout = 0;
   u32 acc = 0;
@@ -1396,7 +1396,11 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   const u32 kv = K / EM;  // stream elements per row
   const u32 nslots = opq(o.nslots) - (norm ? gain_slots(K) : 0u);  // weight slots (after the gain's)
   const u32 ld_in = opq(o.ld_in), ld_out = opq(o.ld_out);
-  const uint64_t in = opq(o.in) + mx.din, outp = opq(o.out) + mx.dout, resp = opq(o.res);
+  // (down of several experts: the first pass reads the first chosen expert's inputs)
+  const uint64_t in0 = opq(o.in);
+  const uint64_t in = in0 + (mx.acc && mx.emask ? uni64((uint64_t)__builtin_ctzll(uni64(mx.emask)) * mx.xstride)
+                                                 : mx.din);
+  const uint64_t outp = opq(o.out) + mx.dout, resp = opq(o.res);
   const bool swiglu = epi == EPI_SWIGLU;
   const u32 nrt = swiglu ? 2 * nrows : nrows;  // stream rows
   const u32 nrg = nrt / R;                      // row groups
@@ -1468,8 +1472,9 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   // slots before waiting for their inputs: while this op waits (for the merged attention heads, the
   // last SwiGLU rows) the loader keeps streaming the following bytes into the freed ring instead of
   // idling this compute unit's share of HBM.
-  // (fp4 fragments hold four times the inputs: half the staged groups keep the registers in bounds)
-  constexpr u32 SG = B != 1 ? 0u : (F4 ? (NF == 1 ? 8u : 4u) : (NF == 1 ? 16u : (NF == 2 ? 8u : 0u)));  // staged row groups
+  // (fp4 stages nothing: staging makes an op wait for slots before it can poll its inputs, and for
+  // fp4 that wait measured longer than the streaming it saved -- 8B shape 2.61 -> 2.48 ms without)
+  constexpr u32 SG = B != 1 || F4 ? 0u : (NF == 1 ? 16u : (NF == 2 ? 8u : 0u));  // staged row groups
   constexpr u32 SS = SG * NF > 0 ? SG * NF : 1u;                          // their slot registers
   u32x4 stg[SS];
   bool staged = SG > 0 && pg >= 8 && nrg >= SG;
@@ -1483,7 +1488,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
   }
   // With PG < 8 pieces per row group a slot holds 8 / PG groups, one piece of one group per wave:
   // the first SGS slots (whole groups only) are staged the same way.
-  constexpr u32 SGS = (B == 1 && NF == 1) ? 8u : 0u;
+  constexpr u32 SGS = (B == 1 && NF == 1 && !F4) ? 8u : 0u;
   static_assert(SGS <= SS, "staged slots fit the staging registers");
   const u32 lgpg = pg < 8 ? (u32)__builtin_ctz(pg) : 0u;
   const u32 gsub = w >> lgpg;                        // (PG < 8) this wave's group within a slot
@@ -1597,13 +1602,25 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
     else (acc).add((wv), xh[f][0], xl[f][0]);                                                \
   } while (0)
 
-  // Several experts' gate / up rows over the same inputs (mixture of experts): one pass per chosen
-  // expert, the inputs, gains and RMS factor shared; otherwise one pass.
+  // Mixture of experts: one pass per chosen expert -- gate / up over the shared inputs, gains and RMS
+  // factor, or down over each expert's own inputs (one fragment: the next expert's fetched during
+  // this pass); otherwise one pass.
   uint64_t em = uni64(mx.emask);
   uint64_t dout = em ? uni64((uint64_t)__builtin_ctzll(em) * mx.xstride) : 0ull;
+  const bool moe_acc = mx.acc && em;
+  constexpr bool XPRE = NF == 1 && !F8 && !F4;  // the next expert's inputs prefetched
+  float xn[XPRE ? XN : 1];
+  const size_t xrow = (size_t)(B == 1 ? 0u : bl) * ld_in;  // this lane's sequence row of an input block
   float rstd[B];
   bool okb[B];
   for (;;) {
+    const u32 ecur = em ? __builtin_amdgcn_readfirstlane((u32)__builtin_ctzll(em)) : 0u;
+    if constexpr (XPRE) {
+      const uint64_t rest = em & (em - 1);
+      if (moe_acc && rest && (fv & 1u))
+        ldn_sc1<XN>((const float*)(in0 + (uint64_t)__builtin_ctzll(rest) * mx.xstride) + xrow +
+                        (pg >= 8 ? w : w % pg) * KP + koff, xn);
+    }
     if (NF > 1 || pg >= 8) {
       // groups in order; a group's nf slots are consecutive and wave w takes piece w of each
       u32 g0 = 0;
@@ -1795,7 +1812,7 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
           const float x = tagged_fix(A, rp, r == tid ? rv[b] : ld_sc1(rp));
           st_tag((float*)outp + (size_t)b * ld_out + row, x + v, par);
         } else if (epi == EPI_MOE_ACC) {  // this expert's share of the rows (one thread per row)
-          g_moeacc[b * 64 * NC + r] += g_moew[b] * v;
+          g_moeacc[b * 64 * NC + r] += g_moew[b * 64 + ecur] * v;
         } else if (epi == EPI_STORE) {
           st_tag((float*)outp + (size_t)b * ld_out + row, v, par);
         } else if (b < A.batch) {  // EPI_LOGITS
@@ -1807,6 +1824,40 @@ __device__ __forceinline__ bool op_gemv_nf(const KArgs& A, const Op& o, u32 w, u
     em &= em - 1;
     if (em == 0) break;
     dout = uni64((uint64_t)__builtin_ctzll(em) * mx.xstride);
+    // (down over several experts runs in one call only with one input fragment per wave, where the
+    // next expert's inputs are prefetched; wider inputs take one call per expert, see op_moe)
+    if constexpr (XPRE) {
+      if (moe_acc) {  // the next expert's inputs, prefetched during this pass, then polled
+        xin = (const float*)(in0 + (uint64_t)__builtin_ctzll(em) * mx.xstride) + xrow;
+#pragma unroll
+        for (int e = 0; e < (int)XN; ++e) xf[0][e] = (fv & 1u) ? xn[e] : 0.0f;
+        if (flags & OPF_TAGGED_IN) {
+          u32 todo = 0;
+#pragma unroll
+          for (int f = 0; f < NF; ++f) todo |= ((fv >> f) & 1u) && !tags_ok<XN>(xf[f], par) ? 1u << f : 0u;
+          Watchdog wd(A);
+          while (__builtin_amdgcn_ballot_w64(todo != 0) != 0) {
+            if (aborted() || wd.expired()) return false;
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+              const u32 q = pg >= 8 ? 8 * f + w : w % pg;
+              if ((todo >> f) & 1u) ldn_sc1<XN>(xin + (q * KP + koff), xf[f]);
+            }
+            todo = 0;
+#pragma unroll
+            for (int f = 0; f < NF; ++f) todo |= ((fv >> f) & 1u) && !tags_ok<XN>(xf[f], par) ? 1u << f : 0u;
+          }
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          u32x4 h, l;
+          split_bf16x8(xf[f], h, l);
+          xh[f][0] = __builtin_bit_cast(bf16x8, h);
+          xl[f][0] = __builtin_bit_cast(bf16x8, l);
+        }
+      }
+    }
     staged = staged_s = false;  // (the staged registers held the first pass's slots)
     if (!cbar(A, gen)) return false;  // the next pass rewrites the partial sums
   }
@@ -1898,13 +1949,18 @@ __device__ __forceinline__ bool op_moe(const KArgs& A, const Op& o, u32 w, u32& 
   if (tid < nrows)
 #pragma unroll
     for (int b = 0; b < B; ++b) g_moeacc[b * 64 * NC + tid] = 0.0f;
-  for (uint64_t mset = any; mset; mset &= mset - 1) {
-    const u32 e = __builtin_amdgcn_readfirstlane((u32)__builtin_ctzll(mset));
-    if (w == 0 && lane == 0)
+  if (w == 0)  // every expert's routing weight per sequence (lane = expert; 0 unless chosen)
 #pragma unroll
-      for (int b = 0; b < B; ++b) g_moew[b] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl[b]), e));
+    for (int b = 0; b < B; ++b) g_moew[b * 64 + lane] = wl[b];
+  // every chosen expert in one GEMV, one pass each (one input fragment per wave: up to 8 pieces per
+  // row group); otherwise one call per expert
+  const bool one_call = opq(o.ppr) <= 8u;
+  for (uint64_t mset = any; mset;) {
+    const uint64_t run = one_call ? mset : (mset & (~mset + 1ull));
+    mset = one_call ? 0ull : (mset & (mset - 1));
     MoeX mx;
-    mx.din = (uint64_t)e * opq(o.moe_xstride);
+    mx.emask = uni64(run);
+    mx.xstride = opq(o.moe_xstride);
     mx.acc = 1;
     const bool alive = op_gemv<B, AM, WF>(A, o, w, seq, gen, mx);
     seq = __builtin_amdgcn_readfirstlane(seq);
