@@ -88,7 +88,9 @@ def bytes_per_step(cfg, ctx_lens) -> float:
 
 
 PMC_FILES = {"8b": os.path.join(ROOT, "profiles", "megakernel_8b_b1_ctx4096_pmc.txt"),
-             "8b-fp8": os.path.join(ROOT, "profiles", "megakernel_8b_fp8_b1_ctx4096_pmc.txt")}
+             "8b-fp8": os.path.join(ROOT, "profiles", "megakernel_8b_fp8_b1_ctx4096_pmc.txt"),
+             "8b-fp4": os.path.join(ROOT, "profiles", "megakernel_8b_fp4_b1_ctx4096_pmc.txt"),
+             "moe": os.path.join(ROOT, "profiles", "megakernel_moe_b1_ctx4096_pmc.txt")}
 
 
 def kernel_source_hash(texts=None) -> str:

@@ -7,7 +7,7 @@ in hand, "tail" how long its last op ends after its median op.
 """
 import numpy as np
 
-OPCODES = {1: "embed", 2: "gemv", 3: "attention", 4: "delta", 5: "mmv"}
+OPCODES = {1: "embed", 2: "gemv", 3: "attention", 4: "delta", 5: "mmv", 6: "moe_gate_up", 7: "moe_down"}
 
 
 def unwrap(tr: dict) -> np.ndarray:
@@ -50,7 +50,7 @@ def check(tr: dict) -> list:
 
 
 def op_summary(tr: dict) -> dict:
-    """Stage time summed per op kind (embed / gemv / attention / delta / mmv) over the step, in us,
+    """Stage time summed per op kind (embed / gemv / attention / delta / mmv / moe_gate_up / moe_down) over the step, in us,
     with the part of it the median op spent waiting for its inputs."""
     out = {}
     for r in stage_table(tr):
