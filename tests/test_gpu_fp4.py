@@ -5,9 +5,9 @@ Same gates as the bf16 parity tests (gpu_harness): logits within 1e-2 max relati
 oracle's greedy id wherever its top-2 gap exceeds 1e-2, per-layer mid-states within 2e-3 normwise,
 and for the delta-rule layers the recurrent and conv states.  fp4 runs one sequence per step; the
 cases cover every shape of that projection path: pieces per row group 1, 2 and 4 (slots holding
-several row groups), 8 with and without padding pieces and row groups staged in registers, 16 (two
-input fragments of 32 per wave, with padding), the RMSNorm gains, q/k norm with a tied bf16 LM
-head, the delta-rule projections, multi-step launches, and the 8B shape at full size.
+several row groups), 8 with and without padding pieces, 16 (two input fragments of 32 per wave,
+with padding), the RMSNorm gains, q/k norm with a tied bf16 LM head, the delta-rule projections,
+multi-step launches, and the 0.6B and 8B shapes at full size.
 """
 import numpy as np
 import pytest
@@ -26,13 +26,16 @@ CASES = {
     "hybrid-fp4": (synth.SMALL["tiny-hybrid"].replace(name="hybrid-fp4", weights="fp4", delta_dk=64, delta_dv=64,
                                                       batch=1, ctx=[16]), 6),
     # QKV / gate-up over 2048 inputs (2 pieces), o_proj over 6144 (8 pieces, 2 of them padding),
-    # down over 10240 (16 pieces, 6 of them padding: two fragments of 32 inputs per wave, staged)
+    # down over 10240 (16 pieces, 6 of them padding: two fragments of 32 inputs per wave)
     "mid-fp4": (synth.Config("mid-fp4", n_layers=2, hidden=2048, n_q_heads=48, n_kv_heads=12, head_dim=128,
                              ffn=10240, vocab=4096, batch=1, ctx=[300], steps=3, seed=41, gain_range=(0.5, 1.5),
                              weights="fp4"), 3),
-    # gate-up over 1024 inputs (1 piece), down over 8192 (8 pieces, no padding, staged)
+    # gate-up over 1024 inputs (1 piece), down over 8192 (8 pieces, no padding)
     "wide-fp4": (synth.Config("wide-fp4", n_layers=2, hidden=1024, n_q_heads=8, n_kv_heads=4, head_dim=128,
                               ffn=8192, vocab=2048, batch=1, ctx=[77], steps=3, seed=42, weights="fp4"), 3),
+    # the 0.6B shape (q/k norm, tied bf16 LM head over 151936 rows; QKV / gate-up over 1024 inputs:
+    # 1 piece, o_proj over 2048: 2, down over 3072: 3 padded to 4)
+    "0.6b-fp4": (synth.CONFIGS["0.6b"].replace(name="0.6b-fp4", weights="fp4"), 3),
     # the 8B shape (QKV / o_proj / gate-up over 4096 inputs: 4 pieces; down over 14336: 16 pieces,
     # 2 of them padding), bf16 LM head over 128256 rows
     "8b-fp4": (synth.CONFIGS["8b"].replace(name="8b-fp4", weights="fp4"), 3),

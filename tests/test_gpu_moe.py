@@ -89,3 +89,16 @@ def test_moe_refuses_verify_windows():
         assert rc == mkd.MK_ERR_UNSUPPORTED, rc
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("case", ["small-moe-b2", "tiny-moe-b4"])
+def test_moe_parity_counters(case, monkeypatch):
+    """The same checks with every dependency taken through the stage counters (the diagnostic plan):
+    the router, gate / up and down stages of the mixture-of-experts layers signal and wait by counter."""
+    monkeypatch.setenv("MK_STAGE_COUNTERS", "1")
+    cfg, steps, schedule = CASES[case]
+    rep = run_parity(cfg, steps, schedule=schedule)
+    say(f"[{case}, counters] {rep.steps} steps, worst logits rel {rep.worst_rel:.2e}, worst mid {rep.worst_mid:.2e}, "
+        f"routing {rep.route_agree}/{rep.route_checked}")
+    assert not rep.failures, "\n".join(rep.failures[:20])
+    assert rep.steps == steps
